@@ -1,0 +1,90 @@
+"""Exact decoding of the quantized indexer inputs, and bf16 score storage.
+
+Test infrastructure only (see the package docstring).
+
+The pages state the indexer's QK path runs in FP4 and its scores are stored
+as BF16 ("DeepSeek V4 结构速览", Lightning Indexer); the fp8 variant follows
+the V3.2-style indexer.  The formats are the OCP ones:
+
+* E4M3 (FN): 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent field 0
+  is subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN; largest finite 448.
+* E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; magnitudes
+  {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+* E8M0: an unsigned power of two, 2^(e - 127); 0xFF is NaN.
+* MXFP4 (OCP MX v1.0): blocks of 32 E2M1 elements sharing one E8M0 scale;
+  two elements per byte, the even element in the low nibble.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """E4M3 byte codes -> float64 values (bit-field decoding)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    v = np.where(e == 0, sub, normal)
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return sign * v
+
+
+def decode_e2m1(nibbles: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes -> float64 values (bit-field decoding)."""
+    n = np.asarray(nibbles, dtype=np.uint8).astype(np.int64)
+    sign = np.where(n & 0x8, -1.0, 1.0)
+    e = (n >> 1) & 0x3
+    m = (n & 0x1).astype(np.float64)
+    v = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0))
+    return sign * v
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def dequant_fp8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """x = E4M3(code) * row_scale, the scale shared along the last axis."""
+    return decode_e4m3(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Unpack [..., n/2] bytes and [..., n/32] E8M0 scales to float64 [..., n]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = p & 0x0F
+    hi = p >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*p.shape[:-1], p.shape[-1] * 2)
+    vals = decode_e2m1(nib)
+    n = vals.shape[-1]
+    blocks = vals.reshape(*vals.shape[:-1], n // 32, 32)
+    blocks = blocks * decode_e8m0(scales)[..., None]
+    return blocks.reshape(vals.shape)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def store_f32(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest float32 (ties to even), as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def store_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> nearest bfloat16 (ties to even), as float64.
+
+    This is how a score computed in fp32 is stored in BF16.  +-inf stay
+    infinite; the rounding is written out on the float32 bit pattern."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    finite = np.isfinite(f)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    r = np.where(finite, r, f.view(np.uint32))
+    return r.view(np.float32).astype(np.float64)
