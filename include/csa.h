@@ -1,0 +1,229 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed sparse attention library.
+ *
+ * Five entry points, one per stage of DeepSeek-V4's compressed sparse
+ * attention (CSA) and heavily compressed attention (HCA) layer:
+ *
+ *   csa_compress      C4A / C128A KV compressor
+ *   lightning_index   indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
+ *   topk_select       causal Top-k over the indexer scores
+ *   sparse_mqa_attn   shared-KV MQA over the Top-k entries plus the window
+ *   hca_attn          dense shared-KV MQA over all C128A entries plus the
+ *                     window, with an attention sink
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.     Every tensor pointer is device memory owned by the caller.  The
+ *             library never allocates, frees or keeps caller memory; scratch
+ *             space comes only from the caller's `workspace`.  Tensors are
+ *             dense, row-major, innermost dimension last.  Every pointer must
+ *             be 16-byte aligned.
+ * Positions.  Token positions are absolute and 0-based.  A call's T query
+ *             tokens are positions q_pos0 .. q_pos0+T-1 in every sequence of
+ *             the batch.  Compressed entry s of ratio m covers raw tokens
+ *             m*s .. m*s+m-1 and is visible to position t iff its whole
+ *             block has arrived: s < V_m(t) = floor((t+1)/m).
+ * Streams.    `stream` is a hipStream_t passed as void* (NULL = the null
+ *             stream).  Calls are asynchronous: a return of CSA_OK means the
+ *             arguments passed validation and the kernels were launched;
+ *             a device-side fault shows up at the caller's synchronisation.
+ * Errors.     Arguments are validated on the host before any HIP call.  A
+ *             non-zero return leaves every output untouched, and
+ *             csa_last_error() returns a message (thread-local, valid until
+ *             the next call on the same thread).
+ * Threads.    Entry points are thread-safe; concurrent calls on one stream
+ *             are serialised by the stream.
+ * Numerics.   Floating-point work is fp32 (bf16 MFMA products with fp32
+ *             accumulation; fp8/MXFP4 MFMA products, which are exact, with
+ *             fp32 accumulation).  bf16 outputs are rounded to nearest even.
+ *             No fast-math reassociation of reductions across launches: the
+ *             same inputs give bit-identical outputs on every run.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define CSA_OK               0
+#define CSA_ERR_INVALID_ARG (-1)  /* null pointer, bad size, bad position, misalignment */
+#define CSA_ERR_UNSUPPORTED (-2)  /* valid request this build does not implement       */
+#define CSA_ERR_HIP         (-3)  /* a HIP call failed; the message holds its string    */
+#define CSA_ERR_WORKSPACE   (-4)  /* workspace missing or smaller than required         */
+
+/* ---- element types ---- */
+#define CSA_F32       0  /* IEEE float32                                               */
+#define CSA_BF16      1  /* bfloat16                                                   */
+#define CSA_FP8_E4M3  2  /* OCP E4M3 (FN) byte codes, with one fp32 scale per 128-row */
+#define CSA_MXFP4     3  /* OCP MX v1.0: E2M1 pairs per byte (even element in the low
+                            nibble), one E8M0 scale byte per 32 elements               */
+
+/* ---- operation ids for csa_workspace_bytes ---- */
+#define CSA_OP_COMPRESS     0
+#define CSA_OP_INDEX        1
+#define CSA_OP_TOPK         2
+#define CSA_OP_SPARSE_ATTN  3
+#define CSA_OP_HCA_ATTN     4
+
+/* Supported head shapes (the pages' configuration). */
+#define CSA_HEADS        64   /* attention query heads                    */
+#define CSA_HEAD_DIM    512   /* attention head dim = shared latent width */
+#define CSA_INDEX_HEADS  64   /* indexer heads                            */
+#define CSA_INDEX_DIM   128   /* indexer head dim                         */
+#define CSA_MAX_TOPK   2048
+
+/*
+ * csa_compress -- stage 1, the KV compressor.
+ *
+ * Defined in "DeepSeek V4 结构速览" (核心设计; C4A Compressor) and the
+ * compression formula of "DeepSeek-V4技术报告解读，全适配国产算力" (2.1):
+ *  ratio 4 (C4A):   entry i pools 8 raw tokens -- the current block
+ *                   4i..4i+3 (contents Ca, weight logits Za, bias rows 0..3)
+ *                   and the previous block 4i-4..4i-1 (Cb, Zb, bias rows
+ *                   4..7).  Per channel, p = softmax over the 8 rows of
+ *                   (Z + bias); y = sum_r p[r] * C[r].  For the first block of
+ *                   a sequence the previous block has zero content and
+ *                   logit -inf.
+ *  ratio 128 (C128A): entry i pools raw tokens 128i..128i+127 (Ca, Za, bias
+ *                   rows 0..127) the same way.
+ *  Then RMSNorm: out = y * rsqrt(mean_c(y^2) + eps) * gamma.
+ *
+ * The call pools the raw tokens pos0 .. pos0+n_tok-1 of each sequence;
+ * pos0 must be a multiple of ratio.  It writes n_tok/ratio entries per
+ * sequence (a trailing partial block produces nothing).
+ *
+ *  Ca, Za          [B, n_tok, c] in_dtype
+ *  Cb, Zb          [B, n_tok, c] in_dtype; ratio 4 only, NULL for ratio 128
+ *  prev_Cb/_Zb     [B, 4, c] in_dtype: raw tokens pos0-4..pos0-1 (the block
+ *                  before the chunk).  Required iff ratio == 4 and pos0 > 0,
+ *                  otherwise NULL.
+ *  bias            [8, c] (ratio 4) or [128, c] (ratio 128) float32
+ *  gamma           [c] float32, or NULL for ones
+ *  eps             > 0 (finite)
+ *  in_dtype        CSA_F32 or CSA_BF16;  out_dtype CSA_F32 or CSA_BF16
+ *  out             entry i of sequence b at out + b*out_batch_stride + i*c
+ *                  (elements); out_batch_stride 0 means (n_tok/ratio)*c.
+ *                  This lets a decode step write straight into a cache slot.
+ *  c               a multiple of 64, at most 1024.
+ */
+int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
+                 const void* Ca, const void* Za, const void* Cb, const void* Zb,
+                 const void* prev_Cb, const void* prev_Zb,
+                 const float* bias, const float* gamma, float eps,
+                 int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
+                 void* stream);
+
+/*
+ * lightning_index -- stage 2, the lightning indexer.
+ *
+ * Defined in "DeepSeek Technical Reports" (DSA, the indexer equation):
+ *   I[t,s] = sum_{j<H_I} w[t,j] * ReLU(q[t,j] . k[s])   -- no scale factor.
+ * "DeepSeek V4 结构速览" (Lightning Indexer): low-precision QK, ReLU, the
+ * head-weighted sum, BF16 scores, causal range.  Scores of entries
+ * s >= V_ratio(t) are written as -inf.
+ *
+ *  q        qk_dtype F32/BF16: [B, T, H_I, d_I];  FP8_E4M3: [B, T, H_I, d_I]
+ *           codes;  MXFP4: [B, T, H_I, d_I/2] packed bytes
+ *  q_scale  FP8_E4M3: [B, T, H_I] float32 (> 0);  MXFP4: [B, T, H_I, d_I/32]
+ *           E8M0 bytes;  NULL otherwise
+ *  w        [B, T, H_I] float32
+ *  k        [B, N, d_I] (same encodings as q);  k_scale FP8: [B, N] float32,
+ *           MXFP4: [B, N, d_I/32] bytes, NULL otherwise
+ *  scores   [B, T, N] score_dtype (CSA_F32 or CSA_BF16)
+ *  Requires H_I = 64, d_I = 128, ratio in {4, 128}, N >= V_ratio(q_pos0+T-1).
+ *  qk_dtype CSA_F32 needs score_dtype CSA_F32.
+ */
+int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                    int H_I, int d_I,
+                    const void* q, const void* q_scale, const float* w,
+                    const void* k, const void* k_scale, int qk_dtype,
+                    void* scores, int score_dtype, void* stream);
+
+/*
+ * topk_select -- stage 3, the causal Top-k selector.
+ *
+ * "DeepSeek Technical Reports" (DSA, the Top-k attention equation) and
+ * "DeepSeek V4 结构速览" (核心设计; Lightning Indexer): each query row keeps
+ * the k entries with the highest stored score among s < V_ratio(t).  Equal
+ * scores go to the lower index; -0.0 equals +0.0.  When fewer than k entries
+ * are visible all are kept.  Output row: the selected indices in ascending
+ * order, then -1 in the remaining slots.  NaN scores are not supported.
+ *
+ *  scores  [B, T, N] score_dtype (CSA_F32 or CSA_BF16)
+ *  idx     [B, T, k] int32
+ *  workspace / ws_bytes: at least csa_workspace_bytes(CSA_OP_TOPK, B, T, N, k)
+ *  bytes (may be 0, then workspace may be NULL).
+ */
+int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k,
+                const void* scores, int score_dtype, int32_t* idx,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_mqa_attn -- stage 4, shared-KV MQA over Top-k entries + window.
+ *
+ * "DeepSeek V4 结构速览" (CSA（c4a 路线）) and "DeepSeek-V4 技术解读：百万
+ * Token 上下文的新里程碑" (2.1): H query heads share one d-dim latent that is
+ * both key and value.  Query t attends over the concatenation (no
+ * de-duplication) of kv_cmp rows idx[t, :] and the raw window rows
+ * max(0, t-window+1) .. t:
+ *   o[t,h] = sum_x softmax_x(scale * q[t,h] . x) * x.
+ * idx slots outside [0, N) (e.g. the -1 padding) contribute nothing.
+ *
+ *  q       [B, T, H, d] io_dtype;   kv_cmp [B, N, d] io_dtype
+ *  idx     [B, T, k] int32
+ *  kv_raw  [B, n_raw, d] io_dtype, raw positions raw_pos0 .. raw_pos0+n_raw-1;
+ *          must cover every query's window.
+ *  out     [B, T, H, d] io_dtype;  lse [B, T, H] float32 natural-log
+ *          softmax denominators, or NULL.
+ *  io_dtype CSA_F32 or CSA_BF16;  H = 64, d = 512, 1 <= window <= 4096.
+ *  workspace: at least csa_workspace_bytes(CSA_OP_SPARSE_ATTN, B, T, N, k).
+ */
+int sparse_mqa_attn(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d,
+                    const void* q, const void* kv_cmp, const int32_t* idx,
+                    const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+                    float scale, int io_dtype, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attn -- stage 5, HCA: dense shared-KV MQA with an attention sink.
+ *
+ * "DeepSeek V4 结构速览" (HCA（c128a 路线）): no indexer; every query attends
+ * over all visible compressed entries s < V_ratio(t) and its raw window, with
+ * an attention sink.  The sink is one logit sink[h] per head (not scaled)
+ * with a zero value vector:
+ *   o[t,h] = sum_x e^{l_x} x / (e^{sink[h]} + sum_x e^{l_x}),
+ *   l_x = scale * q[t,h] . x.
+ * sink == NULL means no sink (plain dense attention; with ratio 4 this is the
+ * dense counterpart of sparse_mqa_attn).  lse includes the sink term.
+ *
+ *  q [B, T, H, d], kv_cmp [B, N, d], kv_raw [B, n_raw, d] io_dtype;
+ *  sink [H] float32 or NULL;  out [B, T, H, d];  lse [B, T, H] or NULL.
+ *  Requires N >= V_ratio(q_pos0+T-1).
+ *  workspace: at least csa_workspace_bytes(CSA_OP_HCA_ATTN, B, T, N, 0).
+ */
+int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
+             const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
+             int64_t n_raw, int window, float scale, const float* sink,
+             int io_dtype, void* out, float* lse,
+             void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the named operation needs for these sizes (0 if none).
+ * For the two attention operations the need depends only on B and T; N and
+ * k are accepted for symmetry.  Returns 0 for an unknown op. */
+size_t csa_workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int k);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* csa_last_error(void);
+
+/* Library version string. */
+const char* csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,194 @@
+"""Python binding of libcsa.so, the gfx950 compressed sparse attention library.
+
+Argument marshalling only: every function checks that its tensors are
+contiguous device tensors, passes their pointers and torch's current HIP
+stream to the C ABI (include/csa.h), and raises on a non-zero status.  All of
+the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and streams, nothing else.
+
+The library is loaded from this package's directory; if it is missing the
+import of any entry point raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
+           "workspace_bytes", "library", "F32", "BF16", "FP8_E4M3", "MXFP4", "CsaError"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa.so")
+
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+OP_COMPRESS, OP_INDEX, OP_TOPK, OP_SPARSE_ATTN, OP_HCA_ATTN = 0, 1, 2, 3, 4
+
+_i64, _int, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "csa_compress": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
+                     _int, _int, _vp, _i64, _vp],
+    "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
+                        _vp, _int, _vp],
+    "topk_select": [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
+    "sparse_mqa_attn": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _i64, _i64,
+                        _int, _f32, _int, _vp, _vp, _vp, _sz, _vp],
+    "hca_attn": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
+                 _vp, _int, _vp, _vp, _vp, _sz, _vp],
+}
+
+_lib = None
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def library() -> ctypes.CDLL:
+    """Load libcsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CsaError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_sparse_compress_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
+        lib.csa_workspace_bytes.restype = ctypes.c_size_t
+        lib.csa_last_error.restype = ctypes.c_char_p
+        lib.csa_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        msg = library().csa_last_error().decode()
+        raise CsaError(f"{name} failed with status {status}: {msg}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_bytes(op: int, B: int, T: int, N: int, k: int) -> int:
+    return int(library().csa_workspace_bytes(op, B, T, N, k))
+
+
+def _workspace(op, B, T, N, k, device, workspace):
+    need = workspace_bytes(op, B, T, N, k)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
+                 gamma=None, eps=1e-6, out=None, out_dtype=None, out_batch_stride=0, stream=None):
+    """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c]."""
+    B, n_tok, c = Ca.shape
+    in_dt = _dt(Ca)
+    if out is None:
+        odt = Ca.dtype if out_dtype is None else out_dtype
+        out = torch.empty(B, n_tok // ratio, c, dtype=odt, device=Ca.device)
+    if out_batch_stride == 0 and out.numel() < B * (n_tok // ratio) * c:
+        raise ValueError("out is too small")
+    st = library().csa_compress(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
+                                _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
+                                _dt(out), _ptr(out), out_batch_stride, _stream(stream))
+    _check(st, "csa_compress")
+    return out
+
+
+def lightning_index(q, w, k, *, q_pos0, ratio=4, qk_dtype=None, q_scale=None, k_scale=None,
+                    score_dtype=torch.bfloat16, scores=None, N=None, stream=None):
+    """Stage 2.  q: [B, T, 64, 128] (or uint8 encodings), w: [B, T, 64], k: [B, N, ...]."""
+    B, T = q.shape[:2]
+    N = k.shape[1] if N is None else N
+    if qk_dtype is None:
+        qk_dtype = _dt(q)
+    if scores is None:
+        scores = torch.empty(B, T, N, dtype=score_dtype, device=q.device)
+    st = library().lightning_index(B, T, N, q_pos0, ratio, 64, 128, _ptr(q), _ptr(q_scale), _ptr(w),
+                                   _ptr(k), _ptr(k_scale), qk_dtype, _ptr(scores), _dt(scores),
+                                   _stream(stream))
+    _check(st, "lightning_index")
+    return scores
+
+
+def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=None):
+    """Stage 3.  scores: [B, T, N]; returns idx [B, T, k] int32 (ascending, then -1)."""
+    B, T, N = scores.shape
+    if idx is None:
+        idx = torch.empty(B, T, k, dtype=torch.int32, device=scores.device)
+    ws, wsb = _workspace(OP_TOPK, B, T, N, k, scores.device, workspace)
+    st = library().topk_select(B, T, N, q_pos0, ratio, k, _ptr(scores), _dt(scores), _ptr(idx),
+                               _ptr(ws), wsb, _stream(stream))
+    _check(st, "topk_select")
+    return idx
+
+
+def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, scale=None,
+                    out=None, lse=None, return_lse=False, workspace=None, stream=None):
+    """Stage 4.  q: [B, T, 64, 512], kv_cmp: [B, N, 512], idx: [B, T, k], kv_raw: [B, n_raw, 512]."""
+    B, T, H, d = q.shape
+    N = kv_cmp.shape[1]
+    k = idx.shape[2]
+    n_raw = kv_raw.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(OP_SPARSE_ATTN, B, T, N, k, q.device, workspace)
+    st = library().sparse_mqa_attn(B, T, N, k, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(idx),
+                                   _ptr(kv_raw), raw_pos0, n_raw, window, scale, _dt(q), _ptr(out),
+                                   _ptr(lse), _ptr(ws), wsb, _stream(stream))
+    _check(st, "sparse_mqa_attn")
+    return (out, lse) if return_lse else out
+
+
+def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, window=128, scale=None,
+             out=None, lse=None, return_lse=False, workspace=None, stream=None):
+    """Stage 5.  Dense MQA over all visible entries and the window, optional sink [64]."""
+    B, T, H, d = q.shape
+    N = kv_cmp.shape[1]
+    n_raw = kv_raw.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(OP_HCA_ATTN, B, T, N, 0, q.device, workspace)
+    st = library().hca_attn(B, T, N, ratio, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(kv_raw),
+                            raw_pos0, n_raw, window, scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse),
+                            _ptr(ws), wsb, _stream(stream))
+    _check(st, "hca_attn")
+    return (out, lse) if return_lse else out

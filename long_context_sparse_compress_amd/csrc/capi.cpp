@@ -1,0 +1,97 @@
+// The extern "C" entry points declared in include/csa.h: validate on the
+// host (validate.h), then hand the arguments to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/csa.h"
+#include "launch.h"
+#include "validate.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int finish(const csa::Check& c) {
+  g_last_error = c.msg;
+  return c.code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_last_error.clear();
+    return CSA_OK;
+  }
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return CSA_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
+                 const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
+                 const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
+                 int out_dtype, void* out, int64_t out_batch_stride, void* stream) {
+  csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
+                                      gamma, eps, in_dtype, out_dtype, out, out_batch_stride);
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs a{ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb,
+                      bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride};
+  return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
+}
+
+int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int H_I, int d_I,
+                    const void* q, const void* q_scale, const float* w, const void* k,
+                    const void* k_scale, int qk_dtype, void* scores, int score_dtype, void* stream) {
+  csa::Check ck = csa::check_index(B, T, N, q_pos0, ratio, H_I, d_I, q, q_scale, w, k, k_scale, qk_dtype,
+                                   scores, score_dtype);
+  if (!ck.ok()) return finish(ck);
+  csa::IndexArgs a{B, T, N, q_pos0, ratio, q, q_scale, w, k, k_scale, qk_dtype, scores, score_dtype};
+  return hip_status(csa::launch_index(a, as_stream(stream)), "lightning_index launch");
+}
+
+int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const void* scores,
+                int score_dtype, int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_topk(B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  csa::TopkArgs a{B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace};
+  return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select launch");
+}
+
+int sparse_mqa_attn(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,
+                    const void* kv_cmp, const int32_t* idx, const void* kv_raw, int64_t raw_pos0,
+                    int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_sparse(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw,
+                                    window, scale, io_dtype, out, lse, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  csa::AttnArgs a{B, T, N, k, 4, q_pos0, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
+                  nullptr, io_dtype, out, lse, workspace};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn launch");
+}
+
+int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
+             const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+             float scale, const float* sink, int io_dtype, void* out, float* lse, void* workspace,
+             size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_hca(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window,
+                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  csa::AttnArgs a{B, T, N, 0, ratio, q_pos0, q, kv_cmp, nullptr, kv_raw, raw_pos0, n_raw, window, scale,
+                  sink, io_dtype, out, lse, workspace};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn launch");
+}
+
+size_t csa_workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int k) {
+  return csa::workspace_bytes(op, B, T, N, k);
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+const char* csa_version(void) { return "csa-gfx950 0.1"; }
+
+}  // extern "C"

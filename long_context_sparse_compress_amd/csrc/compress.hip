@@ -1,0 +1,251 @@
+// Stage 1: the C4A / C128A KV compressor on gfx950.
+//
+// "DeepSeek V4 结构速览" (核心设计; C4A Compressor) and the compression
+// formula of "DeepSeek-V4技术报告解读，全适配国产算力" (2.1): each entry is a
+// per-channel softmax-weighted sum of 8 raw tokens at stride 4 (C4A: the
+// current block from Ca/Za, the previous block from Cb/Zb, a positional bias
+// on the 8 logits) or 128 raw tokens at stride 128 (C128A), then RMSNorm.
+//
+// The work is pure streaming (C128A reads 257 rows' worth of bytes per
+// entry), so the kernel is organised for HBM bandwidth:
+//  * one workgroup per (sequence, entry); each thread owns VEC consecutive
+//    channels and loads 16 bytes per row per tensor (fully coalesced rows);
+//  * the window rows are split across G row groups that each keep an online
+//    softmax state (running max, running sum, running weighted content) per
+//    channel in registers, so every input byte is read exactly once;
+//  * the G partial states are merged through LDS, then RMSNorm is a
+//    block-wide reduction over channels.
+#include "device.h"
+#include "launch.h"
+
+namespace csa {
+namespace {
+
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int n = 4; };
+template <> struct Vec<uint16_t> { static constexpr int n = 8; };
+
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, float* f);
+template <>
+__device__ __forceinline__ void load_vec<float>(const float* p, float* f) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load_vec<uint16_t>(const uint16_t* p, float* f) {
+  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), f);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vec(T* p, const float* f);
+template <>
+__device__ __forceinline__ void store_vec<float>(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+template <>
+__device__ __forceinline__ void store_vec<uint16_t>(uint16_t* p, const float* f) {
+  uint4 v;
+  v.x = pack_bf16x2(f[0], f[1]);
+  v.y = pack_bf16x2(f[2], f[3]);
+  v.z = pack_bf16x2(f[4], f[5]);
+  v.w = pack_bf16x2(f[6], f[7]);
+  *reinterpret_cast<uint4*>(p) = v;
+}
+// 8 channels per thread on the bf16 path but 4 on the fp32 output path is
+// never mixed: VEC follows the input type and the output writes VEC values.
+template <typename TO, int VEC>
+__device__ __forceinline__ void store_out(TO* p, const float* f) {
+  if constexpr (sizeof(TO) == 4) {
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) store_vec<float>(reinterpret_cast<float*>(p) + i, f + i);
+  } else {
+    if constexpr (VEC == 8) {
+      store_vec<uint16_t>(reinterpret_cast<uint16_t*>(p), f);
+    } else {
+      uint2 v;
+      v.x = pack_bf16x2(f[0], f[1]);
+      v.y = pack_bf16x2(f[2], f[3]);
+      *reinterpret_cast<uint2*>(p) = v;
+    }
+  }
+}
+
+struct Online {
+  float m, s, y;
+};
+
+__device__ __forceinline__ void online_push(Online& st, float l, float x) {
+  const float mn = fmaxf(st.m, l);
+  const float a = fast_exp2((st.m - mn) * kLog2e);   // st.m = -inf -> 0
+  const float b = fast_exp2((l - mn) * kLog2e);
+  st.s = st.s * a + b;
+  st.y = st.y * a + b * x;
+  st.m = mn;
+}
+
+__device__ __forceinline__ void online_merge(Online& st, const Online& o) {
+  if (o.m == -INFINITY) return;
+  const float mn = fmaxf(st.m, o.m);
+  const float a = fast_exp2((st.m - mn) * kLog2e);
+  const float b = fast_exp2((o.m - mn) * kLog2e);
+  st.s = st.s * a + o.s * b;
+  st.y = st.y * a + o.y * b;
+  st.m = mn;
+}
+
+// One workgroup per (entry i, sequence b).  blockDim.x = CT * G with
+// CT = c / VEC channel threads and G row groups.
+template <typename TI, typename TO, int RATIO>
+__global__ void __launch_bounds__(256)
+compress_kernel(int64_t n_tok, int c, int64_t pos0,
+                const TI* __restrict__ Ca, const TI* __restrict__ Za,
+                const TI* __restrict__ Cb, const TI* __restrict__ Zb,
+                const TI* __restrict__ pCb, const TI* __restrict__ pZb,
+                const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
+                TO* __restrict__ out, int64_t out_stride, int G) {
+  constexpr int VEC = Vec<TI>::n;
+  constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
+  const int CT = c / VEC;
+  const int tid = threadIdx.x;
+  const int ct = tid % CT;
+  const int g = tid / CT;
+  const int64_t i = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int ch0 = ct * VEC;
+
+  Online st[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) st[v] = Online{-INFINITY, 0.f, 0.f};
+
+  const int64_t seq = b * n_tok * c;
+  // Rows handled by this group: r = g, g + G, ...  Loads of up to UNR rows are
+  // issued before any of them is consumed.
+  constexpr int UNR = 4;
+  for (int r0 = g; r0 < ROWS; r0 += G * UNR) {
+    float zl[UNR][VEC], xl[UNR][VEC];
+    bool have[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * G;
+      have[u] = false;
+      if (r >= ROWS) continue;
+      const TI* zp = nullptr;
+      const TI* xp = nullptr;
+      if (RATIO == 128 || r < 4) {
+        const int64_t tok = i * RATIO + r;
+        zp = Za + seq + tok * c + ch0;
+        xp = Ca + seq + tok * c + ch0;
+      } else if (i > 0) {
+        const int64_t tok = i * 4 - 4 + (r - 4);
+        zp = Zb + seq + tok * c + ch0;
+        xp = Cb + seq + tok * c + ch0;
+      } else if (pos0 > 0) {
+        const int64_t off = (b * 4 + (r - 4)) * c + ch0;
+        zp = pZb + off;
+        xp = pCb + off;
+      }
+      if (zp) {
+        load_vec<TI>(zp, zl[u]);
+        load_vec<TI>(xp, xl[u]);
+        have[u] = true;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (!have[u]) continue;
+      const int r = r0 + u * G;
+      const float* br = bias + static_cast<int64_t>(r) * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) online_push(st[v], zl[u][v] + br[v], xl[u][v]);
+    }
+  }
+
+  // Merge the G row groups' states through LDS (group 0 keeps the result).
+  extern __shared__ float smem[];
+  if (G > 1) {
+    float* sm = smem;                 // [G-1][3][c]
+    if (g > 0) {
+      float* base = sm + static_cast<int64_t>(g - 1) * 3 * c;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        base[ch0 + v] = st[v].m;
+        base[c + ch0 + v] = st[v].s;
+        base[2 * c + ch0 + v] = st[v].y;
+      }
+    }
+    __syncthreads();
+    if (g == 0) {
+      for (int gg = 1; gg < G; ++gg) {
+        const float* base = sm + static_cast<int64_t>(gg - 1) * 3 * c;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+          online_merge(st[v], Online{base[ch0 + v], base[c + ch0 + v], base[2 * c + ch0 + v]});
+      }
+    }
+    __syncthreads();
+  }
+
+  // RMSNorm over the c channels (group 0 threads hold them all).
+  float y[VEC];
+  float ss = 0.f;
+  if (g == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      y[v] = st[v].y / st[v].s;
+      ss += y[v] * y[v];
+    }
+  }
+  ss = wave_sum(g == 0 ? ss : 0.f);
+  float* red = smem;
+  const int wid = tid / 64;
+  const int nw = (blockDim.x + 63) / 64;
+  if ((tid & 63) == 0) red[wid] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < nw; ++w) tot += red[w];
+  if (g != 0) return;
+  const float inv = rsqrtf(tot / static_cast<float>(c) + eps);
+  float o[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * (gamma ? gamma[ch0 + v] : 1.f);
+  store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
+}
+
+template <typename TI, typename TO, int RATIO>
+hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
+  constexpr int VEC = Vec<TI>::n;
+  constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
+  const int CT = static_cast<int>(a.c / VEC);
+  int G = 256 / CT;
+  if (G < 1) G = 1;
+  if (G > ROWS) G = ROWS;
+  const int threads = CT * G;
+  const size_t smem = (G > 1 ? static_cast<size_t>(G - 1) * 3 * a.c : 0) * sizeof(float) + 64;
+  const int64_t n_ent = a.n_tok / RATIO;
+  dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B));
+  const int64_t stride = a.out_batch_stride ? a.out_batch_stride : n_ent * a.c;
+  hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO>), grid, dim3(threads), smem, s, a.n_tok,
+                     static_cast<int>(a.c), a.pos0, static_cast<const TI*>(a.Ca),
+                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.Cb),
+                     static_cast<const TI*>(a.Zb), static_cast<const TI*>(a.prev_Cb),
+                     static_cast<const TI*>(a.prev_Zb), a.bias, a.gamma, a.eps,
+                     static_cast<TO*>(a.out), stride, G);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+hipError_t launch_r(const CompressArgs& a, hipStream_t s) {
+  return a.ratio == 4 ? launch_t<TI, TO, 4>(a, s) : launch_t<TI, TO, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.n_tok / a.ratio == 0) return hipSuccess;
+  if (a.in_dtype == CSA_F32)
+    return a.out_dtype == CSA_F32 ? launch_r<float, float>(a, s) : launch_r<float, uint16_t>(a, s);
+  return a.out_dtype == CSA_F32 ? launch_r<uint16_t, float>(a, s) : launch_r<uint16_t, uint16_t>(a, s);
+}
+
+}  // namespace csa

@@ -1,0 +1,73 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, vector
+// types, MFMA operand types and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Unpack 8 bf16 held in a uint4 into floats.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return exp2f(x); }
+
+// Sum / max over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Round-robin workgroup dispatch puts consecutive workgroup ids on different
+// XCDs (8 on MI355X).  Remap a linear id so that ids [x*per, (x+1)*per) run on
+// XCD x, keeping neighbouring tiles (and their shared data) in one L2.
+__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t id, uint32_t n) {
+  constexpr uint32_t kXcd = 8;
+  if (n % kXcd != 0) return id;
+  const uint32_t per = n / kXcd;
+  return (id % kXcd) * per + id / kXcd;
+}
+
+}  // namespace csa

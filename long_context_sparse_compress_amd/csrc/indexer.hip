@@ -1,0 +1,282 @@
+// Stage 2: the lightning indexer on gfx950.
+//
+// "DeepSeek Technical Reports" (DSA, the indexer equation):
+//   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]),  64 heads of 128 dims.
+// "DeepSeek V4 结构速览" (Lightning Indexer): low-precision QK, ReLU, the
+// head-weighted sum, scores stored as BF16, only the causal range s < V(t).
+//
+// The QK product is a GEMM with the 64 heads of one query as M, entries as N
+// and d_I = 128 as K, so it runs on MFMA:
+//   bf16   v_mfma_f32_16x16x32_bf16           (4 k-steps for K = 128)
+//   fp8    v_mfma_scale_f32_16x16x128_f8f6f4  (E4M3, unit block scale; the
+//          per-row fp32 scales are applied in the epilogue)
+//   MXFP4  v_mfma_scale_f32_16x16x128_f8f6f4  (E2M1 with the E8M0 block
+//          scales fed to the instruction)
+// One 16-entry tile per MFMA column block; a wave owns QPW queries (their q
+// fragments stay in registers) and streams TPW tiles of keys straight from
+// HBM into registers (each lane reads one contiguous run of a key row).  The
+// epilogue -- ReLU, multiply by w, sum over the 64 heads -- is fused: a lane
+// reduces its 16 head values, two cross-lane steps finish the sum, and the
+// scores of four tiles leave as one 128-byte store per query.
+//
+// Because K is contracted, the order of K inside a lane's fragment is free as
+// long as q and k use the same order: every lane loads the same contiguous
+// byte range of its q row and of its key row.
+#include "device.h"
+#include "launch.h"
+
+namespace csa {
+namespace {
+
+constexpr int kH = 64;    // indexer heads
+constexpr int kD = 128;   // indexer dim
+
+// ---------------------------------------------------------------- fp32 path
+// Plain fp32 arithmetic for fp32 inputs (small problems): one workgroup per
+// (64-entry block, query, sequence); q[t] and w[t] are staged in LDS.
+__global__ void __launch_bounds__(256)
+index_f32_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const float* __restrict__ q,
+                 const float* __restrict__ w, const float* __restrict__ k, float* __restrict__ scores) {
+  __shared__ float qs[kH * kD];
+  __shared__ float ws[kH];
+  __shared__ float part[4][64];
+  const int64_t t = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const float* qt = q + (b * T + t) * kH * kD;
+  for (int i = tid; i < kH * kD; i += 256) qs[i] = qt[i];
+  if (tid < kH) ws[tid] = w[(b * T + t) * kH + tid];
+  __syncthreads();
+  const int el = tid % 64, hq = tid / 64;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + el;
+  int64_t vis = (q_pos0 + t + 1) / ratio;
+  if (vis > N) vis = N;
+  float acc = 0.f;
+  if (e < vis) {
+    const float* kr = k + (b * N + e) * kD;
+    for (int h = hq * 16; h < hq * 16 + 16; ++h) {
+      float dot = 0.f;
+      for (int d = 0; d < kD; ++d) dot = fmaf(qs[h * kD + d], kr[d], dot);
+      acc = fmaf(ws[h], fmaxf(dot, 0.f), acc);
+    }
+  }
+  part[hq][el] = acc;
+  __syncthreads();
+  if (hq == 0 && e < N) {
+    const float s = (part[0][el] + part[1][el]) + (part[2][el] + part[3][el]);
+    scores[(b * T + t) * N + e] = (e < vis) ? s : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- MFMA path
+template <int QK> struct Frag;
+
+// bf16: rows of 256 B; lane (r, g) holds bytes [64g, 64g+64) = 4 k-steps of 8.
+template <> struct Frag<CSA_BF16> {
+  static constexpr int kRowBytes = 256;
+  static constexpr int kRegs = 4;  // uint4 per lane per 16-row tile
+  uint4 v[kRegs];
+  __device__ __forceinline__ void load(const uint8_t* row, int g) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + 64 * g);
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) v[i] = p[i];
+  }
+};
+// fp8: rows of 128 B; lane (r, g) holds bytes [32g, 32g+32).
+template <> struct Frag<CSA_FP8_E4M3> {
+  static constexpr int kRowBytes = 128;
+  static constexpr int kRegs = 2;
+  uint4 v[kRegs];
+  __device__ __forceinline__ void load(const uint8_t* row, int g) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + 32 * g);
+    v[0] = p[0];
+    v[1] = p[1];
+  }
+};
+// MXFP4: rows of 64 B + 4 scale bytes; lane (r, g) holds bytes [16g, 16g+16)
+// (the 32 elements of MX block g) and block g's scale.
+template <> struct Frag<CSA_MXFP4> {
+  static constexpr int kRowBytes = 64;
+  static constexpr int kRegs = 1;
+  uint4 v[kRegs];
+  __device__ __forceinline__ void load(const uint8_t* row, int g) {
+    v[0] = *reinterpret_cast<const uint4*>(row + 16 * g);
+  }
+};
+
+template <int QK>
+__device__ __forceinline__ f32x4 qk_tile(const Frag<QK>& a, const Frag<QK>& b, int sa, int sb) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (QK == CSA_BF16) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.v[s]), as_bf16x8(b.v[s]), acc, 0, 0, 0);
+  } else if constexpr (QK == CSA_FP8_E4M3) {
+    const i32x8 av = {(int)a.v[0].x, (int)a.v[0].y, (int)a.v[0].z, (int)a.v[0].w,
+                      (int)a.v[1].x, (int)a.v[1].y, (int)a.v[1].z, (int)a.v[1].w};
+    const i32x8 bv = {(int)b.v[0].x, (int)b.v[0].y, (int)b.v[0].z, (int)b.v[0].w,
+                      (int)b.v[1].x, (int)b.v[1].y, (int)b.v[1].z, (int)b.v[1].w};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+  } else {
+    const i32x8 av = {(int)a.v[0].x, (int)a.v[0].y, (int)a.v[0].z, (int)a.v[0].w, 0, 0, 0, 0};
+    const i32x8 bv = {(int)b.v[0].x, (int)b.v[0].y, (int)b.v[0].z, (int)b.v[0].w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, sa, 0, sb);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void store_score(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_score(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// Grid: x = entry block of 4 * TPW * 16 entries (one TPW-tile run per wave),
+// y = block of QPW queries, z = sequence.  256 threads = 4 waves.
+template <int QK, int QPW, int TPW, typename TS>
+__global__ void __launch_bounds__(256)
+index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                  const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
+                  const float* __restrict__ w, const uint8_t* __restrict__ k,
+                  const void* __restrict__ k_scale, TS* __restrict__ scores) {
+  static_assert(TPW % 4 == 0, "tiles are stored four at a time");
+  using F = Frag<QK>;
+  constexpr int RB = F::kRowBytes;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int col = lane & 15;   // row of a 16-row operand tile / column of the output tile
+  const int g = lane >> 4;     // lane group: K sub-range, and output rows 4g..4g+3
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * QPW;
+  const int64_t e_wave = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * (TPW * 16);
+  if (e_wave >= N) return;
+
+  // q fragments and head weights of this wave's queries.
+  F qa[QPW][4];
+  int qsc[QPW][4];
+  float wv[QPW][4][4];
+  int64_t vis[QPW];
+  int64_t vis_max = 0;
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    int64_t v = (q_pos0 + t + 1) / ratio;
+    if (v > N) v = N;
+    vis[qi] = (t0 + qi < T) ? v : 0;
+    vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
+    const int64_t qrow = (b * T + t) * kH;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      qa[qi][mt].load(q + (qrow + mt * 16 + col) * RB, g);
+      if constexpr (QK == CSA_MXFP4)
+        qsc[qi][mt] = static_cast<const uint8_t*>(q_scale)[(qrow + mt * 16 + col) * 4 + g];
+      else
+        qsc[qi][mt] = 127;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = mt * 16 + 4 * g + i;
+        float wt = w[qrow + h];
+        if constexpr (QK == CSA_FP8_E4M3) wt *= static_cast<const float*>(q_scale)[qrow + h];
+        wv[qi][mt][i] = wt;
+      }
+    }
+  }
+
+  const int64_t krow0 = b * N;
+  for (int tg = 0; tg < TPW / 4; ++tg) {
+    const int64_t eg = e_wave + tg * 64;
+    if (eg >= N) break;
+    float keep[QPW];
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) keep[qi] = -INFINITY;
+    F kb[4];
+    int ksc[4];
+    float kscale[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      int64_t e = eg + tt * 16 + col;
+      if (e >= N) e = N - 1;
+      kb[tt].load(k + (krow0 + e) * RB, g);
+      if constexpr (QK == CSA_MXFP4) ksc[tt] = static_cast<const uint8_t*>(k_scale)[(krow0 + e) * 4 + g];
+      else ksc[tt] = 127;
+      if constexpr (QK == CSA_FP8_E4M3) kscale[tt] = static_cast<const float*>(k_scale)[krow0 + e];
+      else kscale[tt] = 1.f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int64_t et = eg + tt * 16;
+      const int64_t e = et + col;
+      if (et >= vis_max) continue;   // whole tile masked for every query (wave-uniform)
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 c = qk_tile<QK>(qa[qi][mt], kb[tt], qsc[qi][mt], ksc[tt]);
+          part = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), part);
+          part = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), part);
+          part = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), part);
+          part = fmaf(wv[qi][mt][3], fmaxf(c[3], 0.f), part);
+        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        part *= kscale[tt];
+        if (e >= vis[qi]) part = -INFINITY;
+        if (tt == g) keep[qi] = part;
+      }
+    }
+    const int64_t e = eg + g * 16 + col;
+    if (e < N) {
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, keep[qi]);
+      }
+    }
+  }
+}
+
+template <int QK, int QPW, int TPW>
+hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
+  const int64_t per_wg = 4 * TPW * 16;
+  dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
+            static_cast<uint32_t>((a.T + QPW - 1) / QPW), static_cast<uint32_t>(a.B));
+  const auto* q = static_cast<const uint8_t*>(a.q);
+  const auto* k = static_cast<const uint8_t*>(a.k);
+  if (a.score_dtype == CSA_BF16)
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
+                       static_cast<uint16_t*>(a.scores));
+  else
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, float>), grid, dim3(256), 0, s, a.T, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
+                       static_cast<float*>(a.scores));
+  return hipGetLastError();
+}
+
+template <int QK>
+hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
+  if (a.T <= 2) {   // decode: one query per wave, long entry runs
+    constexpr int TPW = (QK == CSA_MXFP4) ? 16 : (QK == CSA_FP8_E4M3 ? 8 : 4);
+    return launch_mfma<QK, 1, TPW>(a, s);
+  }
+  return launch_mfma<QK, 4, 8>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.T == 0 || a.N == 0) return hipSuccess;
+  switch (a.qk_dtype) {
+    case CSA_F32: {
+      dim3 grid(static_cast<uint32_t>((a.N + 63) / 64), static_cast<uint32_t>(a.T),
+                static_cast<uint32_t>(a.B));
+      hipLaunchKernelGGL(index_f32_kernel, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio,
+                         static_cast<const float*>(a.q), a.w, static_cast<const float*>(a.k),
+                         static_cast<float*>(a.scores));
+      return hipGetLastError();
+    }
+    case CSA_BF16: return launch_qk<CSA_BF16>(a, s);
+    case CSA_FP8_E4M3: return launch_qk<CSA_FP8_E4M3>(a, s);
+    case CSA_MXFP4: return launch_qk<CSA_MXFP4>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace csa

@@ -1,0 +1,71 @@
+// Internal launcher interface between the C ABI (capi.cpp) and the kernels.
+// Arguments arrive here already validated by validate.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+struct CompressArgs {
+  int ratio;
+  int64_t B, n_tok, c, pos0;
+  const void *Ca, *Za, *Cb, *Zb, *prev_Cb, *prev_Zb;
+  const float* bias;
+  const float* gamma;
+  float eps;
+  int in_dtype, out_dtype;
+  void* out;
+  int64_t out_batch_stride;
+};
+
+struct IndexArgs {
+  int64_t B, T, N, q_pos0;
+  int ratio;
+  const void* q;
+  const void* q_scale;
+  const float* w;
+  const void* k;
+  const void* k_scale;
+  int qk_dtype;
+  void* scores;
+  int score_dtype;
+};
+
+struct TopkArgs {
+  int64_t B, T, N, q_pos0;
+  int ratio, k;
+  const void* scores;
+  int score_dtype;
+  int32_t* idx;
+  void* ws;
+};
+
+struct AttnArgs {
+  int64_t B, T, N;
+  int k;              // top-k slots per query (sparse); 0 for dense
+  int ratio;          // dense: compressed entries visible are s < (t+1)/ratio
+  int64_t q_pos0;
+  const void* q;
+  const void* kv_cmp;
+  const int32_t* idx; // NULL for dense
+  const void* kv_raw;
+  int64_t raw_pos0, n_raw;
+  int window;
+  float scale;
+  const float* sink;  // dense only, may be NULL
+  int io_dtype;
+  void* out;
+  float* lse;
+  void* ws;
+};
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_index(const IndexArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,240 @@
+// Host-side argument validation for every entry point of csa.h.
+//
+// Plain C++ with no HIP dependency, so the same checks compile with g++ and
+// run on a machine without a GPU.  Each check returns CSA_OK or an error code
+// and fills `msg`.  The rules are the ones csa.h documents for each call.
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+constexpr int kAttnTile = 32;        // rows per attention tile
+constexpr int kMaxWindow = 4096;
+constexpr int kMaxSplits = 32;
+
+inline int64_t visible(int64_t t, int64_t ratio) { return (t + 1) / ratio; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Check {
+  int code = CSA_OK;
+  std::string msg;
+  bool fail(int c, const std::string& m) {
+    if (code == CSA_OK) { code = c; msg = m; }
+    return false;
+  }
+  bool ptr(const void* p, const char* name, bool required = true) {
+    if (!p) return required ? fail(CSA_ERR_INVALID_ARG, std::string(name) + " is NULL") : true;
+    if (!aligned16(p)) return fail(CSA_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+    return true;
+  }
+  bool must_be_null(const void* p, const char* name, const char* why) {
+    if (p) return fail(CSA_ERR_INVALID_ARG, std::string(name) + " must be NULL " + why);
+    return true;
+  }
+  bool ok() const { return code == CSA_OK; }
+};
+
+inline std::string i2s(int64_t v) { return std::to_string(v); }
+
+// Split plan of the attention kernels: how many workgroups share one query's
+// rows.  The workspace bound depends only on B*T; the split count used at run
+// time never exceeds it.
+inline int attn_max_splits(int64_t B, int64_t T) {
+  const int64_t q = B * T;
+  if (q <= 0 || q >= 256) return 1;
+  int64_t s = (1024 + q - 1) / q;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+
+inline int attn_splits(int64_t B, int64_t T, int64_t rows) {
+  int64_t s = attn_max_splits(B, T);
+  const int64_t by_rows = (rows + 4 * kAttnTile - 1) / (4 * kAttnTile);  // >= 4 tiles each
+  if (s > by_rows) s = by_rows;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+
+// Per split and query: 64 x 512 fp32 partial output + 64 running maxima + 64 sums.
+inline size_t attn_split_bytes() { return size_t(CSA_HEADS) * (CSA_HEAD_DIM + 2) * sizeof(float); }
+
+inline size_t attn_workspace_bytes(int64_t B, int64_t T) {
+  const int s = attn_max_splits(B, T);
+  if (s <= 1) return 0;
+  return size_t(B) * size_t(T) * size_t(s) * attn_split_bytes();
+}
+
+// Top-k keeps rows of up to this many candidates in LDS; longer rows use the
+// multi-pass global path, which needs a per-row histogram workspace.
+constexpr int64_t kTopkLdsMax16 = 36864;   // bf16 keys
+constexpr int64_t kTopkLdsMax32 = 18432;   // fp32 keys
+constexpr int kTopkSlices = 64;            // workgroups per row on the global path
+
+inline bool topk_row_in_lds(int64_t N, int dtype) {
+  return N <= (dtype == CSA_BF16 ? kTopkLdsMax16 : kTopkLdsMax32);
+}
+
+// Global path scratch per row: a 2048-bin histogram, per-slice counts and the
+// selection state.
+inline size_t topk_row_ws_bytes() { return (2048 + 4 * kTopkSlices + 16) * sizeof(uint32_t); }
+
+inline size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t N, int dtype) {
+  if (topk_row_in_lds(N, dtype)) return 0;
+  return size_t(B) * size_t(T) * topk_row_ws_bytes();
+}
+
+inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
+                            const void* Ca, const void* Za, const void* Cb, const void* Zb,
+                            const void* prev_Cb, const void* prev_Zb, const float* bias,
+                            const float* gamma, float eps, int in_dtype, int out_dtype,
+                            const void* out, int64_t out_batch_stride) {
+  Check k;
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (B < 0 || n_tok < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and n_tok must be >= 0"); return k; }
+  if (c <= 0 || c % 64 != 0 || c > 1024) { k.fail(CSA_ERR_INVALID_ARG, "c must be a positive multiple of 64, at most 1024, got " + i2s(c)); return k; }
+  if (pos0 < 0 || pos0 % ratio != 0) { k.fail(CSA_ERR_INVALID_ARG, "pos0 must be >= 0 and a multiple of ratio, got " + i2s(pos0)); return k; }
+  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (!(eps > 0.0f) || !std::isfinite(eps)) { k.fail(CSA_ERR_INVALID_ARG, "eps must be positive and finite"); return k; }
+  const int64_t n_ent = n_tok / ratio;
+  if (out_batch_stride != 0 && out_batch_stride < n_ent * c) { k.fail(CSA_ERR_INVALID_ARG, "out_batch_stride smaller than one sequence's output"); return k; }
+  if (out_batch_stride % 8 != 0) { k.fail(CSA_ERR_INVALID_ARG, "out_batch_stride must be a multiple of 8 elements"); return k; }
+  const bool empty = (B == 0 || n_ent == 0);
+  k.ptr(Ca, "Ca", !empty) && k.ptr(Za, "Za", !empty) && k.ptr(bias, "bias", !empty) &&
+      k.ptr(gamma, "gamma", false) && k.ptr(out, "out", !empty);
+  if (!k.ok()) return k;
+  if (ratio == 4) {
+    k.ptr(Cb, "Cb", !empty) && k.ptr(Zb, "Zb", !empty);
+    if (!k.ok()) return k;
+    if (pos0 > 0) {
+      k.ptr(prev_Cb, "prev_Cb", !empty) && k.ptr(prev_Zb, "prev_Zb", !empty);
+    } else {
+      k.must_be_null(prev_Cb, "prev_Cb", "when pos0 == 0") && k.must_be_null(prev_Zb, "prev_Zb", "when pos0 == 0");
+    }
+  } else {
+    k.must_be_null(Cb, "Cb", "for ratio 128") && k.must_be_null(Zb, "Zb", "for ratio 128") &&
+        k.must_be_null(prev_Cb, "prev_Cb", "for ratio 128") && k.must_be_null(prev_Zb, "prev_Zb", "for ratio 128");
+  }
+  return k;
+}
+
+inline Check check_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int H_I, int d_I,
+                         const void* q, const void* q_scale, const float* w, const void* kk,
+                         const void* k_scale, int qk_dtype, const void* scores, int score_dtype) {
+  Check k;
+  if (B < 0 || T < 0 || N < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T and N must be >= 0"); return k; }
+  if (q_pos0 < 0) { k.fail(CSA_ERR_INVALID_ARG, "q_pos0 must be >= 0"); return k; }
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (H_I != CSA_INDEX_HEADS || d_I != CSA_INDEX_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "indexer shape must be H_I=64, d_I=128"); return k; }
+  if (qk_dtype < CSA_F32 || qk_dtype > CSA_MXFP4) { k.fail(CSA_ERR_UNSUPPORTED, "unknown qk_dtype " + i2s(qk_dtype)); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (qk_dtype == CSA_F32 && score_dtype != CSA_F32) { k.fail(CSA_ERR_UNSUPPORTED, "fp32 QK needs fp32 scores"); return k; }
+  if (T > 0 && N < visible(q_pos0 + T - 1, ratio)) { k.fail(CSA_ERR_INVALID_ARG, "N = " + i2s(N) + " is smaller than the entries visible to the last query (" + i2s(visible(q_pos0 + T - 1, ratio)) + ")"); return k; }
+  const bool empty = (B == 0 || T == 0 || N == 0);
+  const bool scaled = (qk_dtype == CSA_FP8_E4M3 || qk_dtype == CSA_MXFP4);
+  k.ptr(q, "q", !empty) && k.ptr(w, "w", !empty) && k.ptr(kk, "k", !empty) && k.ptr(scores, "scores", !empty);
+  if (!k.ok()) return k;
+  if (scaled) {
+    k.ptr(q_scale, "q_scale", !empty) && k.ptr(k_scale, "k_scale", !empty);
+  } else {
+    k.must_be_null(q_scale, "q_scale", "for unscaled qk_dtype") && k.must_be_null(k_scale, "k_scale", "for unscaled qk_dtype");
+  }
+  return k;
+}
+
+inline Check check_topk(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int kk,
+                        const void* scores, int score_dtype, const void* idx, const void* ws, size_t ws_bytes) {
+  Check k;
+  if (B < 0 || T < 0 || N < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T and N must be >= 0"); return k; }
+  if (q_pos0 < 0) { k.fail(CSA_ERR_INVALID_ARG, "q_pos0 must be >= 0"); return k; }
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (kk < 1 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [1, 2048], got " + i2s(kk)); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (T > 0 && N < visible(q_pos0 + T - 1, ratio)) { k.fail(CSA_ERR_INVALID_ARG, "N = " + i2s(N) + " is smaller than the entries visible to the last query (" + i2s(visible(q_pos0 + T - 1, ratio)) + ")"); return k; }
+  const bool empty = (B == 0 || T == 0);
+  k.ptr(scores, "scores", !empty && N > 0) && k.ptr(idx, "idx", !empty);
+  if (!k.ok()) return k;
+  const size_t need = topk_workspace_bytes(B, T, N, score_dtype);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "topk_select needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
+    k.ptr(ws, "workspace");
+  }
+  return k;
+}
+
+inline bool check_attn_common(Check& k, int64_t B, int64_t T, int64_t q_pos0, int H, int d,
+                               int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype) {
+  if (B < 0 || T < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and T must be >= 0"); return false; }
+  if (q_pos0 < 0) { k.fail(CSA_ERR_INVALID_ARG, "q_pos0 must be >= 0"); return false; }
+  if (H != CSA_HEADS || d != CSA_HEAD_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "attention shape must be H=64, d=512"); return false; }
+  if (window < 1 || window > kMaxWindow) { k.fail(CSA_ERR_INVALID_ARG, "window must be in [1, 4096], got " + i2s(window)); return false; }
+  if (!std::isfinite(scale)) { k.fail(CSA_ERR_INVALID_ARG, "scale must be finite"); return false; }
+  if (io_dtype != CSA_F32 && io_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "io_dtype must be CSA_F32 or CSA_BF16"); return false; }
+  if (T > 0) {
+    const int64_t wstart = q_pos0 - window + 1 > 0 ? q_pos0 - window + 1 : 0;
+    if (raw_pos0 < 0 || raw_pos0 > wstart) { k.fail(CSA_ERR_INVALID_ARG, "kv_raw starts at " + i2s(raw_pos0) + ", after the first window position " + i2s(wstart)); return false; }
+    if (raw_pos0 + n_raw < q_pos0 + T) { k.fail(CSA_ERR_INVALID_ARG, "kv_raw ends before the last query position"); return false; }
+  }
+  return true;
+}
+
+inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos0, int H, int d,
+                          const void* q, const void* kv_cmp, const void* idx, const void* kv_raw,
+                          int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype,
+                          const void* out, const void* lse, const void* ws, size_t ws_bytes) {
+  Check k;
+  if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
+  if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
+  if (kk < 0 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [0, 2048], got " + i2s(kk)); return k; }
+  const bool empty = (B == 0 || T == 0);
+  k.ptr(q, "q", !empty) && k.ptr(kv_cmp, "kv_cmp", !empty && N > 0 && kk > 0) &&
+      k.ptr(idx, "idx", !empty && kk > 0) && k.ptr(kv_raw, "kv_raw", !empty) && k.ptr(out, "out", !empty) &&
+      k.ptr(lse, "lse", false);
+  if (!k.ok()) return k;
+  const size_t need = attn_workspace_bytes(B, T);
+  if (need > 0 && !empty) {
+    if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "sparse_mqa_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
+    k.ptr(ws, "workspace");
+  }
+  return k;
+}
+
+inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
+                       const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
+                       int64_t n_raw, int window, float scale, const void* sink, int io_dtype,
+                       const void* out, const void* lse, const void* ws, size_t ws_bytes) {
+  Check k;
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
+  if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
+  if (T > 0 && N < visible(q_pos0 + T - 1, ratio)) { k.fail(CSA_ERR_INVALID_ARG, "N = " + i2s(N) + " is smaller than the entries visible to the last query"); return k; }
+  const bool empty = (B == 0 || T == 0);
+  k.ptr(q, "q", !empty) && k.ptr(kv_cmp, "kv_cmp", !empty && N > 0) && k.ptr(kv_raw, "kv_raw", !empty) &&
+      k.ptr(out, "out", !empty) && k.ptr(lse, "lse", false) && k.ptr(sink, "sink", false);
+  if (!k.ok()) return k;
+  const size_t need = attn_workspace_bytes(B, T);
+  if (need > 0 && !empty) {
+    if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "hca_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
+    k.ptr(ws, "workspace");
+  }
+  return k;
+}
+
+inline size_t workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int kk) {
+  (void)kk;
+  switch (op) {
+    case CSA_OP_TOPK: return topk_workspace_bytes(B, T, N, CSA_BF16) > topk_workspace_bytes(B, T, N, CSA_F32)
+                                 ? topk_workspace_bytes(B, T, N, CSA_BF16) : topk_workspace_bytes(B, T, N, CSA_F32);
+    case CSA_OP_SPARSE_ATTN:
+    case CSA_OP_HCA_ATTN: return attn_workspace_bytes(B, T);
+    default: return 0;
+  }
+}
+
+}  // namespace csa

@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports every symbol include/csa.h declares, and
+rejects bad arguments on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+A = 0x10000          # a 16-byte-aligned fake device address; validation never dereferences it
+MIS = 0x10008        # misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import long_context_sparse_compress_amd as csa
+    return csa.library()
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
+                          "hca_attn", "csa_workspace_bytes", "csa_last_error", "csa_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "long_context_sparse_compress_amd", "libcsa.so")],
+                         capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def _err(lib):
+    return lib.csa_last_error().decode()
+
+
+def test_compress_validation(lib):
+    f = lib.csa_compress
+    ok = dict(ratio=4, B=2, n_tok=8, c=512, pos0=0, Ca=A, Za=A, Cb=A, Zb=A, pCb=None, pZb=None,
+              bias=A, gamma=None, eps=1e-6, idt=1, odt=1, out=A, stride=0, s=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["ratio"], a["B"], a["n_tok"], a["c"], a["pos0"], a["Ca"], a["Za"], a["Cb"], a["Zb"],
+                 a["pCb"], a["pZb"], a["bias"], a["gamma"], a["eps"], a["idt"], a["odt"], a["out"],
+                 a["stride"], a["s"])
+
+    assert call(ratio=8) == -1 and "ratio" in _err(lib)
+    assert call(Ca=None) == -1 and "Ca is NULL" in _err(lib)
+    assert call(Ca=MIS) == -1 and "aligned" in _err(lib)
+    assert call(pos0=6) == -1 and "pos0" in _err(lib)
+    assert call(pos0=8) == -1 and "prev_Cb is NULL" in _err(lib)
+    assert call(pCb=A, pZb=A) == -1 and "must be NULL" in _err(lib)
+    assert call(c=100) == -1 and "multiple of 64" in _err(lib)
+    assert call(idt=2) == -2
+    assert call(eps=0.0) == -1 and "eps" in _err(lib)
+    assert call(ratio=128, n_tok=256) == -1 and "Cb must be NULL" in _err(lib)
+    assert call(stride=100) == -1
+    # nothing to do: succeeds without touching the GPU
+    assert call(n_tok=3, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None) == 0
+    assert call(B=0, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None) == 0
+
+
+def test_index_validation(lib):
+    f = lib.lightning_index
+
+    def call(B=1, T=4, N=64, q_pos0=252, ratio=4, H=64, d=128, q=A, qs=None, w=A, k=A, ks=None,
+             qk=1, sc=A, sdt=1):
+        return f(B, T, N, q_pos0, ratio, H, d, q, qs, w, k, ks, qk, sc, sdt, None)
+
+    assert call(H=32) == -2 and "H_I=64" in _err(lib)
+    assert call(N=10) == -1 and "visible" in _err(lib)
+    assert call(qk=2) == -1 and "q_scale is NULL" in _err(lib)
+    assert call(qk=1, qs=A) == -1 and "must be NULL" in _err(lib)
+    assert call(qk=0, sdt=1) == -2
+    assert call(ratio=5) == -1
+    assert call(w=MIS) == -1 and "aligned" in _err(lib)
+    assert call(qk=7) == -2
+
+
+def test_topk_validation(lib):
+    f = lib.topk_select
+    assert f(1, 1, 64, 255, 4, 0, A, 1, A, None, 0, None) == -1 and "k must be" in _err(lib)
+    assert f(1, 1, 64, 255, 4, 4096, A, 1, A, None, 0, None) == -1
+    assert f(1, 1, 64, 255, 4, 16, A, 2, A, None, 0, None) == -2
+    assert f(1, 1, 10, 255, 4, 16, A, 1, A, None, 0, None) == -1 and "visible" in _err(lib)
+    # rows too long for LDS need a workspace
+    assert f(1, 1, 262144, 1048575, 4, 1024, A, 1, A, None, 0, None) == -4
+    need = lib.csa_workspace_bytes(2, 1, 1, 262144, 1024)
+    assert need > 0
+    assert f(1, 1, 262144, 1048575, 4, 1024, A, 1, A, A, need - 1, None) == -4
+
+
+def test_attention_validation(lib):
+    s = lib.sparse_mqa_attn
+    h = lib.hca_attn
+    ws = lib.csa_workspace_bytes(3, 2, 1, 64, 16)
+    assert ws > 0
+
+    def sp(H=64, d=512, window=128, raw_pos0=128, n_raw=128, io=1, wsp=A, wsb=ws, q=A):
+        return s(2, 1, 64, 16, 255, H, d, q, A, A, A, raw_pos0, n_raw, window, 0.04, io, A, None,
+                 wsp, wsb, None)
+
+    assert sp(H=32) == -2
+    assert sp(raw_pos0=129) == -1 and "first window position" in _err(lib)
+    assert sp(n_raw=127) == -1 and "last query" in _err(lib)
+    assert sp(window=0) == -1
+    assert sp(io=2) == -2
+    assert sp(wsp=None) == -4
+    assert sp(wsb=ws - 1) == -4
+    assert sp(q=None) == -1
+    assert h(2, 1, 1, 128, 255, 64, 512, A, A, A, 128, 128, 128, 0.04, None, 1, A, None, A, ws, None) == -1
+    assert h(2, 1, 2, 3, 255, 64, 512, A, A, A, 128, 128, 128, 0.04, None, 1, A, None, A, ws, None) == -1
+
+
+def test_workspace_query(lib):
+    assert lib.csa_workspace_bytes(0, 8, 1, 64, 0) == 0
+    assert lib.csa_workspace_bytes(3, 1, 4096, 33792, 512) == 0     # prefill: no split
+    assert lib.csa_workspace_bytes(4, 16, 1, 8192, 0) > 0           # decode: split rows
+    assert lib.csa_workspace_bytes(99, 1, 1, 1, 1) == 0
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="no g++")
+def test_validation_compiles_without_hip(tmp_path):
+    """validate.h is plain C++: it builds with g++ and no HIP headers."""
+    src = tmp_path / "v.cpp"
+    src.write_text('#include "validate.h"\nint main(){auto c=csa::check_topk(1,1,8,0,4,0,nullptr,1,nullptr,nullptr,0);'
+                   'return c.code==CSA_ERR_INVALID_ARG?0:1;}\n')
+    exe = tmp_path / "v"
+    r = subprocess.run(["g++", "-std=c++17", "-I", os.path.join(ROOT, "long_context_sparse_compress_amd", "csrc"),
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(exe)]).returncode == 0
