@@ -1,5 +1,380 @@
-// placeholder until the kernel lands
+// Stage 3: the causal Top-k selector on gfx950.
+//
+// "DeepSeek Technical Reports" (DSA, the Top-k attention equation) and
+// "DeepSeek V4 结构速览" (核心设计; Lightning Indexer): each query keeps the k
+// entries with the highest stored indexer score among s < V(t).  Equal
+// scores go to the lower index.
+//
+// Exact radix select on an order-preserving integer image of the stored score
+// (16-bit for bf16, 32-bit for fp32).  Digits are 11 bits wide from the top
+// (bf16: 11 + 5 bits; fp32: 11 + 11 + 10).  Each digit pass builds a
+// histogram of the digit over the keys that match the prefix found so far,
+// then the bin holding the k-th largest key extends the prefix.  After the
+// last digit the prefix is the exact k-th largest key K, and `rem` says how
+// many keys equal to K are taken (the lowest indices).  The output is written
+// in ascending index order by an ordered compaction (block-wide exclusive
+// scan of per-thread counts), so the result is deterministic.
+//
+// Two paths:
+//  * rows of up to ~36K bf16 (~18K fp32) keys: one 1024-thread workgroup per
+//    row holds the whole row in LDS and runs every pass there;
+//  * longer rows (the 1M-context decode has 262,144 candidates): S workgroups
+//    per row, one slice each; per-digit histograms are merged in global
+//    workspace with atomics, one kernel per pass, then a count kernel and an
+//    ordered write kernel.
+#include "device.h"
 #include "launch.h"
+#include "validate.h"
+
 namespace csa {
-hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kBins = 2048;   // 11-bit digits
+
+template <typename KT> struct Digits;
+template <> struct Digits<uint16_t> {
+  static constexpr int n = 2;
+  __device__ static constexpr int shift(int p) { return p == 0 ? 5 : 0; }
+  __device__ static constexpr int bits(int p) { return p == 0 ? 11 : 5; }
+};
+template <> struct Digits<uint32_t> {
+  static constexpr int n = 3;
+  __device__ static constexpr int shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+  __device__ static constexpr int bits(int p) { return p == 0 ? 11 : (p == 1 ? 11 : 10); }
+};
+
+// Order-preserving image of a stored score: larger float -> larger key;
+// -0.0 is mapped to +0.0 first.
+__device__ __forceinline__ uint16_t key_of(uint16_t b) {
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? static_cast<uint16_t>(~b) : static_cast<uint16_t>(b | 0x8000u);
 }
+__device__ __forceinline__ uint32_t key_of(uint32_t b) {
+  if (b == 0x80000000u) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <typename KT>
+__device__ __forceinline__ KT load_key(const KT* row, int64_t i) {
+  return key_of(row[i]);
+}
+
+// Find the digit whose bin holds the rem-th largest key (1-based), given the
+// digit histogram `hist` of nb bins.  Runs on wave 0; lane 0 of wave 0 writes
+// (digit, rem') to out[0..1] where rem' counts from the top of that bin.
+__device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  const int per = (nb + 63) / 64;
+  const int lo = lane * per;
+  const int hi = lo + per < nb ? lo + per : nb;
+  uint32_t sum = 0;
+  for (int i = lo; i < hi; ++i) sum += hist[i];
+  // inclusive suffix sums over lanes: S[l] = sum over lanes >= l
+  uint32_t S = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_down(S, o, 64);
+    if (lane + o < 64) S += v;
+  }
+  const uint64_t ball = __ballot(S >= rem);
+  const int L = 63 - __clzll(static_cast<long long>(ball));   // highest lane with S >= rem
+  if (lane == L) {
+    uint32_t cum = S - sum;   // keys in higher lanes' bins
+    for (int i = hi - 1; i >= lo; --i) {
+      if (cum + hist[i] >= rem) {
+        out[0] = static_cast<uint32_t>(i);
+        out[1] = rem - cum;
+        break;
+      }
+      cum += hist[i];
+    }
+  }
+}
+
+// Block-wide exclusive scan of one uint32 per thread (blockDim.x <= 1024).
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp /* >= 17 words */, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint32_t t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const uint32_t r = tmp[wid] + x - v;
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int64_t row_visible(int64_t t, int64_t q_pos0, int ratio, int64_t N) {
+  const int64_t v = (q_pos0 + t + 1) / ratio;
+  return v < N ? v : N;
+}
+
+// Ordered compaction of one contiguous range [lo, hi) of a row: writes every
+// index whose key > K, and keys == K while the running equal-rank < rem, to
+// out[pos...] in ascending order.  `key(i)` reads the key of index i.
+template <typename KT, typename F>
+__device__ __forceinline__ void emit_range(int64_t lo, int64_t hi, KT K, uint32_t rem, uint32_t gt_before,
+                                           uint32_t eq_before, int32_t* out, F key) {
+  uint32_t pos = gt_before + (eq_before < rem ? eq_before : rem);
+  uint32_t er = eq_before;
+  for (int64_t i = lo; i < hi; ++i) {
+    const KT kk = key(i);
+    if (kk > K) {
+      out[pos++] = static_cast<int32_t>(i);
+    } else if (kk == K) {
+      if (er < rem) out[pos++] = static_cast<int32_t>(i);
+      ++er;
+    }
+  }
+}
+
+// ------------------------------------------------------------ LDS path
+template <typename KT>
+__global__ void __launch_bounds__(1024)
+topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT* __restrict__ scores,
+                int32_t* __restrict__ idx) {
+  extern __shared__ uint8_t smem_raw[];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw);           // kBins
+  uint32_t* tmp = hist + kBins;                                       // 32 words
+  KT* keys = reinterpret_cast<KT*>(tmp + 32);
+  const int64_t row = blockIdx.x;
+  const int64_t t = row % T;
+  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  int32_t* out = idx + row * k;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (V <= k) {
+    for (int i = tid; i < k; i += nt) out[i] = i < V ? i : -1;
+    return;
+  }
+  const KT* src = scores + row * N;
+  for (int64_t i = tid; i < V; i += nt) keys[i] = load_key(src, i);
+
+  KT prefix = 0, mask = 0;
+  uint32_t rem = static_cast<uint32_t>(k);
+  for (int p = 0; p < Digits<KT>::n; ++p) {
+    const int sh = Digits<KT>::shift(p);
+    const int nb = 1 << Digits<KT>::bits(p);
+    for (int i = tid; i < nb; i += nt) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < V; i += nt) {
+      const KT kk = keys[i];
+      if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    resolve_digit(hist, nb, rem, tmp + 20);
+    __syncthreads();
+    prefix |= static_cast<KT>(tmp[20] << sh);
+    mask |= static_cast<KT>((nb - 1) << sh);
+    rem = tmp[21];
+    __syncthreads();
+  }
+  const KT K = prefix;
+
+  const int64_t chunk = (V + nt - 1) / nt;
+  const int64_t lo = tid * chunk < V ? tid * chunk : V;
+  const int64_t hi = lo + chunk < V ? lo + chunk : V;
+  uint32_t gt = 0, eq = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    gt += keys[i] > K;
+    eq += keys[i] == K;
+  }
+  uint32_t total;
+  const uint32_t gtb = block_exclusive_scan(gt, tmp, &total);
+  const uint32_t eqb = block_exclusive_scan(eq, tmp, &total);
+  emit_range<KT>(lo, hi, K, rem, gtb, eqb, out, [&](int64_t i) { return keys[i]; });
+}
+
+// ------------------------------------------------------------ global path
+// Workspace per row (uint32 words): hist[3][2048], counts[S][2].
+constexpr int kWsHist = 3 * kBins;
+
+__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Re-derive (prefix, mask, rem) from the histograms of passes 0..np-1.
+template <typename KT>
+__device__ void derive_state(const uint32_t* rowws, int np, uint32_t k, uint32_t* sh_state, KT& prefix,
+                             KT& mask, uint32_t& rem) {
+  prefix = 0;
+  mask = 0;
+  rem = k;
+  for (int p = 0; p < np; ++p) {
+    const int sh = Digits<KT>::shift(p);
+    const int nb = 1 << Digits<KT>::bits(p);
+    resolve_digit(rowws + p * kBins, nb, rem, sh_state);
+    __syncthreads();
+    prefix |= static_cast<KT>(sh_state[0] << sh);
+    mask |= static_cast<KT>((nb - 1) << sh);
+    rem = sh_state[1];
+    __syncthreads();
+  }
+}
+
+template <typename KT>
+__global__ void __launch_bounds__(256)
+topk_hist_kernel(int pass, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                 const KT* __restrict__ scores, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t st[4];
+  const int64_t row = blockIdx.y;
+  const int64_t t = row % T;
+  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  if (V <= k) return;
+  uint32_t* rowws = ws + row * (kWsHist + 2 * S);
+  KT prefix, mask;
+  uint32_t rem;
+  derive_state<KT>(rowws, pass, static_cast<uint32_t>(k), st, prefix, mask, rem);
+  const int sh = Digits<KT>::shift(pass);
+  const int nb = 1 << Digits<KT>::bits(pass);
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int64_t L = (V + S - 1) / S;
+  const int64_t lo = blockIdx.x * L, hi = lo + L < V ? lo + L : V;
+  const KT* src = scores + row * N;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    const KT kk = load_key(src, i);
+    if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> sh) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = rowws + pass * kBins;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+template <typename KT>
+__global__ void __launch_bounds__(256)
+topk_count_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                  const KT* __restrict__ scores, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t st[4];
+  __shared__ uint32_t red[2][4];
+  const int64_t row = blockIdx.y;
+  const int64_t t = row % T;
+  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  if (V <= k) return;
+  uint32_t* rowws = ws + row * (kWsHist + 2 * S);
+  KT K, mask;
+  uint32_t rem;
+  derive_state<KT>(rowws, Digits<KT>::n, static_cast<uint32_t>(k), st, K, mask, rem);
+  const int64_t L = (V + S - 1) / S;
+  const int64_t lo = blockIdx.x * L, hi = lo + L < V ? lo + L : V;
+  const KT* src = scores + row * N;
+  uint32_t gt = 0, eq = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    const KT kk = load_key(src, i);
+    gt += kk > K;
+    eq += kk == K;
+  }
+  gt = wave_sum_u32(gt);
+  eq = wave_sum_u32(eq);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = gt;
+    red[1][threadIdx.x >> 6] = eq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = rowws + kWsHist;
+    cnt[2 * blockIdx.x] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    cnt[2 * blockIdx.x + 1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
+template <typename KT>
+__global__ void __launch_bounds__(256)
+topk_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                  const KT* __restrict__ scores, uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
+  __shared__ uint32_t st[4];
+  __shared__ uint32_t tmp[32];
+  const int64_t row = blockIdx.y;
+  const int64_t t = row % T;
+  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < V ? i : -1;
+    return;
+  }
+  uint32_t* rowws = ws + row * (kWsHist + 2 * S);
+  KT K, mask;
+  uint32_t rem;
+  derive_state<KT>(rowws, Digits<KT>::n, static_cast<uint32_t>(k), st, K, mask, rem);
+  const uint32_t* cnt = rowws + kWsHist;
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int s = 0; s < static_cast<int>(blockIdx.x); ++s) {
+    gt_before += cnt[2 * s];
+    eq_before += cnt[2 * s + 1];
+  }
+  const int64_t L = (V + S - 1) / S;
+  const int64_t lo = blockIdx.x * L, hi = lo + L < V ? lo + L : V;
+  const KT* src = scores + row * N;
+  // per-thread contiguous sub-ranges of the slice
+  const int nt = blockDim.x;
+  const int64_t len = hi > lo ? hi - lo : 0;
+  const int64_t chunk = (len + nt - 1) / nt;
+  const int64_t a = lo + (threadIdx.x * chunk < len ? threadIdx.x * chunk : len);
+  const int64_t b = a + chunk < hi ? a + chunk : (hi > a ? hi : a);
+  uint32_t gt = 0, eq = 0;
+  for (int64_t i = a; i < b; ++i) {
+    const KT kk = load_key(src, i);
+    gt += kk > K;
+    eq += kk == K;
+  }
+  uint32_t total;
+  const uint32_t gtb = block_exclusive_scan(gt, tmp, &total);
+  const uint32_t eqb = block_exclusive_scan(eq, tmp, &total);
+  emit_range<KT>(a, b, K, rem, gt_before + gtb, eq_before + eqb, out,
+                 [&](int64_t i) { return load_key(src, i); });
+}
+
+template <typename KT>
+hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
+  const KT* sc = static_cast<const KT*>(a.scores);
+  const int64_t rows = a.B * a.T;
+  if (topk_row_in_lds(a.N, a.score_dtype)) {
+    const size_t smem = (kBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
+    hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
+                       a.N, a.q_pos0, a.ratio, a.k, sc, a.idx);
+    return hipGetLastError();
+  }
+  const int S = kTopkSlices;
+  uint32_t* ws = static_cast<uint32_t*>(a.ws);
+  const int64_t words = rows * (kWsHist + 2 * S);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, s, ws,
+                     words);
+  const dim3 grid(S, static_cast<uint32_t>(rows));
+  for (int p = 0; p < Digits<KT>::n; ++p)
+    hipLaunchKernelGGL((topk_hist_kernel<KT>), grid, dim3(256), 0, s, p, a.T, a.N, a.q_pos0, a.ratio, a.k, S,
+                       sc, ws);
+  hipLaunchKernelGGL((topk_count_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc,
+                     ws);
+  hipLaunchKernelGGL((topk_write_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc,
+                     ws, a.idx);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.T == 0) return hipSuccess;
+  if (a.score_dtype == CSA_BF16) return launch_typed<uint16_t>(a, s);
+  return launch_typed<uint32_t>(a, s);
+}
+
+}  // namespace csa

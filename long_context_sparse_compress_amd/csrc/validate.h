@@ -80,9 +80,9 @@ inline bool topk_row_in_lds(int64_t N, int dtype) {
   return N <= (dtype == CSA_BF16 ? kTopkLdsMax16 : kTopkLdsMax32);
 }
 
-// Global path scratch per row: a 2048-bin histogram, per-slice counts and the
-// selection state.
-inline size_t topk_row_ws_bytes() { return (2048 + 4 * kTopkSlices + 16) * sizeof(uint32_t); }
+// Global path scratch per row: one 2048-bin histogram per digit pass (at most
+// three) and a (greater, equal) count pair per slice.
+inline size_t topk_row_ws_bytes() { return (3 * 2048 + 2 * kTopkSlices) * sizeof(uint32_t); }
 
 inline size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t N, int dtype) {
   if (topk_row_in_lds(N, dtype)) return 0;

@@ -1,0 +1,119 @@
+"""GPU parity of topk_select (stage 3) against the oracle, through the C ABI.
+
+Pages: "DeepSeek Technical Reports" (DSA, the Top-k attention equation);
+"DeepSeek V4 结构速览" (核心设计; Lightning Indexer: top-512, causal range).
+Stage-isolated: both sides rank the same stored score tensor, so the selected
+sets must be identical (ties go to the lower index).  The GPU writes the set in
+ascending index order followed by -1 padding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_compress_amd as csa
+import synth
+from oracle import topk as ot
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(prefix, B, T, N, dtype, ties=None):
+    x = synth.normal(prefix, (B, T, N))
+    if ties:
+        x = np.round(x * ties) / ties          # few distinct values: heavy ties
+    if dtype == "bf16":
+        x = synth.round_bf16(x)
+        return x, dev(x, torch.bfloat16)
+    return x, dev(x)
+
+
+def _check(got, ref):
+    got = got.cpu().numpy()
+    B, T, k = got.shape
+    for b in range(B):
+        for t in range(T):
+            g, r = got[b, t], ref[b, t]
+            nv = int((r >= 0).sum())
+            assert np.all(g[nv:] == -1), (b, t)
+            assert np.all(np.diff(g[:nv]) > 0), (b, t)          # ascending
+            assert np.array_equal(g[:nv], np.sort(r[:nv])), (b, t)
+
+
+def _run(x_dev, k, q_pos0, ratio=4):
+    idx = csa.topk_select(x_dev, k, q_pos0=q_pos0, ratio=ratio)
+    torch.cuda.synchronize()
+    return idx
+
+
+def test_tiny_fp32():
+    """256 rows x 64 entries, k = 16 (rows t < 63 see fewer than 16 entries)."""
+    x, d = _scores("tk.tiny", 1, 256, 64, "f32")
+    _check(_run(d, 16, 0), ot.topk_select(x, 16, 0, 4))
+
+
+def test_csa_decode_bf16():
+    """Batch 32, 16,384 bf16 scores per row, k = 512."""
+    x, d = _scores("tk.dec", 32, 1, 16384, "bf16")
+    _check(_run(d, 512, 65535), ot.topk_select(x, 512, 65535, 4))
+
+
+def test_chunked_prefill_bf16_sampled():
+    """4,096 rows over 32,768..33,792 candidates, k = 512 (LDS path); sampled rows."""
+    T, N, q0 = 4096, 33792, 131072
+    x, d = _scores("tk.pf", 1, T, N, "bf16")
+    got = _run(d, 512, q0)
+    rows = [0, 1, 2, 3, 511, 2047, 2048, 4093, 4094, 4095]
+    ref = ot.topk_select(x, 512, q0, 4, rows=rows)
+    _check(got[:, rows], ref)
+
+
+def test_1m_decode_bf16_global_path():
+    """Batch 8, 262,144 candidates per row, k = 1024: the multi-workgroup path."""
+    x, d = _scores("tk.1m", 8, 1, 262144, "bf16")
+    _check(_run(d, 1024, 1048575), ot.topk_select(x, 1024, 1048575, 4))
+
+
+def test_fp32_global_path():
+    x, d = _scores("tk.f32g", 2, 3, 20000, "f32", ties=64)
+    _check(_run(d, 700, 79997), ot.topk_select(x, 700, 79997, 4))
+
+
+@pytest.mark.parametrize("dtype,ties,N,k", [
+    ("bf16", 4, 5000, 300),        # heavy ties at the threshold
+    ("f32", 2, 3000, 1000),
+    ("bf16", 1, 300000, 2048),     # global path, max k, heavy ties
+])
+def test_ties_go_to_lower_index(dtype, ties, N, k):
+    x, d = _scores(f"tk.ties{N}", 2, 1, N, dtype, ties=ties)
+    _check(_run(d, k, 4 * N - 1), ot.topk_select(x, k, 4 * N - 1, 4))
+
+
+def test_all_equal_and_signed_zero():
+    x = np.zeros((1, 2, 4096), dtype=np.float32)
+    x[0, 1, ::2] = -0.0
+    d = dev(x, torch.bfloat16)
+    got = _run(d, 100, 4 * 4096 - 2)
+    assert np.array_equal(got[0, 0].cpu().numpy(), np.arange(100))
+    assert np.array_equal(got[0, 1].cpu().numpy(), np.arange(100))
+
+
+def test_infinite_scores_are_ranked():
+    """-inf inside the visible range ranks last but can still be selected."""
+    x = np.full((1, 1, 64), -np.inf, dtype=np.float32)
+    x[0, 0, 10] = 1.0
+    got = _run(dev(x), 3, 255)
+    assert list(got[0, 0].cpu().numpy()) == [0, 1, 10]
+
+
+@pytest.mark.parametrize("q_pos0,T,N,k", [(0, 40, 10, 4), (0, 4, 1, 1), (13, 6, 6, 5)])
+def test_fewer_visible_than_k(q_pos0, T, N, k):
+    x, d = _scores(f"tk.few{T}", 2, T, N, "f32")
+    _check(_run(d, k, q_pos0), ot.topk_select(x, k, q_pos0, 4))
+
+
+def test_deterministic():
+    _, d = _scores("tk.det", 4, 1, 100000, "bf16", ties=8)
+    a = _run(d, 1024, 399999)
+    b = _run(d, 1024, 399999)
+    assert torch.equal(a, b)
