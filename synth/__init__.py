@@ -225,3 +225,50 @@ def compressor_inputs(prefix: str, B: int, n_tok: int, c: int, ratio: int, pos0:
             if nm != "bias":
                 out[nm] = round_bf16(out[nm])
     return out
+
+
+# --------------------------------------------------------------------------
+# device-side draws for tensors too large to draw on the host
+# --------------------------------------------------------------------------
+
+
+def device_normal(name: str, shape, dtype=None, device="cuda", var: float = 1.0, seed: int = 0):
+    """N(0, var) drawn by torch on the device from a seeded generator, then
+    cast (round to nearest even) to ``dtype``.  Deterministic for a given
+    (seed, name, shape) on a given torch version."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(torch_seed(name, seed))
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if var != 1.0:
+        x.mul_(float(np.sqrt(var)))
+    return x if dtype is None else x.to(dtype)
+
+
+def device_uniform(name: str, shape, device="cuda", seed: int = 0):
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(torch_seed(name, seed))
+    return torch.rand(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+
+
+def random_topk_indices(name: str, B: int, T: int, k: int, visible, seed: int = 0) -> np.ndarray:
+    """A seeded stand-in for Top-k output: for each (b, t) a random set of
+    min(k, visible[t]) distinct entries of [0, visible[t]) in ascending order,
+    then -1 padding.  ``visible`` is a length-T sequence."""
+    g = rng(name, seed)
+    out = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            v = int(visible[t])
+            n = min(k, v)
+            if n == 0:
+                continue
+            if v <= 4 * n:
+                sel = np.sort(g.permutation(v)[:n])
+            else:
+                sel = np.sort(g.choice(v, size=n, replace=False))
+            out[b, t, :n] = sel
+    return out
