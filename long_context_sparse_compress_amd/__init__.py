@@ -111,18 +111,32 @@ def _workspace(op, B, T, N, k, device, workspace):
 
 
 def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
-                 gamma=None, eps=1e-6, out=None, out_dtype=None, out_batch_stride=0, stream=None):
-    """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c]."""
+                 gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, stream=None):
+    """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c].
+
+    With ``cache_entry0`` set, ``out`` is a [B, N_cache, c] cache and the new
+    entries are written in place at entries cache_entry0 .. cache_entry0 +
+    n_tok//ratio - 1 of every sequence."""
     B, n_tok, c = Ca.shape
+    n_ent = n_tok // ratio
     in_dt = _dt(Ca)
     if out is None:
         odt = Ca.dtype if out_dtype is None else out_dtype
-        out = torch.empty(B, n_tok // ratio, c, dtype=odt, device=Ca.device)
-    if out_batch_stride == 0 and out.numel() < B * (n_tok // ratio) * c:
-        raise ValueError("out is too small")
+        out = torch.empty(B, n_ent, c, dtype=odt, device=Ca.device)
+    if cache_entry0 is None:
+        if out.numel() < B * n_ent * c:
+            raise ValueError("out is too small")
+        optr, stride = _ptr(out), 0
+    else:
+        if out.dim() != 3 or out.shape[0] != B or out.shape[2] != c:
+            raise ValueError("cache must be [B, N_cache, c]")
+        if cache_entry0 < 0 or cache_entry0 + n_ent > out.shape[1]:
+            raise ValueError("cache slot out of range")
+        optr = _ptr(out) + cache_entry0 * c * out.element_size()
+        stride = out.shape[1] * c
     st = library().csa_compress(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
                                 _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
-                                _dt(out), _ptr(out), out_batch_stride, _stream(stream))
+                                _dt(out), optr, stride, _stream(stream))
     _check(st, "csa_compress")
     return out
 

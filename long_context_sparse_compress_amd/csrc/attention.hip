@@ -83,12 +83,14 @@ __device__ __forceinline__ List make_list(const Params& P, int64_t t) {
 }
 
 // Address of list row `p` of query (b, t), or nullptr for padding / past the end.
+// `sidx` (optional) is the query's Top-k row already staged in LDS.
 template <typename E>
-__device__ __forceinline__ const E* row_ptr(const Params& P, int64_t b, int64_t t, const List& l, int64_t p) {
+__device__ __forceinline__ const E* row_ptr(const Params& P, int64_t b, int64_t t, const List& l, int64_t p,
+                                            const int32_t* sidx = nullptr) {
   if (p >= l.L) return nullptr;
   if (p < l.n_cmp) {
     int64_t e = p;
-    if (P.idx) e = P.idx[(b * P.T + t) * P.k + p];
+    if (P.idx) e = sidx ? sidx[p] : P.idx[(b * P.T + t) * P.k + p];
     if (e < 0 || e >= P.N) return nullptr;
     return static_cast<const E*>(P.kv_cmp) + (b * P.N + e) * kD;
   }
@@ -105,35 +107,40 @@ __device__ __forceinline__ void split_range(const Params& P, const List& l, int 
   if (t0 > t1) t0 = t1;
 }
 
-// Tile-local rows of transposed group g: {4g..4g+3, 16+4g..16+4g+3}.
-__device__ __forceinline__ int group_row(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
+// ------------------------------------------------------------ bf16 MFMA kernel
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// 8 rows x 8 bf16 (one uint4 per row) -> 8 columns x 8 rows (one uint4 per column).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t w[8][4];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    w[e][0] = in[e].x; w[e][1] = in[e].y; w[e][2] = in[e].z; w[e][3] = in[e].w;
-  }
-#pragma unroll
-  for (int dl = 0; dl < 8; ++dl) {
-    uint32_t c[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t a = w[2 * m][dl >> 1], b = w[2 * m + 1][dl >> 1];
-      c[m] = (dl & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    out[dl] = make_uint4(c[0], c[1], c[2], c[3]);
-  }
+constexpr int kTileBytes = kTile * kKsStride;   // one row-major tile in LDS
+
+// One 1 KB latent row straight from global memory into LDS (16 bytes per lane,
+// lane l's bytes land at dst + 16 l): no registers, no staging.
+__device__ __forceinline__ void row_to_lds(const uint16_t* src_row, uint8_t* dst_row, int lane) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src_row + lane * 8),
+                                   (lds_void*)(dst_row), 16, 0, 0);
 }
 
-// ------------------------------------------------------------ bf16 MFMA kernel
-__global__ void __launch_bounds__(256)
+// B operand of the P V MFMA (rows x 16 columns, k-slice of lane group g) read
+// transposed from the row-major tile: within a 16-lane group, lane k points at
+// row base + k/4, columns 4(k%4)..4(k%4)+3 of the 16-column block; the
+// transposing read hands lane j column j of rows base..base+3.
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* tile, int n, int g, int k) {
+  const uint8_t* p0 = tile + (4 * g + (k >> 2)) * kKsStride + (n * 16 + 4 * (k & 3)) * 2;
+  const uint8_t* p1 = p0 + 16 * kKsStride;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(Params P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* Ks = smem;                                                  // [32][kKsStride]
-  uint4* Vt = reinterpret_cast<uint4*>(smem + kTile * kKsStride);      // [4][512] x 8 rows
-  uint32_t* rvalid = reinterpret_cast<uint32_t*>(smem + kTile * kKsStride + 4 * kD * 16);
+  uint8_t* tiles = smem;                                                    // [2][32][kKsStride]
+  uint32_t* rvalid = reinterpret_cast<uint32_t*>(smem + 2 * kTileBytes);    // [2][32]
+  int32_t* sidx = reinterpret_cast<int32_t*>(rvalid + 2 * kTile);           // [k] Top-k row of this query
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -143,6 +150,15 @@ attn_bf16_kernel(Params P) {
   const List l = make_list(P, t);
   int64_t tile0, tile1;
   split_range(P, l, split, tile0, tile1);
+
+  // Stage the slice of this query's Top-k row that this workgroup's tiles use.
+  if (P.idx) {
+    const int64_t p0 = tile0 * kTile;
+    const int64_t p1 = tile1 * kTile < l.n_cmp ? tile1 * kTile : l.n_cmp;
+    const int32_t* src = P.idx + gq * P.k;
+    for (int64_t p = p0 + tid; p < p1; p += 256) sidx[p] = src[p];
+    __syncthreads();
+  }
 
   // q fragments of head 16*wid + j, d in [g*128, g*128+128)
   uint4 qf[16];
@@ -158,38 +174,29 @@ attn_bf16_kernel(Params P) {
   for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 ld[8];
-  uint32_t vmask = 0;
-  auto load_tile = [&](int64_t tile) {
-    vmask = 0;
+  // The query's own raw row is always in the list: padding rows load it (and are masked).
+  const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) +
+                             (b * P.n_raw + (P.q_pos0 + t - P.raw_pos0)) * kD;
+  // wave w brings rows 8w..8w+7 of a tile
+  auto issue_tile = [&](int64_t tile, int buf) {
+    uint8_t* dst = tiles + buf * kTileBytes;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int r = group_row(wid, e);
-      const uint16_t* p = row_ptr<uint16_t>(P, b, t, l, tile * kTile + r);
-      if (p) {
-        ld[e] = reinterpret_cast<const uint4*>(p)[lane];
-        vmask |= 1u << e;
-      } else {
-        ld[e] = make_uint4(0, 0, 0, 0);
-      }
+      const int r = 8 * wid + e;
+      const uint16_t* p = row_ptr<uint16_t>(P, b, t, l, tile * kTile + r, sidx);
+      row_to_lds(p ? p : safe_row, dst + r * kKsStride, lane);
+      if (lane == 0) rvalid[buf * kTile + r] = p != nullptr;
     }
   };
 
-  if (tile0 < tile1) load_tile(tile0);
+  if (tile0 < tile1) issue_tile(tile0, 0);
   for (int64_t tile = tile0; tile < tile1; ++tile) {
-    __syncthreads();   // the previous tile's LDS reads are done
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint4*>(Ks + group_row(wid, e) * kKsStride + lane * 16) = ld[e];
-    {
-      uint4 tr[8];
-      transpose8x8(ld, tr);
-#pragma unroll
-      for (int dl = 0; dl < 8; ++dl) Vt[wid * kD + lane * 8 + dl] = tr[dl];
-    }
-    if (lane < 8) rvalid[group_row(wid, lane)] = (vmask >> lane) & 1u;
-    __syncthreads();
-    if (tile + 1 < tile1) load_tile(tile + 1);
+    const int cur = static_cast<int>((tile - tile0) & 1);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's row loads into `cur` have landed
+    __syncthreads();                 // ... and every wave's; nobody still reads `cur ^ 1`
+    if (tile + 1 < tile1) issue_tile(tile + 1, cur ^ 1);
+    const uint8_t* Ks = tiles + cur * kTileBytes;
+    const uint32_t* rv = rvalid + cur * kTile;
 
     // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1)
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -203,8 +210,8 @@ attn_bf16_kernel(Params P) {
     float lg[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[i] = rvalid[4 * g + i] ? s0[i] * P.scale_log2 : -INFINITY;
-      lg[4 + i] = rvalid[16 + 4 * g + i] ? s1[i] * P.scale_log2 : -INFINITY;
+      lg[i] = rv[4 * g + i] ? s0[i] * P.scale_log2 : -INFINITY;
+      lg[4 + i] = rv[16 + 4 * g + i] ? s1[i] * P.scale_log2 : -INFINITY;
     }
     float mt = lg[0];
 #pragma unroll
@@ -222,21 +229,21 @@ attn_bf16_kernel(Params P) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    float a4[4];
+    if (__ballot(alpha != 1.f)) {   // some head's running max moved: rescale O
+      float a4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, 64);
+      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      o[n][0] *= a4[0]; o[n][1] *= a4[1]; o[n][2] *= a4[2]; o[n][3] *= a4[3];
+      for (int n = 0; n < 32; ++n) {
+        o[n][0] *= a4[0]; o[n][1] *= a4[1]; o[n][2] *= a4[2]; o[n][3] *= a4[3];
+      }
     }
     const uint4 pa = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
     const bf16x8 pav = as_bf16x8(pa);
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const uint4 vb = Vt[g * kD + n * 16 + j];
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pav, as_bf16x8(vb), o[n], 0, 0, 0);
-    }
+    for (int n = 0; n < 32; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pav, v_operand(Ks, n, g, j), o[n], 0, 0, 0);
   }
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
@@ -400,7 +407,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int64_t ncmp = a.idx ? a.k : (last + 1) / a.ratio;
   if (!a.idx && ncmp > a.N) ncmp = a.N;
   P.splits = attn_splits(a.B, a.T, ncmp + wlen);
-  const size_t smem = kTile * kKsStride + 4 * kD * 16 + kTile * 4;
+  const size_t smem = 2 * kTile * kKsStride + 2 * kTile * 4 + (a.idx ? a.k * 4 : 0);
   hipLaunchKernelGGL(attn_bf16_kernel, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), smem, s, P);
   if (P.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * kH)), dim3(128), 0, s, P);

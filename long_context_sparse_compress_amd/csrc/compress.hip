@@ -97,7 +97,7 @@ __device__ __forceinline__ void online_merge(Online& st, const Online& o) {
 // One workgroup per (entry i, sequence b).  blockDim.x = CT * G with
 // CT = c / VEC channel threads and G row groups.
 template <typename TI, typename TO, int RATIO>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ Ca, const TI* __restrict__ Za,
                 const TI* __restrict__ Cb, const TI* __restrict__ Zb,
@@ -121,9 +121,9 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
   const int64_t seq = b * n_tok * c;
   // Rows handled by this group: r = g, g + G, ...  Loads of up to UNR rows are
   // issued before any of them is consumed.
-  constexpr int UNR = 4;
+  constexpr int UNR = (VEC == 8) ? 6 : 8;
   for (int r0 = g; r0 < ROWS; r0 += G * UNR) {
-    float zl[UNR][VEC], xl[UNR][VEC];
+    uint4 zl[UNR], xl[UNR];    // raw 16-byte row slices; converted when consumed
     bool have[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -146,8 +146,8 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
         xp = pCb + off;
       }
       if (zp) {
-        load_vec<TI>(zp, zl[u]);
-        load_vec<TI>(xp, xl[u]);
+        zl[u] = *reinterpret_cast<const uint4*>(zp);
+        xl[u] = *reinterpret_cast<const uint4*>(xp);
         have[u] = true;
       }
     }
@@ -156,8 +156,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
       if (!have[u]) continue;
       const int r = r0 + u * G;
       const float* br = bias + static_cast<int64_t>(r) * c + ch0;
+      float zf[VEC], xf[VEC];
+      load_vec<TI>(reinterpret_cast<const TI*>(&zl[u]), zf);
+      load_vec<TI>(reinterpret_cast<const TI*>(&xl[u]), xf);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) online_push(st[v], zl[u][v] + br[v], xl[u][v]);
+      for (int v = 0; v < VEC; ++v) online_push(st[v], zf[v] + br[v], xf[v]);
     }
   }
 
@@ -217,7 +220,11 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   const int CT = static_cast<int>(a.c / VEC);
-  int G = 256 / CT;
+  // Few entries (decode) -> wide workgroups so that every row's loads of an
+  // entry are in flight at once; many entries -> 256 threads per entry.
+  const int64_t n_wg = (a.n_tok / RATIO) * a.B;
+  const int max_threads = n_wg >= 1024 ? 256 : 1024;
+  int G = max_threads / CT;
   if (G < 1) G = 1;
   if (G > ROWS) G = ROWS;
   const int threads = CT * G;

@@ -180,25 +180,33 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 
   const int64_t krow0 = b * N;
-  for (int tg = 0; tg < TPW / 4; ++tg) {
-    const int64_t eg = e_wave + tg * 64;
-    if (eg >= N) break;
-    float keep[QPW];
-#pragma unroll
-    for (int qi = 0; qi < QPW; ++qi) keep[qi] = -INFINITY;
-    F kb[4];
-    int ksc[4];
-    float kscale[4];
+  // Key fragments of one 64-entry group (4 tiles); the next group's loads are
+  // issued before the current group's MFMAs.
+  F kb[2][4];
+  int ksc[2][4];
+  float kscale[2][4];
+  auto load_group = [&](int slot, int64_t eg) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       int64_t e = eg + tt * 16 + col;
       if (e >= N) e = N - 1;
-      kb[tt].load(k + (krow0 + e) * RB, g);
-      if constexpr (QK == CSA_MXFP4) ksc[tt] = static_cast<const uint8_t*>(k_scale)[(krow0 + e) * 4 + g];
-      else ksc[tt] = 127;
-      if constexpr (QK == CSA_FP8_E4M3) kscale[tt] = static_cast<const float*>(k_scale)[krow0 + e];
-      else kscale[tt] = 1.f;
+      kb[slot][tt].load(k + (krow0 + e) * RB, g);
+      if constexpr (QK == CSA_MXFP4) ksc[slot][tt] = static_cast<const uint8_t*>(k_scale)[(krow0 + e) * 4 + g];
+      else ksc[slot][tt] = 127;
+      if constexpr (QK == CSA_FP8_E4M3) kscale[slot][tt] = static_cast<const float*>(k_scale)[krow0 + e];
+      else kscale[slot][tt] = 1.f;
     }
+  };
+  load_group(0, e_wave);
+#pragma unroll
+  for (int tg = 0; tg < TPW / 4; ++tg) {
+    const int cur = tg & 1;
+    const int64_t eg = e_wave + tg * 64;
+    if (eg >= N) break;
+    if (tg + 1 < TPW / 4 && eg + 64 < N) load_group(cur ^ 1, eg + 64);
+    float keep[QPW];
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) keep[qi] = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const int64_t et = eg + tt * 16;
@@ -209,7 +217,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         float part = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 c = qk_tile<QK>(qa[qi][mt], kb[tt], qsc[qi][mt], ksc[tt]);
+          const f32x4 c = qk_tile<QK>(qa[qi][mt], kb[cur][tt], qsc[qi][mt], ksc[cur][tt]);
           part = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), part);
           part = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), part);
           part = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), part);
@@ -217,7 +225,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         }
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
-        part *= kscale[tt];
+        part *= kscale[cur][tt];
         if (e >= vis[qi]) part = -INFINITY;
         if (tt == g) keep[qi] = part;
       }
@@ -253,10 +261,13 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
 template <int QK>
 hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
   if (a.T <= 2) {   // decode: one query per wave, long entry runs
-    constexpr int TPW = (QK == CSA_MXFP4) ? 16 : (QK == CSA_FP8_E4M3 ? 8 : 4);
+    constexpr int TPW = (QK == CSA_MXFP4) ? 16 : 8;
     return launch_mfma<QK, 1, TPW>(a, s);
   }
-  return launch_mfma<QK, 4, 8>(a, s);
+  // prefill: several queries per wave share each key tile (bf16 q fragments are
+  // twice the size of fp8 ones, so two queries fit the register budget)
+  if constexpr (QK == CSA_BF16) return launch_mfma<QK, 2, 8>(a, s);
+  else return launch_mfma<QK, 4, 8>(a, s);
 }
 
 }  // namespace

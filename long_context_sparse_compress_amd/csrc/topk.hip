@@ -125,6 +125,25 @@ __device__ __forceinline__ int64_t row_visible(int64_t t, int64_t q_pos0, int ra
   return v < N ? v : N;
 }
 
+// hist[bin] += 1 for every lane with `active`.  Indexer scores crowd into a
+// few bins, so lanes of a wave that share a bin are combined into one LDS
+// atomic (up to four distinct bins per call); any lanes left over add their
+// own.  Must be called by all lanes of the wave.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pending = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (!pending) break;
+    const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+    const uint32_t lb = __shfl(bin, leader, 64);
+    const uint64_t same = __ballot(active && bin == lb) & pending;
+    if (lane == leader) atomicAdd(&hist[lb], static_cast<uint32_t>(__popcll(same)));
+    pending &= ~same;
+  }
+  if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
 // Ordered compaction of one contiguous range [lo, hi) of a row: writes every
 // index whose key > K, and keys == K while the running equal-rank < rem, to
 // out[pos...] in ascending order.  `key(i)` reads the key of index i.
@@ -163,7 +182,19 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
     return;
   }
   const KT* src = scores + row * N;
-  for (int64_t i = tid; i < V; i += nt) keys[i] = load_key(src, i);
+  constexpr int PER = 16 / sizeof(KT);
+  if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    const int64_t nv = V / PER;
+    for (int64_t vi = tid; vi < nv; vi += nt) {
+      const uint4 raw = reinterpret_cast<const uint4*>(src)[vi];
+      const KT* e = reinterpret_cast<const KT*>(&raw);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) keys[vi * PER + u] = key_of(e[u]);
+    }
+    for (int64_t i = nv * PER + tid; i < V; i += nt) keys[i] = load_key(src, i);
+  } else {
+    for (int64_t i = tid; i < V; i += nt) keys[i] = load_key(src, i);
+  }
 
   KT prefix = 0, mask = 0;
   uint32_t rem = static_cast<uint32_t>(k);
@@ -172,9 +203,10 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
     const int nb = 1 << Digits<KT>::bits(p);
     for (int i = tid; i < nb; i += nt) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < V; i += nt) {
-      const KT kk = keys[i];
-      if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> sh) & (nb - 1)], 1u);
+    for (int64_t base = 0; base < V; base += nt) {
+      const int64_t i = base + tid;
+      const KT kk = i < V ? keys[i] : KT(0);
+      hist_add(hist, (kk >> sh) & (nb - 1), i < V && (kk & mask) == prefix);
     }
     __syncthreads();
     resolve_digit(hist, nb, rem, tmp + 20);
@@ -249,9 +281,10 @@ topk_hist_kernel(int pass, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
   const int64_t L = (V + S - 1) / S;
   const int64_t lo = blockIdx.x * L, hi = lo + L < V ? lo + L : V;
   const KT* src = scores + row * N;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const KT kk = load_key(src, i);
-    if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> sh) & (nb - 1)], 1u);
+  for (int64_t base = lo; base < hi; base += blockDim.x) {
+    const int64_t i = base + threadIdx.x;
+    const KT kk = i < hi ? load_key(src, i) : KT(0);
+    hist_add(hist, (kk >> sh) & (nb - 1), i < hi && (kk & mask) == prefix);
   }
   __syncthreads();
   uint32_t* gh = rowws + pass * kBins;

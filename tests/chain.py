@@ -1,0 +1,113 @@
+"""End-to-end chain on the tiny CSA prefill workload: the GPU path and the
+oracle each run compressor -> indexer -> Top-k -> sparse MQA on their own
+(the oracle never reads a GPU result), plus a C128A compressor and HCA
+attention on the same raw tokens.  Used by tests/test_gpu_chain.py and by
+__graft_entry__.smoke().
+
+Workload ("Tiny CSA prefill"): 1 sequence of 256 raw tokens, fp32; Ca, Cb,
+Za, Zb 256 x 512 ~ N(0,1), bias 8 x 512 ~ N(0, 0.1); the indexer keys come
+from the same compressor on 256 x 128 inputs; q_I 256 x 64 x 128 ~ N(0,
+1/128); w ~ U(0,1); k = 16; q 256 x 64 x 512 ~ N(0,1); raw window latents
+256 x 512 ~ N(0,1); scale 1/sqrt(512); seed 0.
+
+Top-k comparison: the selected sets must be equal, except that an entry whose
+oracle score lies within 1e-3 relative of the row's k-th oracle score may be
+swapped for another such entry (ties within fp32 rounding of the two
+summation orders).  Attention is compared on the rows whose sets are equal.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import long_context_sparse_compress_amd as csa
+import synth
+from oracle import attention as oa
+from oracle import compressor as oc
+from oracle import indexer as oi
+from oracle import topk as ot
+
+N_TOK, K, WIN = 256, 16, 128
+
+
+def _d(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def inputs(seed=0):
+    main = synth.compressor_inputs("tiny.main", 1, N_TOK, 512, 4, 0, seed=seed)
+    keyc = synth.compressor_inputs("tiny.key", 1, N_TOK, 128, 4, 0, seed=seed)
+    hca = synth.compressor_inputs("tiny.hca", 1, N_TOK, 512, 128, 0, seed=seed)
+    return dict(
+        main=main, keyc=keyc, hca=hca,
+        qi=synth.normal("tiny.qi", (1, N_TOK, 64, 128), var=1.0 / 128, seed=seed),
+        w=synth.uniform("tiny.w", (1, N_TOK, 64), seed=seed),
+        q=synth.normal("tiny.q", (1, N_TOK, 64, 512), seed=seed),
+        raw=synth.normal("tiny.raw", (1, N_TOK, 512), seed=seed),
+        sink=synth.normal("tiny.sink", (64,), seed=seed),
+    )
+
+
+def run_gpu(x):
+    m, kc, hc = x["main"], x["keyc"], x["hca"]
+    kv = csa.csa_compress(4, _d(m["Ca"]), _d(m["Za"]), _d(m["bias"]), _d(m["Cb"]), _d(m["Zb"]))
+    keys = csa.csa_compress(4, _d(kc["Ca"]), _d(kc["Za"]), _d(kc["bias"]), _d(kc["Cb"]), _d(kc["Zb"]))
+    scores = csa.lightning_index(_d(x["qi"]), _d(x["w"]), keys, q_pos0=0, score_dtype=torch.float32)
+    idx = csa.topk_select(scores, K, q_pos0=0)
+    out = csa.sparse_mqa_attn(_d(x["q"]), kv, idx, _d(x["raw"]), q_pos0=0, raw_pos0=0)
+    kvh = csa.csa_compress(128, _d(hc["Ca"]), _d(hc["Za"]), _d(hc["bias"]))
+    outh = csa.hca_attn(_d(x["q"]), kvh, _d(x["raw"]), q_pos0=0, raw_pos0=0, sink=_d(x["sink"]))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in
+            dict(kv=kv, keys=keys, scores=scores, idx=idx, out=out, kvh=kvh, outh=outh).items()}
+
+
+def run_oracle(x, rows=None):
+    m, kc, hc = x["main"], x["keyc"], x["hca"]
+    kv = oc.compress(m["Ca"], m["Za"], m["bias"], 4, m["Cb"], m["Zb"])
+    keys = oc.compress(kc["Ca"], kc["Za"], kc["bias"], 4, kc["Cb"], kc["Zb"])
+    scores = oi.index_scores(x["qi"], x["w"], keys, 0, 4)
+    stored = scores.astype(np.float32).astype(np.float64)
+    idx = ot.topk_select(stored, K, 0, 4)
+    out, _ = oa.sparse_mqa(x["q"], kv, idx, x["raw"], 0, 0, WIN, rows=rows)
+    kvh = oc.compress(hc["Ca"], hc["Za"], hc["bias"], 128)
+    outh, _ = oa.hca_attention(x["q"], kvh, x["raw"], 0, 0, x["sink"], ratio=128, rows=rows)
+    return dict(kv=kv, keys=keys, scores=scores, idx=idx, out=out, kvh=kvh, outh=outh)
+
+
+def compare(g, o, rows=None):
+    """Returns a dict of diagnostics; raises AssertionError on a mismatch."""
+    rows = list(range(N_TOK)) if rows is None else list(rows)
+    rep = {}
+    rep["kv"] = float(np.max(np.abs(g["kv"] - o["kv"])))
+    rep["keys"] = float(np.max(np.abs(g["keys"] - o["keys"])))
+    rep["kvh"] = float(np.max(np.abs(g["kvh"] - o["kvh"])))
+    assert rep["kv"] < 1e-4 and rep["keys"] < 1e-4 and rep["kvh"] < 1e-4, rep
+    sc_o, sc_g = o["scores"][0], g["scores"][0]
+    fin = np.isfinite(sc_o)
+    assert np.array_equal(fin, np.isfinite(sc_g))
+    rel = np.abs(sc_g[fin] - sc_o[fin]) / np.maximum(np.abs(sc_o[fin]), 1e-30)
+    rep["scores_max_rel"] = float(rel.max()) if rel.size else 0.0
+    assert np.all(np.abs(sc_g[fin] - sc_o[fin]) <= 1e-3 * np.abs(sc_o[fin]) + 1e-6), rep
+    same_rows = []
+    for t in range(N_TOK):
+        gs = set(int(s) for s in g["idx"][0, t] if s >= 0)
+        os_ = set(int(s) for s in o["idx"][0, t] if s >= 0)
+        if gs == os_:
+            same_rows.append(t)
+            continue
+        v = (t + 1) // 4
+        kth = np.sort(sc_o[t, :v])[::-1][K - 1]
+        band = np.abs(sc_o[t, :v] - kth) <= 1e-3 * abs(kth)
+        for s in gs ^ os_:
+            assert band[s], f"row {t}: entry {s} differs outside the tie band"
+    rep["topk_rows_equal"] = len(same_rows)
+    chk = [t for t in rows if t in set(same_rows)]
+    oi_rows = {t: i for i, t in enumerate(rows)}
+    errs = [np.max(np.abs(g["out"][0, t] - o["out"][0, oi_rows[t]])) for t in chk]
+    rep["attn_max_abs"] = float(max(errs)) if errs else 0.0
+    assert rep["attn_max_abs"] < 1e-4, rep
+    errh = [np.max(np.abs(g["outh"][0, t] - o["outh"][0, oi_rows[t]])) for t in rows]
+    rep["hca_max_abs"] = float(max(errh))
+    assert rep["hca_max_abs"] < 1e-4, rep
+    return rep

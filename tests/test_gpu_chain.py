@@ -1,0 +1,15 @@
+"""Chained parity on the tiny CSA prefill: compressor -> indexer -> Top-k ->
+sparse MQA (and C128A -> HCA), GPU chain against the oracle chain."""
+import pytest
+
+import chain
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_chain_all_rows():
+    x = chain.inputs()
+    g = chain.run_gpu(x)
+    o = chain.run_oracle(x)
+    rep = chain.compare(g, o)
+    assert rep["topk_rows_equal"] >= 250
