@@ -72,30 +72,28 @@ __device__ __forceinline__ void store_out(TO* p, const float* f) {
 }
 
 struct Online {
-  float m, s, y;
+  float m, s, y;   // running max (log2 domain), sum of weights, weighted content
 };
 
-__device__ __forceinline__ void online_push(Online& st, float l, float x) {
-  const float mn = fmaxf(st.m, l);
-  const float a = fast_exp2((st.m - mn) * kLog2e);   // st.m = -inf -> 0
-  const float b = fast_exp2((l - mn) * kLog2e);
-  st.s = st.s * a + b;
-  st.y = st.y * a + b * x;
-  st.m = mn;
-}
+// exp2 of a non-positive argument: v_exp_f32 directly.  A result below the
+// smallest normal flushes to zero instead of a denormal, an absolute change
+// of < 2^-126 to weights whose largest is 1.
+__device__ __forceinline__ float exp2_le0(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void online_merge(Online& st, const Online& o) {
   if (o.m == -INFINITY) return;
+  if (st.m == -INFINITY) { st = o; return; }
   const float mn = fmaxf(st.m, o.m);
-  const float a = fast_exp2((st.m - mn) * kLog2e);
-  const float b = fast_exp2((o.m - mn) * kLog2e);
+  const float a = exp2_le0(st.m - mn);
+  const float b = exp2_le0(o.m - mn);
   st.s = st.s * a + o.s * b;
   st.y = st.y * a + o.y * b;
   st.m = mn;
 }
 
 // One workgroup per (entry i, sequence b).  blockDim.x = CT * G with
-// CT = c / VEC channel threads and G row groups.
+// CT = c / VEC channel threads and G (a power of two) row groups; group g
+// owns window rows g, g + G, g + 2G, ...
 template <typename TI, typename TO, int RATIO>
 __global__ void __launch_bounds__(1024)
 compress_kernel(int64_t n_tok, int c, int64_t pos0,
@@ -106,6 +104,7 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 TO* __restrict__ out, int64_t out_stride, int G) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
+  constexpr int UC = 4;   // rows per chunk (all loads of a chunk in flight together)
   const int CT = c / VEC;
   const int tid = threadIdx.x;
   const int ct = tid % CT;
@@ -119,14 +118,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
   for (int v = 0; v < VEC; ++v) st[v] = Online{-INFINITY, 0.f, 0.f};
 
   const int64_t seq = b * n_tok * c;
-  // Rows handled by this group: r = g, g + G, ...  Loads of up to UNR rows are
-  // issued before any of them is consumed.
-  constexpr int UNR = (VEC == 8) ? 6 : 8;
-  for (int r0 = g; r0 < ROWS; r0 += G * UNR) {
-    uint4 zl[UNR], xl[UNR];    // raw 16-byte row slices; converted when consumed
-    bool have[UNR];
+  for (int r0 = g; r0 < ROWS; r0 += G * UC) {
+    uint4 zl[UC], xl[UC];    // raw 16-byte row slices; converted when consumed
+    bool have[UC];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+    for (int u = 0; u < UC; ++u) {
       const int r = r0 + u * G;
       have[u] = false;
       if (r >= ROWS) continue;
@@ -151,25 +147,53 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
         have[u] = true;
       }
     }
+    // logits of the chunk in the log2 domain, and their per-channel max
+    float lg[UC][VEC];
+    float cm[VEC];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+    for (int v = 0; v < VEC; ++v) cm[v] = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
       if (!have[u]) continue;
-      const int r = r0 + u * G;
-      const float* br = bias + static_cast<int64_t>(r) * c + ch0;
-      float zf[VEC], xf[VEC];
+      const float* br = bias + static_cast<int64_t>(r0 + u * G) * c + ch0;
+      float zf[VEC];
       load_vec<TI>(reinterpret_cast<const TI*>(&zl[u]), zf);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        lg[u][v] = (zf[v] + br[v]) * kLog2e;
+        cm[v] = fmaxf(cm[v], lg[u][v]);
+      }
+    }
+    // fold the chunk into the running state: one rescale per chunk, one exp per row
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      if (cm[v] > st[v].m) {
+        const float a = (st[v].m == -INFINITY) ? 0.f : exp2_le0(st[v].m - cm[v]);
+        st[v].s *= a;
+        st[v].y *= a;
+        st[v].m = cm[v];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
+      if (!have[u]) continue;
+      float xf[VEC];
       load_vec<TI>(reinterpret_cast<const TI*>(&xl[u]), xf);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) online_push(st[v], zf[v] + br[v], xf[v]);
+      for (int v = 0; v < VEC; ++v) {
+        const float p = exp2_le0(lg[u][v] - st[v].m);
+        st[v].s += p;
+        st[v].y = fmaf(p, xf[v], st[v].y);
+      }
     }
   }
 
-  // Merge the G row groups' states through LDS (group 0 keeps the result).
+  // Tree merge of the G row groups through LDS: at each level the upper half
+  // of the remaining groups hands its states to the lower half.
   extern __shared__ float smem[];
-  if (G > 1) {
-    float* sm = smem;                 // [G-1][3][c]
-    if (g > 0) {
-      float* base = sm + static_cast<int64_t>(g - 1) * 3 * c;
+  for (int half = G >> 1; half >= 1; half >>= 1) {
+    float* base = smem + static_cast<int64_t>(g - half) * 3 * c;
+    if (g >= half && g < 2 * half) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         base[ch0 + v] = st[v].m;
@@ -178,13 +202,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
       }
     }
     __syncthreads();
-    if (g == 0) {
-      for (int gg = 1; gg < G; ++gg) {
-        const float* base = sm + static_cast<int64_t>(gg - 1) * 3 * c;
+    if (g < half) {
+      const float* src = smem + static_cast<int64_t>(g) * 3 * c;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-          online_merge(st[v], Online{base[ch0 + v], base[c + ch0 + v], base[2 * c + ch0 + v]});
-      }
+      for (int v = 0; v < VEC; ++v)
+        online_merge(st[v], Online{src[ch0 + v], src[c + ch0 + v], src[2 * c + ch0 + v]});
     }
     __syncthreads();
   }
@@ -220,15 +242,14 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   const int CT = static_cast<int>(a.c / VEC);
-  // Few entries (decode) -> wide workgroups so that every row's loads of an
-  // entry are in flight at once; many entries -> 256 threads per entry.
+  // Few entries (decode) -> wide workgroups so that an entry's rows spread over
+  // all four SIMDs of a CU; many entries -> 256 threads per entry.
   const int64_t n_wg = (a.n_tok / RATIO) * a.B;
   const int max_threads = n_wg >= 1024 ? 256 : 1024;
-  int G = max_threads / CT;
-  if (G < 1) G = 1;
-  if (G > ROWS) G = ROWS;
+  int G = 1;
+  while (G * 2 * CT <= max_threads && G * 2 <= ROWS) G *= 2;
   const int threads = CT * G;
-  const size_t smem = (G > 1 ? static_cast<size_t>(G - 1) * 3 * a.c : 0) * sizeof(float) + 64;
+  const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64;
   const int64_t n_ent = a.n_tok / RATIO;
   dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B));
   const int64_t stride = a.out_batch_stride ? a.out_batch_stride : n_ent * a.c;

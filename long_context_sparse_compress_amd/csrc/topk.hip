@@ -30,6 +30,7 @@ namespace csa {
 namespace {
 
 constexpr int kBins = 2048;   // 11-bit digits
+constexpr int kRangeBins = 8192;   // direct histogram of a narrow 16-bit key range
 
 template <typename KT> struct Digits;
 template <> struct Digits<uint16_t> {
@@ -60,16 +61,22 @@ __device__ __forceinline__ KT load_key(const KT* row, int64_t i) {
 }
 
 // Find the digit whose bin holds the rem-th largest key (1-based), given the
-// digit histogram `hist` of nb bins.  Runs on wave 0; lane 0 of wave 0 writes
-// (digit, rem') to out[0..1] where rem' counts from the top of that bin.
+// digit histogram `hist` of nb <= 2048 bins (LDS or global).  Runs on wave 0:
+// each lane first loads its (at most 32) bins into registers, so the search
+// is a register scan, not a chain of dependent loads.  Lane L of wave 0
+// writes (digit, rem') to out[0..1] where rem' counts from the top of that bin.
 __device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32_t* out) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x >= 64) return;
   const int per = (nb + 63) / 64;
   const int lo = lane * per;
-  const int hi = lo + per < nb ? lo + per : nb;
+  uint32_t h[32];
   uint32_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += hist[i];
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    h[q] = (q < per && lo + q < nb) ? hist[lo + q] : 0u;
+    sum += h[q];
+  }
   // inclusive suffix sums over lanes: S[l] = sum over lanes >= l
   uint32_t S = sum;
 #pragma unroll
@@ -81,13 +88,15 @@ __device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32
   const int L = 63 - __clzll(static_cast<long long>(ball));   // highest lane with S >= rem
   if (lane == L) {
     uint32_t cum = S - sum;   // keys in higher lanes' bins
-    for (int i = hi - 1; i >= lo; --i) {
-      if (cum + hist[i] >= rem) {
-        out[0] = static_cast<uint32_t>(i);
+    bool found = false;
+#pragma unroll
+    for (int q = 31; q >= 0; --q) {
+      if (!found && q < per && cum + h[q] >= rem) {
+        out[0] = static_cast<uint32_t>(lo + q);
         out[1] = rem - cum;
-        break;
+        found = true;
       }
-      cum += hist[i];
+      cum += h[q];
     }
   }
 }
@@ -169,8 +178,8 @@ __global__ void __launch_bounds__(1024)
 topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT* __restrict__ scores,
                 int32_t* __restrict__ idx) {
   extern __shared__ uint8_t smem_raw[];
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw);           // kBins
-  uint32_t* tmp = hist + kBins;                                       // 32 words
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw);           // kRangeBins (>= kBins)
+  uint32_t* tmp = hist + kRangeBins;                                  // 32 words
   KT* keys = reinterpret_cast<KT*>(tmp + 32);
   const int64_t row = blockIdx.x;
   const int64_t t = row % T;
@@ -180,6 +189,10 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
   if (V <= k) {
     for (int i = tid; i < k; i += nt) out[i] = i < V ? i : -1;
     return;
+  }
+  if (tid == 0) {
+    tmp[24] = 0xffffffffu;
+    tmp[25] = 0u;
   }
   const KT* src = scores + row * N;
   constexpr int PER = 16 / sizeof(KT);
@@ -196,27 +209,88 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
     for (int64_t i = tid; i < V; i += nt) keys[i] = load_key(src, i);
   }
 
-  KT prefix = 0, mask = 0;
-  uint32_t rem = static_cast<uint32_t>(k);
-  for (int p = 0; p < Digits<KT>::n; ++p) {
-    const int sh = Digits<KT>::shift(p);
-    const int nb = 1 << Digits<KT>::bits(p);
-    for (int i = tid; i < nb; i += nt) hist[i] = 0;
-    __syncthreads();
-    for (int64_t base = 0; base < V; base += nt) {
-      const int64_t i = base + tid;
-      const KT kk = i < V ? keys[i] : KT(0);
-      hist_add(hist, (kk >> sh) & (nb - 1), i < V && (kk & mask) == prefix);
+  __syncthreads();   // every key (and tmp[24..25]) is in LDS
+  KT K;
+  uint32_t rem;
+  // Indexer scores span few distinct bf16 values: when the row's key range
+  // fits in kRangeBins, one exact histogram of (key - min) replaces the digit
+  // passes (and spreads the LDS atomics over many bins).
+  bool done = false;
+  if constexpr (sizeof(KT) == 2) {
+    uint32_t kmin = 0xffffu, kmax = 0u;
+    for (int64_t i = tid; i < V; i += nt) {
+      const uint32_t kk = keys[i];
+      kmin = kk < kmin ? kk : kmin;
+      kmax = kk > kmax ? kk : kmax;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(kmin, o, 64)));
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, o, 64)));
+    }
+    if ((tid & 63) == 0) {
+      atomicMin(&tmp[24], kmin);
+      atomicMax(&tmp[25], kmax);
     }
     __syncthreads();
-    resolve_digit(hist, nb, rem, tmp + 20);
-    __syncthreads();
-    prefix |= static_cast<KT>(tmp[20] << sh);
-    mask |= static_cast<KT>((nb - 1) << sh);
-    rem = tmp[21];
-    __syncthreads();
+    kmin = tmp[24];
+    kmax = tmp[25];
+    if (kmax - kmin < static_cast<uint32_t>(kRangeBins)) {
+      uint32_t* bins = hist;   // kRangeBins words
+      for (int i = tid; i < kRangeBins; i += nt) bins[i] = 0;
+      __syncthreads();
+      for (int64_t i = tid; i < V; i += nt) atomicAdd(&bins[keys[i] - kmin], 1u);
+      __syncthreads();
+      // each thread owns a contiguous run of bins; find the bin holding the k-th largest key
+      const int per = (kRangeBins + nt - 1) / nt;
+      const int b0 = tid * per;
+      uint32_t mine = 0;
+      for (int q = 0; q < per; ++q) mine += (b0 + q < kRangeBins) ? bins[b0 + q] : 0u;
+      uint32_t total;
+      // keys in bins above this thread's run = total - inclusive prefix
+      const uint32_t excl = block_exclusive_scan(mine, tmp, &total);
+      const uint32_t above = total - excl - mine;
+      if (above < static_cast<uint32_t>(k) && above + mine >= static_cast<uint32_t>(k)) {
+        uint32_t cum = above;
+        for (int q = per - 1; q >= 0; --q) {
+          const uint32_t h = (b0 + q < kRangeBins) ? bins[b0 + q] : 0u;
+          if (cum + h >= static_cast<uint32_t>(k)) {
+            tmp[20] = kmin + static_cast<uint32_t>(b0 + q);
+            tmp[21] = static_cast<uint32_t>(k) - cum;
+            break;
+          }
+          cum += h;
+        }
+      }
+      __syncthreads();
+      K = static_cast<KT>(tmp[20]);
+      rem = tmp[21];
+      done = true;
+    }
   }
-  const KT K = prefix;
+  if (!done) {
+    KT prefix = 0, mask = 0;
+    rem = static_cast<uint32_t>(k);
+    for (int p = 0; p < Digits<KT>::n; ++p) {
+      const int sh = Digits<KT>::shift(p);
+      const int nb = 1 << Digits<KT>::bits(p);
+      for (int i = tid; i < nb; i += nt) hist[i] = 0;
+      __syncthreads();
+      for (int64_t base = 0; base < V; base += nt) {
+        const int64_t i = base + tid;
+        const KT kk = i < V ? keys[i] : KT(0);
+        hist_add(hist, (kk >> sh) & (nb - 1), i < V && (kk & mask) == prefix);
+      }
+      __syncthreads();
+      resolve_digit(hist, nb, rem, tmp + 20);
+      __syncthreads();
+      prefix |= static_cast<KT>(tmp[20] << sh);
+      mask |= static_cast<KT>((nb - 1) << sh);
+      rem = tmp[21];
+      __syncthreads();
+    }
+    K = prefix;
+  }
 
   const int64_t chunk = (V + nt - 1) / nt;
   const int64_t lo = tid * chunk < V ? tid * chunk : V;
@@ -381,7 +455,7 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
   const KT* sc = static_cast<const KT*>(a.scores);
   const int64_t rows = a.B * a.T;
   if (topk_row_in_lds(a.N, a.score_dtype)) {
-    const size_t smem = (kBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
+    const size_t smem = (kRangeBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
     hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
                        a.N, a.q_pos0, a.ratio, a.k, sc, a.idx);
     return hipGetLastError();
