@@ -36,9 +36,17 @@ def flags() -> list[str]:
             "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  The indexer's epilogue takes ReLU of MFMA results,
+# which are never NaN for the finite inputs it accepts (NaN inputs are
+# unsupported): without NaN semantics fmaxf(x, 0) is one v_max_f32 instead of
+# a NaN-quieting canonicalize plus the max.  MFMA results are taken in VGPRs
+# (not AGPRs) because every one of them feeds VALU work straight away.
+EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

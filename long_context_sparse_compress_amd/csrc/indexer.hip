@@ -152,7 +152,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   int qsc[QPW][4];
   float wv[QPW][4][4];
   int64_t vis[QPW];
-  int64_t vis_max = 0;
+  int64_t vis_max = 0, vis_min = INT64_MAX;
 #pragma unroll
   for (int qi = 0; qi < QPW; ++qi) {
     int64_t t = t0 + qi;
@@ -161,6 +161,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     if (v > N) v = N;
     vis[qi] = (t0 + qi < T) ? v : 0;
     vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
+    if (t0 + qi < T) vis_min = vis[qi] < vis_min ? vis[qi] : vis_min;
     const int64_t qrow = (b * T + t) * kH;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -212,6 +213,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
       const int64_t et = eg + tt * 16;
       const int64_t e = et + col;
       if (et >= vis_max) continue;   // whole tile masked for every query (wave-uniform)
+      const bool partial = et + 16 > vis_min;   // some query sees only part of the tile
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
         float part = 0.f;
@@ -226,7 +228,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
         part *= kscale[cur][tt];
-        if (e >= vis[qi]) part = -INFINITY;
+        if (partial && e >= vis[qi]) part = -INFINITY;
         if (tt == g) keep[qi] = part;
       }
     }
@@ -267,7 +269,7 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
   // prefill: several queries per wave share each key tile (bf16 q fragments are
   // twice the size of fp8 ones, so two queries fit the register budget)
   if constexpr (QK == CSA_BF16) return launch_mfma<QK, 2, 8>(a, s);
-  else return launch_mfma<QK, 4, 8>(a, s);
+  else return launch_mfma<QK, 2, 8>(a, s);
 }
 
 }  // namespace
