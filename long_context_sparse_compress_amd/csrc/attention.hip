@@ -135,7 +135,10 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* tile, int n, int g, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ void __launch_bounds__(256, 2)
+#ifndef ATTN_WAVES_PER_SIMD
+#define ATTN_WAVES_PER_SIMD 2
+#endif
+__global__ void __launch_bounds__(256, ATTN_WAVES_PER_SIMD)
 attn_bf16_kernel(Params P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* tiles = smem;                                                    // [2][32][kKsStride]
@@ -144,6 +147,10 @@ attn_bf16_kernel(Params P) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
+  int hsrc[4];                                                 // lanes holding heads 4g..4g+3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hsrc[i] = (4 * g + i) << 2;
   const int64_t gq = blockIdx.x / P.splits;
   const int split = static_cast<int>(blockIdx.x % P.splits);
   const int64_t b = gq / P.T, t = gq % P.T;
@@ -198,14 +205,23 @@ attn_bf16_kernel(Params P) {
     const uint8_t* Ks = tiles + cur * kTileBytes;
     const uint32_t* rv = rvalid + cur * kTile;
 
-    // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1)
+    // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1); the operands of step
+    // s+1 are read from LDS while step s's MFMAs run
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* ka = Ks + j * kKsStride + g * 256;
+    uint4 a0 = *reinterpret_cast<const uint4*>(ka);
+    uint4 a1 = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(Ks + j * kKsStride + g * 256 + s * 16);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(Ks + (16 + j) * kKsStride + g * 256 + s * 16);
+      uint4 n0 = a0, n1 = a1;
+      if (s + 1 < 16) {
+        n0 = *reinterpret_cast<const uint4*>(ka + (s + 1) * 16);
+        n1 = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + (s + 1) * 16);
+      }
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s]), s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s]), s1, 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
     }
     float lg[8];
 #pragma unroll
@@ -216,8 +232,8 @@ attn_bf16_kernel(Params P) {
     float mt = lg[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, lg[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, lane_read(x16, mt));
+    mt = fmaxf(mt, lane_read(x32, mt));
     const float m_new = fmaxf(m_run, mt);
     const bool none = (m_new == -INFINITY);
     const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
@@ -232,7 +248,7 @@ attn_bf16_kernel(Params P) {
     if (__ballot(alpha != 1.f)) {   // some head's running max moved: rescale O
       float a4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, 64);
+      for (int i = 0; i < 4; ++i) a4[i] = lane_read(hsrc[i], alpha);
 #pragma unroll
       for (int n = 0; n < 32; ++n) {
         o[n][0] *= a4[0]; o[n][1] *= a4[1]; o[n][2] *= a4[2]; o[n][3] *= a4[3];
@@ -241,15 +257,19 @@ attn_bf16_kernel(Params P) {
     const uint4 pa = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
     const bf16x8 pav = as_bf16x8(pa);
+    bf16x8 vb = v_operand(Ks, 0, g, j);
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pav, v_operand(Ks, n, g, j), o[n], 0, 0, 0);
+    for (int n = 0; n < 32; ++n) {
+      const bf16x8 vn = (n + 1 < 32) ? v_operand(Ks, n + 1, g, j) : vb;
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pav, vb, o[n], 0, 0, 0);
+      vb = vn;
+    }
   }
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  l_tot += lane_read(x16, l_tot);
+  l_tot += lane_read(x32, l_tot);
   const int head_j = 16 * wid + j;
 
   if (P.splits == 1) {
@@ -265,7 +285,7 @@ attn_bf16_kernel(Params P) {
     if (P.lse && g == 0) P.lse[gq * kH + head_j] = kLn2 * (M + log2f(denom));
     float f4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f4[i] = __shfl(f, 4 * g + i, 64);
+    for (int i = 0; i < 4; ++i) f4[i] = lane_read(hsrc[i], f);
     uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + 16 * wid + 4 * g) * kD;
 #pragma unroll
     for (int n = 0; n < 32; ++n)

@@ -103,25 +103,38 @@ template <> struct Frag<CSA_MXFP4> {
   }
 };
 
+// C[mt] = A[mt] x B for the four 16-head blocks of one query against one
+// 16-entry key tile.  The four products are independent, so their MFMAs are
+// issued interleaved (k-step outer, head block inner): no MFMA waits on the
+// one before it.
 template <int QK>
-__device__ __forceinline__ f32x4 qk_tile(const Frag<QK>& a, const Frag<QK>& b, int sa, int sb) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void qk_tiles(const Frag<QK> (&a)[4], const Frag<QK>& b, const int (&sa)[4], int sb,
+                                         f32x4 (&c)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) c[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (QK == CSA_BF16) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.v[s]), as_bf16x8(b.v[s]), acc, 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[mt].v[s]), as_bf16x8(b.v[s]), c[mt], 0, 0, 0);
   } else if constexpr (QK == CSA_FP8_E4M3) {
-    const i32x8 av = {(int)a.v[0].x, (int)a.v[0].y, (int)a.v[0].z, (int)a.v[0].w,
-                      (int)a.v[1].x, (int)a.v[1].y, (int)a.v[1].z, (int)a.v[1].w};
     const i32x8 bv = {(int)b.v[0].x, (int)b.v[0].y, (int)b.v[0].z, (int)b.v[0].w,
                       (int)b.v[1].x, (int)b.v[1].y, (int)b.v[1].z, (int)b.v[1].w};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const i32x8 av = {(int)a[mt].v[0].x, (int)a[mt].v[0].y, (int)a[mt].v[0].z, (int)a[mt].v[0].w,
+                        (int)a[mt].v[1].x, (int)a[mt].v[1].y, (int)a[mt].v[1].z, (int)a[mt].v[1].w};
+      c[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c[mt], 0, 0, 0, 127, 0, 127);
+    }
   } else {
-    const i32x8 av = {(int)a.v[0].x, (int)a.v[0].y, (int)a.v[0].z, (int)a.v[0].w, 0, 0, 0, 0};
     const i32x8 bv = {(int)b.v[0].x, (int)b.v[0].y, (int)b.v[0].z, (int)b.v[0].w, 0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, sa, 0, sb);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const i32x8 av = {(int)a[mt].v[0].x, (int)a[mt].v[0].y, (int)a[mt].v[0].z, (int)a[mt].v[0].w, 0, 0, 0, 0};
+      c[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c[mt], 4, 4, 0, sa[mt], 0, sb);
+    }
   }
-  return acc;
 }
 
 __device__ __forceinline__ void store_score(float* p, float v) { *p = v; }
@@ -180,6 +193,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     }
   }
 
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   const int64_t krow0 = b * N;
   // Key fragments of one 64-entry group (4 tiles); the next group's loads are
   // issued before the current group's MFMAs.
@@ -199,7 +213,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     }
   };
   load_group(0, e_wave);
-#pragma unroll
+#pragma unroll 2
   for (int tg = 0; tg < TPW / 4; ++tg) {
     const int cur = tg & 1;
     const int64_t eg = e_wave + tg * 64;
@@ -214,19 +228,23 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
       const int64_t e = et + col;
       if (et >= vis_max) continue;   // whole tile masked for every query (wave-uniform)
       const bool partial = et + 16 > vis_min;   // some query sees only part of the tile
+      // all MFMAs of the tile first (every query, every head block), then the epilogues
+      f32x4 cc[QPW][4];
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) qk_tiles<QK>(qa[qi], kb[cur][tt], qsc[qi], ksc[cur][tt], cc[qi]);
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
         float part = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 c = qk_tile<QK>(qa[qi][mt], kb[cur][tt], qsc[qi][mt], ksc[cur][tt]);
+          const f32x4 c = cc[qi][mt];
           part = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), part);
           part = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), part);
           part = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), part);
           part = fmaf(wv[qi][mt][3], fmaxf(c[3], 0.f), part);
         }
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
+        part += lane_read(x16, part);
+        part += lane_read(x32, part);
         part *= kscale[cur][tt];
         if (partial && e >= vis[qi]) part = -INFINITY;
         if (tt == g) keep[qi] = part;
@@ -262,14 +280,15 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
 
 template <int QK>
 hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
+  // tiles per wave from a sweep on MI355X (decode: HBM streaming; prefill: the
+  // q prologue amortised over long entry runs)
   if (a.T <= 2) {   // decode: one query per wave, long entry runs
-    constexpr int TPW = (QK == CSA_MXFP4) ? 16 : 8;
+    constexpr int TPW = (QK == CSA_MXFP4) ? 8 : 32;
     return launch_mfma<QK, 1, TPW>(a, s);
   }
   // prefill: several queries per wave share each key tile (bf16 q fragments are
   // twice the size of fp8 ones, so two queries fit the register budget)
-  if constexpr (QK == CSA_BF16) return launch_mfma<QK, 2, 8>(a, s);
-  else return launch_mfma<QK, 2, 8>(a, s);
+  return launch_mfma<QK, 2, 64>(a, s);
 }
 
 }  // namespace
