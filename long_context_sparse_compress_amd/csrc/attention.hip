@@ -11,22 +11,27 @@
 // Both stages are one kernel that walks a per-query "list" of rows: first the
 // compressed slots (the Top-k indices, or entries 0..V(t)-1 for the dense
 // form), then the window's raw rows.  A workgroup owns one query (all 64
-// heads) and a contiguous run of 32-row tiles of that list; wave w owns heads
-// 16w..16w+15.
+// heads) and a contiguous run of 32-row tiles of that list; wave w computes
+// the logits and softmax of heads 16w..16w+15 and the output columns
+// 128w..128w+127 of every head.
 //
 // Per tile (bf16 path):
-//  * every thread loads 8 rows x 16 bytes (one 1 KB row per wave-wide load)
-//    for the next tile into registers while the current tile is computed;
-//  * the tile goes to LDS twice: row-major (padded rows) for S^T = K Q^T, and
-//    as 4 groups of 8 rows transposed to [d][8 rows] for P V -- an in-register
-//    8x8 transpose of bf16 makes that layout without scattered LDS writes;
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the wave's 16 heads' q in
-//    registers.  The C layout of S^T gives lane (head j, group g) the logits of
-//    rows {4g..4g+3, 16+4g..16+4g+3}; the P V MFMA takes exactly those rows as
-//    lane (j, g)'s K slice, so P goes from registers into the next MFMA with no
-//    data movement, as long as the transposed V groups use the same rows;
-//  * online softmax in the exp2 domain (logits pre-multiplied by log2 e);
-//  * O (16 heads x 512 fp32 per wave) stays in registers.
+//  * each wave copies 8 of the tile's rows straight from global memory into a
+//    row-major LDS tile (global_load_lds, 16 bytes per lane, no registers);
+//    later tiles are in flight while the current one is computed;
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, wave w taking heads
+//    16w..16w+15 with their q in registers.  The C layout of S^T gives lane
+//    (head j, group g) the logits of rows {4g..4g+3, 16+4g..16+4g+3};
+//  * online softmax in the exp2 domain (logits pre-multiplied by log2 e) on
+//    those registers.  Packed to bf16 they are already lane (j, g)'s slice of
+//    the A operand of P V for that head block, so each wave publishes them in
+//    LDS as one 16-byte word per lane, with its heads' rescale factors;
+//  * P V is split over the latent dimension instead of the heads: wave w
+//    computes O[all 64 heads, 128w..128w+127] from the four published P blocks
+//    and V columns it reads with transposing LDS reads (ds_read_b64_tr_b16)
+//    from the same row-major tile.  Each wave then reads a quarter of V
+//    instead of all of it, which cuts the tile's LDS reads by 30%;
+//  * O (64 heads x 128 columns fp32 per wave) stays in registers.
 // Decode has few queries, so a query's tiles are split over several
 // workgroups whose partial (max, sum, O) go to the workspace; a combine
 // kernel merges them in a fixed order (bit-reproducible results).
@@ -83,19 +88,34 @@ __device__ __forceinline__ List make_list(const Params& P, int64_t t) {
 }
 
 // Address of list row `p` of query (b, t), or nullptr for padding / past the end.
-// `sidx` (optional) is the query's Top-k row already staged in LDS.
-template <typename E>
-__device__ __forceinline__ const E* row_ptr(const Params& P, int64_t b, int64_t t, const List& l, int64_t p,
-                                            const int32_t* sidx = nullptr) {
+// The Top-k slot is read with `slot(p)`: from global memory, or from the
+// query's Top-k row staged in LDS.
+template <typename E, typename Slot>
+__device__ __forceinline__ const E* row_ptr_by(const Params& P, int64_t b, const List& l, int64_t p, Slot slot) {
   if (p >= l.L) return nullptr;
   if (p < l.n_cmp) {
-    int64_t e = p;
-    if (P.idx) e = sidx ? sidx[p] : P.idx[(b * P.T + t) * P.k + p];
+    const int64_t e = P.idx ? static_cast<int64_t>(slot(p)) : p;
     if (e < 0 || e >= P.N) return nullptr;
     return static_cast<const E*>(P.kv_cmp) + (b * P.N + e) * kD;
   }
   const int64_t u = l.wstart + (p - l.n_cmp) - P.raw_pos0;
   return static_cast<const E*>(P.kv_raw) + (b * P.n_raw + u) * kD;
+}
+
+template <typename E>
+__device__ __forceinline__ const E* row_ptr(const Params& P, int64_t b, int64_t t, const List& l, int64_t p) {
+  const int32_t* idx = P.idx + (b * P.T + t) * P.k;
+  return row_ptr_by<E>(P, b, l, p, [&](int64_t q) { return idx[q]; });
+}
+
+// Whether list row `p` is a real row (row_ptr would not return nullptr).
+__device__ __forceinline__ bool row_valid(const Params& P, const List& l, int64_t p, const int32_t* sidx) {
+  if (p >= l.L) return false;
+  if (p < l.n_cmp && P.idx) {
+    const int32_t e = sidx[p];
+    return e >= 0 && e < P.N;
+  }
+  return true;
 }
 
 __device__ __forceinline__ void split_range(const Params& P, const List& l, int split, int64_t& t0,
@@ -125,32 +145,45 @@ __device__ __forceinline__ void row_to_lds(const uint16_t* src_row, uint8_t* dst
 // transposed from the row-major tile: within a 16-lane group, lane k points at
 // row base + k/4, columns 4(k%4)..4(k%4)+3 of the 16-column block; the
 // transposing read hands lane j column j of rows base..base+3.
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* tile, int n, int g, int k) {
-  const uint8_t* p0 = tile + (4 * g + (k >> 2)) * kKsStride + (n * 16 + 4 * (k & 3)) * 2;
-  const uint8_t* p1 = p0 + 16 * kKsStride;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* tile, int n, uint32_t lane_off) {
+  const uint32_t off = lane_off + n * 32;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + off));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + (off + 16 * kKsStride)));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
-#ifndef ATTN_WAVES_PER_SIMD
-#define ATTN_WAVES_PER_SIMD 2
-#endif
-__global__ void __launch_bounds__(256, ATTN_WAVES_PER_SIMD)
-attn_bf16_kernel(Params P) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* tiles = smem;                                                    // [2][32][kKsStride]
-  uint32_t* rvalid = reinterpret_cast<uint32_t*>(smem + 2 * kTileBytes);    // [2][32]
-  int32_t* sidx = reinterpret_cast<int32_t*>(rvalid + 2 * kTile);           // [k] Top-k row of this query
+// Workgroup barrier that drains only this wave's LDS operations (the caller
+// has already waited for its row loads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(63 & 15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// Tile buffers: rows arrive by DMA in tb1; at the top of each step the landed
+// tile is copied into tb0, where it is computed, and tb1 takes the next
+// tile's rows, requested one row at a time between the QK MFMAs.  Reads of
+// tb0 are then provably disjoint from the loads in flight (distinct arrays),
+// so the compiler does not make them wait for those loads.  A copy, not two
+// alternating buffers, keeps one copy of the loop body, which fits the 256
+// registers that two workgroups per CU allow.
+__global__ void __launch_bounds__(256, 2)
+attn_bf16_kernel(Params P) {
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
+  __shared__ int32_t sidx[CSA_MAX_TOPK];                                   // Top-k row of this query
+  __shared__ uint4 pshare[4 * 64];   // P of each wave's 16 heads, in MFMA operand order (lane-major)
+  __shared__ float4 ashare[kH / 4];  // per-head rescale factor of the current tile
+  __shared__ float4 fshare[kH / 4];  // per-head output factor (epilogue)
+  __shared__ uint4 rescale_any;      // per wave: some head's running max moved
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row addressing stays scalar
   const int j = lane & 15, g = lane >> 4;
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
-  int hsrc[4];                                                 // lanes holding heads 4g..4g+3
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hsrc[i] = (4 * g + i) << 2;
+  // transposing V reads: lane k of group g points at row 4g + k/4, columns 4(k%4)..
+  const uint32_t voff = (4 * g + (j >> 2)) * kKsStride + 8 * (j & 3);
   const int64_t gq = blockIdx.x / P.splits;
   const int split = static_cast<int>(blockIdx.x % P.splits);
   const int64_t b = gq / P.T, t = gq % P.T;
@@ -158,13 +191,29 @@ attn_bf16_kernel(Params P) {
   int64_t tile0, tile1;
   split_range(P, l, split, tile0, tile1);
 
-  // Stage the slice of this query's Top-k row that this workgroup's tiles use.
-  if (P.idx) {
-    const int64_t p0 = tile0 * kTile;
-    const int64_t p1 = tile1 * kTile < l.n_cmp ? tile1 * kTile : l.n_cmp;
-    const int32_t* src = P.idx + gq * P.k;
-    for (int64_t p = p0 + tid; p < p1; p += 256) sidx[p] = src[p];
-    __syncthreads();
+  // The query's own raw row is always in the list: padding rows load it (and are masked).
+  const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) +
+                             (b * P.n_raw + (P.q_pos0 + t - P.raw_pos0)) * kD;
+  // lane e (mod 8) of wave w: source of row 8w + e of `tile`
+  auto row_source = [&](int64_t tile, auto slot) -> uint64_t {
+    const uint16_t* p = row_ptr_by<uint16_t>(P, b, l, tile * kTile + 8 * wid + (lane & 7), slot);
+    return reinterpret_cast<uint64_t>(p ? p : safe_row);
+  };
+  // row 8w + e of a tile, from lane e's source, into tb1
+  auto issue_row = [&](uint64_t src, int e) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(src), e);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(src >> 32), e);
+    row_to_lds(reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo),
+               tb1 + (8 * wid + e) * kKsStride, lane);
+  };
+
+  // The first tile's rows go out before anything else, their indices read
+  // straight from global memory.
+  if (tile0 < tile1) {
+    const int32_t* gidx = P.idx ? P.idx + gq * P.k : nullptr;   // only read for a Top-k list
+    const uint64_t src = row_source(tile0, [&](int64_t q) { return gidx[q]; });
+#pragma unroll
+    for (int e = 0; e < 8; ++e) issue_row(src, e);
   }
 
   // q fragments of head 16*wid + j, d in [g*128, g*128+128)
@@ -176,58 +225,70 @@ attn_bf16_kernel(Params P) {
     for (int s = 0; s < 16; ++s) qf[s] = qp[s];
   }
 
+  // Stage the slice of this query's Top-k row that this workgroup's tiles use.
+  if (P.idx) {
+    const int64_t p0 = tile0 * kTile;
+    const int64_t p1 = tile1 * kTile < l.n_cmp ? tile1 * kTile : l.n_cmp;
+    const int32_t* src = P.idx + gq * P.k;
+    for (int64_t p = p0 + tid; p < p1; p += 256) sidx[p] = src[p];
+    __syncthreads();
+  }
+
+  // O for all 64 heads and d in [128 w, 128 w + 128): o[8 hb + db] holds heads
+  // 16 hb + 4g + i (i = 0..3), column 128 w + 16 db + j
   f32x4 o[32];
 #pragma unroll
   for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // The query's own raw row is always in the list: padding rows load it (and are masked).
-  const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) +
-                             (b * P.n_raw + (P.q_pos0 + t - P.raw_pos0)) * kD;
-  // wave w brings rows 8w..8w+7 of a tile
-  auto issue_tile = [&](int64_t tile, int buf) {
-    uint8_t* dst = tiles + buf * kTileBytes;
+  // one tile: wait for its rows (keeping later tiles in flight), refill the
+  // buffer freed by the previous tile, compute
+  auto step = [&](int64_t tile) {
+    const uint8_t* Ks = tb0;
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's rows landed in tb1
+    lds_barrier();   // nobody still reads tb0
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int r = 8 * wid + e;
-      const uint16_t* p = row_ptr<uint16_t>(P, b, t, l, tile * kTile + r, sidx);
-      row_to_lds(p ? p : safe_row, dst + r * kKsStride, lane);
-      if (lane == 0) rvalid[buf * kTile + r] = p != nullptr;
+      const int off = (8 * wid + e) * kKsStride + lane * 16;
+      *reinterpret_cast<uint4*>(tb0 + off) = *reinterpret_cast<const uint4*>(tb1 + off);
     }
-  };
+    lds_barrier();   // tb0 holds the tile; tb1 is free
+    const bool refill = tile + 1 < tile1;
+    const uint64_t nsrc = refill ? row_source(tile + 1, [&](int64_t q) { return sidx[q]; }) : 0;
 
-  if (tile0 < tile1) issue_tile(tile0, 0);
-  for (int64_t tile = tile0; tile < tile1; ++tile) {
-    const int cur = static_cast<int>((tile - tile0) & 1);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's row loads into `cur` have landed
-    __syncthreads();                 // ... and every wave's; nobody still reads `cur ^ 1`
-    if (tile + 1 < tile1) issue_tile(tile + 1, cur ^ 1);
-    const uint8_t* Ks = tiles + cur * kTileBytes;
-    const uint32_t* rv = rvalid + cur * kTile;
-
-    // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1); the operands of step
-    // s+1 are read from LDS while step s's MFMAs run
+    // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1).  LDS operands are read
+    // kPipe k-steps ahead through a register ring, so an MFMA never waits on
+    // the read issued just before it.
+    constexpr int kPipe = 2;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     const uint8_t* ka = Ks + j * kKsStride + g * 256;
-    uint4 a0 = *reinterpret_cast<const uint4*>(ka);
-    uint4 a1 = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride);
+    uint4 ra[kPipe][2];
+#pragma unroll
+    for (int d = 0; d < kPipe; ++d) {
+      ra[d][0] = *reinterpret_cast<const uint4*>(ka + d * 16);
+      ra[d][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + d * 16);
+    }
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      uint4 n0 = a0, n1 = a1;
-      if (s + 1 < 16) {
-        n0 = *reinterpret_cast<const uint4*>(ka + (s + 1) * 16);
-        n1 = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + (s + 1) * 16);
+      // the next tile's rows go out one at a time between MFMAs: a burst of
+      // row loads would stall this wave until the memory pipeline drains
+      if (refill && (s & 1) == 0) issue_row(nsrc, s / 2);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][0]), as_bf16x8(qf[s]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][1]), as_bf16x8(qf[s]), s1, 0, 0, 0);
+      if (s + kPipe < 16) {
+        ra[s % kPipe][0] = *reinterpret_cast<const uint4*>(ka + (s + kPipe) * 16);
+        ra[s % kPipe][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + (s + kPipe) * 16);
       }
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[s]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[s]), s1, 0, 0, 0);
-      a0 = n0;
-      a1 = n1;
     }
+    // rows of this lane: 4g+i (s0) and 16+4g+i (s1); padding rows are masked
+    // which of the tile's 32 rows are real: lane r (mod 32) tests row r
+    const uint32_t vrows =
+        static_cast<uint32_t>(__ballot(row_valid(P, l, tile * kTile + (lane & 31), sidx))) >> (4 * g);
     float lg[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[i] = rv[4 * g + i] ? s0[i] * P.scale_log2 : -INFINITY;
-      lg[4 + i] = rv[16 + 4 * g + i] ? s1[i] * P.scale_log2 : -INFINITY;
+      lg[i] = (vrows >> i) & 1 ? s0[i] * P.scale_log2 : -INFINITY;
+      lg[4 + i] = (vrows >> (16 + i)) & 1 ? s1[i] * P.scale_log2 : -INFINITY;
     }
     float mt = lg[0];
 #pragma unroll
@@ -245,26 +306,43 @@ attn_bf16_kernel(Params P) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (__ballot(alpha != 1.f)) {   // some head's running max moved: rescale O
-      float a4[4];
+    // hand this wave's P and rescale factors to the other waves
+    pshare[wid * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    if (g == 0) reinterpret_cast<float*>(ashare)[16 * wid + j] = alpha;
+    const bool moved = __ballot(alpha != 1.f) != 0;
+    if (lane == 0) reinterpret_cast<uint32_t*>(&rescale_any)[wid] = moved;
+    lds_barrier();
+
+    // O[:, 128 w .. 128 w + 127] = alpha O + P V over all 64 heads
+    const uint4 any = rescale_any;
+    if (any.x | any.y | any.z | any.w) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = lane_read(hsrc[i], alpha);
+      for (int hb = 0; hb < 4; ++hb) {
+        const float4 a4 = ashare[4 * hb + g];
 #pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        o[n][0] *= a4[0]; o[n][1] *= a4[1]; o[n][2] *= a4[2]; o[n][3] *= a4[3];
+        for (int db = 0; db < 8; ++db) {
+          o[8 * hb + db][0] *= a4.x; o[8 * hb + db][1] *= a4.y;
+          o[8 * hb + db][2] *= a4.z; o[8 * hb + db][3] *= a4.w;
+        }
       }
     }
-    const uint4 pa = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-    const bf16x8 pav = as_bf16x8(pa);
-    bf16x8 vb = v_operand(Ks, 0, g, j);
+    bf16x8 pf[4];
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const bf16x8 vn = (n + 1 < 32) ? v_operand(Ks, n + 1, g, j) : vb;
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pav, vb, o[n], 0, 0, 0);
-      vb = vn;
+    for (int hb = 0; hb < 4; ++hb) pf[hb] = as_bf16x8(pshare[hb * 64 + lane]);
+    bf16x8 vr[kPipe];
+#pragma unroll
+    for (int d = 0; d < kPipe; ++d) vr[d] = v_operand(Ks, 8 * wid + d, voff);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        o[8 * hb + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], vr[db % kPipe], o[8 * hb + db], 0, 0, 0);
+      if (db + kPipe < 8) vr[db % kPipe] = v_operand(Ks, 8 * wid + db + kPipe, voff);
     }
-  }
+  };
+
+  for (int64_t tile = tile0; tile < tile1; ++tile) step(tile);
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
   float l_tot = l_run;
@@ -281,23 +359,33 @@ attn_bf16_kernel(Params P) {
     }
     const float em = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
     const float denom = l_tot * em + (P.sink ? fast_exp2(zl - M) : 0.f);
-    const float f = em / denom;
-    if (P.lse && g == 0) P.lse[gq * kH + head_j] = kLn2 * (M + log2f(denom));
-    float f4[4];
+    if (g == 0) {
+      reinterpret_cast<float*>(fshare)[head_j] = em / denom;
+      if (P.lse) P.lse[gq * kH + head_j] = kLn2 * (M + log2f(denom));
+    }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(P.out) + gq * kH * kD + 128 * wid + j;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f4[i] = lane_read(hsrc[i], f);
-    uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + 16 * wid + 4 * g) * kD;
+    for (int hb = 0; hb < 4; ++hb) {
+      const float4 f4 = fshare[4 * hb + g];
+      const float f[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[i * kD + n * 16 + j] = f32_to_bf16(o[n][i] * f4[i]);
+        for (int i = 0; i < 4; ++i)
+          out[(16 * hb + 4 * g + i) * kD + 16 * db] = f32_to_bf16(o[8 * hb + db][i] * f[i]);
+    }
   } else {
+    // partial O in the MFMA's own layout, 16 bytes per lane: [wave][hb][db][lane]
     float* w = P.ws + (gq * P.splits + split) * (kH * (kD + 2));
-    float* wo = w + (16 * wid + 4 * g) * kD;
+    float4* wo = reinterpret_cast<float4*>(w) + wid * (4 * 8 * 64) + lane;
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wo[i * kD + n * 16 + j] = o[n][i];
+      for (int db = 0; db < 8; ++db) {
+        const f32x4& v = o[8 * hb + db];
+        wo[(hb * 8 + db) * 64] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     if (g == 0) {
       w[kH * kD + head_j] = m_run;
       w[kH * kD + kH + head_j] = l_tot;
@@ -369,40 +457,76 @@ attn_f32_kernel(Params P) {
 }
 
 // ------------------------------------------------------------ split combine
-// One workgroup per (query, head); 128 threads x 4 dims.  Partials are merged
-// in split order.
-__global__ void __launch_bounds__(128)
+// One workgroup per (query, 16-head block hb, 128-column quarter w), which is
+// one contiguous 8 KB run of every split's partial O.  Partials are merged in
+// split order (bit-reproducible); the bf16 result goes through LDS so that
+// each output row is written in full 16-byte pieces.
+__global__ void __launch_bounds__(256)
 attn_combine_kernel(Params P) {
-  const int64_t gq = blockIdx.x / kH;
-  const int h = static_cast<int>(blockIdx.x % kH);
-  const int S = P.splits;
-  const float* base = P.ws + gq * S * (kH * (kD + 2));
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * (kH * (kD + 2)) + kH * kD + h]);
-  float zl = -INFINITY;
-  if (P.sink) {
-    zl = P.sink[h] * kLog2e;
-    M = fmaxf(M, zl);
+  __shared__ __attribute__((aligned(16))) float wgt[kMaxSplits * 16];   // weight of split s for head 16 hb + h
+  __shared__ __attribute__((aligned(16))) float inv[16];                // 1 / softmax denominator per head
+  __shared__ __attribute__((aligned(16))) uint16_t ot[16 * 128];
+  const int64_t gq = blockIdx.x / 16;
+  const int hb = static_cast<int>(blockIdx.x / 4 % 4), w = static_cast<int>(blockIdx.x % 4);
+  const int S = P.splits, tid = threadIdx.x;
+  constexpr int64_t kSplitFloats = kH * (kD + 2);
+  const float* base = P.ws + gq * S * kSplitFloats;
+  if (tid < 16) {
+    // every split's (max, sum) of this head first, all loads in flight at once
+    const int h = 16 * hb + tid;
+    float mv[kMaxSplits], lv[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      mv[s] = s < S ? base[s * kSplitFloats + kH * kD + h] : -INFINITY;
+      lv[s] = s < S ? base[s * kSplitFloats + kH * kD + kH + h] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, mv[s]);
+    float zl = -INFINITY;
+    if (P.sink) {
+      zl = P.sink[h] * kLog2e;
+      M = fmaxf(M, zl);
+    }
+    float denom = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const float e = (mv[s] == -INFINITY) ? 0.f : fast_exp2(mv[s] - M);
+      wgt[s * 16 + tid] = e;
+      denom += lv[s] * e;
+    }
+    if (P.sink) denom += fast_exp2(zl - M);
+    inv[tid] = 1.f / denom;
+    if (P.lse && w == 0) P.lse[gq * kH + h] = kLn2 * (M + log2f(denom));
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float denom = 0.f;
-  const int d0 = threadIdx.x * 4;
+  __syncthreads();
+  // two float4 of the block per thread: d-block db, lane (j, g) of the producing wave
+  const int ln = tid & 63, g = ln >> 4, j = ln & 15, db0 = tid >> 6;
+  const float4* src = reinterpret_cast<const float4*>(base) + ((w * 4 + hb) * 8 + db0) * 64 + ln;
+  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
-    const float* w = base + s * (kH * (kD + 2));
-    const float ms = w[kH * kD + h];
-    const float e = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    denom += w[kH * kD + kH + h] * e;
-    const float4 v = *reinterpret_cast<const float4*>(w + h * kD + d0);
-    acc.x += v.x * e; acc.y += v.y * e; acc.z += v.z * e; acc.w += v.w * e;
+    const float4 v0 = src[s * (kSplitFloats / 4)];
+    const float4 v1 = src[s * (kSplitFloats / 4) + 4 * 64];   // d-block db0 + 4
+    const float4 e = *reinterpret_cast<const float4*>(wgt + s * 16 + 4 * g);
+    acc0.x += v0.x * e.x; acc0.y += v0.y * e.y; acc0.z += v0.z * e.z; acc0.w += v0.w * e.w;
+    acc1.x += v1.x * e.x; acc1.y += v1.y * e.y; acc1.z += v1.z * e.z; acc1.w += v1.w * e.w;
   }
-  if (P.sink) denom += fast_exp2(zl - M);
-  const float f = 1.f / denom;
-  uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + h) * kD + d0;
-  uint2 pk;
-  pk.x = pack_bf16x2(acc.x * f, acc.y * f);
-  pk.y = pack_bf16x2(acc.z * f, acc.w * f);
-  *reinterpret_cast<uint2*>(out) = pk;
-  if (P.lse && threadIdx.x == 0) P.lse[gq * kH + h] = kLn2 * (M + log2f(denom));
+  // heads 4g..4g+3 of the block, column 16 db + j of the quarter
+  const float4 f = *reinterpret_cast<const float4*>(inv + 4 * g);
+  const int c0 = 16 * db0 + j, c1 = c0 + 64;
+  ot[(4 * g + 0) * 128 + c0] = f32_to_bf16(acc0.x * f.x);
+  ot[(4 * g + 1) * 128 + c0] = f32_to_bf16(acc0.y * f.y);
+  ot[(4 * g + 2) * 128 + c0] = f32_to_bf16(acc0.z * f.z);
+  ot[(4 * g + 3) * 128 + c0] = f32_to_bf16(acc0.w * f.w);
+  ot[(4 * g + 0) * 128 + c1] = f32_to_bf16(acc1.x * f.x);
+  ot[(4 * g + 1) * 128 + c1] = f32_to_bf16(acc1.y * f.y);
+  ot[(4 * g + 2) * 128 + c1] = f32_to_bf16(acc1.z * f.z);
+  ot[(4 * g + 3) * 128 + c1] = f32_to_bf16(acc1.w * f.w);
+  __syncthreads();
+  const int r = tid >> 4, c = (tid & 15) * 8;
+  uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + 16 * hb + r) * kD + 128 * w + c;
+  *reinterpret_cast<uint4*>(out) = *reinterpret_cast<const uint4*>(ot + r * 128 + c);
 }
 
 }  // namespace
@@ -427,10 +551,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int64_t ncmp = a.idx ? a.k : (last + 1) / a.ratio;
   if (!a.idx && ncmp > a.N) ncmp = a.N;
   P.splits = attn_splits(a.B, a.T, ncmp + wlen);
-  const size_t smem = 2 * kTile * kKsStride + 2 * kTile * 4 + (a.idx ? a.k * 4 : 0);
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), smem, s, P);
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
   if (P.splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * kH)), dim3(128), 0, s, P);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
   return hipGetLastError();
 }
 
