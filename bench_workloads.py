@@ -14,6 +14,7 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
   csa_1m_decode  8 sequences at 1,048,576 context: C4A compress (KV and keys),
                  MXFP4 indexer over 262,144 keys, top-1024, sparse MQA
   c128a_1m       C128A compress of all 1,048,576 tokens (8,192 entries)
+  hbm_copy       a 1 GiB copy, the calibration point of the HBM byte counters
 """
 from __future__ import annotations
 
@@ -176,6 +177,15 @@ def run(args, torch, csa, synth):
                    ntok * 512 * 4 + ntok // 128 * 1024, 0, "hbm")]
         queries = 0
         info = dict(tokens=ntok, c128a_entries=ntok // 128)
+    elif wl == "hbm_copy":
+        # 1 GiB device-to-device copy: the reference point that turns the HBM
+        # traffic counters (FETCH_SIZE, WRITE_SIZE) into bytes
+        n = 1 << 28
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        stages = [("copy_1GiB", lambda: y.copy_(x), 2 * n * 4, 0, "hbm")]
+        queries = 0
+        info = dict(bytes_read=n * 4, bytes_written=n * 4)
     else:
         raise SystemExit(f"unknown workload {wl}")
 
@@ -205,11 +215,16 @@ def run(args, torch, csa, synth):
             best = (name, t, roof, nbytes)
     name, t, roof, nbytes = best
     roof = dict(roof, kernel=name, traffic=None, avg_launch_us=round(t * 1e3, 2), algorithmic_bytes_per_launch=nbytes)
-    value = queries / (ms * 1e-3) if queries else (1048576 / (ms * 1e-3))
+    if wl == "hbm_copy":
+        value, unit = nbytes / (ms * 1e-3) / 1e9, "GB/s"
+    elif queries:
+        value, unit = queries / (ms * 1e-3), "query-tokens/s"
+    else:
+        value, unit = 1048576 / (ms * 1e-3), "raw-tokens/s"
     return {
         "metric": "CSA/HCA query-tokens/s at 1 GPU; % peak HBM GB/s (decode), % MFMA (prefill)",
         "value": round(value, 1),
-        "unit": "query-tokens/s" if queries else "raw-tokens/s",
+        "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": dict(workload=wl, **info, timing="hip_graph"),
