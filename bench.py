@@ -212,6 +212,26 @@ def cpu_oracle_decode(step, torch, budget_s):
                       f"top-{step.k}, sparse MQA, C128A compressor and HCA attention; {el:.1f} s"}
 
 
+def index_traffic():
+    """HBM bytes per lightning_index launch from the committed counter runs
+    (profiles/lightning_index_decode_traffic.md), or None once the kernel's
+    sources differ from the ones the counters were taken on."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(here, "profiles", "lightning_index_decode_traffic.md")).read()
+        rec = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line and "`" not in line)
+        h = hashlib.sha256()
+        for rel in ("csrc/indexer.hip", "csrc/device.h", "build.py"):
+            with open(os.path.join(here, "long_context_sparse_compress_amd", rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"].strip():
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ---------------------------------------------------------------- timing
 
 
@@ -334,7 +354,7 @@ def main():
                    "index_dim": 128, "cache_copies_rotated": args.rotate,
                    "timing": "eager" if args.eager else "hip_graph"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": index_traffic(),
                      "algorithmic_bytes_per_launch": alg[dom]["bytes"], "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "stages": stages,
