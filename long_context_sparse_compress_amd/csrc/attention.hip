@@ -145,6 +145,9 @@ __device__ __forceinline__ void row_to_lds(const uint16_t* src_row, uint8_t* dst
 // transposed from the row-major tile: within a 16-lane group, lane k points at
 // row base + k/4, columns 4(k%4)..4(k%4)+3 of the 16-column block; the
 // transposing read hands lane j column j of rows base..base+3.
+// Both addresses are formed as tile + one offset: a deeper chain of pointer
+// arithmetic can lose the record of which LDS array a read touches, and the
+// compiler then waits for every row load in flight before that read.
 __device__ __forceinline__ bf16x8 v_operand(const uint8_t* tile, int n, uint32_t lane_off) {
   const uint32_t off = lane_off + n * 32;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + off));
