@@ -100,6 +100,8 @@ class DecodeStep:
         self.ws_topk = self._ws(csa.OP_TOPK, N4, k)
         self.ws_attn = self._ws(csa.OP_SPARSE_ATTN, N4, k)
         self.ws_hca = self._ws(csa.OP_HCA_ATTN, N128, 0)
+        n = csa.workspace_bytes(csa.OP_COMPRESS, B, 128, 512, 128)
+        self.ws_c128 = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
 
     def _ws(self, op, N, k):
         n = self.csa.workspace_bytes(op, self.B, 1, N, k)
@@ -124,7 +126,7 @@ class DecodeStep:
                 workspace=self.ws_attn)),
             ("compress_c128a_kv", lambda: csa.csa_compress(
                 128, c128["Ca"], c128["Za"], self.b128, pos0=self.ctx - 128, out=self.kvh[r],
-                cache_entry0=self.N128 - 1)),
+                cache_entry0=self.N128 - 1, workspace=self.ws_c128)),
             ("hca_attn", lambda: csa.hca_attn(
                 self.qh, self.kvh[r], self.rawh, q_pos0=self.t, raw_pos0=self.raw0, sink=self.sink,
                 out=self.outh, workspace=self.ws_hca)),

@@ -120,10 +120,12 @@ def run(args, torch, csa, synth):
         sink = dn("h.sink", (64,))
         out = torch.empty_like(q)
         ws = torch.empty(max(16, csa.workspace_bytes(csa.OP_HCA_ATTN, B, T, N, 0)), dtype=torch.uint8, device="cuda")
+        wsc = torch.empty(max(16, csa.workspace_bytes(csa.OP_COMPRESS, B, ntok, 512, 128)), dtype=torch.uint8,
+                          device="cuda")
         rows = sum(min((q0 + t + 1) // 128, N) + 128 for t in range(T))
         stages = [
             ("compress_c128a_kv", lambda: csa.csa_compress(128, c["Ca"], c["Za"], b128, pos0=cpos, out=kv,
-                                                           cache_entry0=cpos // 128),
+                                                           cache_entry0=cpos // 128, workspace=wsc),
              B * ntok * 512 * 4 + B * ntok // 128 * 1024, 0, "hbm"),
             ("hca_attn", lambda: csa.hca_attn(q, kv, raw, q_pos0=q0, raw_pos0=raw0, sink=sink, out=out, workspace=ws),
              (B * rows * 1024 if dec else (N + raw.shape[1]) * 1024) + B * T * 2 * 64 * 512 * 2,

@@ -110,13 +110,21 @@ extern "C" {
  *                  (elements); out_batch_stride 0 means (n_tok/ratio)*c.
  *                  This lets a decode step write straight into a cache slot.
  *  c               a multiple of 64, at most 1024.
+ *  workspace / ws_bytes: optional device scratch (the caller owns it; its
+ *                  contents need no initialisation and are not preserved).
+ *                  With at least csa_workspace_bytes(CSA_OP_COMPRESS, B,
+ *                  n_tok, c, ratio) bytes, a C128A call with few entries
+ *                  spreads each entry's rows over several workgroups and
+ *                  merges their partial states; with less (e.g. 0 and NULL)
+ *                  every entry is pooled by one workgroup.  Same results up
+ *                  to floating-point rounding order.
  */
 int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                  const void* Ca, const void* Za, const void* Cb, const void* Zb,
                  const void* prev_Cb, const void* prev_Zb,
                  const float* bias, const float* gamma, float eps,
                  int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
-                 void* stream);
+                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * lightning_index -- stage 2, the lightning indexer.
@@ -214,7 +222,9 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
 
 /* Workspace bytes the named operation needs for these sizes (0 if none).
  * For the two attention operations the need depends only on B and T; N and
- * k are accepted for symmetry.  Returns 0 for an unknown op. */
+ * k are accepted for symmetry.  For CSA_OP_COMPRESS the arguments are
+ * (B, n_tok, c, ratio) and the figure is what enables the row split.
+ * Returns 0 for an unknown op. */
 size_t csa_workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int k);
 
 /* Message for the last non-OK return on this thread ("" if none). */

@@ -29,7 +29,7 @@ _i64, _int, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctype
 
 _SIGS = {
     "csa_compress": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
-                     _int, _int, _vp, _i64, _vp],
+                     _int, _int, _vp, _i64, _vp, _sz, _vp],
     "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
                         _vp, _int, _vp],
     "topk_select": [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
@@ -111,12 +111,14 @@ def _workspace(op, B, T, N, k, device, workspace):
 
 
 def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
-                 gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, stream=None):
+                 gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, workspace=None,
+                 stream=None):
     """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c].
 
     With ``cache_entry0`` set, ``out`` is a [B, N_cache, c] cache and the new
     entries are written in place at entries cache_entry0 .. cache_entry0 +
-    n_tok//ratio - 1 of every sequence."""
+    n_tok//ratio - 1 of every sequence.  ``workspace`` defaults to a fresh
+    buffer of the size that enables the row split; an empty tensor disables it."""
     B, n_tok, c = Ca.shape
     n_ent = n_tok // ratio
     in_dt = _dt(Ca)
@@ -134,9 +136,10 @@ def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=No
             raise ValueError("cache slot out of range")
         optr = _ptr(out) + cache_entry0 * c * out.element_size()
         stride = out.shape[1] * c
+    ws, wsb = _workspace(OP_COMPRESS, B, n_tok, c, ratio, Ca.device, workspace)
     st = library().csa_compress(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
                                 _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
-                                _dt(out), optr, stride, _stream(stream))
+                                _dt(out), optr, stride, _ptr(ws), wsb, _stream(stream))
     _check(st, "csa_compress")
     return out
 

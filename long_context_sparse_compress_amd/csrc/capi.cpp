@@ -35,12 +35,13 @@ extern "C" {
 int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
                  const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
                  const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
-                 int out_dtype, void* out, int64_t out_batch_stride, void* stream) {
+                 int out_dtype, void* out, int64_t out_batch_stride, void* workspace, size_t ws_bytes,
+                 void* stream) {
   csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
-                                      gamma, eps, in_dtype, out_dtype, out, out_batch_stride);
+                                      gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes);
   if (!ck.ok()) return finish(ck);
   csa::CompressArgs a{ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb,
-                      bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride};
+                      bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes};
   return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
 }
 

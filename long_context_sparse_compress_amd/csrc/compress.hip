@@ -17,6 +17,7 @@
 //    block-wide reduction over channels.
 #include "device.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace csa {
 namespace {
@@ -71,6 +72,8 @@ __device__ __forceinline__ void store_out(TO* p, const float* f) {
   }
 }
 
+constexpr int kChunkRows = 4;   // rows per thread whose loads are in flight together
+
 struct Online {
   float m, s, y;   // running max (log2 domain), sum of weights, weighted content
 };
@@ -91,20 +94,24 @@ __device__ __forceinline__ void online_merge(Online& st, const Online& o) {
   st.m = mn;
 }
 
-// One workgroup per (entry i, sequence b).  blockDim.x = CT * G with
-// CT = c / VEC channel threads and G (a power of two) row groups; group g
-// owns window rows g, g + G, g + 2G, ...
-template <typename TI, typename TO, int RATIO>
+// One workgroup per (entry i, sequence b) -- or, with SPLIT, per (entry,
+// sequence, row range z) when there are too few entries to fill the chip.
+// blockDim.x = CT * G with CT = c / VEC channel threads and G (a power of
+// two) row groups; group g owns rows rlo + g, rlo + g + G, ... of the range.
+// Every row slot of a chunk is loaded unconditionally (a missing row reads a
+// harmless in-range address and is masked), so all loads of a chunk,
+// including its bias rows, are in flight together.
+template <typename TI, typename TO, int RATIO, bool SPLIT>
 __global__ void __launch_bounds__(1024)
 compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ Ca, const TI* __restrict__ Za,
                 const TI* __restrict__ Cb, const TI* __restrict__ Zb,
                 const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                 const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
-                TO* __restrict__ out, int64_t out_stride, int G) {
+                TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
-  constexpr int UC = 4;   // rows per chunk (all loads of a chunk in flight together)
+  constexpr int UC = kChunkRows;
   const int CT = c / VEC;
   const int tid = threadIdx.x;
   const int ct = tid % CT;
@@ -112,40 +119,61 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
   const int64_t i = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int ch0 = ct * VEC;
+  const int rows_per = ROWS / static_cast<int>(gridDim.z);
+  const int rlo = static_cast<int>(blockIdx.z) * rows_per, rhi = rlo + rows_per;
+
+  float gm[VEC];   // RMSNorm gain, fetched while the rows load
+  if (!SPLIT && g == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 q = gamma ? *reinterpret_cast<const float4*>(gamma + ch0 + v) : make_float4(1.f, 1.f, 1.f, 1.f);
+      gm[v] = q.x; gm[v + 1] = q.y; gm[v + 2] = q.z; gm[v + 3] = q.w;
+    }
+  }
 
   Online st[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) st[v] = Online{-INFINITY, 0.f, 0.f};
 
   const int64_t seq = b * n_tok * c;
-  for (int r0 = g; r0 < ROWS; r0 += G * UC) {
+  for (int r0 = rlo + g; r0 < rhi; r0 += G * UC) {
     uint4 zl[UC], xl[UC];    // raw 16-byte row slices; converted when consumed
+    float bl[UC][VEC];
     bool have[UC];
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
       const int r = r0 + u * G;
-      have[u] = false;
-      if (r >= ROWS) continue;
-      const TI* zp = nullptr;
-      const TI* xp = nullptr;
-      if (RATIO == 128 || r < 4) {
-        const int64_t tok = i * RATIO + r;
+      const bool in = r < rhi;
+      const int rr = in ? r : rlo;
+      const TI* zp;
+      const TI* xp;
+      bool ok = true;
+      if constexpr (RATIO == 128) {
+        const int64_t tok = i * RATIO + rr;
         zp = Za + seq + tok * c + ch0;
         xp = Ca + seq + tok * c + ch0;
-      } else if (i > 0) {
-        const int64_t tok = i * 4 - 4 + (r - 4);
-        zp = Zb + seq + tok * c + ch0;
-        xp = Cb + seq + tok * c + ch0;
-      } else if (pos0 > 0) {
-        const int64_t off = (b * 4 + (r - 4)) * c + ch0;
-        zp = pZb + off;
-        xp = pCb + off;
+      } else {
+        // rows 0..3: the current block; 4..7: the block before it, from
+        // this chunk (i > 0), from prev_* (i == 0, pos0 > 0) or absent
+        const bool cur = rr < 4;
+        const int64_t tok = cur ? i * 4 + rr : i * 4 - 4 + (rr - 4);
+        const bool here = cur || i > 0;
+        const int64_t off = (b * 4 + (rr & 3)) * c + ch0;
+        ok = here || pos0 > 0;
+        const TI* zs = cur ? Za : Zb;
+        const TI* xs = cur ? Ca : Cb;
+        zp = here ? zs + seq + tok * c + ch0 : (pos0 > 0 ? pZb + off : Za + seq + ch0);
+        xp = here ? xs + seq + tok * c + ch0 : (pos0 > 0 ? pCb + off : Ca + seq + ch0);
       }
-      if (zp) {
-        zl[u] = *reinterpret_cast<const uint4*>(zp);
-        xl[u] = *reinterpret_cast<const uint4*>(xp);
-        have[u] = true;
+      zl[u] = *reinterpret_cast<const uint4*>(zp);
+      xl[u] = *reinterpret_cast<const uint4*>(xp);
+      const float* br = bias + static_cast<int64_t>(rr) * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(br + v);
+        bl[u][v] = q.x; bl[u][v + 1] = q.y; bl[u][v + 2] = q.z; bl[u][v + 3] = q.w;
       }
+      have[u] = in && ok;
     }
     // logits of the chunk in the log2 domain, and their per-channel max
     float lg[UC][VEC];
@@ -154,13 +182,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
     for (int v = 0; v < VEC; ++v) cm[v] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
-      if (!have[u]) continue;
-      const float* br = bias + static_cast<int64_t>(r0 + u * G) * c + ch0;
       float zf[VEC];
       load_vec<TI>(reinterpret_cast<const TI*>(&zl[u]), zf);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        lg[u][v] = (zf[v] + br[v]) * kLog2e;
+        lg[u][v] = have[u] ? (zf[v] + bl[u][v]) * kLog2e : -INFINITY;
         cm[v] = fmaxf(cm[v], lg[u][v]);
       }
     }
@@ -176,12 +202,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
     }
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
-      if (!have[u]) continue;
       float xf[VEC];
       load_vec<TI>(reinterpret_cast<const TI*>(&xl[u]), xf);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        const float p = exp2_le0(lg[u][v] - st[v].m);
+        const float p = have[u] ? exp2_le0(lg[u][v] - st[v].m) : 0.f;
         st[v].s += p;
         st[v].y = fmaf(p, xf[v], st[v].y);
       }
@@ -211,6 +236,21 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
     __syncthreads();
   }
 
+  if constexpr (SPLIT) {
+    // this row range's state, [entry][range][m | s | y][c], merged by compress_merge_kernel
+    if (g == 0) {
+      const int64_t n_ent = n_tok / RATIO;
+      float* pp = part + ((b * n_ent + i) * gridDim.z + blockIdx.z) * 3 * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        pp[v] = st[v].m;
+        pp[c + v] = st[v].s;
+        pp[2 * c + v] = st[v].y;
+      }
+    }
+    return;
+  }
+
   // RMSNorm over the c channels (group 0 threads hold them all).
   float y[VEC];
   float ss = 0.f;
@@ -233,8 +273,51 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
   const float inv = rsqrtf(tot / static_cast<float>(c) + eps);
   float o[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * (gamma ? gamma[ch0 + v] : 1.f);
+  for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * gm[v];
   store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
+}
+
+// Merge of the row-range states of one (entry, sequence), then RMSNorm.  One
+// workgroup of c threads (one channel each) per (entry, sequence); all P
+// states of a channel are loaded before any arithmetic, then combined in
+// range order against their common maximum.
+template <typename TO>
+__global__ void __launch_bounds__(1024)
+compress_merge_kernel(int64_t n_ent, int c, int P, const float* __restrict__ part,
+                      const float* __restrict__ gamma, float eps, TO* __restrict__ out, int64_t out_stride) {
+  constexpr int kMaxP = 16;
+  __shared__ float red[16];
+  const int ch = threadIdx.x;
+  const int64_t i = blockIdx.x, b = blockIdx.y;
+  const float* pp = part + (b * n_ent + i) * P * 3 * c + ch;
+  float m[kMaxP], sv[kMaxP], yv[kMaxP];
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) {
+    const bool in = p < P;
+    m[p] = in ? pp[static_cast<int64_t>(p) * 3 * c] : -INFINITY;
+    sv[p] = in ? pp[static_cast<int64_t>(p) * 3 * c + c] : 0.f;
+    yv[p] = in ? pp[static_cast<int64_t>(p) * 3 * c + 2 * c] : 0.f;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) M = fmaxf(M, m[p]);
+  float S = 0.f, Y = 0.f;
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) {
+    const float e = (m[p] == -INFINITY) ? 0.f : exp2_le0(m[p] - M);
+    S = fmaf(sv[p], e, S);
+    Y = fmaf(yv[p], e, Y);
+  }
+  const float y = Y / S;
+  float ss = wave_sum(y * y);
+  if ((ch & 63) == 0) red[ch / 64] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < (c + 63) / 64; ++w) tot += red[w];
+  const float o = y * rsqrtf(tot / static_cast<float>(c) + eps) * (gamma ? gamma[ch] : 1.f);
+  TO* dst = out + b * out_stride + i * c + ch;
+  if constexpr (sizeof(TO) == 4) *reinterpret_cast<float*>(dst) = o;
+  else *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(o);
 }
 
 template <typename TI, typename TO, int RATIO>
@@ -242,23 +325,44 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   const int CT = static_cast<int>(a.c / VEC);
-  // Few entries (decode) -> wide workgroups so that an entry's rows spread over
-  // all four SIMDs of a CU; many entries -> 256 threads per entry.
-  const int64_t n_wg = (a.n_tok / RATIO) * a.B;
-  const int max_threads = n_wg >= 1024 ? 256 : 1024;
+  const int64_t n_ent = a.n_tok / RATIO;
+  const int64_t n_wg = n_ent * a.B;
+  const int64_t stride = a.out_batch_stride ? a.out_batch_stride : n_ent * a.c;
+  const int P = compress_splits(RATIO, a.B, a.n_tok);
+  const bool split = P > 1 && a.ws_bytes >= compress_workspace_bytes(RATIO, a.B, a.n_tok, a.c);
+  // Row groups: enough that a thread holds at most one chunk of UC rows when
+  // the workgroups are few (latency), at most 256 threads per workgroup when
+  // they are many; never more groups than rows / UC.
+  constexpr int UC = kChunkRows;
+  const int rows = split ? ROWS / P : ROWS;
+  const int max_threads = (split ? n_wg * P : n_wg) >= 1024 ? 256 : 1024;
   int G = 1;
-  while (G * 2 * CT <= max_threads && G * 2 <= ROWS) G *= 2;
+  while (G * 2 * CT <= max_threads && G * 2 * UC <= rows) G *= 2;
   const int threads = CT * G;
   const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64;
-  const int64_t n_ent = a.n_tok / RATIO;
-  dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B));
-  const int64_t stride = a.out_batch_stride ? a.out_batch_stride : n_ent * a.c;
-  hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO>), grid, dim3(threads), smem, s, a.n_tok,
-                     static_cast<int>(a.c), a.pos0, static_cast<const TI*>(a.Ca),
-                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.Cb),
-                     static_cast<const TI*>(a.Zb), static_cast<const TI*>(a.prev_Cb),
-                     static_cast<const TI*>(a.prev_Zb), a.bias, a.gamma, a.eps,
-                     static_cast<TO*>(a.out), stride, G);
+  const auto* Ca = static_cast<const TI*>(a.Ca);
+  const auto* Za = static_cast<const TI*>(a.Za);
+  const auto* Cb = static_cast<const TI*>(a.Cb);
+  const auto* Zb = static_cast<const TI*>(a.Zb);
+  const auto* pCb = static_cast<const TI*>(a.prev_Cb);
+  const auto* pZb = static_cast<const TI*>(a.prev_Zb);
+  if constexpr (RATIO == 128) {
+    if (split) {
+      float* part = static_cast<float*>(a.ws);
+      const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), static_cast<uint32_t>(P));
+      hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, true>), grid, dim3(threads), smem, s, a.n_tok,
+                         static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
+                         static_cast<TO*>(a.out), stride, G, part);
+      hipLaunchKernelGGL((compress_merge_kernel<TO>), dim3(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B)),
+                         dim3(static_cast<uint32_t>(a.c)), 0, s, n_ent, static_cast<int>(a.c), P, part, a.gamma,
+                         a.eps, static_cast<TO*>(a.out), stride);
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), 1);
+  hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, false>), grid, dim3(threads), smem, s, a.n_tok,
+                     static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
+                     static_cast<TO*>(a.out), stride, G, nullptr);
   return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@ struct CompressArgs {
   int in_dtype, out_dtype;
   void* out;
   int64_t out_batch_stride;
+  void* ws;          // optional row-split workspace
+  size_t ws_bytes;
 };
 
 struct IndexArgs {

@@ -89,11 +89,30 @@ inline size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t N, int dtype) {
   return size_t(B) * size_t(T) * topk_row_ws_bytes();
 }
 
+// Compressor row split: a C128A call with few (entry, sequence) pairs spreads
+// each entry's 128 rows over P workgroups (P a power of two up to 16, about
+// 256 workgroups in all) and merges their partial states in a second kernel.
+inline int compress_splits(int ratio, int64_t B, int64_t n_tok) {
+  if (ratio != 128) return 1;
+  const int64_t n_wg = B * (n_tok / ratio);
+  if (n_wg <= 0 || n_wg >= 128) return 1;
+  int P = 16;
+  while (P > 2 && n_wg * P > 256) P /= 2;
+  return P;
+}
+
+// (m, s, y) per channel per row range, fp32.
+inline size_t compress_workspace_bytes(int ratio, int64_t B, int64_t n_tok, int64_t c) {
+  const int P = compress_splits(ratio, B, n_tok);
+  if (P <= 1) return 0;
+  return size_t(B) * size_t(n_tok / ratio) * size_t(P) * 3 * size_t(c) * sizeof(float);
+}
+
 inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                             const void* Ca, const void* Za, const void* Cb, const void* Zb,
                             const void* prev_Cb, const void* prev_Zb, const float* bias,
                             const float* gamma, float eps, int in_dtype, int out_dtype,
-                            const void* out, int64_t out_batch_stride) {
+                            const void* out, int64_t out_batch_stride, const void* ws, size_t ws_bytes) {
   Check k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (B < 0 || n_tok < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and n_tok must be >= 0"); return k; }
@@ -121,6 +140,8 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
     k.must_be_null(Cb, "Cb", "for ratio 128") && k.must_be_null(Zb, "Zb", "for ratio 128") &&
         k.must_be_null(prev_Cb, "prev_Cb", "for ratio 128") && k.must_be_null(prev_Zb, "prev_Zb", "for ratio 128");
   }
+  if (!k.ok()) return k;
+  if (ws_bytes > 0) k.ptr(ws, "workspace");   // optional: too small a workspace just means no split
   return k;
 }
 
@@ -229,6 +250,7 @@ inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos
 inline size_t workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int kk) {
   (void)kk;
   switch (op) {
+    case CSA_OP_COMPRESS: return compress_workspace_bytes(kk, B, T, N);   // (B, n_tok, c, ratio)
     case CSA_OP_TOPK: return topk_workspace_bytes(B, T, N, CSA_BF16) > topk_workspace_bytes(B, T, N, CSA_F32)
                                  ? topk_workspace_bytes(B, T, N, CSA_BF16) : topk_workspace_bytes(B, T, N, CSA_F32);
     case CSA_OP_SPARSE_ATTN:

@@ -46,13 +46,13 @@ def _err(lib):
 def test_compress_validation(lib):
     f = lib.csa_compress
     ok = dict(ratio=4, B=2, n_tok=8, c=512, pos0=0, Ca=A, Za=A, Cb=A, Zb=A, pCb=None, pZb=None,
-              bias=A, gamma=None, eps=1e-6, idt=1, odt=1, out=A, stride=0, s=None)
+              bias=A, gamma=None, eps=1e-6, idt=1, odt=1, out=A, stride=0, ws=None, wsb=0, s=None)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["ratio"], a["B"], a["n_tok"], a["c"], a["pos0"], a["Ca"], a["Za"], a["Cb"], a["Zb"],
                  a["pCb"], a["pZb"], a["bias"], a["gamma"], a["eps"], a["idt"], a["odt"], a["out"],
-                 a["stride"], a["s"])
+                 a["stride"], a["ws"], a["wsb"], a["s"])
 
     assert call(ratio=8) == -1 and "ratio" in _err(lib)
     assert call(Ca=None) == -1 and "Ca is NULL" in _err(lib)
@@ -65,6 +65,9 @@ def test_compress_validation(lib):
     assert call(eps=0.0) == -1 and "eps" in _err(lib)
     assert call(ratio=128, n_tok=256) == -1 and "Cb must be NULL" in _err(lib)
     assert call(stride=100) == -1
+    # the workspace is optional, but one that is declared must be a real, aligned buffer
+    assert call(ws=None, wsb=4096) == -1 and "workspace is NULL" in _err(lib)
+    assert call(ws=MIS, wsb=4096) == -1 and "aligned" in _err(lib)
     # nothing to do: succeeds without touching the GPU
     assert call(n_tok=3, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None) == 0
     assert call(B=0, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None) == 0
@@ -127,6 +130,11 @@ def test_workspace_query(lib):
     assert lib.csa_workspace_bytes(3, 1, 4096, 33792, 512) == 0     # prefill: no split
     assert lib.csa_workspace_bytes(4, 16, 1, 8192, 0) > 0           # decode: split rows
     assert lib.csa_workspace_bytes(99, 1, 1, 1, 1) == 0
+    # compressor (B, n_tok, c, ratio): C128A with few entries splits rows
+    assert lib.csa_workspace_bytes(0, 32, 128, 512, 128) == 32 * 8 * 3 * 512 * 4   # 8 ranges of 16 rows
+    assert lib.csa_workspace_bytes(0, 1, 128, 512, 128) == 16 * 3 * 512 * 4       # at most 16 ranges
+    assert lib.csa_workspace_bytes(0, 2048, 128, 512, 128) == 0                   # enough entries
+    assert lib.csa_workspace_bytes(0, 32, 128, 512, 4) == 0                       # C4A never splits
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="no g++")

@@ -16,7 +16,7 @@ from helpers import COMP_BF16_MAX_ABS, COMP_F32_MAX_ABS, dev, host, max_abs
 pytestmark = pytest.mark.gpu
 
 
-def _run(ratio, B, n_tok, c, pos0, dtype, out_dtype=None, prefix="cmp", gamma=False, eps=1e-6):
+def _run(ratio, B, n_tok, c, pos0, dtype, out_dtype=None, prefix="cmp", gamma=False, eps=1e-6, workspace=None):
     inp = synth.compressor_inputs(prefix, B, n_tok, c, ratio, pos0, dtype=dtype)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     odt = tdt if out_dtype is None else out_dtype
@@ -24,7 +24,7 @@ def _run(ratio, B, n_tok, c, pos0, dtype, out_dtype=None, prefix="cmp", gamma=Fa
     d = {k: dev(v, tdt if k != "bias" else torch.float32) for k, v in inp.items()}
     out = csa.csa_compress(ratio, d["Ca"], d["Za"], d["bias"], d.get("Cb"), d.get("Zb"),
                            d.get("prev_Cb"), d.get("prev_Zb"), pos0=pos0,
-                           gamma=None if g is None else dev(g), eps=eps, out_dtype=odt)
+                           gamma=None if g is None else dev(g), eps=eps, out_dtype=odt, workspace=workspace)
     torch.cuda.synchronize()
     ref = oc.compress(inp["Ca"], inp["Za"], inp["bias"], ratio, inp.get("Cb"), inp.get("Zb"),
                       inp.get("prev_Cb"), inp.get("prev_Zb"), pos0=pos0, gamma=g, eps=eps)
@@ -83,7 +83,7 @@ def test_decode_writes_into_cache_slot():
     st = csa.library().csa_compress(4, B, 4, c, 252, d["Ca"].data_ptr(), d["Za"].data_ptr(),
                                     d["Cb"].data_ptr(), d["Zb"].data_ptr(), d["prev_Cb"].data_ptr(),
                                     d["prev_Zb"].data_ptr(), d["bias"].data_ptr(), None, 1e-6,
-                                    csa.BF16, csa.BF16, slot.data_ptr(), N * c,
+                                    csa.BF16, csa.BF16, slot.data_ptr(), N * c, None, 0,
                                     torch.cuda.current_stream().cuda_stream)
     assert st == 0
     torch.cuda.synchronize()
@@ -93,6 +93,30 @@ def test_decode_writes_into_cache_slot():
     got = host(cache)
     assert max_abs(got[:, N - 1], ref[:, 0]) < COMP_BF16_MAX_ABS
     assert np.all(got[:, :N - 1] == 7.0)
+
+
+@pytest.mark.parametrize("B,n_tok,c,dtype", [
+    (32, 128, 512, "bf16"),    # the decode step: 32 entries, 8 row ranges of 16
+    (100, 128, 128, "f32"),    # 100 entries: 2 ranges of 64
+    (3, 384, 1024, "bf16"),    # 9 entries, widest channels: 16 ranges of 8
+])
+def test_c128a_row_split_matches_single_pass(B, n_tok, c, dtype):
+    """Few C128A entries: the row-split path (partial states merged by a second
+    kernel) and the one-workgroup-per-entry path both match the oracle."""
+    assert csa.workspace_bytes(csa.OP_COMPRESS, B, n_tok, c, 128) > 0
+    pos0 = 1048576 - n_tok
+    split, ref, _ = _run(128, B, n_tok, c, pos0, dtype, prefix=f"split{B}", gamma=True)
+    single, ref2, _ = _run(128, B, n_tok, c, pos0, dtype, prefix=f"split{B}", gamma=True,
+                           workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    assert np.array_equal(ref, ref2)
+    for got in (split, single):
+        if dtype == "f32":
+            assert max_abs(got, ref) < COMP_F32_MAX_ABS
+        else:
+            # gamma scales outputs past |x| ~ 1: allow one bf16 ulp of each value
+            # (2^-7 |x| bounds it) -- the fp32 result can sit on the other side
+            # of a rounding boundary from the oracle's
+            assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 ** -12)
 
 
 def test_deterministic():
