@@ -70,15 +70,18 @@ index_f32_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const float* _
 // ---------------------------------------------------------------- MFMA path
 template <int QK> struct Frag;
 
-// bf16: rows of 256 B; lane (r, g) holds bytes [64g, 64g+64) = 4 k-steps of 8.
+// bf16: rows of 256 B; for k-step i, lane (r, g) holds bytes [64i + 16g, +16),
+// so the four lanes of a row read 64 contiguous bytes per load instruction
+// (16 half cache lines per instruction, not 32 partial ones: about 15% more
+// read bandwidth on MI355X).
 template <> struct Frag<CSA_BF16> {
   static constexpr int kRowBytes = 256;
   static constexpr int kRegs = 4;  // uint4 per lane per 16-row tile
   uint4 v[kRegs];
   __device__ __forceinline__ void load(const uint8_t* row, int g) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + 64 * g);
+    const uint4* p = reinterpret_cast<const uint4*>(row + 16 * g);
 #pragma unroll
-    for (int i = 0; i < kRegs; ++i) v[i] = p[i];
+    for (int i = 0; i < kRegs; ++i) v[i] = p[4 * i];
   }
 };
 // fp8: rows of 128 B; lane (r, g) holds bytes [32g, 32g+32).
@@ -141,14 +144,18 @@ __device__ __forceinline__ void store_score(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_score(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
 // Grid: x = entry block of 4 * TPW * 16 entries (one TPW-tile run per wave),
-// y = block of QPW queries, z = sequence.  256 threads = 4 waves.
-template <int QK, int QPW, int TPW, typename TS>
-__global__ void __launch_bounds__(256)
+// y = block of QPW queries, z = sequence.  256 threads = 4 waves.  Keys are
+// loaded GT tiles (GT * 16 entries) at a time, one group ahead of the group
+// being computed; OCC is the number of waves per SIMD the register budget is
+// sized for (GT = 8 needs the whole register file: one wave per SIMD).
+template <int QK, int QPW, int TPW, int GT, int OCC, typename TS>
+__global__ void __launch_bounds__(256, OCC)
 index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
                   const void* __restrict__ k_scale, TS* __restrict__ scores) {
-  static_assert(TPW % 4 == 0, "tiles are stored four at a time");
+  static_assert(GT % 4 == 0 && TPW % GT == 0, "tiles are stored four at a time");
+  constexpr int KG = GT / 4;   // 4-tile score stores per group
   using F = Frag<QK>;
   constexpr int RB = F::kRowBytes;
   const int lane = threadIdx.x & 63;
@@ -158,6 +165,17 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   const int64_t b = blockIdx.z;
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * QPW;
   const int64_t e_wave = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * (TPW * 16);
+
+  // The workgroup's q rows go through LDS once (coalesced 16-byte loads)
+  // instead of every wave fetching its fragments from global memory.
+  __shared__ __attribute__((aligned(16))) uint8_t qs[QPW * kH * RB];
+  for (int o = threadIdx.x * 16; o < QPW * kH * RB; o += 256 * 16) {
+    const int qi = o / (kH * RB);
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    *reinterpret_cast<uint4*>(qs + o) = *reinterpret_cast<const uint4*>(q + (b * T + t) * kH * RB + o % (kH * RB));
+  }
+  __syncthreads();
   if (e_wave >= N) return;
 
   // q fragments and head weights of this wave's queries.
@@ -178,7 +196,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     const int64_t qrow = (b * T + t) * kH;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      qa[qi][mt].load(q + (qrow + mt * 16 + col) * RB, g);
+      qa[qi][mt].load(qs + (qi * kH + mt * 16 + col) * RB, g);
       if constexpr (QK == CSA_MXFP4)
         qsc[qi][mt] = static_cast<const uint8_t*>(q_scale)[(qrow + mt * 16 + col) * 4 + g];
       else
@@ -195,14 +213,14 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
 
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   const int64_t krow0 = b * N;
-  // Key fragments of one 64-entry group (4 tiles); the next group's loads are
-  // issued before the current group's MFMAs.
-  F kb[2][4];
-  int ksc[2][4];
-  float kscale[2][4];
+  // Key fragments of one group (GT tiles); the next group's loads are issued
+  // before the current group's MFMAs.
+  F kb[2][GT];
+  int ksc[2][GT];
+  float kscale[2][GT];
   auto load_group = [&](int slot, int64_t eg) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < GT; ++tt) {
       int64_t e = eg + tt * 16 + col;
       if (e >= N) e = N - 1;
       kb[slot][tt].load(k + (krow0 + e) * RB, g);
@@ -214,53 +232,61 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   };
   load_group(0, e_wave);
 #pragma unroll 2
-  for (int tg = 0; tg < TPW / 4; ++tg) {
+  for (int tg = 0; tg < TPW / GT; ++tg) {
     const int cur = tg & 1;
-    const int64_t eg = e_wave + tg * 64;
+    const int64_t eg = e_wave + tg * (GT * 16);
     if (eg >= N) break;
-    if (tg + 1 < TPW / 4 && eg + 64 < N) load_group(cur ^ 1, eg + 64);
-    float keep[QPW];
+    if (tg + 1 < TPW / GT && eg + GT * 16 < N) load_group(cur ^ 1, eg + GT * 16);
 #pragma unroll
-    for (int qi = 0; qi < QPW; ++qi) keep[qi] = -INFINITY;
+    for (int kg = 0; kg < KG; ++kg) {
+      // four tiles: each lane's 16 head values reduced in registers, then one
+      // reduce-scatter over the four lane groups (three lane exchanges for
+      // four tiles) leaves lane group g with the score of tile g
+      float part[QPW][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int64_t et = eg + tt * 16;
-      const int64_t e = et + col;
-      if (et >= vis_max) continue;   // whole tile masked for every query (wave-uniform)
-      const bool partial = et + 16 > vis_min;   // some query sees only part of the tile
-      // all MFMAs of the tile first (every query, every head block), then the epilogues
-      f32x4 cc[QPW][4];
+      for (int tq = 0; tq < 4; ++tq) {
+        const int tt = kg * 4 + tq;
+        const int64_t et = eg + tt * 16;
 #pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) qk_tiles<QK>(qa[qi], kb[cur][tt], qsc[qi], ksc[cur][tt], cc[qi]);
+        for (int qi = 0; qi < QPW; ++qi) part[qi][tq] = 0.f;
+        if (et >= vis_max) continue;   // whole tile masked for every query (wave-uniform)
+        // all MFMAs of the tile first (every query, every head block), then the epilogues
+        f32x4 cc[QPW][4];
 #pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        float part = 0.f;
+        for (int qi = 0; qi < QPW; ++qi) qk_tiles<QK>(qa[qi], kb[cur][tt], qsc[qi], ksc[cur][tt], cc[qi]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 c = cc[qi][mt];
-          part = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), part);
-          part = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), part);
-          part = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), part);
-          part = fmaf(wv[qi][mt][3], fmaxf(c[3], 0.f), part);
+        for (int qi = 0; qi < QPW; ++qi) {
+          float acc = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const f32x4 c = cc[qi][mt];
+            acc = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), acc);
+            acc = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), acc);
+            acc = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), acc);
+            acc = fmaf(wv[qi][mt][3], fmaxf(c[3], 0.f), acc);
+          }
+          part[qi][tq] = acc * kscale[cur][tt];
         }
-        part += lane_read(x16, part);
-        part += lane_read(x32, part);
-        part *= kscale[cur][tt];
-        if (partial && e >= vis[qi]) part = -INFINITY;
-        if (tt == g) keep[qi] = part;
       }
-    }
-    const int64_t e = eg + g * 16 + col;
-    if (e < N) {
+      const int64_t e = eg + kg * 64 + g * 16 + col;   // the entry this lane ends up holding
+      const bool hi = g >= 2, odd = g & 1;
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
-        if (t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, keep[qi]);
+        // lane ^ 32 flips g by 2: keep tiles {0,1} (g < 2) or {2,3}
+        float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
+        k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
+        k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
+        // lane ^ 16 flips g by 1: keep tile (g & 1) of the pair
+        float v = odd ? k1 : k0;
+        v += lane_read(x16, odd ? k0 : k1);
+        if (e >= vis[qi]) v = -INFINITY;
+        if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, v);
       }
     }
   }
 }
 
-template <int QK, int QPW, int TPW>
+template <int QK, int QPW, int TPW, int GT, int OCC>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
   dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
@@ -268,11 +294,11 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
   if (a.score_dtype == CSA_BF16)
-    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
                        static_cast<uint16_t*>(a.scores));
   else
-    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, float>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, float>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
                        static_cast<float*>(a.scores));
   return hipGetLastError();
@@ -283,12 +309,12 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
   // tiles per wave from a sweep on MI355X (decode: HBM streaming; prefill: the
   // q prologue amortised over long entry runs)
   if (a.T <= 2) {   // decode: one query per wave, long entry runs
-    constexpr int TPW = (QK == CSA_MXFP4) ? 8 : 32;
-    return launch_mfma<QK, 1, TPW>(a, s);
+    if constexpr (QK == CSA_MXFP4) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
+    else return launch_mfma<QK, 1, 16, 4, 2>(a, s);
   }
   // prefill: several queries per wave share each key tile (bf16 q fragments are
   // twice the size of fp8 ones, so two queries fit the register budget)
-  return launch_mfma<QK, 2, 64>(a, s);
+  return launch_mfma<QK, 2, 64, 4, 2>(a, s);
 }
 
 }  // namespace
