@@ -306,6 +306,207 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
   emit_range<KT>(lo, hi, K, rem, gtb, eqb, out, [&](int64_t i) { return keys[i]; });
 }
 
+// ------------------------------------------------------------ register path
+// bf16 rows of up to 1024 * 8 * CPT keys: thread t holds CPT 16-byte chunks,
+// chunk c being keys 8 (c * 1024 + t) .. + 7, in registers for the whole
+// selection.  LDS only holds the histogram.  The key range is found while
+// the chunks load; an exact histogram of (key - min) (or, for wide ranges,
+// the 11 + 5-bit digit passes) gives the k-th largest key K; the ordered
+// compaction handles two chunks per block-wide scan of four packed 16-bit
+// counts.  Same result as the LDS path.
+__device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* tmp /* >= 17 words */, uint64_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint64_t t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const uint64_t r = tmp[wid] + x - v;
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+template <int CPT>
+__global__ void __launch_bounds__(1024)
+topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const uint16_t* __restrict__ scores,
+                int32_t* __restrict__ idx) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t bins[kRangeBins];
+  __shared__ uint32_t tmp[32];
+  __shared__ uint64_t tmp64[17];
+  const int64_t row = blockIdx.x;
+  const int64_t t = row % T;
+  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  int32_t* out = idx + row * k;
+  const int tid = threadIdx.x;
+  if (V <= k) {
+    for (int i = tid; i < k; i += NT) out[i] = i < V ? i : -1;
+    return;
+  }
+  for (int i = tid; i < kRangeBins; i += NT) bins[i] = 0;
+  if (tid == 0) {
+    tmp[24] = 0xffffu;
+    tmp[25] = 0u;
+  }
+  // keys in registers; chunks at or past V hold no key (valid bits 0)
+  const uint4* src = reinterpret_cast<const uint4*>(scores + row * N);
+  // two 16-bit keys per register: key u of chunk c is KEY(c, u)
+  uint32_t kp[CPT][4];
+  uint32_t valid[CPT];
+#define KEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
+  uint32_t kmin = 0xffffu, kmax = 0u;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t i0 = 8 * (static_cast<int64_t>(c) * NT + tid);
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (i0 < V) raw = src[c * NT + tid];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const int64_t nv = V - i0;
+    valid[c] = nv >= 8 ? 0xffu : (nv > 0 ? (1u << nv) - 1u : 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = key_of(static_cast<uint16_t>(w[j] & 0xffffu));
+      const uint32_t hi = key_of(static_cast<uint16_t>(w[j] >> 16));
+      kp[c][j] = lo | (hi << 16);
+      if ((valid[c] >> (2 * j)) & 1u) { kmin = min(kmin, lo); kmax = max(kmax, lo); }
+      if ((valid[c] >> (2 * j + 1)) & 1u) { kmin = min(kmin, hi); kmax = max(kmax, hi); }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(kmin, o, 64)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, o, 64)));
+  }
+  if ((tid & 63) == 0) {
+    atomicMin(&tmp[24], kmin);
+    atomicMax(&tmp[25], kmax);
+  }
+  __syncthreads();   // range known, bins zeroed
+  kmin = tmp[24];
+  kmax = tmp[25];
+  uint32_t K, rem;
+  if (kmax - kmin < static_cast<uint32_t>(kRangeBins)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if ((valid[c] >> u) & 1u) atomicAdd(&bins[KEY(c, u) - kmin], 1u);
+    __syncthreads();
+    // thread t owns bins 8t .. 8t+7; find the bin holding the k-th largest key
+    constexpr int per = kRangeBins / NT;
+    const int b0 = tid * per;
+    uint32_t h[per], mine = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+      h[q] = bins[b0 + q];
+      mine += h[q];
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan(mine, tmp, &total);
+    const uint32_t above = total - excl - mine;
+    if (above < static_cast<uint32_t>(k) && above + mine >= static_cast<uint32_t>(k)) {
+      uint32_t cum = above;
+      bool found = false;
+#pragma unroll
+      for (int q = per - 1; q >= 0; --q) {
+        if (!found && cum + h[q] >= static_cast<uint32_t>(k)) {
+          tmp[20] = kmin + static_cast<uint32_t>(b0 + q);
+          tmp[21] = static_cast<uint32_t>(k) - cum;
+          found = true;
+        }
+        cum += h[q];
+      }
+    }
+    __syncthreads();
+    K = tmp[20];
+    rem = tmp[21];
+  } else {
+    uint32_t prefix = 0, mask = 0;
+    rem = static_cast<uint32_t>(k);
+    for (int p = 0; p < Digits<uint16_t>::n; ++p) {
+      const int sh = Digits<uint16_t>::shift(p);
+      const int nb = 1 << Digits<uint16_t>::bits(p);
+      for (int i = tid; i < nb; i += NT) bins[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          hist_add(bins, (KEY(c, u) >> sh) & (nb - 1), ((valid[c] >> u) & 1u) && (KEY(c, u) & mask) == prefix);
+      __syncthreads();
+      resolve_digit(bins, nb, rem, tmp + 20);
+      __syncthreads();
+      prefix |= tmp[20] << sh;
+      mask |= static_cast<uint32_t>(nb - 1) << sh;
+      rem = tmp[21];
+      __syncthreads();
+    }
+    K = prefix;
+  }
+
+  // ordered compaction, two chunks per scan: fields gt0 | eq0 | gt1 | eq1
+  uint32_t gt_run = 0, eq_run = 0;
+#pragma unroll
+  for (int c0 = 0; c0 < CPT; c0 += 2) {
+    uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if (c0 + h2 >= CPT) continue;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool vv = (valid[c0 + h2] >> u) & 1u;
+        cnt[h2][0] += vv && KEY(c0 + h2, u) > K;
+        cnt[h2][1] += vv && KEY(c0 + h2, u) == K;
+      }
+    }
+    const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
+                            (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
+    uint64_t tot;
+    const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
+    const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
+    const uint32_t tg1 = (tot >> 32) & 0xffffu, te1 = (tot >> 48) & 0xffffu;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = c0 + h2;
+      if (c >= CPT) continue;
+      const uint32_t gb = gt_run + (h2 ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
+      const uint32_t eb = eq_run + (h2 ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
+      uint32_t pos = gb + (eb < rem ? eb : rem);
+      uint32_t er = eb;
+      const int32_t i0 = static_cast<int32_t>(8 * (c * NT + tid));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!((valid[c] >> u) & 1u)) continue;
+        const uint32_t kk = KEY(c, u);
+        if (kk > K) {
+          out[pos++] = i0 + u;
+        } else if (kk == K) {
+          if (er < rem) out[pos++] = i0 + u;
+          ++er;
+        }
+      }
+    }
+    gt_run += tg0 + tg1;
+    eq_run += te0 + te1;
+  }
+#undef KEY
+}
+
 // ------------------------------------------------------------ global path
 // Workspace per row (uint32 words): hist[3][2048], counts[S][2].
 constexpr int kWsHist = 3 * kBins;
@@ -454,6 +655,22 @@ template <typename KT>
 hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
   const KT* sc = static_cast<const KT*>(a.scores);
   const int64_t rows = a.B * a.T;
+  if constexpr (sizeof(KT) == 2) {
+    // rows of bf16 keys that fit 1024 threads x CPT chunks of 8, 16-byte aligned
+    const int cpt = static_cast<int>((a.N + 8 * 1024 - 1) / (8 * 1024));
+    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && cpt <= 5) {
+      const dim3 grid(static_cast<uint32_t>(rows));
+      const auto* sc16 = static_cast<const uint16_t*>(a.scores);
+      switch (cpt) {
+        case 1: hipLaunchKernelGGL(topk_reg_kernel<1>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+        case 2: hipLaunchKernelGGL(topk_reg_kernel<2>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+        case 3: hipLaunchKernelGGL(topk_reg_kernel<3>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+        case 4: hipLaunchKernelGGL(topk_reg_kernel<4>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+        default: hipLaunchKernelGGL(topk_reg_kernel<5>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+      }
+      return hipGetLastError();
+    }
+  }
   if (topk_row_in_lds(a.N, a.score_dtype)) {
     const size_t smem = (kRangeBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
     hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
