@@ -22,6 +22,8 @@
 // Because K is contracted, the order of K inside a lane's fragment is free as
 // long as q and k use the same order: every lane loads the same contiguous
 // byte range of its q row and of its key row.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -83,6 +85,7 @@ template <> struct Frag<CSA_BF16> {
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) v[i] = p[4 * i];
   }
+  __device__ static constexpr int chunk(int i, int g) { return 4 * i + g; }
 };
 // fp8: rows of 128 B; lane (r, g) holds bytes [32g, 32g+32).
 template <> struct Frag<CSA_FP8_E4M3> {
@@ -94,7 +97,18 @@ template <> struct Frag<CSA_FP8_E4M3> {
     v[0] = p[0];
     v[1] = p[1];
   }
+  __device__ static constexpr int chunk(int i, int g) { return 2 * g + i; }
 };
+// A key tile staged in LDS as [16-byte chunk][row]: chunk c of the 16 rows is
+// 256 contiguous bytes, so the 16 lanes reading one chunk hit 16 distinct
+// bank groups.  Register i of lane (r, g) is chunk Frag::chunk(i, g) of row r.
+template <typename F>
+__device__ __forceinline__ void load_tile_frag(F& f, const uint8_t* tile, int col, int g) {
+#pragma unroll
+  for (int i = 0; i < F::kRegs; ++i)
+    f.v[i] = *reinterpret_cast<const uint4*>(tile + F::chunk(i, g) * 256 + col * 16);
+}
+
 // MXFP4: rows of 64 B + 4 scale bytes; lane (r, g) holds bytes [16g, 16g+16)
 // (the 32 elements of MX block g) and block g's scale.
 template <> struct Frag<CSA_MXFP4> {
@@ -159,7 +173,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   using F = Frag<QK>;
   constexpr int RB = F::kRowBytes;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
   const int col = lane & 15;   // row of a 16-row operand tile / column of the output tile
   const int g = lane >> 4;     // lane group: K sub-range, and output rows 4g..4g+3
   const int64_t b = blockIdx.z;
@@ -218,12 +232,14 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   F kb[2][GT];
   int ksc[2][GT];
   float kscale[2][GT];
+  const uint8_t* kseq = k + krow0 * RB + col * RB;   // this lane's row of every tile, from entry 0
   auto load_group = [&](int slot, int64_t eg) {
+    const bool full = eg + GT * 16 <= N;   // wave-uniform: only the last group can run past N
 #pragma unroll
     for (int tt = 0; tt < GT; ++tt) {
       int64_t e = eg + tt * 16 + col;
       if (e >= N) e = N - 1;
-      kb[slot][tt].load(k + (krow0 + e) * RB, g);
+      kb[slot][tt].load(full ? kseq + (eg + tt * 16) * RB : k + (krow0 + e) * RB, g);
       if constexpr (QK == CSA_MXFP4) ksc[slot][tt] = static_cast<const uint8_t*>(k_scale)[(krow0 + e) * 4 + g];
       else ksc[slot][tt] = 127;
       if constexpr (QK == CSA_FP8_E4M3) kscale[slot][tt] = static_cast<const float*>(k_scale)[krow0 + e];
@@ -286,6 +302,197 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 }
 
+// ---------------------------------------------------------------- ring path
+// bf16 / fp8 keys: each wave streams its TPW tiles through a four-slot ring
+// of LDS tile buffers filled by direct global->LDS loads (no registers held
+// for loads in flight), three tiles ahead of the one being computed.  Each
+// slot is its own LDS array, so the compiler can see that reading slot r does
+// not touch the loads landing in the other slots; the waits for a tile's rows
+// are explicit.  A wave only ever reads its own slots: no barriers.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+template <int QK, int QPW, int TPW, typename TS>
+__global__ void __launch_bounds__(256, 2)
+index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                  const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
+                  const float* __restrict__ w, const uint8_t* __restrict__ k,
+                  const void* __restrict__ k_scale, TS* __restrict__ scores) {
+  static_assert(QK == CSA_BF16 || QK == CSA_FP8_E4M3, "MXFP4 keys use index_mfma_kernel");
+  static_assert(TPW % 4 == 0 && TPW >= 4, "the ring turns four tiles at a time");
+  using F = Frag<QK>;
+  constexpr int RB = F::kRowBytes;
+  constexpr int TB = 16 * RB;                               // bytes per 16-entry tile
+  constexpr int NI = TB / 1024;                             // 1 KB row loads per tile
+  constexpr int OPS = NI + (QK == CSA_FP8_E4M3 ? 1 : 0);    // vector memory ops issued per tile
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * QPW;
+  const int64_t e_wave = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * (TPW * 16);
+
+  __shared__ __attribute__((aligned(16))) uint8_t qs[QPW * kH * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[4][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[4][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[4][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[4][TB];
+  for (int o = threadIdx.x * 16; o < QPW * kH * RB; o += 256 * 16) {
+    const int qi = o / (kH * RB);
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    *reinterpret_cast<uint4*>(qs + o) = *reinterpret_cast<const uint4*>(q + (b * T + t) * kH * RB + o % (kH * RB));
+  }
+  __syncthreads();
+  if (e_wave >= N) return;
+
+  F qa[QPW][4];
+  float wv[QPW][4][4];
+  int64_t vis[QPW];
+  int64_t vis_max = 0;
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    int64_t v = (q_pos0 + t + 1) / ratio;
+    if (v > N) v = N;
+    vis[qi] = (t0 + qi < T) ? v : 0;
+    vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
+    const int64_t qrow = (b * T + t) * kH;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      qa[qi][mt].load(qs + (qi * kH + mt * 16 + col) * RB, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = mt * 16 + 4 * g + i;
+        float wt = w[qrow + h];
+        if constexpr (QK == CSA_FP8_E4M3) wt *= static_cast<const float*>(q_scale)[qrow + h];
+        wv[qi][mt][i] = wt;
+      }
+    }
+  }
+  const int qsc[4] = {127, 127, 127, 127};
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
+
+  if (e_wave >= vis_max) {   // nothing of this wave's run is visible to any of its queries
+#pragma unroll
+    for (int tb = 0; tb < TPW; tb += 4) {
+      const int64_t e = e_wave + 16 * (tb + g) + col;
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi)
+        if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, -INFINITY);
+    }
+    return;
+  }
+
+  // lane l's share of a tile's row loads: row l % 16, chunks 4j + l / 16
+  const int64_t krow0 = b * N;
+  float ks[4] = {1.f, 1.f, 1.f, 1.f};   // fp8 key row scales of the tiles in the ring
+  auto slot = [&](auto rc) -> uint8_t* {
+    constexpr int r = decltype(rc)::value;
+    if constexpr (r == 0) return ring0[wid];
+    else if constexpr (r == 1) return ring1[wid];
+    else if constexpr (r == 2) return ring2[wid];
+    else return ring3[wid];
+  };
+  auto issue = [&](int t, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    uint8_t* dst = slot(rc);
+    int64_t e = e_wave + 16 * t + col;
+    if (e >= N) e = N - 1;
+    const uint8_t* src = k + (krow0 + e) * RB + g * 16;
+    wait_lgkm0();   // this wave's reads of the slot's previous tile are done
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 64 * j), (lds_void*)(dst + 1024 * j), 16, 0, 0);
+    if constexpr (QK == CSA_FP8_E4M3) ks[r] = static_cast<const float*>(k_scale)[krow0 + e];
+  };
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  issue(2, std::integral_constant<int, 2>{});
+
+  float sc[QPW][TPW / 4];
+#pragma unroll
+  for (int tb = 0; tb < TPW; tb += 4) {
+    float part[QPW][4];
+    auto tile = [&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const int t = tb + r;
+      // rows of tile t have landed once at most the ops of the (up to two)
+      // tiles issued after it are outstanding
+      if (t + 2 < TPW) wait_vm<2 * OPS>();
+      else if (t + 1 < TPW) wait_vm<OPS>();
+      else wait_vm<0>();
+      if (t + 3 < TPW) issue(t + 3, std::integral_constant<int, (r + 3) & 3>{});
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) part[qi][r] = 0.f;
+      if (e_wave + 16 * t >= vis_max) return;   // whole tile masked for every query (wave-uniform)
+      F kf;
+      load_tile_frag(kf, slot(rc), col, g);
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        f32x4 cc[4];
+        qk_tiles<QK>(qa[qi], kf, qsc, 127, cc);
+        float acc = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc = fmaf(wv[qi][mt][0], fmaxf(cc[mt][0], 0.f), acc);
+          acc = fmaf(wv[qi][mt][1], fmaxf(cc[mt][1], 0.f), acc);
+          acc = fmaf(wv[qi][mt][2], fmaxf(cc[mt][2], 0.f), acc);
+          acc = fmaf(wv[qi][mt][3], fmaxf(cc[mt][3], 0.f), acc);
+        }
+        part[qi][r] = acc * ks[r];
+      }
+    };
+    tile(std::integral_constant<int, 0>{});
+    tile(std::integral_constant<int, 1>{});
+    tile(std::integral_constant<int, 2>{});
+    tile(std::integral_constant<int, 3>{});
+    // reduce-scatter over the four lane groups: lane group g keeps tile tb + g
+    const int64_t e = e_wave + 16 * (tb + g) + col;
+    const bool hi = g >= 2, odd = g & 1;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
+      k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
+      k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
+      float v = odd ? k1 : k0;
+      v += lane_read(x16, odd ? k0 : k1);
+      sc[qi][tb / 4] = (e >= vis[qi]) ? -INFINITY : v;
+    }
+  }
+  // scores leave after the last tile: no stores among the counted row loads
+#pragma unroll
+  for (int tb = 0; tb < TPW; tb += 4) {
+    const int64_t e = e_wave + 16 * (tb + g) + col;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi)
+      if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, sc[qi][tb / 4]);
+  }
+}
+
+template <int QK, int QPW, int TPW>
+hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
+  const int64_t per_wg = 4 * TPW * 16;
+  dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
+            static_cast<uint32_t>((a.T + QPW - 1) / QPW), static_cast<uint32_t>(a.B));
+  const auto* q = static_cast<const uint8_t*>(a.q);
+  const auto* k = static_cast<const uint8_t*>(a.k);
+  if (a.score_dtype == CSA_BF16)
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores));
+  else
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, float>), grid, dim3(256), 0, s, a.T, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores));
+  return hipGetLastError();
+}
+
 template <int QK, int QPW, int TPW, int GT, int OCC>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
@@ -306,15 +513,15 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
 
 template <int QK>
 hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
-  // tiles per wave from a sweep on MI355X (decode: HBM streaming; prefill: the
-  // q prologue amortised over long entry runs)
-  if (a.T <= 2) {   // decode: one query per wave, long entry runs
-    if constexpr (QK == CSA_MXFP4) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
-    else return launch_mfma<QK, 1, 16, 4, 2>(a, s);
+  // tiles per wave from sweeps on MI355X (decode: HBM streaming, one query per
+  // wave; prefill: two queries per wave share each key tile)
+  if constexpr (QK == CSA_MXFP4) {
+    if (a.T <= 2) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
+    return launch_mfma<QK, 2, 64, 4, 2>(a, s);
+  } else {
+    if (a.T <= 2) return launch_ring<QK, 1, 32>(a, s);
+    return launch_ring<QK, 2, 64>(a, s);
   }
-  // prefill: several queries per wave share each key tile (bf16 q fragments are
-  // twice the size of fp8 ones, so two queries fit the register budget)
-  return launch_mfma<QK, 2, 64, 4, 2>(a, s);
 }
 
 }  // namespace
