@@ -651,6 +651,223 @@ topk_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
                  [&](int64_t i) { return load_key(src, i); });
 }
 
+// ------------------------------------------------------------ long bf16 rows
+// Rows too long for one workgroup (the 1M-context decode: 262,144 keys): S
+// slices per row, one 256-thread workgroup per slice holding its keys in
+// registers (thread t, chunk c: keys lo + 8 (c * 256 + t) .. + 7).
+//   G1  histogram of the top 11 key bits of the slice, merged into the row's
+//       histogram with one atomic per non-empty bin;
+//   G2  with the top bin b* resolved: the slice's count of keys above b* and
+//       its 32-bin histogram of the low 5 bits among keys in b*, kept per
+//       slice and merged into the row's low histogram;
+//   G3  with K resolved: each slice's output offset follows from the per-slice
+//       records of the slices before it, then an ordered compaction.
+// Row workspace (uint32): hist1[2048] | hist2[32] | pad | per-slice [S][33].
+constexpr int kLongHist2 = kBins;                 // offset of hist2
+constexpr int kLongSlices = kBins + 64;           // offset of the per-slice records
+constexpr int kSliceRec = 33;                     // above, low histogram[32]
+
+template <int CPT>
+__device__ __forceinline__ void long_slice_keys(const uint16_t* row, int64_t lo, int64_t hi, uint32_t (&kp)[CPT][4],
+                                                uint32_t (&valid)[CPT]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t i0 = lo + 8 * (static_cast<int64_t>(c) * 256 + tid);
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (i0 < hi) raw = *reinterpret_cast<const uint4*>(row + i0);
+    const int64_t nv = hi - i0;
+    valid[c] = nv >= 8 ? 0xffu : (nv > 0 ? (1u << nv) - 1u : 0u);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      kp[c][j] = key_of(static_cast<uint16_t>(w[j] & 0xffffu)) | (static_cast<uint32_t>(key_of(static_cast<uint16_t>(w[j] >> 16))) << 16);
+  }
+}
+#define LKEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
+
+__device__ __forceinline__ void long_slice_range(int64_t V, int S, int64_t& lo, int64_t& hi) {
+  const int64_t L = ((V + S - 1) / S + 7) / 8 * 8;
+  lo = blockIdx.x * L;
+  hi = lo + L < V ? lo + L : V;
+  if (lo > hi) lo = hi;
+}
+
+template <int CPT>
+__global__ void __launch_bounds__(256)
+topk_long_hist1_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t hist[kBins];
+  const int64_t row = blockIdx.y;
+  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  if (V <= k) return;
+  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0;
+  int64_t lo, hi;
+  long_slice_range(V, S, lo, hi);
+  uint32_t kp[CPT][4], valid[CPT];
+  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) hist_add(hist, LKEY(c, u) >> 5, (valid[c] >> u) & 1u);
+  __syncthreads();
+  uint32_t* h1 = ws + row * (kLongSlices + kSliceRec * S);
+  for (int i = threadIdx.x; i < kBins; i += 256)
+    if (hist[i]) atomicAdd(&h1[i], hist[i]);
+}
+
+template <int CPT>
+__global__ void __launch_bounds__(256)
+topk_long_hist2_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t st[4];
+  __shared__ uint32_t h2[32];
+  __shared__ uint32_t above_s;
+  const int64_t row = blockIdx.y;
+  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  if (V <= k) return;
+  uint32_t* rws = ws + row * (kLongSlices + kSliceRec * S);
+  int64_t lo, hi;
+  long_slice_range(V, S, lo, hi);
+  uint32_t kp[CPT][4], valid[CPT];
+  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);   // in flight while the top bin resolves
+  if (threadIdx.x < 32) h2[threadIdx.x] = 0;
+  if (threadIdx.x == 0) above_s = 0;
+  resolve_digit(rws, kBins, static_cast<uint32_t>(k), st);
+  __syncthreads();
+  const uint32_t bstar = st[0];
+  uint32_t above = 0;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool v = (valid[c] >> u) & 1u;
+      const uint32_t kk = LKEY(c, u);
+      above += v && (kk >> 5) > bstar;
+      if (v && (kk >> 5) == bstar) atomicAdd(&h2[kk & 31], 1u);
+    }
+  above = wave_sum_u32(above);
+  if ((threadIdx.x & 63) == 0) atomicAdd(&above_s, above);
+  __syncthreads();
+  uint32_t* rec = rws + kLongSlices + kSliceRec * blockIdx.x;
+  if (threadIdx.x == 0) rec[0] = above_s;
+  if (threadIdx.x < 32) {
+    rec[1 + threadIdx.x] = h2[threadIdx.x];
+    if (h2[threadIdx.x]) atomicAdd(&rws[kLongHist2 + threadIdx.x], h2[threadIdx.x]);
+  }
+}
+
+template <int CPT>
+__global__ void __launch_bounds__(256)
+topk_long_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
+  __shared__ uint32_t st[4];
+  __shared__ uint32_t st2[4];
+  __shared__ uint64_t tmp64[17];
+  __shared__ uint32_t before[2];
+  const int64_t row = blockIdx.y;
+  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < k; i += 256) out[i] = i < V ? i : -1;
+    return;
+  }
+  const uint32_t* rws = ws + row * (kLongSlices + kSliceRec * S);
+  int64_t lo, hi;
+  long_slice_range(V, S, lo, hi);
+  uint32_t kp[CPT][4], valid[CPT];
+  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);
+  resolve_digit(rws, kBins, static_cast<uint32_t>(k), st);
+  __syncthreads();
+  const uint32_t bstar = st[0], rem1 = st[1];
+  resolve_digit(rws + kLongHist2, 32, rem1, st2);
+  __syncthreads();
+  const uint32_t lowk = st2[0], rem = st2[1];
+  const uint32_t K = (bstar << 5) | lowk;
+  // keys > K and == K in the slices before this one
+  if (threadIdx.x < 64) {
+    uint32_t gt = 0, eq = 0;
+    for (int s2 = threadIdx.x; s2 < static_cast<int>(blockIdx.x); s2 += 64) {
+      const uint32_t* rec = rws + kLongSlices + kSliceRec * s2;
+      gt += rec[0];
+      for (int b = lowk + 1; b < 32; ++b) gt += rec[1 + b];
+      eq += rec[1 + lowk];
+    }
+    gt = wave_sum_u32(gt);
+    eq = wave_sum_u32(eq);
+    if (threadIdx.x == 0) {
+      before[0] = gt;
+      before[1] = eq;
+    }
+  }
+  __syncthreads();
+  uint32_t gt_run = before[0], eq_run = before[1];
+  // ordered compaction of the slice, two chunks per scan (fields gt0 | eq0 | gt1 | eq1)
+#pragma unroll
+  for (int c0 = 0; c0 < CPT; c0 += 2) {
+    uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (c0 + h >= CPT) continue;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool vv = (valid[c0 + h] >> u) & 1u;
+        cnt[h][0] += vv && LKEY(c0 + h, u) > K;
+        cnt[h][1] += vv && LKEY(c0 + h, u) == K;
+      }
+    }
+    const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
+                            (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
+    uint64_t tot;
+    const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
+    const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
+    const uint32_t tg1 = (tot >> 32) & 0xffffu, te1 = (tot >> 48) & 0xffffu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + h;
+      if (c >= CPT) continue;
+      const uint32_t gb = gt_run + (h ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
+      const uint32_t eb = eq_run + (h ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
+      uint32_t pos = gb + (eb < rem ? eb : rem);
+      uint32_t er = eb;
+      const int32_t i0 = static_cast<int32_t>(lo + 8 * (c * 256 + threadIdx.x));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!((valid[c] >> u) & 1u)) continue;
+        const uint32_t kk = LKEY(c, u);
+        if (kk > K) {
+          out[pos++] = i0 + u;
+        } else if (kk == K) {
+          if (er < rem) out[pos++] = i0 + u;
+          ++er;
+        }
+      }
+    }
+    gt_run += tg0 + tg1;
+    eq_run += te0 + te1;
+  }
+}
+#undef LKEY
+
+template <int CPT>
+hipError_t launch_long(const TopkArgs& a, hipStream_t s) {
+  const int S = kTopkSlices;
+  const int64_t rows = a.B * a.T;
+  uint32_t* ws = static_cast<uint32_t*>(a.ws);
+  const auto* sc = static_cast<const uint16_t*>(a.scores);
+  const int64_t per_row = kLongSlices + kSliceRec * S;
+  const int64_t words = rows * per_row;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, s, ws, words);
+  const dim3 grid(S, static_cast<uint32_t>(rows));
+  hipLaunchKernelGGL(topk_long_hist1_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws);
+  hipLaunchKernelGGL(topk_long_hist2_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws);
+  hipLaunchKernelGGL(topk_long_write_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws,
+                     a.idx);
+  return hipGetLastError();
+}
+
 template <typename KT>
 hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
   const KT* sc = static_cast<const KT*>(a.scores);
@@ -676,6 +893,17 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
                        a.N, a.q_pos0, a.ratio, a.k, sc, a.idx);
     return hipGetLastError();
+  }
+  if constexpr (sizeof(KT) == 2) {
+    // long bf16 rows: slices of up to 8 * 256 * 8 keys held in registers
+    const int64_t slice = ((a.N + kTopkSlices - 1) / kTopkSlices + 7) / 8 * 8;
+    const int64_t cpt = (slice + 2047) / 2048;
+    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && cpt <= 8) {
+      if (cpt <= 1) return launch_long<1>(a, s);
+      if (cpt <= 2) return launch_long<2>(a, s);
+      if (cpt <= 4) return launch_long<4>(a, s);
+      return launch_long<8>(a, s);
+    }
   }
   const int S = kTopkSlices;
   uint32_t* ws = static_cast<uint32_t*>(a.ws);

@@ -74,6 +74,13 @@ def test_1m_decode_bf16_global_path():
     _check(_run(d, 1024, 1048575), ot.topk_select(x, 1024, 1048575, 4))
 
 
+def test_long_rows_partly_visible():
+    """Long bf16 rows whose visible range ends inside the row (and mid-chunk:
+    150,001 candidates), k = 1024."""
+    x, d = _scores("tk.longvis", 1, 4, 200000, "bf16")
+    _check(_run(d, 1024, 599999), ot.topk_select(x, 1024, 599999, 4))
+
+
 def test_fp32_global_path():
     x, d = _scores("tk.f32g", 2, 3, 20000, "f32", ties=64)
     _check(_run(d, 700, 79997), ot.topk_select(x, 700, 79997, 4))
