@@ -461,71 +461,73 @@ attn_f32_kernel(Params P) {
 
 // ------------------------------------------------------------ split combine
 // One workgroup per (query, 16-head block hb, 128-column quarter w), which is
-// one contiguous 8 KB run of every split's partial O.  Partials are merged in
-// split order (bit-reproducible); the bf16 result goes through LDS so that
+// one contiguous 8 KB run of every split's partial O.  Each thread owns two
+// float4 of the run (heads 4g..4g+3 of the block, two columns) and folds the
+// splits in order into a running (max, sum, O) of its four heads -- a single
+// pass in which the loads of the next splits are already in flight.  Every
+// thread of a lane group computes the same statistics in the same order, so
+// the result is bit-reproducible.  The bf16 result goes through LDS so that
 // each output row is written in full 16-byte pieces.
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) float wgt[kMaxSplits * 16];   // weight of split s for head 16 hb + h
-  __shared__ __attribute__((aligned(16))) float inv[16];                // 1 / softmax denominator per head
   __shared__ __attribute__((aligned(16))) uint16_t ot[16 * 128];
   const int64_t gq = blockIdx.x / 16;
   const int hb = static_cast<int>(blockIdx.x / 4 % 4), w = static_cast<int>(blockIdx.x % 4);
   const int S = P.splits, tid = threadIdx.x;
   constexpr int64_t kSplitFloats = kH * (kD + 2);
   const float* base = P.ws + gq * S * kSplitFloats;
-  if (tid < 16) {
-    // every split's (max, sum) of this head first, all loads in flight at once
-    const int h = 16 * hb + tid;
-    float mv[kMaxSplits], lv[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      mv[s] = s < S ? base[s * kSplitFloats + kH * kD + h] : -INFINITY;
-      lv[s] = s < S ? base[s * kSplitFloats + kH * kD + kH + h] : 0.f;
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, mv[s]);
-    float zl = -INFINITY;
-    if (P.sink) {
-      zl = P.sink[h] * kLog2e;
-      M = fmaxf(M, zl);
-    }
-    float denom = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const float e = (mv[s] == -INFINITY) ? 0.f : fast_exp2(mv[s] - M);
-      wgt[s * 16 + tid] = e;
-      denom += lv[s] * e;
-    }
-    if (P.sink) denom += fast_exp2(zl - M);
-    inv[tid] = 1.f / denom;
-    if (P.lse && w == 0) P.lse[gq * kH + h] = kLn2 * (M + log2f(denom));
-  }
-  __syncthreads();
-  // two float4 of the block per thread: d-block db, lane (j, g) of the producing wave
   const int ln = tid & 63, g = ln >> 4, j = ln & 15, db0 = tid >> 6;
+  const int h0 = 16 * hb + 4 * g;   // first of this thread's four heads
   const float4* src = reinterpret_cast<const float4*>(base) + ((w * 4 + hb) * 8 + db0) * 64 + ln;
+  float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, L[4] = {0.f, 0.f, 0.f, 0.f};
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
 #pragma unroll 4
   for (int s = 0; s < S; ++s) {
+    const float* st = base + s * kSplitFloats + kH * kD;
+    const float4 ms = *reinterpret_cast<const float4*>(st + h0);
+    const float4 ls = *reinterpret_cast<const float4*>(st + kH + h0);
     const float4 v0 = src[s * (kSplitFloats / 4)];
     const float4 v1 = src[s * (kSplitFloats / 4) + 4 * 64];   // d-block db0 + 4
-    const float4 e = *reinterpret_cast<const float4*>(wgt + s * 16 + 4 * g);
-    acc0.x += v0.x * e.x; acc0.y += v0.y * e.y; acc0.z += v0.z * e.z; acc0.w += v0.w * e.w;
-    acc1.x += v1.x * e.x; acc1.y += v1.y * e.y; acc1.z += v1.z * e.z; acc1.w += v1.w * e.w;
+    const float m4[4] = {ms.x, ms.y, ms.z, ms.w}, l4[4] = {ls.x, ls.y, ls.z, ls.w};
+    float a[4], e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(M[i], m4[i]);
+      a[i] = (M[i] == -INFINITY) ? 0.f : fast_exp2(M[i] - mn);   // rescale of what is folded so far
+      e[i] = (m4[i] == -INFINITY) ? 0.f : fast_exp2(m4[i] - mn);  // weight of split s
+      L[i] = L[i] * a[i] + l4[i] * e[i];
+      M[i] = mn;
+    }
+    acc0.x = acc0.x * a[0] + v0.x * e[0]; acc0.y = acc0.y * a[1] + v0.y * e[1];
+    acc0.z = acc0.z * a[2] + v0.z * e[2]; acc0.w = acc0.w * a[3] + v0.w * e[3];
+    acc1.x = acc1.x * a[0] + v1.x * e[0]; acc1.y = acc1.y * a[1] + v1.y * e[1];
+    acc1.z = acc1.z * a[2] + v1.z * e[2]; acc1.w = acc1.w * a[3] + v1.w * e[3];
   }
-  // heads 4g..4g+3 of the block, column 16 db + j of the quarter
-  const float4 f = *reinterpret_cast<const float4*>(inv + 4 * g);
+  float f[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float denom = L[i], Mi = M[i];
+    if (P.sink) {
+      const float zl = P.sink[h0 + i] * kLog2e;
+      const float mn = fmaxf(Mi, zl);
+      denom = (Mi == -INFINITY ? 0.f : denom * fast_exp2(Mi - mn)) + fast_exp2(zl - mn);
+      f[i] = (Mi == -INFINITY ? 0.f : fast_exp2(Mi - mn)) / denom;
+      Mi = mn;
+    } else {
+      f[i] = 1.f / denom;
+    }
+    if (P.lse && w == 0 && db0 == 0 && j == 0) P.lse[gq * kH + h0 + i] = kLn2 * (Mi + log2f(denom));
+  }
+  // heads 4g..4g+3 of the block, columns 16 db + j of the quarter
   const int c0 = 16 * db0 + j, c1 = c0 + 64;
-  ot[(4 * g + 0) * 128 + c0] = f32_to_bf16(acc0.x * f.x);
-  ot[(4 * g + 1) * 128 + c0] = f32_to_bf16(acc0.y * f.y);
-  ot[(4 * g + 2) * 128 + c0] = f32_to_bf16(acc0.z * f.z);
-  ot[(4 * g + 3) * 128 + c0] = f32_to_bf16(acc0.w * f.w);
-  ot[(4 * g + 0) * 128 + c1] = f32_to_bf16(acc1.x * f.x);
-  ot[(4 * g + 1) * 128 + c1] = f32_to_bf16(acc1.y * f.y);
-  ot[(4 * g + 2) * 128 + c1] = f32_to_bf16(acc1.z * f.z);
-  ot[(4 * g + 3) * 128 + c1] = f32_to_bf16(acc1.w * f.w);
+  ot[(4 * g + 0) * 128 + c0] = f32_to_bf16(acc0.x * f[0]);
+  ot[(4 * g + 1) * 128 + c0] = f32_to_bf16(acc0.y * f[1]);
+  ot[(4 * g + 2) * 128 + c0] = f32_to_bf16(acc0.z * f[2]);
+  ot[(4 * g + 3) * 128 + c0] = f32_to_bf16(acc0.w * f[3]);
+  ot[(4 * g + 0) * 128 + c1] = f32_to_bf16(acc1.x * f[0]);
+  ot[(4 * g + 1) * 128 + c1] = f32_to_bf16(acc1.y * f[1]);
+  ot[(4 * g + 2) * 128 + c1] = f32_to_bf16(acc1.z * f[2]);
+  ot[(4 * g + 3) * 128 + c1] = f32_to_bf16(acc1.w * f[3]);
   __syncthreads();
   const int r = tid >> 4, c = (tid & 15) * 8;
   uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + 16 * hb + r) * kD + 128 * w + c;
