@@ -111,12 +111,13 @@ class DecodeStep:
         csa, c4, c4k, c128 = self.csa, self.c4, self.c4k, self.c128
         pos4 = self.ctx - 4
         return [
-            ("compress_c4a_kv", lambda: csa.csa_compress(
-                4, c4["Ca"], c4["Za"], self.b4, c4["Cb"], c4["Zb"], c4["pCb"], c4["pZb"], pos0=pos4,
-                out=self.kv[r], cache_entry0=self.N4 - 1)),
-            ("compress_c4a_keys", lambda: csa.csa_compress(
-                4, c4k["Ca"], c4k["Za"], self.b4k, c4k["Cb"], c4k["Zb"], c4k["pCb"], c4k["pZb"],
-                pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1)),
+            # the block's 512-d latent and its 128-d indexer key, one launch
+            ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
+                dict(ratio=4, Ca=c4["Ca"], Za=c4["Za"], bias=self.b4, Cb=c4["Cb"], Zb=c4["Zb"], prev_Cb=c4["pCb"],
+                     prev_Zb=c4["pZb"], pos0=pos4, out=self.kv[r], cache_entry0=self.N4 - 1),
+                dict(ratio=4, Ca=c4k["Ca"], Za=c4k["Za"], bias=self.b4k, Cb=c4k["Cb"], Zb=c4k["Zb"],
+                     prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1),
+            ])),
             ("lightning_index", lambda: csa.lightning_index(
                 self.qi, self.w, self.keys[r], q_pos0=self.t, scores=self.scores)),
             ("topk_select", lambda: csa.topk_select(
@@ -139,8 +140,8 @@ class DecodeStep:
         B, N4, k = self.B, self.N4, self.k
         rows = k + 128
         return {
-            "compress_c4a_kv": dict(bytes=B * (4 * 4 + 4 * 2) * 512 * 2 + B * 512 * 2 + 8 * 512 * 4, flops=0),
-            "compress_c4a_keys": dict(bytes=B * (4 * 4 + 4 * 2) * 128 * 2 + B * 128 * 2 + 8 * 128 * 4, flops=0),
+            "compress_c4a_kv_keys": dict(bytes=B * (4 * 4 + 4 * 2) * (512 + 128) * 2 + B * (512 + 128) * 2
+                                         + 8 * (512 + 128) * 4, flops=0),
             "lightning_index": dict(bytes=B * N4 * 128 * 2 + B * 64 * 128 * 2 + B * 64 * 4 + B * N4 * 2,
                                     flops=B * N4 * 64 * 128 * 2),
             "topk_select": dict(bytes=B * N4 * 2 + B * k * 4, flops=0),

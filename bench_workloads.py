@@ -5,7 +5,7 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
 (graph of repeated launches) to give its average kernel time and roofline.
 
   csa_prefill    1 sequence, 131,072 tokens of context + a 4,096-token chunk:
-                 C4A compress of the chunk (512-d KV and 128-d keys, bf16),
+                 C4A compress of the chunk (512-d KV and 128-d keys in one launch),
                  fp8 indexer over 4,096 x 33,792, top-512, sparse MQA
   hca_decode     16 sequences at 1,048,576 context: C128A compress of the
                  last block, dense MQA with sink over 8,192 entries + window
@@ -89,12 +89,12 @@ def run(args, torch, csa, synth):
         out = torch.empty_like(q)
         n_vis = sum(min((q0 + t + 1) // 4, N) for t in range(T))
         stages = [
-            ("compress_c4a_kv", lambda: csa.csa_compress(4, c["Ca"], c["Za"], b4, c["Cb"], c["Zb"], h["Cb"], h["Zb"],
-                                                         pos0=q0, out=kv, cache_entry0=q0 // 4),
-             T * 4 * 512 * 2 + T // 4 * 512 * 2, 0, "hbm"),
-            ("compress_c4a_keys", lambda: csa.csa_compress(4, ck["Ca"], ck["Za"], b4k, ck["Cb"], ck["Zb"], hk["Cb"],
-                                                           hk["Zb"], pos0=q0, out=keys_bf, cache_entry0=q0 // 4),
-             T * 4 * 128 * 2 + T // 4 * 128 * 2, 0, "hbm"),
+            ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
+                dict(ratio=4, Ca=c["Ca"], Za=c["Za"], bias=b4, Cb=c["Cb"], Zb=c["Zb"], prev_Cb=h["Cb"], prev_Zb=h["Zb"],
+                     pos0=q0, out=kv, cache_entry0=q0 // 4),
+                dict(ratio=4, Ca=ck["Ca"], Za=ck["Za"], bias=b4k, Cb=ck["Cb"], Zb=ck["Zb"], prev_Cb=hk["Cb"],
+                     prev_Zb=hk["Zb"], pos0=q0, out=keys_bf, cache_entry0=q0 // 4)]),
+             T * 4 * (512 + 128) * 2 + T // 4 * (512 + 128) * 2, 0, "hbm"),
             ("lightning_index", lambda: csa.lightning_index(qc, w, kc, q_pos0=q0, qk_dtype=csa.FP8_E4M3, q_scale=qs,
                                                             k_scale=ks, scores=scores),
              T * 64 * 132 + N * 132 + T * N * 2, n_vis * 64 * 128 * 2, "fp8"),
@@ -153,12 +153,12 @@ def run(args, torch, csa, synth):
         ws_a = torch.empty(max(16, csa.workspace_bytes(csa.OP_SPARSE_ATTN, B, 1, N, k)), dtype=torch.uint8,
                            device="cuda")
         stages = [
-            ("compress_c4a_kv", lambda: csa.csa_compress(4, c["Ca"], c["Za"], b4, c["Cb"], c["Zb"], c["pCb"], c["pZb"],
-                                                         pos0=q0 - 3, out=kv, cache_entry0=N - 1),
-             B * 24 * 512 * 2, 0, "hbm"),
-            ("compress_c4a_keys", lambda: csa.csa_compress(4, ck["Ca"], ck["Za"], b4k, ck["Cb"], ck["Zb"], ck["pCb"],
-                                                           ck["pZb"], pos0=q0 - 3, out=newkey),
-             B * 24 * 128 * 2, 0, "hbm"),
+            ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
+                dict(ratio=4, Ca=c["Ca"], Za=c["Za"], bias=b4, Cb=c["Cb"], Zb=c["Zb"], prev_Cb=c["pCb"],
+                     prev_Zb=c["pZb"], pos0=q0 - 3, out=kv, cache_entry0=N - 1),
+                dict(ratio=4, Ca=ck["Ca"], Za=ck["Za"], bias=b4k, Cb=ck["Cb"], Zb=ck["Zb"], prev_Cb=ck["pCb"],
+                     prev_Zb=ck["pZb"], pos0=q0 - 3, out=newkey)]),
+             B * 24 * (512 + 128) * 2, 0, "hbm"),
             ("lightning_index", lambda: csa.lightning_index(qp, w, kp, q_pos0=q0, qk_dtype=csa.MXFP4, q_scale=qsc,
                                                             k_scale=ksc, scores=scores, N=N),
              B * N * 68 + B * 64 * 68 + B * N * 2, B * N * 64 * 128 * 2, "hbm"),

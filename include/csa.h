@@ -5,6 +5,7 @@
  * attention (CSA) and heavily compressed attention (HCA) layer:
  *
  *   csa_compress      C4A / C128A KV compressor
+ *   csa_compress_batch  several compressor calls of one ratio in one launch
  *   lightning_index   indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
  *   topk_select       causal Top-k over the indexer scores
  *   sparse_mqa_attn   shared-KV MQA over the Top-k entries plus the window
@@ -125,6 +126,32 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                  const float* bias, const float* gamma, float eps,
                  int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * csa_compress_batch -- several csa_compress calls in one launch.
+ *
+ * The same operation as csa_compress, for callers that compress more than
+ * one stream of the same tokens at once (the CSA layer's 512-d latent and its
+ * 128-d indexer keys both go through a C4A compressor).  Each job carries
+ * exactly the arguments of csa_compress (without workspace and stream) and
+ * obeys the same rules; jobs of one batch must share ratio, in_dtype and
+ * out_dtype.  1 <= n_jobs <= 4.  Jobs with nothing to write are skipped.
+ * The row split that csa_compress's workspace enables is not used here.
+ * Errors name the first offending job.
+ */
+typedef struct csa_compress_job {
+  int ratio;
+  int64_t B, n_tok, c, pos0;
+  const void *Ca, *Za, *Cb, *Zb, *prev_Cb, *prev_Zb;
+  const float* bias;
+  const float* gamma;
+  float eps;
+  int in_dtype, out_dtype;
+  void* out;
+  int64_t out_batch_stride;
+} csa_compress_job;
+
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
 
 /*
  * lightning_index -- stage 2, the lightning indexer.

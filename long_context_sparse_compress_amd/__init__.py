@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
+__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
            "workspace_bytes", "library", "F32", "BF16", "FP8_E4M3", "MXFP4", "CsaError"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,8 @@ def library() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _int, _vp]
+        lib.csa_compress_batch.restype = ctypes.c_int
         lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
         lib.csa_workspace_bytes.restype = ctypes.c_size_t
         lib.csa_last_error.restype = ctypes.c_char_p
@@ -110,6 +112,54 @@ def _workspace(op, B, T, N, k, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+class _CompressJob(ctypes.Structure):
+    """csa_compress_job of csa.h."""
+    _fields_ = [("ratio", _int), ("B", _i64), ("n_tok", _i64), ("c", _i64), ("pos0", _i64),
+                ("Ca", _vp), ("Za", _vp), ("Cb", _vp), ("Zb", _vp), ("prev_Cb", _vp), ("prev_Zb", _vp),
+                ("bias", _vp), ("gamma", _vp), ("eps", _f32), ("in_dtype", _int), ("out_dtype", _int),
+                ("out", _vp), ("out_batch_stride", _i64)]
+
+
+def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
+    """Output tensor, address of entry 0 of sequence 0, and batch stride."""
+    B, n_tok, c = Ca.shape
+    n_ent = n_tok // ratio
+    if out is None:
+        odt = Ca.dtype if out_dtype is None else out_dtype
+        out = torch.empty(B, n_ent, c, dtype=odt, device=Ca.device)
+    if cache_entry0 is None:
+        if out.numel() < B * n_ent * c:
+            raise ValueError("out is too small")
+        return out, _ptr(out), 0
+    if out.dim() != 3 or out.shape[0] != B or out.shape[2] != c:
+        raise ValueError("cache must be [B, N_cache, c]")
+    if cache_entry0 < 0 or cache_entry0 + n_ent > out.shape[1]:
+        raise ValueError("cache slot out of range")
+    return out, _ptr(out) + cache_entry0 * c * out.element_size(), out.shape[1] * c
+
+
+def csa_compress_batch(jobs, stream=None):
+    """Several stage-1 calls of one ratio and dtype pair in one launch.  Each job
+    is a dict of csa_compress's arguments (ratio, Ca, Za, bias and optionally
+    Cb, Zb, prev_Cb, prev_Zb, pos0, gamma, eps, out, out_dtype, cache_entry0);
+    returns the list of outputs."""
+    arr = (_CompressJob * len(jobs))()
+    outs = []
+    for j, d in zip(arr, jobs):
+        Ca = d["Ca"]
+        B, n_tok, c = Ca.shape
+        out, optr, stride = _compress_out(Ca, d["ratio"], d.get("out"), d.get("out_dtype"), d.get("cache_entry0"))
+        outs.append(out)
+        j.ratio, j.B, j.n_tok, j.c, j.pos0 = d["ratio"], B, n_tok, c, d.get("pos0", 0)
+        j.Ca, j.Za, j.Cb, j.Zb = _ptr(Ca), _ptr(d["Za"]), _ptr(d.get("Cb")), _ptr(d.get("Zb"))
+        j.prev_Cb, j.prev_Zb = _ptr(d.get("prev_Cb")), _ptr(d.get("prev_Zb"))
+        j.bias, j.gamma, j.eps = _ptr(d["bias"]), _ptr(d.get("gamma")), d.get("eps", 1e-6)
+        j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _dt(out), optr, stride
+    st = library().csa_compress_batch(arr, len(jobs), _stream(stream))
+    _check(st, "csa_compress_batch")
+    return outs
+
+
 def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
                  gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, workspace=None,
                  stream=None):
@@ -120,22 +170,8 @@ def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=No
     n_tok//ratio - 1 of every sequence.  ``workspace`` defaults to a fresh
     buffer of the size that enables the row split; an empty tensor disables it."""
     B, n_tok, c = Ca.shape
-    n_ent = n_tok // ratio
     in_dt = _dt(Ca)
-    if out is None:
-        odt = Ca.dtype if out_dtype is None else out_dtype
-        out = torch.empty(B, n_ent, c, dtype=odt, device=Ca.device)
-    if cache_entry0 is None:
-        if out.numel() < B * n_ent * c:
-            raise ValueError("out is too small")
-        optr, stride = _ptr(out), 0
-    else:
-        if out.dim() != 3 or out.shape[0] != B or out.shape[2] != c:
-            raise ValueError("cache must be [B, N_cache, c]")
-        if cache_entry0 < 0 or cache_entry0 + n_ent > out.shape[1]:
-            raise ValueError("cache slot out of range")
-        optr = _ptr(out) + cache_entry0 * c * out.element_size()
-        stride = out.shape[1] * c
+    out, optr, stride = _compress_out(Ca, ratio, out, out_dtype, cache_entry0)
     ws, wsb = _workspace(OP_COMPRESS, B, n_tok, c, ratio, Ca.device, workspace)
     st = library().csa_compress(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
                                 _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,

@@ -45,6 +45,29 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, c
   return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
 }
 
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
+  csa::Check ck;
+  if (!jobs) ck.fail(CSA_ERR_INVALID_ARG, "jobs is NULL");
+  else if (n_jobs < 1 || n_jobs > 4) ck.fail(CSA_ERR_INVALID_ARG, "n_jobs must be 1..4, got " + csa::i2s(n_jobs));
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs a[4];
+  for (int q = 0; q < n_jobs; ++q) {
+    const csa_compress_job& j = jobs[q];
+    csa::Check cj = csa::check_compress(j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb,
+                                        j.prev_Zb, j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out,
+                                        j.out_batch_stride, nullptr, 0);
+    if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || j.out_dtype != jobs[0].out_dtype))
+      cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype");
+    if (!cj.ok()) {
+      cj.msg = "job " + csa::i2s(q) + ": " + cj.msg;
+      return finish(cj);
+    }
+    a[q] = csa::CompressArgs{j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb,
+                             j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out, j.out_batch_stride, nullptr, 0};
+  }
+  return hip_status(csa::launch_compress_batch(a, n_jobs, as_stream(stream)), "csa_compress_batch launch");
+}
+
 int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int H_I, int d_I,
                     const void* q, const void* q_scale, const float* w, const void* k,
                     const void* k_scale, int qk_dtype, void* scores, int score_dtype, void* stream) {

@@ -101,14 +101,16 @@ __device__ __forceinline__ void online_merge(Online& st, const Online& o) {
 // Every row slot of a chunk is loaded unconditionally (a missing row reads a
 // harmless in-range address and is masked), so all loads of a chunk,
 // including its bias rows, are in flight together.
+// Entry i of sequence b (rows of range z of nz), by a workgroup of at least
+// CT * G threads (threads past that only join the barriers).
 template <typename TI, typename TO, int RATIO, bool SPLIT>
-__global__ void __launch_bounds__(1024)
-compress_kernel(int64_t n_tok, int c, int64_t pos0,
-                const TI* __restrict__ Ca, const TI* __restrict__ Za,
-                const TI* __restrict__ Cb, const TI* __restrict__ Zb,
-                const TI* __restrict__ pCb, const TI* __restrict__ pZb,
-                const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
-                TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part) {
+__device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int nz, int64_t n_tok, int c, int64_t pos0,
+                                               const TI* __restrict__ Ca, const TI* __restrict__ Za,
+                                               const TI* __restrict__ Cb, const TI* __restrict__ Zb,
+                                               const TI* __restrict__ pCb, const TI* __restrict__ pZb,
+                                               const float* __restrict__ bias, const float* __restrict__ gamma,
+                                               float eps, TO* __restrict__ out, int64_t out_stride, int G,
+                                               float* __restrict__ part) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   constexpr int UC = kChunkRows;
@@ -116,11 +118,9 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
   const int tid = threadIdx.x;
   const int ct = tid % CT;
   const int g = tid / CT;
-  const int64_t i = blockIdx.x;
-  const int64_t b = blockIdx.y;
   const int ch0 = ct * VEC;
-  const int rows_per = ROWS / static_cast<int>(gridDim.z);
-  const int rlo = static_cast<int>(blockIdx.z) * rows_per, rhi = rlo + rows_per;
+  const int rows_per = ROWS / nz;
+  const int rlo = z * rows_per, rhi = g < G ? rlo + rows_per : rlo;   // idle threads own no rows
 
   float gm[VEC];   // RMSNorm gain, fetched while the rows load
   if (!SPLIT && g == 0) {
@@ -240,7 +240,7 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
     // this row range's state, [entry][range][m | s | y][c], merged by compress_merge_kernel
     if (g == 0) {
       const int64_t n_ent = n_tok / RATIO;
-      float* pp = part + ((b * n_ent + i) * gridDim.z + blockIdx.z) * 3 * c + ch0;
+      float* pp = part + ((b * n_ent + i) * nz + z) * 3 * c + ch0;
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         pp[v] = st[v].m;
@@ -275,6 +275,47 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
 #pragma unroll
   for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * gm[v];
   store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
+}
+
+template <typename TI, typename TO, int RATIO, bool SPLIT>
+__global__ void __launch_bounds__(1024)
+compress_kernel(int64_t n_tok, int c, int64_t pos0,
+                const TI* __restrict__ Ca, const TI* __restrict__ Za,
+                const TI* __restrict__ Cb, const TI* __restrict__ Zb,
+                const TI* __restrict__ pCb, const TI* __restrict__ pZb,
+                const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
+                TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part) {
+  compress_entry<TI, TO, RATIO, SPLIT>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
+                                       static_cast<int>(gridDim.z), n_tok, c, pos0, Ca, Za, Cb, Zb, pCb, pZb, bias,
+                                       gamma, eps, out, out_stride, G, part);
+}
+
+// Several compressions of one ratio and dtype pair in one launch (blockIdx.z
+// picks the job); a job's workgroups past its own grid return at once.
+struct CompressJobDev {
+  const void *Ca, *Za, *Cb, *Zb, *pCb, *pZb;
+  const float* bias;
+  const float* gamma;
+  void* out;
+  int64_t n_tok, pos0, out_stride, n_ent, B;
+  float eps;
+  int c, G;
+};
+constexpr int kMaxBatchJobs = 4;
+struct CompressBatch {
+  CompressJobDev j[kMaxBatchJobs];
+};
+
+template <typename TI, typename TO, int RATIO>
+__global__ void __launch_bounds__(1024)
+compress_batch_kernel(CompressBatch jb) {
+  const CompressJobDev& J = jb.j[blockIdx.z];
+  if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
+  compress_entry<TI, TO, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+                                       static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
+                                       static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
+                                       static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias, J.gamma,
+                                       J.eps, static_cast<TO*>(J.out), J.out_stride, J.G, nullptr);
 }
 
 // Merge of the row-range states of one (entry, sequence), then RMSNorm.  One
@@ -366,6 +407,41 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TI, typename TO, int RATIO>
+hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
+  constexpr int VEC = Vec<TI>::n;
+  constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
+  CompressBatch jb{};
+  int threads = 64;
+  size_t smem = 0;
+  int64_t gx = 1, gy = 1;
+  for (int q = 0; q < n; ++q) {
+    const CompressArgs& a = jobs[q];
+    const int CT = static_cast<int>(a.c / VEC);
+    const int64_t n_ent = a.n_tok / RATIO;
+    const int max_threads = n_ent * a.B >= 1024 ? 256 : 1024;
+    int G = 1;
+    while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
+    threads = CT * G > threads ? CT * G : threads;
+    const size_t sm = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float);
+    smem = sm > smem ? sm : smem;
+    gx = n_ent > gx ? n_ent : gx;
+    gy = a.B > gy ? a.B : gy;
+    jb.j[q] = CompressJobDev{a.Ca, a.Za, a.Cb, a.Zb, a.prev_Cb, a.prev_Zb, a.bias, a.gamma, a.out, a.n_tok, a.pos0,
+                             a.out_batch_stride ? a.out_batch_stride : n_ent * a.c, n_ent, a.B, a.eps,
+                             static_cast<int>(a.c), G};
+  }
+  hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO>),
+                     dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
+                     dim3(static_cast<uint32_t>(threads)), smem + 64 * sizeof(float), s, jb);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+hipError_t launch_batch_r(const CompressArgs* jobs, int n, hipStream_t s) {
+  return jobs[0].ratio == 4 ? launch_batch_t<TI, TO, 4>(jobs, n, s) : launch_batch_t<TI, TO, 128>(jobs, n, s);
+}
+
 template <typename TI, typename TO>
 hipError_t launch_r(const CompressArgs& a, hipStream_t s) {
   return a.ratio == 4 ? launch_t<TI, TO, 4>(a, s) : launch_t<TI, TO, 128>(a, s);
@@ -378,6 +454,20 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.in_dtype == CSA_F32)
     return a.out_dtype == CSA_F32 ? launch_r<float, float>(a, s) : launch_r<float, uint16_t>(a, s);
   return a.out_dtype == CSA_F32 ? launch_r<uint16_t, float>(a, s) : launch_r<uint16_t, uint16_t>(a, s);
+}
+
+hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s) {
+  // jobs with nothing to write are dropped; the rest share ratio and dtypes
+  CompressArgs live[kMaxBatchJobs];
+  int m = 0;
+  for (int q = 0; q < n; ++q)
+    if (jobs[q].B > 0 && jobs[q].n_tok / jobs[q].ratio > 0) live[m++] = jobs[q];
+  if (m == 0) return hipSuccess;
+  const CompressArgs& a = live[0];
+  if (a.in_dtype == CSA_F32)
+    return a.out_dtype == CSA_F32 ? launch_batch_r<float, float>(live, m, s) : launch_batch_r<float, uint16_t>(live, m, s);
+  return a.out_dtype == CSA_F32 ? launch_batch_r<uint16_t, float>(live, m, s)
+                                : launch_batch_r<uint16_t, uint16_t>(live, m, s);
 }
 
 }  // namespace csa

@@ -66,6 +66,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+// up to 4 jobs of one ratio and dtype pair, one launch
+hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s);
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

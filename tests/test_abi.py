@@ -73,6 +73,44 @@ def test_compress_validation(lib):
     assert call(B=0, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None) == 0
 
 
+def test_compress_batch_layout_and_validation(lib, tmp_path):
+    """csa_compress_job as the binding lays it out matches the C compiler's
+    layout, and the batch entry point validates every job."""
+    import ctypes
+    import long_context_sparse_compress_amd as csa
+    if shutil.which("g++"):
+        src = tmp_path / "j.cpp"
+        src.write_text('#include <cstddef>\n#include <cstdio>\n#include "csa.h"\n'
+                       'int main(){printf("%zu %zu %zu %zu\\n", sizeof(csa_compress_job), '
+                       'offsetof(csa_compress_job, eps), offsetof(csa_compress_job, out), '
+                       'offsetof(csa_compress_job, out_batch_stride));}\n')
+        exe = tmp_path / "j"
+        r = subprocess.run(["g++", "-std=c++17", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
+        J = csa._CompressJob
+        assert [int(x) for x in got] == [ctypes.sizeof(J), J.eps.offset, J.out.offset, J.out_batch_stride.offset]
+    lib.csa_compress_batch.argtypes = [ctypes.POINTER(csa._CompressJob), ctypes.c_int, ctypes.c_void_p]
+
+    def job(**kw):
+        d = dict(ratio=4, B=2, n_tok=8, c=512, pos0=0, Ca=A, Za=A, Cb=A, Zb=A, prev_Cb=None, prev_Zb=None,
+                 bias=A, gamma=None, eps=1e-6, in_dtype=1, out_dtype=1, out=A, out_batch_stride=0)
+        d.update(kw)
+        return csa._CompressJob(**d)
+
+    arr = (csa._CompressJob * 2)(job(), job(c=128, Ca=None))
+    assert lib.csa_compress_batch(arr, 2, None) == -1 and "job 1: Ca is NULL" in _err(lib)
+    arr = (csa._CompressJob * 2)(job(), job(ratio=128, n_tok=256, Cb=None, Zb=None))
+    assert lib.csa_compress_batch(arr, 2, None) == -1 and "share ratio" in _err(lib)
+    assert lib.csa_compress_batch(arr, 0, None) == -1 and "n_jobs" in _err(lib)
+    assert lib.csa_compress_batch(None, 1, None) == -1
+    # jobs with nothing to write: succeeds without touching the GPU
+    arr = (csa._CompressJob * 2)(job(n_tok=3, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None),
+                                 job(B=0, Ca=None, Za=None, Cb=None, Zb=None, bias=None, out=None))
+    assert lib.csa_compress_batch(arr, 2, None) == 0
+
+
 def test_index_validation(lib):
     f = lib.lightning_index
 

@@ -119,6 +119,30 @@ def test_c128a_row_split_matches_single_pass(B, n_tok, c, dtype):
             assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 ** -12)
 
 
+@pytest.mark.parametrize("ratio,B,n_tok,pos0", [(4, 32, 4, 65532), (4, 3, 37, 8), (128, 4, 256, 0)])
+def test_batch_matches_single_calls(ratio, B, n_tok, pos0):
+    """csa_compress_batch: a 512-d and a 128-d compression of the same tokens in
+    one launch match the two csa_compress results and the oracle (the batched
+    kernel may contract multiply-adds differently, so equal up to rounding)."""
+    jobs, singles, refs = [], [], []
+    for c in (512, 128):
+        inp = synth.compressor_inputs(f"batch{ratio}_{c}", B, n_tok, c, ratio, pos0, dtype="bf16")
+        d = {k: dev(v, torch.bfloat16 if k != "bias" else torch.float32) for k, v in inp.items()}
+        args = dict(ratio=ratio, Ca=d["Ca"], Za=d["Za"], bias=d["bias"], Cb=d.get("Cb"), Zb=d.get("Zb"),
+                    prev_Cb=d.get("prev_Cb"), prev_Zb=d.get("prev_Zb"), pos0=pos0)
+        jobs.append(args)
+        singles.append(csa.csa_compress(args["ratio"], args["Ca"], args["Za"], args["bias"], args["Cb"], args["Zb"],
+                                        args["prev_Cb"], args["prev_Zb"], pos0=pos0,
+                                        workspace=torch.empty(0, dtype=torch.uint8, device="cuda")))
+        refs.append(oc.compress(inp["Ca"], inp["Za"], inp["bias"], ratio, inp.get("Cb"), inp.get("Zb"),
+                                inp.get("prev_Cb"), inp.get("prev_Zb"), pos0=pos0))
+    outs = csa.csa_compress_batch(jobs)
+    torch.cuda.synchronize()
+    for got, one, ref in zip(outs, singles, refs):
+        assert max_abs(host(got), host(one)) < COMP_BF16_MAX_ABS
+        assert max_abs(host(got), ref) < COMP_BF16_MAX_ABS
+
+
 def test_deterministic():
     _, _, a = _run(128, 2, 1024, 512, 0, "bf16", prefix="det")
     _, _, b = _run(128, 2, 1024, 512, 0, "bf16", prefix="det")
