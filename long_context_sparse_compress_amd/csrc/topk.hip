@@ -101,32 +101,41 @@ __device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32
   }
 }
 
-// Block-wide exclusive scan of one uint32 per thread (blockDim.x <= 1024).
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp /* >= 17 words */, uint32_t* total) {
+// Block-wide exclusive scan of one value per thread (blockDim.x <= 1024):
+// a shuffle scan inside each wave, then wave 0 scans the (at most 16) wave
+// totals the same way.  `tmp` holds >= 17 words; `total` gets the block sum.
+template <typename U>
+__device__ U block_exclusive_scan_t(U v, U* tmp, U* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  uint32_t x = v;
+  U x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
+    const U y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   if (lane == 63) tmp[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const uint32_t t = tmp[w];
-      tmp[w] = run;
-      run += t;
+  if (wid == 0) {
+    const U w0 = lane < nw ? tmp[lane] : U(0);
+    U t = w0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const U y = __shfl_up(t, o, 64);
+      if (lane >= o) t += y;
     }
-    tmp[16] = run;
+    if (lane < nw) tmp[lane] = t - w0;
+    if (lane == nw - 1) tmp[16] = t;
   }
   __syncthreads();
-  const uint32_t r = tmp[wid] + x - v;
+  const U r = tmp[wid] + x - v;
   *total = tmp[16];
   __syncthreads();
   return r;
+}
+
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  return block_exclusive_scan_t<uint32_t>(v, tmp, total);
 }
 
 __device__ __forceinline__ int64_t row_visible(int64_t t, int64_t q_pos0, int ratio, int64_t N) {
@@ -314,31 +323,8 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
 // the 11 + 5-bit digit passes) gives the k-th largest key K; the ordered
 // compaction handles two chunks per block-wide scan of four packed 16-bit
 // counts.  Same result as the LDS path.
-__device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* tmp /* >= 17 words */, uint64_t* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  uint64_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wid] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const uint64_t t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[16] = run;
-  }
-  __syncthreads();
-  const uint64_t r = tmp[wid] + x - v;
-  *total = tmp[16];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* tmp, uint64_t* total) {
+  return block_exclusive_scan_t<uint64_t>(v, tmp, total);
 }
 
 template <int CPT>
