@@ -187,8 +187,11 @@ attn_bf16_kernel(Params P) {
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   // transposing V reads: lane k of group g points at row 4g + k/4, columns 4(k%4)..
   const uint32_t voff = (4 * g + (j >> 2)) * kKsStride + 8 * (j & 3);
-  const int64_t gq = blockIdx.x / P.splits;
-  const int split = static_cast<int>(blockIdx.x % P.splits);
+  // all splits of a query (and its q, and the combine that reads its
+  // partials) on one XCD, so they share that XCD's L2
+  const uint32_t wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int64_t gq = wg / P.splits;
+  const int split = static_cast<int>(wg % P.splits);
   const int64_t b = gq / P.T, t = gq % P.T;
   const List l = make_list(P, t);
   int64_t tile0, tile1;
@@ -471,8 +474,9 @@ attn_f32_kernel(Params P) {
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) uint16_t ot[16 * 128];
-  const int64_t gq = blockIdx.x / 16;
-  const int hb = static_cast<int>(blockIdx.x / 4 % 4), w = static_cast<int>(blockIdx.x % 4);
+  const uint32_t wg = xcd_swizzle(blockIdx.x, gridDim.x);   // the XCD its partials were written on
+  const int64_t gq = wg / 16;
+  const int hb = static_cast<int>(wg / 4 % 4), w = static_cast<int>(wg % 4);
   const int S = P.splits, tid = threadIdx.x;
   constexpr int64_t kSplitFloats = kH * (kD + 2);
   const float* base = P.ws + gq * S * kSplitFloats;
