@@ -49,7 +49,9 @@ inline std::string i2s(int64_t v) { return std::to_string(v); }
 inline int attn_max_splits(int64_t B, int64_t T) {
   const int64_t q = B * T;
   if (q <= 0 || q >= 256) return 1;
-  int64_t s = (1024 + q - 1) / q;
+  // about one workgroup per CU: more splits shorten the kernel but every split
+  // adds a 128 KB partial that the combine must read back
+  int64_t s = (256 + q - 1) / q;
   if (s > kMaxSplits) s = kMaxSplits;
   return static_cast<int>(s < 1 ? 1 : s);
 }
