@@ -99,14 +99,19 @@ template <> struct Frag<CSA_FP8_E4M3> {
   }
   __device__ static constexpr int chunk(int i, int g) { return 2 * g + i; }
 };
-// A key tile staged in LDS as [16-byte chunk][row]: chunk c of the 16 rows is
-// 256 contiguous bytes, so the 16 lanes reading one chunk hit 16 distinct
-// bank groups.  Register i of lane (r, g) is chunk Frag::chunk(i, g) of row r.
+// A key tile staged in LDS row by row, the 16-byte chunks of row r permuted
+// by XOR with swz(r): chunk c of row r sits at r * RB + (c ^ swz(r)) * 16.
+// One direct-to-LDS load then fills 1 KB of whole rows (contiguous in HBM
+// too: full cache lines only), and the 16 lanes that read one chunk of the
+// 16 rows hit 16 distinct 16-byte bank groups.
+template <int RB>
+__device__ __forceinline__ constexpr int tile_swz(int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); }
 template <typename F>
 __device__ __forceinline__ void load_tile_frag(F& f, const uint8_t* tile, int col, int g) {
+  constexpr int RB = F::kRowBytes;
 #pragma unroll
   for (int i = 0; i < F::kRegs; ++i)
-    f.v[i] = *reinterpret_cast<const uint4*>(tile + F::chunk(i, g) * 256 + col * 16);
+    f.v[i] = *reinterpret_cast<const uint4*>(tile + col * RB + ((F::chunk(i, g) ^ tile_swz<RB>(col)) << 4));
 }
 
 // MXFP4: rows of 64 B + 4 scale bytes; lane (r, g) holds bytes [16g, 16g+16)
@@ -153,6 +158,10 @@ __device__ __forceinline__ void qk_tiles(const Frag<QK> (&a)[4], const Frag<QK>&
     }
   }
 }
+
+// max(x, 0) as one integer max on the bit pattern: a float with the sign bit
+// set is a negative int32 (fmaxf would add a canonicalising max per value)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ void store_score(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_score(uint16_t* p, float v) { *p = f32_to_bf16(v); }
@@ -276,10 +285,10 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             const f32x4 c = cc[qi][mt];
-            acc = fmaf(wv[qi][mt][0], fmaxf(c[0], 0.f), acc);
-            acc = fmaf(wv[qi][mt][1], fmaxf(c[1], 0.f), acc);
-            acc = fmaf(wv[qi][mt][2], fmaxf(c[2], 0.f), acc);
-            acc = fmaf(wv[qi][mt][3], fmaxf(c[3], 0.f), acc);
+            acc = fmaf(wv[qi][mt][0], relu(c[0]), acc);
+            acc = fmaf(wv[qi][mt][1], relu(c[1]), acc);
+            acc = fmaf(wv[qi][mt][2], relu(c[2]), acc);
+            acc = fmaf(wv[qi][mt][3], relu(c[3]), acc);
           }
           part[qi][tq] = acc * kscale[cur][tt];
         }
@@ -303,13 +312,26 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
 }
 
 // ---------------------------------------------------------------- ring path
-// bf16 / fp8 keys: each wave streams its TPW tiles through a four-slot ring
-// of LDS tile buffers filled by direct global->LDS loads (no registers held
-// for loads in flight), three tiles ahead of the one being computed.  Each
-// slot is its own LDS array, so the compiler can see that reading slot r does
-// not touch the loads landing in the other slots; the waits for a tile's rows
-// are explicit.  A wave only ever reads its own slots: no barriers.
+// bf16 / fp8 keys: each wave streams its TPW tiles through a D-slot ring of
+// LDS tile buffers filled by direct global->LDS loads (no registers held for
+// loads in flight), D - 1 tiles ahead of the one being computed.  Each slot is
+// its own LDS array, so the compiler can see that reading slot r does not
+// touch the loads landing in the other slots; the waits for a tile's rows are
+// explicit.  A wave only ever reads its own slots: no barriers.
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS 16-byte load (lane l's bytes land at dst + 16 l) and a 4-byte
+// register load, both through a buffer resource over [base, base + bytes):
+// a lane whose offset is out of that range reads nothing.
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, no swizzle
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* dst, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ float buffer_load_f32(const float* base, int bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, kRsrcWord3);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -318,42 +340,62 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <int QK, int QPW, int TPW, typename TS>
+// f(integral_constant<I>) for I = 0 .. N-1, every index a compile-time constant
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int QK, int QPW, int TPW, int D, bool XS, typename TS>
 __global__ void __launch_bounds__(256, 2)
 index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
                   const void* __restrict__ k_scale, TS* __restrict__ scores) {
   static_assert(QK == CSA_BF16 || QK == CSA_FP8_E4M3, "MXFP4 keys use index_mfma_kernel");
-  static_assert(TPW % 4 == 0 && TPW >= 4, "the ring turns four tiles at a time");
+  static_assert(TPW % 4 == 0 && TPW >= D, "scores leave four tiles at a time");
+  static_assert(D == 4 || D == 8, "ring of four or eight slots");
   using F = Frag<QK>;
   constexpr int RB = F::kRowBytes;
   constexpr int TB = 16 * RB;                               // bytes per 16-entry tile
   constexpr int NI = TB / 1024;                             // 1 KB row loads per tile
   constexpr int OPS = NI + (QK == CSA_FP8_E4M3 ? 1 : 0);    // vector memory ops issued per tile
+  static_assert((D - 2) * OPS < 64, "the deepest wait must fit vmcnt");
+  constexpr int QB = QPW * kH * RB;                          // query bytes staged per workgroup
+  static_assert(QB % 4096 == 0, "queries are staged 4 KB (one load per wave) at a time");
+  constexpr int WN = QK == CSA_FP8_E4M3 ? 2 * QPW : QPW;     // 256-byte weight / scale rows staged
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.z;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * QPW;
-  const int64_t e_wave = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * (TPW * 16);
+  uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (XS) {
+    // each XCD takes a contiguous range of workgroups: measured on MI355X, a
+    // stream of whole 512 KB key runs reads HBM about 10% faster this way
+    // than with the round-robin spread of neighbouring runs over the XCDs
+    const uint32_t lin = bx + gridDim.x * (by + gridDim.y * bz);
+    const uint32_t sw = xcd_swizzle(lin, gridDim.x * gridDim.y * gridDim.z);
+    bx = sw % gridDim.x;
+    by = (sw / gridDim.x) % gridDim.y;
+    bz = sw / (gridDim.x * gridDim.y);
+  }
+  const int64_t b = bz;
+  const int64_t t0 = static_cast<int64_t>(by) * QPW;
+  const int64_t e_wave = (static_cast<int64_t>(bx) * 4 + wid) * (TPW * 16);
 
-  __shared__ __attribute__((aligned(16))) uint8_t qs[QPW * kH * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[QB + WN * kH * 4];
   __shared__ __attribute__((aligned(16))) uint8_t ring0[4][TB];
   __shared__ __attribute__((aligned(16))) uint8_t ring1[4][TB];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[4][TB];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[4][TB];
-  for (int o = threadIdx.x * 16; o < QPW * kH * RB; o += 256 * 16) {
-    const int qi = o / (kH * RB);
-    int64_t t = t0 + qi;
-    if (t >= T) t = T - 1;
-    *reinterpret_cast<uint4*>(qs + o) = *reinterpret_cast<const uint4*>(q + (b * T + t) * kH * RB + o % (kH * RB));
-  }
-  __syncthreads();
-  if (e_wave >= N) return;
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[D > 4 ? 4 : 1][D > 4 ? TB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring5[D > 4 ? 4 : 1][D > 4 ? TB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring6[D > 4 ? 4 : 1][D > 4 ? TB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring7[D > 4 ? 4 : 1][D > 4 ? TB : 16];
 
-  F qa[QPW][4];
-  float wv[QPW][4][4];
+  // which entries each query sees (scalar arithmetic only)
   int64_t vis[QPW];
   int64_t vis_max = 0;
 #pragma unroll
@@ -364,77 +406,117 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     if (v > N) v = N;
     vis[qi] = (t0 + qi < T) ? v : 0;
     vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
-    const int64_t qrow = (b * T + t) * kH;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      qa[qi][mt].load(qs + (qi * kH + mt * 16 + col) * RB, g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = mt * 16 + 4 * g + i;
-        float wt = w[qrow + h];
-        if constexpr (QK == CSA_FP8_E4M3) wt *= static_cast<const float*>(q_scale)[qrow + h];
-        wv[qi][mt][i] = wt;
-      }
-    }
   }
-  const int qsc[4] = {127, 127, 127, 127};
-  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
+  const bool streams = e_wave < vis_max;   // wave-uniform (vis_max <= N)
 
-  if (e_wave >= vis_max) {   // nothing of this wave's run is visible to any of its queries
+  // The workgroup's queries and head weights go to LDS by direct loads, then
+  // the first D - 1 key tiles follow: all of their latencies overlap.
+  // Wave w's i-th query load fills bytes [(4i + w) KB, (4i + w + 1) KB) of qs.
 #pragma unroll
-    for (int tb = 0; tb < TPW; tb += 4) {
-      const int64_t e = e_wave + 16 * (tb + g) + col;
+  for (int i = 0; i < QB / 4096; ++i) {
+    const int o = (4 * i + wid) * 1024;
+    const int qi = o / (kH * RB);
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    const uint8_t* src = q + (b * T + t) * kH * RB + o % (kH * RB) + 16 * lane;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(qs + o), 16, 0, 0);
+  }
+  // The head weights (and fp8 query scales) of query qi follow: 64 floats,
+  // one 4-byte load per lane, into the same LDS array.  Every wave loads them
+  // (the same values to the same place): no branch around a load into LDS.
 #pragma unroll
-      for (int qi = 0; qi < QPW; ++qi)
-        if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, -INFINITY);
-    }
-    return;
+  for (int j = 0; j < WN; ++j) {
+    const int qi = j % QPW;
+    int64_t t = t0 + qi;
+    if (t >= T) t = T - 1;
+    const float* src = (j < QPW ? w : static_cast<const float*>(q_scale)) + (b * T + t) * kH + lane;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(qs + QB + j * kH * 4), 4, 0, 0);
   }
 
-  // lane l's share of a tile's row loads: row l % 16, chunks 4j + l / 16
   const int64_t krow0 = b * N;
-  float ks[4] = {1.f, 1.f, 1.f, 1.f};   // fp8 key row scales of the tiles in the ring
+  float ks[D];   // fp8 key row scales of the tiles in the ring
+#pragma unroll
+  for (int r = 0; r < D; ++r) ks[r] = 1.f;
   auto slot = [&](auto rc) -> uint8_t* {
     constexpr int r = decltype(rc)::value;
     if constexpr (r == 0) return ring0[wid];
     else if constexpr (r == 1) return ring1[wid];
     else if constexpr (r == 2) return ring2[wid];
-    else return ring3[wid];
+    else if constexpr (r == 3) return ring3[wid];
+    else if constexpr (r == 4) return ring4[wid];
+    else if constexpr (r == 5) return ring5[wid];
+    else if constexpr (r == 6) return ring6[wid];
+    else return ring7[wid];
   };
+  // Load j of a tile fills rows RPI j .. RPI j + RPI - 1; lane l takes chunk
+  // position l % CPR of row RPI j + l / CPR, i.e. chunk (l % CPR) ^ swz(row).
+  // The loads go through a buffer resource whose base is the tile's first row
+  // and whose size ends at row N - 1: the lane offsets are fixed, the per-tile
+  // address arithmetic is scalar, and rows past N - 1 read nothing (their
+  // scores are never stored).  A wave with nothing visible reads row N - 1.
+  constexpr int CPR = RB / 16, RPI = 64 / CPR;
+  uint32_t voff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int row = RPI * j + lane / CPR;
+    voff[j] = static_cast<uint32_t>(row * RB + (((lane % CPR) ^ tile_swz<RB>(row)) << 4));
+  }
   auto issue = [&](int t, auto rc) {
     constexpr int r = decltype(rc)::value;
     uint8_t* dst = slot(rc);
-    int64_t e = e_wave + 16 * t + col;
-    if (e >= N) e = N - 1;
-    const uint8_t* src = k + (krow0 + e) * RB + g * 16;
+    const int64_t e0 = streams ? e_wave + 16 * t : N - 1;
+    const int rows = static_cast<int>(N - e0 < 16 ? N - e0 : 16);   // rows of this tile inside [0, N)
+    const uint8_t* base = k + (krow0 + e0) * RB;
     wait_lgkm0();   // this wave's reads of the slot's previous tile are done
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 64 * j), (lds_void*)(dst + 1024 * j), 16, 0, 0);
-    if constexpr (QK == CSA_FP8_E4M3) ks[r] = static_cast<const float*>(k_scale)[krow0 + e];
+    for (int j = 0; j < NI; ++j) buffer_load_lds16(base, rows * RB, dst + 1024 * j, voff[j]);
+    if constexpr (QK == CSA_FP8_E4M3)   // the scale of this lane's key column
+      ks[r] = buffer_load_f32(static_cast<const float*>(k_scale) + krow0 + e0, rows * 4, col * 4);
   };
-  issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
-  issue(2, std::integral_constant<int, 2>{});
+  // Every wave runs the whole ring, also one whose entries are all masked or
+  // past N (its loads all read entry N - 1, its tiles are skipped and its
+  // scores are -inf): with no branch around a load into LDS the compiler keeps
+  // track of which LDS array each load in flight fills, and reading qs below
+  // does not wait for the key tiles.
+  static_for<0, D - 1>([&](auto rc) { issue(decltype(rc)::value, rc); });
+  wait_vm<(D - 1) * OPS>();   // this wave's query and weight loads have landed ...
+  // ... and every other wave's: a bare barrier (__syncthreads' release fence
+  // would also wait for the key tiles still in flight)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  F qa[QPW][4];
+  float wv[QPW][4][4];   // weights of heads 16 mt + 4 g + i: this lane's accumulator rows
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      qa[qi][mt].load(qs + (qi * kH + mt * 16 + col) * RB, g);
+      float4 wt = *reinterpret_cast<const float4*>(qs + QB + (qi * kH + mt * 16 + 4 * g) * 4);
+      if constexpr (QK == CSA_FP8_E4M3) {
+        const float4 s4 = *reinterpret_cast<const float4*>(qs + QB + ((QPW + qi) * kH + mt * 16 + 4 * g) * 4);
+        wt.x *= s4.x; wt.y *= s4.y; wt.z *= s4.z; wt.w *= s4.w;
+      }
+      wv[qi][mt][0] = wt.x; wv[qi][mt][1] = wt.y; wv[qi][mt][2] = wt.z; wv[qi][mt][3] = wt.w;
+    }
+  const int qsc[4] = {127, 127, 127, 127};
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
 
   float sc[QPW][TPW / 4];
+  float part[QPW][4];
+  static_for<0, TPW>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    constexpr int r = t % D;
+    // rows of tile t have landed once at most the ops of the (up to D - 2)
+    // tiles issued after it are outstanding
+    constexpr int later = (TPW - 1 - t) < (D - 2) ? (TPW - 1 - t) : (D - 2);
+    wait_vm<later * OPS>();
+    if constexpr (t + D - 1 < TPW) issue(t + D - 1, std::integral_constant<int, (t + D - 1) % D>{});
 #pragma unroll
-  for (int tb = 0; tb < TPW; tb += 4) {
-    float part[QPW][4];
-    auto tile = [&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      const int t = tb + r;
-      // rows of tile t have landed once at most the ops of the (up to two)
-      // tiles issued after it are outstanding
-      if (t + 2 < TPW) wait_vm<2 * OPS>();
-      else if (t + 1 < TPW) wait_vm<OPS>();
-      else wait_vm<0>();
-      if (t + 3 < TPW) issue(t + 3, std::integral_constant<int, (r + 3) & 3>{});
-#pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) part[qi][r] = 0.f;
-      if (e_wave + 16 * t >= vis_max) return;   // whole tile masked for every query (wave-uniform)
+    for (int qi = 0; qi < QPW; ++qi) part[qi][t & 3] = 0.f;
+    if (e_wave + 16 * t < vis_max) {   // else the whole tile is masked for every query (wave-uniform)
       F kf;
-      load_tile_frag(kf, slot(rc), col, g);
+      load_tile_frag(kf, slot(std::integral_constant<int, r>{}), col, g);
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
         f32x4 cc[4];
@@ -442,31 +524,29 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         float acc = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          acc = fmaf(wv[qi][mt][0], fmaxf(cc[mt][0], 0.f), acc);
-          acc = fmaf(wv[qi][mt][1], fmaxf(cc[mt][1], 0.f), acc);
-          acc = fmaf(wv[qi][mt][2], fmaxf(cc[mt][2], 0.f), acc);
-          acc = fmaf(wv[qi][mt][3], fmaxf(cc[mt][3], 0.f), acc);
+          acc = fmaf(wv[qi][mt][0], relu(cc[mt][0]), acc);
+          acc = fmaf(wv[qi][mt][1], relu(cc[mt][1]), acc);
+          acc = fmaf(wv[qi][mt][2], relu(cc[mt][2]), acc);
+          acc = fmaf(wv[qi][mt][3], relu(cc[mt][3]), acc);
         }
-        part[qi][r] = acc * ks[r];
+        part[qi][t & 3] = acc * ks[r];
       }
-    };
-    tile(std::integral_constant<int, 0>{});
-    tile(std::integral_constant<int, 1>{});
-    tile(std::integral_constant<int, 2>{});
-    tile(std::integral_constant<int, 3>{});
-    // reduce-scatter over the four lane groups: lane group g keeps tile tb + g
-    const int64_t e = e_wave + 16 * (tb + g) + col;
-    const bool hi = g >= 2, odd = g & 1;
-#pragma unroll
-    for (int qi = 0; qi < QPW; ++qi) {
-      float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
-      k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
-      k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
-      float v = odd ? k1 : k0;
-      v += lane_read(x16, odd ? k0 : k1);
-      sc[qi][tb / 4] = (e >= vis[qi]) ? -INFINITY : v;
     }
-  }
+    if constexpr ((t & 3) == 3) {
+      // reduce-scatter over the four lane groups: lane group g keeps tile t - 3 + g
+      const int64_t e = e_wave + 16 * (t - 3 + g) + col;
+      const bool hi = g >= 2, odd = g & 1;
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
+        k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
+        k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
+        float v = odd ? k1 : k0;
+        v += lane_read(x16, odd ? k0 : k1);
+        sc[qi][t / 4] = (e >= vis[qi]) ? -INFINITY : v;
+      }
+    }
+  });
   // scores leave after the last tile: no stores among the counted row loads
 #pragma unroll
   for (int tb = 0; tb < TPW; tb += 4) {
@@ -477,7 +557,7 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 }
 
-template <int QK, int QPW, int TPW>
+template <int QK, int QPW, int TPW, int D, bool XS>
 hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
   dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
@@ -485,10 +565,10 @@ hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
   if (a.score_dtype == CSA_BF16)
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores));
   else
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, float>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, float>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores));
   return hipGetLastError();
 }
@@ -513,14 +593,19 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
 
 template <int QK>
 hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
-  // tiles per wave from sweeps on MI355X (decode: HBM streaming, one query per
-  // wave; prefill: two queries per wave share each key tile)
+  // Shapes from sweeps on MI355X.  Decode streams keys from HBM: one query per
+  // wave, 32 tiles per wave, a 4-slot ring (an 8-slot ring was slower), each
+  // XCD on a contiguous range of key runs.  Prefill is MFMA and VALU work on
+  // keys that stay in cache: fp8 runs one query per wave (about 110 VGPRs, so
+  // two waves share a SIMD and one's MFMAs overlap the other's ReLU-and-sum);
+  // bf16 lets two queries share each key tile.
   if constexpr (QK == CSA_MXFP4) {
     if (a.T <= 2) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
     return launch_mfma<QK, 2, 64, 4, 2>(a, s);
   } else {
-    if (a.T <= 2) return launch_ring<QK, 1, 32>(a, s);
-    return launch_ring<QK, 2, 64>(a, s);
+    if (a.T <= 2) return launch_ring<QK, 1, 32, 4, true>(a, s);
+    if constexpr (QK == CSA_FP8_E4M3) return launch_ring<QK, 1, 64, 4, false>(a, s);
+    return launch_ring<QK, 2, 64, 4, false>(a, s);
   }
 }
 
