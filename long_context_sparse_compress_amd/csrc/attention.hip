@@ -170,19 +170,28 @@ __device__ __forceinline__ void lds_barrier() {
 // tb0 are then provably disjoint from the loads in flight (distinct arrays),
 // so the compiler does not make them wait for those loads.  A copy, not two
 // alternating buffers, keeps one copy of the loop body, which fits the 256
-// registers that two workgroups per CU allow.
-__global__ void __launch_bounds__(256, 2)
+// registers that two waves per SIMD allow.
+//
+// TGN tile groups of four waves share a workgroup (two for long decode runs): group k
+// takes tiles tile0 + k, tile0 + k + TGN, ... of the workgroup's run with its
+// own buffers, so a run of n tiles takes ceil(n / TGN) steps.  The groups'
+// running (max, sum, O) are merged through LDS at the end.
+template <int TGN>
+__global__ void __launch_bounds__(256 * TGN, 3 - TGN)
 attn_bf16_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
+  static_assert(TGN == 1 || TGN == 2, "one or two tile groups");
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[TGN][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[TGN][kTileBytes];
   __shared__ int32_t sidx[CSA_MAX_TOPK];                                   // Top-k row of this query
-  __shared__ uint4 pshare[4 * 64];   // P of each wave's 16 heads, in MFMA operand order (lane-major)
-  __shared__ float4 ashare[kH / 4];  // per-head rescale factor of the current tile
-  __shared__ float4 fshare[kH / 4];  // per-head output factor (epilogue)
-  __shared__ uint4 rescale_any;      // per wave: some head's running max moved
+  __shared__ uint4 pshare[TGN][4 * 64];   // P of each wave's 16 heads, in MFMA operand order (lane-major)
+  __shared__ float4 ashare[TGN][kH / 4];  // per-head rescale factor of the current tile
+  __shared__ float4 fshare[kH / 4];       // per-head output factor (epilogue)
+  __shared__ uint4 rescale_any[TGN];      // per wave: some head's running max moved
+  __shared__ float mlshare[TGN][2][kH];   // per group: running max and sum of each head (merge)
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row addressing stays scalar
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row addressing stays scalar
+  const int tg = TGN == 1 ? 0 : (wv >> 2), wid = wv & 3;     // tile group, wave within the group
   const int j = lane & 15, g = lane >> 4;
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   // transposing V reads: lane k of group g points at row 4g + k/4, columns 4(k%4)..
@@ -196,6 +205,8 @@ attn_bf16_kernel(Params P) {
   const List l = make_list(P, t);
   int64_t tile0, tile1;
   split_range(P, l, split, tile0, tile1);
+  uint8_t* const T0 = tb0[tg];
+  uint8_t* const T1 = tb1[tg];
 
   // The query's own raw row is always in the list: padding rows load it (and are masked).
   const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) +
@@ -205,19 +216,19 @@ attn_bf16_kernel(Params P) {
     const uint16_t* p = row_ptr_by<uint16_t>(P, b, l, tile * kTile + 8 * wid + (lane & 7), slot);
     return reinterpret_cast<uint64_t>(p ? p : safe_row);
   };
-  // row 8w + e of a tile, from lane e's source, into tb1
+  // row 8w + e of a tile, from lane e's source, into this group's tb1
   auto issue_row = [&](uint64_t src, int e) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(src), e);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(src >> 32), e);
     row_to_lds(reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo),
-               tb1 + (8 * wid + e) * kKsStride, lane);
+               T1 + (8 * wid + e) * kKsStride, lane);
   };
 
-  // The first tile's rows go out before anything else, their indices read
-  // straight from global memory.
-  if (tile0 < tile1) {
+  // The group's first tile's rows go out before anything else, their indices
+  // read straight from global memory.
+  if (tile0 + tg < tile1) {
     const int32_t* gidx = P.idx ? P.idx + gq * P.k : nullptr;   // only read for a Top-k list
-    const uint64_t src = row_source(tile0, [&](int64_t q) { return gidx[q]; });
+    const uint64_t src = row_source(tile0 + tg, [&](int64_t q) { return gidx[q]; });
 #pragma unroll
     for (int e = 0; e < 8; ++e) issue_row(src, e);
   }
@@ -236,7 +247,7 @@ attn_bf16_kernel(Params P) {
     const int64_t p0 = tile0 * kTile;
     const int64_t p1 = tile1 * kTile < l.n_cmp ? tile1 * kTile : l.n_cmp;
     const int32_t* src = P.idx + gq * P.k;
-    for (int64_t p = p0 + tid; p < p1; p += 256) sidx[p] = src[p];
+    for (int64_t p = p0 + tid; p < p1; p += 256 * TGN) sidx[p] = src[p];
     __syncthreads();
   }
 
@@ -247,108 +258,118 @@ attn_bf16_kernel(Params P) {
   for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // one tile: wait for its rows (keeping later tiles in flight), refill the
-  // buffer freed by the previous tile, compute
-  auto step = [&](int64_t tile) {
-    const uint8_t* Ks = tb0;
+  // one step: wait for the group's tile (keeping its next one in flight),
+  // refill the buffer freed by the previous tile, compute.  Every wave takes
+  // part in the barriers; a group whose run has ended only waits.
+  auto step = [&](int64_t tile, bool active) {
+    constexpr int kPipe = 2;
+    const uint8_t* Ks = T0;
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's rows landed in tb1
     lds_barrier();   // nobody still reads tb0
+    if (active) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int off = (8 * wid + e) * kKsStride + lane * 16;
-      *reinterpret_cast<uint4*>(tb0 + off) = *reinterpret_cast<const uint4*>(tb1 + off);
+      for (int e = 0; e < 8; ++e) {
+        const int off = (8 * wid + e) * kKsStride + lane * 16;
+        *reinterpret_cast<uint4*>(T0 + off) = *reinterpret_cast<const uint4*>(T1 + off);
+      }
     }
     lds_barrier();   // tb0 holds the tile; tb1 is free
-    const bool refill = tile + 1 < tile1;
-    const uint64_t nsrc = refill ? row_source(tile + 1, [&](int64_t q) { return sidx[q]; }) : 0;
+    if (active) {
+      const bool refill = tile + TGN < tile1;
+      const uint64_t nsrc = refill ? row_source(tile + TGN, [&](int64_t q) { return sidx[q]; }) : 0;
 
-    // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1).  LDS operands are read
-    // kPipe k-steps ahead through a register ring, so an MFMA never waits on
-    // the read issued just before it.
-    constexpr int kPipe = 2;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* ka = Ks + j * kKsStride + g * 256;
-    uint4 ra[kPipe][2];
+      // S^T = K Q^T for rows 0..15 (s0) and 16..31 (s1).  LDS operands are read
+      // kPipe k-steps ahead through a register ring, so an MFMA never waits on
+      // the read issued just before it.
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* ka = Ks + j * kKsStride + g * 256;
+      uint4 ra[kPipe][2];
 #pragma unroll
-    for (int d = 0; d < kPipe; ++d) {
-      ra[d][0] = *reinterpret_cast<const uint4*>(ka + d * 16);
-      ra[d][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + d * 16);
-    }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      // the next tile's rows go out one at a time between MFMAs: a burst of
-      // row loads would stall this wave until the memory pipeline drains
-      if (refill && (s & 1) == 0) issue_row(nsrc, s / 2);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][0]), as_bf16x8(qf[s]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][1]), as_bf16x8(qf[s]), s1, 0, 0, 0);
-      if (s + kPipe < 16) {
-        ra[s % kPipe][0] = *reinterpret_cast<const uint4*>(ka + (s + kPipe) * 16);
-        ra[s % kPipe][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + (s + kPipe) * 16);
+      for (int d = 0; d < kPipe; ++d) {
+        ra[d][0] = *reinterpret_cast<const uint4*>(ka + d * 16);
+        ra[d][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + d * 16);
       }
-    }
-    // rows of this lane: 4g+i (s0) and 16+4g+i (s1); padding rows are masked
-    // which of the tile's 32 rows are real: lane r (mod 32) tests row r
-    const uint32_t vrows =
-        static_cast<uint32_t>(__ballot(row_valid(P, l, tile * kTile + (lane & 31), sidx))) >> (4 * g);
-    float lg[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lg[i] = (vrows >> i) & 1 ? s0[i] * P.scale_log2 : -INFINITY;
-      lg[4 + i] = (vrows >> (16 + i)) & 1 ? s1[i] * P.scale_log2 : -INFINITY;
-    }
-    float mt = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, lg[i]);
-    mt = fmaxf(mt, lane_read(x16, mt));
-    mt = fmaxf(mt, lane_read(x32, mt));
-    const float m_new = fmaxf(m_run, mt);
-    const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = none ? 0.f : fast_exp2(lg[i] - m_new);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // hand this wave's P and rescale factors to the other waves
-    pshare[wid * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-    if (g == 0) reinterpret_cast<float*>(ashare)[16 * wid + j] = alpha;
-    const bool moved = __ballot(alpha != 1.f) != 0;
-    if (lane == 0) reinterpret_cast<uint32_t*>(&rescale_any)[wid] = moved;
-    lds_barrier();
-
-    // O[:, 128 w .. 128 w + 127] = alpha O + P V over all 64 heads
-    const uint4 any = rescale_any;
-    if (any.x | any.y | any.z | any.w) {
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        const float4 a4 = ashare[4 * hb + g];
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          o[8 * hb + db][0] *= a4.x; o[8 * hb + db][1] *= a4.y;
-          o[8 * hb + db][2] *= a4.z; o[8 * hb + db][3] *= a4.w;
+      for (int s = 0; s < 16; ++s) {
+        // the next tile's rows go out one at a time between MFMAs: a burst of
+        // row loads would stall this wave until the memory pipeline drains
+        if (refill && (s & 1) == 0) issue_row(nsrc, s / 2);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][0]), as_bf16x8(qf[s]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][1]), as_bf16x8(qf[s]), s1, 0, 0, 0);
+        if (s + kPipe < 16) {
+          ra[s % kPipe][0] = *reinterpret_cast<const uint4*>(ka + (s + kPipe) * 16);
+          ra[s % kPipe][1] = *reinterpret_cast<const uint4*>(ka + 16 * kKsStride + (s + kPipe) * 16);
         }
       }
+      // rows of this lane: 4g+i (s0) and 16+4g+i (s1); padding rows are masked
+      // which of the tile's 32 rows are real: lane r (mod 32) tests row r
+      const uint32_t vrows =
+          static_cast<uint32_t>(__ballot(row_valid(P, l, tile * kTile + (lane & 31), sidx))) >> (4 * g);
+      float lg[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lg[i] = (vrows >> i) & 1 ? s0[i] * P.scale_log2 : -INFINITY;
+        lg[4 + i] = (vrows >> (16 + i)) & 1 ? s1[i] * P.scale_log2 : -INFINITY;
+      }
+      float mt = lg[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, lg[i]);
+      mt = fmaxf(mt, lane_read(x16, mt));
+      mt = fmaxf(mt, lane_read(x32, mt));
+      const float m_new = fmaxf(m_run, mt);
+      const bool none = (m_new == -INFINITY);
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = none ? 0.f : fast_exp2(lg[i] - m_new);
+        psum += p[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // hand this wave's P and rescale factors to the other waves of the group
+      pshare[tg][wid * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+      if (g == 0) reinterpret_cast<float*>(ashare[tg])[16 * wid + j] = alpha;
+      const bool moved = __ballot(alpha != 1.f) != 0;
+      if (lane == 0) reinterpret_cast<uint32_t*>(&rescale_any[tg])[wid] = moved;
     }
-    bf16x8 pf[4];
+    lds_barrier();
+    if (active) {
+      // O[:, 128 w .. 128 w + 127] = alpha O + P V over all 64 heads
+      const uint4 any = rescale_any[tg];
+      if (any.x | any.y | any.z | any.w) {
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pf[hb] = as_bf16x8(pshare[hb * 64 + lane]);
-    bf16x8 vr[kPipe];
+        for (int hb = 0; hb < 4; ++hb) {
+          const float4 a4 = ashare[tg][4 * hb + g];
 #pragma unroll
-    for (int d = 0; d < kPipe; ++d) vr[d] = v_operand(Ks, 8 * wid + d, voff);
+          for (int db = 0; db < 8; ++db) {
+            o[8 * hb + db][0] *= a4.x; o[8 * hb + db][1] *= a4.y;
+            o[8 * hb + db][2] *= a4.z; o[8 * hb + db][3] *= a4.w;
+          }
+        }
+      }
+      bf16x8 pf[4];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+      for (int hb = 0; hb < 4; ++hb) pf[hb] = as_bf16x8(pshare[tg][hb * 64 + lane]);
+      bf16x8 vr[kPipe];
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-        o[8 * hb + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], vr[db % kPipe], o[8 * hb + db], 0, 0, 0);
-      if (db + kPipe < 8) vr[db % kPipe] = v_operand(Ks, 8 * wid + db + kPipe, voff);
+      for (int d = 0; d < kPipe; ++d) vr[d] = v_operand(Ks, 8 * wid + d, voff);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[8 * hb + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], vr[db % kPipe], o[8 * hb + db], 0, 0, 0);
+        if (db + kPipe < 8) vr[db % kPipe] = v_operand(Ks, 8 * wid + db + kPipe, voff);
+      }
     }
   };
 
-  for (int64_t tile = tile0; tile < tile1; ++tile) step(tile);
+  const int64_t nsteps = (tile1 - tile0 + TGN - 1) / TGN;
+  for (int64_t i = 0; i < nsteps; ++i) {
+    const int64_t tile = tile0 + tg + i * TGN;
+    step(tile, tile < tile1);
+  }
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
   float l_tot = l_run;
@@ -356,23 +377,85 @@ attn_bf16_kernel(Params P) {
   l_tot += lane_read(x32, l_tot);
   const int head_j = 16 * wid + j;
 
-  if (P.splits == 1) {
-    float M = m_run;
-    float zl = -INFINITY;
-    if (P.sink) {
-      zl = P.sink[head_j] * kLog2e;
-      M = fmaxf(M, zl);
-    }
-    const float em = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-    const float denom = l_tot * em + (P.sink ? fast_exp2(zl - M) : 0.f);
+  // o[] is indexed with constants only (a run-time index would move it to
+  // scratch memory): the group-dependent parts below branch on the group and
+  // run code in which the group is a constant.
+  if constexpr (TGN == 2) {
+    // The two groups merge their (max, sum, O) through LDS.  Group k keeps the
+    // head blocks 2k, 2k+1 (o[16k .. 16k+15]): it parks the other half for the
+    // other group and folds that group's parked copy of its own half in.
     if (g == 0) {
+      mlshare[tg][0][head_j] = m_run;
+      mlshare[tg][1][head_j] = l_tot;
+    }
+    lds_barrier();   // every wave is past its last tile: the tile buffers are free
+    auto park = [&](auto kc) {   // 16 KB per wave: group 0 parks in tb0, group 1 in tb1
+      constexpr int k = decltype(kc)::value;
+      float4* mine = reinterpret_cast<float4*>((k == 0 ? &tb0[0][0] : &tb1[0][0]) + wid * 16384) + lane;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const f32x4& v = o[16 * (1 - k) + n];
+        mine[n * 64] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    };
+    if (tg == 0) park(std::integral_constant<int, 0>{});
+    else park(std::integral_constant<int, 1>{});
+    lds_barrier();
+    auto fold = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const float4* theirs = reinterpret_cast<const float4*>((k == 0 ? &tb1[0][0] : &tb0[0][0]) + wid * 16384) + lane;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int hb = 2 * k + hh;
+        float am[4], at[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 16 * hb + 4 * g + i;
+          const float mm = mlshare[k][0][h], mo = mlshare[1 - k][0][h];
+          const float M = fmaxf(mm, mo);
+          am[i] = mm == -INFINITY ? 0.f : fast_exp2(mm - M);
+          at[i] = mo == -INFINITY ? 0.f : fast_exp2(mo - M);
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const float4 v = theirs[(8 * hh + db) * 64];
+          f32x4& x = o[8 * hb + db];
+          x[0] = x[0] * am[0] + v.x * at[0];
+          x[1] = x[1] * am[1] + v.y * at[1];
+          x[2] = x[2] * am[2] + v.z * at[2];
+          x[3] = x[3] * am[3] + v.w * at[3];
+        }
+      }
+    };
+    if (tg == 0) fold(std::integral_constant<int, 0>{});
+    else fold(std::integral_constant<int, 1>{});
+    const float m0 = mlshare[0][0][head_j], m1 = mlshare[1][0][head_j];
+    const float M = fmaxf(m0, m1);
+    l_tot = (m0 == -INFINITY ? 0.f : mlshare[0][1][head_j] * fast_exp2(m0 - M)) +
+            (m1 == -INFINITY ? 0.f : mlshare[1][1][head_j] * fast_exp2(m1 - M));
+    m_run = M;
+  }
+  // whether this wave writes head block hb: all four, or its group's two (uniform)
+  auto writes = [&](int hb) { return TGN == 1 || (hb >> 1) == tg; };
+
+  if (P.splits == 1) {
+    if (tg == 0 && g == 0) {
+      float M = m_run;
+      float zl = -INFINITY;
+      if (P.sink) {
+        zl = P.sink[head_j] * kLog2e;
+        M = fmaxf(M, zl);
+      }
+      const float em = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+      const float denom = l_tot * em + (P.sink ? fast_exp2(zl - M) : 0.f);
       reinterpret_cast<float*>(fshare)[head_j] = em / denom;
       if (P.lse) P.lse[gq * kH + head_j] = kLn2 * (M + log2f(denom));
     }
-    __syncthreads();
+    lds_barrier();
     uint16_t* out = static_cast<uint16_t*>(P.out) + gq * kH * kD + 128 * wid + j;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
+      if (!writes(hb)) continue;
       const float4 f4 = fshare[4 * hb + g];
       const float f[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
@@ -386,13 +469,15 @@ attn_bf16_kernel(Params P) {
     float* w = P.ws + (gq * P.splits + split) * (kH * (kD + 2));
     float4* wo = reinterpret_cast<float4*>(w) + wid * (4 * 8 * 64) + lane;
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
+    for (int hb = 0; hb < 4; ++hb) {
+      if (!writes(hb)) continue;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const f32x4& v = o[8 * hb + db];
         wo[(hb * 8 + db) * 64] = make_float4(v[0], v[1], v[2], v[3]);
       }
-    if (g == 0) {
+    }
+    if (tg == 0 && g == 0) {
       w[kH * kD + head_j] = m_run;
       w[kH * kD + kH + head_j] = l_tot;
     }
@@ -560,7 +645,16 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   int64_t ncmp = a.idx ? a.k : (last + 1) / a.ratio;
   if (!a.idx && ncmp > a.N) ncmp = a.N;
   P.splits = attn_splits(a.B, a.T, ncmp + wlen);
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
+  // Long runs of tiles per workgroup (decode over long lists): two tile groups
+  // take two tiles per step.  Measured on MI355X a step of two groups costs
+  // about 1.35 of a one-group step, and the groups' second q load and their
+  // merge add about 4 us, so short runs keep one group.
+  const int64_t ntiles = (ncmp + wlen + kAttnTile - 1) / kAttnTile;
+  const int64_t per_split = (ntiles + P.splits - 1) / P.splits;
+  if (P.splits > 1 && per_split >= 8)
+    hipLaunchKernelGGL(attn_bf16_kernel<2>, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0, s, P);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<1>, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
   if (P.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
   return hipGetLastError();
