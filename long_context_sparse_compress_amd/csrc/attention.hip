@@ -35,6 +35,8 @@
 // Decode has few queries, so a query's tiles are split over several
 // workgroups whose partial (max, sum, O) go to the workspace; a combine
 // kernel merges them in a fixed order (bit-reproducible results).
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -164,13 +166,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Tile buffers: rows arrive by DMA in tb1; at the top of each step the landed
-// tile is copied into tb0, where it is computed, and tb1 takes the next
-// tile's rows, requested one row at a time between the QK MFMAs.  Reads of
-// tb0 are then provably disjoint from the loads in flight (distinct arrays),
-// so the compiler does not make them wait for those loads.  A copy, not two
-// alternating buffers, keeps one copy of the loop body, which fits the 256
-// registers that two waves per SIMD allow.
+// Tile buffers: while tile t is computed, tile t + 1's rows arrive by DMA in
+// the other buffer, requested one row at a time between the QK MFMAs, and
+// every read of the tile being computed must be provably disjoint from the
+// loads in flight (distinct LDS arrays), or the compiler drains them before
+// each LDS read.  With two groups the buffers alternate and the loop body is
+// instantiated once per buffer.  One group keeps a single body: rows land in
+// tb1 and each step first copies them into tb0 (two bodies do not fit its
+// registers: the spill reloads, being memory loads, wait for every row load
+// in flight).
 //
 // TGN tile groups of four waves share a workgroup (two for long decode runs): group k
 // takes tiles tile0 + k, tile0 + k + TGN, ... of the workgroup's run with its
@@ -216,12 +220,12 @@ attn_bf16_kernel(Params P) {
     const uint16_t* p = row_ptr_by<uint16_t>(P, b, l, tile * kTile + 8 * wid + (lane & 7), slot);
     return reinterpret_cast<uint64_t>(p ? p : safe_row);
   };
-  // row 8w + e of a tile, from lane e's source, into this group's tb1
-  auto issue_row = [&](uint64_t src, int e) {
+  // row 8w + e of a tile, from lane e's source, into tile buffer `dst`
+  auto issue_row = [&](uint64_t src, int e, uint8_t* dst) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(src), e);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(src >> 32), e);
     row_to_lds(reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo),
-               T1 + (8 * wid + e) * kKsStride, lane);
+               dst + (8 * wid + e) * kKsStride, lane);
   };
 
   // The group's first tile's rows go out before anything else, their indices
@@ -230,7 +234,7 @@ attn_bf16_kernel(Params P) {
     const int32_t* gidx = P.idx ? P.idx + gq * P.k : nullptr;   // only read for a Top-k list
     const uint64_t src = row_source(tile0 + tg, [&](int64_t q) { return gidx[q]; });
 #pragma unroll
-    for (int e = 0; e < 8; ++e) issue_row(src, e);
+    for (int e = 0; e < 8; ++e) issue_row(src, e, TGN == 1 ? T1 : T0);
   }
 
   // q fragments of head 16*wid + j, d in [g*128, g*128+128)
@@ -258,22 +262,25 @@ attn_bf16_kernel(Params P) {
   for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // one step: wait for the group's tile (keeping its next one in flight),
-  // refill the buffer freed by the previous tile, compute.  Every wave takes
-  // part in the barriers; a group whose run has ended only waits.
-  auto step = [&](int64_t tile, bool active) {
+  // one step: wait for the group's tile (in buffer bc), compute it while the
+  // group's next tile streams into the other buffer.  Every wave takes part in
+  // the barriers; a group whose run has ended only waits.
+  auto step = [&](int64_t tile, bool active, auto bc) {
     constexpr int kPipe = 2;
-    const uint8_t* Ks = T0;
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's rows landed in tb1
-    lds_barrier();   // nobody still reads tb0
-    if (active) {
+    // one group: compute in tb0, land in tb1; two groups: alternate
+    uint8_t* const Ks = (TGN == 1 || decltype(bc)::value == 0) ? T0 : T1;
+    uint8_t* const Kn = (TGN == 1 || decltype(bc)::value == 0) ? T1 : T0;
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): this wave's rows of the tile landed
+    lds_barrier();   // every wave's rows landed; nobody still reads the buffer the next rows go to
+    if constexpr (TGN == 1) {
+      // copy the landed tile into the compute buffer (this wave's 8 rows)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int off = (8 * wid + e) * kKsStride + lane * 16;
         *reinterpret_cast<uint4*>(T0 + off) = *reinterpret_cast<const uint4*>(T1 + off);
       }
+      lds_barrier();   // tb0 holds the tile; tb1 is free
     }
-    lds_barrier();   // tb0 holds the tile; tb1 is free
     if (active) {
       const bool refill = tile + TGN < tile1;
       const uint64_t nsrc = refill ? row_source(tile + TGN, [&](int64_t q) { return sidx[q]; }) : 0;
@@ -293,7 +300,7 @@ attn_bf16_kernel(Params P) {
       for (int s = 0; s < 16; ++s) {
         // the next tile's rows go out one at a time between MFMAs: a burst of
         // row loads would stall this wave until the memory pipeline drains
-        if (refill && (s & 1) == 0) issue_row(nsrc, s / 2);
+        if (refill && (s & 1) == 0) issue_row(nsrc, s / 2, Kn);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][0]), as_bf16x8(qf[s]), s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s % kPipe][1]), as_bf16x8(qf[s]), s1, 0, 0, 0);
         if (s + kPipe < 16) {
@@ -366,9 +373,16 @@ attn_bf16_kernel(Params P) {
   };
 
   const int64_t nsteps = (tile1 - tile0 + TGN - 1) / TGN;
-  for (int64_t i = 0; i < nsteps; ++i) {
-    const int64_t tile = tile0 + tg + i * TGN;
-    step(tile, tile < tile1);
+  if constexpr (TGN == 1) {
+    for (int64_t tile = tile0; tile < tile1; ++tile) step(tile, true, std::integral_constant<int, 0>{});
+  } else {
+    // two steps per trip, one per buffer (an odd count ends with a step that
+    // only waits: no branch around the second body)
+    for (int64_t i = 0; i < nsteps; i += 2) {
+      const int64_t tile = tile0 + tg + i * TGN;
+      step(tile, tile < tile1, std::integral_constant<int, 0>{});
+      step(tile + TGN, tile + TGN < tile1, std::integral_constant<int, 1>{});
+    }
   }
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
