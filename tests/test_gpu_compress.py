@@ -147,3 +147,15 @@ def test_deterministic():
     _, _, a = _run(128, 2, 1024, 512, 0, "bf16", prefix="det")
     _, _, b = _run(128, 2, 1024, 512, 0, "bf16", prefix="det")
     assert torch.equal(a, b)
+
+
+def test_row_split_workspace_reused_across_calls_and_shapes():
+    """One workspace serves a run of row-split C128A calls of different shapes
+    (the partial states of one call never leak into the next)."""
+    ws = torch.empty(max(csa.workspace_bytes(csa.OP_COMPRESS, B, 128 * nb, 512, 128)
+                         for B, nb in [(32, 1), (3, 3), (1, 1), (100, 1)]), dtype=torch.uint8, device="cuda")
+    for rep, (B, nb, c) in enumerate([(32, 1, 512), (3, 3, 512), (32, 1, 512), (1, 1, 128), (100, 1, 512),
+                                      (3, 3, 512)]):
+        n_tok = 128 * nb
+        got, ref, _ = _run(128, B, n_tok, c, 1048576 - n_tok, "f32", prefix=f"reuse{rep % 3}", workspace=ws)
+        assert max_abs(got, ref) < COMP_F32_MAX_ABS, (rep, B, nb, c)
