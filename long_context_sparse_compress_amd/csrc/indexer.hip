@@ -349,8 +349,8 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   }
 }
 
-template <int QK, int QPW, int TPW, int D, bool XS, typename TS>
-__global__ void __launch_bounds__(256, 2)
+template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS>
+__global__ void __launch_bounds__(256, PIPE ? 1 : 2)
 index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
@@ -504,6 +504,59 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
 
   float sc[QPW][TPW / 4];
   float part[QPW][4];
+  // four tiles' partial scores -> lane group g keeps tile u - 3 + g's score
+  auto scatter4 = [&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int64_t e = e_wave + 16 * (u - 3 + g) + col;
+    const bool hi = g >= 2, odd = g & 1;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
+      k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
+      k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
+      float v = odd ? k1 : k0;
+      v += lane_read(x16, odd ? k0 : k1);
+      sc[qi][u / 4] = (e >= vis[qi]) ? -INFINITY : v;
+    }
+  };
+  if constexpr (PIPE) {
+    // Software pipeline (prefill, where the MFMAs and the ReLU-weighted sums
+    // both take time): tile t's MFMAs are issued before tile t - 1's sums,
+    // which consume MFMA results that are already done.  Every tile is
+    // computed (masked entries get -inf at the end).
+    f32x4 cc[2][QPW][4];
+    float kss[2];
+    static_for<0, TPW + 1>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (t < TPW) {
+        constexpr int r = t % D;
+        constexpr int later = (TPW - 1 - t) < (D - 2) ? (TPW - 1 - t) : (D - 2);
+        wait_vm<later * OPS>();
+        if constexpr (t + D - 1 < TPW) issue(t + D - 1, std::integral_constant<int, (t + D - 1) % D>{});
+        F kf;
+        load_tile_frag(kf, slot(std::integral_constant<int, r>{}), col, g);
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) qk_tiles<QK>(qa[qi], kf, qsc, 127, cc[t & 1][qi]);
+        kss[t & 1] = ks[r];   // the ring slot's scale is reloaded by the next issue
+      }
+      if constexpr (t >= 1) {
+        constexpr int u = t - 1;
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) {
+          float acc = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            acc = fmaf(wv[qi][mt][0], relu(cc[u & 1][qi][mt][0]), acc);
+            acc = fmaf(wv[qi][mt][1], relu(cc[u & 1][qi][mt][1]), acc);
+            acc = fmaf(wv[qi][mt][2], relu(cc[u & 1][qi][mt][2]), acc);
+            acc = fmaf(wv[qi][mt][3], relu(cc[u & 1][qi][mt][3]), acc);
+          }
+          part[qi][u & 3] = acc * kss[u & 1];
+        }
+        if constexpr ((u & 3) == 3) scatter4(std::integral_constant<int, u>{});
+      }
+    });
+  } else
   static_for<0, TPW>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     constexpr int r = t % D;
@@ -532,20 +585,7 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         part[qi][t & 3] = acc * ks[r];
       }
     }
-    if constexpr ((t & 3) == 3) {
-      // reduce-scatter over the four lane groups: lane group g keeps tile t - 3 + g
-      const int64_t e = e_wave + 16 * (t - 3 + g) + col;
-      const bool hi = g >= 2, odd = g & 1;
-#pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
-        k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
-        k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
-        float v = odd ? k1 : k0;
-        v += lane_read(x16, odd ? k0 : k1);
-        sc[qi][t / 4] = (e >= vis[qi]) ? -INFINITY : v;
-      }
-    }
+    if constexpr ((t & 3) == 3) scatter4(std::integral_constant<int, t>{});
   });
   // scores leave after the last tile: no stores among the counted row loads
 #pragma unroll
@@ -557,7 +597,7 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 }
 
-template <int QK, int QPW, int TPW, int D, bool XS>
+template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE>
 hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
   dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
@@ -565,10 +605,10 @@ hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
   if (a.score_dtype == CSA_BF16)
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores));
   else
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, float>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, float>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores));
   return hipGetLastError();
 }
@@ -603,8 +643,8 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
     if (a.T <= 2) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
     return launch_mfma<QK, 2, 64, 4, 2>(a, s);
   } else {
-    if (a.T <= 2) return launch_ring<QK, 1, 32, 4, true>(a, s);
-    return launch_ring<QK, 2, 64, 4, false>(a, s);
+    if (a.T <= 2) return launch_ring<QK, 1, 32, 4, true, false>(a, s);
+    return launch_ring<QK, 2, 64, 4, false, true>(a, s);
   }
 }
 
