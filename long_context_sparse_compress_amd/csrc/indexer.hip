@@ -372,13 +372,20 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   const int col = lane & 15, g = lane >> 4;
   uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if constexpr (XS) {
-    // each XCD takes a contiguous range of workgroups: measured on MI355X, a
-    // stream of whole 512 KB key runs reads HBM about 10% faster this way
-    // than with the round-robin spread of neighbouring runs over the XCDs
+    // Each XCD takes a contiguous range of workgroups.  Decode (PIPE false):
+    // key runs vary fastest, so an XCD streams one contiguous range of keys
+    // from HBM (measured about 8% faster than the round-robin spread).
+    // Prefill (PIPE): query blocks vary fastest, so an XCD works through one
+    // or two key runs for every query and they stay in its L2.
     const uint32_t lin = bx + gridDim.x * (by + gridDim.y * bz);
     const uint32_t sw = xcd_swizzle(lin, gridDim.x * gridDim.y * gridDim.z);
-    bx = sw % gridDim.x;
-    by = (sw / gridDim.x) % gridDim.y;
+    if constexpr (!PIPE) {
+      bx = sw % gridDim.x;
+      by = (sw / gridDim.x) % gridDim.y;
+    } else {
+      by = sw % gridDim.y;
+      bx = (sw / gridDim.y) % gridDim.x;
+    }
     bz = sw / (gridDim.x * gridDim.y);
   }
   const int64_t b = bz;
@@ -644,7 +651,7 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
     return launch_mfma<QK, 2, 64, 4, 2>(a, s);
   } else {
     if (a.T <= 2) return launch_ring<QK, 1, 32, 4, true, false>(a, s);
-    return launch_ring<QK, 2, 64, 4, false, true>(a, s);
+    return launch_ring<QK, 2, 64, 4, true, true>(a, s);
   }
 }
 
