@@ -316,13 +316,16 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
 }
 
 // ------------------------------------------------------------ register path
-// bf16 rows of up to 1024 * 8 * CPT keys: thread t holds CPT 16-byte chunks,
-// chunk c being keys 8 (c * 1024 + t) .. + 7, in registers for the whole
-// selection.  LDS only holds the histogram.  The key range is found while
-// the chunks load; an exact histogram of (key - min) (or, for wide ranges,
-// the 11 + 5-bit digit passes) gives the k-th largest key K; the ordered
-// compaction handles two chunks per block-wide scan of four packed 16-bit
-// counts.  Same result as the LDS path.
+// bf16 rows of up to 1024 * 8 * CPT keys: thread t holds keys
+// 8 CPT t .. 8 CPT t + 8 CPT - 1 (CPT 16-byte chunks) in registers for the
+// whole selection; LDS only holds a histogram.  The key range [min, max] is
+// found while the chunks load.  Pass 1 histograms (key - min) >> s over at
+// most 8192 bins (s = 0..3, the smallest shift that fits the range), which
+// spreads any score distribution over the bins (no pile-up of atomics on a
+// few digit values); when s > 0, pass 2 histograms the low s bits of the keys
+// in the chosen bin.  That gives the k-th largest key K exactly.  Since each
+// thread's keys are contiguous, the ordered compaction is one block-wide scan
+// of two packed 16-bit counts (keys above K, keys equal to K).
 __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* tmp, uint64_t* total) {
   return block_exclusive_scan_t<uint64_t>(v, tmp, total);
 }
@@ -332,9 +335,9 @@ __global__ void __launch_bounds__(1024)
 topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const uint16_t* __restrict__ scores,
                 int32_t* __restrict__ idx) {
   constexpr int NT = 1024;
+  static_assert(8 * CPT * NT < 65536, "block-wide counts are packed in 16 bits");
   __shared__ uint32_t bins[kRangeBins];
   __shared__ uint32_t tmp[32];
-  __shared__ uint64_t tmp64[17];
   const int64_t row = blockIdx.x;
   const int64_t t = row % T;
   const int64_t V = row_visible(t, q_pos0, ratio, N);
@@ -349,18 +352,20 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
     tmp[24] = 0xffffu;
     tmp[25] = 0u;
   }
-  // keys in registers; chunks at or past V hold no key (valid bits 0)
-  const uint4* src = reinterpret_cast<const uint4*>(scores + row * N);
-  // two 16-bit keys per register: key u of chunk c is KEY(c, u)
+  // keys in registers, two per register: key u of chunk c is KEY(c, u)
+  // (after the range is known: key - min); keys at or past V are not valid
+  // (valid bits 0)
+  const uint4* src = reinterpret_cast<const uint4*>(scores + row * N) + static_cast<int64_t>(tid) * CPT;
+  const int64_t i00 = static_cast<int64_t>(tid) * 8 * CPT;   // this thread's first key
   uint32_t kp[CPT][4];
   uint32_t valid[CPT];
 #define KEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
   uint32_t kmin = 0xffffu, kmax = 0u;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int64_t i0 = 8 * (static_cast<int64_t>(c) * NT + tid);
+    const int64_t i0 = i00 + 8 * c;
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (i0 < V) raw = src[c * NT + tid];
+    if (i0 < V) raw = src[c];
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     const int64_t nv = V - i0;
     valid[c] = nv >= 8 ? 0xffu : (nv > 0 ? (1u << nv) - 1u : 0u);
@@ -385,16 +390,29 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
   __syncthreads();   // range known, bins zeroed
   kmin = tmp[24];
   kmax = tmp[25];
-  uint32_t K, rem;
-  if (kmax - kmin < static_cast<uint32_t>(kRangeBins)) {
+  int sh = 0;
+  while (((kmax - kmin) >> sh) >= static_cast<uint32_t>(kRangeBins)) ++sh;   // 0..3 for 16-bit keys
+  // from here on the registers hold key - min (two 16-bit differences each)
+  {
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    const v2i16 m2 = {static_cast<short>(kmin), static_cast<short>(kmin)};
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if ((valid[c] >> u) & 1u) atomicAdd(&bins[KEY(c, u) - kmin], 1u);
-    __syncthreads();
-    // thread t owns bins 8t .. 8t+7; find the bin holding the k-th largest key
-    constexpr int per = kRangeBins / NT;
+      for (int j = 0; j < 4; ++j)
+        kp[c][j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2i16, kp[c][j]) - m2);
+  }
+
+  // pass 1: bin (key - min) >> sh
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if ((valid[c] >> u) & 1u) atomicAdd(&bins[KEY(c, u) >> sh], 1u);
+  __syncthreads();
+  // thread t owns bins 8t .. 8t+7; find the bin holding the k-th largest key
+  constexpr int per = kRangeBins / NT;
+  {
     const int b0 = tid * per;
     uint32_t h[per], mine = 0;
 #pragma unroll
@@ -411,84 +429,74 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
 #pragma unroll
       for (int q = per - 1; q >= 0; --q) {
         if (!found && cum + h[q] >= static_cast<uint32_t>(k)) {
-          tmp[20] = kmin + static_cast<uint32_t>(b0 + q);
+          tmp[20] = static_cast<uint32_t>(b0 + q);
           tmp[21] = static_cast<uint32_t>(k) - cum;
           found = true;
         }
         cum += h[q];
       }
     }
+  }
+  __syncthreads();
+  const uint32_t bstar = tmp[20];
+  uint32_t rem = tmp[21];
+  uint32_t K = bstar << sh;   // as a difference from min
+  if (sh > 0) {
+    // pass 2: the low sh bits of the keys in bin bstar
+    if (tid < (1 << sh)) bins[tid] = 0;
     __syncthreads();
-    K = tmp[20];
-    rem = tmp[21];
-  } else {
-    uint32_t prefix = 0, mask = 0;
-    rem = static_cast<uint32_t>(k);
-    for (int p = 0; p < Digits<uint16_t>::n; ++p) {
-      const int sh = Digits<uint16_t>::shift(p);
-      const int nb = 1 << Digits<uint16_t>::bits(p);
-      for (int i = tid; i < nb; i += NT) bins[i] = 0;
-      __syncthreads();
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
+    for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          hist_add(bins, (KEY(c, u) >> sh) & (nb - 1), ((valid[c] >> u) & 1u) && (KEY(c, u) & mask) == prefix);
-      __syncthreads();
-      resolve_digit(bins, nb, rem, tmp + 20);
-      __syncthreads();
-      prefix |= tmp[20] << sh;
-      mask |= static_cast<uint32_t>(nb - 1) << sh;
-      rem = tmp[21];
-      __syncthreads();
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t d = KEY(c, u);
+        if (((valid[c] >> u) & 1u) && (d >> sh) == bstar) atomicAdd(&bins[d & ((1u << sh) - 1u)], 1u);
+      }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t cum = 0, f = 0, r = rem;
+      for (int q = (1 << sh) - 1; q >= 0; --q) {
+        if (cum + bins[q] >= rem) { f = static_cast<uint32_t>(q); r = rem - cum; break; }
+        cum += bins[q];
+      }
+      tmp[22] = f;
+      tmp[23] = r;
     }
-    K = prefix;
+    __syncthreads();
+    K += tmp[22];
+    rem = tmp[23];
   }
 
-  // ordered compaction, two chunks per scan: fields gt0 | eq0 | gt1 | eq1
-  uint32_t gt_run = 0, eq_run = 0;
+  // ordered compaction: this thread's keys above K, then the first rem equal to K
+  uint32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int c0 = 0; c0 < CPT; c0 += 2) {
-    uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+  for (int c = 0; c < CPT; ++c)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      if (c0 + h2 >= CPT) continue;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool vv = (valid[c0 + h2] >> u) & 1u;
-        cnt[h2][0] += vv && KEY(c0 + h2, u) > K;
-        cnt[h2][1] += vv && KEY(c0 + h2, u) == K;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const bool vv = (valid[c] >> u) & 1u;
+      gt += vv && KEY(c, u) > K;
+      eq += vv && KEY(c, u) == K;
     }
-    const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
-                            (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
-    uint64_t tot;
-    const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
-    const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
-    const uint32_t tg1 = (tot >> 32) & 0xffffu, te1 = (tot >> 48) & 0xffffu;
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan(gt | (eq << 16), tmp, &tot);
+  // which of this thread's keys are taken (bit 8c + u), then one store per
+  // taken key in index order
+  uint64_t take = 0;
+  uint32_t er = ex >> 16;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int c = c0 + h2;
-      if (c >= CPT) continue;
-      const uint32_t gb = gt_run + (h2 ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
-      const uint32_t eb = eq_run + (h2 ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
-      uint32_t pos = gb + (eb < rem ? eb : rem);
-      uint32_t er = eb;
-      const int32_t i0 = static_cast<int32_t>(8 * (c * NT + tid));
+  for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (!((valid[c] >> u) & 1u)) continue;
-        const uint32_t kk = KEY(c, u);
-        if (kk > K) {
-          out[pos++] = i0 + u;
-        } else if (kk == K) {
-          if (er < rem) out[pos++] = i0 + u;
-          ++er;
-        }
-      }
+    for (int u = 0; u < 8; ++u) {
+      const bool vv = (valid[c] >> u) & 1u;
+      const uint32_t kk = KEY(c, u);
+      const bool tie = vv && kk == K;
+      if ((vv && kk > K) || (tie && er < rem)) take |= uint64_t(1) << (8 * c + u);
+      er += tie;
     }
-    gt_run += tg0 + tg1;
-    eq_run += te0 + te1;
+  uint32_t pos = (ex & 0xffffu) + min(ex >> 16, rem);
+  while (take) {
+    out[pos++] = static_cast<int32_t>(i00 + __builtin_ctzll(take));
+    take &= take - 1;
   }
 #undef KEY
 }

@@ -124,3 +124,17 @@ def test_deterministic():
     a = _run(d, 1024, 399999)
     b = _run(d, 1024, 399999)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("e,ties", [(4, None), (20, None), (40, 64), (100, None), (100, 4)])
+def test_key_range_spreads(e, ties):
+    """Scores sign * 2^U(-e, e) (rounded to bf16) span about 2 * 2e * 128 distinct
+    keys: the range histogram runs with no shift (e = 4) and with a shift of
+    1, 2 and 3 bits plus the pass over the chosen bin's low bits; ties from
+    coarse exponents where `ties` is set."""
+    ex = synth.uniform(f"tk.spread{e}", (8, 1, 16384), lo=-e, hi=e)
+    if ties:
+        ex = np.round(ex * ties / e) * e / ties
+    x = synth.round_bf16(np.sign(synth.normal(f"tk.sign{e}", ex.shape)) * np.exp2(ex))
+    got = _run(dev(x, torch.bfloat16), 512, 65535)
+    _check(got, ot.topk_select(x, 512, 65535, 4))
