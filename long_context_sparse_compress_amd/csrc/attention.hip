@@ -136,6 +136,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTileBytes = kTile * kKsStride;   // one row-major tile in LDS
 
+// One split's partial in the workspace, in floats: O as 64 x 512 bf16 (in the
+// MFMA register layout), then 64 running maxima and 64 sums in fp32.  bf16
+// halves the bytes the split kernels write and the combine reads; its
+// rounding (2^-9 relative) is that of the bf16 output itself.
+constexpr int64_t kSplitFloats = kH * kD / 2 + 2 * kH;
+static_assert(kSplitFloats * 4 == CSA_HEADS * CSA_HEAD_DIM * 2 + 2 * CSA_HEADS * 4, "matches attn_split_bytes");
+
+__device__ __forceinline__ float4 unpack4(uint2 v) {
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
 // One 1 KB latent row straight from global memory into LDS (16 bytes per lane,
 // lane l's bytes land at dst + 16 l): no registers, no staging.
 __device__ __forceinline__ void row_to_lds(const uint16_t* src_row, uint8_t* dst_row, int lane) {
@@ -479,21 +491,22 @@ attn_bf16_kernel(Params P) {
           out[(16 * hb + 4 * g + i) * kD + 16 * db] = f32_to_bf16(o[8 * hb + db][i] * f[i]);
     }
   } else {
-    // partial O in the MFMA's own layout, 16 bytes per lane: [wave][hb][db][lane]
-    float* w = P.ws + (gq * P.splits + split) * (kH * (kD + 2));
-    float4* wo = reinterpret_cast<float4*>(w) + wid * (4 * 8 * 64) + lane;
+    // partial O in bf16 in the MFMA's own layout, 8 bytes per lane:
+    // [wave][hb][db][lane]; then the heads' running max and sum in fp32
+    float* w = P.ws + (gq * P.splits + split) * kSplitFloats;
+    uint2* wo = reinterpret_cast<uint2*>(w) + wid * (4 * 8 * 64) + lane;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       if (!writes(hb)) continue;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const f32x4& v = o[8 * hb + db];
-        wo[(hb * 8 + db) * 64] = make_float4(v[0], v[1], v[2], v[3]);
+        wo[(hb * 8 + db) * 64] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
     if (tg == 0 && g == 0) {
-      w[kH * kD + head_j] = m_run;
-      w[kH * kD + kH + head_j] = l_tot;
+      w[kH * kD / 2 + head_j] = m_run;
+      w[kH * kD / 2 + kH + head_j] = l_tot;
     }
   }
 }
@@ -577,20 +590,19 @@ attn_combine_kernel(Params P) {
   const int64_t gq = wg / 16;
   const int hb = static_cast<int>(wg / 4 % 4), w = static_cast<int>(wg % 4);
   const int S = P.splits, tid = threadIdx.x;
-  constexpr int64_t kSplitFloats = kH * (kD + 2);
   const float* base = P.ws + gq * S * kSplitFloats;
   const int ln = tid & 63, g = ln >> 4, j = ln & 15, db0 = tid >> 6;
   const int h0 = 16 * hb + 4 * g;   // first of this thread's four heads
-  const float4* src = reinterpret_cast<const float4*>(base) + ((w * 4 + hb) * 8 + db0) * 64 + ln;
+  const uint2* src = reinterpret_cast<const uint2*>(base) + ((w * 4 + hb) * 8 + db0) * 64 + ln;
   float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, L[4] = {0.f, 0.f, 0.f, 0.f};
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
 #pragma unroll 4
   for (int s = 0; s < S; ++s) {
-    const float* st = base + s * kSplitFloats + kH * kD;
+    const float* st = base + s * kSplitFloats + kH * kD / 2;
     const float4 ms = *reinterpret_cast<const float4*>(st + h0);
     const float4 ls = *reinterpret_cast<const float4*>(st + kH + h0);
-    const float4 v0 = src[s * (kSplitFloats / 4)];
-    const float4 v1 = src[s * (kSplitFloats / 4) + 4 * 64];   // d-block db0 + 4
+    const float4 v0 = unpack4(src[s * (kSplitFloats / 2)]);
+    const float4 v1 = unpack4(src[s * (kSplitFloats / 2) + 4 * 64]);   // d-block db0 + 4
     const float m4[4] = {ms.x, ms.y, ms.z, ms.w}, l4[4] = {ls.x, ls.y, ls.z, ls.w};
     float a[4], e[4];
 #pragma unroll

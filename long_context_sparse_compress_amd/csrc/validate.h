@@ -63,8 +63,8 @@ inline int attn_splits(int64_t B, int64_t T, int64_t rows) {
   return static_cast<int>(s < 1 ? 1 : s);
 }
 
-// Per split and query: 64 x 512 fp32 partial output + 64 running maxima + 64 sums.
-inline size_t attn_split_bytes() { return size_t(CSA_HEADS) * (CSA_HEAD_DIM + 2) * sizeof(float); }
+// Per split and query: 64 x 512 bf16 partial output + 64 running maxima + 64 sums (fp32).
+inline size_t attn_split_bytes() { return size_t(CSA_HEADS) * CSA_HEAD_DIM * 2 + 2 * size_t(CSA_HEADS) * sizeof(float); }
 
 inline size_t attn_workspace_bytes(int64_t B, int64_t T) {
   const int s = attn_max_splits(B, T);
