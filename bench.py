@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graphs")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--batch-invariant", action="store_true",
+                   help="attention in batch-invariant mode (no row split; default workload only)")
     return p.parse_args()
 
 
@@ -65,8 +67,9 @@ def parse():
 class DecodeStep:
     """One CSA layer + one HCA layer decode step for B sequences at `ctx` context."""
 
-    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4):
+    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False):
         self.csa, self.torch = csa, torch
+        self.bi = batch_invariant
         bf = torch.bfloat16
         dn = synth.device_normal
         self.B, self.ctx, self.k = B, ctx, k
@@ -124,13 +127,13 @@ class DecodeStep:
                 self.scores, self.k, q_pos0=self.t, idx=self.idx, workspace=self.ws_topk)),
             ("sparse_mqa_attn", lambda: csa.sparse_mqa_attn(
                 self.q, self.kv[r], self.idx, self.raw, q_pos0=self.t, raw_pos0=self.raw0, out=self.out,
-                workspace=self.ws_attn)),
+                workspace=self.ws_attn, batch_invariant=self.bi)),
             ("compress_c128a_kv", lambda: csa.csa_compress(
                 128, c128["Ca"], c128["Za"], self.b128, pos0=self.ctx - 128, out=self.kvh[r],
                 cache_entry0=self.N128 - 1, workspace=self.ws_c128)),
             ("hca_attn", lambda: csa.hca_attn(
                 self.qh, self.kvh[r], self.rawh, q_pos0=self.t, raw_pos0=self.raw0, sink=self.sink,
-                out=self.outh, workspace=self.ws_hca)),
+                out=self.outh, workspace=self.ws_hca, batch_invariant=self.bi)),
         ]
 
     queries_per_step = property(lambda self: self.B)
@@ -324,7 +327,7 @@ def main():
         print(json.dumps(bench_workloads.run(args, torch, csa, synth)))
         return
 
-    step = DecodeStep(csa, synth, torch, rotate=args.rotate)
+    step = DecodeStep(csa, synth, torch, rotate=args.rotate, batch_invariant=args.batch_invariant)
     ms, wall = time_graph(torch, step, args.steps, args.warmup, args.rotate, args.eager)
     per_stage = time_stages(torch, step, args.steps, args.rotate)
     alg = step.algorithmic()
@@ -355,7 +358,8 @@ def main():
                    "batch": step.B, "context": step.ctx, "c4a_entries": step.N4, "c128a_entries": step.N128,
                    "topk": step.k, "window": 128, "heads": 64, "head_dim": 512, "index_heads": 64,
                    "index_dim": 128, "cache_copies_rotated": args.rotate,
-                   "timing": "eager" if args.eager else "hip_graph"},
+                   "timing": "eager" if args.eager else "hip_graph",
+                   "attention": "batch_invariant" if args.batch_invariant else "split_kv"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": index_traffic(),
                      "algorithmic_bytes_per_launch": alg[dom]["bytes"], "avg_launch_us": round(dom_ms * 1e3, 2)},

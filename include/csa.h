@@ -247,6 +247,35 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
              int io_dtype, void* out, float* lse,
              void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * sparse_mqa_attn_ex / hca_attn_ex -- the same operations with a flags word.
+ *
+ * CSA_ATTN_BATCH_INVARIANT: "DeepSeek-V4 技术解读：百万 Token 上下文的新里程
+ * 碑" (3.3) makes attention batch-invariant by giving up the split-KV
+ * decomposition: one kernel has a single SM compute a whole sequence, a
+ * second spreads a sequence over several SMs yet stays bit-identical to the
+ * first.  With this flag a query's rows are never split: every output
+ * element is computed by the same operations in the same order whatever B,
+ * T and the other queries of the call, so a query gives the same bits alone
+ * or in any batch (and run to run).  Calls with few queries spread each
+ * query's four 16-head blocks over four workgroups, which yields the same
+ * bits.  No workspace is used (workspace may be NULL, ws_bytes 0).  Without
+ * the flag (flags 0) these are sparse_mqa_attn / hca_attn, whose decode split
+ * (chosen from B * T) makes the last bits depend on the batch size.
+ * Unknown flag bits are an error.
+ */
+#define CSA_ATTN_BATCH_INVARIANT 1
+int sparse_mqa_attn_ex(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d,
+                       const void* q, const void* kv_cmp, const int32_t* idx,
+                       const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+                       float scale, int io_dtype, void* out, float* lse, int flags,
+                       void* workspace, size_t ws_bytes, void* stream);
+int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
+                const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
+                int64_t n_raw, int window, float scale, const float* sink,
+                int io_dtype, void* out, float* lse, int flags,
+                void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes the named operation needs for these sizes (0 if none).
  * For the two attention operations the need depends only on B and T; N and
  * k are accepted for symmetry.  For CSA_OP_COMPRESS the arguments are

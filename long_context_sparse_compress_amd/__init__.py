@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libcsa.so")
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 OP_COMPRESS, OP_INDEX, OP_TOPK, OP_SPARSE_ATTN, OP_HCA_ATTN = 0, 1, 2, 3, 4
+ATTN_BATCH_INVARIANT = 1   # CSA_ATTN_BATCH_INVARIANT
 
 _i64, _int, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -37,6 +38,10 @@ _SIGS = {
                         _int, _f32, _int, _vp, _vp, _vp, _sz, _vp],
     "hca_attn": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
                  _vp, _int, _vp, _vp, _vp, _sz, _vp],
+    "sparse_mqa_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _i64, _i64,
+                           _int, _f32, _int, _vp, _vp, _int, _vp, _sz, _vp],
+    "hca_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
+                    _vp, _int, _vp, _vp, _int, _vp, _sz, _vp],
 }
 
 _lib = None
@@ -209,8 +214,10 @@ def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=
 
 
 def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, scale=None,
-                    out=None, lse=None, return_lse=False, workspace=None, stream=None):
-    """Stage 4.  q: [B, T, 64, 512], kv_cmp: [B, N, 512], idx: [B, T, k], kv_raw: [B, n_raw, 512]."""
+                    out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False,
+                    stream=None):
+    """Stage 4.  q: [B, T, 64, 512], kv_cmp: [B, N, 512], idx: [B, T, k], kv_raw: [B, n_raw, 512].
+    ``batch_invariant``: no row split, so each query's bits do not depend on the batch."""
     B, T, H, d = q.shape
     N = kv_cmp.shape[1]
     k = idx.shape[2]
@@ -220,17 +227,22 @@ def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, sca
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
-    ws, wsb = _workspace(OP_SPARSE_ATTN, B, T, N, k, q.device, workspace)
-    st = library().sparse_mqa_attn(B, T, N, k, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(idx),
-                                   _ptr(kv_raw), raw_pos0, n_raw, window, scale, _dt(q), _ptr(out),
-                                   _ptr(lse), _ptr(ws), wsb, _stream(stream))
+    if batch_invariant:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _workspace(OP_SPARSE_ATTN, B, T, N, k, q.device, workspace)
+    st = library().sparse_mqa_attn_ex(B, T, N, k, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(idx),
+                                      _ptr(kv_raw), raw_pos0, n_raw, window, scale, _dt(q), _ptr(out),
+                                      _ptr(lse), ATTN_BATCH_INVARIANT if batch_invariant else 0, _ptr(ws),
+                                      wsb, _stream(stream))
     _check(st, "sparse_mqa_attn")
     return (out, lse) if return_lse else out
 
 
 def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, window=128, scale=None,
-             out=None, lse=None, return_lse=False, workspace=None, stream=None):
-    """Stage 5.  Dense MQA over all visible entries and the window, optional sink [64]."""
+             out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False, stream=None):
+    """Stage 5.  Dense MQA over all visible entries and the window, optional sink [64].
+    ``batch_invariant``: no row split, so each query's bits do not depend on the batch."""
     B, T, H, d = q.shape
     N = kv_cmp.shape[1]
     n_raw = kv_raw.shape[1]
@@ -239,9 +251,12 @@ def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, windo
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
-    ws, wsb = _workspace(OP_HCA_ATTN, B, T, N, 0, q.device, workspace)
-    st = library().hca_attn(B, T, N, ratio, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(kv_raw),
-                            raw_pos0, n_raw, window, scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse),
-                            _ptr(ws), wsb, _stream(stream))
+    if batch_invariant:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _workspace(OP_HCA_ATTN, B, T, N, 0, q.device, workspace)
+    st = library().hca_attn_ex(B, T, N, ratio, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(kv_raw),
+                               raw_pos0, n_raw, window, scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse),
+                               ATTN_BATCH_INVARIANT if batch_invariant else 0, _ptr(ws), wsb, _stream(stream))
     _check(st, "hca_attn")
     return (out, lse) if return_lse else out

@@ -192,10 +192,21 @@ __device__ __forceinline__ void lds_barrier() {
 // takes tiles tile0 + k, tile0 + k + TGN, ... of the workgroup's run with its
 // own buffers, so a run of n tiles takes ceil(n / TGN) steps.  The groups'
 // running (max, sum, O) are merged through LDS at the end.
-template <int TGN>
+//
+// HB head blocks of 16 heads per workgroup.  HB = 4 is the kernel above.
+// HB = 1 (batch-invariant decode) gives each of a query's four head blocks
+// its own workgroup over the whole row list: wave 0 computes the block's
+// logits and softmax, every wave a quarter of its P V columns.  Every output
+// element then goes through exactly the operations of the HB = 4 kernel with
+// one split (same tiles in the same order, same MFMA operands, same per-head
+// softmax arithmetic), so the two give identical bits -- the multi-workgroup
+// kernel the pages pair with the one-workgroup kernel, with the work divided
+// by heads instead of rows so that no cross-workgroup merge is needed.
+template <int TGN, int HB>
 __global__ void __launch_bounds__(256 * TGN, 3 - TGN)
 attn_bf16_kernel(Params P) {
   static_assert(TGN == 1 || TGN == 2, "one or two tile groups");
+  static_assert(HB == 4 || (HB == 1 && TGN == 1), "one head block per workgroup runs one group");
   __shared__ __attribute__((aligned(16))) uint8_t tb0[TGN][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[TGN][kTileBytes];
   __shared__ int32_t sidx[CSA_MAX_TOPK];                                   // Top-k row of this query
@@ -212,11 +223,17 @@ attn_bf16_kernel(Params P) {
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   // transposing V reads: lane k of group g points at row 4g + k/4, columns 4(k%4)..
   const uint32_t voff = (4 * g + (j >> 2)) * kKsStride + 8 * (j & 3);
-  // all splits of a query (and its q, and the combine that reads its
-  // partials) on one XCD, so they share that XCD's L2
-  const uint32_t wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  // all splits (or head blocks) of a query -- and its q, and the combine
+  // that reads its partials -- on one XCD, so they share that XCD's L2
+  const uint32_t wg0 = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int hq = HB == 4 ? 0 : static_cast<int>(wg0 % 4);    // head block of an HB = 1 workgroup
+  const uint32_t wg = HB == 4 ? wg0 : wg0 / 4;
   const int64_t gq = wg / P.splits;
   const int split = static_cast<int>(wg % P.splits);
+  // the waves that compute logits and softmax, and the head block of each
+  const bool qk_wave = HB == 4 || wid == 0;
+  const int hb_qk = HB == 4 ? wid : hq;     // global head block
+  const int hl_qk = HB == 4 ? wid : 0;      // its slot in this workgroup's LDS exchange
   const int64_t b = gq / P.T, t = gq % P.T;
   const List l = make_list(P, t);
   int64_t tile0, tile1;
@@ -249,11 +266,11 @@ attn_bf16_kernel(Params P) {
     for (int e = 0; e < 8; ++e) issue_row(src, e, TGN == 1 ? T1 : T0);
   }
 
-  // q fragments of head 16*wid + j, d in [g*128, g*128+128)
+  // q fragments of head 16*hb_qk + j, d in [g*128, g*128+128)
   uint4 qf[16];
-  {
+  if (qk_wave) {
     const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
-                                                     ((gq * kH) + 16 * wid + j) * kD + g * 128);
+                                                     ((gq * kH) + 16 * hb_qk + j) * kD + g * 128);
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = qp[s];
   }
@@ -267,11 +284,11 @@ attn_bf16_kernel(Params P) {
     __syncthreads();
   }
 
-  // O for all 64 heads and d in [128 w, 128 w + 128): o[8 hb + db] holds heads
-  // 16 hb + 4g + i (i = 0..3), column 128 w + 16 db + j
-  f32x4 o[32];
+  // O for the workgroup's head blocks and d in [128 w, 128 w + 128): o[8 hb + db]
+  // holds heads 16 hb + 4g + i (i = 0..3) of local block hb, column 128 w + 16 db + j
+  f32x4 o[8 * HB];
 #pragma unroll
-  for (int n = 0; n < 32; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 8 * HB; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   // one step: wait for the group's tile (in buffer bc), compute it while the
@@ -293,7 +310,14 @@ attn_bf16_kernel(Params P) {
       }
       lds_barrier();   // tb0 holds the tile; tb1 is free
     }
-    if (active) {
+    if (active && !qk_wave) {   // HB = 1, waves 1..3: only their rows of the next tile
+      if (tile + TGN < tile1) {
+        const uint64_t nsrc = row_source(tile + TGN, [&](int64_t q) { return sidx[q]; });
+#pragma unroll
+        for (int e = 0; e < 8; ++e) issue_row(nsrc, e, Kn);
+      }
+    }
+    if (active && qk_wave) {
       const bool refill = tile + TGN < tile1;
       const uint64_t nsrc = refill ? row_source(tile + TGN, [&](int64_t q) { return sidx[q]; }) : 0;
 
@@ -347,19 +371,20 @@ attn_bf16_kernel(Params P) {
       l_run = l_run * alpha + psum;
       m_run = m_new;
       // hand this wave's P and rescale factors to the other waves of the group
-      pshare[tg][wid * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-      if (g == 0) reinterpret_cast<float*>(ashare[tg])[16 * wid + j] = alpha;
+      pshare[tg][hl_qk * 64 + lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+      if (g == 0) reinterpret_cast<float*>(ashare[tg])[16 * hl_qk + j] = alpha;
       const bool moved = __ballot(alpha != 1.f) != 0;
-      if (lane == 0) reinterpret_cast<uint32_t*>(&rescale_any[tg])[wid] = moved;
+      if (lane == 0) reinterpret_cast<uint32_t*>(&rescale_any[tg])[hl_qk] = moved;
     }
     lds_barrier();
     if (active) {
-      // O[:, 128 w .. 128 w + 127] = alpha O + P V over all 64 heads
+      // O[:, 128 w .. 128 w + 127] = alpha O + P V over the workgroup's heads
+      // (a rescale by 1 of a head whose maximum did not move is exact)
       const uint4 any = rescale_any[tg];
-      if (any.x | any.y | any.z | any.w) {
+      if (HB == 4 ? (any.x | any.y | any.z | any.w) : any.x) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
           const float4 a4 = ashare[tg][4 * hb + g];
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
@@ -368,16 +393,16 @@ attn_bf16_kernel(Params P) {
           }
         }
       }
-      bf16x8 pf[4];
+      bf16x8 pf[HB];
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pf[hb] = as_bf16x8(pshare[tg][hb * 64 + lane]);
+      for (int hb = 0; hb < HB; ++hb) pf[hb] = as_bf16x8(pshare[tg][hb * 64 + lane]);
       bf16x8 vr[kPipe];
 #pragma unroll
       for (int d = 0; d < kPipe; ++d) vr[d] = v_operand(Ks, 8 * wid + d, voff);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
+        for (int hb = 0; hb < HB; ++hb)
           o[8 * hb + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], vr[db % kPipe], o[8 * hb + db], 0, 0, 0);
         if (db + kPipe < 8) vr[db % kPipe] = v_operand(Ks, 8 * wid + db + kPipe, voff);
       }
@@ -401,7 +426,8 @@ attn_bf16_kernel(Params P) {
   float l_tot = l_run;
   l_tot += lane_read(x16, l_tot);
   l_tot += lane_read(x32, l_tot);
-  const int head_j = 16 * wid + j;
+  const int head_j = 16 * hb_qk + j;      // global head of this lane's logits (qk waves)
+  const int hl_j = 16 * hl_qk + j;        // its slot in this workgroup's exchange
 
   // o[] is indexed with constants only (a run-time index would move it to
   // scratch memory): the group-dependent parts below branch on the group and
@@ -465,7 +491,7 @@ attn_bf16_kernel(Params P) {
   auto writes = [&](int hb) { return TGN == 1 || (hb >> 1) == tg; };
 
   if (P.splits == 1) {
-    if (tg == 0 && g == 0) {
+    if (tg == 0 && qk_wave && g == 0) {
       float M = m_run;
       float zl = -INFINITY;
       if (P.sink) {
@@ -474,23 +500,24 @@ attn_bf16_kernel(Params P) {
       }
       const float em = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
       const float denom = l_tot * em + (P.sink ? fast_exp2(zl - M) : 0.f);
-      reinterpret_cast<float*>(fshare)[head_j] = em / denom;
+      reinterpret_cast<float*>(fshare)[hl_j] = em / denom;
       if (P.lse) P.lse[gq * kH + head_j] = kLn2 * (M + log2f(denom));
     }
     lds_barrier();
     uint16_t* out = static_cast<uint16_t*>(P.out) + gq * kH * kD + 128 * wid + j;
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       if (!writes(hb)) continue;
+      const int hg = HB == 4 ? hb : hq;   // global head block
       const float4 f4 = fshare[4 * hb + g];
       const float f[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          out[(16 * hb + 4 * g + i) * kD + 16 * db] = f32_to_bf16(o[8 * hb + db][i] * f[i]);
+          out[(16 * hg + 4 * g + i) * kD + 16 * db] = f32_to_bf16(o[8 * hb + db][i] * f[i]);
     }
-  } else {
+  } else if constexpr (HB == 4) {
     // partial O in bf16 in the MFMA's own layout, 8 bytes per lane:
     // [wave][hb][db][lane]; then the heads' running max and sum in fp32
     float* w = P.ws + (gq * P.splits + split) * kSplitFloats;
@@ -677,10 +704,21 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   // merge add about 4 us, so short runs keep one group.
   const int64_t ntiles = (ncmp + wlen + kAttnTile - 1) / kAttnTile;
   const int64_t per_split = (ntiles + P.splits - 1) / P.splits;
+  if (a.flags & CSA_ATTN_BATCH_INVARIANT) {
+    // no row split: every query's rows in order in one workgroup's chain;
+    // few queries spread their four head blocks over four workgroups (the
+    // same bits, see attn_bf16_kernel)
+    P.splits = 1;
+    if (nq < 256)
+      hipLaunchKernelGGL((attn_bf16_kernel<1, 1>), dim3(static_cast<uint32_t>(nq * 4)), dim3(256), 0, s, P);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<1, 4>), dim3(static_cast<uint32_t>(nq)), dim3(256), 0, s, P);
+    return hipGetLastError();
+  }
   if (P.splits > 1 && per_split >= 8)
-    hipLaunchKernelGGL(attn_bf16_kernel<2>, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0, s, P);
+    hipLaunchKernelGGL((attn_bf16_kernel<2, 4>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0, s, P);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<1>, dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
+    hipLaunchKernelGGL((attn_bf16_kernel<1, 4>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
   if (P.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
   return hipGetLastError();

@@ -86,28 +86,44 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
   return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select launch");
 }
 
+int sparse_mqa_attn_ex(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,
+                       const void* kv_cmp, const int32_t* idx, const void* kv_raw, int64_t raw_pos0,
+                       int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse, int flags,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_sparse(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw,
+                                    window, scale, io_dtype, out, lse, workspace, ws_bytes, flags);
+  if (!ck.ok()) return finish(ck);
+  csa::AttnArgs a{B, T, N, k, 4, q_pos0, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
+                  nullptr, io_dtype, out, lse, workspace, flags};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn launch");
+}
+
 int sparse_mqa_attn(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,
                     const void* kv_cmp, const int32_t* idx, const void* kv_raw, int64_t raw_pos0,
                     int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse,
                     void* workspace, size_t ws_bytes, void* stream) {
-  csa::Check ck = csa::check_sparse(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw,
-                                    window, scale, io_dtype, out, lse, workspace, ws_bytes);
+  return sparse_mqa_attn_ex(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
+                            io_dtype, out, lse, 0, workspace, ws_bytes, stream);
+}
+
+int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
+                const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+                float scale, const float* sink, int io_dtype, void* out, float* lse, int flags, void* workspace,
+                size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_hca(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window,
+                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes, flags);
   if (!ck.ok()) return finish(ck);
-  csa::AttnArgs a{B, T, N, k, 4, q_pos0, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
-                  nullptr, io_dtype, out, lse, workspace};
-  return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn launch");
+  csa::AttnArgs a{B, T, N, 0, ratio, q_pos0, q, kv_cmp, nullptr, kv_raw, raw_pos0, n_raw, window, scale,
+                  sink, io_dtype, out, lse, workspace, flags};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn launch");
 }
 
 int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
              const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
              float scale, const float* sink, int io_dtype, void* out, float* lse, void* workspace,
              size_t ws_bytes, void* stream) {
-  csa::Check ck = csa::check_hca(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window,
-                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes);
-  if (!ck.ok()) return finish(ck);
-  csa::AttnArgs a{B, T, N, 0, ratio, q_pos0, q, kv_cmp, nullptr, kv_raw, raw_pos0, n_raw, window, scale,
-                  sink, io_dtype, out, lse, workspace};
-  return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn launch");
+  return hca_attn_ex(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window, scale, sink,
+                     io_dtype, out, lse, 0, workspace, ws_bytes, stream);
 }
 
 size_t csa_workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int k) {

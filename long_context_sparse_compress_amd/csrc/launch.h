@@ -63,6 +63,7 @@ struct AttnArgs {
   void* out;
   float* lse;
   void* ws;
+  int flags;          // CSA_ATTN_* bits
 };
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);

@@ -43,6 +43,10 @@ struct Check {
 
 inline std::string i2s(int64_t v) { return std::to_string(v); }
 
+inline void check_attn_flags(Check& k, int flags) {
+  if (flags & ~CSA_ATTN_BATCH_INVARIANT) k.fail(CSA_ERR_INVALID_ARG, "unknown attention flags " + std::to_string(flags));
+}
+
 // Split plan of the attention kernels: how many workgroups share one query's
 // rows.  The workspace bound depends only on B*T; the split count used at run
 // time never exceeds it.
@@ -210,8 +214,10 @@ inline bool check_attn_common(Check& k, int64_t B, int64_t T, int64_t q_pos0, in
 inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos0, int H, int d,
                           const void* q, const void* kv_cmp, const void* idx, const void* kv_raw,
                           int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype,
-                          const void* out, const void* lse, const void* ws, size_t ws_bytes) {
+                          const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0) {
   Check k;
+  check_attn_flags(k, flags);
+  if (!k.ok()) return k;
   if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
   if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
   if (kk < 0 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [0, 2048], got " + i2s(kk)); return k; }
@@ -220,7 +226,8 @@ inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos
       k.ptr(idx, "idx", !empty && kk > 0) && k.ptr(kv_raw, "kv_raw", !empty) && k.ptr(out, "out", !empty) &&
       k.ptr(lse, "lse", false);
   if (!k.ok()) return k;
-  const size_t need = attn_workspace_bytes(B, T);
+  // the batch-invariant mode never splits rows, so it uses no workspace
+  const size_t need = (flags & CSA_ATTN_BATCH_INVARIANT) ? 0 : attn_workspace_bytes(B, T);
   if (need > 0 && !empty) {
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "sparse_mqa_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");
@@ -231,8 +238,10 @@ inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos
 inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
                        const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
                        int64_t n_raw, int window, float scale, const void* sink, int io_dtype,
-                       const void* out, const void* lse, const void* ws, size_t ws_bytes) {
+                       const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0) {
   Check k;
+  check_attn_flags(k, flags);
+  if (!k.ok()) return k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
   if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
@@ -241,7 +250,8 @@ inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos
   k.ptr(q, "q", !empty) && k.ptr(kv_cmp, "kv_cmp", !empty && N > 0) && k.ptr(kv_raw, "kv_raw", !empty) &&
       k.ptr(out, "out", !empty) && k.ptr(lse, "lse", false) && k.ptr(sink, "sink", false);
   if (!k.ok()) return k;
-  const size_t need = attn_workspace_bytes(B, T);
+  // the batch-invariant mode never splits rows, so it uses no workspace
+  const size_t need = (flags & CSA_ATTN_BATCH_INVARIANT) ? 0 : attn_workspace_bytes(B, T);
   if (need > 0 && !empty) {
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "hca_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");

@@ -30,7 +30,8 @@ def lib():
 def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
-                          "hca_attn", "csa_workspace_bytes", "csa_last_error", "csa_version"}
+                          "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_workspace_bytes",
+                          "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "long_context_sparse_compress_amd", "libcsa.so")],
@@ -161,6 +162,32 @@ def test_attention_validation(lib):
     assert sp(q=None) == -1
     assert h(2, 1, 1, 128, 255, 64, 512, A, A, A, 128, 128, 128, 0.04, None, 1, A, None, A, ws, None) == -1
     assert h(2, 1, 2, 3, 255, 64, 512, A, A, A, 128, 128, 128, 0.04, None, 1, A, None, A, ws, None) == -1
+
+
+def test_attention_flags_validation(lib):
+    """The _ex entry points reject unknown flag bits before anything else, and
+    the batch-invariant flag needs no workspace (the other checks still apply)."""
+    se, he = lib.sparse_mqa_attn_ex, lib.hca_attn_ex
+    ws = lib.csa_workspace_bytes(3, 2, 1, 64, 16)
+
+    def sp(flags, wsp=None, wsb=0, H=64, n_raw=128):
+        return se(2, 1, 64, 16, 255, H, 512, A, A, A, A, 128, n_raw, 128, 0.04, 1, A, None, flags,
+                  wsp, wsb, None)
+
+    def hc(flags, wsp=None, wsb=0, n_raw=128):
+        return he(2, 1, 2, 128, 255, 64, 512, A, A, A, 128, n_raw, 128, 0.04, None, 1, A, None, flags,
+                  wsp, wsb, None)
+
+    for f in (2, 4, -1, 1 | 8):
+        assert sp(f, A, ws) == -1 and "unknown attention flags" in _err(lib)
+        assert hc(f, A, ws) == -1 and "unknown attention flags" in _err(lib)
+    # without the flag the split decode wants its workspace
+    assert sp(0) == -4 and "workspace" in _err(lib)
+    assert hc(0) == -4 and "workspace" in _err(lib)
+    # with it, the remaining argument checks still run
+    assert sp(1, H=32) == -2
+    assert sp(1, n_raw=127) == -1 and "last query" in _err(lib)
+    assert hc(1, n_raw=127) == -1 and "last query" in _err(lib)
 
 
 def test_workspace_query(lib):

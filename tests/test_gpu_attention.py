@@ -234,3 +234,66 @@ def test_deterministic_split_decode():
     b = csa.hca_attn(q, kv, raw, q_pos0=1048575, raw_pos0=rp0, sink=sink)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_batch_invariant_csa_decode_bits():
+    """Batch-invariant mode ("DeepSeek-V4 技术解读：百万 Token 上下文的新里程碑",
+    3.3): a decode query gives the same bits alone, in a small batch (one
+    workgroup per head block) and in a batch of 300 (one workgroup per query),
+    and matches the oracle."""
+    B, N, k, q0 = 300, 2048, 512, 8191
+    q, kv, raw, idx, rp0 = _sparse_case("at.bi", B, 1, N, k, q0)
+    di = dev(idx, torch.int32)
+    big, lse = csa.sparse_mqa_attn(q, kv, di, raw, q_pos0=q0, raw_pos0=rp0, batch_invariant=True,
+                                   return_lse=True)
+    for pick in ([0, 77, 299], [150]):
+        s = torch.as_tensor(pick, device="cuda")
+        small, sl = csa.sparse_mqa_attn(q[s].contiguous(), kv[s].contiguous(), di[s].contiguous(),
+                                        raw[s].contiguous(), q_pos0=q0, raw_pos0=rp0,
+                                        batch_invariant=True, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(small, big[s]), pick
+        assert torch.equal(sl, lse[s]), pick
+    got = host(big)
+    for b in [0, 150, 299]:
+        _assert_bf16(got[b, 0], _sparse_ref(q, kv, idx, raw, rp0, q0, b, 0))
+
+
+def test_batch_invariant_prefill_query_equals_decode():
+    """A query of a 512-token prefill chunk and the same query decoded alone
+    give the same bits in batch-invariant mode (CSA, and HCA with sink)."""
+    T, N, k, q0 = 512, 4096, 512, 16384
+    q, kv, raw, idx, rp0 = _sparse_case("at.bip", 1, T, N, k, q0)
+    di = dev(idx, torch.int32)
+    chunk = csa.sparse_mqa_attn(q, kv, di, raw, q_pos0=q0, raw_pos0=rp0, batch_invariant=True)
+    Nh = (q0 + T) // 128
+    hq, hkv, hraw, sink, hrp0 = _hca_case("at.bih", 1, T, Nh, q0)
+    hchunk = csa.hca_attn(hq, hkv, hraw, q_pos0=q0, raw_pos0=hrp0, sink=sink, batch_invariant=True)
+    for t in [0, 1, 127, 300, 511]:
+        one = csa.sparse_mqa_attn(q[:, t:t + 1].contiguous(), kv, di[:, t:t + 1].contiguous(), raw,
+                                  q_pos0=q0 + t, raw_pos0=rp0, batch_invariant=True)
+        hone = csa.hca_attn(hq[:, t:t + 1].contiguous(), hkv, hraw, q_pos0=q0 + t, raw_pos0=hrp0,
+                            sink=sink, batch_invariant=True)
+        torch.cuda.synchronize()
+        assert torch.equal(one[:, 0], chunk[:, t]), t
+        assert torch.equal(hone[:, 0], hchunk[:, t]), t
+    got, hgot = host(chunk), host(hchunk)
+    for t in [0, 511]:
+        _assert_bf16(got[0, t], _sparse_ref(q, kv, idx, raw, rp0, q0, 0, t))
+        r, _ = _dense_ref(hq, hkv, hraw, hrp0, q0, 0, t, 128, sink)
+        _assert_bf16(hgot[0, t], r)
+
+
+def test_batch_invariant_hca_decode_matches_oracle():
+    """HCA decode with sink in batch-invariant mode: a batch of 16 at 1M
+    context (one workgroup per head block) against the oracle."""
+    B, N, q0 = 16, 8192, 1048575
+    q, kv, raw, sink, rp0 = _hca_case("at.hdec", B, 1, N, q0)
+    out, lse = csa.hca_attn(q, kv, raw, q_pos0=q0, raw_pos0=rp0, sink=sink, return_lse=True,
+                            batch_invariant=True)
+    torch.cuda.synchronize()
+    got, gl = host(out), host(lse)
+    for b in [0, 15]:
+        r, rl = _dense_ref(q, kv, raw, rp0, q0, b, 0, 128, sink)
+        _assert_bf16(got[b, 0], r)
+        assert max_abs(gl[b, 0], rl) < 1e-3
