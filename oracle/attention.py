@@ -25,10 +25,15 @@ Readings taken:
 * lse is the natural log of the full softmax denominator (sink included).
 * Compressed entry s is visible to t iff s < floor((t + 1) / ratio).
 * Top-k slots holding -1 are padding and contribute nothing.
+* With rope_dims > 0 the output of query position pos gets inverse RoPE at
+  pos on its last rope_dims dimensions (``oracle.rope``); q and the rows are
+  taken as given (already rotated by their producers).
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import rope as _rope
 
 
 def window_rows(t: int, window: int):
@@ -48,7 +53,8 @@ def _attend(qh: np.ndarray, X: np.ndarray, scale: float):
 
 
 def sparse_mqa(q, kv_cmp, idx, kv_raw, raw_pos0: int, q_pos0: int, window: int = 128,
-               scale: float | None = None, rows=None):
+               scale: float | None = None, rows=None, rope_dims: int = 0,
+               rope_base: float = _rope.DEFAULT_BASE):
     """Attention over Top-k entries concatenated with the window.
 
     q: [B, T, H, d]; kv_cmp: [B, N, d]; idx: [B, T, k] (-1 = padding);
@@ -70,11 +76,14 @@ def sparse_mqa(q, kv_cmp, idx, kv_raw, raw_pos0: int, q_pos0: int, window: int =
             win = [u - raw_pos0 for u in window_rows(pos, window)]
             X = np.concatenate([kv_cmp[b, sel], kv_raw[b, win]], axis=0)
             o[b, r], lse[b, r] = _attend(q[b, t], X, scale)
+            if rope_dims:
+                o[b, r] = _rope.rotate(o[b, r], pos, rope_dims, rope_base, inverse=True)
     return o, lse
 
 
 def dense_attention(q, kv_cmp, kv_raw, raw_pos0: int, q_pos0: int, ratio: int,
-                    window: int = 128, scale: float | None = None, sink=None, rows=None):
+                    window: int = 128, scale: float | None = None, sink=None, rows=None,
+                    rope_dims: int = 0, rope_base: float = _rope.DEFAULT_BASE):
     """Masked dense attention over all compressed entries plus the window.
 
     Written separately from ``sparse_mqa``: one logit matrix over every cache
@@ -111,11 +120,14 @@ def dense_attention(q, kv_cmp, kv_raw, raw_pos0: int, q_pos0: int, ratio: int,
             s = e.sum(axis=1, keepdims=True)
             o[b, r] = (e @ vals) / s
             lse[b, r] = (m + np.log(s))[:, 0]
+            if rope_dims:
+                o[b, r] = _rope.rotate(o[b, r], pos, rope_dims, rope_base, inverse=True)
     return o, lse
 
 
 def hca_attention(q, kv_cmp, kv_raw, raw_pos0: int, q_pos0: int, sink, ratio: int = 128,
-                  window: int = 128, scale: float | None = None, rows=None):
+                  window: int = 128, scale: float | None = None, rows=None, rope_dims: int = 0,
+                  rope_base: float = _rope.DEFAULT_BASE):
     """HCA: dense attention over all visible C128A entries and the window, with a sink."""
     return dense_attention(q, kv_cmp, kv_raw, raw_pos0, q_pos0, ratio, window, scale,
-                           sink=sink, rows=rows)
+                           sink=sink, rows=rows, rope_dims=rope_dims, rope_base=rope_base)

@@ -25,13 +25,17 @@ Readings taken where the pages are silent or garbled:
   the previous block's offsets 0..3; C128A has a [128, c] bias.
 * Block 0's missing weights are -inf, so its zero content gets weight 0 and
   entry 0 pools only its own 4 tokens.
-* RMSNorm has eps = 1e-6 and weight gamma (ones unless given).  RoPE is not
-  applied here.
+* RMSNorm has eps = 1e-6 and weight gamma (ones unless given).
+* With rope_dims > 0, partial RoPE (``oracle.rope``) turns the last rope_dims
+  channels of each entry after RMSNorm, at the entry's anchor position
+  ratio * s + rope_anchor (s the entry's absolute index).
 * Trailing tokens that do not complete a block produce no entry.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import rope as _rope
 
 PREV = 4  # raw tokens in the C4A "previous block"
 
@@ -52,7 +56,8 @@ def _rmsnorm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
 
 
 def compress_sequence(Ca, Za, bias, ratio, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None,
-                      pos0=0, gamma=None, eps=1e-6):
+                      pos0=0, gamma=None, eps=1e-6, rope_dims=0, rope_base=_rope.DEFAULT_BASE,
+                      rope_anchor=0):
     """Compress one sequence's chunk of raw tokens.
 
     Ca, Za (and Cb, Zb for C4A): [n_tok, c], raw tokens pos0 .. pos0+n_tok-1.
@@ -102,12 +107,15 @@ def compress_sequence(Ca, Za, bias, ratio, Cb=None, Zb=None, prev_Cb=None, prev_
             L, X = L_cur, X_cur
         y, p = _softmax_pool(L, X)
         out[i] = _rmsnorm(y, g, eps)
+        if rope_dims:
+            at = _rope.entry_position(pos0 // ratio + i, ratio, rope_anchor)
+            out[i] = _rope.rotate(out[i], at, rope_dims, rope_base)
         weights[i] = p
     return out, weights
 
 
 def compress(Ca, Za, bias, ratio, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, pos0=0,
-             gamma=None, eps=1e-6):
+             gamma=None, eps=1e-6, rope_dims=0, rope_base=_rope.DEFAULT_BASE, rope_anchor=0):
     """Batched form: inputs [B, n_tok, c] (halo [B, 4, c]); returns out [B, n_ent, c]."""
     Ca = np.asarray(Ca)
     outs = []
@@ -116,6 +124,7 @@ def compress(Ca, Za, bias, ratio, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, 
             Ca[b], Za[b], bias, ratio,
             None if Cb is None else Cb[b], None if Zb is None else Zb[b],
             None if prev_Cb is None else prev_Cb[b], None if prev_Zb is None else prev_Zb[b],
-            pos0=pos0, gamma=gamma, eps=eps)
+            pos0=pos0, gamma=gamma, eps=eps, rope_dims=rope_dims, rope_base=rope_base,
+            rope_anchor=rope_anchor)
         outs.append(o)
     return np.stack(outs)
