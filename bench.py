@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--batch-invariant", action="store_true",
                    help="attention in batch-invariant mode (no row split; default workload only)")
+    p.add_argument("--rope", type=int, default=0,
+                   help="partial RoPE dims fused into the compressors and the attention epilogues "
+                        "(default workload only; 0 = none)")
     return p.parse_args()
 
 
@@ -67,9 +70,10 @@ def parse():
 class DecodeStep:
     """One CSA layer + one HCA layer decode step for B sequences at `ctx` context."""
 
-    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False):
+    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False, rope=0):
         self.csa, self.torch = csa, torch
         self.bi = batch_invariant
+        self.rope = rope
         bf = torch.bfloat16
         dn = synth.device_normal
         self.B, self.ctx, self.k = B, ctx, k
@@ -117,9 +121,10 @@ class DecodeStep:
             # the block's 512-d latent and its 128-d indexer key, one launch
             ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
                 dict(ratio=4, Ca=c4["Ca"], Za=c4["Za"], bias=self.b4, Cb=c4["Cb"], Zb=c4["Zb"], prev_Cb=c4["pCb"],
-                     prev_Zb=c4["pZb"], pos0=pos4, out=self.kv[r], cache_entry0=self.N4 - 1),
+                     prev_Zb=c4["pZb"], pos0=pos4, out=self.kv[r], cache_entry0=self.N4 - 1, rope_dims=self.rope),
                 dict(ratio=4, Ca=c4k["Ca"], Za=c4k["Za"], bias=self.b4k, Cb=c4k["Cb"], Zb=c4k["Zb"],
-                     prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1),
+                     prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1,
+                     rope_dims=self.rope),
             ])),
             ("lightning_index", lambda: csa.lightning_index(
                 self.qi, self.w, self.keys[r], q_pos0=self.t, scores=self.scores)),
@@ -127,13 +132,13 @@ class DecodeStep:
                 self.scores, self.k, q_pos0=self.t, idx=self.idx, workspace=self.ws_topk)),
             ("sparse_mqa_attn", lambda: csa.sparse_mqa_attn(
                 self.q, self.kv[r], self.idx, self.raw, q_pos0=self.t, raw_pos0=self.raw0, out=self.out,
-                workspace=self.ws_attn, batch_invariant=self.bi)),
+                workspace=self.ws_attn, batch_invariant=self.bi, rope_dims=self.rope)),
             ("compress_c128a_kv", lambda: csa.csa_compress(
                 128, c128["Ca"], c128["Za"], self.b128, pos0=self.ctx - 128, out=self.kvh[r],
-                cache_entry0=self.N128 - 1, workspace=self.ws_c128)),
+                cache_entry0=self.N128 - 1, workspace=self.ws_c128, rope_dims=self.rope)),
             ("hca_attn", lambda: csa.hca_attn(
                 self.qh, self.kvh[r], self.rawh, q_pos0=self.t, raw_pos0=self.raw0, sink=self.sink,
-                out=self.outh, workspace=self.ws_hca, batch_invariant=self.bi)),
+                out=self.outh, workspace=self.ws_hca, batch_invariant=self.bi, rope_dims=self.rope)),
         ]
 
     queries_per_step = property(lambda self: self.B)
@@ -327,7 +332,8 @@ def main():
         print(json.dumps(bench_workloads.run(args, torch, csa, synth)))
         return
 
-    step = DecodeStep(csa, synth, torch, rotate=args.rotate, batch_invariant=args.batch_invariant)
+    step = DecodeStep(csa, synth, torch, rotate=args.rotate, batch_invariant=args.batch_invariant,
+                      rope=args.rope)
     ms, wall = time_graph(torch, step, args.steps, args.warmup, args.rotate, args.eager)
     per_stage = time_stages(torch, step, args.steps, args.rotate)
     alg = step.algorithmic()
@@ -359,7 +365,8 @@ def main():
                    "topk": step.k, "window": 128, "heads": 64, "head_dim": 512, "index_heads": 64,
                    "index_dim": 128, "cache_copies_rotated": args.rotate,
                    "timing": "eager" if args.eager else "hip_graph",
-                   "attention": "batch_invariant" if args.batch_invariant else "split_kv"},
+                   "attention": "batch_invariant" if args.batch_invariant else "split_kv",
+                   "rope_dims": args.rope},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": index_traffic(),
                      "algorithmic_bytes_per_launch": alg[dom]["bytes"], "avg_launch_us": round(dom_ms * 1e3, 2)},

@@ -12,6 +12,10 @@
  *   hca_attn          dense shared-KV MQA over all C128A entries plus the
  *                     window, with an attention sink
  *
+ * and, around them: csa_compress_ex / sparse_mqa_attn_ex / hca_attn_ex (the
+ * same operations with partial RoPE fused in, and the batch-invariant
+ * attention mode), csa_rope (partial RoPE on query or window rows).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.     Every tensor pointer is device memory owned by the caller.  The
@@ -128,12 +132,46 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Partial RoPE, shared by the _ex entry points and csa_rope.
+ *
+ * "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding, under CSA; the
+ * CSA operator graph): compressed entries get RoPE after their RMSNorm at an
+ * anchor position, the query gets RoPE at its position, and the attention
+ * output gets inverse RoPE on its last 64 dimensions.  The rotation is
+ * RoFormer's: over the last R = rope_dims dimensions of a row, pair p =
+ * (x[D-R+2p], x[D-R+2p+1]) turns by the angle pos * rope_base^(-2p/R):
+ *   (x, y) -> (x cos a - y sin a, x sin a + y cos a);
+ * the inverse turns by -a.  The pages give R = 64 and no base (10000 is
+ * RoFormer's).  rope_dims is 0 (no RoPE) or a multiple of 8 up to the row
+ * width; rope_base must be finite and > 1 when rope_dims > 0.  Angles are
+ * formed and reduced in fp64, the rotation is fp32 before the output's
+ * rounding.
+ *
+ * csa_compress_ex -- csa_compress, then partial RoPE on each entry.
+ *
+ * Entry i of the call (absolute entry pos0/ratio + i) is rotated at position
+ * pos0 + ratio*i + rope_anchor.  The pages name the anchor position but its
+ * symbol is lost in the text; the caller picks the offset inside the block,
+ * 0 <= rope_anchor < ratio (0: the block's first raw token).  The row-split
+ * C128A path (workspace given) applies it in its merge step.  Other
+ * arguments, rules and errors are those of csa_compress; csa_compress is this
+ * call with rope_dims 0.
+ */
+int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
+                    const void* Ca, const void* Za, const void* Cb, const void* Zb,
+                    const void* prev_Cb, const void* prev_Zb,
+                    const float* bias, const float* gamma, float eps,
+                    int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
+                    int rope_dims, float rope_base, int rope_anchor,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * csa_compress_batch -- several csa_compress calls in one launch.
  *
  * The same operation as csa_compress, for callers that compress more than
  * one stream of the same tokens at once (the CSA layer's 512-d latent and its
  * 128-d indexer keys both go through a C4A compressor).  Each job carries
- * exactly the arguments of csa_compress (without workspace and stream) and
+ * exactly the arguments of csa_compress_ex (without workspace and stream) and
  * obeys the same rules; jobs of one batch must share ratio, in_dtype and
  * out_dtype.  1 <= n_jobs <= 4.  Jobs with nothing to write are skipped.
  * The row split that csa_compress's workspace enables is not used here.
@@ -149,6 +187,9 @@ typedef struct csa_compress_job {
   int in_dtype, out_dtype;
   void* out;
   int64_t out_batch_stride;
+  int rope_dims;      /* csa_compress_ex's partial RoPE; 0 for none */
+  float rope_base;
+  int rope_anchor;
 } csa_compress_job;
 
 int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
@@ -248,7 +289,14 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
              void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * sparse_mqa_attn_ex / hca_attn_ex -- the same operations with a flags word.
+ * sparse_mqa_attn_ex / hca_attn_ex -- the same operations with a flags word
+ * and the output's inverse RoPE.
+ *
+ * rope_dims > 0: each output row of query position t = q_pos0 + tq gets
+ * inverse partial RoPE at t on its last rope_dims dimensions (the RoPE
+ * convention above), after normalisation and before the output's rounding;
+ * lse is unchanged.  q and the rows are taken as given: the caller rotates q
+ * and the window rows (csa_rope) and the entries (csa_compress_ex).
  *
  * CSA_ATTN_BATCH_INVARIANT: "DeepSeek-V4 技术解读：百万 Token 上下文的新里程
  * 碑" (3.3) makes attention batch-invariant by giving up the split-KV
@@ -269,12 +317,30 @@ int sparse_mqa_attn_ex(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, i
                        const void* q, const void* kv_cmp, const int32_t* idx,
                        const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
                        float scale, int io_dtype, void* out, float* lse, int flags,
+                       int rope_dims, float rope_base,
                        void* workspace, size_t ws_bytes, void* stream);
 int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
                 const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
                 int64_t n_raw, int window, float scale, const float* sink,
                 int io_dtype, void* out, float* lse, int flags,
+                int rope_dims, float rope_base,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * csa_rope -- partial RoPE (or its inverse) in place on rows of a tensor.
+ *
+ * "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding; the CSA
+ * operator graph: the query is rotated at its position, and so is each raw
+ * latent of the sliding window, whose rows are the keys and values of the
+ * window).  x is [B, T, H, D] of dtype (CSA_F32 or CSA_BF16), dense; row
+ * (b, t, h) sits at position pos0 + t and its last rope_dims dimensions are
+ * rotated by the RoPE convention above (by -angle when inverse = 1).  Use H =
+ * 1 for [B, T, D] rows.  D is a multiple of 8 up to 65536; rope_dims is a
+ * multiple of 8 in [8, min(D, 1024)]; 0 <= pos0 <= 2^40; B * T < 2^31,
+ * H <= 2^24.  The first D - rope_dims dimensions are not read or written.
+ */
+int csa_rope(int64_t B, int64_t T, int64_t H, int64_t D, int64_t pos0, int rope_dims,
+             float rope_base, int inverse, int dtype, void* x, void* stream);
 
 /* Workspace bytes the named operation needs for these sizes (0 if none).
  * For the two attention operations the need depends only on B and T; N and

@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
-           "workspace_bytes", "library", "F32", "BF16", "FP8_E4M3", "MXFP4", "CsaError"]
+           "rope", "workspace_bytes", "library", "F32", "BF16", "FP8_E4M3", "MXFP4", "CsaError"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa.so")
@@ -25,12 +25,16 @@ LIB_PATH = os.path.join(HERE, "libcsa.so")
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 OP_COMPRESS, OP_INDEX, OP_TOPK, OP_SPARSE_ATTN, OP_HCA_ATTN = 0, 1, 2, 3, 4
 ATTN_BATCH_INVARIANT = 1   # CSA_ATTN_BATCH_INVARIANT
+ROPE_BASE = 10000.0        # the rotary base used when none is given
 
 _i64, _int, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
 _SIGS = {
     "csa_compress": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                      _int, _int, _vp, _i64, _vp, _sz, _vp],
+    "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
+                        _int, _int, _vp, _i64, _int, _f32, _int, _vp, _sz, _vp],
+    "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
     "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
                         _vp, _int, _vp],
     "topk_select": [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
@@ -39,9 +43,9 @@ _SIGS = {
     "hca_attn": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
                  _vp, _int, _vp, _vp, _vp, _sz, _vp],
     "sparse_mqa_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _i64, _i64,
-                           _int, _f32, _int, _vp, _vp, _int, _vp, _sz, _vp],
+                           _int, _f32, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
     "hca_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
-                    _vp, _int, _vp, _vp, _int, _vp, _sz, _vp],
+                    _vp, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
 }
 
 _lib = None
@@ -122,7 +126,8 @@ class _CompressJob(ctypes.Structure):
     _fields_ = [("ratio", _int), ("B", _i64), ("n_tok", _i64), ("c", _i64), ("pos0", _i64),
                 ("Ca", _vp), ("Za", _vp), ("Cb", _vp), ("Zb", _vp), ("prev_Cb", _vp), ("prev_Zb", _vp),
                 ("bias", _vp), ("gamma", _vp), ("eps", _f32), ("in_dtype", _int), ("out_dtype", _int),
-                ("out", _vp), ("out_batch_stride", _i64)]
+                ("out", _vp), ("out_batch_stride", _i64), ("rope_dims", _int), ("rope_base", _f32),
+                ("rope_anchor", _int)]
 
 
 def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
@@ -146,8 +151,8 @@ def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
 def csa_compress_batch(jobs, stream=None):
     """Several stage-1 calls of one ratio and dtype pair in one launch.  Each job
     is a dict of csa_compress's arguments (ratio, Ca, Za, bias and optionally
-    Cb, Zb, prev_Cb, prev_Zb, pos0, gamma, eps, out, out_dtype, cache_entry0);
-    returns the list of outputs."""
+    Cb, Zb, prev_Cb, prev_Zb, pos0, gamma, eps, out, out_dtype, cache_entry0,
+    rope_dims, rope_base, rope_anchor); returns the list of outputs."""
     arr = (_CompressJob * len(jobs))()
     outs = []
     for j, d in zip(arr, jobs):
@@ -160,6 +165,8 @@ def csa_compress_batch(jobs, stream=None):
         j.prev_Cb, j.prev_Zb = _ptr(d.get("prev_Cb")), _ptr(d.get("prev_Zb"))
         j.bias, j.gamma, j.eps = _ptr(d["bias"]), _ptr(d.get("gamma")), d.get("eps", 1e-6)
         j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _dt(out), optr, stride
+        j.rope_dims, j.rope_base, j.rope_anchor = (d.get("rope_dims", 0), d.get("rope_base", ROPE_BASE),
+                                                   d.get("rope_anchor", 0))
     st = library().csa_compress_batch(arr, len(jobs), _stream(stream))
     _check(st, "csa_compress_batch")
     return outs
@@ -167,20 +174,23 @@ def csa_compress_batch(jobs, stream=None):
 
 def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
                  gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, workspace=None,
-                 stream=None):
+                 rope_dims=0, rope_base=ROPE_BASE, rope_anchor=0, stream=None):
     """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c].
 
     With ``cache_entry0`` set, ``out`` is a [B, N_cache, c] cache and the new
     entries are written in place at entries cache_entry0 .. cache_entry0 +
     n_tok//ratio - 1 of every sequence.  ``workspace`` defaults to a fresh
-    buffer of the size that enables the row split; an empty tensor disables it."""
+    buffer of the size that enables the row split; an empty tensor disables it.
+    ``rope_dims`` > 0: partial RoPE on each entry's last rope_dims channels at
+    position pos0 + ratio*i + rope_anchor (csa_compress_ex)."""
     B, n_tok, c = Ca.shape
     in_dt = _dt(Ca)
     out, optr, stride = _compress_out(Ca, ratio, out, out_dtype, cache_entry0)
     ws, wsb = _workspace(OP_COMPRESS, B, n_tok, c, ratio, Ca.device, workspace)
-    st = library().csa_compress(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
-                                _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
-                                _dt(out), optr, stride, _ptr(ws), wsb, _stream(stream))
+    st = library().csa_compress_ex(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
+                                   _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
+                                   _dt(out), optr, stride, rope_dims, rope_base, rope_anchor, _ptr(ws), wsb,
+                                   _stream(stream))
     _check(st, "csa_compress")
     return out
 
@@ -215,9 +225,10 @@ def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=
 
 def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, scale=None,
                     out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False,
-                    stream=None):
+                    rope_dims=0, rope_base=ROPE_BASE, stream=None):
     """Stage 4.  q: [B, T, 64, 512], kv_cmp: [B, N, 512], idx: [B, T, k], kv_raw: [B, n_raw, 512].
-    ``batch_invariant``: no row split, so each query's bits do not depend on the batch."""
+    ``batch_invariant``: no row split, so each query's bits do not depend on the batch.
+    ``rope_dims`` > 0: inverse partial RoPE on the output at each query's position."""
     B, T, H, d = q.shape
     N = kv_cmp.shape[1]
     k = idx.shape[2]
@@ -233,16 +244,18 @@ def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, sca
         ws, wsb = _workspace(OP_SPARSE_ATTN, B, T, N, k, q.device, workspace)
     st = library().sparse_mqa_attn_ex(B, T, N, k, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(idx),
                                       _ptr(kv_raw), raw_pos0, n_raw, window, scale, _dt(q), _ptr(out),
-                                      _ptr(lse), ATTN_BATCH_INVARIANT if batch_invariant else 0, _ptr(ws),
-                                      wsb, _stream(stream))
+                                      _ptr(lse), ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims,
+                                      rope_base, _ptr(ws), wsb, _stream(stream))
     _check(st, "sparse_mqa_attn")
     return (out, lse) if return_lse else out
 
 
 def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, window=128, scale=None,
-             out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False, stream=None):
+             out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False, rope_dims=0,
+             rope_base=ROPE_BASE, stream=None):
     """Stage 5.  Dense MQA over all visible entries and the window, optional sink [64].
-    ``batch_invariant``: no row split, so each query's bits do not depend on the batch."""
+    ``batch_invariant``: no row split, so each query's bits do not depend on the batch.
+    ``rope_dims`` > 0: inverse partial RoPE on the output at each query's position."""
     B, T, H, d = q.shape
     N = kv_cmp.shape[1]
     n_raw = kv_raw.shape[1]
@@ -257,6 +270,20 @@ def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, windo
         ws, wsb = _workspace(OP_HCA_ATTN, B, T, N, 0, q.device, workspace)
     st = library().hca_attn_ex(B, T, N, ratio, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(kv_raw),
                                raw_pos0, n_raw, window, scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse),
-                               ATTN_BATCH_INVARIANT if batch_invariant else 0, _ptr(ws), wsb, _stream(stream))
+                               ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims, rope_base, _ptr(ws),
+                               wsb, _stream(stream))
     _check(st, "hca_attn")
     return (out, lse) if return_lse else out
+
+
+def rope(x, *, pos0, rope_dims=64, rope_base=ROPE_BASE, inverse=False, stream=None):
+    """Partial RoPE in place on x [B, T, H, D] or [B, T, D] (row t at pos0 + t); returns x."""
+    if x.dim() == 3:
+        B, T, D = x.shape
+        H = 1
+    else:
+        B, T, H, D = x.shape
+    st = library().csa_rope(B, T, H, D, pos0, rope_dims, rope_base, 1 if inverse else 0, _dt(x), _ptr(x),
+                            _stream(stream))
+    _check(st, "csa_rope")
+    return x

@@ -37,6 +37,8 @@
 // kernel merges them in a fixed order (bit-reproducible results).
 #include <type_traits>
 
+#include <cmath>
+
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -67,7 +69,25 @@ struct Params {
   float* lse;
   float* ws;
   int splits;
+  int rope_R;           // inverse RoPE on the output's last rope_R dims (0: none)
+  double rope_l2b;      // log2 of the rotary base
 };
+
+// Inverse partial RoPE of one output value held by this lane at column col,
+// given the (cos, sin) of its pair's angle; the value of column col ^ 1 sits
+// in lane ^ 1.  Every lane of the wave calls it (the exchange is wave-wide);
+// columns outside the rotated part keep their value.
+__device__ __forceinline__ float inv_rope_lane(float v, int col, float2 k, const Params& P) {
+  const float other = __shfl_xor(v, 1, 64);
+  if (col < kD - P.rope_R) return v;
+  return (col & 1) ? other * k.y + v * k.x : v * k.x - other * k.y;
+}
+// (cos, sin) of the inverse rotation of the pair holding column col
+__device__ __forceinline__ float2 inv_rope_cs(int col, int64_t pos, const Params& P) {
+  float c = 1.f, s = 0.f;
+  if (col >= kD - P.rope_R) rope_cos_sin(-pos, (col - (kD - P.rope_R)) >> 1, P.rope_R, P.rope_l2b, c, s);
+  return make_float2(c, s);
+}
 
 struct List {
   int64_t n_cmp;   // compressed slots at the head of the list
@@ -215,6 +235,7 @@ attn_bf16_kernel(Params P) {
   __shared__ float4 fshare[kH / 4];       // per-head output factor (epilogue)
   __shared__ uint4 rescale_any[TGN];      // per wave: some head's running max moved
   __shared__ float mlshare[TGN][2][kH];   // per group: running max and sum of each head (merge)
+  __shared__ float2 rope_cs[kD / 2];      // inverse RoPE (cos, sin) of this query's output pairs
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row addressing stays scalar
@@ -238,6 +259,7 @@ attn_bf16_kernel(Params P) {
   const List l = make_list(P, t);
   int64_t tile0, tile1;
   split_range(P, l, split, tile0, tile1);
+
   uint8_t* const T0 = tb0[tg];
   uint8_t* const T1 = tb1[tg];
 
@@ -422,6 +444,15 @@ attn_bf16_kernel(Params P) {
     }
   }
 
+  // The output's inverse RoPE angles, one pair per thread into LDS (formed in
+  // the prologue they would keep values live through the loop and spill);
+  // read after the epilogue's barrier.  A split run leaves this to the
+  // combine.
+  if (__builtin_expect(P.rope_R > 0 && P.splits == 1, 0)) {
+    for (int p = tid; p < P.rope_R / 2; p += 256 * TGN)
+      rope_cs[p] = inv_rope_cs(kD - P.rope_R + 2 * p, P.q_pos0 + t, P);
+  }
+
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
   float l_tot = l_run;
   l_tot += lane_read(x16, l_tot);
@@ -512,10 +543,19 @@ attn_bf16_kernel(Params P) {
       const float4 f4 = fshare[4 * hb + g];
       const float f[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < 8; ++db) {
+        float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[(16 * hg + 4 * g + i) * kD + 16 * db] = f32_to_bf16(o[8 * hb + db][i] * f[i]);
+        for (int i = 0; i < 4; ++i) v[i] = o[8 * hb + db][i] * f[i];
+        if (__builtin_expect(P.rope_R > 0, 0)) {
+          const int col = 128 * wid + 16 * db + j;
+          const float2 k = rope_cs[(col - (kD - P.rope_R) > 0 ? col - (kD - P.rope_R) : 0) >> 1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = inv_rope_lane(v[i], col, k, P);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[(16 * hg + 4 * g + i) * kD + 16 * db] = f32_to_bf16(v[i]);
+      }
     }
   } else if constexpr (HB == 4) {
     // partial O in bf16 in the MFMA's own layout, 8 bytes per lane:
@@ -597,7 +637,20 @@ attn_f32_kernel(Params P) {
   const float f = em / denom;
   float* out = static_cast<float*>(P.out) + (gq * kH + head) * kD + part * 16;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) out[i] = ov[i] * f;
+  for (int i = 0; i < 16; ++i) ov[i] *= f;
+  if (__builtin_expect(P.rope_R > 0, 0)) {   // inverse partial RoPE at the query's position; pairs are thread-local
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int col = part * 16 + i;
+      if (col >= kD - P.rope_R) {
+        float cs, sn;
+        rope_cos_sin(-(P.q_pos0 + t), (col - (kD - P.rope_R)) >> 1, P.rope_R, P.rope_l2b, cs, sn);
+        rope_pair(ov[i], ov[i + 1], cs, sn);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) out[i] = ov[i];
   if (P.lse && part == 0) P.lse[gq * kH + head] = kLn2 * (M + log2f(denom));
 }
 
@@ -621,6 +674,15 @@ attn_combine_kernel(Params P) {
   const int ln = tid & 63, g = ln >> 4, j = ln & 15, db0 = tid >> 6;
   const int h0 = 16 * hb + 4 * g;   // first of this thread's four heads
   const uint2* src = reinterpret_cast<const uint2*>(base) + ((w * 4 + hb) * 8 + db0) * 64 + ln;
+  // inverse RoPE (cos, sin) of this thread's two columns, formed while the
+  // partials load
+  const int c0 = 16 * db0 + j, c1 = c0 + 64;
+  float2 k0 = make_float2(1.f, 0.f), k1 = k0;
+  if (__builtin_expect(P.rope_R > 0, 0)) {
+    const int64_t pos = P.q_pos0 + gq % P.T;
+    k0 = inv_rope_cs(128 * w + c0, pos, P);
+    k1 = inv_rope_cs(128 * w + c1, pos, P);
+  }
   float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, L[4] = {0.f, 0.f, 0.f, 0.f};
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
 #pragma unroll 4
@@ -661,15 +723,20 @@ attn_combine_kernel(Params P) {
     if (P.lse && w == 0 && db0 == 0 && j == 0) P.lse[gq * kH + h0 + i] = kLn2 * (Mi + log2f(denom));
   }
   // heads 4g..4g+3 of the block, columns 16 db + j of the quarter
-  const int c0 = 16 * db0 + j, c1 = c0 + 64;
-  ot[(4 * g + 0) * 128 + c0] = f32_to_bf16(acc0.x * f[0]);
-  ot[(4 * g + 1) * 128 + c0] = f32_to_bf16(acc0.y * f[1]);
-  ot[(4 * g + 2) * 128 + c0] = f32_to_bf16(acc0.z * f[2]);
-  ot[(4 * g + 3) * 128 + c0] = f32_to_bf16(acc0.w * f[3]);
-  ot[(4 * g + 0) * 128 + c1] = f32_to_bf16(acc1.x * f[0]);
-  ot[(4 * g + 1) * 128 + c1] = f32_to_bf16(acc1.y * f[1]);
-  ot[(4 * g + 2) * 128 + c1] = f32_to_bf16(acc1.z * f[2]);
-  ot[(4 * g + 3) * 128 + c1] = f32_to_bf16(acc1.w * f[3]);
+  float v0[4] = {acc0.x * f[0], acc0.y * f[1], acc0.z * f[2], acc0.w * f[3]};
+  float v1[4] = {acc1.x * f[0], acc1.y * f[1], acc1.z * f[2], acc1.w * f[3]};
+  if (__builtin_expect(P.rope_R > 0, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v0[i] = inv_rope_lane(v0[i], 128 * w + c0, k0, P);
+      v1[i] = inv_rope_lane(v1[i], 128 * w + c1, k1, P);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ot[(4 * g + i) * 128 + c0] = f32_to_bf16(v0[i]);
+    ot[(4 * g + i) * 128 + c1] = f32_to_bf16(v1[i]);
+  }
   __syncthreads();
   const int r = tid >> 4, c = (tid & 15) * 8;
   uint16_t* out = static_cast<uint16_t*>(P.out) + (gq * kH + 16 * hb + r) * kD + 128 * w + c;
@@ -686,6 +753,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   P.raw_pos0 = a.raw_pos0; P.n_raw = a.n_raw; P.window = a.window;
   P.scale_log2 = a.scale * kLog2e; P.sink = a.sink; P.out = a.out; P.lse = a.lse;
   P.ws = static_cast<float*>(a.ws);
+  P.rope_R = a.rope_dims;
+  P.rope_l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
   const int64_t nq = a.B * a.T;
   if (a.io_dtype == CSA_F32) {
     P.splits = 1;

@@ -32,17 +32,28 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
+int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
+                    const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
+                    const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
+                    int out_dtype, void* out, int64_t out_batch_stride, int rope_dims, float rope_base,
+                    int rope_anchor, void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
+                                      gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes,
+                                      rope_dims, rope_base, rope_anchor);
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs a{ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb,
+                      bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes,
+                      rope_dims, rope_base, rope_anchor};
+  return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
+}
+
 int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
                  const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
                  const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
                  int out_dtype, void* out, int64_t out_batch_stride, void* workspace, size_t ws_bytes,
                  void* stream) {
-  csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
-                                      gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes);
-  if (!ck.ok()) return finish(ck);
-  csa::CompressArgs a{ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb,
-                      bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes};
-  return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
+  return csa_compress_ex(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,
+                         out_dtype, out, out_batch_stride, 0, 0.f, 0, workspace, ws_bytes, stream);
 }
 
 int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
@@ -55,7 +66,7 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
     const csa_compress_job& j = jobs[q];
     csa::Check cj = csa::check_compress(j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb,
                                         j.prev_Zb, j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out,
-                                        j.out_batch_stride, nullptr, 0);
+                                        j.out_batch_stride, nullptr, 0, j.rope_dims, j.rope_base, j.rope_anchor);
     if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || j.out_dtype != jobs[0].out_dtype))
       cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype");
     if (!cj.ok()) {
@@ -63,7 +74,8 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
       return finish(cj);
     }
     a[q] = csa::CompressArgs{j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb,
-                             j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out, j.out_batch_stride, nullptr, 0};
+                             j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out, j.out_batch_stride, nullptr, 0,
+                             j.rope_dims, j.rope_base, j.rope_anchor};
   }
   return hip_status(csa::launch_compress_batch(a, n_jobs, as_stream(stream)), "csa_compress_batch launch");
 }
@@ -89,12 +101,13 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
 int sparse_mqa_attn_ex(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,
                        const void* kv_cmp, const int32_t* idx, const void* kv_raw, int64_t raw_pos0,
                        int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse, int flags,
-                       void* workspace, size_t ws_bytes, void* stream) {
+                       int rope_dims, float rope_base, void* workspace, size_t ws_bytes, void* stream) {
   csa::Check ck = csa::check_sparse(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw,
-                                    window, scale, io_dtype, out, lse, workspace, ws_bytes, flags);
+                                    window, scale, io_dtype, out, lse, workspace, ws_bytes, flags, rope_dims,
+                                    rope_base);
   if (!ck.ok()) return finish(ck);
   csa::AttnArgs a{B, T, N, k, 4, q_pos0, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
-                  nullptr, io_dtype, out, lse, workspace, flags};
+                  nullptr, io_dtype, out, lse, workspace, flags, rope_dims, rope_base};
   return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn launch");
 }
 
@@ -103,18 +116,18 @@ int sparse_mqa_attn(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int 
                     int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse,
                     void* workspace, size_t ws_bytes, void* stream) {
   return sparse_mqa_attn_ex(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
-                            io_dtype, out, lse, 0, workspace, ws_bytes, stream);
+                            io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
 }
 
 int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
                 const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
-                float scale, const float* sink, int io_dtype, void* out, float* lse, int flags, void* workspace,
-                size_t ws_bytes, void* stream) {
+                float scale, const float* sink, int io_dtype, void* out, float* lse, int flags, int rope_dims,
+                float rope_base, void* workspace, size_t ws_bytes, void* stream) {
   csa::Check ck = csa::check_hca(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window,
-                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes, flags);
+                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes, flags, rope_dims, rope_base);
   if (!ck.ok()) return finish(ck);
   csa::AttnArgs a{B, T, N, 0, ratio, q_pos0, q, kv_cmp, nullptr, kv_raw, raw_pos0, n_raw, window, scale,
-                  sink, io_dtype, out, lse, workspace, flags};
+                  sink, io_dtype, out, lse, workspace, flags, rope_dims, rope_base};
   return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn launch");
 }
 
@@ -123,7 +136,15 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
              float scale, const float* sink, int io_dtype, void* out, float* lse, void* workspace,
              size_t ws_bytes, void* stream) {
   return hca_attn_ex(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window, scale, sink,
-                     io_dtype, out, lse, 0, workspace, ws_bytes, stream);
+                     io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
+}
+
+int csa_rope(int64_t B, int64_t T, int64_t H, int64_t D, int64_t pos0, int rope_dims, float rope_base,
+             int inverse, int dtype, void* x, void* stream) {
+  csa::Check ck = csa::check_rope_rows(B, T, H, D, pos0, rope_dims, rope_base, inverse, dtype, x);
+  if (!ck.ok()) return finish(ck);
+  csa::RopeArgs a{B, T, H, D, pos0, rope_dims, rope_base, inverse, dtype, x};
+  return hip_status(csa::launch_rope(a, as_stream(stream)), "csa_rope launch");
 }
 
 size_t csa_workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int k) {

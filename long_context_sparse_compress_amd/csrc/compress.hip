@@ -4,7 +4,9 @@
 // formula of "DeepSeek-V4技术报告解读，全适配国产算力" (2.1): each entry is a
 // per-channel softmax-weighted sum of 8 raw tokens at stride 4 (C4A: the
 // current block from Ca/Za, the previous block from Cb/Zb, a positional bias
-// on the 8 logits) or 128 raw tokens at stride 128 (C128A), then RMSNorm.
+// on the 8 logits) or 128 raw tokens at stride 128 (C128A), then RMSNorm and,
+// when asked, partial RoPE at the entry's anchor position (Partial Rotary
+// Positional Embedding; the CSA operator graph's RMSNorm + RoPE).
 //
 // The work is pure streaming (C128A reads 257 rows' worth of bytes per
 // entry), so the kernel is organised for HBM bandwidth:
@@ -15,6 +17,8 @@
 //    channel in registers, so every input byte is read exactly once;
 //  * the G partial states are merged through LDS, then RMSNorm is a
 //    block-wide reduction over channels.
+#include <cmath>
+
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -73,6 +77,7 @@ __device__ __forceinline__ void store_out(TO* p, const float* f) {
 }
 
 constexpr int kChunkRows = 4;   // rows per thread whose loads are in flight together
+constexpr int kMaxRopePairs = 512;   // c <= 1024
 
 struct Online {
   float m, s, y;   // running max (log2 domain), sum of weights, weighted content
@@ -110,7 +115,8 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                                                const float* __restrict__ bias, const float* __restrict__ gamma,
                                                float eps, TO* __restrict__ out, int64_t out_stride, int G,
-                                               float* __restrict__ part) {
+                                               float* __restrict__ part, int rope_R, double rope_l2b,
+                                               int rope_anchor) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   constexpr int UC = kChunkRows;
@@ -134,6 +140,21 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
   Online st[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) st[v] = Online{-INFINITY, 0.f, 0.f};
+
+  // Partial RoPE (cos, sin) of the entry's R/2 channel pairs at its anchor
+  // position: one pair per thread, into LDS, before the rows stream in (kept
+  // in registers through the loop they would push it past the register limit
+  // of 1024-thread workgroups; formed after it by the few threads that own
+  // them, their latency would add up).  Read after the RMSNorm barrier.
+  __shared__ float2 rope_tab[kMaxRopePairs];
+  if (!SPLIT && __builtin_expect(rope_R > 0, 0)) {
+    for (int p = tid; p < rope_R / 2; p += blockDim.x) {
+      float cs, sn;
+      rope_cos_sin(pos0 + i * RATIO + rope_anchor, p, rope_R, rope_l2b, cs, sn);
+      rope_tab[p] = make_float2(cs, sn);
+    }
+  }
+
 
   const int64_t seq = b * n_tok * c;
   for (int r0 = rlo + g; r0 < rhi; r0 += G * UC) {
@@ -274,6 +295,17 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
   float o[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * gm[v];
+  // partial RoPE at the entry's anchor position; a thread's VEC channels hold
+  // whole pairs (the rotated part starts at an even channel)
+  if (__builtin_expect(rope_R > 0, 0) && ch0 + VEC > c - rope_R) {
+#pragma unroll
+    for (int v = 0; v < VEC; v += 2) {
+      if (ch0 + v >= c - rope_R) {
+        const float2 k = rope_tab[(ch0 + v - (c - rope_R)) / 2];
+        rope_pair(o[v], o[v + 1], k.x, k.y);
+      }
+    }
+  }
   store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
 }
 
@@ -284,10 +316,11 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ Cb, const TI* __restrict__ Zb,
                 const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                 const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
-                TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part) {
+                TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part, int rope_R,
+                double rope_l2b, int rope_anchor) {
   compress_entry<TI, TO, RATIO, SPLIT>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
                                        static_cast<int>(gridDim.z), n_tok, c, pos0, Ca, Za, Cb, Zb, pCb, pZb, bias,
-                                       gamma, eps, out, out_stride, G, part);
+                                       gamma, eps, out, out_stride, G, part, rope_R, rope_l2b, rope_anchor);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -300,6 +333,9 @@ struct CompressJobDev {
   int64_t n_tok, pos0, out_stride, n_ent, B;
   float eps;
   int c, G;
+  int rope_R;
+  double rope_l2b;
+  int rope_anchor;
 };
 constexpr int kMaxBatchJobs = 4;
 struct CompressBatch {
@@ -315,7 +351,8 @@ compress_batch_kernel(CompressBatch jb) {
                                        static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                        static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
                                        static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias, J.gamma,
-                                       J.eps, static_cast<TO*>(J.out), J.out_stride, J.G, nullptr);
+                                       J.eps, static_cast<TO*>(J.out), J.out_stride, J.G, nullptr, J.rope_R,
+                                       J.rope_l2b, J.rope_anchor);
 }
 
 // Merge of the row-range states of one (entry, sequence), then RMSNorm.  One
@@ -325,7 +362,8 @@ compress_batch_kernel(CompressBatch jb) {
 template <typename TO>
 __global__ void __launch_bounds__(1024)
 compress_merge_kernel(int64_t n_ent, int c, int P, const float* __restrict__ part,
-                      const float* __restrict__ gamma, float eps, TO* __restrict__ out, int64_t out_stride) {
+                      const float* __restrict__ gamma, float eps, TO* __restrict__ out, int64_t out_stride,
+                      int64_t pos0, int ratio, int rope_R, double rope_l2b, int rope_anchor) {
   constexpr int kMaxP = 16;
   __shared__ float red[16];
   const int ch = threadIdx.x;
@@ -355,11 +393,23 @@ compress_merge_kernel(int64_t n_ent, int c, int P, const float* __restrict__ par
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < (c + 63) / 64; ++w) tot += red[w];
-  const float o = y * rsqrtf(tot / static_cast<float>(c) + eps) * (gamma ? gamma[ch] : 1.f);
+  float o = y * rsqrtf(tot / static_cast<float>(c) + eps) * (gamma ? gamma[ch] : 1.f);
+  if (__builtin_expect(rope_R > 0, 0)) {   // partial RoPE: the pair partner of channel ch is lane ch ^ 1
+    const float other = __shfl_xor(o, 1, 64);
+    if (ch >= c - rope_R) {
+      float cs, sn;
+      rope_cos_sin(pos0 + i * ratio + rope_anchor, (ch - (c - rope_R)) / 2, rope_R, rope_l2b, cs, sn);
+      float x = (ch & 1) ? other : o, yv = (ch & 1) ? o : other;
+      rope_pair(x, yv, cs, sn);
+      o = (ch & 1) ? yv : x;
+    }
+  }
   TO* dst = out + b * out_stride + i * c + ch;
   if constexpr (sizeof(TO) == 4) *reinterpret_cast<float*>(dst) = o;
   else *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(o);
 }
+
+double rope_log2_base(const CompressArgs& a) { return a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0; }
 
 template <typename TI, typename TO, int RATIO>
 hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
@@ -393,17 +443,18 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
       const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), static_cast<uint32_t>(P));
       hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, true>), grid, dim3(threads), smem, s, a.n_tok,
                          static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
-                         static_cast<TO*>(a.out), stride, G, part);
+                         static_cast<TO*>(a.out), stride, G, part, 0, 0.0, 0);
       hipLaunchKernelGGL((compress_merge_kernel<TO>), dim3(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B)),
                          dim3(static_cast<uint32_t>(a.c)), 0, s, n_ent, static_cast<int>(a.c), P, part, a.gamma,
-                         a.eps, static_cast<TO*>(a.out), stride);
+                         a.eps, static_cast<TO*>(a.out), stride, a.pos0, RATIO, a.rope_dims, rope_log2_base(a),
+                         a.rope_anchor);
       return hipGetLastError();
     }
   }
   const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), 1);
   hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, false>), grid, dim3(threads), smem, s, a.n_tok,
                      static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
-                     static_cast<TO*>(a.out), stride, G, nullptr);
+                     static_cast<TO*>(a.out), stride, G, nullptr, a.rope_dims, rope_log2_base(a), a.rope_anchor);
   return hipGetLastError();
 }
 
@@ -429,7 +480,7 @@ hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
     gy = a.B > gy ? a.B : gy;
     jb.j[q] = CompressJobDev{a.Ca, a.Za, a.Cb, a.Zb, a.prev_Cb, a.prev_Zb, a.bias, a.gamma, a.out, a.n_tok, a.pos0,
                              a.out_batch_stride ? a.out_batch_stride : n_ent * a.c, n_ent, a.B, a.eps,
-                             static_cast<int>(a.c), G};
+                             static_cast<int>(a.c), G, a.rope_dims, rope_log2_base(a), a.rope_anchor};
   }
   hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO>),
                      dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),

@@ -73,6 +73,29 @@ __device__ __forceinline__ float lane_read(int addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
 }
 
+// Partial rotary embedding ("DeepSeek V4 结构速览", Partial Rotary Positional
+// Embedding; the rotation is RoFormer's): pair p of the last R dimensions,
+// (x[2p], x[2p+1]) of that part, turns by pos * base^(-2p/R).  At a million
+// tokens of context the angle reaches ~1e6 rad, so it is counted in turns in
+// fp64 -- pos * theta / 2pi, whose fractional part is exact -- and only the
+// reduced angle, |a| <= pi, goes to the fp32 sine and cosine (an angle error
+// near 1e-9 rad; no fp64 trigonometry with its long-argument reduction).
+// log2_base = log2(base), formed once on the host in fp64.
+__device__ inline void rope_cos_sin(int64_t pos, int p, int R, double log2_base, float& c, float& s) {
+  constexpr double kLog2TwoPi = 2.65149612947231879804;   // log2(2 pi)
+  constexpr double k2Pi = 6.28318530717958647693;
+  const double turns = static_cast<double>(pos) * exp2(-(2.0 * p / R) * log2_base - kLog2TwoPi);
+  const double frac = turns - rint(turns);              // in [-1/2, 1/2]
+  sincosf(static_cast<float>(frac * k2Pi), &s, &c);
+}
+// (x, y) -> (x c - y s, x s + y c)
+__device__ __forceinline__ void rope_pair(float& x, float& y, float c, float s) {
+  const float nx = x * c - y * s;
+  const float ny = x * s + y * c;
+  x = nx;
+  y = ny;
+}
+
 // Round-robin workgroup dispatch puts consecutive workgroup ids on different
 // XCDs (8 on MI355X).  Remap a linear id so that ids [x*per, (x+1)*per) run on
 // XCD x, keeping neighbouring tiles (and their shared data) in one L2.

@@ -22,6 +22,9 @@ struct CompressArgs {
   int64_t out_batch_stride;
   void* ws;          // optional row-split workspace
   size_t ws_bytes;
+  int rope_dims;     // partial RoPE on the last rope_dims channels (0: none)
+  float rope_base;
+  int rope_anchor;   // entry i's position: pos0 + ratio * i + rope_anchor
 };
 
 struct IndexArgs {
@@ -64,6 +67,17 @@ struct AttnArgs {
   float* lse;
   void* ws;
   int flags;          // CSA_ATTN_* bits
+  int rope_dims;      // inverse RoPE on the output's last rope_dims dims (0: none)
+  float rope_base;
+};
+
+struct RopeArgs {
+  int64_t B, T, H, D, pos0;
+  int dims;
+  float base;
+  int inverse;
+  int dtype;
+  void* x;
 };
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
@@ -72,5 +86,6 @@ hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s)
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 
 }  // namespace csa

@@ -43,6 +43,21 @@ struct Check {
 
 inline std::string i2s(int64_t v) { return std::to_string(v); }
 
+// Partial RoPE parameters: 0 dims (none), or a multiple of 8 up to the row
+// width with a finite base > 1.
+inline bool check_rope(Check& k, int dims, float base, int64_t width) {
+  if (dims < 0 || dims % 8 != 0 || dims > width) {
+    k.fail(CSA_ERR_INVALID_ARG, "rope_dims must be 0 or a multiple of 8 up to " + std::to_string(width) + ", got " +
+                                    std::to_string(dims));
+    return false;
+  }
+  if (dims > 0 && !(base > 1.0f && std::isfinite(base))) {
+    k.fail(CSA_ERR_INVALID_ARG, "rope_base must be finite and > 1");
+    return false;
+  }
+  return true;
+}
+
 inline void check_attn_flags(Check& k, int flags) {
   if (flags & ~CSA_ATTN_BATCH_INVARIANT) k.fail(CSA_ERR_INVALID_ARG, "unknown attention flags " + std::to_string(flags));
 }
@@ -118,11 +133,14 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
                             const void* Ca, const void* Za, const void* Cb, const void* Zb,
                             const void* prev_Cb, const void* prev_Zb, const float* bias,
                             const float* gamma, float eps, int in_dtype, int out_dtype,
-                            const void* out, int64_t out_batch_stride, const void* ws, size_t ws_bytes) {
+                            const void* out, int64_t out_batch_stride, const void* ws, size_t ws_bytes,
+                            int rope_dims = 0, float rope_base = 0.f, int rope_anchor = 0) {
   Check k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (B < 0 || n_tok < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and n_tok must be >= 0"); return k; }
   if (c <= 0 || c % 64 != 0 || c > 1024) { k.fail(CSA_ERR_INVALID_ARG, "c must be a positive multiple of 64, at most 1024, got " + i2s(c)); return k; }
+  if (!check_rope(k, rope_dims, rope_base, c)) return k;
+  if (rope_anchor < 0 || rope_anchor >= ratio) { k.fail(CSA_ERR_INVALID_ARG, "rope_anchor must be in [0, ratio), got " + i2s(rope_anchor)); return k; }
   if (pos0 < 0 || pos0 % ratio != 0) { k.fail(CSA_ERR_INVALID_ARG, "pos0 must be >= 0 and a multiple of ratio, got " + i2s(pos0)); return k; }
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
   if (out_dtype != CSA_F32 && out_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32 or CSA_BF16"); return k; }
@@ -214,11 +232,13 @@ inline bool check_attn_common(Check& k, int64_t B, int64_t T, int64_t q_pos0, in
 inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos0, int H, int d,
                           const void* q, const void* kv_cmp, const void* idx, const void* kv_raw,
                           int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype,
-                          const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0) {
+                          const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0,
+                          int rope_dims = 0, float rope_base = 0.f) {
   Check k;
   check_attn_flags(k, flags);
   if (!k.ok()) return k;
   if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
+  if (!check_rope(k, rope_dims, rope_base, d)) return k;
   if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
   if (kk < 0 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [0, 2048], got " + i2s(kk)); return k; }
   const bool empty = (B == 0 || T == 0);
@@ -238,12 +258,14 @@ inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos
 inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
                        const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
                        int64_t n_raw, int window, float scale, const void* sink, int io_dtype,
-                       const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0) {
+                       const void* out, const void* lse, const void* ws, size_t ws_bytes, int flags = 0,
+                       int rope_dims = 0, float rope_base = 0.f) {
   Check k;
   check_attn_flags(k, flags);
   if (!k.ok()) return k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (!check_attn_common(k, B, T, q_pos0, H, d, raw_pos0, n_raw, window, scale, io_dtype)) return k;
+  if (!check_rope(k, rope_dims, rope_base, d)) return k;
   if (N < 0) { k.fail(CSA_ERR_INVALID_ARG, "N must be >= 0"); return k; }
   if (T > 0 && N < visible(q_pos0 + T - 1, ratio)) { k.fail(CSA_ERR_INVALID_ARG, "N = " + i2s(N) + " is smaller than the entries visible to the last query"); return k; }
   const bool empty = (B == 0 || T == 0);
@@ -256,6 +278,22 @@ inline Check check_hca(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "hca_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");
   }
+  return k;
+}
+
+inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t pos0, int dims, float base,
+                             int inverse, int dtype, const void* x) {
+  Check k;
+  if (B < 0 || T < 0 || H < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T and H must be >= 0"); return k; }
+  if (D <= 0 || D % 8 != 0 || D > 65536) { k.fail(CSA_ERR_INVALID_ARG, "D must be a positive multiple of 8, at most 65536, got " + i2s(D)); return k; }
+  if (dims == 0 || dims > 1024) { k.fail(CSA_ERR_INVALID_ARG, "rope_dims must be in [8, 1024], got " + i2s(dims)); return k; }
+  if (!check_rope(k, dims, base, D)) return k;
+  if (B * T > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B * T must be below 2^31"); return k; }
+  if (H > (int64_t{1} << 24)) { k.fail(CSA_ERR_INVALID_ARG, "H must be at most 2^24"); return k; }
+  if (pos0 < 0 || pos0 > (int64_t{1} << 40)) { k.fail(CSA_ERR_INVALID_ARG, "pos0 must be in [0, 2^40]"); return k; }
+  if (inverse != 0 && inverse != 1) { k.fail(CSA_ERR_INVALID_ARG, "inverse must be 0 or 1"); return k; }
+  if (dtype != CSA_F32 && dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "dtype must be CSA_F32 or CSA_BF16"); return k; }
+  k.ptr(x, "x", B > 0 && T > 0 && H > 0);
   return k;
 }
 

@@ -10,6 +10,12 @@ from the same compressor on 256 x 128 inputs; q_I 256 x 64 x 128 ~ N(0,
 1/128); w ~ U(0,1); k = 16; q 256 x 64 x 512 ~ N(0,1); raw window latents
 256 x 512 ~ N(0,1); scale 1/sqrt(512); seed 0.
 
+With ``rope`` (a number of dims R), partial RoPE runs through the chain on
+both sides: the compressor rotates its entries (512-d and 128-d keys, anchor
+offsets 1 for C4A and 5 for C128A), q, the indexer queries and the window
+rows are rotated at their positions, and both attentions apply the inverse
+RoPE to their outputs.
+
 Top-k comparison: the selected sets must be equal, except that an entry whose
 oracle score lies within 1e-3 relative of the row's k-th oracle score may be
 swapped for another such entry (ties within fp32 rounding of the two
@@ -25,9 +31,11 @@ import synth
 from oracle import attention as oa
 from oracle import compressor as oc
 from oracle import indexer as oi
+from oracle import rope as orp
 from oracle import topk as ot
 
 N_TOK, K, WIN = 256, 16, 128
+ANCHOR4, ANCHOR128 = 1, 5
 
 
 def _d(x):
@@ -48,30 +56,39 @@ def inputs(seed=0):
     )
 
 
-def run_gpu(x):
+def run_gpu(x, rope=0):
     m, kc, hc = x["main"], x["keyc"], x["hca"]
-    kv = csa.csa_compress(4, _d(m["Ca"]), _d(m["Za"]), _d(m["bias"]), _d(m["Cb"]), _d(m["Zb"]))
-    keys = csa.csa_compress(4, _d(kc["Ca"]), _d(kc["Za"]), _d(kc["bias"]), _d(kc["Cb"]), _d(kc["Zb"]))
-    scores = csa.lightning_index(_d(x["qi"]), _d(x["w"]), keys, q_pos0=0, score_dtype=torch.float32)
+    r4 = dict(rope_dims=rope, rope_anchor=ANCHOR4)
+    kv = csa.csa_compress(4, _d(m["Ca"]), _d(m["Za"]), _d(m["bias"]), _d(m["Cb"]), _d(m["Zb"]), **r4)
+    keys = csa.csa_compress(4, _d(kc["Ca"]), _d(kc["Za"]), _d(kc["bias"]), _d(kc["Cb"]), _d(kc["Zb"]), **r4)
+    qi, q, raw = _d(x["qi"]), _d(x["q"]), _d(x["raw"])
+    if rope:
+        for t in (qi, q, raw):
+            csa.rope(t, pos0=0, rope_dims=rope)
+    scores = csa.lightning_index(qi, _d(x["w"]), keys, q_pos0=0, score_dtype=torch.float32)
     idx = csa.topk_select(scores, K, q_pos0=0)
-    out = csa.sparse_mqa_attn(_d(x["q"]), kv, idx, _d(x["raw"]), q_pos0=0, raw_pos0=0)
-    kvh = csa.csa_compress(128, _d(hc["Ca"]), _d(hc["Za"]), _d(hc["bias"]))
-    outh = csa.hca_attn(_d(x["q"]), kvh, _d(x["raw"]), q_pos0=0, raw_pos0=0, sink=_d(x["sink"]))
+    out = csa.sparse_mqa_attn(q, kv, idx, raw, q_pos0=0, raw_pos0=0, rope_dims=rope)
+    kvh = csa.csa_compress(128, _d(hc["Ca"]), _d(hc["Za"]), _d(hc["bias"]), rope_dims=rope, rope_anchor=ANCHOR128)
+    outh = csa.hca_attn(q, kvh, raw, q_pos0=0, raw_pos0=0, sink=_d(x["sink"]), rope_dims=rope)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in
             dict(kv=kv, keys=keys, scores=scores, idx=idx, out=out, kvh=kvh, outh=outh).items()}
 
 
-def run_oracle(x, rows=None):
+def run_oracle(x, rows=None, rope=0):
     m, kc, hc = x["main"], x["keyc"], x["hca"]
-    kv = oc.compress(m["Ca"], m["Za"], m["bias"], 4, m["Cb"], m["Zb"])
-    keys = oc.compress(kc["Ca"], kc["Za"], kc["bias"], 4, kc["Cb"], kc["Zb"])
-    scores = oi.index_scores(x["qi"], x["w"], keys, 0, 4)
+    r4 = dict(rope_dims=rope, rope_anchor=ANCHOR4)
+    kv = oc.compress(m["Ca"], m["Za"], m["bias"], 4, m["Cb"], m["Zb"], **r4)
+    keys = oc.compress(kc["Ca"], kc["Za"], kc["bias"], 4, kc["Cb"], kc["Zb"], **r4)
+    qi, q, raw = x["qi"], x["q"], x["raw"]
+    if rope:
+        qi, q, raw = (orp.rotate_rows(t, 0, rope) for t in (qi, q, raw))
+    scores = oi.index_scores(qi, x["w"], keys, 0, 4)
     stored = scores.astype(np.float32).astype(np.float64)
     idx = ot.topk_select(stored, K, 0, 4)
-    out, _ = oa.sparse_mqa(x["q"], kv, idx, x["raw"], 0, 0, WIN, rows=rows)
-    kvh = oc.compress(hc["Ca"], hc["Za"], hc["bias"], 128)
-    outh, _ = oa.hca_attention(x["q"], kvh, x["raw"], 0, 0, x["sink"], ratio=128, rows=rows)
+    out, _ = oa.sparse_mqa(q, kv, idx, raw, 0, 0, WIN, rows=rows, rope_dims=rope)
+    kvh = oc.compress(hc["Ca"], hc["Za"], hc["bias"], 128, rope_dims=rope, rope_anchor=ANCHOR128)
+    outh, _ = oa.hca_attention(q, kvh, raw, 0, 0, x["sink"], ratio=128, rows=rows, rope_dims=rope)
     return dict(kv=kv, keys=keys, scores=scores, idx=idx, out=out, kvh=kvh, outh=outh)
 
 

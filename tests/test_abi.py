@@ -30,8 +30,8 @@ def lib():
 def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
-                          "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_workspace_bytes",
-                          "csa_last_error", "csa_version"}
+                          "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
+                          "csa_workspace_bytes", "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "long_context_sparse_compress_amd", "libcsa.so")],
@@ -170,13 +170,13 @@ def test_attention_flags_validation(lib):
     se, he = lib.sparse_mqa_attn_ex, lib.hca_attn_ex
     ws = lib.csa_workspace_bytes(3, 2, 1, 64, 16)
 
-    def sp(flags, wsp=None, wsb=0, H=64, n_raw=128):
+    def sp(flags, wsp=None, wsb=0, H=64, n_raw=128, rd=0, rb=10000.0):
         return se(2, 1, 64, 16, 255, H, 512, A, A, A, A, 128, n_raw, 128, 0.04, 1, A, None, flags,
-                  wsp, wsb, None)
+                  rd, rb, wsp, wsb, None)
 
-    def hc(flags, wsp=None, wsb=0, n_raw=128):
+    def hc(flags, wsp=None, wsb=0, n_raw=128, rd=0, rb=10000.0):
         return he(2, 1, 2, 128, 255, 64, 512, A, A, A, 128, n_raw, 128, 0.04, None, 1, A, None, flags,
-                  wsp, wsb, None)
+                  rd, rb, wsp, wsb, None)
 
     for f in (2, 4, -1, 1 | 8):
         assert sp(f, A, ws) == -1 and "unknown attention flags" in _err(lib)
@@ -188,6 +188,46 @@ def test_attention_flags_validation(lib):
     assert sp(1, H=32) == -2
     assert sp(1, n_raw=127) == -1 and "last query" in _err(lib)
     assert hc(1, n_raw=127) == -1 and "last query" in _err(lib)
+    # the output's inverse RoPE: a multiple of 8 up to 512, base > 1
+    for rd in (4, 12, 520, -8):
+        assert sp(1, rd=rd) == -1 and "rope_dims" in _err(lib), rd
+        assert hc(1, rd=rd) == -1 and "rope_dims" in _err(lib), rd
+    for rb in (1.0, 0.5, float("inf"), float("nan")):
+        assert sp(1, rd=64, rb=rb) == -1 and "rope_base" in _err(lib), rb
+    assert sp(1, rd=64, n_raw=127) == -1 and "last query" in _err(lib)
+
+
+def test_rope_validation(lib):
+    """csa_compress_ex's RoPE arguments and csa_rope's checks (host only)."""
+    ce = lib.csa_compress_ex
+
+    def cmp(rd=64, rb=10000.0, ra=0, ratio=4, c=512):
+        cb = A if ratio == 4 else None
+        return ce(ratio, 2, 8, c, 0, A, A, cb, cb, None, None, A, None, 1e-6, 1, 1, A, 0, rd, rb, ra,
+                  None, 0, None)
+
+    for rd in (4, 12, 520, -8):
+        assert cmp(rd=rd) == -1 and "rope_dims" in _err(lib), rd
+    assert cmp(rd=1024, c=512) == -1
+    assert cmp(rb=1.0) == -1 and "rope_base" in _err(lib)
+    assert cmp(ra=4) == -1 and "rope_anchor" in _err(lib)
+    assert cmp(ra=-1) == -1 and "rope_anchor" in _err(lib)
+    assert cmp(ra=127, ratio=128) == 0    # a valid anchor; 8 tokens complete no C128A block: no launch
+    r = lib.csa_rope
+
+    def rp(B=2, T=3, H=4, D=512, pos0=0, rd=64, rb=10000.0, inv=0, dt=1, x=A):
+        return r(B, T, H, D, pos0, rd, rb, inv, dt, x, None)
+
+    assert rp(rd=0) == -1 and "rope_dims" in _err(lib)
+    assert rp(rd=2048, D=4096) == -1 and "rope_dims" in _err(lib)
+    assert rp(rd=520) == -1
+    assert rp(D=12) == -1 and "D must" in _err(lib)
+    assert rp(inv=2) == -1 and "inverse" in _err(lib)
+    assert rp(dt=2) == -2
+    assert rp(x=None) == -1
+    assert rp(pos0=-1) == -1 and "pos0" in _err(lib)
+    assert rp(rb=0.9) == -1 and "rope_base" in _err(lib)
+    assert rp(B=0, x=None) == 0           # nothing to do: no pointer needed, no launch
 
 
 def test_workspace_query(lib):

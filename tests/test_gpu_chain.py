@@ -13,3 +13,12 @@ def test_tiny_chain_all_rows():
     o = chain.run_oracle(x)
     rep = chain.compare(g, o)
     assert rep["topk_rows_equal"] >= 250
+
+
+def test_tiny_chain_with_rope():
+    """The same chain with partial RoPE (64 dims) through every stage."""
+    x = chain.inputs()
+    g = chain.run_gpu(x, rope=64)
+    o = chain.run_oracle(x, rope=64)
+    rep = chain.compare(g, o)
+    assert rep["topk_rows_equal"] >= 250
