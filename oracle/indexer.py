@@ -45,3 +45,31 @@ def index_scores(q, w, k, q_pos0: int, ratio: int = 4, rows=None):
             dots = q[b, t] @ k[b, :v].T            # [H_I, v]
             out[b, r, :v] = w[b, t] @ np.maximum(dots, 0.0)
     return out
+
+
+def pool_scores(q, w, k, pool):
+    """Scores of a candidate pool ("DeepSeek 模型原理进化史", CSA2: the
+    hierarchical sparse indexer re-scores, with the layer's own query, only
+    the entries of a candidate pool found by a full indexer pass).
+
+    q: [B, T, H_I, d_I], w: [B, T, H_I], k: [B, N, d_I], pool: [B, T, P]
+    entry ids (-1, or any id outside 0..N-1, marks an empty slot).  Returns
+    float64 [B, T, P]: the indexer score of entry pool[b,t,j], -inf for an
+    empty slot.  The same equation as ``index_scores``; visibility is the
+    pool's business (a pool from a causal Top-P holds visible entries only)."""
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    pool = np.asarray(pool)
+    B, T, P = pool.shape
+    N = k.shape[1]
+    out = np.full((B, T, P), -np.inf)
+    for b in range(B):
+        for t in range(T):
+            ids = pool[b, t]
+            ok = (ids >= 0) & (ids < N)
+            if not ok.any():
+                continue
+            dots = q[b, t] @ k[b, ids[ok]].T          # [H_I, n_ok]
+            out[b, t, ok] = w[b, t] @ np.maximum(dots, 0.0)
+    return out

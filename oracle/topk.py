@@ -46,3 +46,28 @@ def topk_select(scores, k: int, q_pos0: int, ratio: int = 4, rows=None):
             v = min(visible(q_pos0 + t, ratio), N)
             out[b, r] = select_row(scores[b, t], v, k)
     return out
+
+
+def pool_select(scores, pool, k: int, N: int | None = None):
+    """Top-k inside a candidate pool ("DeepSeek 模型原理进化史", CSA2:
+    hierarchical sparse indexer).
+
+    scores: [B, T, P] stored scores of the pool slots; pool: [B, T, P] entry
+    ids (-1, or an id >= N when N is given, = empty).  The candidates of
+    row (b, t) are its non-empty slots;
+    they are ranked by score, equal scores by the lower entry id (the rule
+    of the full Top-k), and the k best entry ids are returned in rank order,
+    then -1 padding.  [B, T, k] int64."""
+    scores = np.asarray(scores)
+    pool = np.asarray(pool)
+    B, T, P = pool.shape
+    out = np.full((B, T, k), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(T):
+            ok = (pool[b, t] >= 0) & ((pool[b, t] < N) if N is not None else True)
+            ids = pool[b, t][ok].astype(np.int64)
+            key = np.asarray(scores[b, t][ok], dtype=np.float64) + 0.0
+            order = np.lexsort((ids, -key))
+            take = ids[order[:min(k, len(ids))]]
+            out[b, t, :len(take)] = take
+    return out
