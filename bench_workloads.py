@@ -14,6 +14,13 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
   csa_1m_decode  8 sequences at 1,048,576 context: C4A compress (KV and keys),
                  MXFP4 indexer over 262,144 keys, top-1024, sparse MQA
   c128a_1m       C128A compress of all 1,048,576 tokens (8,192 entries)
+  csa_reindex_decode / csa_reindex_prefill
+                 a Reindex layer of the hierarchical sparse indexer: the pool
+                 (2,048 entries per query) comes from a Full layer computed once
+                 before timing (bf16 indexer + top-2,048); timed: pool scoring,
+                 top-512 inside the pool, sparse MQA.  Decode: 32 sequences at
+                 65,536 context (16,384 entries); prefill: the 4,096-token chunk
+                 after 131,072 tokens (33,792 entries)
   hbm_copy       a 1 GiB copy, the calibration point of the HBM byte counters
 """
 from __future__ import annotations
@@ -179,6 +186,42 @@ def run(args, torch, csa, synth):
                    ntok * 512 * 4 + ntok // 128 * 1024, 0, "hbm")]
         queries = 0
         info = dict(tokens=ntok, c128a_entries=ntok // 128)
+    elif wl in ("csa_reindex_decode", "csa_reindex_prefill"):
+        dec = wl == "csa_reindex_decode"
+        B, T, N, q0 = (32, 1, 16384, 65535) if dec else (1, 4096, 33792, 131072)
+        P, k = 2048, 512
+        raw0 = q0 - 127
+        keys = dn("r.keys", (B, N, 128), bf)
+        # the Full layer (untimed): its own query over every key, top-P
+        qf = dn("r.qf", (B, T, 64, 128), bf, var=1.0 / 128)
+        wf = synth.device_uniform("r.wf", (B, T, 64))
+        sf = csa.lightning_index(qf, wf, keys, q_pos0=q0, score_dtype=bf)
+        pool = csa.topk_select(sf, P, q_pos0=q0)
+        del sf, qf, wf
+        # the Reindex layer
+        qi = dn("r.qi", (B, T, 64, 128), bf, var=1.0 / 128)
+        w = synth.device_uniform("r.w", (B, T, 64))
+        kv = dn("r.kv", (B, N, 512), bf)
+        q = dn("r.q", (B, T, 64, 512), bf)
+        raw = dn("r.raw", (B, T + 127, 512), bf)
+        scores = torch.empty(B, T, P, dtype=bf, device="cuda")
+        idx = torch.empty(B, T, k, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+        ws_a = torch.empty(max(16, csa.workspace_bytes(csa.OP_SPARSE_ATTN, B, T, N, k)), dtype=torch.uint8,
+                           device="cuda")
+        nq = B * T
+        stages = [
+            ("lightning_index_pool", lambda: csa.lightning_index_pool(qi, w, keys, pool, scores=scores),
+             nq * (P * 256 + P * 4 + 64 * 128 * 2 + 64 * 4 + P * 2), nq * P * 64 * 128 * 2, "hbm" if dec else "bf16"),
+            ("topk_select_pool", lambda: csa.topk_select_pool(scores, pool, k, N=N, idx=idx),
+             nq * (P * 2 + 2 * k * 4), 0, "hbm"),
+            ("sparse_mqa_attn", lambda: csa.sparse_mqa_attn(q, kv, idx, raw, q_pos0=q0, raw_pos0=raw0, out=out,
+                                                            workspace=ws_a),
+             nq * ((k + 128) * 1024 + k * 4 + 2 * 64 * 512 * 2), nq * (k + 128) * 64 * 512 * 4,
+             "hbm" if dec else "bf16"),
+        ]
+        queries = nq
+        info = dict(batch=B, chunk=T, context=q0 + 1 if dec else q0 + T, c4a_entries=N, pool=P, topk=k)
     elif wl == "hbm_copy":
         # 1 GiB device-to-device copy: the reference point that turns the HBM
         # traffic counters (FETCH_SIZE, WRITE_SIZE) into bytes

@@ -14,7 +14,8 @@
  *
  * and, around them: csa_compress_ex / sparse_mqa_attn_ex / hca_attn_ex (the
  * same operations with partial RoPE fused in, and the batch-invariant
- * attention mode), csa_rope (partial RoPE on query or window rows).
+ * attention mode), csa_rope (partial RoPE on query or window rows), and
+ * lightning_index_pool / topk_select_pool (the hierarchical indexer).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -238,6 +239,41 @@ int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio,
 int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k,
                 const void* scores, int score_dtype, int32_t* idx,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lightning_index_pool / topk_select_pool -- the hierarchical sparse indexer.
+ *
+ * "DeepSeek 模型原理进化史" (CSA2: cross-layer KV and index reuse;
+ * hierarchical sparse indexer): a Full-indexer layer scans the whole context
+ * (lightning_index + topk_select with a large k = P) and yields a candidate
+ * pool per query; a later Reindex layer re-scores with its own query only the
+ * pool's entries and takes its Top-k inside the pool; Reuse layers pass an
+ * earlier layer's idx straight to sparse_mqa_attn (nothing to compute).
+ *
+ * lightning_index_pool:
+ *   scores[b,t,j] = sum_h w[b,t,h] * ReLU(q[b,t,h] . k[b, pool[b,t,j]])
+ * (the indexer equation of lightning_index, no scale), -inf where the slot is
+ * empty: pool[b,t,j] < 0 or >= N (such slots read no key).  Visibility is the
+ * pool's: a pool from topk_select holds visible entries only.
+ *  q [B, T, 64, 128] bf16;  w [B, T, 64] float32;  k [B, N, 128] bf16;
+ *  pool [B, T, P] int32;  scores [B, T, P] float32 or bf16 (score_dtype).
+ *  qk_dtype must be CSA_BF16.  0 <= P <= 65536.
+ *
+ * topk_select_pool: for each row, the k pool entries with the highest scores,
+ * equal scores to the earlier slot; a slot is written as its entry id
+ * pool[b,t,j], and as -1 when the slot is empty (-1 or >= N) or when the row
+ * has fewer than k slots.  When pool rows list entry ids in ascending order
+ * and then empty slots -- as topk_select writes them -- the earlier slot is
+ * the lower id (the tie rule of topk_select) and idx is ascending entry ids,
+ * then -1.  scores [B, T, P] (as lightning_index_pool writes them), pool
+ * [B, T, P], idx [B, T, k] int32.  0 <= P <= 16384, 1 <= k <= 2048.  No
+ * workspace.
+ */
+int lightning_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I,
+                         const void* q, const float* w, const void* k, int qk_dtype,
+                         const int32_t* pool, void* scores, int score_dtype, void* stream);
+int topk_select_pool(int64_t B, int64_t T, int64_t N, int64_t P, int k, const void* scores,
+                     int score_dtype, const int32_t* pool, int32_t* idx, void* stream);
 
 /*
  * sparse_mqa_attn -- stage 4, shared-KV MQA over Top-k entries + window.

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
-           "rope", "workspace_bytes", "library", "F32", "BF16", "FP8_E4M3", "MXFP4", "CsaError"]
+           "rope", "lightning_index_pool", "topk_select_pool", "workspace_bytes", "library", "F32", "BF16",
+           "FP8_E4M3", "MXFP4", "CsaError"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa.so")
@@ -35,6 +36,8 @@ _SIGS = {
     "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                         _int, _int, _vp, _i64, _int, _f32, _int, _vp, _sz, _vp],
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
+    "lightning_index_pool": [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp],
+    "topk_select_pool": [_i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp],
     "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
                         _vp, _int, _vp],
     "topk_select": [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
@@ -220,6 +223,32 @@ def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=
     st = library().topk_select(B, T, N, q_pos0, ratio, k, _ptr(scores), _dt(scores), _ptr(idx),
                                _ptr(ws), wsb, _stream(stream))
     _check(st, "topk_select")
+    return idx
+
+
+def lightning_index_pool(q, w, k, pool, *, score_dtype=torch.bfloat16, scores=None, stream=None):
+    """Hierarchical indexer, Reindex layer: scores of each query's candidate pool.
+    q: [B, T, 64, 128] bf16, w: [B, T, 64], k: [B, N, 128] bf16, pool: [B, T, P] int32
+    (-1 = empty); returns scores [B, T, P] (-inf at empty slots)."""
+    B, T, P = pool.shape
+    N = k.shape[1]
+    if scores is None:
+        scores = torch.empty(B, T, P, dtype=score_dtype, device=q.device)
+    st = library().lightning_index_pool(B, T, N, P, 64, 128, _ptr(q), _ptr(w), _ptr(k), _dt(q), _ptr(pool),
+                                        _ptr(scores), _dt(scores), _stream(stream))
+    _check(st, "lightning_index_pool")
+    return scores
+
+
+def topk_select_pool(scores, pool, k, *, N, idx=None, stream=None):
+    """Top-k inside the pool: returns idx [B, T, k] int32 of entry ids (ascending
+    when the pool is), -1 padded.  N: entries in the cache (slots >= N are empty)."""
+    B, T, P = pool.shape
+    if idx is None:
+        idx = torch.empty(B, T, k, dtype=torch.int32, device=pool.device)
+    st = library().topk_select_pool(B, T, N, P, k, _ptr(scores), _dt(scores), _ptr(pool), _ptr(idx),
+                                    _stream(stream))
+    _check(st, "topk_select_pool")
     return idx
 
 

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["capi.cpp", "compress.hip", "indexer.hip", "topk.hip", "attention.hip", "rope.hip"]
+SOURCES = ["capi.cpp", "compress.hip", "indexer.hip", "topk.hip", "attention.hip", "rope.hip", "pool.hip"]
 ARCH = "gfx950"
 
 

@@ -94,8 +94,28 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
                 int score_dtype, int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
   csa::Check ck = csa::check_topk(B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace, ws_bytes);
   if (!ck.ok()) return finish(ck);
-  csa::TopkArgs a{B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace};
+  csa::TopkArgs a{B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace, nullptr, 0};
   return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select launch");
+}
+
+int lightning_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I, const void* q,
+                         const float* w, const void* k, int qk_dtype, const int32_t* pool, void* scores,
+                         int score_dtype, void* stream) {
+  csa::Check ck = csa::check_index_pool(B, T, N, P, H_I, d_I, q, w, k, qk_dtype, pool, scores, score_dtype);
+  if (!ck.ok()) return finish(ck);
+  csa::IndexPoolArgs a{B, T, N, P, q, w, k, pool, scores, score_dtype};
+  return hip_status(csa::launch_index_pool(a, as_stream(stream)), "lightning_index_pool launch");
+}
+
+int topk_select_pool(int64_t B, int64_t T, int64_t N, int64_t P, int k, const void* scores, int score_dtype,
+                     const int32_t* pool, int32_t* idx, void* stream) {
+  csa::Check ck = csa::check_topk_pool(B, T, N, P, k, scores, score_dtype, pool, idx);
+  if (!ck.ok()) return finish(ck);
+  // every slot of a row is a candidate (ratio 1, positions past the row):
+  // the register / LDS selection over P slots, each selected slot written as
+  // its pool entry
+  csa::TopkArgs a{B, T, P, P, 1, k, scores, score_dtype, idx, nullptr, pool, N};
+  return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select_pool launch");
 }
 
 int sparse_mqa_attn_ex(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,

@@ -47,6 +47,18 @@ struct TopkArgs {
   int score_dtype;
   int32_t* idx;
   void* ws;
+  const int32_t* pool;   // pool mode: a selected slot j is written as pool[row][j] (-1 if outside 0..n_ent-1)
+  int64_t n_ent;
+};
+
+struct IndexPoolArgs {
+  int64_t B, T, N, P;
+  const void* q;         // [B, T, 64, 128] bf16
+  const float* w;        // [B, T, 64]
+  const void* k;         // [B, N, 128] bf16
+  const int32_t* pool;   // [B, T, P]
+  void* scores;          // [B, T, P]
+  int score_dtype;
 };
 
 struct AttnArgs {
@@ -85,6 +97,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s);
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 

@@ -165,17 +165,26 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 // Ordered compaction of one contiguous range [lo, hi) of a row: writes every
 // index whose key > K, and keys == K while the running equal-rank < rem, to
 // out[pos...] in ascending order.  `key(i)` reads the key of index i.
+// In pool mode (pool != NULL) the written value is the pool row's entry id
+// at the selected slot, -1 for an empty slot.
+__device__ __forceinline__ int32_t pool_map(const int32_t* prow, int64_t n_ent, int64_t i) {
+  if (!prow) return static_cast<int32_t>(i);
+  const int32_t v = prow[i];
+  return v >= 0 && v < n_ent ? v : -1;
+}
+
 template <typename KT, typename F>
 __device__ __forceinline__ void emit_range(int64_t lo, int64_t hi, KT K, uint32_t rem, uint32_t gt_before,
-                                           uint32_t eq_before, int32_t* out, F key) {
+                                           uint32_t eq_before, int32_t* out, F key,
+                                           const int32_t* prow = nullptr, int64_t n_ent = 0) {
   uint32_t pos = gt_before + (eq_before < rem ? eq_before : rem);
   uint32_t er = eq_before;
   for (int64_t i = lo; i < hi; ++i) {
     const KT kk = key(i);
     if (kk > K) {
-      out[pos++] = static_cast<int32_t>(i);
+      out[pos++] = pool_map(prow, n_ent, i);
     } else if (kk == K) {
-      if (er < rem) out[pos++] = static_cast<int32_t>(i);
+      if (er < rem) out[pos++] = pool_map(prow, n_ent, i);
       ++er;
     }
   }
@@ -185,7 +194,7 @@ __device__ __forceinline__ void emit_range(int64_t lo, int64_t hi, KT K, uint32_
 template <typename KT>
 __global__ void __launch_bounds__(1024)
 topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT* __restrict__ scores,
-                int32_t* __restrict__ idx) {
+                int32_t* __restrict__ idx, const int32_t* __restrict__ pool, int64_t n_ent) {
   extern __shared__ uint8_t smem_raw[];
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw);           // kRangeBins (>= kBins)
   uint32_t* tmp = hist + kRangeBins;                                  // 32 words
@@ -194,9 +203,10 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
   const int64_t t = row % T;
   const int64_t V = row_visible(t, q_pos0, ratio, N);
   int32_t* out = idx + row * k;
+  const int32_t* prow = pool ? pool + row * N : nullptr;
   const int tid = threadIdx.x, nt = blockDim.x;
   if (V <= k) {
-    for (int i = tid; i < k; i += nt) out[i] = i < V ? i : -1;
+    for (int i = tid; i < k; i += nt) out[i] = i < V ? pool_map(prow, n_ent, i) : -1;
     return;
   }
   if (tid == 0) {
@@ -312,7 +322,7 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
   uint32_t total;
   const uint32_t gtb = block_exclusive_scan(gt, tmp, &total);
   const uint32_t eqb = block_exclusive_scan(eq, tmp, &total);
-  emit_range<KT>(lo, hi, K, rem, gtb, eqb, out, [&](int64_t i) { return keys[i]; });
+  emit_range<KT>(lo, hi, K, rem, gtb, eqb, out, [&](int64_t i) { return keys[i]; }, prow, n_ent);
 }
 
 // ------------------------------------------------------------ register path
@@ -333,7 +343,7 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
 template <int CPT>
 __global__ void __launch_bounds__(1024)
 topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const uint16_t* __restrict__ scores,
-                int32_t* __restrict__ idx) {
+                int32_t* __restrict__ idx, const int32_t* __restrict__ pool, int64_t n_ent) {
   constexpr int NT = 1024;
   static_assert(8 * CPT * NT < 65536, "block-wide counts are packed in 16 bits");
   __shared__ uint32_t bins[kRangeBins];
@@ -342,9 +352,10 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
   const int64_t t = row % T;
   const int64_t V = row_visible(t, q_pos0, ratio, N);
   int32_t* out = idx + row * k;
+  const int32_t* prow = pool ? pool + row * N : nullptr;
   const int tid = threadIdx.x;
   if (V <= k) {
-    for (int i = tid; i < k; i += NT) out[i] = i < V ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = i < V ? pool_map(prow, n_ent, i) : -1;
     return;
   }
   for (int i = tid; i < kRangeBins; i += NT) bins[i] = 0;
@@ -495,7 +506,7 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
     }
   uint32_t pos = (ex & 0xffffu) + min(ex >> 16, rem);
   while (take) {
-    out[pos++] = static_cast<int32_t>(i00 + __builtin_ctzll(take));
+    out[pos++] = pool_map(prow, n_ent, i00 + __builtin_ctzll(take));
     take &= take - 1;
   }
 #undef KEY
@@ -873,11 +884,11 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
       const dim3 grid(static_cast<uint32_t>(rows));
       const auto* sc16 = static_cast<const uint16_t*>(a.scores);
       switch (cpt) {
-        case 1: hipLaunchKernelGGL(topk_reg_kernel<1>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
-        case 2: hipLaunchKernelGGL(topk_reg_kernel<2>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
-        case 3: hipLaunchKernelGGL(topk_reg_kernel<3>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
-        case 4: hipLaunchKernelGGL(topk_reg_kernel<4>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
-        default: hipLaunchKernelGGL(topk_reg_kernel<5>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx); break;
+        case 1: hipLaunchKernelGGL(topk_reg_kernel<1>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 2: hipLaunchKernelGGL(topk_reg_kernel<2>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 3: hipLaunchKernelGGL(topk_reg_kernel<3>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 4: hipLaunchKernelGGL(topk_reg_kernel<4>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        default: hipLaunchKernelGGL(topk_reg_kernel<5>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
       }
       return hipGetLastError();
     }
@@ -885,7 +896,7 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
   if (topk_row_in_lds(a.N, a.score_dtype)) {
     const size_t smem = (kRangeBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
     hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
-                       a.N, a.q_pos0, a.ratio, a.k, sc, a.idx);
+                       a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, a.pool, a.n_ent);
     return hipGetLastError();
   }
   if constexpr (sizeof(KT) == 2) {

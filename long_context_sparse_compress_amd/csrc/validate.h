@@ -213,6 +213,39 @@ inline Check check_topk(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int rat
   return k;
 }
 
+// Hierarchical indexer: pool scoring and Top-k inside the pool.
+constexpr int64_t kMaxPool = 65536;       // pool slots a query may score
+constexpr int64_t kMaxPoolTopk = 16384;   // pool slots Top-k selects from (one workgroup per row, no workspace)
+
+inline Check check_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I, const void* q,
+                              const float* w, const void* kk, int qk_dtype, const int32_t* pool, const void* scores,
+                              int score_dtype) {
+  Check k;
+  if (B < 0 || T < 0 || N < 0 || P < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T, N and P must be >= 0"); return k; }
+  if (P > kMaxPool) { k.fail(CSA_ERR_INVALID_ARG, "P must be at most 65536, got " + i2s(P)); return k; }
+  if (H_I != CSA_INDEX_HEADS || d_I != CSA_INDEX_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "indexer shape must be H_I=64, d_I=128"); return k; }
+  if (qk_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "lightning_index_pool takes bf16 q and keys"); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (B * T * ((P + 255) / 256) > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B * T * ceil(P / 256) must be below 2^31"); return k; }
+  const bool empty = (B == 0 || T == 0 || P == 0);
+  k.ptr(q, "q", !empty) && k.ptr(w, "w", !empty) && k.ptr(kk, "k", !empty && N > 0) && k.ptr(pool, "pool", !empty) &&
+      k.ptr(scores, "scores", !empty);
+  return k;
+}
+
+inline Check check_topk_pool(int64_t B, int64_t T, int64_t N, int64_t P, int kk, const void* scores, int score_dtype,
+                             const int32_t* pool, const void* idx) {
+  Check k;
+  if (B < 0 || T < 0 || N < 0 || P < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T, N and P must be >= 0"); return k; }
+  if (P > kMaxPoolTopk) { k.fail(CSA_ERR_INVALID_ARG, "P must be at most 16384, got " + i2s(P)); return k; }
+  if (kk < 1 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [1, 2048], got " + i2s(kk)); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (B * T > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B * T must be below 2^31"); return k; }
+  const bool empty = (B == 0 || T == 0);
+  k.ptr(scores, "scores", !empty && P > 0) && k.ptr(pool, "pool", !empty && P > 0) && k.ptr(idx, "idx", !empty);
+  return k;
+}
+
 inline bool check_attn_common(Check& k, int64_t B, int64_t T, int64_t q_pos0, int H, int d,
                                int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype) {
   if (B < 0 || T < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and T must be >= 0"); return false; }

@@ -31,7 +31,8 @@ def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
-                          "csa_workspace_bytes", "csa_last_error", "csa_version"}
+                          "lightning_index_pool", "topk_select_pool", "csa_workspace_bytes",
+                          "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "long_context_sparse_compress_amd", "libcsa.so")],
@@ -253,3 +254,33 @@ def test_validation_compiles_without_hip(tmp_path):
                         str(src), "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_pool_validation(lib):
+    """lightning_index_pool / topk_select_pool argument checks (host only)."""
+    ip, tp = lib.lightning_index_pool, lib.topk_select_pool
+
+    def idx_pool(B=2, T=1, N=64, P=128, H=64, d=128, dt=1, sd=1, q=A, w=A, k=A, pool=A, sc=A):
+        return ip(B, T, N, P, H, d, q, w, k, dt, pool, sc, sd, None)
+
+    assert idx_pool(H=32) == -2 and "H_I=64" in _err(lib)
+    assert idx_pool(dt=0) == -2 and "bf16" in _err(lib)
+    assert idx_pool(dt=2) == -2
+    assert idx_pool(sd=2) == -2
+    assert idx_pool(P=65537) == -1 and "P must" in _err(lib)
+    assert idx_pool(P=-1) == -1
+    assert idx_pool(pool=None) == -1 and "pool" in _err(lib)
+    assert idx_pool(k=MIS) == -1
+    assert idx_pool(N=0, k=None, B=0) == 0          # nothing to do
+    assert idx_pool(P=0, q=None, w=None, k=None, pool=None, sc=None) == 0
+
+    def top_pool(B=2, T=1, N=64, P=128, k=16, sd=1, sc=A, pool=A, idx=A):
+        return tp(B, T, N, P, k, sc, sd, pool, idx, None)
+
+    assert top_pool(P=16385) == -1 and "P must" in _err(lib)
+    assert top_pool(k=0) == -1 and "k must" in _err(lib)
+    assert top_pool(k=2049) == -1
+    assert top_pool(sd=3) == -2
+    assert top_pool(pool=None) == -1 and "pool" in _err(lib)
+    assert top_pool(idx=None) == -1
+    assert top_pool(B=0, sc=None, pool=None, idx=None) == 0
