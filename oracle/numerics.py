@@ -1,4 +1,5 @@
-"""Exact decoding of the quantized indexer inputs, and bf16 score storage.
+"""Exact decoding of the quantized indexer inputs, bf16 score storage, and the
+fp8 row quantizer of quantize-on-write.
 
 Test infrastructure only (see the package docstring).
 
@@ -88,3 +89,36 @@ def store_bf16(x: np.ndarray) -> np.ndarray:
     r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
     r = np.where(finite, r, f.view(np.uint32))
     return r.view(np.float32).astype(np.float64)
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """Values -> E4M3 byte codes: the nearest finite E4M3 value, ties to the
+    code with an even mantissa (round to nearest even), magnitudes past 448
+    to 448 (saturation); the sign is kept, so -0.0 -> 0x80.  A brute-force
+    search over the 126 finite non-negative codes."""
+    x = np.asarray(x, dtype=np.float64)
+    codes = np.arange(0x7F, dtype=np.uint8)               # 0x00 .. 0x7E: every finite non-negative code
+    vals = decode_e4m3(codes)
+    a = np.abs(x)[..., None]
+    d = np.abs(a - vals)
+    best = d.min(axis=-1, keepdims=True)
+    tie_ok = d == best
+    # among equally near codes take the one with an even mantissa (bit 0 clear)
+    even = (codes & 1) == 0
+    pick = np.where(tie_ok & even, 0, np.where(tie_ok, 1, 2))
+    idx = np.argmin(pick, axis=-1)
+    out = codes[idx]
+    return np.where(np.signbit(x), out | 0x80, out).astype(np.uint8)
+
+
+def quant_fp8_rows_f32(y: np.ndarray):
+    """Quantize-on-write of rows to fp8 ("DeepSeek-V4 技术报告解读" / "DeepSeek V4
+    结构速览": the indexer keys are kept in low precision): per row of the last
+    axis, scale = amax / 448 and code = E4M3(y / scale), every step in fp32
+    (the precision the writing kernel decides in); an all-zero row gets scale
+    1.  Returns (codes uint8 like y, scale float32 like y.shape[:-1])."""
+    y = np.asarray(y, dtype=np.float32)
+    amax = np.abs(y).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (y / scale[..., None]).astype(np.float32)
+    return encode_e4m3(v), scale

@@ -1,0 +1,52 @@
+"""Pins of the fp8 quantize-on-write oracle (E4M3 encoder and the per-row
+quantizer).
+
+The encoder is a brute-force nearest-code search; it is pinned against the
+OCP E4M3 code table (every finite code encodes to itself), hand-picked
+midpoints (ties to the even mantissa), saturation, and torch's own
+float8_e4m3fn conversion on random in-range values.
+"""
+import numpy as np
+import torch
+
+from oracle import numerics as on
+
+
+def test_every_finite_code_round_trips():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(on.encode_e4m3(on.decode_e4m3(codes)), codes)
+
+
+def test_midpoints_tie_to_even_and_saturation():
+    # 1.0625 lies halfway between 1.0 (0x38, mantissa 0) and 1.125 (0x39): -> 1.0
+    assert on.encode_e4m3(np.array([1.0625]))[0] == 0x38
+    # 1.1875 lies halfway between 1.125 (0x39) and 1.25 (0x3A, even): -> 1.25
+    assert on.encode_e4m3(np.array([1.1875]))[0] == 0x3A
+    # the largest subnormal step: 2^-9 * 0.5 -> 0 (even), 2^-9 * 1.5 -> 2 * 2^-9 (even)
+    assert on.encode_e4m3(np.array([2.0 ** -10]))[0] == 0x00
+    assert on.encode_e4m3(np.array([1.5 * 2.0 ** -9]))[0] == 0x02
+    # past the largest finite value: saturate to 448, keep the sign
+    assert list(on.encode_e4m3(np.array([460.0, 464.0, 1e6, -1e6]))) == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert on.encode_e4m3(np.array([-0.0]))[0] == 0x80
+
+
+def test_matches_torch_float8_e4m3fn_in_range():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.normal(size=4000) * 30, g.normal(size=2000) * 0.01, g.uniform(-448, 448, 2000)])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(on.encode_e4m3(x), ref)
+
+
+def test_row_quantizer_bounds():
+    g = np.random.default_rng(1)
+    y = (g.normal(size=(50, 128)) * np.exp(g.normal(size=(50, 1)))).astype(np.float32)
+    y[3] = 0.0
+    codes, scale = on.quant_fp8_rows_f32(y)
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+    back = on.decode_e4m3(codes) * scale[:, None]
+    # each row's largest magnitude maps to 448 (up to the fp32 division), and
+    # every element is within half an E4M3 step of its value
+    assert np.all(np.abs(on.decode_e4m3(codes)).max(axis=1)[np.arange(50) != 3] == 448.0)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(y / scale[:, None]), 2.0 ** -6))) - 3)
+    assert np.all(np.abs(back - y) <= 0.5 * step * scale[:, None] * (1 + 1e-6) + 1e-30)
