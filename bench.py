@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--batch-invariant", action="store_true",
                    help="attention in batch-invariant mode (no row split; default workload only)")
+    p.add_argument("--fp8-keys", action="store_true",
+                   help="index keys quantized on write to fp8 E4M3 (in the latent's compressor launch) and the "
+                        "fp8 indexer (default workload only)")
     p.add_argument("--rope", type=int, default=0,
                    help="partial RoPE dims fused into the compressors and the attention epilogues "
                         "(default workload only; 0 = none)")
@@ -71,10 +74,12 @@ def parse():
 class DecodeStep:
     """One CSA layer + one HCA layer decode step for B sequences at `ctx` context."""
 
-    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False, rope=0):
+    def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False, rope=0,
+                 fp8_keys=False):
         self.csa, self.torch = csa, torch
         self.bi = batch_invariant
         self.rope = rope
+        self.fp8 = fp8_keys
         bf = torch.bfloat16
         dn = synth.device_normal
         self.B, self.ctx, self.k = B, ctx, k
@@ -98,6 +103,11 @@ class DecodeStep:
         self.q = dn("b.q", (B, 1, 64, 512), bf)
         self.qh = dn("b.qh", (B, 1, 64, 512), bf)
         self.qi = dn("b.qi", (B, 1, 64, 128), bf, var=1.0 / 128)
+        if fp8_keys:
+            # the key caches as fp8 codes + row scales (input preparation of the
+            # resident cache; the step itself writes its new key quantized)
+            self.keys, self.kscale = zip(*[_quant_fp8(torch, kk) for kk in self.keys])
+            self.qi8, self.qscale = _quant_fp8(torch, self.qi)
         self.w = synth.device_uniform("b.w", (B, 1, 64))
         self.sink = dn("b.sink", (64,))
         # outputs and workspaces
@@ -118,17 +128,28 @@ class DecodeStep:
     def stages(self, r):
         csa, c4, c4k, c128 = self.csa, self.c4, self.c4k, self.c128
         pos4 = self.ctx - 4
-        return [
-            # the block's 512-d latent and its 128-d indexer key, one launch
-            ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
-                dict(ratio=4, Ca=c4["Ca"], Za=c4["Za"], bias=self.b4, Cb=c4["Cb"], Zb=c4["Zb"], prev_Cb=c4["pCb"],
-                     prev_Zb=c4["pZb"], pos0=pos4, out=self.kv[r], cache_entry0=self.N4 - 1, rope_dims=self.rope),
-                dict(ratio=4, Ca=c4k["Ca"], Za=c4k["Za"], bias=self.b4k, Cb=c4k["Cb"], Zb=c4k["Zb"],
-                     prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1,
-                     rope_dims=self.rope),
-            ])),
-            ("lightning_index", lambda: csa.lightning_index(
-                self.qi, self.w, self.keys[r], q_pos0=self.t, scores=self.scores)),
+        kv_job = dict(ratio=4, Ca=c4["Ca"], Za=c4["Za"], bias=self.b4, Cb=c4["Cb"], Zb=c4["Zb"], prev_Cb=c4["pCb"],
+                      prev_Zb=c4["pZb"], pos0=pos4, out=self.kv[r], cache_entry0=self.N4 - 1, rope_dims=self.rope)
+        key_job = dict(ratio=4, Ca=c4k["Ca"], Za=c4k["Za"], bias=self.b4k, Cb=c4k["Cb"], Zb=c4k["Zb"],
+                       prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1,
+                       rope_dims=self.rope)
+        if self.fp8:
+            key_job["out_scale"] = self.kscale[r]
+            head = [
+                # the 512-d latent in bf16 and the key quantized on write, one launch
+                ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([kv_job, key_job])),
+                ("lightning_index", lambda: csa.lightning_index(
+                    self.qi8, self.w, self.keys[r], q_pos0=self.t, qk_dtype=csa.FP8_E4M3, q_scale=self.qscale,
+                    k_scale=self.kscale[r], scores=self.scores)),
+            ]
+        else:
+            head = [
+                # the block's 512-d latent and its 128-d indexer key, one launch
+                ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([kv_job, key_job])),
+                ("lightning_index", lambda: csa.lightning_index(
+                    self.qi, self.w, self.keys[r], q_pos0=self.t, scores=self.scores)),
+            ]
+        return head + [
             ("topk_select", lambda: csa.topk_select(
                 self.scores, self.k, q_pos0=self.t, idx=self.idx, workspace=self.ws_topk)),
             ("sparse_mqa_attn", lambda: csa.sparse_mqa_attn(
@@ -148,11 +169,22 @@ class DecodeStep:
         """Algorithmic bytes / flops of each stage for one launch (unique bytes only)."""
         B, N4, k = self.B, self.N4, self.k
         rows = k + 128
+        if self.fp8:
+            head = {
+                "compress_c4a_kv_keys": dict(bytes=B * 24 * (512 + 128) * 2 + B * (512 * 2 + 128 + 4)
+                                             + 8 * (512 + 128) * 4, flops=0),
+                "lightning_index": dict(bytes=B * N4 * 132 + B * 64 * 132 + B * 64 * 4 + B * N4 * 2,
+                                        flops=B * N4 * 64 * 128 * 2),
+            }
+        else:
+            head = {
+                "compress_c4a_kv_keys": dict(bytes=B * (4 * 4 + 4 * 2) * (512 + 128) * 2 + B * (512 + 128) * 2
+                                             + 8 * (512 + 128) * 4, flops=0),
+                "lightning_index": dict(bytes=B * N4 * 128 * 2 + B * 64 * 128 * 2 + B * 64 * 4 + B * N4 * 2,
+                                        flops=B * N4 * 64 * 128 * 2),
+            }
         return {
-            "compress_c4a_kv_keys": dict(bytes=B * (4 * 4 + 4 * 2) * (512 + 128) * 2 + B * (512 + 128) * 2
-                                         + 8 * (512 + 128) * 4, flops=0),
-            "lightning_index": dict(bytes=B * N4 * 128 * 2 + B * 64 * 128 * 2 + B * 64 * 4 + B * N4 * 2,
-                                    flops=B * N4 * 64 * 128 * 2),
+            **head,
             "topk_select": dict(bytes=B * N4 * 2 + B * k * 4, flops=0),
             "sparse_mqa_attn": dict(bytes=B * (rows * 1024 + k * 4 + 2 * 64 * 512 * 2),
                                     flops=B * rows * 64 * 512 * 4),
@@ -160,6 +192,15 @@ class DecodeStep:
             "hca_attn": dict(bytes=B * ((self.N128 + 128) * 1024 + 2 * 64 * 512 * 2),
                              flops=B * (self.N128 + 128) * 64 * 512 * 4),
         }
+
+
+def _quant_fp8(torch, x):
+    """Per-row E4M3 codes and fp32 scales (amax / 448) of a resident tensor, on
+    the device (input preparation)."""
+    amax = x.float().abs().amax(dim=-1).clamp_min(1e-30)
+    scale = (amax / 448.0).contiguous()
+    codes = (x.float() / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, scale
 
 
 def cpu_oracle_decode(step, torch, budget_s):
@@ -334,7 +375,7 @@ def main():
         return
 
     step = DecodeStep(csa, synth, torch, rotate=args.rotate, batch_invariant=args.batch_invariant,
-                      rope=args.rope)
+                      rope=args.rope, fp8_keys=args.fp8_keys)
     ms, wall = time_graph(torch, step, args.steps, args.warmup, args.rotate, args.eager)
     per_stage = time_stages(torch, step, args.steps, args.rotate)
     alg = step.algorithmic()
@@ -367,15 +408,15 @@ def main():
                    "index_dim": 128, "cache_copies_rotated": args.rotate,
                    "timing": "eager" if args.eager else "hip_graph",
                    "attention": "batch_invariant" if args.batch_invariant else "split_kv",
-                   "rope_dims": args.rope},
+                   "rope_dims": args.rope, "index_keys": "fp8_e4m3" if args.fp8_keys else "bf16"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": index_traffic(),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.fp8_keys else index_traffic(),
                      "algorithmic_bytes_per_launch": alg[dom]["bytes"], "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "stages": stages,
         "wall_s_timed": round(wall, 3),
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not args.fp8_keys:
         rec["cpu_baseline"] = cpu_oracle_decode(step, torch, args.cpu_seconds)
     print(json.dumps(rec))
 

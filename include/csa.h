@@ -154,16 +154,27 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
  * pos0 + ratio*i + rope_anchor.  The pages name the anchor position but its
  * symbol is lost in the text; the caller picks the offset inside the block,
  * 0 <= rope_anchor < ratio (0: the block's first raw token).  The row-split
- * C128A path (workspace given) applies it in its merge step.  Other
- * arguments, rules and errors are those of csa_compress; csa_compress is this
- * call with rope_dims 0.
+ * C128A path (workspace given) applies it in its merge step.
+ *
+ * Quantize-on-write: out_dtype CSA_FP8_E4M3 (C4A only -- the indexer keys,
+ * which "DeepSeek V4 结构速览" (Lightning Indexer) keeps in low precision)
+ * writes each entry as E4M3 codes (OCP, round to nearest even, saturating)
+ * of out / scale with scale = amax / 448 over the entry's channels (after
+ * RMSNorm and RoPE; 1 for an all-zero entry), each step in fp32, and the
+ * scale to out_scale: entry i of sequence b at out_scale[b * S + i] with S =
+ * out_batch_stride / c (out_batch_stride a multiple of c), or n_tok/ratio
+ * when out_batch_stride is 0 -- the byte codes and per-row scales
+ * lightning_index reads as CSA_FP8_E4M3 keys.  out_scale is 4-byte aligned;
+ * NULL for other output types.  Other arguments, rules and errors are those
+ * of csa_compress; csa_compress is this call with out_scale NULL and
+ * rope_dims 0.
  */
 int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                     const void* Ca, const void* Za, const void* Cb, const void* Zb,
                     const void* prev_Cb, const void* prev_Zb,
                     const float* bias, const float* gamma, float eps,
                     int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
-                    int rope_dims, float rope_base, int rope_anchor,
+                    float* out_scale, int rope_dims, float rope_base, int rope_anchor,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -174,7 +185,10 @@ int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0
  * 128-d indexer keys both go through a C4A compressor).  Each job carries
  * exactly the arguments of csa_compress_ex (without workspace and stream) and
  * obeys the same rules; jobs of one batch must share ratio, in_dtype and
- * out_dtype.  1 <= n_jobs <= 4.  Jobs with nothing to write are skipped.
+ * out_dtype, except that CSA_FP8_E4M3 jobs (quantize-on-write, C4A) may sit
+ * beside jobs of one other output type -- the CSA layer's bf16 latent and its
+ * fp8 indexer key in one launch.  1 <= n_jobs <= 4.  Jobs with nothing to
+ * write are skipped.
  * The row split that csa_compress's workspace enables is not used here.
  * Errors name the first offending job.
  */
@@ -191,6 +205,7 @@ typedef struct csa_compress_job {
   int rope_dims;      /* csa_compress_ex's partial RoPE; 0 for none */
   float rope_base;
   int rope_anchor;
+  float* out_scale;   /* csa_compress_ex's fp8 scales; NULL unless out_dtype is CSA_FP8_E4M3 */
 } csa_compress_job;
 
 int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);

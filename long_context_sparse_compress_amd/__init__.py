@@ -34,7 +34,7 @@ _SIGS = {
     "csa_compress": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                      _int, _int, _vp, _i64, _vp, _sz, _vp],
     "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
-                        _int, _int, _vp, _i64, _int, _f32, _int, _vp, _sz, _vp],
+                        _int, _int, _vp, _i64, _vp, _int, _f32, _int, _vp, _sz, _vp],
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
     "lightning_index_pool": [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp],
     "topk_select_pool": [_i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp],
@@ -130,7 +130,29 @@ class _CompressJob(ctypes.Structure):
                 ("Ca", _vp), ("Za", _vp), ("Cb", _vp), ("Zb", _vp), ("prev_Cb", _vp), ("prev_Zb", _vp),
                 ("bias", _vp), ("gamma", _vp), ("eps", _f32), ("in_dtype", _int), ("out_dtype", _int),
                 ("out", _vp), ("out_batch_stride", _i64), ("rope_dims", _int), ("rope_base", _f32),
-                ("rope_anchor", _int)]
+                ("rope_anchor", _int), ("out_scale", _vp)]
+
+
+def _out_dt(t: torch.Tensor) -> int:
+    """Compressor output type: uint8 tensors hold fp8 E4M3 codes (quantize-on-write)."""
+    return FP8_E4M3 if t.dtype == torch.uint8 else _dt(t)
+
+
+def _compress_scale(out, out_scale, cache_entry0, n_ent):
+    """fp8 output: the per-entry scale tensor ([B, n_ent] or the cache's [B, N_cache])
+    and the address of the first entry's scale."""
+    if out.dtype != torch.uint8:
+        if out_scale is not None:
+            raise ValueError("out_scale is only for fp8 (uint8) output")
+        return None, None
+    B = out.shape[0]
+    if out_scale is None:
+        if cache_entry0 is not None:
+            raise ValueError("writing fp8 entries into a cache needs the cache's out_scale [B, N_cache]")
+        out_scale = torch.empty(B, n_ent, dtype=torch.float32, device=out.device)
+    if out_scale.dtype != torch.float32 or not out_scale.is_contiguous():
+        raise ValueError("out_scale must be a contiguous float32 tensor")
+    return out_scale, out_scale.data_ptr() + (cache_entry0 or 0) * 4
 
 
 def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
@@ -162,12 +184,14 @@ def csa_compress_batch(jobs, stream=None):
         Ca = d["Ca"]
         B, n_tok, c = Ca.shape
         out, optr, stride = _compress_out(Ca, d["ratio"], d.get("out"), d.get("out_dtype"), d.get("cache_entry0"))
-        outs.append(out)
+        sc, sptr = _compress_scale(out, d.get("out_scale"), d.get("cache_entry0"), n_tok // d["ratio"])
+        outs.append(out if sc is None else (out, sc))
         j.ratio, j.B, j.n_tok, j.c, j.pos0 = d["ratio"], B, n_tok, c, d.get("pos0", 0)
         j.Ca, j.Za, j.Cb, j.Zb = _ptr(Ca), _ptr(d["Za"]), _ptr(d.get("Cb")), _ptr(d.get("Zb"))
         j.prev_Cb, j.prev_Zb = _ptr(d.get("prev_Cb")), _ptr(d.get("prev_Zb"))
         j.bias, j.gamma, j.eps = _ptr(d["bias"]), _ptr(d.get("gamma")), d.get("eps", 1e-6)
-        j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _dt(out), optr, stride
+        j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _out_dt(out), optr, stride
+        j.out_scale = sptr
         j.rope_dims, j.rope_base, j.rope_anchor = (d.get("rope_dims", 0), d.get("rope_base", ROPE_BASE),
                                                    d.get("rope_anchor", 0))
     st = library().csa_compress_batch(arr, len(jobs), _stream(stream))
@@ -177,7 +201,7 @@ def csa_compress_batch(jobs, stream=None):
 
 def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None, *, pos0=0,
                  gamma=None, eps=1e-6, out=None, out_dtype=None, cache_entry0=None, workspace=None,
-                 rope_dims=0, rope_base=ROPE_BASE, rope_anchor=0, stream=None):
+                 rope_dims=0, rope_base=ROPE_BASE, rope_anchor=0, out_scale=None, stream=None):
     """Stage 1.  Ca, Za (Cb, Zb): [B, n_tok, c]; returns out [B, n_tok//ratio, c].
 
     With ``cache_entry0`` set, ``out`` is a [B, N_cache, c] cache and the new
@@ -185,17 +209,21 @@ def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=No
     n_tok//ratio - 1 of every sequence.  ``workspace`` defaults to a fresh
     buffer of the size that enables the row split; an empty tensor disables it.
     ``rope_dims`` > 0: partial RoPE on each entry's last rope_dims channels at
-    position pos0 + ratio*i + rope_anchor (csa_compress_ex)."""
+    position pos0 + ratio*i + rope_anchor (csa_compress_ex).  ``out_dtype=torch.uint8``
+    (or a uint8 ``out``) quantizes on write to fp8 E4M3 codes with one fp32 scale
+    per entry (into ``out_scale``, the cache's [B, N_cache] with ``cache_entry0``);
+    then (codes, scales) is returned."""
     B, n_tok, c = Ca.shape
     in_dt = _dt(Ca)
     out, optr, stride = _compress_out(Ca, ratio, out, out_dtype, cache_entry0)
+    sc, sptr = _compress_scale(out, out_scale, cache_entry0, n_tok // ratio)
     ws, wsb = _workspace(OP_COMPRESS, B, n_tok, c, ratio, Ca.device, workspace)
     st = library().csa_compress_ex(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
                                    _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
-                                   _dt(out), optr, stride, rope_dims, rope_base, rope_anchor, _ptr(ws), wsb,
-                                   _stream(stream))
+                                   _out_dt(out), optr, stride, sptr, rope_dims, rope_base, rope_anchor, _ptr(ws),
+                                   wsb, _stream(stream))
     _check(st, "csa_compress")
-    return out
+    return out if sc is None else (out, sc)
 
 
 def lightning_index(q, w, k, *, q_pos0, ratio=4, qk_dtype=None, q_scale=None, k_scale=None,

@@ -35,15 +35,15 @@ extern "C" {
 int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
                     const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
                     const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
-                    int out_dtype, void* out, int64_t out_batch_stride, int rope_dims, float rope_base,
-                    int rope_anchor, void* workspace, size_t ws_bytes, void* stream) {
+                    int out_dtype, void* out, int64_t out_batch_stride, float* out_scale, int rope_dims,
+                    float rope_base, int rope_anchor, void* workspace, size_t ws_bytes, void* stream) {
   csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
                                       gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes,
-                                      rope_dims, rope_base, rope_anchor);
+                                      rope_dims, rope_base, rope_anchor, out_scale);
   if (!ck.ok()) return finish(ck);
   csa::CompressArgs a{ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb,
                       bias, gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes,
-                      rope_dims, rope_base, rope_anchor};
+                      rope_dims, rope_base, rope_anchor, out_scale};
   return hip_status(csa::launch_compress(a, as_stream(stream)), "csa_compress launch");
 }
 
@@ -53,7 +53,7 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, c
                  int out_dtype, void* out, int64_t out_batch_stride, void* workspace, size_t ws_bytes,
                  void* stream) {
   return csa_compress_ex(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,
-                         out_dtype, out, out_batch_stride, 0, 0.f, 0, workspace, ws_bytes, stream);
+                         out_dtype, out, out_batch_stride, nullptr, 0, 0.f, 0, workspace, ws_bytes, stream);
 }
 
 int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
@@ -66,16 +66,23 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
     const csa_compress_job& j = jobs[q];
     csa::Check cj = csa::check_compress(j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb,
                                         j.prev_Zb, j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out,
-                                        j.out_batch_stride, nullptr, 0, j.rope_dims, j.rope_base, j.rope_anchor);
-    if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || j.out_dtype != jobs[0].out_dtype))
-      cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype");
+                                        j.out_batch_stride, nullptr, 0, j.rope_dims, j.rope_base, j.rope_anchor,
+                                        j.out_scale);
+    // fp8 jobs (quantize-on-write, C4A) may sit beside jobs of one float output type
+    bool same_out = true;
+    for (int p = 0; p < q; ++p)
+      if (jobs[p].out_dtype != j.out_dtype && jobs[p].out_dtype != CSA_FP8_E4M3 && j.out_dtype != CSA_FP8_E4M3)
+        same_out = false;
+    if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || !same_out))
+      cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype (fp8 jobs may join "
+                                   "jobs of one other output type)");
     if (!cj.ok()) {
       cj.msg = "job " + csa::i2s(q) + ": " + cj.msg;
       return finish(cj);
     }
     a[q] = csa::CompressArgs{j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb,
                              j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out, j.out_batch_stride, nullptr, 0,
-                             j.rope_dims, j.rope_base, j.rope_anchor};
+                             j.rope_dims, j.rope_base, j.rope_anchor, j.out_scale};
   }
   return hip_status(csa::launch_compress_batch(a, n_jobs, as_stream(stream)), "csa_compress_batch launch");
 }

@@ -116,7 +116,8 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                const float* __restrict__ bias, const float* __restrict__ gamma,
                                                float eps, TO* __restrict__ out, int64_t out_stride, int G,
                                                float* __restrict__ part, int rope_R, double rope_l2b,
-                                               int rope_anchor) {
+                                               int rope_anchor, float* __restrict__ out_scale,
+                                               int64_t scale_stride) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   constexpr int UC = kChunkRows;
@@ -290,6 +291,48 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < nw; ++w) tot += red[w];
+  if constexpr (sizeof(TO) == 1) {
+    // Quantize-on-write: E4M3 codes with one fp32 scale per entry, amax / 448
+    // over the entry's normalised (and rotated) channels -- a second block
+    // reduction, which every thread joins -- and each code from the fp32
+    // quotient o / scale.
+    float o[VEC];
+    float am = 0.f;
+    if (g == 0) {
+      const float inv = rsqrtf(tot / static_cast<float>(c) + eps);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * gm[v];
+      if (__builtin_expect(rope_R > 0, 0) && ch0 + VEC > c - rope_R) {
+#pragma unroll
+        for (int v = 0; v < VEC; v += 2) {
+          if (ch0 + v >= c - rope_R) {
+            const float2 k = rope_tab[(ch0 + v - (c - rope_R)) / 2];
+            rope_pair(o[v], o[v + 1], k.x, k.y);
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(o[v]));
+    }
+    am = wave_max(am);
+    float* red_max = smem + 32;   // red holds at most 16 wave sums
+    if ((tid & 63) == 0) red_max[wid] = am;
+    __syncthreads();
+    float amax = 0.f;
+    for (int w = 0; w < nw; ++w) amax = fmaxf(amax, red_max[w]);
+    if (g != 0) return;
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    uint32_t word[VEC / 4];
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4)
+      word[v / 4] = f32_to_e4m3(o[v] / scale) | (f32_to_e4m3(o[v + 1] / scale) << 8) |
+                    (f32_to_e4m3(o[v + 2] / scale) << 16) | (f32_to_e4m3(o[v + 3] / scale) << 24);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(out + b * out_stride + i * c + ch0);
+    if constexpr (VEC == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
+    else *reinterpret_cast<uint32_t*>(dst) = word[0];
+    if (ct == 0) out_scale[b * scale_stride + i] = scale;
+    return;
+  }
   if (g != 0) return;
   const float inv = rsqrtf(tot / static_cast<float>(c) + eps);
   float o[VEC];
@@ -309,18 +352,23 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
   store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
 }
 
+// C4A workgroups hold at most 512 threads (c / 4 channel threads x 2 row
+// groups), C128A ones up to 1024; the bound sets the register budget.
+template <int RATIO> constexpr int kCompressThreads = RATIO == 4 ? 512 : 1024;
+
 template <typename TI, typename TO, int RATIO, bool SPLIT>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ Ca, const TI* __restrict__ Za,
                 const TI* __restrict__ Cb, const TI* __restrict__ Zb,
                 const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                 const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
                 TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part, int rope_R,
-                double rope_l2b, int rope_anchor) {
+                double rope_l2b, int rope_anchor, float* __restrict__ out_scale, int64_t scale_stride) {
   compress_entry<TI, TO, RATIO, SPLIT>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
                                        static_cast<int>(gridDim.z), n_tok, c, pos0, Ca, Za, Cb, Zb, pCb, pZb, bias,
-                                       gamma, eps, out, out_stride, G, part, rope_R, rope_l2b, rope_anchor);
+                                       gamma, eps, out, out_stride, G, part, rope_R, rope_l2b, rope_anchor,
+                                       out_scale, scale_stride);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -336,23 +384,38 @@ struct CompressJobDev {
   int rope_R;
   double rope_l2b;
   int rope_anchor;
+  float* out_scale;       // fp8 output: one scale per entry
+  int64_t scale_stride;
 };
 constexpr int kMaxBatchJobs = 4;
 struct CompressBatch {
   CompressJobDev j[kMaxBatchJobs];
 };
 
-template <typename TI, typename TO, int RATIO>
-__global__ void __launch_bounds__(1024)
+// MIXED: some jobs write fp8 codes (quantize-on-write; their out_scale is
+// set) and the others TO -- the CSA layer's bf16 latent and fp8 indexer keys
+// in one launch.  The choice is per workgroup (one job each).
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
+__global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_batch_kernel(CompressBatch jb) {
   const CompressJobDev& J = jb.j[blockIdx.z];
   if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
+  if (MIXED && J.out_scale) {
+    compress_entry<TI, uint8_t, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+                                              static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
+                                              static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
+                                              static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias,
+                                              J.gamma, J.eps, static_cast<uint8_t*>(J.out), J.out_stride, J.G,
+                                              nullptr, J.rope_R, J.rope_l2b, J.rope_anchor, J.out_scale,
+                                              J.scale_stride);
+    return;
+  }
   compress_entry<TI, TO, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
                                        static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                        static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
                                        static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias, J.gamma,
                                        J.eps, static_cast<TO*>(J.out), J.out_stride, J.G, nullptr, J.rope_R,
-                                       J.rope_l2b, J.rope_anchor);
+                                       J.rope_l2b, J.rope_anchor, J.out_scale, J.scale_stride);
 }
 
 // Merge of the row-range states of one (entry, sequence), then RMSNorm.  One
@@ -443,7 +506,7 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
       const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), static_cast<uint32_t>(P));
       hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, true>), grid, dim3(threads), smem, s, a.n_tok,
                          static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
-                         static_cast<TO*>(a.out), stride, G, part, 0, 0.0, 0);
+                         static_cast<TO*>(a.out), stride, G, part, 0, 0.0, 0, nullptr, 0);
       hipLaunchKernelGGL((compress_merge_kernel<TO>), dim3(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B)),
                          dim3(static_cast<uint32_t>(a.c)), 0, s, n_ent, static_cast<int>(a.c), P, part, a.gamma,
                          a.eps, static_cast<TO*>(a.out), stride, a.pos0, RATIO, a.rope_dims, rope_log2_base(a),
@@ -454,11 +517,12 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), 1);
   hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, false>), grid, dim3(threads), smem, s, a.n_tok,
                      static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
-                     static_cast<TO*>(a.out), stride, G, nullptr, a.rope_dims, rope_log2_base(a), a.rope_anchor);
+                     static_cast<TO*>(a.out), stride, G, nullptr, a.rope_dims, rope_log2_base(a), a.rope_anchor,
+                     a.out_scale, stride / a.c);
   return hipGetLastError();
 }
 
-template <typename TI, typename TO, int RATIO>
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
 hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
@@ -480,9 +544,10 @@ hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
     gy = a.B > gy ? a.B : gy;
     jb.j[q] = CompressJobDev{a.Ca, a.Za, a.Cb, a.Zb, a.prev_Cb, a.prev_Zb, a.bias, a.gamma, a.out, a.n_tok, a.pos0,
                              a.out_batch_stride ? a.out_batch_stride : n_ent * a.c, n_ent, a.B, a.eps,
-                             static_cast<int>(a.c), G, a.rope_dims, rope_log2_base(a), a.rope_anchor};
+                             static_cast<int>(a.c), G, a.rope_dims, rope_log2_base(a), a.rope_anchor, a.out_scale,
+                             (a.out_batch_stride ? a.out_batch_stride : n_ent * a.c) / a.c};
   }
-  hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO>),
+  hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO, MIXED>),
                      dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
                      dim3(static_cast<uint32_t>(threads)), smem + 64 * sizeof(float), s, jb);
   return hipGetLastError();
@@ -502,6 +567,8 @@ hipError_t launch_r(const CompressArgs& a, hipStream_t s) {
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.B == 0 || a.n_tok / a.ratio == 0) return hipSuccess;
+  if (a.out_dtype == CSA_FP8_E4M3)   // C4A only (validated): the indexer keys
+    return a.in_dtype == CSA_F32 ? launch_t<float, uint8_t, 4>(a, s) : launch_t<uint16_t, uint8_t, 4>(a, s);
   if (a.in_dtype == CSA_F32)
     return a.out_dtype == CSA_F32 ? launch_r<float, float>(a, s) : launch_r<float, uint16_t>(a, s);
   return a.out_dtype == CSA_F32 ? launch_r<uint16_t, float>(a, s) : launch_r<uint16_t, uint16_t>(a, s);
@@ -514,11 +581,29 @@ hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s)
   for (int q = 0; q < n; ++q)
     if (jobs[q].B > 0 && jobs[q].n_tok / jobs[q].ratio > 0) live[m++] = jobs[q];
   if (m == 0) return hipSuccess;
+  // the output type of the jobs that do not write fp8 (all fp8: none)
+  int odt = CSA_FP8_E4M3;
+  for (int q = 0; q < m; ++q)
+    if (live[q].out_dtype != CSA_FP8_E4M3) odt = live[q].out_dtype;
+  const bool any_fp8 = [&] {
+    for (int q = 0; q < m; ++q)
+      if (live[q].out_dtype == CSA_FP8_E4M3) return true;
+    return false;
+  }();
   const CompressArgs& a = live[0];
+  if (odt == CSA_FP8_E4M3)
+    return a.in_dtype == CSA_F32 ? launch_batch_t<float, uint8_t, 4>(live, m, s)
+                                 : launch_batch_t<uint16_t, uint8_t, 4>(live, m, s);
+  if (any_fp8) {   // C4A (validated): float outputs with fp8 ones
+    if (a.in_dtype == CSA_F32)
+      return odt == CSA_F32 ? launch_batch_t<float, float, 4, true>(live, m, s)
+                            : launch_batch_t<float, uint16_t, 4, true>(live, m, s);
+    return odt == CSA_F32 ? launch_batch_t<uint16_t, float, 4, true>(live, m, s)
+                          : launch_batch_t<uint16_t, uint16_t, 4, true>(live, m, s);
+  }
   if (a.in_dtype == CSA_F32)
-    return a.out_dtype == CSA_F32 ? launch_batch_r<float, float>(live, m, s) : launch_batch_r<float, uint16_t>(live, m, s);
-  return a.out_dtype == CSA_F32 ? launch_batch_r<uint16_t, float>(live, m, s)
-                                : launch_batch_r<uint16_t, uint16_t>(live, m, s);
+    return odt == CSA_F32 ? launch_batch_r<float, float>(live, m, s) : launch_batch_r<float, uint16_t>(live, m, s);
+  return odt == CSA_F32 ? launch_batch_r<uint16_t, float>(live, m, s) : launch_batch_r<uint16_t, uint16_t>(live, m, s);
 }
 
 }  // namespace csa

@@ -96,6 +96,28 @@ __device__ __forceinline__ void rope_pair(float& x, float& y, float c, float s) 
   y = ny;
 }
 
+// fp32 -> OCP E4M3 byte code: round to nearest even, magnitudes from 464 (the
+// midpoint past the largest finite value, 448) up saturate to 448, the sign
+// is kept.  Normal results round the float's mantissa to 3 bits on its bit
+// pattern (a carry moves into the exponent, which is then rebiased from 127
+// to 7); results below 2^-6 are subnormal multiples of 2^-9, rounded with
+// rint (the scaling by 2^9 is exact).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43e80000u) {                 // |v| >= 464 (or not finite)
+    code = 0x7eu;
+  } else if (a >= 0x3c800000u) {          // |v| >= 2^-6: normal
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+  } else {
+    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.f));
+  }
+  return sign | code;
+}
+
 // Round-robin workgroup dispatch puts consecutive workgroup ids on different
 // XCDs (8 on MI355X).  Remap a linear id so that ids [x*per, (x+1)*per) run on
 // XCD x, keeping neighbouring tiles (and their shared data) in one L2.

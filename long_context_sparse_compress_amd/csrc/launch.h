@@ -25,6 +25,7 @@ struct CompressArgs {
   int rope_dims;     // partial RoPE on the last rope_dims channels (0: none)
   float rope_base;
   int rope_anchor;   // entry i's position: pos0 + ratio * i + rope_anchor
+  float* out_scale;  // fp8 output: the scale of entry i of sequence b at out_scale[b * (stride / c) + i]
 };
 
 struct IndexArgs {

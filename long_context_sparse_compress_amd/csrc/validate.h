@@ -134,7 +134,8 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
                             const void* prev_Cb, const void* prev_Zb, const float* bias,
                             const float* gamma, float eps, int in_dtype, int out_dtype,
                             const void* out, int64_t out_batch_stride, const void* ws, size_t ws_bytes,
-                            int rope_dims = 0, float rope_base = 0.f, int rope_anchor = 0) {
+                            int rope_dims = 0, float rope_base = 0.f, int rope_anchor = 0,
+                            const float* out_scale = nullptr) {
   Check k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (B < 0 || n_tok < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and n_tok must be >= 0"); return k; }
@@ -143,7 +144,16 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
   if (rope_anchor < 0 || rope_anchor >= ratio) { k.fail(CSA_ERR_INVALID_ARG, "rope_anchor must be in [0, ratio), got " + i2s(rope_anchor)); return k; }
   if (pos0 < 0 || pos0 % ratio != 0) { k.fail(CSA_ERR_INVALID_ARG, "pos0 must be >= 0 and a multiple of ratio, got " + i2s(pos0)); return k; }
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
-  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16 or CSA_FP8_E4M3"); return k; }
+  if (out_dtype == CSA_FP8_E4M3) {
+    if (ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "fp8 output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
+    if (out_batch_stride % c != 0) { k.fail(CSA_ERR_INVALID_ARG, "fp8 output needs out_batch_stride to be a multiple of c"); return k; }
+    if (!out_scale && B > 0 && n_tok / ratio > 0) { k.fail(CSA_ERR_INVALID_ARG, "out_scale is NULL"); return k; }
+    if ((reinterpret_cast<uintptr_t>(out_scale) & 3u) != 0) { k.fail(CSA_ERR_INVALID_ARG, "out_scale is not 4-byte aligned"); return k; }
+  } else if (out_scale) {
+    k.fail(CSA_ERR_INVALID_ARG, "out_scale must be NULL unless out_dtype is CSA_FP8_E4M3");
+    return k;
+  }
   if (!(eps > 0.0f) || !std::isfinite(eps)) { k.fail(CSA_ERR_INVALID_ARG, "eps must be positive and finite"); return k; }
   const int64_t n_ent = n_tok / ratio;
   if (out_batch_stride != 0 && out_batch_stride < n_ent * c) { k.fail(CSA_ERR_INVALID_ARG, "out_batch_stride smaller than one sequence's output"); return k; }

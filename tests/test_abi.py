@@ -202,9 +202,9 @@ def test_rope_validation(lib):
     """csa_compress_ex's RoPE arguments and csa_rope's checks (host only)."""
     ce = lib.csa_compress_ex
 
-    def cmp(rd=64, rb=10000.0, ra=0, ratio=4, c=512):
+    def cmp(rd=64, rb=10000.0, ra=0, ratio=4, c=512, odt=1, osc=None, stride=0):
         cb = A if ratio == 4 else None
-        return ce(ratio, 2, 8, c, 0, A, A, cb, cb, None, None, A, None, 1e-6, 1, 1, A, 0, rd, rb, ra,
+        return ce(ratio, 2, 8, c, 0, A, A, cb, cb, None, None, A, None, 1e-6, 1, odt, A, stride, osc, rd, rb, ra,
                   None, 0, None)
 
     for rd in (4, 12, 520, -8):
@@ -214,6 +214,13 @@ def test_rope_validation(lib):
     assert cmp(ra=4) == -1 and "rope_anchor" in _err(lib)
     assert cmp(ra=-1) == -1 and "rope_anchor" in _err(lib)
     assert cmp(ra=127, ratio=128) == 0    # a valid anchor; 8 tokens complete no C128A block: no launch
+    # quantize-on-write (fp8 output): C4A only, needs its scales, stride a multiple of c
+    assert cmp(rd=0, odt=2) == -1 and "out_scale" in _err(lib)
+    assert cmp(rd=0, odt=2, osc=A + 2) == -1 and "4-byte" in _err(lib)
+    assert cmp(rd=0, odt=2, osc=A, stride=520) == -1 and "multiple of c" in _err(lib)
+    assert cmp(rd=0, odt=2, osc=A, ratio=128, ra=0) == -2 and "ratio must be 4" in _err(lib)
+    assert cmp(rd=0, odt=1, osc=A) == -1 and "out_scale must be NULL" in _err(lib)
+    assert cmp(rd=0, odt=3) == -2
     r = lib.csa_rope
 
     def rp(B=2, T=3, H=4, D=512, pos0=0, rd=64, rb=10000.0, inv=0, dt=1, x=A):
