@@ -27,8 +27,8 @@ The CPU baseline times the oracle (NumPy fp64, test infrastructure) on a
 bounded sample of the same step's query tokens.
 
 Other workloads (--workload): csa_prefill, hca_decode, hca_prefill,
-csa_1m_decode, c128a_1m, csa_reindex_decode, csa_reindex_prefill -- each
-prints its own JSON line.
+csa_1m_decode, c128a_1m, csa_reindex_decode, csa_reindex_prefill,
+csa_paged_decode -- each prints its own JSON line.
 """
 from __future__ import annotations
 

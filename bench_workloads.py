@@ -21,6 +21,12 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
                  top-512 inside the pool, sparse MQA.  Decode: 32 sequences at
                  65,536 context (16,384 entries); prefill: the 4,096-token chunk
                  after 131,072 tokens (33,792 entries)
+  csa_paged_decode
+                 decode over the heterogeneous cache: 32 sequences at ragged
+                 positions (49,152 .. 81,919; mean about 65,536), their C4A and
+                 C128A entries in shuffled 128-raw-token blocks of two pools
+                 under block tables, the window in 256-row rings; sparse MQA
+                 over top-512 and HCA with sink, one query per sequence
   hbm_copy       a 1 GiB copy, the calibration point of the HBM byte counters
 """
 from __future__ import annotations
@@ -222,6 +228,46 @@ def run(args, torch, csa, synth):
         ]
         queries = nq
         info = dict(batch=B, chunk=T, context=q0 + 1 if dec else q0 + T, c4a_entries=N, pool=P, topk=k)
+    elif wl == "csa_paged_decode":
+        B, k, ring = 32, 512, 256
+        g = np.random.default_rng(11)
+        seq = [int(x) for x in g.integers(49152, 81920, size=B)]
+        nblk = [(p + 1) // 128 + 1 for p in seq]
+        max_blocks = max(nblk)
+        n_pool = sum(nblk)
+        perm = g.permutation(n_pool)
+        table_np = np.full((B, max_blocks), -1, dtype=np.int32)
+        o = 0
+        for b in range(B):
+            table_np[b, :nblk[b]] = perm[o:o + nblk[b]]
+            o += nblk[b]
+        table = torch.from_numpy(table_np).cuda()
+        pool4 = dn("g.pool4", (n_pool, 32, 512), bf)
+        pool128 = dn("g.pool128", (n_pool, 512), bf)
+        win = dn("g.win", (B, ring, 512), bf)
+        q = dn("g.q", (B, 64, 512), bf)
+        qh = dn("g.qh", (B, 64, 512), bf)
+        sink = dn("g.sink", (64,))
+        idx_np = np.stack([np.sort(g.choice((p + 1) // 4, size=k, replace=False)) for p in seq]).astype(np.int32)
+        idx = torch.from_numpy(idx_np).cuda()
+        sp = torch.tensor(seq, dtype=torch.int64, device="cuda")
+        maxp = max(seq)
+        out, outh = torch.empty_like(q), torch.empty_like(qh)
+        ws_a = torch.empty(max(16, csa.workspace_bytes(csa.OP_SPARSE_ATTN, B, 1, 1, 0)), dtype=torch.uint8,
+                           device="cuda")
+        ws_h = torch.empty(max(16, csa.workspace_bytes(csa.OP_HCA_ATTN, B, 1, 1, 0)), dtype=torch.uint8,
+                           device="cuda")
+        vh = sum((p + 1) // 128 for p in seq)
+        stages = [
+            ("sparse_mqa_attn_paged", lambda: csa.sparse_mqa_attn_paged(q, pool4, table, idx, win, sp, max_pos=maxp,
+                                                                        out=out, workspace=ws_a),
+             B * ((k + 128) * 1024 + k * 4 + 2 * 64 * 512 * 2), B * (k + 128) * 64 * 512 * 4, "hbm"),
+            ("hca_attn_paged", lambda: csa.hca_attn_paged(qh, pool128, table, win, sp, sink=sink, max_pos=maxp,
+                                                          out=outh, workspace=ws_h),
+             (vh + B * 128) * 1024 + B * 2 * 64 * 512 * 2, (vh + B * 128) * 64 * 512 * 4, "hbm"),
+        ]
+        queries = B
+        info = dict(batch=B, positions="49152..81919 (seeded)", topk=k, ring=ring, blocks=n_pool)
     elif wl == "hbm_copy":
         # 1 GiB device-to-device copy: the reference point that turns the HBM
         # traffic counters (FETCH_SIZE, WRITE_SIZE) into bytes

@@ -15,7 +15,8 @@
  * and, around them: csa_compress_ex / sparse_mqa_attn_ex / hca_attn_ex (the
  * same operations with partial RoPE fused in, and the batch-invariant
  * attention mode), csa_rope (partial RoPE on query or window rows), and
- * lightning_index_pool / topk_select_pool (the hierarchical indexer).
+ * lightning_index_pool / topk_select_pool (the hierarchical indexer), and
+ * sparse_mqa_attn_paged / hca_attn_paged (decode over the paged cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -376,6 +377,47 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
                 int io_dtype, void* out, float* lse, int flags,
                 int rope_dims, float rope_base,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_mqa_attn_paged / hca_attn_paged -- decode attention over the
+ * heterogeneous KV cache.
+ *
+ * "DeepSeek-V4技术报告解读，全适配国产算力" (3.2): compressed entries live in a
+ * classical paged cache, blocks of 128 raw tokens per request, and the
+ * sliding-window KV in a per-request state cache.  One query per sequence,
+ * each at its own position seq_pos[b] (a ragged batch).
+ *  q          [B, 64, 512] (io_dtype)
+ *  kv_pool    sparse: [n_pool, 32, 512] -- the 32 C4A entries of a block;
+ *             hca:    [n_pool, 512]     -- its one C128A entry
+ *  block_table [B, max_blocks] int32: physical block of each logical block
+ *             (raw tokens 128j .. 128j+127) of sequence b; entry e of b is
+ *             slot e % 32 (C4A) of block block_table[b][e / 32], or block
+ *             block_table[b][e] (C128A).  Ids outside [0, n_pool) mark absent
+ *             blocks: their entries are treated as padding and never read.
+ *  idx        sparse: [B, k] int32 entry ids (as topk_select writes them, -1
+ *             padding); entries past max_blocks' reach are padding too.
+ *             hca: every entry e < floor((seq_pos[b] + 1) / 128) is attended.
+ *  win        [B, ring, 512]: the window ring; raw position p of sequence b
+ *             at row p % ring.  ring is a power of two >= window, and holds
+ *             positions seq_pos[b] - window + 1 .. seq_pos[b] when called.
+ *  seq_pos    [B] int64 query positions; max_pos >= every seq_pos[b] (a
+ *             host-side bound that plans the decode split; a longer list is
+ *             still computed in full, with longer splits).
+ *  window, scale, sink, io_dtype, out [B, 64, 512], lse [B, 64], flags,
+ *  rope_dims, rope_base, workspace: as sparse_mqa_attn_ex / hca_attn_ex with
+ *  T = 1 (workspace per csa_workspace_bytes(op, B, 1, ...)).
+ */
+int sparse_mqa_attn_paged(int64_t B, int k, int H, int d, const void* q, const void* kv_pool,
+                          int64_t n_pool, const int32_t* block_table, int64_t max_blocks,
+                          const int32_t* idx, const void* win, int64_t ring, const int64_t* seq_pos,
+                          int64_t max_pos, int window, float scale, int io_dtype, void* out,
+                          float* lse, int flags, int rope_dims, float rope_base, void* workspace,
+                          size_t ws_bytes, void* stream);
+int hca_attn_paged(int64_t B, int H, int d, const void* q, const void* kv_pool, int64_t n_pool,
+                   const int32_t* block_table, int64_t max_blocks, const void* win, int64_t ring,
+                   const int64_t* seq_pos, int64_t max_pos, int window, float scale,
+                   const float* sink, int io_dtype, void* out, float* lse, int flags,
+                   int rope_dims, float rope_base, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * csa_rope -- partial RoPE (or its inverse) in place on rows of a tensor.

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
-           "rope", "lightning_index_pool", "topk_select_pool", "workspace_bytes", "library", "F32", "BF16",
+           "rope", "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
+           "workspace_bytes", "library", "F32", "BF16",
            "FP8_E4M3", "MXFP4", "CsaError"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,10 @@ _SIGS = {
     "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                         _int, _int, _vp, _i64, _vp, _int, _f32, _int, _vp, _sz, _vp],
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
+    "sparse_mqa_attn_paged": [_i64, _int, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
+                              _int, _f32, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
+    "hca_attn_paged": [_i64, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _f32, _vp, _int,
+                       _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
     "lightning_index_pool": [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp],
     "topk_select_pool": [_i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp],
     "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
@@ -330,6 +335,67 @@ def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, windo
                                ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims, rope_base, _ptr(ws),
                                wsb, _stream(stream))
     _check(st, "hca_attn")
+    return (out, lse) if return_lse else out
+
+
+def _paged_common(q, seq_pos, max_pos, out, lse, return_lse, workspace, batch_invariant, op):
+    B = seq_pos.shape[0]
+    if q.dim() == 4:
+        if q.shape[1] != 1:
+            raise ValueError("paged attention is a decode step: one query per sequence")
+    elif q.dim() != 3:
+        raise ValueError("q must be [B, 64, 512] or [B, 1, 64, 512]")
+    if seq_pos.dtype != torch.int64:
+        raise TypeError("seq_pos must be int64")
+    if max_pos is None:
+        max_pos = int(seq_pos.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty(B, 64, dtype=torch.float32, device=q.device)
+    if batch_invariant:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _workspace(op, B, 1, 1, 0, q.device, workspace)
+    return B, max_pos, out, lse, ws, wsb
+
+
+def sparse_mqa_attn_paged(q, kv_pool, block_table, idx, win, seq_pos, *, max_pos=None, window=128, scale=None,
+                          out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False,
+                          rope_dims=0, rope_base=ROPE_BASE, stream=None):
+    """Paged decode, stage 4: one query per sequence at seq_pos[b] (int64 [B]).
+    kv_pool [n_pool, 32, 512] (32 C4A entries per 128-raw-token block), block_table
+    [B, max_blocks] int32, idx [B, k] entry ids, win [B, ring, 512] (position p at
+    row p % ring, ring a power of two >= window)."""
+    B, max_pos, out, lse, ws, wsb = _paged_common(q, seq_pos, max_pos, out, lse, return_lse, workspace,
+                                                  batch_invariant, OP_SPARSE_ATTN)
+    k = idx.shape[-1]
+    d = q.shape[-1]
+    scale = d ** -0.5 if scale is None else scale
+    st = library().sparse_mqa_attn_paged(B, k, 64, d, _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(block_table),
+                                         block_table.shape[1], _ptr(idx), _ptr(win), win.shape[1], _ptr(seq_pos),
+                                         max_pos, window, scale, _dt(q), _ptr(out), _ptr(lse),
+                                         ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims, rope_base,
+                                         _ptr(ws), wsb, _stream(stream))
+    _check(st, "sparse_mqa_attn_paged")
+    return (out, lse) if return_lse else out
+
+
+def hca_attn_paged(q, kv_pool, block_table, win, seq_pos, *, sink=None, max_pos=None, window=128, scale=None,
+                   out=None, lse=None, return_lse=False, workspace=None, batch_invariant=False, rope_dims=0,
+                   rope_base=ROPE_BASE, stream=None):
+    """Paged decode, stage 5: dense MQA over the visible C128A entries of each
+    sequence (kv_pool [n_pool, 512], one entry per block) and its window ring."""
+    B, max_pos, out, lse, ws, wsb = _paged_common(q, seq_pos, max_pos, out, lse, return_lse, workspace,
+                                                  batch_invariant, OP_HCA_ATTN)
+    d = q.shape[-1]
+    scale = d ** -0.5 if scale is None else scale
+    st = library().hca_attn_paged(B, 64, d, _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(block_table),
+                                  block_table.shape[1], _ptr(win), win.shape[1], _ptr(seq_pos), max_pos, window,
+                                  scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse),
+                                  ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims, rope_base, _ptr(ws),
+                                  wsb, _stream(stream))
+    _check(st, "hca_attn_paged")
     return (out, lse) if return_lse else out
 
 

@@ -71,6 +71,16 @@ struct Params {
   int splits;
   int rope_R;           // inverse RoPE on the output's last rope_R dims (0: none)
   double rope_l2b;      // log2 of the rotary base
+  // paged decode (heterogeneous cache): compressed entry e of sequence b is
+  // row (block_table[b][e >> page_shift] << page_shift) + (e & mask) of the
+  // pool kv_cmp (n_pool blocks; other block ids are padding); window position
+  // p is row p % ring (ring a power of two) of sequence b's ring kv_raw;
+  // sequence b's query sits at seq_pos[b] (T = 1)
+  const int32_t* block_table;
+  int64_t max_blocks, n_pool;
+  int page_shift;
+  int64_t ring;
+  const int64_t* seq_pos;
 };
 
 // Inverse partial RoPE of one output value held by this lane at column col,
@@ -93,11 +103,16 @@ struct List {
   int64_t n_cmp;   // compressed slots at the head of the list
   int64_t wstart;  // first window position
   int64_t L;       // list length
+  int64_t pos;     // the query's position
 };
 
-__device__ __forceinline__ List make_list(const Params& P, int64_t t) {
-  const int64_t pos = P.q_pos0 + t;
+// PG: the paged-decode addressing of Params may be in use (checked at run
+// time); without it the kernels compile the contiguous addressing only.
+template <bool PG>
+__device__ __forceinline__ List make_list(const Params& P, int64_t b, int64_t t) {
+  const int64_t pos = (PG && P.seq_pos) ? P.seq_pos[b] : P.q_pos0 + t;
   List l;
+  l.pos = pos;
   l.wstart = pos - P.window + 1 > 0 ? pos - P.window + 1 : 0;
   if (P.idx) {
     l.n_cmp = P.k;
@@ -112,30 +127,50 @@ __device__ __forceinline__ List make_list(const Params& P, int64_t t) {
 // Address of list row `p` of query (b, t), or nullptr for padding / past the end.
 // The Top-k slot is read with `slot(p)`: from global memory, or from the
 // query's Top-k row staged in LDS.
-template <typename E, typename Slot>
+// Row of compressed entry e of sequence b in kv_cmp (-1: none), paged or not.
+template <bool PG>
+__device__ __forceinline__ int64_t cmp_row(const Params& P, int64_t b, int64_t e) {
+  if (e < 0 || e >= P.N) return -1;
+  if (!PG || !P.block_table) return b * P.N + e;
+  const int64_t blk = P.block_table[b * P.max_blocks + (e >> P.page_shift)];
+  if (blk < 0 || blk >= P.n_pool) return -1;
+  return (blk << P.page_shift) + (e & ((int64_t{1} << P.page_shift) - 1));
+}
+
+// Row of raw (window) position u of sequence b in kv_raw: a ring or a run
+// starting at raw_pos0.
+template <bool PG>
+__device__ __forceinline__ int64_t raw_row(const Params& P, int64_t b, int64_t u) {
+  return (PG && P.ring) ? b * P.ring + (u & (P.ring - 1)) : b * P.n_raw + (u - P.raw_pos0);
+}
+
+template <typename E, bool PG, typename Slot>
 __device__ __forceinline__ const E* row_ptr_by(const Params& P, int64_t b, const List& l, int64_t p, Slot slot) {
   if (p >= l.L) return nullptr;
   if (p < l.n_cmp) {
-    const int64_t e = P.idx ? static_cast<int64_t>(slot(p)) : p;
-    if (e < 0 || e >= P.N) return nullptr;
-    return static_cast<const E*>(P.kv_cmp) + (b * P.N + e) * kD;
+    const int64_t r = cmp_row<PG>(P, b, P.idx ? static_cast<int64_t>(slot(p)) : p);
+    return r < 0 ? nullptr : static_cast<const E*>(P.kv_cmp) + r * kD;
   }
-  const int64_t u = l.wstart + (p - l.n_cmp) - P.raw_pos0;
-  return static_cast<const E*>(P.kv_raw) + (b * P.n_raw + u) * kD;
+  return static_cast<const E*>(P.kv_raw) + raw_row<PG>(P, b, l.wstart + (p - l.n_cmp)) * kD;
 }
 
-template <typename E>
+template <typename E, bool PG>
 __device__ __forceinline__ const E* row_ptr(const Params& P, int64_t b, int64_t t, const List& l, int64_t p) {
   const int32_t* idx = P.idx + (b * P.T + t) * P.k;
-  return row_ptr_by<E>(P, b, l, p, [&](int64_t q) { return idx[q]; });
+  return row_ptr_by<E, PG>(P, b, l, p, [&](int64_t q) { return idx[q]; });
 }
 
 // Whether list row `p` is a real row (row_ptr would not return nullptr).
-__device__ __forceinline__ bool row_valid(const Params& P, const List& l, int64_t p, const int32_t* sidx) {
+template <bool PG>
+__device__ __forceinline__ bool row_valid(const Params& P, int64_t b, const List& l, int64_t p,
+                                          const int32_t* sidx) {
   if (p >= l.L) return false;
-  if (p < l.n_cmp && P.idx) {
-    const int32_t e = sidx[p];
-    return e >= 0 && e < P.N;
+  if (p < l.n_cmp) {
+    if (PG && P.block_table) return cmp_row<PG>(P, b, P.idx ? static_cast<int64_t>(sidx[p]) : p) >= 0;
+    if (P.idx) {
+      const int32_t e = sidx[p];
+      return e >= 0 && e < P.N;
+    }
   }
   return true;
 }
@@ -222,7 +257,7 @@ __device__ __forceinline__ void lds_barrier() {
 // softmax arithmetic), so the two give identical bits -- the multi-workgroup
 // kernel the pages pair with the one-workgroup kernel, with the work divided
 // by heads instead of rows so that no cross-workgroup merge is needed.
-template <int TGN, int HB>
+template <int TGN, int HB, bool PG = false>
 __global__ void __launch_bounds__(256 * TGN, 3 - TGN)
 attn_bf16_kernel(Params P) {
   static_assert(TGN == 1 || TGN == 2, "one or two tile groups");
@@ -256,7 +291,7 @@ attn_bf16_kernel(Params P) {
   const int hb_qk = HB == 4 ? wid : hq;     // global head block
   const int hl_qk = HB == 4 ? wid : 0;      // its slot in this workgroup's LDS exchange
   const int64_t b = gq / P.T, t = gq % P.T;
-  const List l = make_list(P, t);
+  const List l = make_list<PG>(P, b, t);
   int64_t tile0, tile1;
   split_range(P, l, split, tile0, tile1);
 
@@ -264,11 +299,10 @@ attn_bf16_kernel(Params P) {
   uint8_t* const T1 = tb1[tg];
 
   // The query's own raw row is always in the list: padding rows load it (and are masked).
-  const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) +
-                             (b * P.n_raw + (P.q_pos0 + t - P.raw_pos0)) * kD;
+  const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) + raw_row<PG>(P, b, l.pos) * kD;
   // lane e (mod 8) of wave w: source of row 8w + e of `tile`
   auto row_source = [&](int64_t tile, auto slot) -> uint64_t {
-    const uint16_t* p = row_ptr_by<uint16_t>(P, b, l, tile * kTile + 8 * wid + (lane & 7), slot);
+    const uint16_t* p = row_ptr_by<uint16_t, PG>(P, b, l, tile * kTile + 8 * wid + (lane & 7), slot);
     return reinterpret_cast<uint64_t>(p ? p : safe_row);
   };
   // row 8w + e of a tile, from lane e's source, into tile buffer `dst`
@@ -369,7 +403,7 @@ attn_bf16_kernel(Params P) {
       // rows of this lane: 4g+i (s0) and 16+4g+i (s1); padding rows are masked
       // which of the tile's 32 rows are real: lane r (mod 32) tests row r
       const uint32_t vrows =
-          static_cast<uint32_t>(__ballot(row_valid(P, l, tile * kTile + (lane & 31), sidx))) >> (4 * g);
+          static_cast<uint32_t>(__ballot(row_valid<PG>(P, b, l, tile * kTile + (lane & 31), sidx))) >> (4 * g);
       float lg[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -450,7 +484,7 @@ attn_bf16_kernel(Params P) {
   // combine.
   if (__builtin_expect(P.rope_R > 0 && P.splits == 1, 0)) {
     for (int p = tid; p < P.rope_R / 2; p += 256 * TGN)
-      rope_cs[p] = inv_rope_cs(kD - P.rope_R + 2 * p, P.q_pos0 + t, P);
+      rope_cs[p] = inv_rope_cs(kD - P.rope_R + 2 * p, l.pos, P);
   }
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
@@ -592,7 +626,7 @@ attn_f32_kernel(Params P) {
   const int64_t b = gq / P.T, t = gq % P.T;
   const int head = hg * 8 + tid / 32;
   const int part = tid % 32;
-  const List l = make_list(P, t);
+  const List l = make_list<true>(P, b, t);
   float qv[16], ov[16];
   const float* qp = static_cast<const float*>(P.q) + (gq * kH + head) * kD + part * 16;
 #pragma unroll
@@ -605,7 +639,7 @@ attn_f32_kernel(Params P) {
     __syncthreads();
     for (int i = tid; i < 16 * kD; i += 256) {
       const int r = i / kD, c = i % kD;
-      const float* p = row_ptr<float>(P, b, t, l, base + r);
+      const float* p = row_ptr<float, true>(P, b, t, l, base + r);
       xs[r][c] = p ? p[c] : 0.f;
       if (c == 0) xv[r] = p != nullptr;
     }
@@ -644,7 +678,7 @@ attn_f32_kernel(Params P) {
       const int col = part * 16 + i;
       if (col >= kD - P.rope_R) {
         float cs, sn;
-        rope_cos_sin(-(P.q_pos0 + t), (col - (kD - P.rope_R)) >> 1, P.rope_R, P.rope_l2b, cs, sn);
+        rope_cos_sin(-l.pos, (col - (kD - P.rope_R)) >> 1, P.rope_R, P.rope_l2b, cs, sn);
         rope_pair(ov[i], ov[i + 1], cs, sn);
       }
     }
@@ -679,7 +713,7 @@ attn_combine_kernel(Params P) {
   const int c0 = 16 * db0 + j, c1 = c0 + 64;
   float2 k0 = make_float2(1.f, 0.f), k1 = k0;
   if (__builtin_expect(P.rope_R > 0, 0)) {
-    const int64_t pos = P.q_pos0 + gq % P.T;
+    const int64_t pos = P.seq_pos ? P.seq_pos[gq / P.T] : P.q_pos0 + gq % P.T;
     k0 = inv_rope_cs(128 * w + c0, pos, P);
     k1 = inv_rope_cs(128 * w + c1, pos, P);
   }
@@ -743,6 +777,28 @@ attn_combine_kernel(Params P) {
   *reinterpret_cast<uint4*>(out) = *reinterpret_cast<const uint4*>(ot + r * 128 + c);
 }
 
+template <bool PG>
+hipError_t launch_bf16(Params& P, int64_t nq, int64_t per_split, int flags, hipStream_t s) {
+  if (flags & CSA_ATTN_BATCH_INVARIANT) {
+    // no row split: every query's rows in order in one workgroup's chain;
+    // few queries spread their four head blocks over four workgroups (the
+    // same bits, see attn_bf16_kernel)
+    P.splits = 1;
+    if (nq < 256)
+      hipLaunchKernelGGL((attn_bf16_kernel<1, 1, PG>), dim3(static_cast<uint32_t>(nq * 4)), dim3(256), 0, s, P);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<1, 4, PG>), dim3(static_cast<uint32_t>(nq)), dim3(256), 0, s, P);
+    return hipGetLastError();
+  }
+  if (P.splits > 1 && per_split >= 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<2, 4, PG>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0, s, P);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<1, 4, PG>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
+  if (P.splits > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
@@ -753,6 +809,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   P.raw_pos0 = a.raw_pos0; P.n_raw = a.n_raw; P.window = a.window;
   P.scale_log2 = a.scale * kLog2e; P.sink = a.sink; P.out = a.out; P.lse = a.lse;
   P.ws = static_cast<float*>(a.ws);
+  P.block_table = a.block_table; P.max_blocks = a.max_blocks; P.n_pool = a.n_pool;
+  P.page_shift = a.page_shift; P.ring = a.ring; P.seq_pos = a.seq_pos;
   P.rope_R = a.rope_dims;
   P.rope_l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
   const int64_t nq = a.B * a.T;
@@ -762,7 +820,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   // longest list over the call's queries bounds the split count
-  const int64_t last = a.q_pos0 + a.T - 1;
+  const int64_t last = a.seq_pos ? a.max_pos : a.q_pos0 + a.T - 1;   // the longest list bounds the split
   const int64_t wlen = last - (last - a.window + 1 > 0 ? last - a.window + 1 : 0) + 1;
   int64_t ncmp = a.idx ? a.k : (last + 1) / a.ratio;
   if (!a.idx && ncmp > a.N) ncmp = a.N;
@@ -773,24 +831,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   // merge add about 4 us, so short runs keep one group.
   const int64_t ntiles = (ncmp + wlen + kAttnTile - 1) / kAttnTile;
   const int64_t per_split = (ntiles + P.splits - 1) / P.splits;
-  if (a.flags & CSA_ATTN_BATCH_INVARIANT) {
-    // no row split: every query's rows in order in one workgroup's chain;
-    // few queries spread their four head blocks over four workgroups (the
-    // same bits, see attn_bf16_kernel)
-    P.splits = 1;
-    if (nq < 256)
-      hipLaunchKernelGGL((attn_bf16_kernel<1, 1>), dim3(static_cast<uint32_t>(nq * 4)), dim3(256), 0, s, P);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<1, 4>), dim3(static_cast<uint32_t>(nq)), dim3(256), 0, s, P);
-    return hipGetLastError();
-  }
-  if (P.splits > 1 && per_split >= 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<2, 4>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0, s, P);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<1, 4>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(256), 0, s, P);
-  if (P.splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
-  return hipGetLastError();
+  if (a.block_table || a.seq_pos) return launch_bf16<true>(P, nq, per_split, a.flags, s);
+  return launch_bf16<false>(P, nq, per_split, a.flags, s);
 }
+
 
 }  // namespace csa

@@ -166,6 +166,38 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
                      io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
 }
 
+int sparse_mqa_attn_paged(int64_t B, int k, int H, int d, const void* q, const void* kv_pool, int64_t n_pool,
+                          const int32_t* block_table, int64_t max_blocks, const int32_t* idx, const void* win,
+                          int64_t ring, const int64_t* seq_pos, int64_t max_pos, int window, float scale,
+                          int io_dtype, void* out, float* lse, int flags, int rope_dims, float rope_base,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_paged(true, B, k, H, d, q, kv_pool, n_pool, block_table, max_blocks, idx, win, ring,
+                                   seq_pos, max_pos, window, scale, nullptr, io_dtype, out, lse, flags, rope_dims,
+                                   rope_base, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  // 32 C4A entries per block of 128 raw tokens
+  csa::AttnArgs a{B, 1, max_blocks << 5, k, 4, 0, q, kv_pool, idx, win, 0, ring, window, scale,
+                  nullptr, io_dtype, out, lse, workspace, flags, rope_dims, rope_base,
+                  block_table, max_blocks, n_pool, 5, ring, seq_pos, max_pos};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn_paged launch");
+}
+
+int hca_attn_paged(int64_t B, int H, int d, const void* q, const void* kv_pool, int64_t n_pool,
+                   const int32_t* block_table, int64_t max_blocks, const void* win, int64_t ring,
+                   const int64_t* seq_pos, int64_t max_pos, int window, float scale, const float* sink, int io_dtype,
+                   void* out, float* lse, int flags, int rope_dims, float rope_base, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_paged(false, B, 0, H, d, q, kv_pool, n_pool, block_table, max_blocks, nullptr, win,
+                                   ring, seq_pos, max_pos, window, scale, sink, io_dtype, out, lse, flags,
+                                   rope_dims, rope_base, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  // one C128A entry per block of 128 raw tokens
+  csa::AttnArgs a{B, 1, max_blocks, 0, 128, 0, q, kv_pool, nullptr, win, 0, ring, window, scale,
+                  sink, io_dtype, out, lse, workspace, flags, rope_dims, rope_base,
+                  block_table, max_blocks, n_pool, 0, ring, seq_pos, max_pos};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn_paged launch");
+}
+
 int csa_rope(int64_t B, int64_t T, int64_t H, int64_t D, int64_t pos0, int rope_dims, float rope_base,
              int inverse, int dtype, void* x, void* stream) {
   csa::Check ck = csa::check_rope_rows(B, T, H, D, pos0, rope_dims, rope_base, inverse, dtype, x);

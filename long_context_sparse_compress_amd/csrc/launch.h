@@ -82,6 +82,13 @@ struct AttnArgs {
   int flags;          // CSA_ATTN_* bits
   int rope_dims;      // inverse RoPE on the output's last rope_dims dims (0: none)
   float rope_base;
+  // paged decode (all zero / NULL otherwise): see Params in attention.hip
+  const int32_t* block_table = nullptr;
+  int64_t max_blocks = 0, n_pool = 0;
+  int page_shift = 0;
+  int64_t ring = 0;
+  const int64_t* seq_pos = nullptr;
+  int64_t max_pos = 0;
 };
 
 struct RopeArgs {

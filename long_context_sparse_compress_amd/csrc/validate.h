@@ -340,6 +340,39 @@ inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t
   return k;
 }
 
+// Paged decode attention (heterogeneous cache): one query per sequence at
+// seq_pos[b], compressed entries through a block table, the window from a ring.
+inline Check check_paged(bool sparse, int64_t B, int kk, int H, int d, const void* q, const void* kv_pool,
+                         int64_t n_pool, const int32_t* block_table, int64_t max_blocks, const int32_t* idx,
+                         const void* win, int64_t ring, const int64_t* seq_pos, int64_t max_pos, int window,
+                         float scale, const float* sink, int io_dtype, const void* out, const float* lse, int flags,
+                         int rope_dims, float rope_base, const void* ws, size_t ws_bytes) {
+  Check k;
+  check_attn_flags(k, flags);
+  if (!k.ok()) return k;
+  if (!check_attn_common(k, B, 0, 0, H, d, 0, 0, window, scale, io_dtype)) return k;
+  if (!check_rope(k, rope_dims, rope_base, d)) return k;
+  if (sparse && (kk < 0 || kk > CSA_MAX_TOPK)) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [0, 2048], got " + i2s(kk)); return k; }
+  if (n_pool < 0) { k.fail(CSA_ERR_INVALID_ARG, "n_pool must be >= 0"); return k; }
+  if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
+  if (ring < window) { k.fail(CSA_ERR_INVALID_ARG, "the window ring holds " + i2s(ring) + " rows, fewer than the window " + i2s(window)); return k; }
+  if (ring & (ring - 1)) { k.fail(CSA_ERR_INVALID_ARG, "the window ring size must be a power of two, got " + i2s(ring)); return k; }
+  if (max_pos < 0) { k.fail(CSA_ERR_INVALID_ARG, "max_pos must be >= 0"); return k; }
+  const bool empty = (B == 0);
+  k.ptr(q, "q", !empty) && k.ptr(kv_pool, "kv_pool", !empty && n_pool > 0) &&
+      k.ptr(block_table, "block_table", !empty) && k.ptr(idx, "idx", sparse && !empty && kk > 0) &&
+      k.ptr(win, "win", !empty) && k.ptr(seq_pos, "seq_pos", !empty) && k.ptr(out, "out", !empty) &&
+      k.ptr(lse, "lse", false) && k.ptr(sink, "sink", false);
+  if (!k.ok()) return k;
+  if (sparse && sink) { k.fail(CSA_ERR_INVALID_ARG, "sparse attention has no sink"); return k; }
+  const size_t need = (flags & CSA_ATTN_BATCH_INVARIANT) ? 0 : attn_workspace_bytes(B, 1);
+  if (need > 0 && !empty) {
+    if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "paged attention needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
+    k.ptr(ws, "workspace");
+  }
+  return k;
+}
+
 inline size_t workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int kk) {
   (void)kk;
   switch (op) {

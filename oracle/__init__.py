@@ -22,6 +22,8 @@ Pages and the parts each module follows:
 * ``attention`` -- "DeepSeek V4 结构速览" (CSA（c4a 路线）; HCA（c128a 路线）)
   and "DeepSeek-V4 技术解读：百万 Token 上下文的新里程碑" (2.1, shared-KV MQA).
 * ``kv_accounting`` -- "DeepSeek V4 结构速览" (KV cache 账).
+* ``cache`` -- "DeepSeek-V4技术报告解读，全适配国产算力" (3.2, the heterogeneous
+  KV cache: paged classical cache, per-request state cache).
 * ``rope`` -- "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding
   under CSA; RoPE anchors of the compressor; inverse RoPE on the output).
 * ``numerics`` -- decoding of the quantized inputs and bf16 score storage.
@@ -32,4 +34,4 @@ pages leave open (which block is "a", bias row order, the block-0 fill, the
 RMSNorm eps, no indexer scale, the sink semantics) are readings that no page
 value fixes; they are listed with each function.
 """
-from . import attention, compressor, indexer, kv_accounting, numerics, rope, topk  # noqa: F401
+from . import attention, cache, compressor, indexer, kv_accounting, numerics, rope, topk  # noqa: F401

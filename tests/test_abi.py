@@ -31,7 +31,8 @@ def test_header_symbols_exported(lib):
     names = _declared()
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
-                          "lightning_index_pool", "topk_select_pool", "csa_workspace_bytes",
+                          "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
+                          "csa_workspace_bytes",
                           "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -291,3 +292,33 @@ def test_pool_validation(lib):
     assert top_pool(pool=None) == -1 and "pool" in _err(lib)
     assert top_pool(idx=None) == -1
     assert top_pool(B=0, sc=None, pool=None, idx=None) == 0
+
+
+def test_paged_validation(lib):
+    """sparse_mqa_attn_paged / hca_attn_paged argument checks (host only)."""
+    sp, hp = lib.sparse_mqa_attn_paged, lib.hca_attn_paged
+    ws = lib.csa_workspace_bytes(3, 4, 1, 1, 0)
+
+    def s_(B=4, k=16, H=64, nb=8, ring=256, win=128, maxpos=1000, flags=0, wsp=A, wsb=ws, tbl=A, sp_=A, idx=A):
+        return sp(B, k, H, 512, A, A, 100, tbl, nb, idx, A, ring, sp_, maxpos, win, 0.04, 1, A, None, flags, 0,
+                  10000.0, wsp, wsb, None)
+
+    def h_(B=4, ring=256, sink=None, wsp=A, wsb=ws):
+        return hp(B, 64, 512, A, A, 100, A, 8, A, ring, A, 1000, 128, 0.04, sink, 1, A, None, 0, 0, 10000.0,
+                  wsp, wsb, None)
+
+    assert s_(H=32) == -2
+    assert s_(ring=100) == -1 and "fewer than the window" in _err(lib)
+    assert s_(ring=192) == -1 and "power of two" in _err(lib)
+    assert s_(nb=0) == -1 and "max_blocks" in _err(lib)
+    assert s_(maxpos=-1) == -1
+    assert s_(tbl=None) == -1 and "block_table" in _err(lib)
+    assert s_(sp_=None) == -1 and "seq_pos" in _err(lib)
+    assert s_(idx=None) == -1 and "idx" in _err(lib)
+    assert s_(k=2049) == -1
+    assert s_(wsp=None) == -4
+    assert s_(flags=2) == -1 and "unknown attention flags" in _err(lib)
+    assert h_(ring=64) == -1
+    assert h_(wsp=None) == -4
+    assert h_(sink=MIS) == -1
+    assert s_(B=0, wsp=None, tbl=None, sp_=None, idx=None) == 0

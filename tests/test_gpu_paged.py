@@ -1,0 +1,175 @@
+"""GPU parity of decode attention over the heterogeneous KV cache
+(sparse_mqa_attn_paged, hca_attn_paged) against the oracle, through the C ABI.
+
+Page: "DeepSeek-V4技术报告解读，全适配国产算力" (3.2: the classical paged cache
+in blocks of 128 raw tokens, the per-request state cache holding the sliding
+window).  Every sequence sits at its own position; the physical blocks are
+shuffled; the window ring wraps.  The oracle gathers each sequence's entries
+and window rows back into contiguous arrays (oracle.cache) and runs the
+attention oracles.  Tolerances as for the contiguous attention (bf16 2e-2
+max-abs plus the normwise guard, lse 1e-3); paged and contiguous layouts of
+the same data give identical bits.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_compress_amd as csa
+import synth
+from oracle import attention as oa
+from oracle import cache as occ
+from helpers import ATTN_BF16_MAX_ABS, ATTN_NORMWISE, dev, host, max_abs, normwise_rel
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+
+
+def _assert_bf16(got, ref):
+    assert max_abs(got, ref) < ATTN_BF16_MAX_ABS
+    assert normwise_rel(got, ref) < ATTN_NORMWISE
+
+
+def _paged_cache(name, seq_pos, per_block, ring, spare=5):
+    """Blocks for every sequence's visible entries, shuffled in one pool;
+    unused table slots hold -1.  Returns (pool, table, ring_win, n_blocks)."""
+    B = len(seq_pos)
+    ratio = 128 // per_block
+    nblk = [(p + 1) // 128 + 1 for p in seq_pos]          # blocks covering positions 0..p
+    max_blocks = max(nblk) + 2
+    n_pool = sum(nblk) + spare
+    g = np.random.default_rng(zlib.crc32(name.encode()))
+    perm = g.permutation(n_pool)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    shape = (n_pool, per_block, 512) if per_block > 1 else (n_pool, 512)
+    pool = synth.device_normal(name + ".pool", shape, BF)
+    win = synth.device_normal(name + ".win", (B, ring, 512), BF)
+    return pool, table, win, ratio
+
+
+def _entries(pool, table_row, n, per_block):
+    return occ.paged_entries(host(pool), table_row, n, per_block)
+
+
+def _window(win_b, pos, window=128):
+    w0 = max(0, pos - window + 1)
+    return occ.ring_rows(host(win_b), range(w0, pos + 1)), w0
+
+
+SEQ_POS = [4095, 9000, 65535, 70001, 131071, 333, 12345, 65536]
+
+
+@pytest.mark.parametrize("bi", [False, True])
+def test_paged_sparse_decode(bi):
+    """8 sequences at different positions, top-512 lists, shuffled blocks, a
+    256-row window ring; the split decode and the batch-invariant kernel."""
+    B, k, ring = len(SEQ_POS), 512, 256
+    pool, table, win, _ = _paged_cache("pg.sp", SEQ_POS, 32, ring)
+    q = synth.device_normal("pg.sp.q", (B, 64, 512), BF)
+    idx = np.concatenate([synth.random_topk_indices(f"pg.sp.idx{b}", 1, 1, k, [(p + 1) // 4])[0]
+                          for b, p in enumerate(SEQ_POS)])
+    sp = torch.tensor(SEQ_POS, dtype=torch.int64, device="cuda")
+    out, lse = csa.sparse_mqa_attn_paged(q, pool, dev(table, torch.int32), dev(idx, torch.int32), win, sp,
+                                         return_lse=True, batch_invariant=bi)
+    torch.cuda.synchronize()
+    got, gl = host(out), host(lse)
+    for b, pos in enumerate(SEQ_POS):
+        sel = idx[b][idx[b] >= 0]
+        rows = _entries(pool, table[b], int(sel.max()) + 1, 32)[sel]
+        rw, w0 = _window(win[b], pos)
+        o, l = oa.sparse_mqa(host(q[b])[None, None], rows[None], np.arange(len(sel))[None, None], rw[None],
+                             w0, pos, 128)
+        _assert_bf16(got[b], o[0, 0])
+        assert max_abs(gl[b], l[0, 0]) < 1e-3
+
+
+def test_paged_hca_decode_with_sink():
+    """6 sequences up to 1M context (up to 8,192 C128A entries each), one entry
+    per block, shuffled blocks, a 128-row ring, sink."""
+    seq = [1048575, 300000, 128, 127, 65535, 777777]
+    B, ring = len(seq), 128
+    pool, table, win, _ = _paged_cache("pg.h", seq, 1, ring)
+    q = synth.device_normal("pg.h.q", (B, 64, 512), BF)
+    sink = synth.device_normal("pg.h.sink", (64,))
+    sp = torch.tensor(seq, dtype=torch.int64, device="cuda")
+    out, lse = csa.hca_attn_paged(q, pool, dev(table, torch.int32), win, sp, sink=sink, return_lse=True)
+    torch.cuda.synchronize()
+    got, gl = host(out), host(lse)
+    for b, pos in enumerate(seq):
+        V = (pos + 1) // 128
+        kv = _entries(pool, table[b], V, 1) if V else np.zeros((0, 512))
+        rw, w0 = _window(win[b], pos)
+        o, l = oa.dense_attention(host(q[b])[None, None], kv[None], rw[None], w0, pos, 128, 128,
+                                  sink=host(sink))
+        _assert_bf16(got[b], o[0, 0])
+        assert max_abs(gl[b], l[0, 0]) < 1e-3
+
+
+def test_absent_blocks_are_padding():
+    """Top-k slots that point into a block the table marks absent contribute
+    nothing (and are not read)."""
+    seq = [9000, 9000]
+    B, k, ring = 2, 64, 128
+    pool, table, win, _ = _paged_cache("pg.abs", seq, 32, ring)
+    table = table.copy()
+    table[0, 3] = -1                 # entries 96..127 of sequence 0: absent
+    table[1, 5] = 10 ** 6            # past the pool: absent
+    q = synth.device_normal("pg.abs.q", (B, 64, 512), BF)
+    idx = np.tile(np.arange(80, 80 + 2 * k, 2, dtype=np.int32), (B, 1))   # entries 80..206
+    sp = torch.tensor(seq, dtype=torch.int64, device="cuda")
+    out = csa.sparse_mqa_attn_paged(q, pool, dev(table, torch.int32), dev(idx, torch.int32), win, sp)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b, pos in enumerate(seq):
+        blk = table[b][idx[b] // 32]
+        keep = idx[b][(blk >= 0) & (blk < pool.shape[0])]
+        t = table[b].copy()
+        t[(t < 0) | (t >= pool.shape[0])] = 0
+        rows = _entries(pool, t, int(idx[b].max()) + 1, 32)[keep]
+        rw, w0 = _window(win[b], pos)
+        o, _ = oa.sparse_mqa(host(q[b])[None, None], rows[None], np.arange(len(keep))[None, None], rw[None], w0,
+                             pos, 128)
+        _assert_bf16(got[b], o[0, 0])
+
+
+def test_paged_equals_contiguous_bits():
+    """The same entries and window laid out contiguously (sparse_mqa_attn_ex,
+    hca_attn_ex) and paged, all sequences at one position: identical bits."""
+    B, N, k, pos = 16, 4096, 512, 16383
+    kv = synth.device_normal("pg.eq.kv", (B, N, 512), BF)
+    raw = synth.device_normal("pg.eq.raw", (B, 128, 512), BF)
+    q = synth.device_normal("pg.eq.q", (B, 1, 64, 512), BF)
+    idx = dev(synth.random_topk_indices("pg.eq.idx", B, 1, k, [N]), torch.int32)
+    # pages: blocks of sequence b are b*128 + j, the pool shuffled under a table
+    nb = N // 32
+    g = np.random.default_rng(5)
+    perm = g.permutation(B * nb).astype(np.int32)
+    table = perm.reshape(B, nb)
+    pool = torch.empty(B * nb, 32, 512, dtype=BF, device="cuda")
+    pool[torch.as_tensor(table.reshape(-1), device="cuda").long()] = kv.reshape(B * nb, 32, 512)
+    ring = torch.empty(B, 128, 512, dtype=BF, device="cuda")
+    r0 = pos - 127
+    ring[:, torch.arange(r0, pos + 1, device="cuda") % 128] = raw
+    sp = torch.full((B,), pos, dtype=torch.int64, device="cuda")
+    for bi in (False, True):
+        a = csa.sparse_mqa_attn(q, kv, idx, raw, q_pos0=pos, raw_pos0=r0, batch_invariant=bi)
+        p = csa.sparse_mqa_attn_paged(q[:, 0], pool, dev(table, torch.int32), idx[:, 0], ring, sp,
+                                      batch_invariant=bi)
+        torch.cuda.synchronize()
+        assert torch.equal(a[:, 0], p), bi
+    # HCA: one entry per block
+    Nh = (pos + 1) // 128
+    kvh = synth.device_normal("pg.eq.kvh", (B, Nh, 512), BF)
+    sink = synth.device_normal("pg.eq.sink", (64,))
+    permh = g.permutation(B * Nh).astype(np.int32).reshape(B, Nh)
+    poolh = torch.empty(B * Nh, 512, dtype=BF, device="cuda")
+    poolh[torch.as_tensor(permh.reshape(-1), device="cuda").long()] = kvh.reshape(B * Nh, 512)
+    a = csa.hca_attn(q, kvh, raw, q_pos0=pos, raw_pos0=r0, sink=sink)
+    p = csa.hca_attn_paged(q[:, 0], poolh, dev(permh, torch.int32), ring, sp, sink=sink)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, 0], p)
