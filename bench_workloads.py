@@ -25,8 +25,9 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
                  decode over the heterogeneous cache: 32 sequences at ragged
                  positions (49,152 .. 81,919; mean about 65,536), their C4A and
                  C128A entries in shuffled 128-raw-token blocks of two pools
-                 under block tables, the window in 256-row rings; sparse MQA
-                 over top-512 and HCA with sink, one query per sequence
+                 under block tables, the window in 256-row rings: the paged
+                 indexer over bf16 keys, Top-k per sequence, sparse MQA over
+                 the top-512 and HCA with sink, one query per sequence
   hbm_copy       a 1 GiB copy, the calibration point of the HBM byte counters
 """
 from __future__ import annotations
@@ -258,7 +259,20 @@ def run(args, torch, csa, synth):
         ws_h = torch.empty(max(16, csa.workspace_bytes(csa.OP_HCA_ATTN, B, 1, 1, 0)), dtype=torch.uint8,
                            device="cuda")
         vh = sum((p + 1) // 128 for p in seq)
+        vis4 = sum((p + 1) // 4 for p in seq)
+        kpool = dn("g.keys", (n_pool, 32, 128), bf)
+        qi = dn("g.qi", (B, 64, 128), bf, var=1.0 / 128)
+        wi = synth.device_uniform("g.wi", (B, 64))
+        Nmax = 32 * max_blocks
+        scores = torch.empty(B, Nmax, dtype=bf, device="cuda")
+        idx2 = torch.empty(B, k, dtype=torch.int32, device="cuda")
+        ws_t = torch.empty(max(16, csa.workspace_bytes(csa.OP_TOPK, B, 1, Nmax, k)), dtype=torch.uint8,
+                           device="cuda")
         stages = [
+            ("lightning_index_paged", lambda: csa.lightning_index_paged(qi, wi, kpool, table, sp, scores=scores),
+             vis4 * 256 + B * 64 * 128 * 2 + B * 64 * 4 + B * Nmax * 2, vis4 * 64 * 128 * 2, "hbm"),
+            ("topk_select_paged", lambda: csa.topk_select_paged(scores, k, sp, idx=idx2, workspace=ws_t),
+             B * Nmax * 2 + B * k * 4, 0, "hbm"),
             ("sparse_mqa_attn_paged", lambda: csa.sparse_mqa_attn_paged(q, pool4, table, idx, win, sp, max_pos=maxp,
                                                                         out=out, workspace=ws_a),
              B * ((k + 128) * 1024 + k * 4 + 2 * 64 * 512 * 2), B * (k + 128) * 64 * 512 * 4, "hbm"),

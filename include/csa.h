@@ -16,7 +16,8 @@
  * same operations with partial RoPE fused in, and the batch-invariant
  * attention mode), csa_rope (partial RoPE on query or window rows), and
  * lightning_index_pool / topk_select_pool (the hierarchical indexer), and
- * sparse_mqa_attn_paged / hca_attn_paged (decode over the paged cache).
+ * lightning_index_paged / topk_select_paged / sparse_mqa_attn_paged /
+ * hca_attn_paged (decode over the paged cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -407,6 +408,33 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
  *  rope_dims, rope_base, workspace: as sparse_mqa_attn_ex / hca_attn_ex with
  *  T = 1 (workspace per csa_workspace_bytes(op, B, 1, ...)).
  */
+/*
+ * lightning_index_paged / topk_select_paged -- the decode indexer and Top-k
+ * over the heterogeneous cache (the same operations as lightning_index and
+ * topk_select with T = 1 and one position per sequence).
+ *
+ * lightning_index_paged: scores[b, e] of entry e of sequence b, index keys in
+ * k_pool [n_pool, 32, 128] (bf16, or E4M3 codes with k_scale [n_pool, 32]
+ * fp32 -- what csa_compress_ex's quantize-on-write produces), entry e at slot
+ * e % 32 of block block_table[b][e / 32] (ids outside [0, n_pool) read block
+ * 0: the blocks holding a sequence's visible entries must be mapped).
+ * q [B, 64, 128] (bf16 or E4M3 with q_scale [B, 64]), w [B, 64];
+ * scores [B, 32 * max_blocks]: -inf for e >= floor((seq_pos[b] + 1) / 4).
+ * qk_dtype CSA_BF16 or CSA_FP8_E4M3; n_pool >= 1.
+ *
+ * topk_select_paged: topk_select's selection over scores [B, N] where row b's
+ * candidates are e < min(N, floor((seq_pos[b] + 1) / ratio)); idx [B, k],
+ * ascending then -1.  Workspace as csa_workspace_bytes(CSA_OP_TOPK, B, 1, N, k).
+ */
+int lightning_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, const void* q,
+                          const void* q_scale, const float* w, const void* k_pool,
+                          const void* k_scale, int64_t n_pool, const int32_t* block_table,
+                          const int64_t* seq_pos, int qk_dtype, void* scores, int score_dtype,
+                          void* stream);
+int topk_select_paged(int64_t B, int64_t N, const int64_t* seq_pos, int ratio, int k,
+                      const void* scores, int score_dtype, int32_t* idx, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 int sparse_mqa_attn_paged(int64_t B, int k, int H, int d, const void* q, const void* kv_pool,
                           int64_t n_pool, const int32_t* block_table, int64_t max_blocks,
                           const int32_t* idx, const void* win, int64_t ring, const int64_t* seq_pos,

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
-           "rope", "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
+           "rope", "lightning_index_pool", "topk_select_pool", "lightning_index_paged", "topk_select_paged",
+           "sparse_mqa_attn_paged", "hca_attn_paged",
            "workspace_bytes", "library", "F32", "BF16",
            "FP8_E4M3", "MXFP4", "CsaError"]
 
@@ -37,6 +38,9 @@ _SIGS = {
     "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                         _int, _int, _vp, _i64, _vp, _int, _f32, _int, _vp, _sz, _vp],
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
+    "lightning_index_paged": [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _int,
+                              _vp],
+    "topk_select_paged": [_i64, _i64, _vp, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
     "sparse_mqa_attn_paged": [_i64, _int, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                               _int, _f32, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
     "hca_attn_paged": [_i64, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _f32, _vp, _int,
@@ -358,6 +362,36 @@ def _paged_common(q, seq_pos, max_pos, out, lse, return_lse, workspace, batch_in
     else:
         ws, wsb = _workspace(op, B, 1, 1, 0, q.device, workspace)
     return B, max_pos, out, lse, ws, wsb
+
+
+def lightning_index_paged(q, w, k_pool, block_table, seq_pos, *, qk_dtype=None, q_scale=None, k_scale=None,
+                          score_dtype=torch.bfloat16, scores=None, stream=None):
+    """Paged decode indexer: q [B, 64, 128] (bf16, or uint8 E4M3 codes with q_scale [B, 64]),
+    w [B, 64], k_pool [n_pool, 32, 128] (bf16, or uint8 codes with k_scale [n_pool, 32]),
+    block_table [B, max_blocks] int32, seq_pos [B] int64; returns scores [B, 32 * max_blocks]."""
+    B, max_blocks = block_table.shape
+    if qk_dtype is None:
+        qk_dtype = FP8_E4M3 if q.dtype == torch.uint8 else _dt(q)
+    if scores is None:
+        scores = torch.empty(B, 32 * max_blocks, dtype=score_dtype, device=q.device)
+    st = library().lightning_index_paged(B, max_blocks, 64, 128, _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_pool),
+                                         _ptr(k_scale), k_pool.shape[0], _ptr(block_table), _ptr(seq_pos), qk_dtype,
+                                         _ptr(scores), _dt(scores), _stream(stream))
+    _check(st, "lightning_index_paged")
+    return scores
+
+
+def topk_select_paged(scores, k, seq_pos, *, ratio=4, idx=None, workspace=None, stream=None):
+    """Top-k of each sequence's visible entries (row b: e < (seq_pos[b] + 1) // ratio);
+    scores [B, N]; returns idx [B, k] int32."""
+    B, N = scores.shape
+    if idx is None:
+        idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
+    ws, wsb = _workspace(OP_TOPK, B, 1, N, k, scores.device, workspace)
+    st = library().topk_select_paged(B, N, _ptr(seq_pos), ratio, k, _ptr(scores), _dt(scores), _ptr(idx), _ptr(ws),
+                                     wsb, _stream(stream))
+    _check(st, "topk_select_paged")
+    return idx
 
 
 def sparse_mqa_attn_paged(q, kv_pool, block_table, idx, win, seq_pos, *, max_pos=None, window=128, scale=None,

@@ -166,6 +166,26 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
                      io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
 }
 
+int lightning_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, const void* q, const void* q_scale,
+                          const float* w, const void* k_pool, const void* k_scale, int64_t n_pool,
+                          const int32_t* block_table, const int64_t* seq_pos, int qk_dtype, void* scores,
+                          int score_dtype, void* stream) {
+  csa::Check ck = csa::check_index_paged(B, max_blocks, H_I, d_I, q, q_scale, w, k_pool, k_scale, n_pool, block_table,
+                                         seq_pos, qk_dtype, scores, score_dtype);
+  if (!ck.ok()) return finish(ck);
+  csa::IndexArgs a{B, 1, max_blocks * 32, 0, 4, q, q_scale, w, k_pool, k_scale, qk_dtype, scores, score_dtype,
+                   block_table, max_blocks, n_pool, seq_pos};
+  return hip_status(csa::launch_index(a, as_stream(stream)), "lightning_index_paged launch");
+}
+
+int topk_select_paged(int64_t B, int64_t N, const int64_t* seq_pos, int ratio, int k, const void* scores,
+                      int score_dtype, int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  csa::Check ck = csa::check_topk_paged(B, N, seq_pos, ratio, k, scores, score_dtype, idx, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  csa::TopkArgs a{B, 1, N, 0, ratio, k, scores, score_dtype, idx, workspace, nullptr, 0, seq_pos};
+  return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select_paged launch");
+}
+
 int sparse_mqa_attn_paged(int64_t B, int k, int H, int d, const void* q, const void* kv_pool, int64_t n_pool,
                           const int32_t* block_table, int64_t max_blocks, const int32_t* idx, const void* win,
                           int64_t ring, const int64_t* seq_pos, int64_t max_pos, int window, float scale,

@@ -349,12 +349,23 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   }
 }
 
-template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS>
+// Paged keys (the heterogeneous cache's classical blocks): entry e of
+// sequence b is row (table[b][e / 32] * 32 + e % 32) of the key pool, and the
+// sequence's query sits at seq_pos[b].  A 16-entry tile never straddles a
+// 32-entry block, so paging only moves a tile's base row.
+struct KeyPages {
+  const int32_t* table;
+  int64_t max_blocks, n_pool;
+  const int64_t* seq_pos;
+};
+
+template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS, bool PG = false>
 __global__ void __launch_bounds__(256, PIPE ? 1 : 2)
 index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
-                  const void* __restrict__ k_scale, TS* __restrict__ scores) {
+                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg) {
+  static_assert(!PG || (QPW == 1 && TPW <= 128), "paged keys: decode shape, a wave's blocks in one lane each");
   static_assert(QK == CSA_BF16 || QK == CSA_FP8_E4M3, "MXFP4 keys use index_mfma_kernel");
   static_assert(TPW % 4 == 0 && TPW >= D, "scores leave four tiles at a time");
   static_assert(D == 4 || D == 8, "ring of four or eight slots");
@@ -402,6 +413,18 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   __shared__ __attribute__((aligned(16))) uint8_t ring6[D > 4 ? 4 : 1][D > 4 ? TB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ring7[D > 4 ? 4 : 1][D > 4 ? TB : 16];
 
+  // paged: lane i holds the physical block of the wave's i-th 32-entry
+  // block, loaded before anything else (the counter of loads in flight is in
+  // order, so waiting for it later does not wait for the queries); ids
+  // outside the pool, and blocks past the table, read block 0
+  [[maybe_unused]] int32_t my_blk = 0;
+  if constexpr (PG) {
+    const int64_t lb = (e_wave >> 5) + lane;
+    int32_t v = 0;
+    if (lane < TPW / 2 && lb < pg.max_blocks) v = pg.table[b * pg.max_blocks + lb];
+    my_blk = (v >= 0 && v < pg.n_pool) ? v : 0;
+  }
+
   // which entries each query sees (scalar arithmetic only)
   int64_t vis[QPW];
   int64_t vis_max = 0;
@@ -409,7 +432,8 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   for (int qi = 0; qi < QPW; ++qi) {
     int64_t t = t0 + qi;
     if (t >= T) t = T - 1;
-    int64_t v = (q_pos0 + t + 1) / ratio;
+    int64_t v = ((PG && pg.seq_pos) ? pg.seq_pos[b] : q_pos0 + t) + 1;
+    v /= ratio;
     if (v > N) v = N;
     vis[qi] = (t0 + qi < T) ? v : 0;
     vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
@@ -472,13 +496,22 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     constexpr int r = decltype(rc)::value;
     uint8_t* dst = slot(rc);
     const int64_t e0 = streams ? e_wave + 16 * t : N - 1;
-    const int rows = static_cast<int>(N - e0 < 16 ? N - e0 : 16);   // rows of this tile inside [0, N)
-    const uint8_t* base = k + (krow0 + e0) * RB;
+    int64_t srow;   // the tile's first row in the key array
+    int rows;       // rows of this tile that may be read
+    if constexpr (PG) {
+      const int32_t blk = __builtin_amdgcn_readlane(my_blk, streams ? (t >> 1) : 0);
+      srow = (static_cast<int64_t>(blk) << 5) + (streams ? (e0 & 31) : 0);
+      rows = 16;    // inside its block
+    } else {
+      srow = krow0 + e0;
+      rows = static_cast<int>(N - e0 < 16 ? N - e0 : 16);   // rows of this tile inside [0, N)
+    }
+    const uint8_t* base = k + srow * RB;
     wait_lgkm0();   // this wave's reads of the slot's previous tile are done
 #pragma unroll
     for (int j = 0; j < NI; ++j) buffer_load_lds16(base, rows * RB, dst + 1024 * j, voff[j]);
     if constexpr (QK == CSA_FP8_E4M3)   // the scale of this lane's key column
-      ks[r] = buffer_load_f32(static_cast<const float*>(k_scale) + krow0 + e0, rows * 4, col * 4);
+      ks[r] = buffer_load_f32(static_cast<const float*>(k_scale) + srow, rows * 4, col * 4);
   };
   // Every wave runs the whole ring, also one whose entries are all masked or
   // past N (its loads all read entry N - 1, its tiles are skipped and its
@@ -604,19 +637,20 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 }
 
-template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE>
+template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, bool PG = false>
 hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
   dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
             static_cast<uint32_t>((a.T + QPW - 1) / QPW), static_cast<uint32_t>(a.B));
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
+  const KeyPages pg{a.block_table, a.max_blocks, a.n_pool, a.seq_pos};
   if (a.score_dtype == CSA_BF16)
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
-                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores));
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, uint16_t, PG>), grid, dim3(256), 0, s, a.T,
+                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores), pg);
   else
-    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, float>), grid, dim3(256), 0, s, a.T, a.N,
-                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores));
+    hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, float, PG>), grid, dim3(256), 0, s, a.T,
+                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores), pg);
   return hipGetLastError();
 }
 
@@ -650,6 +684,7 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
     if (a.T <= 2) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
     return launch_mfma<QK, 2, 64, 4, 2>(a, s);
   } else {
+    if (a.block_table) return launch_ring<QK, 1, 32, 4, true, false, true>(a, s);   // paged decode (T = 1)
     if (a.T <= 2) return launch_ring<QK, 1, 32, 4, true, false>(a, s);
     return launch_ring<QK, 2, 64, 4, true, true>(a, s);
   }

@@ -39,6 +39,10 @@ struct IndexArgs {
   int qk_dtype;
   void* scores;
   int score_dtype;
+  // paged decode keys (NULL otherwise): k is a pool of 32-entry blocks
+  const int32_t* block_table = nullptr;
+  int64_t max_blocks = 0, n_pool = 0;
+  const int64_t* seq_pos = nullptr;
 };
 
 struct TopkArgs {
@@ -50,6 +54,7 @@ struct TopkArgs {
   void* ws;
   const int32_t* pool;   // pool mode: a selected slot j is written as pool[row][j] (-1 if outside 0..n_ent-1)
   int64_t n_ent;
+  const int64_t* seq_pos = nullptr;   // ragged decode: row b's position (T = 1)
 };
 
 struct IndexPoolArgs {

@@ -138,8 +138,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return block_exclusive_scan_t<uint32_t>(v, tmp, total);
 }
 
-__device__ __forceinline__ int64_t row_visible(int64_t t, int64_t q_pos0, int ratio, int64_t N) {
-  const int64_t v = (q_pos0 + t + 1) / ratio;
+// Candidates of score row `row` (query t = row % T of sequence row / T): the
+// entries visible to its position -- q_pos0 + t, or the sequence's own
+// position seq_pos[row / T] in a ragged decode batch.
+__device__ __forceinline__ int64_t row_visible(int64_t row, int64_t T, int64_t q_pos0, int ratio, int64_t N,
+                                               const int64_t* seq_pos) {
+  const int64_t pos = seq_pos ? seq_pos[row / T] : q_pos0 + row % T;
+  const int64_t v = (pos + 1) / ratio;
   return v < N ? v : N;
 }
 
@@ -193,7 +198,7 @@ __device__ __forceinline__ void emit_range(int64_t lo, int64_t hi, KT K, uint32_
 // ------------------------------------------------------------ LDS path
 template <typename KT>
 __global__ void __launch_bounds__(1024)
-topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT* __restrict__ scores,
+topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, const KT* __restrict__ scores,
                 int32_t* __restrict__ idx, const int32_t* __restrict__ pool, int64_t n_ent) {
   extern __shared__ uint8_t smem_raw[];
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw);           // kRangeBins (>= kBins)
@@ -201,7 +206,7 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const KT
   KT* keys = reinterpret_cast<KT*>(tmp + 32);
   const int64_t row = blockIdx.x;
   const int64_t t = row % T;
-  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
   const int32_t* prow = pool ? pool + row * N : nullptr;
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -342,7 +347,7 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
 
 template <int CPT>
 __global__ void __launch_bounds__(1024)
-topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const uint16_t* __restrict__ scores,
+topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, const uint16_t* __restrict__ scores,
                 int32_t* __restrict__ idx, const int32_t* __restrict__ pool, int64_t n_ent) {
   constexpr int NT = 1024;
   static_assert(8 * CPT * NT < 65536, "block-wide counts are packed in 16 bits");
@@ -350,7 +355,7 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const ui
   __shared__ uint32_t tmp[32];
   const int64_t row = blockIdx.x;
   const int64_t t = row % T;
-  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
   const int32_t* prow = pool ? pool + row * N : nullptr;
   const int tid = threadIdx.x;
@@ -542,13 +547,13 @@ __device__ void derive_state(const uint32_t* rowws, int np, uint32_t k, uint32_t
 
 template <typename KT>
 __global__ void __launch_bounds__(256)
-topk_hist_kernel(int pass, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_hist_kernel(int pass, int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                  const KT* __restrict__ scores, uint32_t* __restrict__ ws) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t st[4];
   const int64_t row = blockIdx.y;
   const int64_t t = row % T;
-  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   if (V <= k) return;
   uint32_t* rowws = ws + row * (kWsHist + 2 * S);
   KT prefix, mask;
@@ -574,13 +579,13 @@ topk_hist_kernel(int pass, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
 
 template <typename KT>
 __global__ void __launch_bounds__(256)
-topk_count_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_count_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                   const KT* __restrict__ scores, uint32_t* __restrict__ ws) {
   __shared__ uint32_t st[4];
   __shared__ uint32_t red[2][4];
   const int64_t row = blockIdx.y;
   const int64_t t = row % T;
-  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   if (V <= k) return;
   uint32_t* rowws = ws + row * (kWsHist + 2 * S);
   KT K, mask;
@@ -611,13 +616,13 @@ topk_count_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
 
 template <typename KT>
 __global__ void __launch_bounds__(256)
-topk_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                   const KT* __restrict__ scores, uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
   __shared__ uint32_t st[4];
   __shared__ uint32_t tmp[32];
   const int64_t row = blockIdx.y;
   const int64_t t = row % T;
-  const int64_t V = row_visible(t, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
   if (V <= k) {
     if (blockIdx.x == 0)
@@ -700,11 +705,11 @@ __device__ __forceinline__ void long_slice_range(int64_t V, int S, int64_t& lo, 
 
 template <int CPT>
 __global__ void __launch_bounds__(256)
-topk_long_hist1_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_long_hist1_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                        const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
   __shared__ uint32_t hist[kBins];
   const int64_t row = blockIdx.y;
-  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   if (V <= k) return;
   for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0;
   int64_t lo, hi;
@@ -724,13 +729,13 @@ topk_long_hist1_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, i
 
 template <int CPT>
 __global__ void __launch_bounds__(256)
-topk_long_hist2_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_long_hist2_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                        const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
   __shared__ uint32_t st[4];
   __shared__ uint32_t h2[32];
   __shared__ uint32_t above_s;
   const int64_t row = blockIdx.y;
-  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   if (V <= k) return;
   uint32_t* rws = ws + row * (kLongSlices + kSliceRec * S);
   int64_t lo, hi;
@@ -765,14 +770,14 @@ topk_long_hist2_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, i
 
 template <int CPT>
 __global__ void __launch_bounds__(256)
-topk_long_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, int S,
+topk_long_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
                        const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
   __shared__ uint32_t st[4];
   __shared__ uint32_t st2[4];
   __shared__ uint64_t tmp64[17];
   __shared__ uint32_t before[2];
   const int64_t row = blockIdx.y;
-  const int64_t V = row_visible(row % T, q_pos0, ratio, N);
+  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
   if (V <= k) {
     if (blockIdx.x == 0)
@@ -866,9 +871,9 @@ hipError_t launch_long(const TopkArgs& a, hipStream_t s) {
   const int64_t words = rows * per_row;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, s, ws, words);
   const dim3 grid(S, static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(topk_long_hist1_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws);
-  hipLaunchKernelGGL(topk_long_hist2_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws);
-  hipLaunchKernelGGL(topk_long_write_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc, ws,
+  hipLaunchKernelGGL(topk_long_hist1_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws);
+  hipLaunchKernelGGL(topk_long_hist2_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws);
+  hipLaunchKernelGGL(topk_long_write_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws,
                      a.idx);
   return hipGetLastError();
 }
@@ -884,11 +889,11 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
       const dim3 grid(static_cast<uint32_t>(rows));
       const auto* sc16 = static_cast<const uint16_t*>(a.scores);
       switch (cpt) {
-        case 1: hipLaunchKernelGGL(topk_reg_kernel<1>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
-        case 2: hipLaunchKernelGGL(topk_reg_kernel<2>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
-        case 3: hipLaunchKernelGGL(topk_reg_kernel<3>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
-        case 4: hipLaunchKernelGGL(topk_reg_kernel<4>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
-        default: hipLaunchKernelGGL(topk_reg_kernel<5>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 1: hipLaunchKernelGGL(topk_reg_kernel<1>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 2: hipLaunchKernelGGL(topk_reg_kernel<2>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 3: hipLaunchKernelGGL(topk_reg_kernel<3>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        case 4: hipLaunchKernelGGL(topk_reg_kernel<4>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc16, a.idx, a.pool, a.n_ent); break;
+        default: hipLaunchKernelGGL(topk_reg_kernel<5>, grid, dim3(1024), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc16, a.idx, a.pool, a.n_ent); break;
       }
       return hipGetLastError();
     }
@@ -896,7 +901,7 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
   if (topk_row_in_lds(a.N, a.score_dtype)) {
     const size_t smem = (kRangeBins + 32) * sizeof(uint32_t) + static_cast<size_t>(a.N) * sizeof(KT);
     hipLaunchKernelGGL((topk_lds_kernel<KT>), dim3(static_cast<uint32_t>(rows)), dim3(1024), smem, s, a.T,
-                       a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, a.pool, a.n_ent);
+                       a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, sc, a.idx, a.pool, a.n_ent);
     return hipGetLastError();
   }
   if constexpr (sizeof(KT) == 2) {
@@ -917,11 +922,11 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
                      words);
   const dim3 grid(S, static_cast<uint32_t>(rows));
   for (int p = 0; p < Digits<KT>::n; ++p)
-    hipLaunchKernelGGL((topk_hist_kernel<KT>), grid, dim3(256), 0, s, p, a.T, a.N, a.q_pos0, a.ratio, a.k, S,
+    hipLaunchKernelGGL((topk_hist_kernel<KT>), grid, dim3(256), 0, s, p, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S,
                        sc, ws);
-  hipLaunchKernelGGL((topk_count_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc,
+  hipLaunchKernelGGL((topk_count_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc,
                      ws);
-  hipLaunchKernelGGL((topk_write_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.k, S, sc,
+  hipLaunchKernelGGL((topk_write_kernel<KT>), grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc,
                      ws, a.idx);
   return hipGetLastError();
 }

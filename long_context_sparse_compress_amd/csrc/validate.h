@@ -340,6 +340,51 @@ inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t
   return k;
 }
 
+// Paged decode indexer / Top-k (heterogeneous cache): one query per sequence
+// at seq_pos[b], index keys in a pool of 32-entry blocks under a block table.
+inline Check check_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, const void* q, const void* q_scale,
+                               const float* w, const void* kpool, const void* kscale, int64_t n_pool,
+                               const int32_t* table, const int64_t* seq_pos, int qk_dtype, const void* scores,
+                               int score_dtype) {
+  Check k;
+  if (B < 0) { k.fail(CSA_ERR_INVALID_ARG, "B must be >= 0"); return k; }
+  if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
+  if (H_I != CSA_INDEX_HEADS || d_I != CSA_INDEX_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "indexer shape must be H_I=64, d_I=128"); return k; }
+  if (qk_dtype != CSA_BF16 && qk_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "paged keys are bf16 or fp8 E4M3"); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (B > 0 && n_pool < 1) { k.fail(CSA_ERR_INVALID_ARG, "the key pool holds no block"); return k; }
+  if (B * max_blocks * 32 > (int64_t{1} << 40)) { k.fail(CSA_ERR_INVALID_ARG, "B * max_blocks too large"); return k; }
+  const bool empty = B == 0;
+  const bool fp8 = qk_dtype == CSA_FP8_E4M3;
+  k.ptr(q, "q", !empty) && k.ptr(w, "w", !empty) && k.ptr(kpool, "k_pool", !empty) &&
+      k.ptr(table, "block_table", !empty) && k.ptr(seq_pos, "seq_pos", !empty) && k.ptr(scores, "scores", !empty);
+  if (!k.ok()) return k;
+  if (fp8) {
+    k.ptr(q_scale, "q_scale", !empty) && k.ptr(kscale, "k_scale", !empty);
+  } else {
+    k.must_be_null(q_scale, "q_scale", "for bf16") && k.must_be_null(kscale, "k_scale", "for bf16");
+  }
+  return k;
+}
+
+inline Check check_topk_paged(int64_t B, int64_t N, const int64_t* seq_pos, int ratio, int kk, const void* scores,
+                              int score_dtype, const void* idx, const void* ws, size_t ws_bytes) {
+  Check k;
+  if (B < 0 || N < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and N must be >= 0"); return k; }
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (kk < 1 || kk > CSA_MAX_TOPK) { k.fail(CSA_ERR_INVALID_ARG, "k must be in [1, 2048], got " + i2s(kk)); return k; }
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  const bool empty = B == 0;
+  k.ptr(scores, "scores", !empty && N > 0) && k.ptr(idx, "idx", !empty) && k.ptr(seq_pos, "seq_pos", !empty);
+  if (!k.ok()) return k;
+  const size_t need = topk_workspace_bytes(B, 1, N, score_dtype);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "topk_select_paged needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
+    k.ptr(ws, "workspace");
+  }
+  return k;
+}
+
 // Paged decode attention (heterogeneous cache): one query per sequence at
 // seq_pos[b], compressed entries through a block table, the window from a ring.
 inline Check check_paged(bool sparse, int64_t B, int kk, int H, int d, const void* q, const void* kv_pool,

@@ -32,6 +32,7 @@ def test_header_symbols_exported(lib):
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
                           "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
+                          "lightning_index_paged", "topk_select_paged",
                           "csa_workspace_bytes",
                           "csa_last_error", "csa_version"}
     for n in names:
@@ -322,3 +323,29 @@ def test_paged_validation(lib):
     assert h_(wsp=None) == -4
     assert h_(sink=MIS) == -1
     assert s_(B=0, wsp=None, tbl=None, sp_=None, idx=None) == 0
+
+
+def test_paged_index_topk_validation(lib):
+    ip, tp = lib.lightning_index_paged, lib.topk_select_paged
+
+    def ix(B=4, mb=8, H=64, dt=1, qs=None, ks=None, npool=10, tbl=A, sp_=A, sd=1):
+        return ip(B, mb, H, 128, A, qs, A, A, ks, npool, tbl, sp_, dt, A, sd, None)
+
+    assert ix(H=32) == -2
+    assert ix(dt=3) == -2 and "bf16 or fp8" in _err(lib)
+    assert ix(dt=2) == -1 and "q_scale" in _err(lib)
+    assert ix(dt=1, qs=A) == -1 and "must be NULL" in _err(lib)
+    assert ix(npool=0) == -1 and "no block" in _err(lib)
+    assert ix(mb=0) == -1
+    assert ix(tbl=None) == -1 and "block_table" in _err(lib)
+    assert ix(sp_=None) == -1 and "seq_pos" in _err(lib)
+    assert ix(B=0, tbl=None, sp_=None, npool=0) == 0
+
+    def tk(B=4, N=1024, k=16, sp_=A, ratio=4, ws=None, wsb=0):
+        return tp(B, N, sp_, ratio, k, A, 1, A, ws, wsb, None)
+
+    assert tk(ratio=3) == -1
+    assert tk(k=0) == -1
+    assert tk(sp_=None) == -1 and "seq_pos" in _err(lib)
+    assert tk(N=262144) == -4            # long rows need a workspace
+    assert tk(B=0, sp_=None) == 0

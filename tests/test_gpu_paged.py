@@ -173,3 +173,121 @@ def test_paged_equals_contiguous_bits():
     p = csa.hca_attn_paged(q[:, 0], poolh, dev(permh, torch.int32), ring, sp, sink=sink)
     torch.cuda.synchronize()
     assert torch.equal(a[:, 0], p)
+
+
+# ---------------------------------------------------------------- indexer / Top-k over paged keys
+
+from oracle import indexer as oi  # noqa: E402
+from oracle import numerics as on  # noqa: E402
+from oracle import topk as ot  # noqa: E402
+from helpers import index_close  # noqa: E402
+
+IDX_POS = [4095, 9000, 65535, 70001, 131071, 333, 12345, 2]
+
+
+def _key_pool(name, seq_pos, fp8):
+    """bf16 keys (or their E4M3 codes + row scales) for every sequence's
+    visible entries, shuffled 32-entry blocks, -1 past each sequence."""
+    B = len(seq_pos)
+    nblk = [(p + 1) // 128 + 1 for p in seq_pos]
+    max_blocks = max(nblk) + 1
+    n_pool = sum(nblk) + 3
+    g = np.random.default_rng(zlib.crc32(name.encode()))
+    perm = g.permutation(n_pool)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    keys = synth.round_bf16(synth.normal(name + ".k", (n_pool, 32, 128)))
+    if fp8:
+        codes, scale = synth.quant_fp8_rows(keys)
+        return dev(codes, torch.uint8), dev(scale), on.dequant_fp8_rows(codes, scale), table
+    return dev(keys, BF), None, keys, table
+
+
+def _queries(name, B, fp8):
+    q = synth.normal(name + ".q", (B, 64, 128), var=1.0 if fp8 else 1.0 / 128)
+    w = synth.uniform(name + ".w", (B, 64))
+    if fp8:
+        qc, qs = synth.quant_fp8_rows(q)
+        return dev(qc, torch.uint8), dev(qs), on.dequant_fp8_rows(qc, qs), w
+    qb = synth.round_bf16(q)
+    return dev(qb, BF), None, qb, w
+
+
+def _oracle_scores(qv, w, keys_host, table, seq_pos):
+    """Per sequence: the indexer oracle over the entries gathered from the pool."""
+    out = []
+    for b, pos in enumerate(seq_pos):
+        vis = (pos + 1) // 4
+        kb = occ.paged_entries(keys_host, table[b], vis, 32) if vis else np.zeros((0, 128))
+        out.append(oi.index_scores(qv[b][None, None], w[b][None, None], kb[None], pos, 4)[0, 0])
+    return out
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_paged_indexer_and_topk(fp8):
+    """Ragged positions (2 .. 131,071, one with no visible entry), shuffled
+    blocks, bf16 and fp8 keys: scores against the oracle, -inf past each
+    sequence, and Top-k on the same scores equal to the oracle's selection."""
+    B, K = len(IDX_POS), 512
+    kp, ks, keys_host, table = _key_pool(f"pg.ix{int(fp8)}", IDX_POS, fp8)
+    q, qs, qv, w = _queries(f"pg.ix{int(fp8)}", B, fp8)
+    sp = torch.tensor(IDX_POS, dtype=torch.int64, device="cuda")
+    s = csa.lightning_index_paged(q, dev(w), kp, dev(table, torch.int32), sp, q_scale=qs, k_scale=ks,
+                                  score_dtype=torch.float32)
+    idx = csa.topk_select_paged(s, K, sp)
+    torch.cuda.synchronize()
+    hs, hi = host(s), host(idx)
+    ref = _oracle_scores(qv, w, keys_host, table, IDX_POS)
+    for b, pos in enumerate(IDX_POS):
+        vis = (pos + 1) // 4
+        if vis:
+            index_close(hs[b, :vis][None], ref[b][None])
+        assert np.all(np.isneginf(hs[b, vis:]))
+        want = np.sort(ot.select_row(hs[b], vis, K))
+        want = np.concatenate([want[want >= 0], want[want < 0]])
+        assert np.array_equal(hi[b], want), b
+
+
+def test_paged_decode_chain_against_the_oracle_chain():
+    """The whole CSA decode step on the paged cache -- indexer over paged bf16
+    keys, Top-k per sequence, sparse MQA over paged latents and the window
+    ring -- against the oracle's own chain on the gathered data.  Selections
+    may differ only between entries whose oracle scores tie within 1e-3; the
+    attention is compared where the selections agree."""
+    B, K, ring = len(IDX_POS), 512, 256
+    kp, _, keys_host, table = _key_pool("pg.chain", IDX_POS, False)
+    q_i, _, qv, w = _queries("pg.chain", B, False)
+    pool = synth.device_normal("pg.chain.kv", (kp.shape[0], 32, 512), BF)
+    win = synth.device_normal("pg.chain.win", (B, ring, 512), BF)
+    q = synth.device_normal("pg.chain.q", (B, 64, 512), BF)
+    dt = dev(table, torch.int32)
+    sp = torch.tensor(IDX_POS, dtype=torch.int64, device="cuda")
+    s = csa.lightning_index_paged(q_i, dev(w), kp, dt, sp, score_dtype=torch.float32)
+    idx = csa.topk_select_paged(s, K, sp)
+    out = csa.sparse_mqa_attn_paged(q, pool, dt, idx, win, sp)
+    torch.cuda.synchronize()
+    hi, got = host(idx), host(out)
+    ref_scores = _oracle_scores(qv, w, keys_host, table, IDX_POS)
+    agree = 0
+    for b, pos in enumerate(IDX_POS):
+        vis = (pos + 1) // 4
+        so = ref_scores[b]
+        osel = ot.select_row(so, vis, K)
+        oset, gset = set(int(e) for e in osel if e >= 0), set(int(e) for e in hi[b] if e >= 0)
+        if oset != gset:
+            kth = np.sort(so[:vis])[::-1][min(K, vis) - 1]
+            for e in oset ^ gset:
+                assert abs(so[e] - kth) <= 1e-3 * abs(kth), (b, e)
+            continue
+        agree += 1
+        sel = np.array(sorted(oset), dtype=np.int64)
+        rows = occ.paged_entries(host(pool), table[b], int(sel.max()) + 1, 32)[sel] if len(sel) else \
+            np.zeros((0, 512))
+        rw, w0 = _window(win[b], pos)
+        o, _ = oa.sparse_mqa(host(q[b])[None, None], rows[None], np.arange(len(sel))[None, None], rw[None], w0,
+                             pos, 128)
+        _assert_bf16(got[b], o[0, 0])
+    assert agree >= B - 1
