@@ -26,8 +26,9 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
                  positions (49,152 .. 81,919; mean about 65,536), their C4A and
                  C128A entries in shuffled 128-raw-token blocks of two pools
                  under block tables, the window in 256-row rings: the paged
-                 indexer over bf16 keys, Top-k per sequence, sparse MQA over
-                 the top-512 and HCA with sink, one query per sequence
+                 compressor write of every sequence's block (latent and key),
+                 the paged indexer over bf16 keys, Top-k per sequence, sparse
+                 MQA over the top-512 and HCA with sink, one query per sequence
   hbm_copy       a 1 GiB copy, the calibration point of the HBM byte counters
 """
 from __future__ import annotations
@@ -268,7 +269,18 @@ def run(args, torch, csa, synth):
         idx2 = torch.empty(B, k, dtype=torch.int32, device="cuda")
         ws_t = torch.empty(max(16, csa.workspace_bytes(csa.OP_TOPK, B, 1, Nmax, k)), dtype=torch.uint8,
                            device="cuda")
+        # the decode write: every sequence's current block (the most a step does)
+        p0 = torch.tensor([p - p % 4 for p in seq], dtype=torch.int64, device="cuda")
+        rb = {nm: dn(f"g.rb.{nm}", (B, 4, 512), bf) for nm in ("Ca", "Za", "pCb", "pZb")}
+        rbk = {nm: dn(f"g.rbk.{nm}", (B, 4, 128), bf) for nm in ("Ca", "Za", "pCb", "pZb")}
+        b4, b4k = dn("g.b4", (8, 512), var=0.1), dn("g.b4k", (8, 128), var=0.1)
         stages = [
+            ("compress_paged_kv", lambda: csa.csa_compress_paged(4, rb["Ca"], rb["Za"], b4, pool4, table, p0,
+                                                                 prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
+             B * 12 * 512 * 2 + B * 512 * 2 + 8 * 512 * 4, 0, "hbm"),
+            ("compress_paged_keys", lambda: csa.csa_compress_paged(4, rbk["Ca"], rbk["Za"], b4k, kpool, table, p0,
+                                                                   prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"]),
+             B * 12 * 128 * 2 + B * 128 * 2 + 8 * 128 * 4, 0, "hbm"),
             ("lightning_index_paged", lambda: csa.lightning_index_paged(qi, wi, kpool, table, sp, scores=scores),
              vis4 * 256 + B * 64 * 128 * 2 + B * 64 * 4 + B * Nmax * 2, vis4 * 64 * 128 * 2, "hbm"),
             ("topk_select_paged", lambda: csa.topk_select_paged(scores, k, sp, idx=idx2, workspace=ws_t),

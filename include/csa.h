@@ -16,8 +16,8 @@
  * same operations with partial RoPE fused in, and the batch-invariant
  * attention mode), csa_rope (partial RoPE on query or window rows), and
  * lightning_index_pool / topk_select_pool (the hierarchical indexer), and
- * lightning_index_paged / topk_select_paged / sparse_mqa_attn_paged /
- * hca_attn_paged (decode over the paged cache).
+ * csa_compress_paged / lightning_index_paged / topk_select_paged /
+ * sparse_mqa_attn_paged / hca_attn_paged (decode over the paged cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -408,6 +408,35 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
  *  rope_dims, rope_base, workspace: as sparse_mqa_attn_ex / hca_attn_ex with
  *  T = 1 (workspace per csa_workspace_bytes(op, B, 1, ...)).
  */
+/*
+ * csa_compress_paged -- the decode step's compressor write into the paged
+ * cache: one block per sequence, each at its own position.
+ *
+ * "DeepSeek V4 结构速览" (C4A Compressor: at decode the previous block is the
+ * latest complete block and the current block the rolling buffer) and
+ * "DeepSeek-V4技术报告解读，全适配国产算力" (3.2, classical blocks of 128 raw
+ * tokens).  Sequence b pools the block of raw tokens pos0[b] .. pos0[b] +
+ * ratio - 1 exactly as csa_compress_ex does for a one-block chunk (RMSNorm,
+ * optional RoPE at pos0[b] + rope_anchor, optional fp8 quantize-on-write) and
+ * writes entry e = pos0[b] / ratio to slot e % 32 of block
+ * block_table[b][e / 32] of pool [n_pool, 32, c] (C4A), or to block
+ * block_table[b][e] of pool [n_pool, c] (C128A).  A sequence whose pos0 is
+ * negative or not a multiple of ratio, or whose block is outside
+ * [0, n_pool) or past max_blocks, writes nothing.
+ *  pos0        [B] int64 (device)
+ *  Ca, Za      [B, ratio, c] in_dtype: the rolling buffer (current block)
+ *  prev_Cb/_Zb [B, 4, c] (C4A): the previous block's rows; not read for a
+ *              sequence at pos0 0.  NULL for C128A.
+ *  bias, gamma, eps, in_dtype, out_dtype, rope_*: as csa_compress_ex;
+ *  scale_pool  [n_pool, 32] fp32 for CSA_FP8_E4M3 output, else NULL.
+ */
+int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca,
+                       const void* Za, const void* prev_Cb, const void* prev_Zb,
+                       const float* bias, const float* gamma, float eps, int in_dtype,
+                       int out_dtype, void* pool, float* scale_pool, int64_t n_pool,
+                       const int32_t* block_table, int64_t max_blocks, int rope_dims,
+                       float rope_base, int rope_anchor, void* stream);
+
 /*
  * lightning_index_paged / topk_select_paged -- the decode indexer and Top-k
  * over the heterogeneous cache (the same operations as lightning_index and

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
-           "rope", "lightning_index_pool", "topk_select_pool", "lightning_index_paged", "topk_select_paged",
+           "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "lightning_index_paged",
+           "topk_select_paged",
            "sparse_mqa_attn_paged", "hca_attn_paged",
            "workspace_bytes", "library", "F32", "BF16",
            "FP8_E4M3", "MXFP4", "CsaError"]
@@ -38,6 +39,8 @@ _SIGS = {
     "csa_compress_ex": [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
                         _int, _int, _vp, _i64, _vp, _int, _f32, _int, _vp, _sz, _vp],
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
+    "csa_compress_paged": [_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int, _int, _vp, _vp, _i64,
+                           _vp, _i64, _int, _f32, _int, _vp],
     "lightning_index_paged": [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _int,
                               _vp],
     "topk_select_paged": [_i64, _i64, _vp, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
@@ -362,6 +365,21 @@ def _paged_common(q, seq_pos, max_pos, out, lse, return_lse, workspace, batch_in
     else:
         ws, wsb = _workspace(op, B, 1, 1, 0, q.device, workspace)
     return B, max_pos, out, lse, ws, wsb
+
+
+def csa_compress_paged(ratio, Ca, Za, bias, pool, block_table, pos0, *, prev_Cb=None, prev_Zb=None, gamma=None,
+                       eps=1e-6, scale_pool=None, rope_dims=0, rope_base=ROPE_BASE, rope_anchor=0, stream=None):
+    """Decode write into the paged cache: sequence b pools its block starting at
+    pos0[b] (int64 [B]) from the rolling buffer Ca, Za [B, ratio, c] (and, C4A, the
+    previous block prev_Cb, prev_Zb [B, 4, c]) into its page slot of ``pool``
+    ([n_pool, 32, c] C4A, [n_pool, c] C128A; uint8 for fp8 keys with ``scale_pool``)."""
+    B, _, c = Ca.shape
+    st = library().csa_compress_paged(ratio, B, c, _ptr(pos0), _ptr(Ca), _ptr(Za), _ptr(prev_Cb), _ptr(prev_Zb),
+                                      _ptr(bias), _ptr(gamma), eps, _dt(Ca), _out_dt(pool), _ptr(pool),
+                                      _ptr(scale_pool), pool.shape[0], _ptr(block_table), block_table.shape[1],
+                                      rope_dims, rope_base, rope_anchor, _stream(stream))
+    _check(st, "csa_compress_paged")
+    return pool
 
 
 def lightning_index_paged(q, w, k_pool, block_table, seq_pos, *, qk_dtype=None, q_scale=None, k_scale=None,

@@ -371,6 +371,37 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
                                        out_scale, scale_stride);
 }
 
+// The rolling-buffer write of a decode step into the heterogeneous cache's
+// pages ("DeepSeek V4 结构速览": at decode the previous block is the latest
+// complete one, the current block the rolling buffer; "DeepSeek-V4技术报告解读"
+// 3.2: compressed entries live in blocks of 128 raw tokens).  Workgroup b
+// pools sequence b's block starting at pos0s[b] into entry pos0s[b] / RATIO,
+// slot (e % 32 for C4A) of its physical block table[b][e / (32 or 1)].  A
+// sequence whose position is not a block start, or whose block is absent,
+// writes nothing (the whole workgroup returns before any barrier).
+template <typename TI, typename TO, int RATIO>
+__global__ void __launch_bounds__(kCompressThreads<RATIO>)
+compress_paged_kernel(int c, const int64_t* __restrict__ pos0s, const TI* __restrict__ Ca,
+                      const TI* __restrict__ Za, const TI* __restrict__ pCb, const TI* __restrict__ pZb,
+                      const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
+                      TO* __restrict__ pool, float* __restrict__ scale_pool, int64_t n_pool,
+                      const int32_t* __restrict__ table, int64_t max_blocks, int G, int rope_R, double rope_l2b,
+                      int rope_anchor) {
+  constexpr int SH = RATIO == 4 ? 5 : 0;   // log2 entries per block
+  const int64_t b = blockIdx.y;
+  const int64_t p0 = pos0s[b];
+  if (p0 < 0 || p0 % RATIO) return;
+  const int64_t e = p0 / RATIO;
+  if ((e >> SH) >= max_blocks) return;
+  const int64_t blk = table[b * max_blocks + (e >> SH)];
+  if (blk < 0 || blk >= n_pool) return;
+  const int64_t row = (blk << SH) + (e & ((int64_t{1} << SH) - 1));
+  // entry 0 of a one-block chunk whose output row is `row` (no batch stride)
+  compress_entry<TI, TO, RATIO, false>(0, b, 0, 1, RATIO, c, p0, Ca, Za, nullptr, nullptr, pCb, pZb, bias, gamma,
+                                       eps, pool + row * c, 0, G, nullptr, rope_R, rope_l2b, rope_anchor,
+                                       scale_pool ? scale_pool + row : nullptr, 0);
+}
+
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
 // picks the job); a job's workgroups past its own grid return at once.
 struct CompressJobDev {
@@ -572,6 +603,41 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.in_dtype == CSA_F32)
     return a.out_dtype == CSA_F32 ? launch_r<float, float>(a, s) : launch_r<float, uint16_t>(a, s);
   return a.out_dtype == CSA_F32 ? launch_r<uint16_t, float>(a, s) : launch_r<uint16_t, uint16_t>(a, s);
+}
+
+namespace {
+
+template <typename TI, typename TO, int RATIO>
+hipError_t launch_paged_t(const CompressPagedArgs& a, hipStream_t s) {
+  constexpr int VEC = Vec<TI>::n;
+  constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
+  const int CT = static_cast<int>(a.c / VEC);
+  const int max_threads = a.B >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
+  int G = 1;
+  while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
+  const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64 * sizeof(float);
+  const double l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
+  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO>), dim3(1, static_cast<uint32_t>(a.B)), dim3(CT * G),
+                     smem, s, static_cast<int>(a.c), a.pos0, static_cast<const TI*>(a.Ca),
+                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.prev_Cb),
+                     static_cast<const TI*>(a.prev_Zb), a.bias, a.gamma, a.eps, static_cast<TO*>(a.pool),
+                     a.scale_pool, a.n_pool, a.block_table, a.max_blocks, G, a.rope_dims, l2b, a.rope_anchor);
+  return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t launch_paged_i(const CompressPagedArgs& a, hipStream_t s) {
+  if (a.out_dtype == CSA_FP8_E4M3) return launch_paged_t<TI, uint8_t, 4>(a, s);   // C4A keys (validated)
+  if (a.ratio == 4)
+    return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 4>(a, s) : launch_paged_t<TI, uint16_t, 4>(a, s);
+  return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 128>(a, s) : launch_paged_t<TI, uint16_t, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_compress_paged(const CompressPagedArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  return a.in_dtype == CSA_F32 ? launch_paged_i<float>(a, s) : launch_paged_i<uint16_t>(a, s);
 }
 
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s) {

@@ -28,6 +28,27 @@ struct CompressArgs {
   float* out_scale;  // fp8 output: the scale of entry i of sequence b at out_scale[b * (stride / c) + i]
 };
 
+// The decode write of one block per sequence into the paged cache.
+struct CompressPagedArgs {
+  int ratio;
+  int64_t B, c;
+  const int64_t* pos0;          // [B] block start of each sequence's block
+  const void *Ca, *Za;          // [B, ratio, c]: the rolling buffer
+  const void *prev_Cb, *prev_Zb;  // [B, 4, c]: the previous block (C4A)
+  const float* bias;
+  const float* gamma;
+  float eps;
+  int in_dtype, out_dtype;
+  void* pool;                   // [n_pool, 32, c] (C4A) or [n_pool, c] (C128A)
+  float* scale_pool;            // fp8: [n_pool, 32]
+  int64_t n_pool;
+  const int32_t* block_table;   // [B, max_blocks]
+  int64_t max_blocks;
+  int rope_dims;
+  float rope_base;
+  int rope_anchor;
+};
+
 struct IndexArgs {
   int64_t B, T, N, q_pos0;
   int ratio;
@@ -108,6 +129,7 @@ struct RopeArgs {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 // up to 4 jobs of one ratio and dtype pair, one launch
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s);
+hipError_t launch_compress_paged(const CompressPagedArgs& a, hipStream_t s);
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);

@@ -340,6 +340,43 @@ inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t
   return k;
 }
 
+inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,
+                                  const void* pCb, const void* pZb, const float* bias, const float* gamma, float eps,
+                                  int in_dtype, int out_dtype, const void* pool, const float* scale_pool,
+                                  int64_t n_pool, const int32_t* table, int64_t max_blocks, int rope_dims,
+                                  float rope_base, int rope_anchor) {
+  Check k;
+  if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
+  if (B < 0) { k.fail(CSA_ERR_INVALID_ARG, "B must be >= 0"); return k; }
+  if (c <= 0 || c % 64 != 0 || c > 1024) { k.fail(CSA_ERR_INVALID_ARG, "c must be a positive multiple of 64, at most 1024, got " + i2s(c)); return k; }
+  if (!check_rope(k, rope_dims, rope_base, c)) return k;
+  if (rope_anchor < 0 || rope_anchor >= ratio) { k.fail(CSA_ERR_INVALID_ARG, "rope_anchor must be in [0, ratio), got " + i2s(rope_anchor)); return k; }
+  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16 or CSA_FP8_E4M3"); return k; }
+  if (out_dtype == CSA_FP8_E4M3 && ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "fp8 output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
+  if (!(eps > 0.0f) || !std::isfinite(eps)) { k.fail(CSA_ERR_INVALID_ARG, "eps must be positive and finite"); return k; }
+  if (n_pool < 0) { k.fail(CSA_ERR_INVALID_ARG, "n_pool must be >= 0"); return k; }
+  if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
+  if (B > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B must be below 2^31"); return k; }
+  const bool empty = B == 0;
+  k.ptr(pos0, "pos0", !empty) && k.ptr(Ca, "Ca", !empty) && k.ptr(Za, "Za", !empty) && k.ptr(bias, "bias", !empty) &&
+      k.ptr(gamma, "gamma", false) && k.ptr(pool, "pool", !empty && n_pool > 0) && k.ptr(table, "block_table", !empty);
+  if (!k.ok()) return k;
+  if (ratio == 4) {
+    k.ptr(pCb, "prev_Cb", !empty) && k.ptr(pZb, "prev_Zb", !empty);
+  } else {
+    k.must_be_null(pCb, "prev_Cb", "for ratio 128") && k.must_be_null(pZb, "prev_Zb", "for ratio 128");
+  }
+  if (!k.ok()) return k;
+  if (out_dtype == CSA_FP8_E4M3) {
+    if (!scale_pool && !empty && n_pool > 0) { k.fail(CSA_ERR_INVALID_ARG, "scale_pool is NULL"); return k; }
+  } else if (scale_pool) {
+    k.fail(CSA_ERR_INVALID_ARG, "scale_pool must be NULL unless out_dtype is CSA_FP8_E4M3");
+    return k;
+  }
+  return k;
+}
+
 // Paged decode indexer / Top-k (heterogeneous cache): one query per sequence
 // at seq_pos[b], index keys in a pool of 32-entry blocks under a block table.
 inline Check check_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, const void* q, const void* q_scale,

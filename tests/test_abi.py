@@ -32,7 +32,7 @@ def test_header_symbols_exported(lib):
     assert set(names) >= {"csa_compress", "lightning_index", "topk_select", "sparse_mqa_attn",
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
                           "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
-                          "lightning_index_paged", "topk_select_paged",
+                          "lightning_index_paged", "topk_select_paged", "csa_compress_paged",
                           "csa_workspace_bytes",
                           "csa_last_error", "csa_version"}
     for n in names:
@@ -349,3 +349,23 @@ def test_paged_index_topk_validation(lib):
     assert tk(sp_=None) == -1 and "seq_pos" in _err(lib)
     assert tk(N=262144) == -4            # long rows need a workspace
     assert tk(B=0, sp_=None) == 0
+
+
+def test_compress_paged_validation(lib):
+    cp = lib.csa_compress_paged
+
+    def c_(ratio=4, B=4, c=512, od=1, sc=None, pc=A, npool=10, mb=8, tbl=A, p0=A, ra=0):
+        return cp(ratio, B, c, p0, A, A, pc, pc, A, None, 1e-6, 1, od, A, sc, npool, tbl, mb, 0, 10000.0, ra, None)
+
+    assert c_(ratio=8) == -1
+    assert c_(c=100) == -1
+    assert c_(od=2) == -1 and "scale_pool" in _err(lib)
+    assert c_(od=2, sc=A, ratio=128, pc=None) == -2
+    assert c_(od=1, sc=A) == -1 and "scale_pool must be NULL" in _err(lib)
+    assert c_(pc=None) == -1 and "prev_Cb" in _err(lib)
+    assert c_(ratio=128) == -1 and "must be NULL" in _err(lib)
+    assert c_(mb=0) == -1
+    assert c_(tbl=None) == -1 and "block_table" in _err(lib)
+    assert c_(p0=None) == -1 and "pos0" in _err(lib)
+    assert c_(ra=4) == -1 and "rope_anchor" in _err(lib)
+    assert c_(npool=0) == 0 and c_(B=0, p0=None, tbl=None) == 0      # nothing to write

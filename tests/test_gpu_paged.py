@@ -291,3 +291,81 @@ def test_paged_decode_chain_against_the_oracle_chain():
                              pos, 128)
         _assert_bf16(got[b], o[0, 0])
     assert agree >= B - 1
+
+
+# ---------------------------------------------------------------- the rolling-buffer write into pages
+
+from oracle import compressor as oc  # noqa: E402
+
+
+@pytest.mark.parametrize("ratio,c,out", [(4, 512, "bf16"), (4, 128, "fp8"), (128, 512, "bf16"), (4, 192, "f32")])
+def test_compress_paged_decode_write(ratio, c, out):
+    """Sequences at different positions pool their current block into their
+    own page slot; sequences not at a block start (and one whose block is
+    absent) write nothing; every other slot of the pool is left alone."""
+    per = 32 if ratio == 4 else 1
+    pos = [4 * 1000, 128 * 7, 0, 65532, 77, 4 * 4095] if ratio == 4 else [128 * 7, 0, 128 * 8191, 130, 128 * 300]
+    B = len(pos)
+    nblk = [p // 128 + 1 for p in pos]
+    max_blocks = max(nblk) + 1
+    n_pool = sum(nblk) + 2
+    g = np.random.default_rng(zlib.crc32(f"cp{ratio}{c}{out}".encode()))
+    perm = g.permutation(n_pool)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    absent = 1
+    e_abs = pos[absent] // ratio
+    table[absent, e_abs // per] = -1             # this sequence's block is not mapped
+    dtype = "f32" if out == "f32" else "bf16"
+    tdt = torch.float32 if dtype == "f32" else BF
+    inp = {}
+    for b, p in enumerate(pos):
+        p0 = p - p % ratio
+        inp[b] = synth.compressor_inputs(f"cp.{ratio}.{c}.{b}", 1, ratio, c, ratio, p0 if p0 else 0, dtype=dtype)
+    Ca = np.concatenate([inp[b]["Ca"] for b in range(B)])
+    Za = np.concatenate([inp[b]["Za"] for b in range(B)])
+    bias = inp[0]["bias"]
+    if ratio == 4:
+        pC = np.concatenate([inp[b].get("prev_Cb", np.zeros((1, 4, c), np.float32)) for b in range(B)])
+        pZ = np.concatenate([inp[b].get("prev_Zb", np.zeros((1, 4, c), np.float32)) for b in range(B)])
+    shape = (n_pool, per, c) if per > 1 else (n_pool, c)
+    if out == "fp8":
+        pool = torch.full(shape, 0x33, dtype=torch.uint8, device="cuda")
+        spool = torch.full((n_pool, per), 5.0, dtype=torch.float32, device="cuda")
+    else:
+        pool = torch.full(shape, 3.0, dtype=torch.float32 if out == "f32" else BF, device="cuda")
+        spool = None
+    before = pool.clone()
+    csa.csa_compress_paged(ratio, dev(Ca, tdt), dev(Za, tdt), dev(bias), pool, dev(table, torch.int32),
+                           torch.tensor(pos, dtype=torch.int64, device="cuda"),
+                           prev_Cb=dev(pC, tdt) if ratio == 4 else None, prev_Zb=dev(pZ, tdt) if ratio == 4 else None,
+                           scale_pool=spool, rope_dims=64, rope_anchor=ratio - 1)
+    torch.cuda.synchronize()
+    hp, hb = host(pool), host(before)
+    written = np.zeros(hp.shape[:2] if per > 1 else hp.shape[:1], dtype=bool)
+    for b, p in enumerate(pos):
+        if p % ratio or b == absent:
+            continue
+        e = p // ratio
+        blk = table[b, e // per]
+        slot = (blk, e % per) if per > 1 else (blk,)
+        written[slot] = True
+        ib = inp[b]
+        # one bias for the call (sequence 0's), as the kernel got it
+        ref = oc.compress(ib["Ca"], ib["Za"], bias, ratio, ib["Cb"], ib["Zb"],
+                          ib.get("prev_Cb") if p else None, ib.get("prev_Zb") if p else None, pos0=p,
+                          rope_dims=64, rope_anchor=ratio - 1)[0, 0] if ratio == 4 else \
+            oc.compress(ib["Ca"], ib["Za"], bias, 128, pos0=p, rope_dims=64, rope_anchor=127)[0, 0]
+        got = hp[slot]
+        if out == "fp8":
+            dec = on.decode_e4m3(got) * host(spool)[slot]
+            assert np.max(np.abs(dec - ref)) <= np.abs(ref).max() / 448 * 16 + 1e-4
+        elif out == "f32":
+            assert np.max(np.abs(got - ref)) < 1e-4
+        else:
+            assert np.max(np.abs(got - ref)) < 2e-2
+    assert written.sum() == sum(1 for b, p in enumerate(pos) if p % ratio == 0 and b != absent)
+    assert np.array_equal(hp[~written], hb[~written])
