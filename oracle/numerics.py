@@ -122,3 +122,37 @@ def quant_fp8_rows_f32(y: np.ndarray):
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     v = (y / scale[..., None]).astype(np.float32)
     return encode_e4m3(v), scale
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """Values -> E2M1 nibbles: the nearest of the 8 magnitudes, ties to the
+    code with an even mantissa, magnitudes past 6 to 6; a value that rounds
+    to 0 is written +0 (code 0).  Brute force over the table."""
+    v = np.asarray(v, dtype=np.float64)
+    codes = np.arange(8, dtype=np.uint8)
+    mags = decode_e2m1(codes)
+    d = np.abs(np.abs(v)[..., None] - mags)
+    best = d.min(axis=-1, keepdims=True)
+    tie = d == best
+    pick = np.where(tie & ((codes & 1) == 0), 0, np.where(tie, 1, 2))
+    code = codes[np.argmin(pick, axis=-1)]
+    return np.where((v < 0) & (code != 0), code | 8, code).astype(np.uint8)
+
+
+def quant_mxfp4_rows_f32(y: np.ndarray):
+    """Quantize-on-write of rows to MXFP4 (OCP MX v1.0; "DeepSeek V4 结构速览",
+    CSA operator graph: the indexer scores in FP4): per block of 32 elements of
+    the last axis, the shared exponent E = floor(log2(amax)) - 2 (E + 127 as
+    E8M0, clipped to [0, 254]; 0 for an all-zero block), elements y / 2^E
+    (exact) as E2M1, two per byte with element 2i in the low nibble.
+    Returns (packed uint8 [..., n/2], scales uint8 [..., n/32])."""
+    y = np.asarray(y, dtype=np.float32).astype(np.float64)
+    n = y.shape[-1]
+    blocks = y.reshape(*y.shape[:-1], n // 32, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex with m in [0.5, 1): floor(log2) = ex - 1
+    E = np.where(amax > 0, ex - 1 - 2, -127)
+    E = np.clip(E, -127, 127).astype(np.int64)
+    nib = encode_e2m1(blocks * np.exp2(-E)[..., None]).reshape(*y.shape[:-1], n)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (E + 127).astype(np.uint8)

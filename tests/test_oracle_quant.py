@@ -50,3 +50,41 @@ def test_row_quantizer_bounds():
     assert np.all(np.abs(on.decode_e4m3(codes)).max(axis=1)[np.arange(50) != 3] == 448.0)
     step = np.exp2(np.floor(np.log2(np.maximum(np.abs(y / scale[:, None]), 2.0 ** -6))) - 3)
     assert np.all(np.abs(back - y) <= 0.5 * step * scale[:, None] * (1 + 1e-6) + 1e-30)
+
+
+def test_e2m1_midpoints_ties_and_clamp():
+    # 0.25 -> 0 (even), 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2, 3.5 -> 4, 5 -> 4, 7 -> 6
+    got = on.encode_e2m1(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.1, -5.5]))
+    assert list(got) == [0, 2, 2, 4, 4, 6, 6, 7, 0, 0xF]
+    codes = np.arange(16, dtype=np.uint8)
+    back = on.encode_e2m1(on.decode_e2m1(codes))
+    assert np.array_equal(back, np.where(codes == 8, 0, codes))     # -0 is written +0
+
+
+def test_mxfp4_rows_round_trip_and_bound():
+    g = np.random.default_rng(2)
+    y = (g.normal(size=(40, 128)) * np.exp(2 * g.normal(size=(40, 4)).repeat(32, axis=1))).astype(np.float32)
+    y[5, 32:64] = 0.0
+    packed, scales = on.quant_mxfp4_rows_f32(y)
+    back = on.dequant_mxfp4(packed, scales)
+    blocks = y.reshape(40, 4, 32).astype(np.float64)
+    amax = np.abs(blocks).max(axis=-1)
+    s = on.decode_e8m0(scales)
+    # the largest element of a block lands on 4 or 6 (amax / 2^E in [4, 8))
+    big = np.abs(on.dequant_mxfp4(packed, scales).reshape(40, 4, 32)).max(axis=-1)
+    nz = amax > 0
+    assert np.all(np.isin(np.round(big[nz] / s[nz], 6), [4.0, 6.0]))
+    assert scales[5, 1] == 0 and np.all(back.reshape(40, 4, 32)[5, 1] == 0)
+    # every element within half an E2M1 step (1 above 4, 0.25 below 1, ...) of its value, or clamped at 6
+    v = blocks / s[..., None]
+    a = np.abs(v)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    err = np.abs(back.reshape(40, 4, 32) / s[..., None] - v)
+    assert np.all((err <= 0.5 * step + 1e-12) | (a > 6))
+    # a hand-checked block: amax 3 -> E = floor(log2 3) - 2 = -1, elements doubled
+    blk = np.zeros((1, 32), np.float32)
+    blk[0, :4] = [3.0, -0.6, 0.2, 1.1]
+    p1, s1 = on.quant_mxfp4_rows_f32(blk)
+    assert s1[0, 0] == 126
+    # 6.0 -> 7, -1.2 -> 1.0 (code 2, negative: 0xA), 0.4 -> 0.5 (code 1), 2.2 -> 2.0 (code 4)
+    assert p1[0, 0] == (7 | (0xA << 4)) and p1[0, 1] == (1 | (4 << 4))
