@@ -59,9 +59,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--batch-invariant", action="store_true",
                    help="attention in batch-invariant mode (no row split; default workload only)")
-    p.add_argument("--fp8-keys", action="store_true",
-                   help="index keys quantized on write to fp8 E4M3 (in the latent's compressor launch) and the "
-                        "fp8 indexer (default workload only)")
+    p.add_argument("--keys", choices=("bf16", "fp8", "fp4"), default="bf16",
+                   help="index keys: bf16, or quantized on write (in the latent's compressor launch) to fp8 E4M3 "
+                        "or MXFP4 and scored by the indexer of that format (default workload only)")
+    p.add_argument("--fp8-keys", dest="keys", action="store_const", const="fp8", help="same as --keys fp8")
     p.add_argument("--rope", type=int, default=0,
                    help="partial RoPE dims fused into the compressors and the attention epilogues "
                         "(default workload only; 0 = none)")
@@ -75,11 +76,11 @@ class DecodeStep:
     """One CSA layer + one HCA layer decode step for B sequences at `ctx` context."""
 
     def __init__(self, csa, synth, torch, B=32, ctx=65536, k=512, rotate=4, batch_invariant=False, rope=0,
-                 fp8_keys=False):
+                 keys="bf16"):
         self.csa, self.torch = csa, torch
         self.bi = batch_invariant
         self.rope = rope
-        self.fp8 = fp8_keys
+        self.kfmt = keys
         bf = torch.bfloat16
         dn = synth.device_normal
         self.B, self.ctx, self.k = B, ctx, k
@@ -103,11 +104,15 @@ class DecodeStep:
         self.q = dn("b.q", (B, 1, 64, 512), bf)
         self.qh = dn("b.qh", (B, 1, 64, 512), bf)
         self.qi = dn("b.qi", (B, 1, 64, 128), bf, var=1.0 / 128)
-        if fp8_keys:
+        if keys == "fp8":
             # the key caches as fp8 codes + row scales (input preparation of the
             # resident cache; the step itself writes its new key quantized)
             self.keys, self.kscale = zip(*[_quant_fp8(torch, kk) for kk in self.keys])
             self.qi8, self.qscale = _quant_fp8(torch, self.qi)
+        elif keys == "fp4":
+            # MXFP4 codes (two per byte) + one E8M0 byte per 32 dims, same preparation
+            self.keys, self.kscale = zip(*[_quant_mxfp4(torch, kk) for kk in self.keys])
+            self.qi8, self.qscale = _quant_mxfp4(torch, self.qi)
         self.w = synth.device_uniform("b.w", (B, 1, 64))
         self.sink = dn("b.sink", (64,))
         # outputs and workspaces
@@ -133,13 +138,14 @@ class DecodeStep:
         key_job = dict(ratio=4, Ca=c4k["Ca"], Za=c4k["Za"], bias=self.b4k, Cb=c4k["Cb"], Zb=c4k["Zb"],
                        prev_Cb=c4k["pCb"], prev_Zb=c4k["pZb"], pos0=pos4, out=self.keys[r], cache_entry0=self.N4 - 1,
                        rope_dims=self.rope)
-        if self.fp8:
+        if self.kfmt != "bf16":
             key_job["out_scale"] = self.kscale[r]
+            qk = csa.FP8_E4M3 if self.kfmt == "fp8" else csa.MXFP4
             head = [
                 # the 512-d latent in bf16 and the key quantized on write, one launch
                 ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([kv_job, key_job])),
                 ("lightning_index", lambda: csa.lightning_index(
-                    self.qi8, self.w, self.keys[r], q_pos0=self.t, qk_dtype=csa.FP8_E4M3, q_scale=self.qscale,
+                    self.qi8, self.w, self.keys[r], q_pos0=self.t, qk_dtype=qk, q_scale=self.qscale,
                     k_scale=self.kscale[r], scores=self.scores)),
             ]
         else:
@@ -169,7 +175,15 @@ class DecodeStep:
         """Algorithmic bytes / flops of each stage for one launch (unique bytes only)."""
         B, N4, k = self.B, self.N4, self.k
         rows = k + 128
-        if self.fp8:
+        if self.kfmt == "fp4":
+            # a key row: 64 code bytes + 4 scale bytes; a query head the same
+            head = {
+                "compress_c4a_kv_keys": dict(bytes=B * 24 * (512 + 128) * 2 + B * (512 * 2 + 64 + 4)
+                                             + 8 * (512 + 128) * 4, flops=0),
+                "lightning_index": dict(bytes=B * N4 * 68 + B * 64 * 68 + B * 64 * 4 + B * N4 * 2,
+                                        flops=B * N4 * 64 * 128 * 2),
+            }
+        elif self.kfmt == "fp8":
             head = {
                 "compress_c4a_kv_keys": dict(bytes=B * 24 * (512 + 128) * 2 + B * (512 * 2 + 128 + 4)
                                              + 8 * (512 + 128) * 4, flops=0),
@@ -201,6 +215,24 @@ def _quant_fp8(torch, x):
     scale = (amax / 448.0).contiguous()
     codes = (x.float() / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     return codes, scale
+
+
+def _quant_mxfp4(torch, x):
+    """Per-32 MXFP4 codes of a resident tensor, on the device (input
+    preparation): E8M0 exponent floor(log2 amax) - 2, elements rounded to the
+    E2M1 grid, ties to the even code, even element in the low nibble."""
+    xs = x.float().reshape(*x.shape[:-1], x.shape[-1] // 32, 32)
+    amax = xs.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 2, torch.full_like(amax, -127))
+    e = e.clamp(-127, 127)
+    v = xs / torch.exp2(e)[..., None]
+    a = v.abs()
+    code = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int() + (a > 2.5).int()
+            + (a >= 3.5).int() + (a > 5).int())
+    nib = code + 8 * ((v < 0) & (code > 0)).int()
+    nib = nib.reshape(*x.shape[:-1], x.shape[-1])
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).to(torch.uint8).contiguous()
+    return packed, (e + 127).to(torch.uint8).contiguous()
 
 
 def cpu_oracle_decode(step, torch, budget_s):
@@ -375,7 +407,7 @@ def main():
         return
 
     step = DecodeStep(csa, synth, torch, rotate=args.rotate, batch_invariant=args.batch_invariant,
-                      rope=args.rope, fp8_keys=args.fp8_keys)
+                      rope=args.rope, keys=args.keys)
     ms, wall = time_graph(torch, step, args.steps, args.warmup, args.rotate, args.eager)
     per_stage = time_stages(torch, step, args.steps, args.rotate)
     alg = step.algorithmic()
@@ -408,15 +440,15 @@ def main():
                    "index_dim": 128, "cache_copies_rotated": args.rotate,
                    "timing": "eager" if args.eager else "hip_graph",
                    "attention": "batch_invariant" if args.batch_invariant else "split_kv",
-                   "rope_dims": args.rope, "index_keys": "fp8_e4m3" if args.fp8_keys else "bf16"},
+                   "rope_dims": args.rope, "index_keys": {"bf16": "bf16", "fp8": "fp8_e4m3", "fp4": "mxfp4"}[args.keys]},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.fp8_keys else index_traffic(),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.keys != "bf16" else index_traffic(),
                      "algorithmic_bytes_per_launch": alg[dom]["bytes"], "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "stages": stages,
         "wall_s_timed": round(wall, 3),
     }
-    if not args.no_cpu and not args.fp8_keys:
+    if not args.no_cpu and args.keys == "bf16":
         rec["cpu_baseline"] = cpu_oracle_decode(step, torch, args.cpu_seconds)
     print(json.dumps(rec))
 

@@ -11,7 +11,8 @@ HBM, captured in a HIP graph and replayed; every stage is also timed alone
                  last block, dense MQA with sink over 8,192 entries + window
   hca_prefill    the last 2,048 tokens of a 1,048,576 context: C128A compress
                  of the chunk, dense MQA with sink
-  csa_1m_decode  8 sequences at 1,048,576 context: C4A compress (KV and keys),
+  csa_1m_decode  8 sequences at 1,048,576 context: C4A compress (the KV latent, and
+                 the key quantized on write into the MXFP4 cache),
                  MXFP4 indexer over 262,144 keys, top-1024, sparse MQA
   c128a_1m       C128A compress of all 1,048,576 tokens (8,192 entries)
   csa_reindex_decode / csa_reindex_prefill
@@ -155,7 +156,6 @@ def run(args, torch, csa, synth):
         ck = {nm: dn(f"m.k{nm}", (B, 4, 128), bf) for nm in ("Ca", "Za", "Cb", "Zb", "pCb", "pZb")}
         b4, b4k = dn("m.b4", (8, 512), var=0.1), dn("m.b4k", (8, 128), var=0.1)
         kv = dn("m.kv", (B, N, 512), bf)
-        newkey = torch.empty(B, 1, 128, dtype=bf, device="cuda")
         kp, ksc = _rand_mxfp4_dev(torch, "m.keys", (B, N), synth)
         qp, qsc = _rand_mxfp4_dev(torch, "m.qi", (B, 1, 64), synth)
         w = synth.device_uniform("m.w", (B, 1, 64))
@@ -171,9 +171,10 @@ def run(args, torch, csa, synth):
             ("compress_c4a_kv_keys", lambda: csa.csa_compress_batch([
                 dict(ratio=4, Ca=c["Ca"], Za=c["Za"], bias=b4, Cb=c["Cb"], Zb=c["Zb"], prev_Cb=c["pCb"],
                      prev_Zb=c["pZb"], pos0=q0 - 3, out=kv, cache_entry0=N - 1),
+                # the new key quantized on write into its MXFP4 cache slot
                 dict(ratio=4, Ca=ck["Ca"], Za=ck["Za"], bias=b4k, Cb=ck["Cb"], Zb=ck["Zb"], prev_Cb=ck["pCb"],
-                     prev_Zb=ck["pZb"], pos0=q0 - 3, out=newkey)]),
-             B * 24 * (512 + 128) * 2, 0, "hbm"),
+                     prev_Zb=ck["pZb"], pos0=q0 - 3, out=kp, out_scale=ksc, cache_entry0=N - 1)]),
+             B * 24 * (512 + 128) * 2 + B * (512 * 2 + 64 + 4) + 8 * (512 + 128) * 4, 0, "hbm"),
             ("lightning_index", lambda: csa.lightning_index(qp, w, kp, q_pos0=q0, qk_dtype=csa.MXFP4, q_scale=qsc,
                                                             k_scale=ksc, scores=scores, N=N),
              B * N * 68 + B * 64 * 68 + B * N * 2, B * N * 64 * 128 * 2, "hbm"),

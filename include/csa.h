@@ -166,17 +166,28 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
  * scale to out_scale: entry i of sequence b at out_scale[b * S + i] with S =
  * out_batch_stride / c (out_batch_stride a multiple of c), or n_tok/ratio
  * when out_batch_stride is 0 -- the byte codes and per-row scales
- * lightning_index reads as CSA_FP8_E4M3 keys.  out_scale is 4-byte aligned;
- * NULL for other output types.  Other arguments, rules and errors are those
- * of csa_compress; csa_compress is this call with out_scale NULL and
- * rope_dims 0.
+ * lightning_index reads as CSA_FP8_E4M3 keys.  out_scale is 4-byte aligned.
+ *
+ * out_dtype CSA_MXFP4 (C4A; "DeepSeek V4 结构速览", CSA operator graph: the
+ * indexer scores in FP4) writes OCP MX v1.0 MXFP4 instead: per block of 32
+ * channels the shared exponent E = floor(log2 amax) - 2 (E8M0 byte E + 127,
+ * clipped to [0, 254]; 0 for an all-zero block) and the elements out * 2^-E
+ * as E2M1 (nearest, ties to the even mantissa, clamped to 6; -0 written +0),
+ * two per byte with the even channel in the low nibble: entry i of sequence b
+ * at byte (b * out_batch_stride + i * c) / 2 of out, its c / 32 scale bytes
+ * at out_scale[(b * S + i) * c / 32 ..] -- the packed keys and scales
+ * lightning_index reads as CSA_MXFP4.
+ *
+ * out_scale is NULL for float output types.  Other arguments, rules and
+ * errors are those of csa_compress; csa_compress is this call with out_scale
+ * NULL and rope_dims 0.
  */
 int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
                     const void* Ca, const void* Za, const void* Cb, const void* Zb,
                     const void* prev_Cb, const void* prev_Zb,
                     const float* bias, const float* gamma, float eps,
                     int in_dtype, int out_dtype, void* out, int64_t out_batch_stride,
-                    float* out_scale, int rope_dims, float rope_base, int rope_anchor,
+                    void* out_scale, int rope_dims, float rope_base, int rope_anchor,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -188,8 +199,8 @@ int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0
  * exactly the arguments of csa_compress_ex (without workspace and stream) and
  * obeys the same rules; jobs of one batch must share ratio, in_dtype and
  * out_dtype, except that CSA_FP8_E4M3 jobs (quantize-on-write, C4A) may sit
- * beside jobs of one other output type -- the CSA layer's bf16 latent and its
- * fp8 indexer key in one launch.  1 <= n_jobs <= 4.  Jobs with nothing to
+ * (and CSA_MXFP4 jobs) beside jobs of one other output type -- the CSA
+ * layer's bf16 latent and its quantized indexer key in one launch.  1 <= n_jobs <= 4.  Jobs with nothing to
  * write are skipped.
  * The row split that csa_compress's workspace enables is not used here.
  * Errors name the first offending job.
@@ -207,7 +218,7 @@ typedef struct csa_compress_job {
   int rope_dims;      /* csa_compress_ex's partial RoPE; 0 for none */
   float rope_base;
   int rope_anchor;
-  float* out_scale;   /* csa_compress_ex's fp8 scales; NULL unless out_dtype is CSA_FP8_E4M3 */
+  void* out_scale;    /* csa_compress_ex's scales (fp8: fp32, MXFP4: E8M0); NULL for float outputs */
 } csa_compress_job;
 
 int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
@@ -427,13 +438,15 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
  *  Ca, Za      [B, ratio, c] in_dtype: the rolling buffer (current block)
  *  prev_Cb/_Zb [B, 4, c] (C4A): the previous block's rows; not read for a
  *              sequence at pos0 0.  NULL for C128A.
- *  bias, gamma, eps, in_dtype, out_dtype, rope_*: as csa_compress_ex;
- *  scale_pool  [n_pool, 32] fp32 for CSA_FP8_E4M3 output, else NULL.
+ *  bias, gamma, eps, in_dtype, out_dtype, rope_*: as csa_compress_ex
+ *              (pool rows of c / 2 bytes for CSA_MXFP4);
+ *  scale_pool  [n_pool, 32] fp32 for CSA_FP8_E4M3 output, [n_pool, 32, c / 32]
+ *              E8M0 bytes for CSA_MXFP4, else NULL.
  */
 int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca,
                        const void* Za, const void* prev_Cb, const void* prev_Zb,
                        const float* bias, const float* gamma, float eps, int in_dtype,
-                       int out_dtype, void* pool, float* scale_pool, int64_t n_pool,
+                       int out_dtype, void* pool, void* scale_pool, int64_t n_pool,
                        const int32_t* block_table, int64_t max_blocks, int rope_dims,
                        float rope_base, int rope_anchor, void* stream);
 

@@ -145,26 +145,32 @@ class _CompressJob(ctypes.Structure):
                 ("rope_anchor", _int), ("out_scale", _vp)]
 
 
-def _out_dt(t: torch.Tensor) -> int:
-    """Compressor output type: uint8 tensors hold fp8 E4M3 codes (quantize-on-write)."""
-    return FP8_E4M3 if t.dtype == torch.uint8 else _dt(t)
+def _out_dt(t: torch.Tensor, c=None) -> int:
+    """Compressor output type: uint8 tensors hold fp8 E4M3 codes, or packed MXFP4
+    (two elements per byte) when their rows are c / 2 bytes (quantize-on-write)."""
+    if t.dtype == torch.uint8:
+        return MXFP4 if (c is not None and t.shape[-1] * 2 == c) else FP8_E4M3
+    return _dt(t)
 
 
-def _compress_scale(out, out_scale, cache_entry0, n_ent):
-    """fp8 output: the per-entry scale tensor ([B, n_ent] or the cache's [B, N_cache])
-    and the address of the first entry's scale."""
+def _compress_scale(out, out_scale, cache_entry0, n_ent, c):
+    """Quantized output: the scale tensor (fp8: [B, n_ent] fp32; MXFP4: [B, n_ent, c/32]
+    uint8; or the cache's) and the address of the first entry's scales."""
     if out.dtype != torch.uint8:
         if out_scale is not None:
-            raise ValueError("out_scale is only for fp8 (uint8) output")
+            raise ValueError("out_scale is only for quantized (uint8) output")
         return None, None
     B = out.shape[0]
+    fp4 = _out_dt(out, c) == MXFP4
+    per = c // 32 if fp4 else 1
     if out_scale is None:
         if cache_entry0 is not None:
-            raise ValueError("writing fp8 entries into a cache needs the cache's out_scale [B, N_cache]")
-        out_scale = torch.empty(B, n_ent, dtype=torch.float32, device=out.device)
-    if out_scale.dtype != torch.float32 or not out_scale.is_contiguous():
-        raise ValueError("out_scale must be a contiguous float32 tensor")
-    return out_scale, out_scale.data_ptr() + (cache_entry0 or 0) * 4
+            raise ValueError("writing quantized entries into a cache needs the cache's out_scale")
+        out_scale = torch.empty((B, n_ent, per) if fp4 else (B, n_ent), dtype=torch.uint8 if fp4 else torch.float32,
+                                device=out.device)
+    if out_scale.dtype != (torch.uint8 if fp4 else torch.float32) or not out_scale.is_contiguous():
+        raise ValueError("out_scale must be contiguous uint8 (MXFP4) or float32 (fp8)")
+    return out_scale, out_scale.data_ptr() + (cache_entry0 or 0) * (per if fp4 else 4)
 
 
 def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
@@ -172,17 +178,22 @@ def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
     B, n_tok, c = Ca.shape
     n_ent = n_tok // ratio
     if out is None:
-        odt = Ca.dtype if out_dtype is None else out_dtype
-        out = torch.empty(B, n_ent, c, dtype=odt, device=Ca.device)
+        if out_dtype == MXFP4:       # packed fp4: c / 2 bytes per entry
+            out = torch.empty(B, n_ent, c // 2, dtype=torch.uint8, device=Ca.device)
+        else:
+            odt = Ca.dtype if out_dtype is None else out_dtype
+            out = torch.empty(B, n_ent, c, dtype=odt, device=Ca.device)
+    row = out.shape[-1] if out.dim() == 3 else c     # stored elements (bytes for MXFP4) per entry
+    per_elem = c // row                              # channels per stored element: 2 for MXFP4
     if cache_entry0 is None:
-        if out.numel() < B * n_ent * c:
+        if out.numel() < B * n_ent * row:
             raise ValueError("out is too small")
         return out, _ptr(out), 0
-    if out.dim() != 3 or out.shape[0] != B or out.shape[2] != c:
-        raise ValueError("cache must be [B, N_cache, c]")
+    if out.dim() != 3 or out.shape[0] != B or out.shape[2] * per_elem != c:
+        raise ValueError("cache must be [B, N_cache, c] (c / 2 bytes for MXFP4)")
     if cache_entry0 < 0 or cache_entry0 + n_ent > out.shape[1]:
         raise ValueError("cache slot out of range")
-    return out, _ptr(out) + cache_entry0 * c * out.element_size(), out.shape[1] * c
+    return out, _ptr(out) + cache_entry0 * row * out.element_size(), out.shape[1] * c
 
 
 def csa_compress_batch(jobs, stream=None):
@@ -196,13 +207,13 @@ def csa_compress_batch(jobs, stream=None):
         Ca = d["Ca"]
         B, n_tok, c = Ca.shape
         out, optr, stride = _compress_out(Ca, d["ratio"], d.get("out"), d.get("out_dtype"), d.get("cache_entry0"))
-        sc, sptr = _compress_scale(out, d.get("out_scale"), d.get("cache_entry0"), n_tok // d["ratio"])
+        sc, sptr = _compress_scale(out, d.get("out_scale"), d.get("cache_entry0"), n_tok // d["ratio"], c)
         outs.append(out if sc is None else (out, sc))
         j.ratio, j.B, j.n_tok, j.c, j.pos0 = d["ratio"], B, n_tok, c, d.get("pos0", 0)
         j.Ca, j.Za, j.Cb, j.Zb = _ptr(Ca), _ptr(d["Za"]), _ptr(d.get("Cb")), _ptr(d.get("Zb"))
         j.prev_Cb, j.prev_Zb = _ptr(d.get("prev_Cb")), _ptr(d.get("prev_Zb"))
         j.bias, j.gamma, j.eps = _ptr(d["bias"]), _ptr(d.get("gamma")), d.get("eps", 1e-6)
-        j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _out_dt(out), optr, stride
+        j.in_dtype, j.out_dtype, j.out, j.out_batch_stride = _dt(Ca), _out_dt(out, c), optr, stride
         j.out_scale = sptr
         j.rope_dims, j.rope_base, j.rope_anchor = (d.get("rope_dims", 0), d.get("rope_base", ROPE_BASE),
                                                    d.get("rope_anchor", 0))
@@ -224,15 +235,16 @@ def csa_compress(ratio, Ca, Za, bias, Cb=None, Zb=None, prev_Cb=None, prev_Zb=No
     position pos0 + ratio*i + rope_anchor (csa_compress_ex).  ``out_dtype=torch.uint8``
     (or a uint8 ``out``) quantizes on write to fp8 E4M3 codes with one fp32 scale
     per entry (into ``out_scale``, the cache's [B, N_cache] with ``cache_entry0``);
-    then (codes, scales) is returned."""
+    ``out_dtype=MXFP4`` (or a uint8 ``out`` of c / 2 bytes per entry) to packed
+    MXFP4 with E8M0 scales [.., c / 32]; then (codes, scales) is returned."""
     B, n_tok, c = Ca.shape
     in_dt = _dt(Ca)
     out, optr, stride = _compress_out(Ca, ratio, out, out_dtype, cache_entry0)
-    sc, sptr = _compress_scale(out, out_scale, cache_entry0, n_tok // ratio)
+    sc, sptr = _compress_scale(out, out_scale, cache_entry0, n_tok // ratio, c)
     ws, wsb = _workspace(OP_COMPRESS, B, n_tok, c, ratio, Ca.device, workspace)
     st = library().csa_compress_ex(ratio, B, n_tok, c, pos0, _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
                                    _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, in_dt,
-                                   _out_dt(out), optr, stride, sptr, rope_dims, rope_base, rope_anchor, _ptr(ws),
+                                   _out_dt(out, c), optr, stride, sptr, rope_dims, rope_base, rope_anchor, _ptr(ws),
                                    wsb, _stream(stream))
     _check(st, "csa_compress")
     return out if sc is None else (out, sc)
@@ -375,7 +387,7 @@ def csa_compress_paged(ratio, Ca, Za, bias, pool, block_table, pos0, *, prev_Cb=
     ([n_pool, 32, c] C4A, [n_pool, c] C128A; uint8 for fp8 keys with ``scale_pool``)."""
     B, _, c = Ca.shape
     st = library().csa_compress_paged(ratio, B, c, _ptr(pos0), _ptr(Ca), _ptr(Za), _ptr(prev_Cb), _ptr(prev_Zb),
-                                      _ptr(bias), _ptr(gamma), eps, _dt(Ca), _out_dt(pool), _ptr(pool),
+                                      _ptr(bias), _ptr(gamma), eps, _dt(Ca), _out_dt(pool, c), _ptr(pool),
                                       _ptr(scale_pool), pool.shape[0], _ptr(block_table), block_table.shape[1],
                                       rope_dims, rope_base, rope_anchor, _stream(stream))
     _check(st, "csa_compress_paged")

@@ -35,7 +35,7 @@ extern "C" {
 int csa_compress_ex(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, const void* Ca,
                     const void* Za, const void* Cb, const void* Zb, const void* prev_Cb,
                     const void* prev_Zb, const float* bias, const float* gamma, float eps, int in_dtype,
-                    int out_dtype, void* out, int64_t out_batch_stride, float* out_scale, int rope_dims,
+                    int out_dtype, void* out, int64_t out_batch_stride, void* out_scale, int rope_dims,
                     float rope_base, int rope_anchor, void* workspace, size_t ws_bytes, void* stream) {
   csa::Check ck = csa::check_compress(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias,
                                       gamma, eps, in_dtype, out_dtype, out, out_batch_stride, workspace, ws_bytes,
@@ -68,11 +68,11 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
                                         j.prev_Zb, j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out,
                                         j.out_batch_stride, nullptr, 0, j.rope_dims, j.rope_base, j.rope_anchor,
                                         j.out_scale);
-    // fp8 jobs (quantize-on-write, C4A) may sit beside jobs of one float output type
+    // quantized jobs (quantize-on-write, C4A) may sit beside jobs of one float output type
+    auto quant = [](int dt) { return dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; };
     bool same_out = true;
     for (int p = 0; p < q; ++p)
-      if (jobs[p].out_dtype != j.out_dtype && jobs[p].out_dtype != CSA_FP8_E4M3 && j.out_dtype != CSA_FP8_E4M3)
-        same_out = false;
+      if (jobs[p].out_dtype != j.out_dtype && !quant(jobs[p].out_dtype) && !quant(j.out_dtype)) same_out = false;
     if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || !same_out))
       cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype (fp8 jobs may join "
                                    "jobs of one other output type)");
@@ -168,7 +168,7 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
 
 int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,
                        const void* prev_Cb, const void* prev_Zb, const float* bias, const float* gamma, float eps,
-                       int in_dtype, int out_dtype, void* pool, float* scale_pool, int64_t n_pool,
+                       int in_dtype, int out_dtype, void* pool, void* scale_pool, int64_t n_pool,
                        const int32_t* block_table, int64_t max_blocks, int rope_dims, float rope_base, int rope_anchor,
                        void* stream) {
   csa::Check ck = csa::check_compress_paged(ratio, B, c, pos0, Ca, Za, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,

@@ -18,6 +18,7 @@
 //  * the G partial states are merged through LDS, then RMSNorm is a
 //    block-wide reduction over channels.
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "launch.h"
@@ -76,6 +77,12 @@ __device__ __forceinline__ void store_out(TO* p, const float* f) {
   }
 }
 
+// Output type of MXFP4 quantize-on-write: two E2M1 elements per byte (the
+// element pointer of an entry then counts bytes of c / 2).
+struct E2M1x2 {
+  uint8_t b;
+};
+
 constexpr int kChunkRows = 4;   // rows per thread whose loads are in flight together
 constexpr int kMaxRopePairs = 512;   // c <= 1024
 
@@ -116,7 +123,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                const float* __restrict__ bias, const float* __restrict__ gamma,
                                                float eps, TO* __restrict__ out, int64_t out_stride, int G,
                                                float* __restrict__ part, int rope_R, double rope_l2b,
-                                               int rope_anchor, float* __restrict__ out_scale,
+                                               int rope_anchor, void* __restrict__ out_scale,
                                                int64_t scale_stride) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
@@ -291,7 +298,44 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < nw; ++w) tot += red[w];
-  if constexpr (sizeof(TO) == 1) {
+  if constexpr (std::is_same_v<TO, E2M1x2>) {
+    // Quantize-on-write to MXFP4 (OCP MX v1.0): per block of 32 channels --
+    // 32 / VEC neighbouring channel threads, i.e. lanes -- the shared exponent
+    // E = floor(log2 amax) - 2 read off amax's float bits (E8M0 = E + 127,
+    // clipped to [0, 254]), elements o * 2^-E (exact) rounded to E2M1, two
+    // per byte with the even channel in the low nibble.
+    if (g != 0) return;
+    const float inv = rsqrtf(tot / static_cast<float>(c) + eps);
+    float o[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = y[v] * inv * gm[v];
+    if (__builtin_expect(rope_R > 0, 0) && ch0 + VEC > c - rope_R) {
+#pragma unroll
+      for (int v = 0; v < VEC; v += 2) {
+        if (ch0 + v >= c - rope_R) {
+          const float2 k = rope_tab[(ch0 + v - (c - rope_R)) / 2];
+          rope_pair(o[v], o[v + 1], k.x, k.y);
+        }
+      }
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(o[v]));
+#pragma unroll
+    for (int m = 1; m < 32 / VEC; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+    int E = am > 0.f ? static_cast<int>((__float_as_uint(am) >> 23) & 0xffu) - 129 : -127;
+    E = E < -127 ? -127 : (E > 127 ? 127 : E);
+    uint32_t word = 0;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) word |= f32_to_e2m1(ldexpf(o[v], -E)) << (4 * v);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (b * out_stride + i * c + ch0) / 2;
+    if constexpr (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = word;
+    else *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(word);
+    if (ct % (32 / VEC) == 0)
+      static_cast<uint8_t*>(out_scale)[(b * scale_stride + i) * (c / 32) + ch0 / 32] = static_cast<uint8_t>(E + 127);
+    return;
+  }
+  if constexpr (std::is_same_v<TO, uint8_t>) {
     // Quantize-on-write: E4M3 codes with one fp32 scale per entry, amax / 448
     // over the entry's normalised (and rotated) channels -- a second block
     // reduction, which every thread joins -- and each code from the fp32
@@ -330,7 +374,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
     uint8_t* dst = reinterpret_cast<uint8_t*>(out + b * out_stride + i * c + ch0);
     if constexpr (VEC == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
     else *reinterpret_cast<uint32_t*>(dst) = word[0];
-    if (ct == 0) out_scale[b * scale_stride + i] = scale;
+    if (ct == 0) static_cast<float*>(out_scale)[b * scale_stride + i] = scale;
     return;
   }
   if (g != 0) return;
@@ -364,7 +408,7 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                 const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
                 TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part, int rope_R,
-                double rope_l2b, int rope_anchor, float* __restrict__ out_scale, int64_t scale_stride) {
+                double rope_l2b, int rope_anchor, void* __restrict__ out_scale, int64_t scale_stride) {
   compress_entry<TI, TO, RATIO, SPLIT>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
                                        static_cast<int>(gridDim.z), n_tok, c, pos0, Ca, Za, Cb, Zb, pCb, pZb, bias,
                                        gamma, eps, out, out_stride, G, part, rope_R, rope_l2b, rope_anchor,
@@ -384,7 +428,7 @@ __global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_paged_kernel(int c, const int64_t* __restrict__ pos0s, const TI* __restrict__ Ca,
                       const TI* __restrict__ Za, const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                       const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
-                      TO* __restrict__ pool, float* __restrict__ scale_pool, int64_t n_pool,
+                      TO* __restrict__ pool, void* __restrict__ scale_pool, int64_t n_pool,
                       const int32_t* __restrict__ table, int64_t max_blocks, int G, int rope_R, double rope_l2b,
                       int rope_anchor) {
   constexpr int SH = RATIO == 4 ? 5 : 0;   // log2 entries per block
@@ -397,9 +441,13 @@ compress_paged_kernel(int c, const int64_t* __restrict__ pos0s, const TI* __rest
   if (blk < 0 || blk >= n_pool) return;
   const int64_t row = (blk << SH) + (e & ((int64_t{1} << SH) - 1));
   // entry 0 of a one-block chunk whose output row is `row` (no batch stride)
+  constexpr bool kFp4 = std::is_same_v<TO, E2M1x2>;
+  TO* dst = kFp4 ? reinterpret_cast<TO*>(reinterpret_cast<uint8_t*>(pool) + row * c / 2) : pool + row * c;
+  void* sdst = !scale_pool ? nullptr
+               : kFp4      ? static_cast<void*>(static_cast<uint8_t*>(scale_pool) + row * (c / 32))
+                           : static_cast<void*>(static_cast<float*>(scale_pool) + row);
   compress_entry<TI, TO, RATIO, false>(0, b, 0, 1, RATIO, c, p0, Ca, Za, nullptr, nullptr, pCb, pZb, bias, gamma,
-                                       eps, pool + row * c, 0, G, nullptr, rope_R, rope_l2b, rope_anchor,
-                                       scale_pool ? scale_pool + row : nullptr, 0);
+                                       eps, dst, 0, G, nullptr, rope_R, rope_l2b, rope_anchor, sdst, 0);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -415,8 +463,9 @@ struct CompressJobDev {
   int rope_R;
   double rope_l2b;
   int rope_anchor;
-  float* out_scale;       // fp8 output: one scale per entry
+  void* out_scale;        // quantized output: fp32 scale per entry (fp8), E8M0 per 32 channels (fp4)
   int64_t scale_stride;
+  int qfmt;               // MIXED batches: 1 fp8, 2 fp4, 0 the float type
 };
 constexpr int kMaxBatchJobs = 4;
 struct CompressBatch {
@@ -431,7 +480,7 @@ __global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_batch_kernel(CompressBatch jb) {
   const CompressJobDev& J = jb.j[blockIdx.z];
   if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
-  if (MIXED && J.out_scale) {
+  if (MIXED && J.qfmt == 1) {
     compress_entry<TI, uint8_t, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
                                               static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                               static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
@@ -439,6 +488,16 @@ compress_batch_kernel(CompressBatch jb) {
                                               J.gamma, J.eps, static_cast<uint8_t*>(J.out), J.out_stride, J.G,
                                               nullptr, J.rope_R, J.rope_l2b, J.rope_anchor, J.out_scale,
                                               J.scale_stride);
+    return;
+  }
+  if (MIXED && J.qfmt == 2) {
+    compress_entry<TI, E2M1x2, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+                                             static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
+                                             static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
+                                             static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias,
+                                             J.gamma, J.eps, static_cast<E2M1x2*>(J.out), J.out_stride, J.G,
+                                             nullptr, J.rope_R, J.rope_l2b, J.rope_anchor, J.out_scale,
+                                             J.scale_stride);
     return;
   }
   compress_entry<TI, TO, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
@@ -576,7 +635,8 @@ hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
     jb.j[q] = CompressJobDev{a.Ca, a.Za, a.Cb, a.Zb, a.prev_Cb, a.prev_Zb, a.bias, a.gamma, a.out, a.n_tok, a.pos0,
                              a.out_batch_stride ? a.out_batch_stride : n_ent * a.c, n_ent, a.B, a.eps,
                              static_cast<int>(a.c), G, a.rope_dims, rope_log2_base(a), a.rope_anchor, a.out_scale,
-                             (a.out_batch_stride ? a.out_batch_stride : n_ent * a.c) / a.c};
+                             (a.out_batch_stride ? a.out_batch_stride : n_ent * a.c) / a.c,
+                             a.out_dtype == CSA_FP8_E4M3 ? 1 : (a.out_dtype == CSA_MXFP4 ? 2 : 0)};
   }
   hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO, MIXED>),
                      dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
@@ -600,6 +660,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.B == 0 || a.n_tok / a.ratio == 0) return hipSuccess;
   if (a.out_dtype == CSA_FP8_E4M3)   // C4A only (validated): the indexer keys
     return a.in_dtype == CSA_F32 ? launch_t<float, uint8_t, 4>(a, s) : launch_t<uint16_t, uint8_t, 4>(a, s);
+  if (a.out_dtype == CSA_MXFP4)
+    return a.in_dtype == CSA_F32 ? launch_t<float, E2M1x2, 4>(a, s) : launch_t<uint16_t, E2M1x2, 4>(a, s);
   if (a.in_dtype == CSA_F32)
     return a.out_dtype == CSA_F32 ? launch_r<float, float>(a, s) : launch_r<float, uint16_t>(a, s);
   return a.out_dtype == CSA_F32 ? launch_r<uint16_t, float>(a, s) : launch_r<uint16_t, uint16_t>(a, s);
@@ -628,6 +690,7 @@ hipError_t launch_paged_t(const CompressPagedArgs& a, hipStream_t s) {
 template <typename TI>
 hipError_t launch_paged_i(const CompressPagedArgs& a, hipStream_t s) {
   if (a.out_dtype == CSA_FP8_E4M3) return launch_paged_t<TI, uint8_t, 4>(a, s);   // C4A keys (validated)
+  if (a.out_dtype == CSA_MXFP4) return launch_paged_t<TI, E2M1x2, 4>(a, s);
   if (a.ratio == 4)
     return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 4>(a, s) : launch_paged_t<TI, uint16_t, 4>(a, s);
   return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 128>(a, s) : launch_paged_t<TI, uint16_t, 128>(a, s);
@@ -647,20 +710,24 @@ hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s)
   for (int q = 0; q < n; ++q)
     if (jobs[q].B > 0 && jobs[q].n_tok / jobs[q].ratio > 0) live[m++] = jobs[q];
   if (m == 0) return hipSuccess;
-  // the output type of the jobs that do not write fp8 (all fp8: none)
-  int odt = CSA_FP8_E4M3;
-  for (int q = 0; q < m; ++q)
-    if (live[q].out_dtype != CSA_FP8_E4M3) odt = live[q].out_dtype;
-  const bool any_fp8 = [&] {
-    for (int q = 0; q < m; ++q)
-      if (live[q].out_dtype == CSA_FP8_E4M3) return true;
-    return false;
-  }();
+  // quantized jobs (fp8, fp4) may sit beside jobs of one float type
+  auto quant = [](int dt) { return dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; };
+  int odt = -1;
+  int nq8 = 0, nq4 = 0;
+  for (int q = 0; q < m; ++q) {
+    if (!quant(live[q].out_dtype)) odt = live[q].out_dtype;
+    nq8 += live[q].out_dtype == CSA_FP8_E4M3;
+    nq4 += live[q].out_dtype == CSA_MXFP4;
+  }
   const CompressArgs& a = live[0];
-  if (odt == CSA_FP8_E4M3)
+  if (odt < 0 && nq4 == 0)
     return a.in_dtype == CSA_F32 ? launch_batch_t<float, uint8_t, 4>(live, m, s)
                                  : launch_batch_t<uint16_t, uint8_t, 4>(live, m, s);
-  if (any_fp8) {   // C4A (validated): float outputs with fp8 ones
+  if (odt < 0 && nq8 == 0)
+    return a.in_dtype == CSA_F32 ? launch_batch_t<float, E2M1x2, 4>(live, m, s)
+                                 : launch_batch_t<uint16_t, E2M1x2, 4>(live, m, s);
+  if (odt < 0) odt = CSA_BF16;   // fp8 and fp4 jobs only: any float type serves as the third path
+  if (nq8 + nq4 > 0) {   // C4A (validated): float outputs with quantized ones
     if (a.in_dtype == CSA_F32)
       return odt == CSA_F32 ? launch_batch_t<float, float, 4, true>(live, m, s)
                             : launch_batch_t<float, uint16_t, 4, true>(live, m, s);

@@ -118,6 +118,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
+// fp32 -> OCP E2M1 nibble: the nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to
+// the even mantissa (code), magnitudes past 6 to 6; a value that rounds to 0
+// is written +0.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t code = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                      : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return (v < 0.f && code) ? (code | 8u) : code;
+}
+
 // Round-robin workgroup dispatch puts consecutive workgroup ids on different
 // XCDs (8 on MI355X).  Remap a linear id so that ids [x*per, (x+1)*per) run on
 // XCD x, keeping neighbouring tiles (and their shared data) in one L2.

@@ -25,7 +25,7 @@ struct CompressArgs {
   int rope_dims;     // partial RoPE on the last rope_dims channels (0: none)
   float rope_base;
   int rope_anchor;   // entry i's position: pos0 + ratio * i + rope_anchor
-  float* out_scale;  // fp8 output: the scale of entry i of sequence b at out_scale[b * (stride / c) + i]
+  void* out_scale;   // fp8: fp32 scale of entry i of sequence b at [b * (stride / c) + i]; fp4: E8M0 bytes, c / 32 per entry
 };
 
 // The decode write of one block per sequence into the paged cache.
@@ -40,7 +40,7 @@ struct CompressPagedArgs {
   float eps;
   int in_dtype, out_dtype;
   void* pool;                   // [n_pool, 32, c] (C4A) or [n_pool, c] (C128A)
-  float* scale_pool;            // fp8: [n_pool, 32]
+  void* scale_pool;             // fp8: [n_pool, 32] fp32; fp4: [n_pool, 32, c / 32] E8M0
   int64_t n_pool;
   const int32_t* block_table;   // [B, max_blocks]
   int64_t max_blocks;

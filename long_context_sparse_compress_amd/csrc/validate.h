@@ -135,7 +135,7 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
                             const float* gamma, float eps, int in_dtype, int out_dtype,
                             const void* out, int64_t out_batch_stride, const void* ws, size_t ws_bytes,
                             int rope_dims = 0, float rope_base = 0.f, int rope_anchor = 0,
-                            const float* out_scale = nullptr) {
+                            const void* out_scale = nullptr) {
   Check k;
   if (ratio != 4 && ratio != 128) { k.fail(CSA_ERR_INVALID_ARG, "ratio must be 4 or 128, got " + i2s(ratio)); return k; }
   if (B < 0 || n_tok < 0) { k.fail(CSA_ERR_INVALID_ARG, "B and n_tok must be >= 0"); return k; }
@@ -144,14 +144,14 @@ inline Check check_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int6
   if (rope_anchor < 0 || rope_anchor >= ratio) { k.fail(CSA_ERR_INVALID_ARG, "rope_anchor must be in [0, ratio), got " + i2s(rope_anchor)); return k; }
   if (pos0 < 0 || pos0 % ratio != 0) { k.fail(CSA_ERR_INVALID_ARG, "pos0 must be >= 0 and a multiple of ratio, got " + i2s(pos0)); return k; }
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
-  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16 or CSA_FP8_E4M3"); return k; }
-  if (out_dtype == CSA_FP8_E4M3) {
-    if (ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "fp8 output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
-    if (out_batch_stride % c != 0) { k.fail(CSA_ERR_INVALID_ARG, "fp8 output needs out_batch_stride to be a multiple of c"); return k; }
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3 && out_dtype != CSA_MXFP4) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16, CSA_FP8_E4M3 or CSA_MXFP4"); return k; }
+  if (out_dtype == CSA_FP8_E4M3 || out_dtype == CSA_MXFP4) {
+    if (ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "quantized output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
+    if (out_batch_stride % c != 0) { k.fail(CSA_ERR_INVALID_ARG, "quantized output needs out_batch_stride to be a multiple of c"); return k; }
     if (!out_scale && B > 0 && n_tok / ratio > 0) { k.fail(CSA_ERR_INVALID_ARG, "out_scale is NULL"); return k; }
-    if ((reinterpret_cast<uintptr_t>(out_scale) & 3u) != 0) { k.fail(CSA_ERR_INVALID_ARG, "out_scale is not 4-byte aligned"); return k; }
+    if (out_dtype == CSA_FP8_E4M3 && (reinterpret_cast<uintptr_t>(out_scale) & 3u) != 0) { k.fail(CSA_ERR_INVALID_ARG, "out_scale is not 4-byte aligned"); return k; }
   } else if (out_scale) {
-    k.fail(CSA_ERR_INVALID_ARG, "out_scale must be NULL unless out_dtype is CSA_FP8_E4M3");
+    k.fail(CSA_ERR_INVALID_ARG, "out_scale must be NULL unless the output is quantized (CSA_FP8_E4M3, CSA_MXFP4)");
     return k;
   }
   if (!(eps > 0.0f) || !std::isfinite(eps)) { k.fail(CSA_ERR_INVALID_ARG, "eps must be positive and finite"); return k; }
@@ -342,7 +342,7 @@ inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t
 
 inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,
                                   const void* pCb, const void* pZb, const float* bias, const float* gamma, float eps,
-                                  int in_dtype, int out_dtype, const void* pool, const float* scale_pool,
+                                  int in_dtype, int out_dtype, const void* pool, const void* scale_pool,
                                   int64_t n_pool, const int32_t* table, int64_t max_blocks, int rope_dims,
                                   float rope_base, int rope_anchor) {
   Check k;
@@ -352,8 +352,9 @@ inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t
   if (!check_rope(k, rope_dims, rope_base, c)) return k;
   if (rope_anchor < 0 || rope_anchor >= ratio) { k.fail(CSA_ERR_INVALID_ARG, "rope_anchor must be in [0, ratio), got " + i2s(rope_anchor)); return k; }
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "in_dtype must be CSA_F32 or CSA_BF16"); return k; }
-  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16 or CSA_FP8_E4M3"); return k; }
-  if (out_dtype == CSA_FP8_E4M3 && ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "fp8 output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
+  if (out_dtype != CSA_F32 && out_dtype != CSA_BF16 && out_dtype != CSA_FP8_E4M3 && out_dtype != CSA_MXFP4) { k.fail(CSA_ERR_UNSUPPORTED, "out_dtype must be CSA_F32, CSA_BF16, CSA_FP8_E4M3 or CSA_MXFP4"); return k; }
+  const bool quant = out_dtype == CSA_FP8_E4M3 || out_dtype == CSA_MXFP4;
+  if (quant && ratio != 4) { k.fail(CSA_ERR_UNSUPPORTED, "quantized output (quantize-on-write) is for C4A keys: ratio must be 4"); return k; }
   if (!(eps > 0.0f) || !std::isfinite(eps)) { k.fail(CSA_ERR_INVALID_ARG, "eps must be positive and finite"); return k; }
   if (n_pool < 0) { k.fail(CSA_ERR_INVALID_ARG, "n_pool must be >= 0"); return k; }
   if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
@@ -368,10 +369,11 @@ inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t
     k.must_be_null(pCb, "prev_Cb", "for ratio 128") && k.must_be_null(pZb, "prev_Zb", "for ratio 128");
   }
   if (!k.ok()) return k;
-  if (out_dtype == CSA_FP8_E4M3) {
+  if (quant) {
     if (!scale_pool && !empty && n_pool > 0) { k.fail(CSA_ERR_INVALID_ARG, "scale_pool is NULL"); return k; }
+    if (out_dtype == CSA_FP8_E4M3 && (reinterpret_cast<uintptr_t>(scale_pool) & 3u) != 0) { k.fail(CSA_ERR_INVALID_ARG, "scale_pool is not 4-byte aligned"); return k; }
   } else if (scale_pool) {
-    k.fail(CSA_ERR_INVALID_ARG, "scale_pool must be NULL unless out_dtype is CSA_FP8_E4M3");
+    k.fail(CSA_ERR_INVALID_ARG, "scale_pool must be NULL unless the output is quantized (CSA_FP8_E4M3, CSA_MXFP4)");
     return k;
   }
   return k;

@@ -222,7 +222,8 @@ def test_rope_validation(lib):
     assert cmp(rd=0, odt=2, osc=A, stride=520) == -1 and "multiple of c" in _err(lib)
     assert cmp(rd=0, odt=2, osc=A, ratio=128, ra=0) == -2 and "ratio must be 4" in _err(lib)
     assert cmp(rd=0, odt=1, osc=A) == -1 and "out_scale must be NULL" in _err(lib)
-    assert cmp(rd=0, odt=3) == -2
+    assert cmp(rd=0, odt=3) == -1 and "out_scale" in _err(lib)      # MXFP4 output needs its scale bytes
+    assert cmp(rd=0, odt=4) == -2
     r = lib.csa_rope
 
     def rp(B=2, T=3, H=4, D=512, pos0=0, rd=64, rb=10000.0, inv=0, dt=1, x=A):

@@ -298,7 +298,8 @@ def test_paged_decode_chain_against_the_oracle_chain():
 from oracle import compressor as oc  # noqa: E402
 
 
-@pytest.mark.parametrize("ratio,c,out", [(4, 512, "bf16"), (4, 128, "fp8"), (128, 512, "bf16"), (4, 192, "f32")])
+@pytest.mark.parametrize("ratio,c,out", [(4, 512, "bf16"), (4, 128, "fp8"), (4, 128, "fp4"), (128, 512, "bf16"),
+                                         (4, 192, "f32")])
 def test_compress_paged_decode_write(ratio, c, out):
     """Sequences at different positions pool their current block into their
     own page slot; sequences not at a block start (and one whose block is
@@ -335,6 +336,9 @@ def test_compress_paged_decode_write(ratio, c, out):
     if out == "fp8":
         pool = torch.full(shape, 0x33, dtype=torch.uint8, device="cuda")
         spool = torch.full((n_pool, per), 5.0, dtype=torch.float32, device="cuda")
+    elif out == "fp4":
+        pool = torch.full((n_pool, per, c // 2), 0x33, dtype=torch.uint8, device="cuda")
+        spool = torch.full((n_pool, per, c // 32), 9, dtype=torch.uint8, device="cuda")
     else:
         pool = torch.full(shape, 3.0, dtype=torch.float32 if out == "f32" else BF, device="cuda")
         spool = None
@@ -363,6 +367,10 @@ def test_compress_paged_decode_write(ratio, c, out):
         if out == "fp8":
             dec = on.decode_e4m3(got) * host(spool)[slot]
             assert np.max(np.abs(dec - ref)) <= np.abs(ref).max() / 448 * 16 + 1e-4
+        elif out == "fp4":
+            dec = on.dequant_mxfp4(got[None], host(spool)[slot][None])[0]
+            # within half the largest E2M1 step (2 at scale 2^E, E = floor(log2 amax) - 2) of each value
+            assert np.max(np.abs(dec - ref)) <= np.abs(ref).max() / 4 + 1e-4
         elif out == "f32":
             assert np.max(np.abs(got - ref)) < 1e-4
         else:

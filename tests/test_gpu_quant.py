@@ -147,3 +147,79 @@ def test_mixed_batch_bf16_latent_and_fp8_key():
     assert np.max(np.abs(host(kv)[:, N - 1] - refs[0][:, 0])) < 2e-2
     assert np.all(host(kv)[:, :N - 1] == 0)
     _check(host(keys)[:, N - 1], host(kscale)[:, N - 1], refs[1][:, 0])
+
+
+# ---------------------------------------------------------------- MXFP4 (the pages' FP4 indexer keys)
+
+def _check_fp4(packed, scales, ref):
+    """packed [.., c/2], scales [.., c/32] (GPU); ref [.., c] fp64 (oracle)."""
+    c = ref.shape[-1]
+    dec = on.dequant_mxfp4(packed, scales)
+    s = np.repeat(on.decode_e8m0(scales), 32, axis=-1)
+    o_p, o_s = on.quant_mxfp4_rows_f32(ref)
+    # the shared exponent may differ only when a block's amax lies next to a power of two
+    blocks = np.abs(ref.reshape(*ref.shape[:-1], c // 32, 32)).max(axis=-1)
+    near_pow2 = np.abs(np.log2(np.maximum(blocks, 1e-30)) - np.round(np.log2(np.maximum(blocks, 1e-30)))) < 1e-4
+    assert np.all((scales == o_s) | near_pow2)
+    v = ref / s
+    a = np.abs(v)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    err = np.abs(dec - ref)
+    assert np.all((err <= (0.5 * step * (1 + 1e-6)) * s + PRE_TOL) | (a > 6)), np.max(err - 0.5 * step * s)
+    # elements agree with the oracle's codes except next to a rounding midpoint
+    same_scale = np.repeat(scales == o_s, 32, axis=-1)
+    dec_o = on.dequant_mxfp4(o_p, o_s)
+    diff = (dec != dec_o) & same_scale
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    near_mid = np.min(np.abs(a[..., None] - mids), axis=-1) <= PRE_TOL / s * 2 + 1e-6 * a
+    assert np.all(near_mid[diff])
+
+
+@pytest.mark.parametrize("B,n_tok,pos0,dtype,R", [
+    (2, 4096, 131072, "bf16", 0),
+    (1, 256, 0, "f32", 0),
+    (3, 37, 8, "bf16", 64),
+])
+def test_mxfp4_keys(B, n_tok, pos0, dtype, R):
+    c = 128
+    inp = synth.compressor_inputs(f"q4.{n_tok}.{pos0}", B, n_tok, c, 4, pos0, dtype=dtype)
+    tdt = torch.float32 if dtype == "f32" else BF
+    d = {k: dev(v, tdt if k != "bias" else torch.float32) for k, v in inp.items()}
+    packed, scales = csa.csa_compress(4, d["Ca"], d["Za"], d["bias"], d["Cb"], d["Zb"], d.get("prev_Cb"),
+                                      d.get("prev_Zb"), pos0=pos0, out_dtype=csa.MXFP4, rope_dims=R)
+    torch.cuda.synchronize()
+    assert packed.shape == (B, n_tok // 4, c // 2) and scales.shape == (B, n_tok // 4, c // 32)
+    ref = oc.compress(inp["Ca"], inp["Za"], inp["bias"], 4, inp["Cb"], inp["Zb"], inp.get("prev_Cb"),
+                      inp.get("prev_Zb"), pos0=pos0, rope_dims=R)
+    _check_fp4(host(packed), host(scales), ref)
+
+
+def test_mxfp4_keys_feed_the_mxfp4_indexer_and_mix_in_a_batch():
+    """A bf16 latent and MXFP4 keys in one batch launch, into cache slots; the
+    keys are what lightning_index reads as CSA_MXFP4 (byte-for-byte hand-over)."""
+    B, N = 4, 64
+    kv = torch.zeros(B, N, 512, dtype=BF, device="cuda")
+    keys = torch.zeros(B, N, 64, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(B, N, 4, dtype=torch.uint8, device="cuda")
+    jobs, refs = [], []
+    for c, out in ((512, kv), (128, keys)):
+        inp = synth.compressor_inputs(f"q4.mix.{c}", B, 4 * N, c, 4, 0, dtype="bf16")
+        d = {k: dev(v, BF if k != "bias" else torch.float32) for k, v in inp.items()}
+        job = dict(ratio=4, Ca=d["Ca"], Za=d["Za"], bias=d["bias"], Cb=d["Cb"], Zb=d["Zb"], pos0=0, out=out,
+                   cache_entry0=0)
+        if c == 128:
+            job["out_scale"] = ks
+        jobs.append(job)
+        refs.append(oc.compress(inp["Ca"], inp["Za"], inp["bias"], 4, inp["Cb"], inp["Zb"], pos0=0))
+    csa.csa_compress_batch(jobs)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(host(kv) - refs[0])) < 2e-2
+    _check_fp4(host(keys), host(ks), refs[1])
+    qp, qs = synth.quant_mxfp4(synth.normal("q4.mix.q", (B, 8, 64, 128)))
+    w = dev(synth.uniform("q4.mix.w", (B, 8, 64)))
+    args = dict(q_pos0=4 * N - 8, qk_dtype=csa.MXFP4, q_scale=dev(qs, torch.uint8), score_dtype=torch.float32)
+    s1 = csa.lightning_index(dev(qp, torch.uint8), w, keys, k_scale=ks, **args)
+    s2 = csa.lightning_index(dev(qp, torch.uint8), w, dev(host(keys), torch.uint8),
+                             k_scale=dev(host(ks), torch.uint8), **args)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)

@@ -88,3 +88,34 @@ def test_mxfp4_rows_round_trip_and_bound():
     assert s1[0, 0] == 126
     # 6.0 -> 7, -1.2 -> 1.0 (code 2, negative: 0xA), 0.4 -> 0.5 (code 1), 2.2 -> 2.0 (code 4)
     assert p1[0, 0] == (7 | (0xA << 4)) and p1[0, 1] == (1 | (4 << 4))
+
+
+def test_mxfp4_shared_exponent_at_powers_of_two():
+    """E = floor(log2 amax) - 2: a block whose amax is 2^e gets E = e - 2 and
+    its largest element lands on 4; the float just below 2^e gets e - 3 and
+    lands on 6 (7.99.. rounds and clamps to 6).  E8M0 decodes to 2^E."""
+    for e in range(-30, 31, 3):
+        blk = np.zeros((2, 32), np.float32)
+        blk[0, 7] = 2.0 ** e
+        blk[1, 7] = -np.nextafter(np.float32(2.0 ** e), np.float32(0))
+        blk[:, 0] = np.float32(2.0 ** (e - 4))          # 1/16 of 2^e: E2M1 0.25 -> rounds to 0
+        packed, scales = on.quant_mxfp4_rows_f32(blk)
+        assert list(scales[:, 0]) == [e - 2 + 127, e - 3 + 127]
+        assert list(on.decode_e8m0(scales[:, 0])) == [2.0 ** (e - 2), 2.0 ** (e - 3)]
+        back = on.dequant_mxfp4(packed, scales)
+        assert back[0, 7] == 2.0 ** e and back[1, 7] == -6 * 2.0 ** (e - 3)
+        assert back[0, 0] == 0.0 and back[1, 0] == 0.5 * 2.0 ** (e - 3)   # 2^(e-4) / 2^(e-3) = 0.5, exact
+
+
+def test_mxfp4_exponent_clamps_at_e8m0_zero():
+    """A block of float32 subnormals: floor(log2 amax) - 2 falls below -127,
+    so E clamps to -127 (E8M0 byte 0) and the elements, scaled by 2^127, are
+    still tiny; at amax = 2^-125, E = -127 exactly."""
+    blk = np.zeros((2, 32), np.float32)
+    blk[0, 3] = np.float32(2.0 ** -140)
+    blk[0, 4] = np.float32(-3 * 2.0 ** -128)            # 3 * 2^-128 / 2^-127 = 1.5: code 3
+    blk[1, 0] = np.float32(2.0 ** -125)
+    packed, scales = on.quant_mxfp4_rows_f32(blk)
+    assert list(scales[:, 0]) == [0, 0]
+    back = on.dequant_mxfp4(packed, scales)
+    assert back[0, 3] == 0.0 and back[0, 4] == np.float32(-3 * 2.0 ** -128) and back[1, 0] == 2.0 ** -125
