@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="csa_hca_decode")
     p.add_argument("--rotate", type=int, default=4, help="cache copies cycled over the steps")
-    p.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graphs")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches instead of HIP graphs (every workload; the counter runs need it)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--batch-invariant", action="store_true",

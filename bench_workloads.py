@@ -77,6 +77,21 @@ def _rand_mxfp4_dev(torch, name, shape_rows, synth):
     return packed, scales
 
 
+def _etime(torch, st, fn, reps):
+    """Eager launches between two events (the counter runs: kernels launched
+    inside a graph are not seen by the profiler's counter collection)."""
+    with torch.cuda.stream(st):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps   # ms
+
+
 def run(args, torch, csa, synth):
     bf = torch.bfloat16
     dn = synth.device_normal
@@ -312,11 +327,12 @@ def run(args, torch, csa, synth):
         for s in stages:
             s[1]()
 
-    ms = _gtime(torch, st, whole, max(2, min(args.steps, 20)))
+    timer = _etime if args.eager else _gtime
+    ms = timer(torch, st, whole, max(2, min(args.steps, 20)))
     per = {}
     best = None
     for name, fn, nbytes, flops, bound in stages:
-        t = _gtime(torch, st, fn, max(2, min(args.steps, 20)))
+        t = timer(torch, st, fn, max(2, min(args.steps, 20)))
         gbs = nbytes / (t * 1e-3) / 1e9
         tfl = flops / (t * 1e-3) / 1e12 if flops else None
         if bound == "hbm":
@@ -345,6 +361,6 @@ def run(args, torch, csa, synth):
         "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": dict(workload=wl, **info, timing="hip_graph"),
+        "data": "synthetic", "config": dict(workload=wl, **info, timing="eager" if args.eager else "hip_graph"),
         "roofline": roof, "stages": per,
     }
