@@ -513,11 +513,11 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     if constexpr (QK == CSA_FP8_E4M3)   // the scale of this lane's key column
       ks[r] = buffer_load_f32(static_cast<const float*>(k_scale) + srow, rows * 4, col * 4);
   };
-  // Every wave runs the whole ring, also one whose entries are all masked or
-  // past N (its loads all read entry N - 1, its tiles are skipped and its
-  // scores are -inf): with no branch around a load into LDS the compiler keeps
-  // track of which LDS array each load in flight fills, and reading qs below
-  // does not wait for the key tiles.
+  // Every wave issues the first tiles, also one whose entries are all masked
+  // or past N (its loads all read entry N - 1): with no branch around a load
+  // into LDS the compiler keeps track of which LDS array each load in flight
+  // fills, and reading qs below does not wait for the key tiles.  Such a
+  // wave skips the tile loop below.
   static_for<0, D - 1>([&](auto rc) { issue(decltype(rc)::value, rc); });
   wait_vm<(D - 1) * OPS>();   // this wave's query and weight loads have landed ...
   // ... and every other wave's: a bare barrier (__syncthreads' release fence
@@ -559,6 +559,22 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
       sc[qi][u / 4] = (e >= vis[qi]) ? -INFINITY : v;
     }
   };
+  if (!streams) {
+    // Nothing of this wave's run is visible to the workgroup's queries (a key
+    // run past N, or past a short sequence): no tile to score.  Its prologue
+    // tile loads are drained, so no load into LDS is left in flight, its
+    // scores are -inf, and the wave ends: wave-uniform, and no barrier
+    // follows the prologue's.
+    wait_vm<0>();
+#pragma unroll
+    for (int tb = 0; tb < TPW; tb += 4) {
+      const int64_t e = e_wave + 16 * (tb + g) + col;
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi)
+        if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, -INFINITY);
+    }
+    return;
+  }
   if constexpr (PIPE) {
     // Software pipeline (prefill, where the MFMAs and the ReLU-weighted sums
     // both take time): tile t's MFMAs are issued before tile t - 1's sums,
