@@ -127,3 +127,28 @@ def test_scores_nonnegative_and_deterministic():
     b = _gpu(d, 4 * 5000 - 1, score_dtype=torch.bfloat16)
     assert np.all(a >= 0)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,q0", [(1, 399), (3, 399), (16, 0), (5, 12000)])
+def test_key_runs_with_nothing_visible_still_write_every_score(T, q0):
+    """Key runs wholly past every query's causal bound but inside N: the
+    waves that own them score no tile and end early, and every one of their
+    entries must still read -inf (the output starts as NaN).  T = 1 takes
+    the decode kernel, T >= 3 the pipelined prefill kernel."""
+    B, N = 2, 5000
+    q = synth.round_bf16(synth.normal(f"ix.idle.{T}.q", (B, T, 64, 128), var=1.0 / 128))
+    w = synth.uniform(f"ix.idle.{T}.w", (B, T, 64))
+    k = synth.round_bf16(synth.normal(f"ix.idle.{T}.k", (B, N, 128)))
+    ref = oi.index_scores(q, w, k, q0, 4)
+    for sd in (torch.float32, torch.bfloat16):
+        s = torch.full((B, T, N), float("nan"), dtype=sd, device="cuda")
+        csa.lightning_index(dev(q, torch.bfloat16), dev(w), dev(k, torch.bfloat16), q_pos0=q0, ratio=4, scores=s)
+        torch.cuda.synchronize()
+        got = host(s)
+        assert not np.isnan(got).any()
+        if sd == torch.float32:
+            index_close(got, ref)
+        else:
+            fin = np.isfinite(ref)
+            assert np.array_equal(np.isfinite(got), fin) and np.all(got[~fin] == -np.inf)
+            assert np.all(np.abs(got[fin] - ref[fin]) <= np.abs(ref[fin]) * 2.0 ** -8 + 1e-6)
