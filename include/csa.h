@@ -137,7 +137,8 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0,
 /*
  * Partial RoPE, shared by the _ex entry points and csa_rope.
  *
- * "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding, under CSA; the
+ * "DeepSeek Technical Reports" (DeepSeek-V4, Hybrid Attention, CSA: position
+ * is handled by a partial rotary embedding) and "DeepSeek V4 结构速览" (the
  * CSA operator graph): compressed entries get RoPE after their RMSNorm at an
  * anchor position, the query gets RoPE at its position, and the attention
  * output gets inverse RoPE on its last 64 dimensions.  The rotation is
@@ -271,8 +272,8 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
 /*
  * lightning_index_pool / topk_select_pool -- the hierarchical sparse indexer.
  *
- * "DeepSeek 模型原理进化史" (CSA2: cross-layer KV and index reuse;
- * hierarchical sparse indexer): a Full-indexer layer scans the whole context
+ * "DeepSeek Technical Reports" (DeepSeek-V4.1, CSA2: Cross-Layer KV and
+ * Index Reuse; Hierarchical Sparse Indexer): a Full-indexer layer scans the whole context
  * (lightning_index + topk_select with a large k = P) and yields a candidate
  * pool per query; a later Reindex layer re-scores with its own query only the
  * pool's entries and takes its Top-k inside the pool; Reuse layers pass an
@@ -492,8 +493,8 @@ int hca_attn_paged(int64_t B, int H, int d, const void* q, const void* kv_pool, 
 /*
  * csa_rope -- partial RoPE (or its inverse) in place on rows of a tensor.
  *
- * "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding; the CSA
- * operator graph: the query is rotated at its position, and so is each raw
+ * "DeepSeek Technical Reports" (Hybrid Attention, CSA: partial RoPE) and
+ * "DeepSeek V4 结构速览" (the CSA operator graph: the query is rotated at its position, and so is each raw
  * latent of the sliding window, whose rows are the keys and values of the
  * window).  x is [B, T, H, D] of dtype (CSA_F32 or CSA_BF16), dense; row
  * (b, t, h) sits at position pos0 + t and its last rope_dims dimensions are

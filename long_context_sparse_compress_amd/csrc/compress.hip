@@ -5,8 +5,9 @@
 // per-channel softmax-weighted sum of 8 raw tokens at stride 4 (C4A: the
 // current block from Ca/Za, the previous block from Cb/Zb, a positional bias
 // on the 8 logits) or 128 raw tokens at stride 128 (C128A), then RMSNorm and,
-// when asked, partial RoPE at the entry's anchor position (Partial Rotary
-// Positional Embedding; the CSA operator graph's RMSNorm + RoPE).
+// when asked, partial RoPE at the entry's anchor position ("DeepSeek
+// Technical Reports", Hybrid Attention, CSA; the CSA operator graph's
+// RMSNorm + RoPE in "DeepSeek V4 结构速览").
 //
 // The work is pure streaming (C128A reads 257 rows' worth of bytes per
 // entry), so the kernel is organised for HBM bandwidth:
@@ -583,7 +584,8 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   int G = 1;
   while (G * 2 * CT <= max_threads && G * 2 * UC <= rows) G *= 2;
   const int threads = CT * G;
-  const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64;
+  // + 64 floats: the RMSNorm sums (red[0..15]) and the fp8 amax (red_max = red + 32)
+  const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64 * sizeof(float);
   const auto* Ca = static_cast<const TI*>(a.Ca);
   const auto* Za = static_cast<const TI*>(a.Za);
   const auto* Cb = static_cast<const TI*>(a.Cb);

@@ -73,8 +73,9 @@ __device__ __forceinline__ float lane_read(int addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
 }
 
-// Partial rotary embedding ("DeepSeek V4 结构速览", Partial Rotary Positional
-// Embedding; the rotation is RoFormer's): pair p of the last R dimensions,
+// Partial rotary embedding ("DeepSeek Technical Reports", Hybrid Attention,
+// CSA; "DeepSeek V4 结构速览", the CSA operator graph; the rotation is
+// RoFormer's): pair p of the last R dimensions,
 // (x[2p], x[2p+1]) of that part, turns by pos * base^(-2p/R).  At a million
 // tokens of context the angle reaches ~1e6 rad, so it is counted in turns in
 // fp64 -- pos * theta / 2pi, whose fractional part is exact -- and only the

@@ -1,7 +1,7 @@
 // Hierarchical sparse indexer: scores of a per-query candidate pool.
 //
-// "DeepSeek 模型原理进化史" (CSA2: cross-layer KV and index reuse; the
-// hierarchical sparse indexer): a full indexer pass over the whole context
+// "DeepSeek Technical Reports" (DeepSeek-V4.1, CSA2: Cross-Layer KV and
+// Index Reuse; Hierarchical Sparse Indexer): a full indexer pass over the whole context
 // gives each query a large candidate pool; later Reindex layers score, with
 // their own query, only the entries of that pool.  The score is the indexer
 // equation of "DeepSeek Technical Reports" (DSA):

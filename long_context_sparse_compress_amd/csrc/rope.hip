@@ -1,7 +1,7 @@
 // Partial RoPE (or its inverse) in place on query or window rows.
 //
-// "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding; the CSA
-// operator graph): the query and each raw latent of the sliding window are
+// "DeepSeek Technical Reports" (Hybrid Attention, CSA: partial RoPE) and
+// "DeepSeek V4 结构速览" (the CSA operator graph): the query and each raw latent of the sliding window are
 // rotated at their own positions on their last R dimensions, pair p turning by
 // pos * base^(-2p/R) (RoFormer's rotation).  The compressed entries get theirs
 // in the compressor's epilogue and the output its inverse in the attention

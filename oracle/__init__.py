@@ -24,8 +24,9 @@ Pages and the parts each module follows:
 * ``kv_accounting`` -- "DeepSeek V4 结构速览" (KV cache 账).
 * ``cache`` -- "DeepSeek-V4技术报告解读，全适配国产算力" (3.2, the heterogeneous
   KV cache: paged classical cache, per-request state cache).
-* ``rope`` -- "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding
-  under CSA; RoPE anchors of the compressor; inverse RoPE on the output).
+* ``rope`` -- "DeepSeek Technical Reports" (DeepSeek-V4, Hybrid Attention,
+  CSA: the Partial Rotary Positional Embedding section is named there) and
+  "DeepSeek V4 结构速览" (the CSA operator graph; RoPE anchors of the compressor; inverse RoPE on the output).
 * ``numerics`` -- decoding of the quantized inputs and bf16 score storage.
 
 Parity status: every function is pinned by the CPU tests against closed forms,

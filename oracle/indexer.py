@@ -48,8 +48,8 @@ def index_scores(q, w, k, q_pos0: int, ratio: int = 4, rows=None):
 
 
 def pool_scores(q, w, k, pool):
-    """Scores of a candidate pool ("DeepSeek 模型原理进化史", CSA2: the
-    hierarchical sparse indexer re-scores, with the layer's own query, only
+    """Scores of a candidate pool ("DeepSeek Technical Reports",
+    DeepSeek-V4.1, CSA2: the Hierarchical Sparse Indexer re-scores, with the layer's own query, only
     the entries of a candidate pool found by a full indexer pass).
 
     q: [B, T, H_I, d_I], w: [B, T, H_I], k: [B, N, d_I], pool: [B, T, P]

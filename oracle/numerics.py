@@ -66,17 +66,6 @@ def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return blocks.reshape(vals.shape)
 
 
-def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    """uint16 bfloat16 bit patterns -> float64."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
-
-
-def store_f32(x: np.ndarray) -> np.ndarray:
-    """float64 -> nearest float32 (ties to even), as float64."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
-
-
 def store_bf16(x: np.ndarray) -> np.ndarray:
     """float64 -> float32 -> nearest bfloat16 (ties to even), as float64.
 

@@ -4,9 +4,11 @@ Test infrastructure only (see the package docstring).
 
 What the pages define:
 
-* "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding is named under
-  CSA; the CSA operator graph): because compressed entries stand for several
-  tokens, position is handled by a partial rotary embedding.  The query gets
+* "DeepSeek Technical Reports" (DeepSeek-V4, Hybrid Attention, CSA): because
+  compressed entries stand for several tokens, position needs its own
+  treatment, which the report gives in its Partial Rotary Positional
+  Embedding section.
+* "DeepSeek V4 结构速览" (the CSA operator graph; C4A Compressor; HCA):  The query gets
   RoPE at its position; each compressed entry gets RoPE after its RMSNorm,
   at an anchor position whose symbol is lost in the extraction (one for C4A,
   one for HCA); the attention output has inverse RoPE applied to its last 64

@@ -49,8 +49,8 @@ def topk_select(scores, k: int, q_pos0: int, ratio: int = 4, rows=None):
 
 
 def pool_select(scores, pool, k: int, N: int | None = None):
-    """Top-k inside a candidate pool ("DeepSeek 模型原理进化史", CSA2:
-    hierarchical sparse indexer).
+    """Top-k inside a candidate pool ("DeepSeek Technical Reports",
+    DeepSeek-V4.1, CSA2: Hierarchical Sparse Indexer).
 
     scores: [B, T, P] stored scores of the pool slots; pool: [B, T, P] entry
     ids (-1, or an id >= N when N is given, = empty).  The candidates of

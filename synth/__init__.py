@@ -272,3 +272,67 @@ def random_topk_indices(name: str, B: int, T: int, k: int, visible, seed: int = 
                 sel = np.sort(g.choice(v, size=n, replace=False))
             out[b, t, :n] = sel
     return out
+
+
+# --------------------------------------------------------------------------
+# the same input encodings in torch, for tensors drawn on the device
+# --------------------------------------------------------------------------
+
+
+def _torch_round_to_table(mag, table):
+    """torch form of _round_to_table (float64 magnitudes, increasing float64 table)."""
+    import torch
+
+    mag = torch.minimum(mag, table[-1])
+    flat = mag.reshape(-1).contiguous()
+    hi = torch.searchsorted(table, flat, right=False).clamp(1, table.numel() - 1)
+    lo = hi - 1
+    dlo = flat - table[lo]
+    dhi = table[hi] - flat
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    idx = torch.where(pick_hi, hi, lo)
+    idx = torch.where(flat == table[0], torch.zeros_like(idx), idx)
+    return idx.reshape(mag.shape)
+
+
+def device_quant_fp8_rows(x):
+    """quant_fp8_rows for a torch tensor (any device): per row of the last axis
+    scale = amax / 448 in float32 (1 for an all-zero row), codes = E4M3(x / scale)
+    with the quotient in float64, nearest even, saturating.  Bit-identical to
+    quant_fp8_rows.  Returns (codes uint8, scale float32)."""
+    import torch
+
+    x = x.to(torch.float32)
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / torch.tensor(448.0, dtype=torch.float32, device=x.device),
+                        torch.ones_like(amax))
+    v = x.to(torch.float64) / scale.to(torch.float64)[..., None]
+    table = torch.from_numpy(_E4M3).to(x.device)
+    idx = _torch_round_to_table(v.abs(), table).to(torch.uint8)
+    sign = ((v < 0) & (idx != 0)).to(torch.uint8) * 0x80
+    return (idx | sign).contiguous(), scale.contiguous()
+
+
+def device_quant_mxfp4(x):
+    """quant_mxfp4 for a torch tensor (any device): per block of 32 along the
+    last axis E = floor(log2 amax) - 2 (read off frexp, exact; -127 for an
+    all-zero block; clipped to [-127, 127]), elements x / 2^E to E2M1, nearest
+    even, clamped to 6, even element in the low nibble.  Bit-identical to
+    quant_mxfp4.  Returns (packed uint8 [..., n/2], scales uint8 [..., n/32])."""
+    import torch
+
+    n = x.shape[-1]
+    if n % 32:
+        raise ValueError("last axis must be a multiple of 32")
+    blocks = x.to(torch.float32).to(torch.float64).reshape(*x.shape[:-1], n // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                      # amax = m 2^ex, m in [0.5, 1)
+    e = torch.where(amax > 0, ex.to(torch.int64) - 3, torch.full_like(ex, -127, dtype=torch.int64))
+    e = e.clamp(-127, 127)
+    scaled = blocks / torch.exp2(e.to(torch.float64))[..., None]
+    table = torch.from_numpy(_E2M1).to(x.device)
+    idx = _torch_round_to_table(scaled.abs(), table).to(torch.uint8)
+    sign = ((scaled < 0) & (idx != 0)).to(torch.uint8) * 8
+    nib = (idx | sign).reshape(*x.shape[:-1], n)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).contiguous()
+    return packed, (e + 127).to(torch.uint8).contiguous()

@@ -24,6 +24,11 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     import long_context_sparse_compress_amd as csa
+    alt = os.environ.get("CSA_ABI_HOSTCHECK_LIB")
+    if alt:
+        # the sanitized host-only build of the same C-ABI layer (see
+        # test_validation_under_sanitizers)
+        csa.LIB_PATH = alt
     return csa.library()
 
 
@@ -370,3 +375,28 @@ def test_compress_paged_validation(lib):
     assert c_(p0=None) == -1 and "pos0" in _err(lib)
     assert c_(ra=4) == -1 and "rope_anchor" in _err(lib)
     assert c_(npool=0) == 0 and c_(B=0, p0=None, tbl=None) == 0      # nothing to write
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or os.environ.get("CSA_ABI_HOSTCHECK_LIB") is not None,
+                    reason="no g++, or already inside the sanitized run")
+def test_validation_under_sanitizers(tmp_path):
+    """The C-ABI's host side -- capi.cpp and validate.h, with the kernel
+    launchers replaced by host stubs (abi_host_stub.cpp) -- built with g++ under
+    AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts), then
+    every argument-validation test of this file run against it in a child
+    process."""
+    so = tmp_path / "libcsa_hostcheck.so"
+    csrc = os.path.join(ROOT, "long_context_sparse_compress_amd", "csrc")
+    cmd = ["g++", "-std=c++17", "-shared", "-fPIC", "-O1", "-g", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I", csrc, "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined",
+           "-o", str(so), os.path.join(csrc, "capi.cpp"), os.path.join(ROOT, "tests", "abi_host_stub.cpp")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    env = dict(os.environ, CSA_ABI_HOSTCHECK_LIB=str(so), LD_PRELOAD=asan,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run(["python", "-m", "pytest", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+                        os.path.join(ROOT, "tests", "test_abi.py"), "-k", "validation or workspace_query"],
+                       capture_output=True, text=True, env=env, cwd=ROOT)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    assert "passed" in r.stdout and "failed" not in r.stdout

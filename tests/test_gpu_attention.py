@@ -297,3 +297,69 @@ def test_batch_invariant_hca_decode_matches_oracle():
         r, rl = _dense_ref(q, kv, raw, rp0, q0, b, 0, 128, sink)
         _assert_bf16(got[b, 0], r)
         assert max_abs(gl[b, 0], rl) < 1e-3
+
+
+def _scramble(idx, N, name, dup=True, far=False):
+    """Any slot order, -1 anywhere, repeated entries and (far) ids >= N: the
+    forms include/csa.h allows for idx.  Returns (scrambled, the same with ids
+    >= N written as -1)."""
+    g = synth.rng(name)
+    out = idx.copy()
+    B, T, k = out.shape
+    for b in range(B):
+        for t in range(T):
+            row = out[b, t]
+            valid = row[row >= 0]
+            n = len(valid)
+            slots = g.permutation(k)
+            new = np.full(k, -1, dtype=np.int32)
+            new[slots[:n]] = valid                      # shuffled, -1 in between
+            if dup and n >= 4:
+                free = slots[n:]
+                for j in range(min(3, len(free))):      # a few entries twice
+                    new[free[j]] = valid[g.integers(n)]
+            if n >= 2:
+                new[slots[0]] = -1                      # a hole where an entry was
+            if far and k - n > 4:
+                new[slots[-1]] = N + int(g.integers(1000))
+                new[slots[-2]] = 2 ** 30
+            out[b, t] = new
+    as_pad = np.where(out >= N, -1, out).astype(np.int32)
+    return out.astype(np.int32), as_pad
+
+
+@pytest.mark.parametrize("B,T,N,k,q0", [
+    (32, 1, 16384, 512, 65535),      # split decode + combine
+    (2, 40, 4096, 512, 16383 - 39),  # one workgroup per query (prefill shape)
+    (3, 1, 300, 512, 1199),          # fewer entries than k: most slots empty
+])
+def test_sparse_idx_any_order_padding_duplicates(B, T, N, k, q0):
+    name = f"at.scr.{B}.{T}.{N}"
+    q, kv, raw, idx, rp0 = _sparse_case(name, B, T, N, k, q0)
+    scr, pad = _scramble(idx, N, name + ".s", far=True)
+    out = csa.sparse_mqa_attn(q, kv, dev(scr, torch.int32), raw, q_pos0=q0, raw_pos0=rp0)
+    out_pad = csa.sparse_mqa_attn(q, kv, dev(pad, torch.int32), raw, q_pos0=q0, raw_pos0=rp0)
+    torch.cuda.synchronize()
+    got, got_pad = host(out), host(out_pad)
+    # ids >= N are padding exactly as -1 is
+    assert np.array_equal(got, got_pad)
+    for b in range(B):
+        for t in sorted({0, T // 2, T - 1}):
+            _assert_bf16(got[b, t], _sparse_ref(q, kv, pad, raw, rp0, q0, b, t))
+
+
+def test_sparse_idx_whole_tiles_of_padding():
+    """Slot runs of 32 and 64 -1s (whole row tiles) between valid slots, split decode."""
+    B, N, k, q0 = 16, 16384, 512, 65535
+    q, kv, raw, idx, rp0 = _sparse_case("at.holes", B, 1, N, k, q0)
+    g = synth.rng("at.holes.s")
+    scr = np.full_like(idx, -1)
+    for b in range(B):
+        valid = idx[b, 0][idx[b, 0] >= 0][:320]
+        pos = np.concatenate([np.arange(0, 32), np.arange(96, 192), np.arange(256, 448)])   # 320 slots
+        scr[b, 0, pos] = g.permutation(valid)
+    out = csa.sparse_mqa_attn(q, kv, dev(scr, torch.int32), raw, q_pos0=q0, raw_pos0=rp0)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        _assert_bf16(got[b, 0], _sparse_ref(q, kv, scr, raw, rp0, q0, b, 0))

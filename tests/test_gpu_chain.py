@@ -11,7 +11,7 @@ def test_tiny_chain_all_rows():
     x = chain.inputs()
     g = chain.run_gpu(x)
     o = chain.run_oracle(x)
-    rep = chain.compare(g, o)
+    rep = chain.compare(g, o, x=x)
     assert rep["topk_rows_equal"] >= 250
 
 
@@ -20,5 +20,5 @@ def test_tiny_chain_with_rope():
     x = chain.inputs()
     g = chain.run_gpu(x, rope=64)
     o = chain.run_oracle(x, rope=64)
-    rep = chain.compare(g, o)
+    rep = chain.compare(g, o, x=x, rope=64)
     assert rep["topk_rows_equal"] >= 250

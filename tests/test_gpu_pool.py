@@ -1,7 +1,7 @@
 """GPU parity of the hierarchical sparse indexer (lightning_index_pool,
 topk_select_pool) against the oracle, through the C ABI.
 
-Page: "DeepSeek 模型原理进化史" (CSA2: a full indexer pass yields a candidate
+Page: "DeepSeek Technical Reports" (DeepSeek-V4.1, CSA2: a full indexer pass yields a candidate
 pool; Reindex layers re-score only the pool with their own query).
 Tolerances as for lightning_index: fp32 scores 1e-3 relative (plus a floor of
 1e-5 of the row's largest score), bf16 scores within one bf16 ulp of the

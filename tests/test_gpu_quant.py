@@ -70,6 +70,20 @@ def test_fp8_keys(B, n_tok, pos0, dtype, R):
     _check(host(codes), host(scale), ref)
 
 
+def test_fp8_wide_rows_fp32_many_workgroups():
+    """fp32 inputs with c = 1024 and 1,024 entries: one 256-thread row group per
+    workgroup (the launch shape whose RMSNorm and amax reductions use only the
+    small reduction area of the workgroup's LDS)."""
+    B, n_tok, c = 1, 4096, 1024
+    inp = synth.compressor_inputs("q8.wide", B, n_tok, c, 4, 0)
+    d = {k: dev(v) for k, v in inp.items()}
+    codes, scale = csa.csa_compress(4, d["Ca"], d["Za"], d["bias"], d["Cb"], d["Zb"], out_dtype=torch.uint8)
+    torch.cuda.synchronize()
+    ref = oc.compress(inp["Ca"], inp["Za"], inp["bias"], 4, inp["Cb"], inp["Zb"])
+    assert codes.shape == (B, n_tok // 4, c)
+    _check(host(codes), host(scale), ref)
+
+
 def test_fp8_key_into_cache_slot_at_decode():
     """A decode step writes entry 16,383 of every sequence's fp8 key cache and
     its scale in place; nothing else in the caches changes."""

@@ -4,7 +4,8 @@ on query and window rows, the compressor's RoPE at the entry anchor
 inverse RoPE (sparse_mqa_attn_ex / hca_attn_ex: one-workgroup, split +
 combine, batch-invariant and fp32 paths).
 
-Page: "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding; RMSNorm +
+Pages: "DeepSeek Technical Reports" (DeepSeek-V4, Hybrid Attention, CSA:
+position handled by partial RoPE) and "DeepSeek V4 结构速览" (RMSNorm +
 RoPE in the compressor; inverse RoPE on the last 64 output dims).
 Tolerances: fp32 rows 2e-6 max-abs (|x| ~ 1; the angles are fp64, the
 rotation fp32); bf16 rows one bf16 ulp of the result (2^-8 |ref|, plus a

@@ -138,3 +138,14 @@ def test_key_range_spreads(e, ties):
     x = synth.round_bf16(np.sign(synth.normal(f"tk.sign{e}", ex.shape)) * np.exp2(ex))
     got = _run(dev(x, torch.bfloat16), 512, 65535)
     _check(got, ot.topk_select(x, 512, 65535, 4))
+
+
+@pytest.mark.parametrize("dtype,N,k,ties", [
+    ("f32", 16384, 512, None),    # fp32 row in LDS: 64 KiB of keys + the histogram
+    ("f32", 18432, 2048, 16),     # the longest fp32 row the LDS path takes, max k, ties
+    ("bf16", 30001, 512, None),   # bf16 row with N % 8 != 0: the LDS path, not the register one
+])
+def test_lds_path_large_rows(dtype, N, k, ties):
+    """Rows whose LDS copy needs more than 64 KiB of dynamic LDS."""
+    x, d = _scores(f"tk.lds{N}", 3, 1, N, dtype, ties=ties)
+    _check(_run(d, k, 4 * N - 1), ot.topk_select(x, k, 4 * N - 1, 4))

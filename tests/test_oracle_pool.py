@@ -1,7 +1,8 @@
 """Pins of the hierarchical-indexer oracles (pool scoring and Top-k inside a
 candidate pool).
 
-Page: "DeepSeek 模型原理进化史" (CSA2: cross-layer KV and index reuse; the
+Page: "DeepSeek Technical Reports" (DeepSeek-V4.1, CSA2: Cross-Layer KV and Index
+Reuse; the
 hierarchical sparse indexer -- a full indexer pass over the whole context
 yields a large candidate pool, and later Reindex layers re-score only inside
 that pool with their own query).  The pins tie both functions to the full

@@ -44,11 +44,51 @@ def test_row_quantizer_bounds():
     y[3] = 0.0
     codes, scale = on.quant_fp8_rows_f32(y)
     assert scale[3] == 1.0 and np.all(codes[3] == 0)
-    back = on.decode_e4m3(codes) * scale[:, None]
+    back = on.dequant_fp8_rows(codes, scale)
     # each row's largest magnitude maps to 448 (up to the fp32 division), and
     # every element is within half an E4M3 step of its value
     assert np.all(np.abs(on.decode_e4m3(codes)).max(axis=1)[np.arange(50) != 3] == 448.0)
     step = np.exp2(np.floor(np.log2(np.maximum(np.abs(y / scale[:, None]), 2.0 ** -6))) - 3)
+    assert np.all(np.abs(back - y) <= 0.5 * step * scale[:, None] * (1 + 1e-6) + 1e-30)
+
+
+def test_dequant_fp8_rows_hand_decoded():
+    """x = E4M3(code) * scale of the code's row.  Codes decoded by hand from the
+    OCP E4M3 bit fields: 0x38 = 2^0 = 1, 0x40 = 2^1 = 2, 0xB8 = -1, 0x7E =
+    1.75 * 2^8 = 448, 0x01 = 1/8 * 2^-6 = 2^-9 (subnormal), 0x30 = 2^-1,
+    0x4C = 1.5 * 2^2 = 6, 0x00 = 0, 0xC4 = -(1.5 * 2^1) = -3.  A square block
+    with three distinct row scales: a scale broadcast along the wrong axis, a
+    divide in place of the multiply or a dropped scale each give other values."""
+    codes = np.array([[0x38, 0x40, 0xB8],
+                      [0x7E, 0x01, 0x30],
+                      [0x4C, 0x00, 0xC4]], dtype=np.uint8)
+    scale = np.array([0.5, 3.0, 0.25], dtype=np.float32)
+    want = np.array([[0.5, 1.0, -0.5],
+                     [1344.0, 3.0 * 2.0 ** -9, 1.5],
+                     [1.5, 0.0, -0.75]])
+    got = on.dequant_fp8_rows(codes, scale)
+    assert got.dtype == np.float64 and got.shape == (3, 3)
+    assert np.array_equal(got, want)
+    # batch axes in front: [2, 3, 3] codes with [2, 3] scales, one scale per row
+    codes2 = np.stack([codes, codes[::-1]])
+    scale2 = np.stack([scale, scale * 2])
+    got2 = on.dequant_fp8_rows(codes2, scale2)
+    assert np.array_equal(got2[0], want)
+    assert np.array_equal(got2[1], (want[::-1] / scale[::-1, None]) * (2 * scale)[:, None])
+
+
+def test_dequant_fp8_rows_round_trip():
+    """Per-row quantize-on-write followed by dequant_fp8_rows gives every row back
+    within half an E4M3 step at the row's scale, and each row's largest
+    magnitude exactly (it maps to 448 = amax / scale)."""
+    g = np.random.default_rng(5)
+    y = (g.normal(size=(16, 128)) * np.exp(3 * g.normal(size=(16, 1)))).astype(np.float32)
+    codes, scale = on.quant_fp8_rows_f32(y)
+    back = on.dequant_fp8_rows(codes, scale)
+    amax = np.abs(y).max(axis=1)
+    assert np.allclose(np.abs(back).max(axis=1), amax, rtol=1e-6, atol=0)
+    v = np.abs(y / scale[:, None])
+    step = np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** -6))) - 3)
     assert np.all(np.abs(back - y) <= 0.5 * step * scale[:, None] * (1 + 1e-6) + 1e-30)
 
 

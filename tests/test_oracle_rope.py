@@ -1,8 +1,8 @@
 """Pins of the partial-RoPE oracle and of its use in the compressor and
 attention oracles.
 
-Page: "DeepSeek V4 结构速览" (Partial Rotary Positional Embedding under CSA;
-the compressor's RMSNorm + RoPE at an anchor position; inverse RoPE on the
+Pages: "DeepSeek Technical Reports" (DeepSeek-V4, Hybrid Attention, CSA:
+position handled by partial RoPE) and "DeepSeek V4 结构速览" (the compressor's RMSNorm + RoPE at an anchor position; inverse RoPE on the
 last 64 output dimensions).  The rotation convention (adjacent pairs of the
 last R dimensions, theta_p = base^(-2p/R)) is RoFormer's, a reading; the pins
 below fix it by closed forms, and fix the way the three uses fit together by
