@@ -392,6 +392,31 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_mqa_attn_noalloc -- sparse_mqa_attn for callers that cannot
+ * allocate: code under HIP graph capture, allocation-free serving loops, and
+ * harnesses that forbid hipMalloc.
+ *
+ * The same operation, arguments, rules and results as sparse_mqa_attn with a
+ * workspace (the same kernels and split plan, so the same bits), except that
+ * the decode split's partials live in a static device scratch of 24 MiB that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of a caller workspace.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  The caller still passes every input and
+ * output.  Calls whose split plan needs more than the scratch -- B*T between
+ * 191 and 255 -- return CSA_ERR_WORKSPACE with a message naming the sizes
+ * (use sparse_mqa_attn with a workspace there); B*T <= 190 and B*T >= 256
+ * always fit.  All calls on one GPU share its scratch, which keeps the last
+ * call's partials (nothing in it needs clearing: each call writes every
+ * partial it reads): calls that overlap on one GPU, on any streams, race --
+ * serialise them.  The first call on a device looks the scratch's address up
+ * once with that device current; a failure there returns CSA_ERR_HIP.
+ */
+int sparse_mqa_attn_noalloc(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d,
+                            const void* q, const void* kv_cmp, const int32_t* idx,
+                            const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+                            float scale, int io_dtype, void* out, float* lse, void* stream);
+
+/*
  * sparse_mqa_attn_paged / hca_attn_paged -- decode attention over the
  * heterogeneous KV cache.
  *

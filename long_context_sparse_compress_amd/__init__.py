@@ -17,6 +17,7 @@ import os
 import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
+           "sparse_mqa_attn_noalloc",
            "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "lightning_index_paged",
            "topk_select_paged",
            "sparse_mqa_attn_paged", "hca_attn_paged",
@@ -59,6 +60,8 @@ _SIGS = {
                  _vp, _int, _vp, _vp, _vp, _sz, _vp],
     "sparse_mqa_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _i64, _i64,
                            _int, _f32, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
+    "sparse_mqa_attn_noalloc": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _i64, _i64,
+                                _int, _f32, _int, _vp, _vp, _vp],
     "hca_attn_ex": [_i64, _i64, _i64, _int, _i64, _int, _int, _vp, _vp, _vp, _i64, _i64, _int, _f32,
                     _vp, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
 }
@@ -329,6 +332,23 @@ def sparse_mqa_attn(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, window=128, sca
                                       rope_base, _ptr(ws), wsb, _stream(stream))
     _check(st, "sparse_mqa_attn")
     return (out, lse) if return_lse else out
+
+
+def sparse_mqa_attn_noalloc(q, kv_cmp, idx, kv_raw, *, q_pos0, raw_pos0, out, window=128, scale=None, lse=None,
+                            stream=None):
+    """Stage 4 without any allocation: the split partials live in the library's
+    static scratch (calls on one GPU must not overlap).  ``out`` (and ``lse``,
+    optional) are the caller's; nothing is allocated here."""
+    B, T, H, d = q.shape
+    N = kv_cmp.shape[1]
+    k = idx.shape[2]
+    n_raw = kv_raw.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    st = library().sparse_mqa_attn_noalloc(B, T, N, k, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(idx), _ptr(kv_raw),
+                                           raw_pos0, n_raw, window, scale, _dt(q), _ptr(out), _ptr(lse),
+                                           _stream(stream))
+    _check(st, "sparse_mqa_attn_noalloc")
+    return out
 
 
 def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, window=128, scale=None,

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include <cmath>
+#include <mutex>
 
 #include "device.h"
 #include "launch.h"
@@ -800,6 +801,32 @@ hipError_t launch_bf16(Params& P, int64_t nq, int64_t per_split, int flags, hipS
 }
 
 }  // namespace
+
+// Split partials of sparse_mqa_attn_noalloc, for callers that cannot
+// allocate (graph capture, allocation-free serving loops).  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name is only a stand-in: the array's device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kAttnStaticScratchBytes];
+
+hipError_t attn_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return hipSuccess;

@@ -146,6 +146,22 @@ int sparse_mqa_attn(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int 
                             io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
 }
 
+int sparse_mqa_attn_noalloc(int64_t B, int64_t T, int64_t N, int k, int64_t q_pos0, int H, int d, const void* q,
+                            const void* kv_cmp, const int32_t* idx, const void* kv_raw, int64_t raw_pos0,
+                            int64_t n_raw, int window, float scale, int io_dtype, void* out, float* lse,
+                            void* stream) {
+  csa::Check ck = csa::check_sparse_noalloc(B, T, N, k, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw,
+                                            window, scale, io_dtype, out, lse);
+  if (!ck.ok()) return finish(ck);
+  if (B == 0 || T == 0) return finish(ck);
+  void* ws = nullptr;
+  const hipError_t e = csa::attn_static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "sparse_mqa_attn_noalloc scratch lookup");
+  csa::AttnArgs a{B, T, N, k, 4, q_pos0, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
+                  nullptr, io_dtype, out, lse, ws, 0, 0, 0.f};
+  return hip_status(csa::launch_attn(a, as_stream(stream)), "sparse_mqa_attn_noalloc launch");
+}
+
 int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
                 const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
                 float scale, const float* sink, int io_dtype, void* out, float* lse, int flags, int rope_dims,

@@ -134,6 +134,9 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// Device address, on the current device, of the attention kernels' static
+// scratch (kAttnStaticScratchBytes bytes); looked up once per device.
+hipError_t attn_static_scratch(void** ptr);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 
 }  // namespace csa

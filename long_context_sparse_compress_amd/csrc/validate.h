@@ -91,6 +91,11 @@ inline size_t attn_workspace_bytes(int64_t B, int64_t T) {
   return size_t(B) * size_t(T) * size_t(s) * attn_split_bytes();
 }
 
+// Size of the static device scratch that sparse_mqa_attn_noalloc's split
+// partials live in: 24 MiB, enough for the split plan of every call with
+// B*T <= 190 (and B*T >= 256 needs none).
+constexpr size_t kAttnStaticScratchBytes = size_t(24) << 20;
+
 // Top-k keeps rows of up to this many candidates in LDS; longer rows use the
 // multi-pass global path, which needs a per-row histogram workspace.
 constexpr int64_t kTopkLdsMax16 = 36864;   // bf16 keys
@@ -295,6 +300,24 @@ inline Check check_sparse(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "sparse_mqa_attn needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");
   }
+  return k;
+}
+
+// sparse_mqa_attn_noalloc: the arguments of sparse_mqa_attn (flags 0, no
+// RoPE), with the split partials in the library's static scratch instead of a
+// caller workspace -- calls whose plan needs more than it are rejected.
+inline Check check_sparse_noalloc(int64_t B, int64_t T, int64_t N, int kk, int64_t q_pos0, int H, int d,
+                                  const void* q, const void* kv_cmp, const void* idx, const void* kv_raw,
+                                  int64_t raw_pos0, int64_t n_raw, int window, float scale, int io_dtype,
+                                  const void* out, const void* lse) {
+  Check k = check_sparse(B, T, N, kk, q_pos0, H, d, q, kv_cmp, idx, kv_raw, raw_pos0, n_raw, window, scale,
+                         io_dtype, out, lse, nullptr, 0, CSA_ATTN_BATCH_INVARIANT);
+  if (!k.ok()) return k;
+  const size_t need = (B == 0 || T == 0) ? 0 : attn_workspace_bytes(B, T);
+  if (need > kAttnStaticScratchBytes)
+    k.fail(CSA_ERR_WORKSPACE, "sparse_mqa_attn_noalloc: the split partials of B*T = " + i2s(B * T) +
+                                  " queries need " + i2s((int64_t)need) + " bytes, more than its static scratch of " +
+                                  i2s((int64_t)kAttnStaticScratchBytes) + " (call sparse_mqa_attn with a workspace)");
   return k;
 }
 

@@ -14,6 +14,10 @@ hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_pool(const IndexPoolArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_rope(const RopeArgs&, hipStream_t) { return hipSuccess; }
+hipError_t attn_static_scratch(void** ptr) {
+  *ptr = nullptr;
+  return hipSuccess;
+}
 }  // namespace csa
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "host stub"; }

@@ -400,3 +400,23 @@ def test_validation_under_sanitizers(tmp_path):
                        capture_output=True, text=True, env=env, cwd=ROOT)
     assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
     assert "passed" in r.stdout and "failed" not in r.stdout
+
+
+def test_noalloc_validation(lib):
+    """sparse_mqa_attn_noalloc: sparse_mqa_attn's argument checks, plus the
+    static scratch's bound (host only: rejected calls make no HIP call)."""
+    f = lib.sparse_mqa_attn_noalloc
+
+    def call(B=32, T=1, N=16384, k=512, q0=65535, H=64, q=A, kv=A, idx=A, raw=A, rp0=65408, nraw=128, out=A,
+             lse=None):
+        return f(B, T, N, k, q0, H, 512, q, kv, idx, raw, rp0, nraw, 128, 0.0442, 1, out, lse, None)
+
+    assert call(H=32) == -2
+    assert call(idx=None) == -1 and "idx" in _err(lib)
+    assert call(out=MIS) == -1
+    assert call(k=2049) == -1
+    assert call(nraw=64) == -1
+    # B*T = 200: the split plan needs 2 x 200 partials of 66,048 bytes > 24 MiB
+    assert call(B=200) == -4 and "static scratch" in _err(lib) and "26419200" in _err(lib)
+    assert call(B=255) == -4
+    assert call(B=0, q=None, kv=None, idx=None, raw=None, out=None) == 0      # nothing to do, no HIP call
