@@ -16,8 +16,8 @@
  * same operations with partial RoPE fused in, and the batch-invariant
  * attention mode), csa_rope (partial RoPE on query or window rows), and
  * lightning_index_pool / topk_select_pool (the hierarchical indexer), and
- * csa_compress_paged / lightning_index_paged / topk_select_paged /
- * sparse_mqa_attn_paged / hca_attn_paged (decode over the paged cache).
+ * csa_compress_paged / csa_compress_paged_chunk / lightning_index_paged /
+ * topk_select_paged / sparse_mqa_attn_paged / hca_attn_paged (the paged cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -477,18 +477,53 @@ int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, con
                        float rope_base, int rope_anchor, void* stream);
 
 /*
+ * csa_compress_paged_chunk -- a chunk of raw tokens per sequence (chunked
+ * prefill) compressed into the paged cache: the same operation as
+ * csa_compress_ex over [B, n_tok, c] (C4A overlapping blocks, C128A
+ * classical blocks), each sequence's chunk starting at its own block start
+ * pos0[b], entry i of sequence b (e = pos0[b] / ratio + i) written to its
+ * page row as csa_compress_paged writes e.  csa_compress_paged is the case
+ * n_tok = ratio.  Pages: "DeepSeek V4 结构速览" (C4A Compressor) and
+ * "DeepSeek-V4技术报告解读，全适配国产算力" (3.2: compressed entries live in
+ * the classical cache, several blocks per request, while tokens not yet
+ * compressed wait in the state cache).
+ *  n_tok       raw tokens per sequence in the chunk; floor(n_tok / ratio)
+ *              entries are written (at most 2^22); trailing tokens are ignored
+ *  Ca, Za      [B, n_tok, c] in_dtype: the chunk's projections
+ *  Cb, Zb      [B, n_tok, c] (C4A): previous-block projections of the
+ *              chunk, read for entries i >= 1 (required when n_tok >= 8);
+ *              NULL for C128A
+ *  prev_Cb/_Zb [B, 4, c] (C4A): previous-block rows of the block before the
+ *              chunk, read for entry 0 of a sequence at pos0 > 0
+ *  the rest    as csa_compress_paged.  Entries whose block is absent
+ *              (outside [0, n_pool) or past max_blocks) are skipped; a
+ *              sequence whose pos0 is negative or not a multiple of ratio
+ *              writes nothing.
+ */
+int csa_compress_paged_chunk(int ratio, int64_t B, int64_t n_tok, int64_t c, const int64_t* pos0,
+                             const void* Ca, const void* Za, const void* Cb, const void* Zb,
+                             const void* prev_Cb, const void* prev_Zb, const float* bias,
+                             const float* gamma, float eps, int in_dtype, int out_dtype, void* pool,
+                             void* scale_pool, int64_t n_pool, const int32_t* block_table,
+                             int64_t max_blocks, int rope_dims, float rope_base, int rope_anchor,
+                             void* stream);
+
+/*
  * lightning_index_paged / topk_select_paged -- the decode indexer and Top-k
  * over the heterogeneous cache (the same operations as lightning_index and
  * topk_select with T = 1 and one position per sequence).
  *
  * lightning_index_paged: scores[b, e] of entry e of sequence b, index keys in
- * k_pool [n_pool, 32, 128] (bf16, or E4M3 codes with k_scale [n_pool, 32]
- * fp32 -- what csa_compress_ex's quantize-on-write produces), entry e at slot
+ * k_pool [n_pool, 32, 128] (bf16; E4M3 codes with k_scale [n_pool, 32]
+ * fp32; or MXFP4 [n_pool, 32, 64] packed E2M1 with k_scale [n_pool, 32, 4]
+ * E8M0 -- what the quantize-on-write compressors produce), entry e at slot
  * e % 32 of block block_table[b][e / 32] (ids outside [0, n_pool) read block
  * 0: the blocks holding a sequence's visible entries must be mapped).
- * q [B, 64, 128] (bf16 or E4M3 with q_scale [B, 64]), w [B, 64];
- * scores [B, 32 * max_blocks]: -inf for e >= floor((seq_pos[b] + 1) / 4).
- * qk_dtype CSA_BF16 or CSA_FP8_E4M3; n_pool >= 1.
+ * q [B, 64, 128] (bf16; E4M3 with q_scale [B, 64]; or MXFP4 [B, 64, 64] with
+ * q_scale [B, 64, 4]), w [B, 64]; scores [B, 32 * max_blocks]: -inf for
+ * e >= floor((seq_pos[b] + 1) / 4).  qk_dtype CSA_BF16, CSA_FP8_E4M3 or
+ * CSA_MXFP4 ("DeepSeek V4 结构速览", Lightning Indexer: the Pro model's QK
+ * path runs in FP4); n_pool >= 1.
  *
  * topk_select_paged: topk_select's selection over scores [B, N] where row b's
  * candidates are e < min(N, floor((seq_pos[b] + 1) / ratio)); idx [B, k],

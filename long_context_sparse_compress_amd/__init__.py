@@ -18,7 +18,8 @@ import torch
 
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
            "sparse_mqa_attn_noalloc",
-           "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "lightning_index_paged",
+           "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "csa_compress_paged_chunk",
+           "lightning_index_paged",
            "topk_select_paged",
            "sparse_mqa_attn_paged", "hca_attn_paged",
            "workspace_bytes", "library", "F32", "BF16",
@@ -42,6 +43,8 @@ _SIGS = {
     "csa_rope": [_i64, _i64, _i64, _i64, _i64, _int, _f32, _int, _int, _vp, _vp],
     "csa_compress_paged": [_int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int, _int, _vp, _vp, _i64,
                            _vp, _i64, _int, _f32, _int, _vp],
+    "csa_compress_paged_chunk": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int,
+                                 _int, _vp, _vp, _i64, _vp, _i64, _int, _f32, _int, _vp],
     "lightning_index_paged": [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _int,
                               _vp],
     "topk_select_paged": [_i64, _i64, _vp, _int, _int, _vp, _int, _vp, _vp, _sz, _vp],
@@ -414,14 +417,37 @@ def csa_compress_paged(ratio, Ca, Za, bias, pool, block_table, pos0, *, prev_Cb=
     return pool
 
 
+def csa_compress_paged_chunk(ratio, Ca, Za, bias, pool, block_table, pos0, *, Cb=None, Zb=None, prev_Cb=None,
+                             prev_Zb=None, gamma=None, eps=1e-6, scale_pool=None, rope_dims=0, rope_base=ROPE_BASE,
+                             rope_anchor=0, stream=None):
+    """Chunked-prefill write into the paged cache: sequence b compresses its chunk
+    Ca, Za [B, n_tok, c] (C4A: with the chunk's Cb, Zb and the block before it,
+    prev_Cb, prev_Zb [B, 4, c]) starting at block start pos0[b] (int64 [B]); entry
+    pos0[b] / ratio + i lands in its page slot of ``pool`` as csa_compress_paged
+    writes it."""
+    B, n_tok, c = Ca.shape
+    st = library().csa_compress_paged_chunk(ratio, B, n_tok, c, _ptr(pos0), _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb),
+                                            _ptr(prev_Cb), _ptr(prev_Zb), _ptr(bias), _ptr(gamma), eps, _dt(Ca),
+                                            _out_dt(pool, c), _ptr(pool), _ptr(scale_pool), pool.shape[0],
+                                            _ptr(block_table), block_table.shape[1], rope_dims, rope_base,
+                                            rope_anchor, _stream(stream))
+    _check(st, "csa_compress_paged_chunk")
+    return pool
+
+
 def lightning_index_paged(q, w, k_pool, block_table, seq_pos, *, qk_dtype=None, q_scale=None, k_scale=None,
                           score_dtype=torch.bfloat16, scores=None, stream=None):
-    """Paged decode indexer: q [B, 64, 128] (bf16, or uint8 E4M3 codes with q_scale [B, 64]),
-    w [B, 64], k_pool [n_pool, 32, 128] (bf16, or uint8 codes with k_scale [n_pool, 32]),
-    block_table [B, max_blocks] int32, seq_pos [B] int64; returns scores [B, 32 * max_blocks]."""
+    """Paged decode indexer: q [B, 64, 128] (bf16, or uint8 E4M3 codes with q_scale [B, 64],
+    or packed MXFP4 [B, 64, 64] with E8M0 q_scale [B, 64, 4]), w [B, 64], k_pool [n_pool, 32, 128]
+    (bf16, or uint8 codes with k_scale [n_pool, 32], or packed MXFP4 [n_pool, 32, 64] with
+    k_scale [n_pool, 32, 4]), block_table [B, max_blocks] int32, seq_pos [B] int64; returns
+    scores [B, 32 * max_blocks]."""
     B, max_blocks = block_table.shape
     if qk_dtype is None:
-        qk_dtype = FP8_E4M3 if q.dtype == torch.uint8 else _dt(q)
+        if q.dtype == torch.uint8:
+            qk_dtype = MXFP4 if q.shape[-1] == 64 else FP8_E4M3
+        else:
+            qk_dtype = _dt(q)
     if scores is None:
         scores = torch.empty(B, 32 * max_blocks, dtype=score_dtype, device=q.device)
     st = library().lightning_index_paged(B, max_blocks, 64, 128, _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_pool),

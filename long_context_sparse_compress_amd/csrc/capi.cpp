@@ -182,19 +182,31 @@ int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, 
                      io_dtype, out, lse, 0, 0, 0.f, workspace, ws_bytes, stream);
 }
 
+int csa_compress_paged_chunk(int ratio, int64_t B, int64_t n_tok, int64_t c, const int64_t* pos0, const void* Ca,
+                             const void* Za, const void* Cb, const void* Zb, const void* prev_Cb, const void* prev_Zb,
+                             const float* bias, const float* gamma, float eps, int in_dtype, int out_dtype, void* pool,
+                             void* scale_pool, int64_t n_pool, const int32_t* block_table, int64_t max_blocks,
+                             int rope_dims, float rope_base, int rope_anchor, void* stream) {
+  csa::Check ck = csa::check_compress_paged(ratio, B, n_tok, c, pos0, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias, gamma,
+                                            eps, in_dtype, out_dtype, pool, scale_pool, n_pool, block_table,
+                                            max_blocks, rope_dims, rope_base, rope_anchor);
+  if (!ck.ok()) return finish(ck);
+  if (n_pool == 0 || B == 0 || n_tok < ratio) return finish(ck);   // nothing to write
+  csa::CompressPagedArgs a{ratio, B, c, pos0, n_tok, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,
+                           out_dtype, pool, scale_pool, n_pool, block_table, max_blocks, rope_dims, rope_base,
+                           rope_anchor};
+  return hip_status(csa::launch_compress_paged(a, as_stream(stream)), "csa_compress_paged launch");
+}
+
 int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,
                        const void* prev_Cb, const void* prev_Zb, const float* bias, const float* gamma, float eps,
                        int in_dtype, int out_dtype, void* pool, void* scale_pool, int64_t n_pool,
                        const int32_t* block_table, int64_t max_blocks, int rope_dims, float rope_base, int rope_anchor,
                        void* stream) {
-  csa::Check ck = csa::check_compress_paged(ratio, B, c, pos0, Ca, Za, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,
-                                            out_dtype, pool, scale_pool, n_pool, block_table, max_blocks, rope_dims,
-                                            rope_base, rope_anchor);
-  if (!ck.ok()) return finish(ck);
-  if (n_pool == 0) return finish(ck);   // no block to write into
-  csa::CompressPagedArgs a{ratio, B, c, pos0, Ca, Za, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype, out_dtype,
-                           pool, scale_pool, n_pool, block_table, max_blocks, rope_dims, rope_base, rope_anchor};
-  return hip_status(csa::launch_compress_paged(a, as_stream(stream)), "csa_compress_paged launch");
+  // one block per sequence: a chunk of ratio raw tokens whose previous block is prev_Cb / prev_Zb
+  return csa_compress_paged_chunk(ratio, B, ratio, c, pos0, Ca, Za, nullptr, nullptr, prev_Cb, prev_Zb, bias, gamma,
+                                  eps, in_dtype, out_dtype, pool, scale_pool, n_pool, block_table, max_blocks,
+                                  rope_dims, rope_base, rope_anchor, stream);
 }
 
 int lightning_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, const void* q, const void* q_scale,

@@ -125,8 +125,9 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                float eps, TO* __restrict__ out, int64_t out_stride, int G,
                                                float* __restrict__ part, int rope_R, double rope_l2b,
                                                int rope_anchor, void* __restrict__ out_scale,
-                                               int64_t scale_stride) {
+                                               int64_t scale_stride, int64_t out_i = -1) {
   constexpr int VEC = Vec<TI>::n;
+  const int64_t io = out_i >= 0 ? out_i : i;   // where the entry is written (a paged row: 0 from its row)
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   constexpr int UC = kChunkRows;
   const int CT = c / VEC;
@@ -329,11 +330,11 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
     uint32_t word = 0;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) word |= f32_to_e2m1(ldexpf(o[v], -E)) << (4 * v);
-    uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (b * out_stride + i * c + ch0) / 2;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (b * out_stride + io * c + ch0) / 2;
     if constexpr (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = word;
     else *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(word);
     if (ct % (32 / VEC) == 0)
-      static_cast<uint8_t*>(out_scale)[(b * scale_stride + i) * (c / 32) + ch0 / 32] = static_cast<uint8_t>(E + 127);
+      static_cast<uint8_t*>(out_scale)[(b * scale_stride + io) * (c / 32) + ch0 / 32] = static_cast<uint8_t>(E + 127);
     return;
   }
   if constexpr (std::is_same_v<TO, uint8_t>) {
@@ -372,10 +373,10 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
     for (int v = 0; v < VEC; v += 4)
       word[v / 4] = f32_to_e4m3(o[v] / scale) | (f32_to_e4m3(o[v + 1] / scale) << 8) |
                     (f32_to_e4m3(o[v + 2] / scale) << 16) | (f32_to_e4m3(o[v + 3] / scale) << 24);
-    uint8_t* dst = reinterpret_cast<uint8_t*>(out + b * out_stride + i * c + ch0);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(out + b * out_stride + io * c + ch0);
     if constexpr (VEC == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
     else *reinterpret_cast<uint32_t*>(dst) = word[0];
-    if (ct == 0) static_cast<float*>(out_scale)[b * scale_stride + i] = scale;
+    if (ct == 0) static_cast<float*>(out_scale)[b * scale_stride + io] = scale;
     return;
   }
   if (g != 0) return;
@@ -394,7 +395,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
       }
     }
   }
-  store_out<TO, VEC>(out + b * out_stride + i * c + ch0, o);
+  store_out<TO, VEC>(out + b * out_stride + io * c + ch0, o);
 }
 
 // C4A workgroups hold at most 512 threads (c / 4 channel threads x 2 row
@@ -426,29 +427,31 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
 // writes nothing (the whole workgroup returns before any barrier).
 template <typename TI, typename TO, int RATIO>
 __global__ void __launch_bounds__(kCompressThreads<RATIO>)
-compress_paged_kernel(int c, const int64_t* __restrict__ pos0s, const TI* __restrict__ Ca,
-                      const TI* __restrict__ Za, const TI* __restrict__ pCb, const TI* __restrict__ pZb,
+compress_paged_kernel(int c, int64_t n_tok, const int64_t* __restrict__ pos0s, const TI* __restrict__ Ca,
+                      const TI* __restrict__ Za, const TI* __restrict__ Cb, const TI* __restrict__ Zb,
+                      const TI* __restrict__ pCb, const TI* __restrict__ pZb,
                       const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
                       TO* __restrict__ pool, void* __restrict__ scale_pool, int64_t n_pool,
                       const int32_t* __restrict__ table, int64_t max_blocks, int G, int rope_R, double rope_l2b,
                       int rope_anchor) {
   constexpr int SH = RATIO == 4 ? 5 : 0;   // log2 entries per block
   const int64_t b = blockIdx.y;
+  const int64_t i = blockIdx.x;            // entry of the chunk
   const int64_t p0 = pos0s[b];
   if (p0 < 0 || p0 % RATIO) return;
-  const int64_t e = p0 / RATIO;
+  const int64_t e = p0 / RATIO + i;
   if ((e >> SH) >= max_blocks) return;
   const int64_t blk = table[b * max_blocks + (e >> SH)];
   if (blk < 0 || blk >= n_pool) return;
   const int64_t row = (blk << SH) + (e & ((int64_t{1} << SH) - 1));
-  // entry 0 of a one-block chunk whose output row is `row` (no batch stride)
+  // entry i of the chunk, written at `row` (no batch stride)
   constexpr bool kFp4 = std::is_same_v<TO, E2M1x2>;
   TO* dst = kFp4 ? reinterpret_cast<TO*>(reinterpret_cast<uint8_t*>(pool) + row * c / 2) : pool + row * c;
   void* sdst = !scale_pool ? nullptr
                : kFp4      ? static_cast<void*>(static_cast<uint8_t*>(scale_pool) + row * (c / 32))
                            : static_cast<void*>(static_cast<float*>(scale_pool) + row);
-  compress_entry<TI, TO, RATIO, false>(0, b, 0, 1, RATIO, c, p0, Ca, Za, nullptr, nullptr, pCb, pZb, bias, gamma,
-                                       eps, dst, 0, G, nullptr, rope_R, rope_l2b, rope_anchor, sdst, 0);
+  compress_entry<TI, TO, RATIO, false>(i, b, 0, 1, n_tok, c, p0, Ca, Za, Cb, Zb, pCb, pZb, bias, gamma, eps, dst, 0,
+                                       G, nullptr, rope_R, rope_l2b, rope_anchor, sdst, 0, 0);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -676,14 +679,17 @@ hipError_t launch_paged_t(const CompressPagedArgs& a, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   const int CT = static_cast<int>(a.c / VEC);
-  const int max_threads = a.B >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
+  const int64_t n_ent = a.n_tok / RATIO;
+  if (n_ent == 0) return hipSuccess;
+  const int max_threads = a.B * n_ent >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
   int G = 1;
   while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
   const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64 * sizeof(float);
   const double l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
-  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO>), dim3(1, static_cast<uint32_t>(a.B)), dim3(CT * G),
-                     smem, s, static_cast<int>(a.c), a.pos0, static_cast<const TI*>(a.Ca),
-                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.prev_Cb),
+  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO>), dim3(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B)),
+                     dim3(CT * G), smem, s, static_cast<int>(a.c), a.n_tok, a.pos0, static_cast<const TI*>(a.Ca),
+                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.Cb), static_cast<const TI*>(a.Zb),
+                     static_cast<const TI*>(a.prev_Cb),
                      static_cast<const TI*>(a.prev_Zb), a.bias, a.gamma, a.eps, static_cast<TO*>(a.pool),
                      a.scale_pool, a.n_pool, a.block_table, a.max_blocks, G, a.rope_dims, l2b, a.rope_anchor);
   return hipGetLastError();

@@ -166,18 +166,31 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 __device__ __forceinline__ void store_score(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_score(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Paged keys (the heterogeneous cache's classical blocks): entry e of
+// sequence b is row (table[b][e / 32] * 32 + e % 32) of the key pool, and the
+// sequence's query sits at seq_pos[b].  A 16-entry tile never straddles a
+// 32-entry block, so paging only moves a tile's base row.
+struct KeyPages {
+  const int32_t* table;
+  int64_t max_blocks, n_pool;
+  const int64_t* seq_pos;
+};
+
 // Grid: x = entry block of 4 * TPW * 16 entries (one TPW-tile run per wave),
 // y = block of QPW queries, z = sequence.  256 threads = 4 waves.  Keys are
 // loaded GT tiles (GT * 16 entries) at a time, one group ahead of the group
 // being computed; OCC is the number of waves per SIMD the register budget is
 // sized for (GT = 8 needs the whole register file: one wave per SIMD).
-template <int QK, int QPW, int TPW, int GT, int OCC, typename TS>
+// PG: keys in the paged pool (decode, T = 1): a tile's block comes from the
+// block table by one wave-uniform load, ids outside the pool read block 0.
+template <int QK, int QPW, int TPW, int GT, int OCC, typename TS, bool PG = false>
 __global__ void __launch_bounds__(256, OCC)
 index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
-                  const void* __restrict__ k_scale, TS* __restrict__ scores) {
+                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg) {
   static_assert(GT % 4 == 0 && TPW % GT == 0, "tiles are stored four at a time");
+  static_assert(!PG || QPW == 1, "paged keys: decode shape");
   constexpr int KG = GT / 4;   // 4-tile score stores per group
   using F = Frag<QK>;
   constexpr int RB = F::kRowBytes;
@@ -211,7 +224,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   for (int qi = 0; qi < QPW; ++qi) {
     int64_t t = t0 + qi;
     if (t >= T) t = T - 1;
-    int64_t v = (q_pos0 + t + 1) / ratio;
+    int64_t v = ((PG ? pg.seq_pos[b] : q_pos0 + t) + 1) / ratio;
     if (v > N) v = N;
     vis[qi] = (t0 + qi < T) ? v : 0;
     vis_max = vis[qi] > vis_max ? vis[qi] : vis_max;
@@ -246,12 +259,24 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     const bool full = eg + GT * 16 <= N;   // wave-uniform: only the last group can run past N
 #pragma unroll
     for (int tt = 0; tt < GT; ++tt) {
-      int64_t e = eg + tt * 16 + col;
-      if (e >= N) e = N - 1;
-      kb[slot][tt].load(full ? kseq + (eg + tt * 16) * RB : k + (krow0 + e) * RB, g);
-      if constexpr (QK == CSA_MXFP4) ksc[slot][tt] = static_cast<const uint8_t*>(k_scale)[(krow0 + e) * 4 + g];
+      int64_t row;   // this lane's key row in k
+      if constexpr (PG) {
+        // N is a whole number of 32-entry blocks: a tile lies wholly inside
+        // or wholly past it; a tile past it (never stored) reads the last one
+        int64_t e0 = eg + tt * 16;
+        if (e0 >= N) e0 = N - 16;
+        int64_t blk = pg.table[b * pg.max_blocks + (e0 >> 5)];
+        if (blk < 0 || blk >= pg.n_pool) blk = 0;
+        row = (blk << 5) + (e0 & 31) + col;
+      } else {
+        int64_t e = eg + tt * 16 + col;
+        if (e >= N) e = N - 1;
+        row = full ? krow0 + eg + tt * 16 + col : krow0 + e;
+      }
+      kb[slot][tt].load((PG || !full) ? k + row * RB : kseq + (eg + tt * 16) * RB, g);
+      if constexpr (QK == CSA_MXFP4) ksc[slot][tt] = static_cast<const uint8_t*>(k_scale)[row * 4 + g];
       else ksc[slot][tt] = 127;
-      if constexpr (QK == CSA_FP8_E4M3) kscale[slot][tt] = static_cast<const float*>(k_scale)[krow0 + e];
+      if constexpr (QK == CSA_FP8_E4M3) kscale[slot][tt] = static_cast<const float*>(k_scale)[row];
       else kscale[slot][tt] = 1.f;
     }
   };
@@ -348,16 +373,6 @@ __device__ __forceinline__ void static_for(Fn&& f) {
     static_for<I + 1, N>(f);
   }
 }
-
-// Paged keys (the heterogeneous cache's classical blocks): entry e of
-// sequence b is row (table[b][e / 32] * 32 + e % 32) of the key pool, and the
-// sequence's query sits at seq_pos[b].  A 16-entry tile never straddles a
-// 32-entry block, so paging only moves a tile's base row.
-struct KeyPages {
-  const int32_t* table;
-  int64_t max_blocks, n_pool;
-  const int64_t* seq_pos;
-};
 
 template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS, bool PG = false>
 __global__ void __launch_bounds__(256, PIPE ? 1 : 2)
@@ -670,21 +685,22 @@ hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int QK, int QPW, int TPW, int GT, int OCC>
+template <int QK, int QPW, int TPW, int GT, int OCC, bool PG = false>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
   const int64_t per_wg = 4 * TPW * 16;
   dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg),
             static_cast<uint32_t>((a.T + QPW - 1) / QPW), static_cast<uint32_t>(a.B));
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
+  const KeyPages pg{a.block_table, a.max_blocks, a.n_pool, a.seq_pos};
   if (a.score_dtype == CSA_BF16)
-    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, uint16_t>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, uint16_t, PG>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
-                       static_cast<uint16_t*>(a.scores));
+                       static_cast<uint16_t*>(a.scores), pg);
   else
-    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, float>), grid, dim3(256), 0, s, a.T, a.N,
+    hipLaunchKernelGGL((index_mfma_kernel<QK, QPW, TPW, GT, OCC, float, PG>), grid, dim3(256), 0, s, a.T, a.N,
                        a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
-                       static_cast<float*>(a.scores));
+                       static_cast<float*>(a.scores), pg);
   return hipGetLastError();
 }
 
@@ -697,6 +713,7 @@ hipError_t launch_qk(const IndexArgs& a, hipStream_t s) {
   // query per wave, at two waves per SIMD, measured 13% slower on random
   // data).
   if constexpr (QK == CSA_MXFP4) {
+    if (a.block_table) return launch_mfma<QK, 1, 8, 4, 2, true>(a, s);   // paged decode (T = 1)
     if (a.T <= 2) return launch_mfma<QK, 1, 8, 4, 2>(a, s);
     return launch_mfma<QK, 2, 64, 4, 2>(a, s);
   } else {

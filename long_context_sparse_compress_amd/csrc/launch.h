@@ -32,9 +32,11 @@ struct CompressArgs {
 struct CompressPagedArgs {
   int ratio;
   int64_t B, c;
-  const int64_t* pos0;          // [B] block start of each sequence's block
-  const void *Ca, *Za;          // [B, ratio, c]: the rolling buffer
-  const void *prev_Cb, *prev_Zb;  // [B, 4, c]: the previous block (C4A)
+  const int64_t* pos0;          // [B] chunk start of each sequence (a block start)
+  int64_t n_tok;                // raw tokens per sequence in the chunk (ratio at decode)
+  const void *Ca, *Za;          // [B, n_tok, c]: the chunk (at decode the rolling buffer)
+  const void *Cb, *Zb;          // [B, n_tok, c]: previous-block projections of the chunk (C4A, entries >= 1)
+  const void *prev_Cb, *prev_Zb;  // [B, 4, c]: the block before the chunk (C4A)
   const float* bias;
   const float* gamma;
   float eps;

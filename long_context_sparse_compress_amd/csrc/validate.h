@@ -363,7 +363,8 @@ inline Check check_rope_rows(int64_t B, int64_t T, int64_t H, int64_t D, int64_t
   return k;
 }
 
-inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,
+inline Check check_compress_paged(int ratio, int64_t B, int64_t n_tok, int64_t c, const int64_t* pos0, const void* Ca,
+                                  const void* Za, const void* Cb, const void* Zb,
                                   const void* pCb, const void* pZb, const float* bias, const float* gamma, float eps,
                                   int in_dtype, int out_dtype, const void* pool, const void* scale_pool,
                                   int64_t n_pool, const int32_t* table, int64_t max_blocks, int rope_dims,
@@ -382,14 +383,19 @@ inline Check check_compress_paged(int ratio, int64_t B, int64_t c, const int64_t
   if (n_pool < 0) { k.fail(CSA_ERR_INVALID_ARG, "n_pool must be >= 0"); return k; }
   if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
   if (B > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B must be below 2^31"); return k; }
-  const bool empty = B == 0;
+  // one workgroup of at most 1024 threads per entry: entries * threads stay below 2^32
+  if (n_tok < 0 || n_tok / ratio > (int64_t{1} << 22)) { k.fail(CSA_ERR_INVALID_ARG, "n_tok must be >= 0 with at most 2^22 entries per sequence, got " + i2s(n_tok)); return k; }
+  const bool empty = B == 0 || n_tok < ratio;   // nothing to write
   k.ptr(pos0, "pos0", !empty) && k.ptr(Ca, "Ca", !empty) && k.ptr(Za, "Za", !empty) && k.ptr(bias, "bias", !empty) &&
       k.ptr(gamma, "gamma", false) && k.ptr(pool, "pool", !empty && n_pool > 0) && k.ptr(table, "block_table", !empty);
   if (!k.ok()) return k;
   if (ratio == 4) {
-    k.ptr(pCb, "prev_Cb", !empty) && k.ptr(pZb, "prev_Zb", !empty);
+    // entries after the chunk's first take their previous block from the chunk itself
+    k.ptr(pCb, "prev_Cb", !empty) && k.ptr(pZb, "prev_Zb", !empty) && k.ptr(Cb, "Cb", !empty && n_tok >= 8) &&
+        k.ptr(Zb, "Zb", !empty && n_tok >= 8);
   } else {
-    k.must_be_null(pCb, "prev_Cb", "for ratio 128") && k.must_be_null(pZb, "prev_Zb", "for ratio 128");
+    k.must_be_null(pCb, "prev_Cb", "for ratio 128") && k.must_be_null(pZb, "prev_Zb", "for ratio 128") &&
+        k.must_be_null(Cb, "Cb", "for ratio 128") && k.must_be_null(Zb, "Zb", "for ratio 128");
   }
   if (!k.ok()) return k;
   if (quant) {
@@ -412,16 +418,16 @@ inline Check check_index_paged(int64_t B, int64_t max_blocks, int H_I, int d_I, 
   if (B < 0) { k.fail(CSA_ERR_INVALID_ARG, "B must be >= 0"); return k; }
   if (max_blocks < 1 || max_blocks > (int64_t{1} << 26)) { k.fail(CSA_ERR_INVALID_ARG, "max_blocks must be in [1, 2^26]"); return k; }
   if (H_I != CSA_INDEX_HEADS || d_I != CSA_INDEX_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "indexer shape must be H_I=64, d_I=128"); return k; }
-  if (qk_dtype != CSA_BF16 && qk_dtype != CSA_FP8_E4M3) { k.fail(CSA_ERR_UNSUPPORTED, "paged keys are bf16 or fp8 E4M3"); return k; }
+  if (qk_dtype != CSA_BF16 && qk_dtype != CSA_FP8_E4M3 && qk_dtype != CSA_MXFP4) { k.fail(CSA_ERR_UNSUPPORTED, "paged keys are bf16, fp8 E4M3 or MXFP4"); return k; }
   if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
   if (B > 0 && n_pool < 1) { k.fail(CSA_ERR_INVALID_ARG, "the key pool holds no block"); return k; }
   if (B * max_blocks * 32 > (int64_t{1} << 40)) { k.fail(CSA_ERR_INVALID_ARG, "B * max_blocks too large"); return k; }
   const bool empty = B == 0;
-  const bool fp8 = qk_dtype == CSA_FP8_E4M3;
+  const bool quant = qk_dtype == CSA_FP8_E4M3 || qk_dtype == CSA_MXFP4;
   k.ptr(q, "q", !empty) && k.ptr(w, "w", !empty) && k.ptr(kpool, "k_pool", !empty) &&
       k.ptr(table, "block_table", !empty) && k.ptr(seq_pos, "seq_pos", !empty) && k.ptr(scores, "scores", !empty);
   if (!k.ok()) return k;
-  if (fp8) {
+  if (quant) {
     k.ptr(q_scale, "q_scale", !empty) && k.ptr(kscale, "k_scale", !empty);
   } else {
     k.must_be_null(q_scale, "q_scale", "for bf16") && k.must_be_null(kscale, "k_scale", "for bf16");

@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
                           "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
                           "lightning_index_paged", "topk_select_paged", "csa_compress_paged",
-                          "csa_workspace_bytes",
+                          "csa_compress_paged_chunk", "csa_workspace_bytes",
                           "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -338,7 +338,9 @@ def test_paged_index_topk_validation(lib):
         return ip(B, mb, H, 128, A, qs, A, A, ks, npool, tbl, sp_, dt, A, sd, None)
 
     assert ix(H=32) == -2
-    assert ix(dt=3) == -2 and "bf16 or fp8" in _err(lib)
+    assert ix(dt=0) == -2 and "bf16, fp8 E4M3 or MXFP4" in _err(lib)
+    assert ix(dt=3) == -1 and "q_scale" in _err(lib)        # MXFP4 keys need both scale arrays
+    assert ix(dt=3, qs=A) == -1 and "k_scale" in _err(lib)
     assert ix(dt=2) == -1 and "q_scale" in _err(lib)
     assert ix(dt=1, qs=A) == -1 and "must be NULL" in _err(lib)
     assert ix(npool=0) == -1 and "no block" in _err(lib)
@@ -375,6 +377,28 @@ def test_compress_paged_validation(lib):
     assert c_(p0=None) == -1 and "pos0" in _err(lib)
     assert c_(ra=4) == -1 and "rope_anchor" in _err(lib)
     assert c_(npool=0) == 0 and c_(B=0, p0=None, tbl=None) == 0      # nothing to write
+
+
+def test_compress_paged_chunk_validation(lib):
+    cp = lib.csa_compress_paged_chunk
+
+    def c_(ratio=4, B=4, n=64, c=512, cb=A, pc=A, od=1, sc=None, npool=10, mb=8, tbl=A, p0=A):
+        return cp(ratio, B, n, c, p0, A, A, cb, cb, pc, pc, A, None, 1e-6, 1, od, A, sc, npool, tbl, mb, 0, 10000.0, 0,
+                  None)
+
+    # the pointers are fake: every call below must fail validation or have nothing to write
+    assert c_(n=-1) == -1 and "n_tok" in _err(lib)
+    assert c_(n=4 * ((1 << 22) + 1)) == -1 and "2^22" in _err(lib)
+    assert c_(cb=None) == -1 and "Cb" in _err(lib)          # more than one entry: the chunk's own previous blocks
+    assert c_(pc=None) == -1 and "prev_Cb" in _err(lib)
+    # C128A takes no Cb / prev_Cb: with them absent, the call gets as far as the scale_pool check
+    assert c_(ratio=128, cb=None, pc=None, n=256, sc=A) == -1 and "scale_pool must be NULL" in _err(lib)
+    assert c_(ratio=128, cb=A, pc=None, n=256) == -1 and "Cb" in _err(lib)
+    assert c_(od=2) == -1 and "scale_pool" in _err(lib)
+    assert c_(n=3) == 0 and c_(n=3, p0=None, tbl=None, cb=None, pc=None) == 0   # fewer tokens than one block
+    assert c_(B=0, p0=None, tbl=None, cb=None, pc=None) == 0
+    # one entry reads prev_Cb only: without Cb the call gets as far as the scale_pool check
+    assert c_(n=4, cb=None, od=2) == -1 and "scale_pool is NULL" in _err(lib)
 
 
 @pytest.mark.skipif(shutil.which("g++") is None or os.environ.get("CSA_ABI_HOSTCHECK_LIB") is not None,

@@ -185,9 +185,10 @@ from helpers import index_close  # noqa: E402
 IDX_POS = [4095, 9000, 65535, 70001, 131071, 333, 12345, 2]
 
 
-def _key_pool(name, seq_pos, fp8):
-    """bf16 keys (or their E4M3 codes + row scales) for every sequence's
-    visible entries, shuffled 32-entry blocks, -1 past each sequence."""
+def _key_pool(name, seq_pos, fmt):
+    """bf16 keys (or their E4M3 codes + row scales, or MXFP4 codes + E8M0
+    scales) for every sequence's visible entries, shuffled 32-entry blocks, -1
+    past each sequence."""
     B = len(seq_pos)
     nblk = [(p + 1) // 128 + 1 for p in seq_pos]
     max_blocks = max(nblk) + 1
@@ -200,18 +201,24 @@ def _key_pool(name, seq_pos, fp8):
         table[b, :nblk[b]] = perm[o:o + nblk[b]]
         o += nblk[b]
     keys = synth.round_bf16(synth.normal(name + ".k", (n_pool, 32, 128)))
-    if fp8:
+    if fmt == "fp8":
         codes, scale = synth.quant_fp8_rows(keys)
         return dev(codes, torch.uint8), dev(scale), on.dequant_fp8_rows(codes, scale), table
+    if fmt == "mxfp4":
+        packed, sc = synth.quant_mxfp4(keys)
+        return dev(packed, torch.uint8), dev(sc, torch.uint8), on.dequant_mxfp4(packed, sc), table
     return dev(keys, BF), None, keys, table
 
 
-def _queries(name, B, fp8):
-    q = synth.normal(name + ".q", (B, 64, 128), var=1.0 if fp8 else 1.0 / 128)
+def _queries(name, B, fmt):
+    q = synth.normal(name + ".q", (B, 64, 128), var=1.0 if fmt != "bf16" else 1.0 / 128)
     w = synth.uniform(name + ".w", (B, 64))
-    if fp8:
+    if fmt == "fp8":
         qc, qs = synth.quant_fp8_rows(q)
         return dev(qc, torch.uint8), dev(qs), on.dequant_fp8_rows(qc, qs), w
+    if fmt == "mxfp4":
+        qp, qs = synth.quant_mxfp4(q)
+        return dev(qp, torch.uint8), dev(qs, torch.uint8), on.dequant_mxfp4(qp, qs), w
     qb = synth.round_bf16(q)
     return dev(qb, BF), None, qb, w
 
@@ -226,27 +233,35 @@ def _oracle_scores(qv, w, keys_host, table, seq_pos):
     return out
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_paged_indexer_and_topk(fp8):
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_paged_indexer_and_topk(fmt):
     """Ragged positions (2 .. 131,071, one with no visible entry), shuffled
-    blocks, bf16 and fp8 keys: scores against the oracle, -inf past each
-    sequence, and Top-k on the same scores equal to the oracle's selection."""
+    blocks, bf16, fp8 and MXFP4 keys: scores against the oracle, -inf past each
+    sequence.  Per-sequence Top-k, stage-isolated: the GPU selects over the
+    oracle's scores (stored in fp32) and must return the oracle's selection."""
     B, K = len(IDX_POS), 512
-    kp, ks, keys_host, table = _key_pool(f"pg.ix{int(fp8)}", IDX_POS, fp8)
-    q, qs, qv, w = _queries(f"pg.ix{int(fp8)}", B, fp8)
+    kp, ks, keys_host, table = _key_pool(f"pg.ix.{fmt}", IDX_POS, fmt)
+    q, qs, qv, w = _queries(f"pg.ix.{fmt}", B, fmt)
     sp = torch.tensor(IDX_POS, dtype=torch.int64, device="cuda")
     s = csa.lightning_index_paged(q, dev(w), kp, dev(table, torch.int32), sp, q_scale=qs, k_scale=ks,
                                   score_dtype=torch.float32)
-    idx = csa.topk_select_paged(s, K, sp)
     torch.cuda.synchronize()
-    hs, hi = host(s), host(idx)
+    hs = host(s)
     ref = _oracle_scores(qv, w, keys_host, table, IDX_POS)
+    Nmax = hs.shape[1]
+    ref_rows = np.full((B, Nmax), -np.inf, dtype=np.float32)
     for b, pos in enumerate(IDX_POS):
         vis = (pos + 1) // 4
         if vis:
             index_close(hs[b, :vis][None], ref[b][None])
+            ref_rows[b, :vis] = ref[b].astype(np.float32)
         assert np.all(np.isneginf(hs[b, vis:]))
-        want = np.sort(ot.select_row(hs[b], vis, K))
+    idx = csa.topk_select_paged(dev(ref_rows), K, sp)
+    torch.cuda.synchronize()
+    hi = host(idx)
+    for b, pos in enumerate(IDX_POS):
+        vis = (pos + 1) // 4
+        want = np.sort(ot.select_row(ref_rows[b].astype(np.float64), vis, K))
         want = np.concatenate([want[want >= 0], want[want < 0]])
         assert np.array_equal(hi[b], want), b
 
@@ -258,8 +273,8 @@ def test_paged_decode_chain_against_the_oracle_chain():
     may differ only between entries whose oracle scores tie within 1e-3; the
     attention is compared where the selections agree."""
     B, K, ring = len(IDX_POS), 512, 256
-    kp, _, keys_host, table = _key_pool("pg.chain", IDX_POS, False)
-    q_i, _, qv, w = _queries("pg.chain", B, False)
+    kp, _, keys_host, table = _key_pool("pg.chain", IDX_POS, "bf16")
+    q_i, _, qv, w = _queries("pg.chain", B, "bf16")
     pool = synth.device_normal("pg.chain.kv", (kp.shape[0], 32, 512), BF)
     win = synth.device_normal("pg.chain.win", (B, ring, 512), BF)
     q = synth.device_normal("pg.chain.q", (B, 64, 512), BF)
@@ -376,4 +391,90 @@ def test_compress_paged_decode_write(ratio, c, out):
         else:
             assert np.max(np.abs(got - ref)) < 2e-2
     assert written.sum() == sum(1 for b, p in enumerate(pos) if p % ratio == 0 and b != absent)
+    assert np.array_equal(hp[~written], hb[~written])
+
+
+@pytest.mark.parametrize("ratio,c,out,n_tok", [(4, 512, "bf16", 256), (4, 128, "fp8", 130), (4, 128, "fp4", 64),
+                                               (128, 512, "bf16", 300), (4, 192, "f32", 36), (128, 256, "f32", 384)])
+def test_compress_paged_chunk_write(ratio, c, out, n_tok):
+    """Chunked prefill into pages: each sequence compresses its own chunk,
+    starting at its own block start, entry by entry into its page slots.
+    The chunks cross page boundaries; one sequence has an absent page in the
+    middle of its chunk (those entries are skipped), one is not at a block
+    start (writes nothing); every other slot is left alone.  Each entry is
+    compared with the oracle's compression of that sequence's chunk."""
+    per = 32 if ratio == 4 else 1
+    n_ent = n_tok // ratio
+    pos = [0, 4 * 1000, 128 * 37, 6] if ratio == 4 else [0, 128 * 7, 128 * 8000, 130]
+    B = len(pos)
+    last = [(p // ratio + max(n_ent, 1) - 1) // per for p in pos]
+    max_blocks = max(last) + 2
+    nblk = [lb + 1 for lb in last]
+    n_pool = sum(nblk) + 3
+    g = np.random.default_rng(zlib.crc32(f"cpc{ratio}{c}{out}{n_tok}".encode()))
+    perm = g.permutation(n_pool)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    absent = 1                                    # the page of this sequence's chunk-middle entry is not mapped
+    e_mid = pos[absent] // ratio + n_ent // 2
+    table[absent, e_mid // per] = -1
+    dtype = "f32" if out == "f32" else "bf16"
+    tdt = torch.float32 if dtype == "f32" else BF
+    inp = [synth.compressor_inputs(f"cpc.{ratio}.{c}.{n_tok}.{b}", 1, n_tok, c, ratio, p - p % ratio, dtype=dtype)
+           for b, p in enumerate(pos)]
+    cat = {nm: np.concatenate([x[nm] for x in inp]) for nm in (["Ca", "Za", "Cb", "Zb"] if ratio == 4 else
+                                                               ["Ca", "Za"])}
+    bias = inp[0]["bias"]
+    if ratio == 4:
+        for nm in ("prev_Cb", "prev_Zb"):
+            cat[nm] = np.concatenate([x.get(nm, np.zeros((1, 4, c), np.float32)) for x in inp])
+    shape = (n_pool, per, c) if per > 1 else (n_pool, c)
+    if out == "fp8":
+        pool = torch.full(shape, 0x33, dtype=torch.uint8, device="cuda")
+        spool = torch.full((n_pool, per), 5.0, dtype=torch.float32, device="cuda")
+    elif out == "fp4":
+        pool = torch.full((n_pool, per, c // 2), 0x33, dtype=torch.uint8, device="cuda")
+        spool = torch.full((n_pool, per, c // 32), 9, dtype=torch.uint8, device="cuda")
+    else:
+        pool = torch.full(shape, 3.0, dtype=torch.float32 if out == "f32" else BF, device="cuda")
+        spool = None
+    before = pool.clone()
+    d = {nm: dev(v, tdt) for nm, v in cat.items()}
+    csa.csa_compress_paged_chunk(ratio, d["Ca"], d["Za"], dev(bias), pool, dev(table, torch.int32),
+                                 torch.tensor(pos, dtype=torch.int64, device="cuda"), Cb=d.get("Cb"),
+                                 Zb=d.get("Zb"), prev_Cb=d.get("prev_Cb"), prev_Zb=d.get("prev_Zb"),
+                                 scale_pool=spool, rope_dims=64, rope_anchor=ratio - 1)
+    torch.cuda.synchronize()
+    hp, hb = host(pool), host(before)
+    written = np.zeros(hp.shape[:2] if per > 1 else hp.shape[:1], dtype=bool)
+    for b, p in enumerate(pos):
+        if p % ratio:
+            continue
+        x = inp[b]
+        ref = oc.compress(x["Ca"], x["Za"], bias, ratio, x.get("Cb"), x.get("Zb"), x.get("prev_Cb"),
+                          x.get("prev_Zb"), pos0=p, rope_dims=64, rope_anchor=ratio - 1)[0]
+        for i in range(n_ent):
+            e = p // ratio + i
+            blk = table[b, e // per]
+            if blk < 0:
+                continue
+            slot = (blk, e % per) if per > 1 else (blk,)
+            written[slot] = True
+            got = hp[slot]
+            if out == "fp8":
+                dec = on.decode_e4m3(got) * host(spool)[slot]
+                assert np.max(np.abs(dec - ref[i])) <= np.abs(ref[i]).max() / 448 * 16 + 1e-4, (b, i)
+            elif out == "fp4":
+                dec = on.dequant_mxfp4(got[None], host(spool)[slot][None])[0]
+                assert np.max(np.abs(dec - ref[i])) <= np.abs(ref[i]).max() / 4 + 1e-4, (b, i)
+            elif out == "f32":
+                assert np.max(np.abs(got - ref[i])) < 1e-4, (b, i)
+            else:
+                assert np.max(np.abs(got - ref[i])) < 2e-2, (b, i)
+    skipped = sum(1 for i in range(n_ent) if table[absent, (pos[absent] // ratio + i) // per] < 0)
+    assert skipped >= 1
+    assert written.sum() == 3 * n_ent - skipped
     assert np.array_equal(hp[~written], hb[~written])
