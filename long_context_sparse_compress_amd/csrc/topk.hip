@@ -15,13 +15,15 @@
 // in ascending index order by an ordered compaction (block-wide exclusive
 // scan of per-thread counts), so the result is deterministic.
 //
-// Two paths:
+// Paths:
 //  * rows of up to ~36K bf16 (~18K fp32) keys: one 1024-thread workgroup per
-//    row holds the whole row in LDS and runs every pass there;
-//  * longer rows (the 1M-context decode has 262,144 candidates): S workgroups
-//    per row, one slice each; per-digit histograms are merged in global
-//    workspace with atomics, one kernel per pass, then a count kernel and an
-//    ordered write kernel.
+//    row holds the whole row in registers or LDS and runs every pass there;
+//  * longer bf16 rows (the 1M-context decode has 262,144 candidates): slices
+//    of 16,384 keys, one workgroup each, a full 16-bit histogram per slice,
+//    two launches (below);
+//  * longer fp32 rows: S workgroups per row, one slice each; per-digit
+//    histograms are merged in global workspace with atomics, one kernel per
+//    pass, then a count kernel and an ordered write kernel.
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -60,6 +62,44 @@ __device__ __forceinline__ KT load_key(const KT* row, int64_t i) {
   return key_of(row[i]);
 }
 
+// Wave-wide inclusive scans on the DPP cross-lane paths (no LDS round trip):
+// Hillis-Steele shifts inside each row of 16 lanes, then the row totals are
+// carried across rows with the row broadcasts of lanes 15 and 31.
+#define CSA_DPP(old, x, ctrl, rmask, bound0) \
+  static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(x), ctrl, rmask, 0xf, bound0))
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
+  x += CSA_DPP(0u, x, 0x111, 0xf, true);   // row_shr:1
+  x += CSA_DPP(0u, x, 0x112, 0xf, true);   // row_shr:2
+  x += CSA_DPP(0u, x, 0x114, 0xf, true);   // row_shr:4
+  x += CSA_DPP(0u, x, 0x118, 0xf, true);   // row_shr:8
+  x += CSA_DPP(0u, x, 0x142, 0xa, false);  // row_bcast:15 into rows 1 and 3
+  x += CSA_DPP(0u, x, 0x143, 0xc, false);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_total_add(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_add(x)), 63));
+}
+// min / max over the wave (lanes out of a row keep the identity)
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x111, 0xf, false));
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x112, 0xf, false));
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x114, 0xf, false));
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x118, 0xf, false));
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x142, 0xa, false));
+  x = min(x, CSA_DPP(0xffffffffu, x, 0x143, 0xc, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, CSA_DPP(0u, x, 0x111, 0xf, false));
+  x = max(x, CSA_DPP(0u, x, 0x112, 0xf, false));
+  x = max(x, CSA_DPP(0u, x, 0x114, 0xf, false));
+  x = max(x, CSA_DPP(0u, x, 0x118, 0xf, false));
+  x = max(x, CSA_DPP(0u, x, 0x142, 0xa, false));
+  x = max(x, CSA_DPP(0u, x, 0x143, 0xc, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+#undef CSA_DPP
+
 // Find the digit whose bin holds the rem-th largest key (1-based), given the
 // digit histogram `hist` of nb <= 2048 bins (LDS or global).  Runs on wave 0:
 // each lane first loads its (at most 32) bins into registers, so the search
@@ -78,12 +118,8 @@ __device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32
     sum += h[q];
   }
   // inclusive suffix sums over lanes: S[l] = sum over lanes >= l
-  uint32_t S = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_down(S, o, 64);
-    if (lane + o < 64) S += v;
-  }
+  const uint32_t incl = wave_incl_add(sum);
+  const uint32_t S = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63)) - incl + sum;
   const uint64_t ball = __ballot(S >= rem);
   const int L = 63 - __clzll(static_cast<long long>(ball));   // highest lane with S >= rem
   if (lane == L) {
@@ -104,26 +140,24 @@ __device__ void resolve_digit(const uint32_t* hist, int nb, uint32_t rem, uint32
 // Block-wide exclusive scan of one value per thread (blockDim.x <= 1024):
 // a shuffle scan inside each wave, then wave 0 scans the (at most 16) wave
 // totals the same way.  `tmp` holds >= 17 words; `total` gets the block sum.
+// For 64-bit values the two 32-bit halves are scanned apart: callers pack
+// 16-bit counts whose sums never carry out of their field.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) { return wave_incl_add(x); }
+__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
+  return static_cast<uint64_t>(wave_incl_add(static_cast<uint32_t>(x))) |
+         (static_cast<uint64_t>(wave_incl_add(static_cast<uint32_t>(x >> 32))) << 32);
+}
+
 template <typename U>
 __device__ U block_exclusive_scan_t(U v, U* tmp, U* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  U x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const U y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const U x = wave_incl_scan(v);
   if (lane == 63) tmp[wid] = x;
   __syncthreads();
   if (wid == 0) {
     const U w0 = lane < nw ? tmp[lane] : U(0);
-    U t = w0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const U y = __shfl_up(t, o, 64);
-      if (lane >= o) t += y;
-    }
+    const U t = wave_incl_scan(w0);
     if (lane < nw) tmp[lane] = t - w0;
     if (lane == nw - 1) tmp[16] = t;
   }
@@ -143,8 +177,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
 // position seq_pos[row / T] in a ragged decode batch.
 __device__ __forceinline__ int64_t row_visible(int64_t row, int64_t T, int64_t q_pos0, int ratio, int64_t N,
                                                const int64_t* seq_pos) {
-  const int64_t pos = seq_pos ? seq_pos[row / T] : q_pos0 + row % T;
-  const int64_t v = (pos + 1) / ratio;
+  int64_t b, t;
+  if (T == 1) {
+    b = row;
+    t = 0;
+  } else if (((row | T) >> 31) == 0) {
+    b = static_cast<uint32_t>(row) / static_cast<uint32_t>(T);
+    t = static_cast<uint32_t>(row) - static_cast<uint32_t>(b) * static_cast<uint32_t>(T);
+  } else {
+    b = row / T;
+    t = row - b * T;
+  }
+  const int64_t pos = seq_pos ? seq_pos[b] : q_pos0 + t;
+  // ratio is a power of two: 4 or 128, or 1 for pool rows
+  const int64_t v = pos < 0 ? 0 : (pos + 1) >> __builtin_ctz(static_cast<unsigned>(ratio));
   return v < N ? v : N;
 }
 
@@ -159,7 +205,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
   for (int it = 0; it < 4; ++it) {
     if (!pending) break;
     const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-    const uint32_t lb = __shfl(bin, leader, 64);
+    const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
     const uint64_t same = __ballot(active && bin == lb) & pending;
     if (lane == leader) atomicAdd(&hist[lb], static_cast<uint32_t>(__popcll(same)));
     pending &= ~same;
@@ -247,11 +293,8 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
       kmin = kk < kmin ? kk : kmin;
       kmax = kk > kmax ? kk : kmax;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(kmin, o, 64)));
-      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, o, 64)));
-    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
     if ((tid & 63) == 0) {
       atomicMin(&tmp[24], kmin);
       atomicMax(&tmp[25], kmax);
@@ -394,11 +437,8 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
       if ((valid[c] >> (2 * j + 1)) & 1u) { kmin = min(kmin, hi); kmax = max(kmax, hi); }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(kmin, o, 64)));
-    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, o, 64)));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if ((tid & 63) == 0) {
     atomicMin(&tmp[24], kmin);
     atomicMax(&tmp[25], kmax);
@@ -600,8 +640,8 @@ topk_count_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t
     gt += kk > K;
     eq += kk == K;
   }
-  gt = wave_sum_u32(gt);
-  eq = wave_sum_u32(eq);
+  gt = wave_total_add(gt);
+  eq = wave_total_add(eq);
   if ((threadIdx.x & 63) == 0) {
     red[0][threadIdx.x >> 6] = gt;
     red[1][threadIdx.x >> 6] = eq;
@@ -662,28 +702,36 @@ topk_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t
 }
 
 // ------------------------------------------------------------ long bf16 rows
-// Rows too long for one workgroup (the 1M-context decode: 262,144 keys): S
-// slices per row, one 256-thread workgroup per slice holding its keys in
-// registers (thread t, chunk c: keys lo + 8 (c * 256 + t) .. + 7).
-//   G1  histogram of the top 11 key bits of the slice, merged into the row's
-//       histogram with one atomic per non-empty bin;
-//   G2  with the top bin b* resolved: the slice's count of keys above b* and
-//       its 32-bin histogram of the low 5 bits among keys in b*, kept per
-//       slice and merged into the row's low histogram;
-//   G3  with K resolved: each slice's output offset follows from the per-slice
-//       records of the slices before it, then an ordered compaction.
-// Row workspace (uint32): hist1[2048] | hist2[32] | pad | per-slice [S][33].
-constexpr int kLongHist2 = kBins;                 // offset of hist2
-constexpr int kLongSlices = kBins + 64;           // offset of the per-slice records
-constexpr int kSliceRec = 33;                     // above, low histogram[32]
+// Rows longer than one workgroup keeps in registers (the 1M-context decode
+// has 262,144 candidates) are cut into slices of kFineSlice keys, one
+// 1024-thread workgroup each, and selected in two launches.  A key's top 10
+// bits are its coarse bin, the low 6 its fine bin inside it.
+//   F1  The slice's full 65,536-bin histogram of 16-bit keys in LDS (two
+//       16-bit counts per word).  From it the slice's record: per coarse bin
+//       c the number of keys at or above c and the number of distinct keys at
+//       or above c, then the distinct keys with their counts in descending
+//       order.  The list stops after the coarse bin that holds the slice's own
+//       k-th largest key: the row's k-th largest key K is at least that key
+//       (the slice alone has k keys at or above it), so the coarse bin of K is
+//       never below it, and the list holds at most k - 1 + 64 entries.
+//   F2  Every workgroup of the row sums the slices' coarse counts to find the
+//       coarse bin c* of K, sums the listed keys of c* over the slices to find
+//       K and how many keys equal to K are taken (`rem`), and the same sums
+//       over the slices before its own give its output offset; then an
+//       ordered compaction of its slice.
+// Every record is written whole by its slice, so the workspace needs no
+// clearing and no global atomics are used.
+constexpr int kFineSlice = 16384;   // keys per slice
+constexpr int kFineThreads = 1024;  // 16 keys per thread, two 16-byte chunks
+constexpr int kCoarse = 1024;       // coarse bins (top 10 key bits), one per F1 thread
+static_assert(kFineSlice == kTopkFineSlice && kCoarse == kTopkFineCoarse, "shared with the workspace sizing");
 
-template <int CPT>
-__device__ __forceinline__ void long_slice_keys(const uint16_t* row, int64_t lo, int64_t hi, uint32_t (&kp)[CPT][4],
-                                                uint32_t (&valid)[CPT]) {
-  const int tid = threadIdx.x;
+template <int NC>
+__device__ __forceinline__ void fine_slice_keys(const uint16_t* row, int64_t lo, int64_t hi, uint32_t (&kp)[NC][4],
+                                                uint32_t (&valid)[NC]) {
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int64_t i0 = lo + 8 * (static_cast<int64_t>(c) * 256 + tid);
+  for (int c = 0; c < NC; ++c) {
+    const int64_t i0 = lo + 8 * (static_cast<int64_t>(c) * kFineThreads + threadIdx.x);
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (i0 < hi) raw = *reinterpret_cast<const uint4*>(row + i0);
     const int64_t nv = hi - i0;
@@ -691,190 +739,273 @@ __device__ __forceinline__ void long_slice_keys(const uint16_t* row, int64_t lo,
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      kp[c][j] = key_of(static_cast<uint16_t>(w[j] & 0xffffu)) | (static_cast<uint32_t>(key_of(static_cast<uint16_t>(w[j] >> 16))) << 16);
+      kp[c][j] = key_of(static_cast<uint16_t>(w[j] & 0xffffu)) |
+                 (static_cast<uint32_t>(key_of(static_cast<uint16_t>(w[j] >> 16))) << 16);
   }
 }
-#define LKEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
+#define FKEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
 
-__device__ __forceinline__ void long_slice_range(int64_t V, int S, int64_t& lo, int64_t& hi) {
-  const int64_t L = ((V + S - 1) / S + 7) / 8 * 8;
-  lo = blockIdx.x * L;
-  hi = lo + L < V ? lo + L : V;
-  if (lo > hi) lo = hi;
+// Word w of the histogram (bins 2w, 2w + 1) lives at fine_slot(w): the 32
+// words of coarse bin j = w / 32 are 8 quads, quad q stored at q ^ (j & 7), so
+// lanes reading quad q of consecutive coarse bins hit different banks.
+__device__ __forceinline__ uint32_t fine_slot(uint32_t w) {
+  const uint32_t j = w >> 5;
+  return (j << 5) | ((((w >> 2) & 7u) ^ (j & 7u)) << 2) | (w & 3u);
 }
 
-template <int CPT>
-__global__ void __launch_bounds__(256)
-topk_long_hist1_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
-                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
-  __shared__ uint32_t hist[kBins];
+__global__ void __launch_bounds__(kFineThreads)
+topk_fine_record_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k,
+                        const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws, int64_t rec_words,
+                        int64_t row_words) {
+  __shared__ uint32_t hist[32768];               // bin 2w in the low half of word w, 2w + 1 in the high half
+  __shared__ uint32_t lst[CSA_MAX_TOPK + 64];    // the list, staged
+  __shared__ uint32_t tmp[32];
   const int64_t row = blockIdx.y;
   const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
-  if (V <= k) return;
-  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0;
-  int64_t lo, hi;
-  long_slice_range(V, S, lo, hi);
-  uint32_t kp[CPT][4], valid[CPT];
-  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFineSlice;
+  if (V <= k || lo >= V) return;
+  const int64_t hi = lo + kFineSlice < V ? lo + kFineSlice : V;
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t kp[2][4], valid[2];
+  fine_slice_keys<2>(scores + row * N, lo, hi, kp, valid);
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) h4[q * kFineThreads + tid] = make_uint4(0, 0, 0, 0);
+  }
+  if (tid == 0) tmp[20] = 0xffffffffu;
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) hist_add(hist, LKEY(c, u) >> 5, (valid[c] >> u) & 1u);
+    for (int u = 0; u < 8; ++u)
+      if ((valid[c] >> u) & 1u) {
+        const uint32_t kk = FKEY(c, u);
+        atomicAdd(&hist[fine_slot(kk >> 1)], 1u << (16 * (kk & 1u)));
+      }
   __syncthreads();
-  uint32_t* h1 = ws + row * (kLongSlices + kSliceRec * S);
-  for (int i = threadIdx.x; i < kBins; i += 256)
-    if (hist[i]) atomicAdd(&h1[i], hist[i]);
-}
-
-template <int CPT>
-__global__ void __launch_bounds__(256)
-topk_long_hist2_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
-                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws) {
-  __shared__ uint32_t st[4];
-  __shared__ uint32_t h2[32];
-  __shared__ uint32_t above_s;
-  const int64_t row = blockIdx.y;
-  const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
-  if (V <= k) return;
-  uint32_t* rws = ws + row * (kLongSlices + kSliceRec * S);
-  int64_t lo, hi;
-  long_slice_range(V, S, lo, hi);
-  uint32_t kp[CPT][4], valid[CPT];
-  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);   // in flight while the top bin resolves
-  if (threadIdx.x < 32) h2[threadIdx.x] = 0;
-  if (threadIdx.x == 0) above_s = 0;
-  resolve_digit(rws, kBins, static_cast<uint32_t>(k), st);
-  __syncthreads();
-  const uint32_t bstar = st[0];
-  uint32_t above = 0;
+  // thread t owns coarse bin cb = 1023 - t (fine bins 64 cb .. 64 cb + 63):
+  // count its distinct keys and its keys
+  const uint32_t cb = static_cast<uint32_t>(kCoarse - 1 - tid);
+  const uint4* hq = reinterpret_cast<const uint4*>(hist) + cb * 8;
+  uint32_t nd = 0, ns = 0;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = hq[q ^ (cb & 7u)];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool v = (valid[c] >> u) & 1u;
-      const uint32_t kk = LKEY(c, u);
-      above += v && (kk >> 5) > bstar;
-      if (v && (kk >> 5) == bstar) atomicAdd(&h2[kk & 31], 1u);
+    for (int j = 0; j < 4; ++j) {
+      nd += ((w4[j] & 0xffffu) != 0) + ((w4[j] >> 16) != 0);
+      ns += (w4[j] & 0xffffu) + (w4[j] >> 16);
     }
-  above = wave_sum_u32(above);
-  if ((threadIdx.x & 63) == 0) atomicAdd(&above_s, above);
-  __syncthreads();
-  uint32_t* rec = rws + kLongSlices + kSliceRec * blockIdx.x;
-  if (threadIdx.x == 0) rec[0] = above_s;
-  if (threadIdx.x < 32) {
-    rec[1 + threadIdx.x] = h2[threadIdx.x];
-    if (h2[threadIdx.x]) atomicAdd(&rws[kLongHist2 + threadIdx.x], h2[threadIdx.x]);
   }
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan(nd | (ns << 16), tmp, &tot);   // both totals <= 16384
+  const uint32_t incl = ex + (nd | (ns << 16));
+  if ((incl >> 16) >= static_cast<uint32_t>(k)) atomicMin(&tmp[20], static_cast<uint32_t>(tid));
+  __syncthreads();
+  // the list runs through the coarse bin of the slice's k-th largest key (all
+  // of it when the slice has fewer than k keys).  Each wave stages the
+  // non-empty coarse bins of its own threads, one bin at a time, a lane per
+  // fine bin in descending order.
+  const uint32_t last = tmp[20] == 0xffffffffu ? kFineThreads - 1 : tmp[20];
+  if (tid == static_cast<int>(last)) tmp[21] = incl & 0xffffu;
+  {
+    const uint32_t w0 = static_cast<uint32_t>(tid & ~63);
+    uint64_t todo = __ballot(nd != 0 && static_cast<uint32_t>(tid) <= last);
+    while (todo) {
+      const int j = __ffsll(static_cast<long long>(todo)) - 1;
+      todo &= todo - 1;
+      const uint32_t base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ex & 0xffffu), j));
+      const uint32_t bin = 64 * (kCoarse - 1 - (w0 + j)) + 63 - lane;
+      const uint32_t cnt = (hist[fine_slot(bin >> 1)] >> (16 * (bin & 1u))) & 0xffffu;
+      const uint64_t has = __ballot(cnt != 0);
+      if (cnt) lst[base + __popcll(has & ((uint64_t(1) << lane) - 1))] = (bin << 16) | cnt;
+    }
+  }
+  __syncthreads();
+  // the record's global stores come last: no barrier waits for them
+  uint32_t* rec = ws + row * row_words + static_cast<int64_t>(blockIdx.x) * rec_words;
+  rec[cb] = incl >> 16;                  // keys at or above coarse bin cb
+  rec[kCoarse + cb] = incl & 0xffffu;    // distinct keys at or above coarse bin cb
+  const uint32_t n_list = tmp[21];
+  for (uint32_t e = tid; e < n_list; e += kFineThreads) rec[2 * kCoarse + e] = lst[e];
 }
 
-template <int CPT>
-__global__ void __launch_bounds__(256)
-topk_long_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, int S,
-                       const uint16_t* __restrict__ scores, uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
-  __shared__ uint32_t st[4];
-  __shared__ uint32_t st2[4];
+__global__ void __launch_bounds__(kFineThreads)
+topk_fine_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k,
+                       const uint16_t* __restrict__ scores, const uint32_t* __restrict__ ws, int64_t rec_words,
+                       int64_t row_words, int32_t* __restrict__ idx) {
+  constexpr int kMaxS = kFineThreads;   // slices whose list ranges are staged in LDS at once
+  __shared__ uint32_t fine[64], fine_before[64];
+  __shared__ uint32_t tot_c[kCoarse + 1], before_c[kCoarse + 1];
+  __shared__ uint32_t e_lo[kMaxS], e_cnt[kMaxS + 1];
+  __shared__ uint32_t st[8];
   __shared__ uint64_t tmp64[17];
-  __shared__ uint32_t before[2];
+  __shared__ uint32_t tmp32[20];
   const int64_t row = blockIdx.y;
   const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
+  const int tid = threadIdx.x;
   if (V <= k) {
     if (blockIdx.x == 0)
-      for (int i = threadIdx.x; i < k; i += 256) out[i] = i < V ? i : -1;
+      for (int i = tid; i < k; i += kFineThreads) out[i] = i < V ? i : -1;
     return;
   }
-  const uint32_t* rws = ws + row * (kLongSlices + kSliceRec * S);
-  int64_t lo, hi;
-  long_slice_range(V, S, lo, hi);
-  uint32_t kp[CPT][4], valid[CPT];
-  long_slice_keys<CPT>(scores + row * N, lo, hi, kp, valid);
-  resolve_digit(rws, kBins, static_cast<uint32_t>(k), st);
-  __syncthreads();
-  const uint32_t bstar = st[0], rem1 = st[1];
-  resolve_digit(rws + kLongHist2, 32, rem1, st2);
-  __syncthreads();
-  const uint32_t lowk = st2[0], rem = st2[1];
-  const uint32_t K = (bstar << 5) | lowk;
-  // keys > K and == K in the slices before this one
-  if (threadIdx.x < 64) {
-    uint32_t gt = 0, eq = 0;
-    for (int s2 = threadIdx.x; s2 < static_cast<int>(blockIdx.x); s2 += 64) {
-      const uint32_t* rec = rws + kLongSlices + kSliceRec * s2;
-      gt += rec[0];
-      for (int b = lowk + 1; b < 32; ++b) gt += rec[1 + b];
-      eq += rec[1 + lowk];
-    }
-    gt = wave_sum_u32(gt);
-    eq = wave_sum_u32(eq);
-    if (threadIdx.x == 0) {
-      before[0] = gt;
-      before[1] = eq;
-    }
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFineSlice;
+  if (lo >= V) return;
+  const int64_t hi = lo + kFineSlice < V ? lo + kFineSlice : V;
+  const int S = static_cast<int>((V + kFineSlice - 1) / kFineSlice);
+  const int me = static_cast<int>(blockIdx.x);
+  uint32_t kp[2][4], valid[2];
+  fine_slice_keys<2>(scores + row * N, lo, hi, kp, valid);
+  const uint32_t* rws = ws + row * row_words;
+  tot_c[tid] = 0;
+  before_c[tid] = 0;
+  if (tid < 64) {
+    fine[tid] = 0;
+    fine_before[tid] = 0;
+  } else if (tid == 64) {
+    tot_c[kCoarse] = 0;
+    before_c[kCoarse] = 0;
   }
   __syncthreads();
-  uint32_t gt_run = before[0], eq_run = before[1];
-  // ordered compaction of the slice, two chunks per scan (fields gt0 | eq0 | gt1 | eq1)
+  // coarse counts (keys at or above each coarse bin) summed over all slices
+  // and over the slices before this one: thread t adds quad t % 256 of slices
+  // t / 256, t / 256 + 4, ..., four loads in flight at a time
+  {
+    const int q = tid & 255, g = tid >> 8;
+    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+    for (int i0 = g; i0 < S; i0 += 16) {
+      uint4 v[4];
 #pragma unroll
-  for (int c0 = 0; c0 < CPT; c0 += 2) {
-    uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 4 * j;
+        v[j] = i < S ? reinterpret_cast<const uint4*>(rws + static_cast<int64_t>(i) * rec_words)[q]
+                     : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (c0 + h >= CPT) continue;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool vv = (valid[c0 + h] >> u) & 1u;
-        cnt[h][0] += vv && LKEY(c0 + h, u) > K;
-        cnt[h][1] += vv && LKEY(c0 + h, u) == K;
+      for (int j = 0; j < 4; ++j) {
+        a.x += v[j].x; a.y += v[j].y; a.z += v[j].z; a.w += v[j].w;
+        if (i0 + 4 * j < me) { b.x += v[j].x; b.y += v[j].y; b.z += v[j].z; b.w += v[j].w; }
       }
     }
-    const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
-                            (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
-    uint64_t tot;
-    const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
-    const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
-    const uint32_t tg1 = (tot >> 32) & 0xffffu, te1 = (tot >> 48) & 0xffffu;
+    atomicAdd(&tot_c[4 * q], a.x); atomicAdd(&tot_c[4 * q + 1], a.y);
+    atomicAdd(&tot_c[4 * q + 2], a.z); atomicAdd(&tot_c[4 * q + 3], a.w);
+    atomicAdd(&before_c[4 * q], b.x); atomicAdd(&before_c[4 * q + 1], b.y);
+    atomicAdd(&before_c[4 * q + 2], b.z); atomicAdd(&before_c[4 * q + 3], b.w);
+  }
+  __syncthreads();
+  // c*: the highest coarse bin with at least k keys at or above it
+  if (tot_c[tid] >= static_cast<uint32_t>(k) && tot_c[tid + 1] < static_cast<uint32_t>(k)) st[0] = tid;
+  __syncthreads();
+  const int cs = static_cast<int>(st[0]);
+  const uint32_t rem1 = static_cast<uint32_t>(k) - tot_c[cs + 1];   // keys of bin c* still to take
+  // the listed keys of c* in every slice: entries [distinct above c*, distinct
+  // at or above c*) of its list (at most 64 per slice), four loads in flight
+  for (int s0 = 0; s0 < S; s0 += kMaxS) {
+    const int ns = S - s0 < kMaxS ? S - s0 : kMaxS;
+    uint32_t cnt = 0;
+    if (tid < ns) {
+      const uint32_t* rec = rws + static_cast<int64_t>(s0 + tid) * rec_words;
+      const uint32_t e0 = cs < kCoarse - 1 ? rec[kCoarse + cs + 1] : 0u;
+      cnt = rec[kCoarse + cs] - e0;
+      e_lo[tid] = e0;
+    }
+    uint32_t tot_e;
+    const uint32_t ex = block_exclusive_scan(cnt, tmp32, &tot_e);
+    if (tid < ns) e_cnt[tid] = ex;
+    if (tid == 0) e_cnt[ns] = tot_e;
+    __syncthreads();
+    for (uint32_t f0 = 0; f0 < tot_e; f0 += 4 * kFineThreads) {
+      uint32_t v[4];
+      int sl[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = c0 + h;
-      if (c >= CPT) continue;
-      const uint32_t gb = gt_run + (h ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
-      const uint32_t eb = eq_run + (h ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
-      uint32_t pos = gb + (eb < rem ? eb : rem);
-      uint32_t er = eb;
-      const int32_t i0 = static_cast<int32_t>(lo + 8 * (c * 256 + threadIdx.x));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (!((valid[c] >> u) & 1u)) continue;
-        const uint32_t kk = LKEY(c, u);
-        if (kk > K) {
-          out[pos++] = i0 + u;
-        } else if (kk == K) {
-          if (er < rem) out[pos++] = i0 + u;
-          ++er;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t f = f0 + j * kFineThreads + tid;
+        v[j] = 0;
+        sl[j] = -1;
+        if (f < tot_e) {
+          int lo_s = 0, hi_s = ns;   // the slice whose range holds flat entry f: e_cnt[s] <= f < e_cnt[s + 1]
+          while (hi_s - lo_s > 1) {
+            const int mid = (lo_s + hi_s) >> 1;
+            if (e_cnt[mid] <= f) lo_s = mid; else hi_s = mid;
+          }
+          sl[j] = lo_s;
+          v[j] = rws[static_cast<int64_t>(s0 + lo_s) * rec_words + 2 * kCoarse + e_lo[lo_s] + (f - e_cnt[lo_s])];
         }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (sl[j] < 0) continue;
+        const uint32_t fb = (v[j] >> 16) & 63u, n = v[j] & 0xffffu;
+        atomicAdd(&fine[fb], n);
+        if (s0 + sl[j] < me) atomicAdd(&fine_before[fb], n);
+      }
     }
-    gt_run += tg0 + tg1;
-    eq_run += te0 + te1;
+    __syncthreads();
+  }
+  resolve_digit(fine, 64, rem1, st + 2);
+  __syncthreads();
+  const uint32_t fs = st[2], rem = st[3];
+  const uint32_t K = (static_cast<uint32_t>(cs) << 6) | fs;
+  // keys above K and equal to K in the slices before this one
+  if (tid < 64) {
+    uint32_t g = tid > static_cast<int>(fs) ? fine_before[tid] : 0u;
+    g = wave_total_add(g);
+    if (tid == 0) st[4] = g + before_c[cs + 1];
+  }
+  __syncthreads();
+  uint32_t gt_run = st[4], eq_run = fine_before[fs];
+  // ordered compaction of the slice (fields gt0 | eq0 | gt1 | eq1 of the two chunks)
+  uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool vv = (valid[h] >> u) & 1u;
+      cnt[h][0] += vv && FKEY(h, u) > K;
+      cnt[h][1] += vv && FKEY(h, u) == K;
+    }
+  const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
+                          (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
+  uint64_t tot;
+  const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
+  const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t gb = gt_run + (h ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
+    const uint32_t eb = eq_run + (h ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
+    uint32_t pos = gb + (eb < rem ? eb : rem);
+    uint32_t er = eb;
+    const int32_t i0 = static_cast<int32_t>(lo + 8 * (h * kFineThreads + tid));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!((valid[h] >> u) & 1u)) continue;
+      const uint32_t kk = FKEY(h, u);
+      if (kk > K) {
+        out[pos++] = i0 + u;
+      } else if (kk == K) {
+        if (er < rem) out[pos++] = i0 + u;
+        ++er;
+      }
+    }
   }
 }
-#undef LKEY
+#undef FKEY
 
-template <int CPT>
-hipError_t launch_long(const TopkArgs& a, hipStream_t s) {
-  const int S = kTopkSlices;
+hipError_t launch_fine(const TopkArgs& a, hipStream_t s) {
   const int64_t rows = a.B * a.T;
+  const int64_t S = (a.N + kFineSlice - 1) / kFineSlice;
+  const int64_t rec = topk_fine_rec_words(a.k);
+  const int64_t per_row = S * rec;
   uint32_t* ws = static_cast<uint32_t*>(a.ws);
   const auto* sc = static_cast<const uint16_t*>(a.scores);
-  const int64_t per_row = kLongSlices + kSliceRec * S;
-  const int64_t words = rows * per_row;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, s, ws, words);
-  const dim3 grid(S, static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(topk_long_hist1_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws);
-  hipLaunchKernelGGL(topk_long_hist2_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws);
-  hipLaunchKernelGGL(topk_long_write_kernel<CPT>, grid, dim3(256), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos, a.k, S, sc, ws,
-                     a.idx);
+  const dim3 grid(static_cast<uint32_t>(S), static_cast<uint32_t>(rows));
+  hipLaunchKernelGGL(topk_fine_record_kernel, grid, dim3(kFineThreads), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos,
+                     a.k, sc, ws, rec, per_row);
+  hipLaunchKernelGGL(topk_fine_write_kernel, grid, dim3(kFineThreads), 0, s, a.T, a.N, a.q_pos0, a.ratio, a.seq_pos,
+                     a.k, sc, ws, rec, per_row, a.idx);
   return hipGetLastError();
 }
 
@@ -905,15 +1036,8 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if constexpr (sizeof(KT) == 2) {
-    // long bf16 rows: slices of up to 8 * 256 * 8 keys held in registers
-    const int64_t slice = ((a.N + kTopkSlices - 1) / kTopkSlices + 7) / 8 * 8;
-    const int64_t cpt = (slice + 2047) / 2048;
-    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && cpt <= 8) {
-      if (cpt <= 1) return launch_long<1>(a, s);
-      if (cpt <= 2) return launch_long<2>(a, s);
-      if (cpt <= 4) return launch_long<4>(a, s);
-      return launch_long<8>(a, s);
-    }
+    // long bf16 rows: slices of 8192 keys, a full 16-bit histogram each
+    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0) return launch_fine(a, s);
   }
   const int S = kTopkSlices;
   uint32_t* ws = static_cast<uint32_t*>(a.ws);

@@ -110,9 +110,21 @@ inline bool topk_row_in_lds(int64_t N, int dtype) {
 // three) and a (greater, equal) count pair per slice.
 inline size_t topk_row_ws_bytes() { return (3 * 2048 + 2 * kTopkSlices) * sizeof(uint32_t); }
 
-inline size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t N, int dtype) {
+// Long bf16 rows: one record per slice of 16384 keys -- two 1024-word coarse
+// count tables and a list of at most k + 63 (key, count) words, the record
+// rounded up to 16 bytes.
+constexpr int64_t kTopkFineSlice = 16384;
+constexpr int kTopkFineCoarse = 1024;
+inline int64_t topk_fine_rec_words(int k) { return 2 * kTopkFineCoarse + (int64_t(k) + 64 + 3) / 4 * 4; }
+inline size_t topk_fine_row_ws_bytes(int64_t N, int k) {
+  return size_t((N + kTopkFineSlice - 1) / kTopkFineSlice) * size_t(topk_fine_rec_words(k)) * sizeof(uint32_t);
+}
+
+inline size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t N, int k, int dtype) {
   if (topk_row_in_lds(N, dtype)) return 0;
-  return size_t(B) * size_t(T) * topk_row_ws_bytes();
+  size_t per = topk_row_ws_bytes();
+  if (dtype == CSA_BF16 && topk_fine_row_ws_bytes(N, k) > per) per = topk_fine_row_ws_bytes(N, k);
+  return size_t(B) * size_t(T) * per;
 }
 
 // Compressor row split: a C128A call with few (entry, sequence) pairs spreads
@@ -220,7 +232,7 @@ inline Check check_topk(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int rat
   const bool empty = (B == 0 || T == 0);
   k.ptr(scores, "scores", !empty && N > 0) && k.ptr(idx, "idx", !empty);
   if (!k.ok()) return k;
-  const size_t need = topk_workspace_bytes(B, T, N, score_dtype);
+  const size_t need = topk_workspace_bytes(B, T, N, kk, score_dtype);
   if (need > 0) {
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "topk_select needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");
@@ -445,7 +457,7 @@ inline Check check_topk_paged(int64_t B, int64_t N, const int64_t* seq_pos, int 
   const bool empty = B == 0;
   k.ptr(scores, "scores", !empty && N > 0) && k.ptr(idx, "idx", !empty) && k.ptr(seq_pos, "seq_pos", !empty);
   if (!k.ok()) return k;
-  const size_t need = topk_workspace_bytes(B, 1, N, score_dtype);
+  const size_t need = topk_workspace_bytes(B, 1, N, kk, score_dtype);
   if (need > 0) {
     if (!ws || ws_bytes < need) { k.fail(CSA_ERR_WORKSPACE, "topk_select_paged needs " + i2s((int64_t)need) + " workspace bytes, got " + i2s((int64_t)ws_bytes)); return k; }
     k.ptr(ws, "workspace");
@@ -490,8 +502,8 @@ inline size_t workspace_bytes(int op, int64_t B, int64_t T, int64_t N, int kk) {
   (void)kk;
   switch (op) {
     case CSA_OP_COMPRESS: return compress_workspace_bytes(kk, B, T, N);   // (B, n_tok, c, ratio)
-    case CSA_OP_TOPK: return topk_workspace_bytes(B, T, N, CSA_BF16) > topk_workspace_bytes(B, T, N, CSA_F32)
-                                 ? topk_workspace_bytes(B, T, N, CSA_BF16) : topk_workspace_bytes(B, T, N, CSA_F32);
+    case CSA_OP_TOPK: return topk_workspace_bytes(B, T, N, kk, CSA_BF16) > topk_workspace_bytes(B, T, N, kk, CSA_F32)
+                                 ? topk_workspace_bytes(B, T, N, kk, CSA_BF16) : topk_workspace_bytes(B, T, N, kk, CSA_F32);
     case CSA_OP_SPARSE_ATTN:
     case CSA_OP_HCA_ATTN: return attn_workspace_bytes(B, T);
     default: return 0;
