@@ -29,7 +29,8 @@ The five configurations of the method (one GPU):
 Other workloads (``bench.py --workload NAME``): csa_hca_decode (a CSA and an
 HCA layer decode step at 65,536 context, with the --keys / --rope /
 --batch-invariant variants), c128a_1m, csa_reindex_decode,
-csa_reindex_prefill, csa_paged_decode, hbm_copy (the counter calibration).
+csa_reindex_prefill, csa_paged_decode, hbm_copy (the counter calibration), hbm_read (a plain
+streaming read, the attainable read bandwidth).
 
 The CPU baseline of each configuration runs the oracle (NumPy fp64, test
 infrastructure) over a bounded sample of the same step: whole query tokens
@@ -694,5 +695,30 @@ def hbm_copy(torch, csa, synth, copies=1):
     return wk
 
 
+def hbm_read(torch, csa, synth, copies=4):
+    """A plain streaming read (libcsa_probe.so) of as many bytes as the 1M decode's
+    MXFP4 keys and scales, over rotating buffers: what a kernel that only reads
+    HBM attains on this machine, beside the 8 TB/s peak."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(csa.__file__)), "libcsa_probe.so"))
+    lib.csa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    nbytes = 8 * 262144 * (64 + 4)
+    grid = 1024
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(r + 1) for r in range(copies)]
+    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+
+    def run(r):
+        st = torch.cuda.current_stream().cuda_stream
+        assert lib.csa_probe_stream_read(bufs[r].data_ptr(), nbytes, out.data_ptr(), grid, ctypes.c_void_p(st)) == 0
+
+    wk = Work("hbm_read", f"hbm_read: a streaming read of {nbytes:,} bytes (the 1M decode's MXFP4 keys and scales), "
+              f"{copies} rotating buffers", 0, copies, dict(bytes_read=nbytes, grid=grid), "stream_read",
+              unit="GB/s", units=nbytes / 1e9)
+    wk.add("stream_read", run, nbytes, 0, "hbm")
+    return wk
+
+
 EXTRAS = {"csa_hca_decode": csa_hca_decode, "c128a_1m": c128a_1m, "csa_reindex_decode": csa_reindex_decode,
-          "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode, "hbm_copy": hbm_copy}
+          "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode, "hbm_copy": hbm_copy,
+          "hbm_read": hbm_read}

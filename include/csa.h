@@ -284,9 +284,14 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
  * (the indexer equation of lightning_index, no scale), -inf where the slot is
  * empty: pool[b,t,j] < 0 or >= N (such slots read no key).  Visibility is the
  * pool's: a pool from topk_select holds visible entries only.
- *  q [B, T, 64, 128] bf16;  w [B, T, 64] float32;  k [B, N, 128] bf16;
- *  pool [B, T, P] int32;  scores [B, T, P] float32 or bf16 (score_dtype).
- *  qk_dtype must be CSA_BF16.  0 <= P <= 65536.
+ *  q, k in qk_dtype, as lightning_index takes them: CSA_BF16 (q [B, T, 64,
+ *  128], k [B, N, 128]); CSA_FP8_E4M3 (E4M3 codes, q_scale [B, T, 64] and
+ *  k_scale [B, N] fp32 row scales); CSA_MXFP4 (packed E2M1 q [B, T, 64, 64]
+ *  and k [B, N, 64], E8M0 q_scale [B, T, 64, 4] and k_scale [B, N, 4]) --
+ *  the key precision of the indexer cache the pool came from ("DeepSeek V4
+ *  结构速览", Lightning Indexer: FP4 QK).  q_scale, k_scale NULL for bf16.
+ *  w [B, T, 64] float32;  pool [B, T, P] int32;  scores [B, T, P] float32 or
+ *  bf16 (score_dtype).  0 <= P <= 65536.
  *
  * topk_select_pool: for each row, the k pool entries with the highest scores,
  * equal scores to the earlier slot; a slot is written as its entry id
@@ -299,8 +304,9 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
  * workspace.
  */
 int lightning_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I,
-                         const void* q, const float* w, const void* k, int qk_dtype,
-                         const int32_t* pool, void* scores, int score_dtype, void* stream);
+                         const void* q, const void* q_scale, const float* w, const void* k,
+                         const void* k_scale, int qk_dtype, const int32_t* pool, void* scores,
+                         int score_dtype, void* stream);
 int topk_select_pool(int64_t B, int64_t T, int64_t N, int64_t P, int k, const void* scores,
                      int score_dtype, const int32_t* pool, int32_t* idx, void* stream);
 

@@ -52,7 +52,7 @@ _SIGS = {
                               _int, _f32, _int, _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
     "hca_attn_paged": [_i64, _int, _int, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _f32, _vp, _int,
                        _vp, _vp, _int, _int, _f32, _vp, _sz, _vp],
-    "lightning_index_pool": [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp],
+    "lightning_index_pool": [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp],
     "topk_select_pool": [_i64, _i64, _i64, _i64, _int, _vp, _int, _vp, _vp, _vp],
     "lightning_index": [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _int,
                         _vp, _int, _vp],
@@ -284,16 +284,22 @@ def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=
     return idx
 
 
-def lightning_index_pool(q, w, k, pool, *, score_dtype=torch.bfloat16, scores=None, stream=None):
+def lightning_index_pool(q, w, k, pool, *, qk_dtype=None, q_scale=None, k_scale=None, score_dtype=torch.bfloat16,
+                         scores=None, stream=None):
     """Hierarchical indexer, Reindex layer: scores of each query's candidate pool.
-    q: [B, T, 64, 128] bf16, w: [B, T, 64], k: [B, N, 128] bf16, pool: [B, T, P] int32
-    (-1 = empty); returns scores [B, T, P] (-inf at empty slots)."""
+    q: [B, T, 64, 128] bf16 (or uint8 E4M3 codes with q_scale [B, T, 64], or packed
+    MXFP4 [B, T, 64, 64] with E8M0 q_scale [B, T, 64, 4]), w: [B, T, 64], k: [B, N, 128]
+    in the same form (k_scale [B, N] or [B, N, 4]), pool: [B, T, P] int32 (-1 = empty);
+    returns scores [B, T, P] (-inf at empty slots)."""
     B, T, P = pool.shape
     N = k.shape[1]
+    if qk_dtype is None:
+        qk_dtype = (MXFP4 if q.shape[-1] == 64 else FP8_E4M3) if q.dtype == torch.uint8 else _dt(q)
     if scores is None:
         scores = torch.empty(B, T, P, dtype=score_dtype, device=q.device)
-    st = library().lightning_index_pool(B, T, N, P, 64, 128, _ptr(q), _ptr(w), _ptr(k), _dt(q), _ptr(pool),
-                                        _ptr(scores), _dt(scores), _stream(stream))
+    st = library().lightning_index_pool(B, T, N, P, 64, 128, _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k),
+                                        _ptr(k_scale), qk_dtype, _ptr(pool), _ptr(scores), _dt(scores),
+                                        _stream(stream))
     _check(st, "lightning_index_pool")
     return scores
 

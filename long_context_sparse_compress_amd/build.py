@@ -1,10 +1,12 @@
-"""Build libcsa.so, the gfx950 HIP library behind include/csa.h.
+"""Build libcsa.so, the gfx950 HIP library behind include/csa.h, and
+libcsa_probe.so, the measurement helper that bench.py's stream-read workload
+uses (not part of the C ABI).
 
     python -m long_context_sparse_compress_amd.build
 
 Every source is compiled with hipcc for gfx950 only, -O3, without fast-math,
 and with packed fp32 instructions disabled.  Objects go to _build/ next to
-this file; the library is written in-tree next to this file.
+this file; the libraries are written in-tree next to this file.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
 SOURCES = ["capi.cpp", "compress.hip", "indexer.hip", "topk.hip", "attention.hip", "rope.hip", "pool.hip"]
+PROBE_SOURCES = ["probe/stream_read.hip"]
+PROBE_LIB = os.path.join(HERE, "libcsa_probe.so")
 ARCH = "gfx950"
 
 
@@ -45,7 +49,7 @@ EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(src)[0].replace("/", "_") + ".o")
     cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,18 +57,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

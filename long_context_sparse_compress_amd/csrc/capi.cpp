@@ -106,11 +106,12 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
 }
 
 int lightning_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I, const void* q,
-                         const float* w, const void* k, int qk_dtype, const int32_t* pool, void* scores,
-                         int score_dtype, void* stream) {
-  csa::Check ck = csa::check_index_pool(B, T, N, P, H_I, d_I, q, w, k, qk_dtype, pool, scores, score_dtype);
+                         const void* q_scale, const float* w, const void* k, const void* k_scale, int qk_dtype,
+                         const int32_t* pool, void* scores, int score_dtype, void* stream) {
+  csa::Check ck = csa::check_index_pool(B, T, N, P, H_I, d_I, q, q_scale, w, k, k_scale, qk_dtype, pool, scores,
+                                        score_dtype);
   if (!ck.ok()) return finish(ck);
-  csa::IndexPoolArgs a{B, T, N, P, q, w, k, pool, scores, score_dtype};
+  csa::IndexPoolArgs a{B, T, N, P, q, q_scale, w, k, k_scale, qk_dtype, pool, scores, score_dtype};
   return hip_status(csa::launch_index_pool(a, as_stream(stream)), "lightning_index_pool launch");
 }
 

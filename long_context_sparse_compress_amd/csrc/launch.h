@@ -82,9 +82,12 @@ struct TopkArgs {
 
 struct IndexPoolArgs {
   int64_t B, T, N, P;
-  const void* q;         // [B, T, 64, 128] bf16
+  const void* q;         // [B, T, 64, 128] in qk_dtype
+  const void* q_scale;   // fp8: [B, T, 64] fp32; MXFP4: [B, T, 64, 4] E8M0; else NULL
   const float* w;        // [B, T, 64]
-  const void* k;         // [B, N, 128] bf16
+  const void* k;         // [B, N, 128] in qk_dtype
+  const void* k_scale;   // fp8: [B, N] fp32; MXFP4: [B, N, 4] E8M0; else NULL
+  int qk_dtype;
   const int32_t* pool;   // [B, T, P]
   void* scores;          // [B, T, P]
   int score_dtype;

@@ -245,18 +245,24 @@ constexpr int64_t kMaxPool = 65536;       // pool slots a query may score
 constexpr int64_t kMaxPoolTopk = 16384;   // pool slots Top-k selects from (one workgroup per row, no workspace)
 
 inline Check check_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I, const void* q,
-                              const float* w, const void* kk, int qk_dtype, const int32_t* pool, const void* scores,
-                              int score_dtype) {
+                              const void* q_scale, const float* w, const void* kk, const void* k_scale, int qk_dtype,
+                              const int32_t* pool, const void* scores, int score_dtype) {
   Check k;
   if (B < 0 || T < 0 || N < 0 || P < 0) { k.fail(CSA_ERR_INVALID_ARG, "B, T, N and P must be >= 0"); return k; }
   if (P > kMaxPool) { k.fail(CSA_ERR_INVALID_ARG, "P must be at most 65536, got " + i2s(P)); return k; }
   if (H_I != CSA_INDEX_HEADS || d_I != CSA_INDEX_DIM) { k.fail(CSA_ERR_UNSUPPORTED, "indexer shape must be H_I=64, d_I=128"); return k; }
-  if (qk_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "lightning_index_pool takes bf16 q and keys"); return k; }
+  if (qk_dtype != CSA_BF16 && qk_dtype != CSA_FP8_E4M3 && qk_dtype != CSA_MXFP4) { k.fail(CSA_ERR_UNSUPPORTED, "lightning_index_pool takes bf16, fp8 E4M3 or MXFP4 q and keys"); return k; }
   if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) { k.fail(CSA_ERR_UNSUPPORTED, "score_dtype must be CSA_F32 or CSA_BF16"); return k; }
   if (B * T * ((P + 255) / 256) > 0x7fffffff) { k.fail(CSA_ERR_INVALID_ARG, "B * T * ceil(P / 256) must be below 2^31"); return k; }
   const bool empty = (B == 0 || T == 0 || P == 0);
   k.ptr(q, "q", !empty) && k.ptr(w, "w", !empty) && k.ptr(kk, "k", !empty && N > 0) && k.ptr(pool, "pool", !empty) &&
       k.ptr(scores, "scores", !empty);
+  if (!k.ok()) return k;
+  if (qk_dtype == CSA_BF16) {
+    k.must_be_null(q_scale, "q_scale", "for bf16") && k.must_be_null(k_scale, "k_scale", "for bf16");
+  } else {
+    k.ptr(q_scale, "q_scale", !empty) && k.ptr(k_scale, "k_scale", !empty && N > 0);
+  }
   return k;
 }
 

@@ -275,12 +275,15 @@ def test_pool_validation(lib):
     """lightning_index_pool / topk_select_pool argument checks (host only)."""
     ip, tp = lib.lightning_index_pool, lib.topk_select_pool
 
-    def idx_pool(B=2, T=1, N=64, P=128, H=64, d=128, dt=1, sd=1, q=A, w=A, k=A, pool=A, sc=A):
-        return ip(B, T, N, P, H, d, q, w, k, dt, pool, sc, sd, None)
+    def idx_pool(B=2, T=1, N=64, P=128, H=64, d=128, dt=1, sd=1, q=A, w=A, k=A, pool=A, sc=A, qs=None, ks=None):
+        return ip(B, T, N, P, H, d, q, qs, w, k, ks, dt, pool, sc, sd, None)
 
     assert idx_pool(H=32) == -2 and "H_I=64" in _err(lib)
-    assert idx_pool(dt=0) == -2 and "bf16" in _err(lib)
-    assert idx_pool(dt=2) == -2
+    assert idx_pool(dt=0) == -2 and "bf16, fp8 E4M3 or MXFP4" in _err(lib)
+    assert idx_pool(dt=5) == -2
+    assert idx_pool(dt=2) == -1 and "q_scale" in _err(lib)          # fp8 needs both scale arrays
+    assert idx_pool(dt=3, qs=A) == -1 and "k_scale" in _err(lib)     # MXFP4 too
+    assert idx_pool(qs=A) == -1 and "must be NULL" in _err(lib)      # bf16 takes none
     assert idx_pool(sd=2) == -2
     assert idx_pool(P=65537) == -1 and "P must" in _err(lib)
     assert idx_pool(P=-1) == -1

@@ -193,3 +193,92 @@ def test_long_runs_with_a_ragged_pool():
     got = host(_scores(q, w, k, pool, torch.float32))
     rows = [0, 1, 63, 64, 500, 1099]
     index_close(got[:, rows], oi.pool_scores(q[:, rows], w[:, rows], k, pool[:, rows]))
+
+
+# ---------------------------------------------------------------- low-precision pools
+# "DeepSeek V4 结构速览" (Lightning Indexer: the QK path runs in low precision,
+# FP4 in the Pro model): a Reindex layer scores its pool from the same key
+# cache the Full layer read, so it takes the cache's precision.  The oracle
+# scores the decoded q and keys (the quantization is the input's, not the
+# method's); tolerances as for the full indexer.
+
+
+def _quant_layer(prefix, B, T, N, fmt):
+    """q, k drawn N(0, 1) then encoded; returns device tensors and the decoded
+    fp64 copies the oracle reads."""
+    q = synth.normal(prefix + ".q", (B, T, 64, 128))
+    w = synth.uniform(prefix + ".w", (B, T, 64))
+    k = synth.normal(prefix + ".k", (B, N, 128))
+    if fmt == "fp8":
+        qc, qs = synth.quant_fp8_rows(q)
+        kc, ks = synth.quant_fp8_rows(k)
+        qd, kd = on.dequant_fp8_rows(qc, qs), on.dequant_fp8_rows(kc, ks)
+        dq = dict(q=dev(qc, torch.uint8), q_scale=dev(qs), k=dev(kc, torch.uint8), k_scale=dev(ks),
+                  qk_dtype=csa.FP8_E4M3)
+    else:
+        qc, qs = synth.quant_mxfp4(q)
+        kc, ks = synth.quant_mxfp4(k)
+        qd, kd = on.dequant_mxfp4(qc, qs), on.dequant_mxfp4(kc, ks)
+        dq = dict(q=dev(qc, torch.uint8), q_scale=dev(qs, torch.uint8), k=dev(kc, torch.uint8),
+                  k_scale=dev(ks, torch.uint8), qk_dtype=csa.MXFP4)
+    return dq, w, qd, kd
+
+
+def _quant_scores(dq, w, pool, sd):
+    s = csa.lightning_index_pool(dq["q"], dev(w), dq["k"], dev(pool, torch.int32), qk_dtype=dq["qk_dtype"],
+                                 q_scale=dq["q_scale"], k_scale=dq["k_scale"], score_dtype=sd)
+    torch.cuda.synchronize()
+    return host(s)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_quantized_pool_all_rows(fmt):
+    """Ragged pools (empty slots at the end of rows, an empty row, ids past
+    N) over fp8 / MXFP4 keys, fp32 and bf16 scores."""
+    B, T, N, q0, P = 2, 3, 3000, 11000, 600
+    dq, w, qd, kd = _quant_layer(f"pl.q.{fmt}", B, T, N, fmt)
+    pool = synth.random_topk_indices(f"pl.q.{fmt}.pool", B, T, P, [min(N, 500 + 200 * t) for t in range(T)])
+    pool[1, 2, :] = -1
+    pool[0, 1, 3:5] = [N, N + 77]
+    ref = oi.pool_scores(qd, w, kd, pool)
+    index_close(_quant_scores(dq, w, pool, torch.float32), ref)
+    _bf16_close(_quant_scores(dq, w, pool, BF), ref)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_quantized_pool_long_runs(fmt):
+    """The long-run kernel (eight chunks per wave) over quantized keys, sampled rows."""
+    B, T, N, P = 1, 1100, 5000, 700
+    dq, w, qd, kd = _quant_layer(f"pl.ql.{fmt}", B, T, N, fmt)
+    pool = synth.random_topk_indices(f"pl.ql.{fmt}.pool", B, T, P, [min(N, 400 + t) for t in range(T)])
+    got = _quant_scores(dq, w, pool, torch.float32)
+    rows = [0, 1, 63, 64, 700, 1099]
+    index_close(got[:, rows], oi.pool_scores(qd[:, rows], w[:, rows], kd, pool[:, rows]))
+
+
+def test_pro_decode_reindex_mxfp4():
+    """The Pro decode shape: batch 8 at 1,048,576 context (262,144 C4A
+    entries), MXFP4 keys, a 2,048-entry pool per query, top-1024 inside it.
+    Keys are drawn and encoded on the device; the oracle reads back the
+    pooled rows."""
+    B, N, P, K = 8, 262144, 2048, 1024
+    kp, ks = synth.device_quant_mxfp4(synth.device_normal("pl.pro.k", (B, N, 128)))
+    q = synth.normal("pl.pro.q", (B, 1, 64, 128))
+    qc, qs = synth.quant_mxfp4(q)
+    w = synth.uniform("pl.pro.w", (B, 1, 64))
+    pool = synth.random_topk_indices("pl.pro.pool", B, 1, P, [N] * B)
+    dpool = dev(pool, torch.int32)
+    s = csa.lightning_index_pool(dev(qc, torch.uint8), dev(w), kp, dpool, qk_dtype=csa.MXFP4,
+                                 q_scale=dev(qs, torch.uint8), k_scale=ks, score_dtype=BF)
+    idx = csa.topk_select_pool(s, dpool, K, N=N)
+    torch.cuda.synchronize()
+    hs, hi = host(s), host(idx)
+    qd = on.dequant_mxfp4(qc, qs)
+    for b in range(B):
+        ids = pool[b, 0][pool[b, 0] >= 0].astype(np.int64)
+        sel = torch.as_tensor(ids, device="cuda")
+        kd = on.dequant_mxfp4(host(kp[b][sel]), host(ks[b][sel]))      # the pooled rows, in pool order
+        local = np.full((1, 1, P), -1, dtype=np.int64)
+        local[0, 0, :len(ids)] = np.arange(len(ids))
+        _bf16_close(hs[b:b + 1], oi.pool_scores(qd[b:b + 1], w[b:b + 1], kd[None], local))
+    assert np.array_equal(hi, _ascending(ot.pool_select(hs, pool, K, N=N)))
