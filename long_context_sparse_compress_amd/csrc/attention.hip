@@ -277,7 +277,6 @@ attn_bf16_kernel(Params P) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: row addressing stays scalar
   const int tg = TGN == 1 ? 0 : (wv >> 2), wid = wv & 3;     // tile group, wave within the group
   const int j = lane & 15, g = lane >> 4;
-  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   // transposing V reads: lane k of group g points at row 4g + k/4, columns 4(k%4)..
   const uint32_t voff = (4 * g + (j >> 2)) * kKsStride + 8 * (j & 3);
   // all splits (or head blocks) of a query -- and its q, and the combine
@@ -414,8 +413,8 @@ attn_bf16_kernel(Params P) {
       float mt = lg[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, lg[i]);
-      mt = fmaxf(mt, lane_read(x16, mt));
-      mt = fmaxf(mt, lane_read(x32, mt));
+      mt = pair_max16(mt);
+      mt = pair_max32(mt);
       const float m_new = fmaxf(m_run, mt);
       const bool none = (m_new == -INFINITY);
       const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
@@ -490,8 +489,8 @@ attn_bf16_kernel(Params P) {
 
   // per-head totals: lanes with (lane & 15) == h hold head 16*wid + h
   float l_tot = l_run;
-  l_tot += lane_read(x16, l_tot);
-  l_tot += lane_read(x32, l_tot);
+  l_tot = pair_sum16(l_tot, l_tot);
+  l_tot = pair_sum32(l_tot, l_tot);
   const int head_j = 16 * hb_qk + j;      // global head of this lane's logits (qk waves)
   const int hl_j = 16 * hl_qk + j;        // its slot in this workgroup's exchange
 

@@ -73,6 +73,31 @@ __device__ __forceinline__ float lane_read(int addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
 }
 
+// Pairwise combines across the two lane halves (32) or across neighbouring
+// 16-lane rows (16) on the gfx950 lane-swap instructions, with no LDS round
+// trip.  v_permlane32_swap trades the upper half of a with the lower half of
+// b, so the two results added give a[l] + a[l + 32] in the lower half and
+// b[l - 32] + b[l] in the upper half; v_permlane16_swap does the same for the
+// odd rows of a and the even rows of b (a[l] + a[l + 16] in rows 0 and 2,
+// b[l - 16] + b[l] in rows 1 and 3).  With a = b that is v + v[l ^ 32] (or
+// v[l ^ 16]) in every lane.  Every lane of the wave must take part.
+__device__ __forceinline__ float pair_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Partial rotary embedding ("DeepSeek Technical Reports", Hybrid Attention,
 // CSA; "DeepSeek V4 结构速览", the CSA operator graph; the rotation is
 // RoFormer's): pair p of the last R dimensions,

@@ -247,7 +247,6 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
     }
   }
 
-  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
   const int64_t krow0 = b * N;
   // Key fragments of one group (GT tiles); the next group's loads are issued
   // before the current group's MFMAs.
@@ -319,16 +318,12 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         }
       }
       const int64_t e = eg + kg * 64 + g * 16 + col;   // the entry this lane ends up holding
-      const bool hi = g >= 2, odd = g & 1;
 #pragma unroll
       for (int qi = 0; qi < QPW; ++qi) {
-        // lane ^ 32 flips g by 2: keep tiles {0,1} (g < 2) or {2,3}
-        float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
-        k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
-        k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
-        // lane ^ 16 flips g by 1: keep tile (g & 1) of the pair
-        float v = odd ? k1 : k0;
-        v += lane_read(x16, odd ? k0 : k1);
+        // across the halves (g by 2): lanes g < 2 keep tiles {0, 1}, g >= 2 tiles {2, 3};
+        // then across rows (g by 1): lane group g keeps tile g
+        const float k0 = pair_sum32(part[qi][0], part[qi][2]), k1 = pair_sum32(part[qi][1], part[qi][3]);
+        float v = pair_sum16(k0, k1);
         if (e >= vis[qi]) v = -INFINITY;
         if (e < N && t0 + qi < T) store_score(scores + (b * T + t0 + qi) * N + e, v);
       }
@@ -555,7 +550,6 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
       wv[qi][mt][0] = wt.x; wv[qi][mt][1] = wt.y; wv[qi][mt][2] = wt.z; wv[qi][mt][3] = wt.w;
     }
   const int qsc[4] = {127, 127, 127, 127};
-  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // ds_bpermute addresses
 
   float sc[QPW][TPW / 4];
   float part[QPW][4];
@@ -563,14 +557,10 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   auto scatter4 = [&](auto uc) {
     constexpr int u = decltype(uc)::value;
     const int64_t e = e_wave + 16 * (u - 3 + g) + col;
-    const bool hi = g >= 2, odd = g & 1;
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
-      float k0 = hi ? part[qi][2] : part[qi][0], k1 = hi ? part[qi][3] : part[qi][1];
-      k0 += lane_read(x32, hi ? part[qi][0] : part[qi][2]);
-      k1 += lane_read(x32, hi ? part[qi][1] : part[qi][3]);
-      float v = odd ? k1 : k0;
-      v += lane_read(x16, odd ? k0 : k1);
+      const float k0 = pair_sum32(part[qi][0], part[qi][2]), k1 = pair_sum32(part[qi][1], part[qi][3]);
+      float v = pair_sum16(k0, k1);
       sc[qi][u / 4] = (e >= vis[qi]) ? -INFINITY : v;
     }
   };

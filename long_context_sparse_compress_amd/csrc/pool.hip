@@ -155,8 +155,8 @@ index_pool_kernel(int64_t T, int64_t N, int64_t P, int64_t nblk, const uint8_t* 
         acc += wv[hb].x * fmaxf(cc[0], 0.f) + wv[hb].y * fmaxf(cc[1], 0.f) + wv[hb].z * fmaxf(cc[2], 0.f) +
                wv[hb].w * fmaxf(cc[3], 0.f);
       }
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
+      acc = pair_sum16(acc, acc);
+      acc = pair_sum32(acc, acc);
       if constexpr (QK == CSA_FP8_E4M3) acc *= kr[cur][u];
       const int64_t j = j0 + kChunk * c + 16 * u + r;
       if (g == 0 && j < P) out[j] = to_score<TS>(id[4 * c + u] >= 0 ? acc : -INFINITY);
