@@ -31,7 +31,7 @@ bounded sample of each configuration's step (about --cpu-seconds each).
 --workload NAME prints the same record for one workload: a configuration
 (csa_1m_decode, csa_decode, csa_prefill, hca_decode, hca_prefill) or another
 workload (csa_hca_decode, c128a_1m, csa_reindex_decode, csa_reindex_prefill,
-csa_paged_decode, hbm_copy, hbm_read).
+csa_paged_decode, csa_paged_1m_decode, hbm_copy, hbm_read).
 """
 from __future__ import annotations
 

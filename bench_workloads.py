@@ -684,6 +684,79 @@ def csa_paged_decode(torch, csa, synth, copies=1):
     return wk
 
 
+def csa_paged_1m_decode(torch, csa, synth, copies=2):
+    """The 1M-context Pro decode over the heterogeneous cache: 8 sequences at ragged
+    positions near 1,048,576, their C4A latents (bf16) and MXFP4 keys in shuffled
+    32-entry blocks of two pools under block tables, the window in 256-row rings;
+    paged compressor writes (latent, and the key quantized on write to MXFP4), the
+    paged MXFP4 indexer, per-sequence top-1024, paged sparse MQA.  Key pools and
+    their block tables are rotated over `copies` seeded copies (more than the
+    Infinity Cache in all)."""
+    bf = torch.bfloat16
+    dn = synth.device_normal
+    B, k, ring = 8, 1024, 256
+    g = np.random.default_rng(13)
+    seq = [int(x) for x in g.integers(1040384, 1048576, size=B)]
+    nblk = [(p + 1) // 128 + 1 for p in seq]
+    max_blocks = max(nblk)
+    n_pool = sum(nblk)
+    tables, kpools, kscales = [], [], []
+    for r in range(copies):
+        perm = g.permutation(n_pool)
+        t_np = np.full((B, max_blocks), -1, dtype=np.int32)
+        o = 0
+        for b in range(B):
+            t_np[b, :nblk[b]] = perm[o:o + nblk[b]]
+            o += nblk[b]
+        tables.append(torch.from_numpy(t_np).cuda())
+        x = dn(f"pm.keys.{r}", (n_pool, 32, 128))
+        a, sc = synth.device_quant_mxfp4(x)
+        del x
+        kpools.append(a)
+        kscales.append(sc)
+    pool4 = dn("pm.pool4", (n_pool, 32, 512), bf)
+    win = dn("pm.win", (B, ring, 512), bf)
+    q = dn("pm.q", (B, 64, 512), bf)
+    sp = torch.tensor(seq, dtype=torch.int64, device="cuda")
+    maxp = max(seq)
+    out = torch.empty_like(q)
+    ws_a = _ws(torch, csa, csa.OP_SPARSE_ATTN, B, 1, 1, 0)
+    vis4 = sum((p + 1) // 4 for p in seq)
+    qp, qs = synth.device_quant_mxfp4(dn("pm.qi", (B, 64, 128)))
+    wi = synth.device_uniform("pm.wi", (B, 64))
+    Nmax = 32 * max_blocks
+    scores = torch.empty(B, Nmax, dtype=bf, device="cuda")
+    idx = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    ws_t = _ws(torch, csa, csa.OP_TOPK, B, 1, Nmax, k)
+    p0 = torch.tensor([p - p % 4 for p in seq], dtype=torch.int64, device="cuda")
+    rb = {nm: dn(f"pm.rb.{nm}", (B, 4, 512), bf) for nm in ("Ca", "Za", "pCb", "pZb")}
+    rbk = {nm: dn(f"pm.rbk.{nm}", (B, 4, 128), bf) for nm in ("Ca", "Za", "pCb", "pZb")}
+    b4, b4k = dn("pm.b4", (8, 512), var=0.1), dn("pm.b4k", (8, 128), var=0.1)
+    wk = Work("csa_paged_1m_decode", "csa_paged_1m_decode: the 1M-context Pro decode over the paged cache, 8 sequences "
+              "at positions 1,040,384..1,048,575: paged compressor writes (latent bf16, key MXFP4), paged MXFP4 "
+              "indexer, per-sequence top-1024, paged sparse MQA", B, copies,
+              dict(batch=B, positions="1040384..1048575 (seeded)", topk=k, ring=ring, blocks=n_pool,
+                   index_qk="mxfp4", key_pool_copies_rotated=copies),
+              "lightning_index_paged")
+    wk.add("compress_paged_kv", lambda r: csa.csa_compress_paged(4, rb["Ca"], rb["Za"], b4, pool4, tables[r], p0,
+                                                                 prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
+           _c4_decode_bytes(B, 512), 0, "hbm")
+    wk.add("compress_paged_keys", lambda r: csa.csa_compress_paged(4, rbk["Ca"], rbk["Za"], b4k, kpools[r], tables[r],
+                                                                   p0, prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"],
+                                                                   scale_pool=kscales[r]),
+           _c4_decode_bytes(B, 128, 64 + 4), 0, "hbm")
+    wk.add("lightning_index_paged", lambda r: csa.lightning_index_paged(qp, wi, kpools[r], tables[r], sp,
+                                                                        qk_dtype=csa.MXFP4, q_scale=qs,
+                                                                        k_scale=kscales[r], scores=scores),
+           vis4 * 68 + B * 64 * 68 + B * 64 * 4 + B * Nmax * 2, vis4 * 64 * 128 * 2, "hbm")
+    wk.add("topk_select_paged", lambda r: csa.topk_select_paged(scores, k, sp, idx=idx, workspace=ws_t),
+           B * Nmax * 2 + B * k * 4, 0, "hbm")
+    wk.add("sparse_mqa_attn_paged", lambda r: csa.sparse_mqa_attn_paged(q, pool4, tables[r], idx, win, sp,
+                                                                        max_pos=maxp, out=out, workspace=ws_a),
+           B * ((k + 128) * 1024 + k * 4 + 2 * 64 * 512 * 2), B * (k + 128) * 64 * 512 * 4, "hbm")
+    return wk
+
+
 def hbm_copy(torch, csa, synth, copies=1):
     """A 1 GiB device copy: the calibration point of the HBM byte counters."""
     n = 1 << 28
@@ -720,5 +793,6 @@ def hbm_read(torch, csa, synth, copies=4):
 
 
 EXTRAS = {"csa_hca_decode": csa_hca_decode, "c128a_1m": c128a_1m, "csa_reindex_decode": csa_reindex_decode,
-          "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode, "hbm_copy": hbm_copy,
+          "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode,
+          "csa_paged_1m_decode": csa_paged_1m_decode, "hbm_copy": hbm_copy,
           "hbm_read": hbm_read}

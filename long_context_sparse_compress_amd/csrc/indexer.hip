@@ -248,6 +248,17 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   }
 
   const int64_t krow0 = b * N;
+  // paged: lane i holds the physical block of the wave's i-th 32-entry block
+  // (ids outside the pool, and blocks past the table, read block 0), so a
+  // tile's block is a readlane away instead of a dependent load per tile
+  [[maybe_unused]] int32_t my_blk = 0;
+  if constexpr (PG) {
+    static_assert(TPW % 2 == 0 && TPW / 2 <= 64, "a wave's blocks fit its lanes");
+    const int64_t lb = (e_wave >> 5) + lane;
+    int32_t v = 0;
+    if (lane < TPW / 2 && lb < pg.max_blocks) v = pg.table[b * pg.max_blocks + lb];
+    my_blk = (v >= 0 && v < pg.n_pool) ? v : 0;
+  }
   // Key fragments of one group (GT tiles); the next group's loads are issued
   // before the current group's MFMAs.
   F kb[2][GT];
@@ -264,8 +275,7 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
         // or wholly past it; a tile past it (never stored) reads the last one
         int64_t e0 = eg + tt * 16;
         if (e0 >= N) e0 = N - 16;
-        int64_t blk = pg.table[b * pg.max_blocks + (e0 >> 5)];
-        if (blk < 0 || blk >= pg.n_pool) blk = 0;
+        const int64_t blk = __builtin_amdgcn_readlane(my_blk, static_cast<int>((e0 - e_wave) >> 5));
         row = (blk << 5) + (e0 & 31) + col;
       } else {
         int64_t e = eg + tt * 16 + col;

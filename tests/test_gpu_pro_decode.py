@@ -175,3 +175,27 @@ def test_pro_decode_chain_one_sequence():
     ref, _ = oa.sparse_mqa(q, rows[None], np.arange(len(sel))[None, None], raw, RAW0, T_POS, 128)
     assert max_abs(g_out, ref[0, 0]) < ATTN_BF16_MAX_ABS
     assert normwise_rel(g_out, ref[0, 0]) < ATTN_NORMWISE
+
+
+def test_mxfp4_paged_indexer_equals_contiguous_full_size():
+    """The paged MXFP4 indexer over the same 8 x 262,144 keys laid out in
+    shuffled 32-entry pages gives the contiguous indexer's scores bit for bit
+    (same kernel shape; paging only moves each tile's base row)."""
+    kp, ks = _mxfp4_keys("pro.pg.k", B)
+    q = synth.device_normal("pro.pg.q", (B, 1, 64, 128))
+    qp, qs = synth.device_quant_mxfp4(q)
+    w = synth.device_uniform("pro.pg.w", (B, 1, 64))
+    per_seq = N // 32
+    g = np.random.default_rng(5)
+    perm = torch.as_tensor(g.permutation(B * per_seq), dtype=torch.int64, device="cuda")
+    pool = torch.empty(B * per_seq, 32, 64, dtype=torch.uint8, device="cuda")
+    spool = torch.empty(B * per_seq, 32, 4, dtype=torch.uint8, device="cuda")
+    pool[perm] = kp.reshape(B * per_seq, 32, 64)
+    spool[perm] = ks.reshape(B * per_seq, 32, 4)
+    table = perm.reshape(B, per_seq).to(torch.int32)
+    seq_pos = torch.full((B,), T_POS, dtype=torch.int64, device="cuda")
+    ref = csa.lightning_index(qp, w, kp, q_pos0=T_POS, qk_dtype=csa.MXFP4, q_scale=qs, k_scale=ks, score_dtype=BF)
+    got = csa.lightning_index_paged(qp[:, 0], w[:, 0], pool, table, seq_pos, qk_dtype=csa.MXFP4, q_scale=qs[:, 0],
+                                    k_scale=spool, score_dtype=BF)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref[:, 0])
