@@ -19,9 +19,12 @@ Timing: W untimed steps, then K steps between two HIP events on the stream
 the kernels run on (one HIP graph per cache copy; --eager times eager
 launches), ms_per_step = elapsed / K and value = query tokens / s.  A second,
 eager pass brackets every stage with events on that stream: each stage's
-average duration, and from it the dominant kernel's roofline fraction
-(algorithmic bytes or FLOPs of one launch / duration, against 8 TB/s HBM or
-the MFMA peak of its dtype).  `traffic` is the HBM bytes per launch read
+average duration (which includes its launch's dispatch).  The dominant
+kernel's launch duration is timed on its own: a HIP graph of its launches
+back to back over the cache copies, replayed between two events on its
+stream; from it the roofline fraction (algorithmic bytes or FLOPs of one
+launch / duration, against 8 TB/s HBM or the MFMA peak of its dtype).
+`traffic` is the HBM bytes per launch read
 from the committed FETCH_SIZE / WRITE_SIZE counter record of that kernel
 (profiles/), or null when the kernel's sources changed since.
 
@@ -134,6 +137,35 @@ def time_stages(torch, wk, steps):
     return {n: v / steps for n, v in acc.items()}
 
 
+def time_kernel(torch, wk, stage, reps=10):
+    """Average duration of one launch of `stage` alone: a HIP graph of 2 x copies
+    back-to-back launches (cache copy i % copies each), replayed `reps` times
+    between two events on its stream (ms per launch)."""
+    fn = next(s for s in wk.stages if s[0] == stage)[1]
+    st = torch.cuda.Stream()
+    n = 2 * wk.copies
+    with torch.cuda.stream(st):
+        for i in range(n):
+            fn(i % wk.copies)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for i in range(n):
+            fn(i % wk.copies)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * n)
+
+
 # ---------------------------------------------------------------- records
 
 
@@ -176,8 +208,11 @@ def measure(torch, wk, args):
                         "TFLOP/s": round(fl / (t * 1e-3) / 1e12, 2) if fl else None,
                         "roofline": roofline(bound, nb, fl, t)}
     dom = next(s for s in wk.stages if s[0] == wk.dominant)
-    roof = dict(stages[dom[0]]["roofline"], kernel=dom[0], traffic=counter_traffic(wk.key, dom[0]),
-                avg_launch_us=stages[dom[0]]["us"])
+    # the dominant kernel's launch time: its launches back to back in a graph
+    # (the stage table's eager events also hold each launch's dispatch)
+    t_dom = time_kernel(torch, wk, dom[0]) if not args.eager else per[dom[0]]
+    roof = dict(roofline(dom[4], dom[2], dom[3], t_dom), kernel=dom[0], traffic=counter_traffic(wk.key, dom[0]),
+                avg_launch_us=round(t_dom * 1e3, 2), eager_event_us=stages[dom[0]]["us"])
     roof["algorithmic_bytes_per_launch" if dom[4] == "hbm" else "algorithmic_flops_per_launch"] = \
         dom[2] if dom[4] == "hbm" else dom[3]
     total = sum(s[2] for s in wk.stages)
