@@ -394,9 +394,11 @@ def test_compress_paged_decode_write(ratio, c, out):
     assert np.array_equal(hp[~written], hb[~written])
 
 
-@pytest.mark.parametrize("ratio,c,out,n_tok", [(4, 512, "bf16", 256), (4, 128, "fp8", 130), (4, 128, "fp4", 64),
-                                               (128, 512, "bf16", 300), (4, 192, "f32", 36), (128, 256, "f32", 384)])
-def test_compress_paged_chunk_write(ratio, c, out, n_tok):
+@pytest.mark.parametrize("ratio,c,out,n_tok,rope", [(4, 512, "bf16", 256, 64), (4, 128, "fp8", 130, 64),
+                                                    (4, 128, "fp4", 64, 64), (128, 512, "bf16", 300, 64),
+                                                    (4, 192, "f32", 36, 64), (128, 256, "f32", 384, 64),
+                                                    (4, 512, "bf16", 40, 0), (128, 512, "f32", 256, 0)])
+def test_compress_paged_chunk_write(ratio, c, out, n_tok, rope):
     """Chunked prefill into pages: each sequence compresses its own chunk,
     starting at its own block start, entry by entry into its page slots.
     The chunks cross page boundaries; one sequence has an absent page in the
@@ -446,7 +448,7 @@ def test_compress_paged_chunk_write(ratio, c, out, n_tok):
     csa.csa_compress_paged_chunk(ratio, d["Ca"], d["Za"], dev(bias), pool, dev(table, torch.int32),
                                  torch.tensor(pos, dtype=torch.int64, device="cuda"), Cb=d.get("Cb"),
                                  Zb=d.get("Zb"), prev_Cb=d.get("prev_Cb"), prev_Zb=d.get("prev_Zb"),
-                                 scale_pool=spool, rope_dims=64, rope_anchor=ratio - 1)
+                                 scale_pool=spool, rope_dims=rope, rope_anchor=ratio - 1 if rope else 0)
     torch.cuda.synchronize()
     hp, hb = host(pool), host(before)
     written = np.zeros(hp.shape[:2] if per > 1 else hp.shape[:1], dtype=bool)
@@ -455,7 +457,7 @@ def test_compress_paged_chunk_write(ratio, c, out, n_tok):
             continue
         x = inp[b]
         ref = oc.compress(x["Ca"], x["Za"], bias, ratio, x.get("Cb"), x.get("Zb"), x.get("prev_Cb"),
-                          x.get("prev_Zb"), pos0=p, rope_dims=64, rope_anchor=ratio - 1)[0]
+                          x.get("prev_Zb"), pos0=p, rope_dims=rope, rope_anchor=ratio - 1 if rope else 0)[0]
         for i in range(n_ent):
             e = p // ratio + i
             blk = table[b, e // per]
