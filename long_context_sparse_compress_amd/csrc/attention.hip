@@ -23,9 +23,12 @@
 //    16w..16w+15 with their q in registers.  The C layout of S^T gives lane
 //    (head j, group g) the logits of rows {4g..4g+3, 16+4g..16+4g+3};
 //  * online softmax in the exp2 domain (logits pre-multiplied by log2 e) on
-//    those registers.  Packed to bf16 they are already lane (j, g)'s slice of
-//    the A operand of P V for that head block, so each wave publishes them in
-//    LDS as one 16-byte word per lane, with its heads' rescale factors;
+//    those registers, against a reference maximum that moves only when a
+//    tile's maximum exceeds it by more than a factor 2^8, so O is rarely
+//    rescaled.  Packed to bf16 the probabilities are already lane (j, g)'s
+//    slice of the A operand of P V for that head block, so each wave
+//    publishes them in LDS as one 16-byte word per lane, with its heads'
+//    rescale factors;
 //  * P V is split over the latent dimension instead of the heads: wave w
 //    computes O[all 64 heads, 128w..128w+127] from the four published P blocks
 //    and V columns it reads with transposing LDS reads (ds_read_b64_tr_b16)
@@ -52,6 +55,7 @@ constexpr int kD = 512;
 constexpr int kTile = kAttnTile;            // 32 rows
 constexpr int kKsStride = kD * 2 + 16;      // bytes per row of the row-major tile (padded)
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLazyMax = 8.f;             // see the online softmax in attn_bf16_kernel
 
 struct Params {
   int64_t B, T, N;
@@ -415,9 +419,16 @@ attn_bf16_kernel(Params P) {
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, lg[i]);
       mt = pair_max16(mt);
       mt = pair_max32(mt);
-      const float m_new = fmaxf(m_run, mt);
+      // The reference maximum moves only when the tile's exceeds it by more
+      // than kLazyMax (log2 units): the exponentials stay below 2^kLazyMax,
+      // and a running maximum that creeps up costs no rescale of O.  Every
+      // later merge takes (max, sum, O) relative to whatever reference each
+      // side used, so the result is the same up to rounding.
+      const bool move = mt > m_run + kLazyMax;   // false while both are -inf
+      const float m_new = move ? mt : m_run;
       const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+      // (before the first real row O and the sum are zero: nothing to rescale)
+      const float alpha = move && m_run != -INFINITY ? fast_exp2(m_run - m_new) : 1.f;
       float p[8], psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {

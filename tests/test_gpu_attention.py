@@ -363,3 +363,37 @@ def test_sparse_idx_whole_tiles_of_padding():
     got = host(out)
     for b in range(B):
         _assert_bf16(got[b, 0], _sparse_ref(q, kv, scr, raw, rp0, q0, b, 0))
+
+
+@pytest.mark.parametrize("T,bi", [(1, False), (1, True), (40, False)])
+def test_growing_logits_force_rescales(T, bi):
+    """Rows whose logits climb from tile to tile by steps both below and above
+    the kernel's rescale threshold (a factor 2^8), so the running reference
+    maximum both stays put and moves after O has accumulated: split decode,
+    batch-invariant and a multi-query chunk against the oracle."""
+    B, N, k = 2, 2048, 640
+    q0 = 4 * N - T
+    q, kv, raw, idx, rp0 = _sparse_case(f"at.grow{T}{bi}", B, T, N, k, q0)
+    rng = np.random.default_rng(7)
+    u = q[:, :, :].float().mean(dim=(1, 2))                       # [B, 512]
+    u = u / u.norm(dim=1, keepdim=True)
+    for b in range(B):
+        # entry order of query 0's list: tile i (32 slots) gets rows along u
+        # with a per-tile level climbing by 0 to ~14 log2 units a tile
+        sel = idx[b, 0]
+        level = np.cumsum(rng.uniform(0.0, 80.0, size=k // 32))
+        lv = np.repeat(level, 32) + rng.normal(0.0, 4.0, size=k)
+        rows = torch.as_tensor(lv, dtype=torch.float32, device=kv.device)[:, None] * u[b][None, :]
+        for p in range(k):
+            if sel[p] >= 0:
+                kv[b, int(sel[p])] = (rows[p] + 0.1 * kv[b, int(sel[p])].float()).to(BF)
+    out = csa.sparse_mqa_attn(q, kv, dev(idx, torch.int32), raw, q_pos0=q0, raw_pos0=rp0,
+                              batch_invariant=bi)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        for t in sorted({0, T // 2, T - 1}):
+            r = _sparse_ref(q, kv, idx, raw, rp0, q0, b, t)
+            big = np.abs(r).max()
+            assert max_abs(got[b, t], r) < ATTN_BF16_MAX_ABS * max(1.0, big)
+            assert normwise_rel(got[b, t], r) < ATTN_NORMWISE
