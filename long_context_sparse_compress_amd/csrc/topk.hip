@@ -1036,7 +1036,7 @@ hipError_t launch_typed(const TopkArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if constexpr (sizeof(KT) == 2) {
-    // long bf16 rows: slices of 8192 keys, a full 16-bit histogram each
+    // long bf16 rows: slices of kFineSlice keys, a full 16-bit histogram each
     if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0) return launch_fine(a, s);
   }
   const int S = kTopkSlices;
