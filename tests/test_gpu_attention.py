@@ -397,3 +397,29 @@ def test_growing_logits_force_rescales(T, bi):
             big = np.abs(r).max()
             assert max_abs(got[b, t], r) < ATTN_BF16_MAX_ABS * max(1.0, big)
             assert normwise_rel(got[b, t], r) < ATTN_NORMWISE
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_growing_logits_force_rescales_dense(T):
+    """Dense HCA rows (with sink) whose logits climb from tile to tile by steps
+    on both sides of the rescale threshold: the two-tile-group split decode
+    (T = 1, 8,320 rows) and a short chunk, against the oracle."""
+    B, N = 2, 8192
+    q0 = 128 * N - T
+    q, kv, raw, sink, rp0 = _hca_case(f"at.hgrow{T}", B, T, N, q0)
+    rng = np.random.default_rng(11)
+    u = q.float().mean(dim=(1, 2))
+    u = u / u.norm(dim=1, keepdim=True)
+    level = np.repeat(np.cumsum(rng.uniform(0.0, 80.0, size=N // 32)), 32) + rng.normal(0.0, 4.0, size=N)
+    lv = torch.as_tensor(level, dtype=torch.float32, device=kv.device)
+    for b in range(B):
+        kv[b] = (lv[:, None] * u[b][None, :] + 0.1 * kv[b].float()).to(BF)
+    out = csa.hca_attn(q, kv, raw, q_pos0=q0, raw_pos0=rp0, sink=sink)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        for t in sorted({0, T - 1}):
+            r, _ = _dense_ref(q, kv, raw, rp0, q0, b, t, 128, sink)
+            big = np.abs(r).max()
+            assert max_abs(got[b, t], r) < ATTN_BF16_MAX_ABS * max(1.0, big)
+            assert normwise_rel(got[b, t], r) < ATTN_NORMWISE
