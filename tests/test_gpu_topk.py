@@ -149,3 +149,22 @@ def test_lds_path_large_rows(dtype, N, k, ties):
     """Rows whose LDS copy needs more than 64 KiB of dynamic LDS."""
     x, d = _scores(f"tk.lds{N}", 3, 1, N, dtype, ties=ties)
     _check(_run(d, k, 4 * N - 1), ot.topk_select(x, k, 4 * N - 1, 4))
+
+
+def test_long_rows_ragged_batch_slice_edges():
+    """The long-row (sliced) path with each sequence at its own position: visible
+    lengths 0, k - 1, k, k + 1, one and just past one 16,384-key slice, a ragged
+    mid-row end and the whole row, with heavy ties; k = 1024."""
+    N, k = 262144, 1024
+    V = [0, k - 1, k, k + 1, 16384, 16385, 100003, N]
+    x, d = _scores("tk.ragged", len(V), 1, N, "bf16", ties=8)
+    x, d = x[:, 0], d[:, 0].contiguous()
+    sp = torch.as_tensor([4 * v + 2 for v in V], dtype=torch.int64, device="cuda")   # (pos + 1) // 4 = v
+    got = csa.topk_select_paged(d, k, sp)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    for b, v in enumerate(V):
+        r = ot.select_row(x[b], v, k)
+        nv = int((r >= 0).sum())
+        assert np.all(got[b, nv:] == -1), b
+        assert np.array_equal(got[b, :nv], np.sort(r[:nv])), b
