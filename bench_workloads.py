@@ -665,12 +665,13 @@ def csa_paged_decode(torch, csa, synth, copies=1):
               "49,152..81,919: paged compressor writes, paged indexer, per-sequence Top-k, paged sparse MQA and HCA",
               B, copies, dict(batch=B, positions="49152..81919 (seeded)", topk=k, ring=ring, blocks=n_pool),
               "lightning_index_paged")
-    wk.add("compress_paged_kv", lambda r: csa.csa_compress_paged(4, rb["Ca"], rb["Za"], b4, pool4, table, p0,
-                                                                 prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
-           _c4_decode_bytes(B, 512), 0, "hbm")
-    wk.add("compress_paged_keys", lambda r: csa.csa_compress_paged(4, rbk["Ca"], rbk["Za"], b4k, kpool, table, p0,
-                                                                   prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"]),
-           _c4_decode_bytes(B, 128), 0, "hbm")
+    # the latent and the indexer key in one launch
+    wk.add("compress_paged_kv_keys", lambda r: csa.csa_compress_paged_batch([
+        dict(ratio=4, Ca=rb["Ca"], Za=rb["Za"], bias=b4, pool=pool4, block_table=table, pos0=p0,
+             prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
+        dict(ratio=4, Ca=rbk["Ca"], Za=rbk["Za"], bias=b4k, pool=kpool, block_table=table, pos0=p0,
+             prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"])]),
+           _c4_decode_bytes(B, 512) + _c4_decode_bytes(B, 128), 0, "hbm")
     wk.add("lightning_index_paged", lambda r: csa.lightning_index_paged(qi, wi, kpool, table, sp, scores=scores),
            vis4 * 256 + B * 64 * 128 * 2 + B * 64 * 4 + B * Nmax * 2, vis4 * 64 * 128 * 2, "hbm")
     wk.add("topk_select_paged", lambda r: csa.topk_select_paged(scores, k, sp, idx=idx, workspace=ws_t),
@@ -738,13 +739,13 @@ def csa_paged_1m_decode(torch, csa, synth, copies=2):
               dict(batch=B, positions="1040384..1048575 (seeded)", topk=k, ring=ring, blocks=n_pool,
                    index_qk="mxfp4", key_pool_copies_rotated=copies),
               "lightning_index_paged")
-    wk.add("compress_paged_kv", lambda r: csa.csa_compress_paged(4, rb["Ca"], rb["Za"], b4, pool4, tables[r], p0,
-                                                                 prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
-           _c4_decode_bytes(B, 512), 0, "hbm")
-    wk.add("compress_paged_keys", lambda r: csa.csa_compress_paged(4, rbk["Ca"], rbk["Za"], b4k, kpools[r], tables[r],
-                                                                   p0, prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"],
-                                                                   scale_pool=kscales[r]),
-           _c4_decode_bytes(B, 128, 64 + 4), 0, "hbm")
+    # the bf16 latent and the MXFP4 indexer key in one launch
+    wk.add("compress_paged_kv_keys", lambda r: csa.csa_compress_paged_batch([
+        dict(ratio=4, Ca=rb["Ca"], Za=rb["Za"], bias=b4, pool=pool4, block_table=tables[r], pos0=p0,
+             prev_Cb=rb["pCb"], prev_Zb=rb["pZb"]),
+        dict(ratio=4, Ca=rbk["Ca"], Za=rbk["Za"], bias=b4k, pool=kpools[r], block_table=tables[r], pos0=p0,
+             prev_Cb=rbk["pCb"], prev_Zb=rbk["pZb"], scale_pool=kscales[r])]),
+           _c4_decode_bytes(B, 512) + _c4_decode_bytes(B, 128, 64 + 4), 0, "hbm")
     wk.add("lightning_index_paged", lambda r: csa.lightning_index_paged(qp, wi, kpools[r], tables[r], sp,
                                                                         qk_dtype=csa.MXFP4, q_scale=qs,
                                                                         k_scale=kscales[r], scores=scores),

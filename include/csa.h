@@ -16,8 +16,9 @@
  * same operations with partial RoPE fused in, and the batch-invariant
  * attention mode), csa_rope (partial RoPE on query or window rows), and
  * lightning_index_pool / topk_select_pool (the hierarchical indexer), and
- * csa_compress_paged / csa_compress_paged_chunk / lightning_index_paged /
- * topk_select_paged / sparse_mqa_attn_paged / hca_attn_paged (the paged cache).
+ * csa_compress_paged / csa_compress_paged_chunk / csa_compress_paged_batch /
+ * lightning_index_paged / topk_select_paged / sparse_mqa_attn_paged /
+ * hca_attn_paged (the paged cache).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -513,6 +514,41 @@ int csa_compress_paged_chunk(int ratio, int64_t B, int64_t n_tok, int64_t c, con
                              void* scale_pool, int64_t n_pool, const int32_t* block_table,
                              int64_t max_blocks, int rope_dims, float rope_base, int rope_anchor,
                              void* stream);
+
+/*
+ * csa_compress_paged_batch -- several csa_compress_paged_chunk calls in one
+ * launch.
+ *
+ * The same operation as csa_compress_paged_chunk, for callers that write
+ * more than one compressed stream per step (the paged decode step's 512-d
+ * latent and its 128-d indexer key): each job is exactly that call's
+ * arguments (without stream), and the results are those of the separate
+ * calls, bit for bit.  1 to 4 jobs, sharing ratio and in_dtype; their
+ * out_dtype is one float type, or CSA_FP8_E4M3 / CSA_MXFP4 jobs (C4A) beside
+ * jobs of one float type.  Errors: those of csa_compress_paged_chunk for each
+ * job (the message names the job), CSA_ERR_INVALID_ARG for a NULL jobs, a job
+ * count outside 1..4 or jobs that do not share ratio and dtypes.
+ */
+typedef struct csa_compress_paged_job {
+  int ratio;
+  int64_t B, n_tok, c;
+  const int64_t* pos0;
+  const void *Ca, *Za, *Cb, *Zb, *prev_Cb, *prev_Zb;
+  const float* bias;
+  const float* gamma;
+  float eps;
+  int in_dtype, out_dtype;
+  void* pool;
+  void* scale_pool;
+  int64_t n_pool;
+  const int32_t* block_table;
+  int64_t max_blocks;
+  int rope_dims;
+  float rope_base;
+  int rope_anchor;
+} csa_compress_paged_job;
+
+int csa_compress_paged_batch(const csa_compress_paged_job* jobs, int n_jobs, void* stream);
 
 /*
  * lightning_index_paged / topk_select_paged -- the decode indexer and Top-k

@@ -19,6 +19,7 @@ import torch
 __all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
            "sparse_mqa_attn_noalloc",
            "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "csa_compress_paged_chunk",
+           "csa_compress_paged_batch",
            "lightning_index_paged",
            "topk_select_paged",
            "sparse_mqa_attn_paged", "hca_attn_paged",
@@ -90,6 +91,8 @@ def library() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _int, _vp]
         lib.csa_compress_batch.restype = ctypes.c_int
+        lib.csa_compress_paged_batch.argtypes = [ctypes.POINTER(_CompressPagedJob), _int, _vp]
+        lib.csa_compress_paged_batch.restype = ctypes.c_int
         lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
         lib.csa_workspace_bytes.restype = ctypes.c_size_t
         lib.csa_last_error.restype = ctypes.c_char_p
@@ -149,6 +152,15 @@ class _CompressJob(ctypes.Structure):
                 ("bias", _vp), ("gamma", _vp), ("eps", _f32), ("in_dtype", _int), ("out_dtype", _int),
                 ("out", _vp), ("out_batch_stride", _i64), ("rope_dims", _int), ("rope_base", _f32),
                 ("rope_anchor", _int), ("out_scale", _vp)]
+
+
+class _CompressPagedJob(ctypes.Structure):
+    """csa_compress_paged_job of csa.h."""
+    _fields_ = [("ratio", _int), ("B", _i64), ("n_tok", _i64), ("c", _i64), ("pos0", _vp),
+                ("Ca", _vp), ("Za", _vp), ("Cb", _vp), ("Zb", _vp), ("prev_Cb", _vp), ("prev_Zb", _vp),
+                ("bias", _vp), ("gamma", _vp), ("eps", _f32), ("in_dtype", _int), ("out_dtype", _int),
+                ("pool", _vp), ("scale_pool", _vp), ("n_pool", _i64), ("block_table", _vp), ("max_blocks", _i64),
+                ("rope_dims", _int), ("rope_base", _f32), ("rope_anchor", _int)]
 
 
 def _out_dt(t: torch.Tensor, c=None) -> int:
@@ -439,6 +451,29 @@ def csa_compress_paged_chunk(ratio, Ca, Za, bias, pool, block_table, pos0, *, Cb
                                             rope_anchor, _stream(stream))
     _check(st, "csa_compress_paged_chunk")
     return pool
+
+
+def csa_compress_paged_batch(jobs, stream=None):
+    """Several csa_compress_paged_chunk calls in one launch.  Each job is a dict of
+    that call's arguments (ratio, Ca, Za, bias, pool, block_table, pos0 and
+    optionally Cb, Zb, prev_Cb, prev_Zb, gamma, eps, scale_pool, rope_dims,
+    rope_base, rope_anchor); returns the pools."""
+    arr = (_CompressPagedJob * len(jobs))()
+    for j, d in zip(arr, jobs):
+        Ca, pool, table = d["Ca"], d["pool"], d["block_table"]
+        B, n_tok, c = Ca.shape
+        j.ratio, j.B, j.n_tok, j.c, j.pos0 = d["ratio"], B, n_tok, c, _ptr(d["pos0"])
+        j.Ca, j.Za, j.Cb, j.Zb = _ptr(Ca), _ptr(d["Za"]), _ptr(d.get("Cb")), _ptr(d.get("Zb"))
+        j.prev_Cb, j.prev_Zb = _ptr(d.get("prev_Cb")), _ptr(d.get("prev_Zb"))
+        j.bias, j.gamma, j.eps = _ptr(d["bias"]), _ptr(d.get("gamma")), d.get("eps", 1e-6)
+        j.in_dtype, j.out_dtype = _dt(Ca), _out_dt(pool, c)
+        j.pool, j.scale_pool, j.n_pool = _ptr(pool), _ptr(d.get("scale_pool")), pool.shape[0]
+        j.block_table, j.max_blocks = _ptr(table), table.shape[1]
+        j.rope_dims, j.rope_base, j.rope_anchor = (d.get("rope_dims", 0), d.get("rope_base", ROPE_BASE),
+                                                   d.get("rope_anchor", 0))
+    st = library().csa_compress_paged_batch(arr, len(jobs), _stream(stream))
+    _check(st, "csa_compress_paged_batch")
+    return [d["pool"] for d in jobs]
 
 
 def lightning_index_paged(q, w, k_pool, block_table, seq_pos, *, qk_dtype=None, q_scale=None, k_scale=None,

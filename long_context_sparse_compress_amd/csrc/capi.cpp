@@ -196,7 +196,37 @@ int csa_compress_paged_chunk(int ratio, int64_t B, int64_t n_tok, int64_t c, con
   csa::CompressPagedArgs a{ratio, B, c, pos0, n_tok, Ca, Za, Cb, Zb, prev_Cb, prev_Zb, bias, gamma, eps, in_dtype,
                            out_dtype, pool, scale_pool, n_pool, block_table, max_blocks, rope_dims, rope_base,
                            rope_anchor};
-  return hip_status(csa::launch_compress_paged(a, as_stream(stream)), "csa_compress_paged launch");
+  return hip_status(csa::launch_compress_paged(&a, 1, as_stream(stream)), "csa_compress_paged launch");
+}
+
+int csa_compress_paged_batch(const csa_compress_paged_job* jobs, int n_jobs, void* stream) {
+  csa::Check ck;
+  if (!jobs) ck.fail(CSA_ERR_INVALID_ARG, "jobs is NULL");
+  else if (n_jobs < 1 || n_jobs > 4) ck.fail(CSA_ERR_INVALID_ARG, "n_jobs must be 1..4, got " + csa::i2s(n_jobs));
+  if (!ck.ok()) return finish(ck);
+  csa::CompressPagedArgs a[4];
+  auto quant = [](int dt) { return dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; };
+  for (int q = 0; q < n_jobs; ++q) {
+    const csa_compress_paged_job& j = jobs[q];
+    csa::Check cj = csa::check_compress_paged(j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb,
+                                              j.prev_Zb, j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.pool,
+                                              j.scale_pool, j.n_pool, j.block_table, j.max_blocks, j.rope_dims,
+                                              j.rope_base, j.rope_anchor);
+    bool same_out = true;
+    for (int p = 0; p < q; ++p)
+      if (jobs[p].out_dtype != j.out_dtype && !quant(jobs[p].out_dtype) && !quant(j.out_dtype)) same_out = false;
+    if (cj.ok() && (j.ratio != jobs[0].ratio || j.in_dtype != jobs[0].in_dtype || !same_out))
+      cj.fail(CSA_ERR_INVALID_ARG, "jobs of one batch must share ratio, in_dtype and out_dtype (fp8 / MXFP4 jobs "
+                                   "may join jobs of one other output type)");
+    if (!cj.ok()) {
+      cj.msg = "job " + csa::i2s(q) + ": " + cj.msg;
+      return finish(cj);
+    }
+    a[q] = csa::CompressPagedArgs{j.ratio, j.B, j.c, j.pos0, j.n_tok, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb,
+                                  j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.pool, j.scale_pool, j.n_pool,
+                                  j.block_table, j.max_blocks, j.rope_dims, j.rope_base, j.rope_anchor};
+  }
+  return hip_status(csa::launch_compress_paged(a, n_jobs, as_stream(stream)), "csa_compress_paged_batch launch");
 }
 
 int csa_compress_paged(int ratio, int64_t B, int64_t c, const int64_t* pos0, const void* Ca, const void* Za,

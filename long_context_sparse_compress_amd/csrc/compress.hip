@@ -425,33 +425,67 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
 // slot (e % 32 for C4A) of its physical block table[b][e / (32 or 1)].  A
 // sequence whose position is not a block start, or whose block is absent,
 // writes nothing (the whole workgroup returns before any barrier).
+// One compression into pages (a call's arguments on the device).
+struct PagedJobDev {
+  const void *Ca, *Za, *Cb, *Zb, *pCb, *pZb;
+  const float* bias;
+  const float* gamma;
+  void* pool;
+  void* scale_pool;
+  const int64_t* pos0s;
+  const int32_t* table;
+  int64_t n_tok, n_ent, B, n_pool, max_blocks;
+  float eps;
+  int c, G;
+  int rope_R;
+  double rope_l2b;
+  int rope_anchor;
+  int qfmt;   // MIXED batches: 1 fp8, 2 fp4, 0 the float type
+};
+constexpr int kMaxPagedJobs = 4;
+struct PagedBatch {
+  PagedJobDev j[kMaxPagedJobs];
+};
+
 template <typename TI, typename TO, int RATIO>
-__global__ void __launch_bounds__(kCompressThreads<RATIO>)
-compress_paged_kernel(int c, int64_t n_tok, const int64_t* __restrict__ pos0s, const TI* __restrict__ Ca,
-                      const TI* __restrict__ Za, const TI* __restrict__ Cb, const TI* __restrict__ Zb,
-                      const TI* __restrict__ pCb, const TI* __restrict__ pZb,
-                      const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
-                      TO* __restrict__ pool, void* __restrict__ scale_pool, int64_t n_pool,
-                      const int32_t* __restrict__ table, int64_t max_blocks, int G, int rope_R, double rope_l2b,
-                      int rope_anchor) {
+__device__ __forceinline__ void paged_entry(const PagedJobDev& J) {
   constexpr int SH = RATIO == 4 ? 5 : 0;   // log2 entries per block
   const int64_t b = blockIdx.y;
   const int64_t i = blockIdx.x;            // entry of the chunk
-  const int64_t p0 = pos0s[b];
+  const int64_t p0 = J.pos0s[b];
   if (p0 < 0 || p0 % RATIO) return;
   const int64_t e = p0 / RATIO + i;
-  if ((e >> SH) >= max_blocks) return;
-  const int64_t blk = table[b * max_blocks + (e >> SH)];
-  if (blk < 0 || blk >= n_pool) return;
+  if ((e >> SH) >= J.max_blocks) return;
+  const int64_t blk = J.table[b * J.max_blocks + (e >> SH)];
+  if (blk < 0 || blk >= J.n_pool) return;
   const int64_t row = (blk << SH) + (e & ((int64_t{1} << SH) - 1));
+  const int c = J.c;
   // entry i of the chunk, written at `row` (no batch stride)
   constexpr bool kFp4 = std::is_same_v<TO, E2M1x2>;
-  TO* dst = kFp4 ? reinterpret_cast<TO*>(reinterpret_cast<uint8_t*>(pool) + row * c / 2) : pool + row * c;
-  void* sdst = !scale_pool ? nullptr
-               : kFp4      ? static_cast<void*>(static_cast<uint8_t*>(scale_pool) + row * (c / 32))
-                           : static_cast<void*>(static_cast<float*>(scale_pool) + row);
-  compress_entry<TI, TO, RATIO, false>(i, b, 0, 1, n_tok, c, p0, Ca, Za, Cb, Zb, pCb, pZb, bias, gamma, eps, dst, 0,
-                                       G, nullptr, rope_R, rope_l2b, rope_anchor, sdst, 0, 0);
+  TO* dst = kFp4 ? reinterpret_cast<TO*>(static_cast<uint8_t*>(J.pool) + row * c / 2) : static_cast<TO*>(J.pool) + row * c;
+  void* sdst = !J.scale_pool ? nullptr
+               : kFp4        ? static_cast<void*>(static_cast<uint8_t*>(J.scale_pool) + row * (c / 32))
+                             : static_cast<void*>(static_cast<float*>(J.scale_pool) + row);
+  compress_entry<TI, TO, RATIO, false>(i, b, 0, 1, J.n_tok, c, p0, static_cast<const TI*>(J.Ca),
+                                       static_cast<const TI*>(J.Za), static_cast<const TI*>(J.Cb),
+                                       static_cast<const TI*>(J.Zb), static_cast<const TI*>(J.pCb),
+                                       static_cast<const TI*>(J.pZb), J.bias, J.gamma, J.eps, dst, 0, J.G, nullptr,
+                                       J.rope_R, J.rope_l2b, J.rope_anchor, sdst, 0, 0);
+}
+
+// Up to four writes into pages in one launch (blockIdx.z picks the job; the
+// paged decode step's bf16 latent and quantized indexer key together).
+// MIXED: jobs writing fp8 or MXFP4 codes sit beside jobs of the float type TO.
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
+__global__ void __launch_bounds__(kCompressThreads<RATIO>)
+compress_paged_kernel(PagedBatch jb) {
+  const PagedJobDev& J = jb.j[blockIdx.z];
+  if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
+  if constexpr (MIXED) {
+    if (J.qfmt == 1) return paged_entry<TI, uint8_t, RATIO>(J);
+    if (J.qfmt == 2) return paged_entry<TI, E2M1x2, RATIO>(J);
+  }
+  paged_entry<TI, TO, RATIO>(J);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -674,41 +708,71 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 
 namespace {
 
-template <typename TI, typename TO, int RATIO>
-hipError_t launch_paged_t(const CompressPagedArgs& a, hipStream_t s) {
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
+hipError_t launch_paged_t(const CompressPagedArgs* jobs, int n, hipStream_t s) {
   constexpr int VEC = Vec<TI>::n;
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
-  const int CT = static_cast<int>(a.c / VEC);
-  const int64_t n_ent = a.n_tok / RATIO;
-  if (n_ent == 0) return hipSuccess;
-  const int max_threads = a.B * n_ent >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
-  int G = 1;
-  while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
-  const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64 * sizeof(float);
-  const double l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
-  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO>), dim3(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B)),
-                     dim3(CT * G), smem, s, static_cast<int>(a.c), a.n_tok, a.pos0, static_cast<const TI*>(a.Ca),
-                     static_cast<const TI*>(a.Za), static_cast<const TI*>(a.Cb), static_cast<const TI*>(a.Zb),
-                     static_cast<const TI*>(a.prev_Cb),
-                     static_cast<const TI*>(a.prev_Zb), a.bias, a.gamma, a.eps, static_cast<TO*>(a.pool),
-                     a.scale_pool, a.n_pool, a.block_table, a.max_blocks, G, a.rope_dims, l2b, a.rope_anchor);
+  PagedBatch jb{};
+  int threads = 64;
+  size_t smem = 0;
+  int64_t gx = 1, gy = 1;
+  for (int q = 0; q < n; ++q) {
+    const CompressPagedArgs& a = jobs[q];
+    const int CT = static_cast<int>(a.c / VEC);
+    const int64_t n_ent = a.n_tok / RATIO;
+    const int max_threads = a.B * n_ent >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
+    int G = 1;
+    while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
+    threads = CT * G > threads ? CT * G : threads;
+    const size_t sm = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float);
+    smem = sm > smem ? sm : smem;
+    gx = n_ent > gx ? n_ent : gx;
+    gy = a.B > gy ? a.B : gy;
+    const double l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
+    jb.j[q] = PagedJobDev{a.Ca, a.Za, a.Cb, a.Zb, a.prev_Cb, a.prev_Zb, a.bias, a.gamma, a.pool, a.scale_pool, a.pos0,
+                          a.block_table, a.n_tok, n_ent, a.B, a.n_pool, a.max_blocks, a.eps, static_cast<int>(a.c), G,
+                          a.rope_dims, l2b, a.rope_anchor,
+                          a.out_dtype == CSA_FP8_E4M3 ? 1 : (a.out_dtype == CSA_MXFP4 ? 2 : 0)};
+  }
+  // + 64 floats: the RMSNorm sums and the fp8 amax
+  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO, MIXED>),
+                     dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
+                     dim3(static_cast<uint32_t>(threads)), smem + 64 * sizeof(float), s, jb);
   return hipGetLastError();
 }
 
+// jobs share ratio and input type; quantized jobs (C4A fp8, MXFP4) may sit
+// beside jobs of one float output type
 template <typename TI>
-hipError_t launch_paged_i(const CompressPagedArgs& a, hipStream_t s) {
-  if (a.out_dtype == CSA_FP8_E4M3) return launch_paged_t<TI, uint8_t, 4>(a, s);   // C4A keys (validated)
-  if (a.out_dtype == CSA_MXFP4) return launch_paged_t<TI, E2M1x2, 4>(a, s);
-  if (a.ratio == 4)
-    return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 4>(a, s) : launch_paged_t<TI, uint16_t, 4>(a, s);
-  return a.out_dtype == CSA_F32 ? launch_paged_t<TI, float, 128>(a, s) : launch_paged_t<TI, uint16_t, 128>(a, s);
+hipError_t launch_paged_i(const CompressPagedArgs* jobs, int n, hipStream_t s) {
+  auto quant = [](int dt) { return dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; };
+  int odt = -1, nq8 = 0, nq4 = 0;
+  for (int q = 0; q < n; ++q) {
+    if (!quant(jobs[q].out_dtype)) odt = jobs[q].out_dtype;
+    nq8 += jobs[q].out_dtype == CSA_FP8_E4M3;
+    nq4 += jobs[q].out_dtype == CSA_MXFP4;
+  }
+  if (odt < 0 && nq4 == 0) return launch_paged_t<TI, uint8_t, 4>(jobs, n, s);
+  if (odt < 0 && nq8 == 0) return launch_paged_t<TI, E2M1x2, 4>(jobs, n, s);
+  if (odt < 0) odt = CSA_BF16;   // fp8 and fp4 jobs only: any float type serves as the third path
+  if (nq8 + nq4 > 0)
+    return odt == CSA_F32 ? launch_paged_t<TI, float, 4, true>(jobs, n, s)
+                          : launch_paged_t<TI, uint16_t, 4, true>(jobs, n, s);
+  if (jobs[0].ratio == 4)
+    return odt == CSA_F32 ? launch_paged_t<TI, float, 4>(jobs, n, s) : launch_paged_t<TI, uint16_t, 4>(jobs, n, s);
+  return odt == CSA_F32 ? launch_paged_t<TI, float, 128>(jobs, n, s) : launch_paged_t<TI, uint16_t, 128>(jobs, n, s);
 }
 
 }  // namespace
 
-hipError_t launch_compress_paged(const CompressPagedArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
-  return a.in_dtype == CSA_F32 ? launch_paged_i<float>(a, s) : launch_paged_i<uint16_t>(a, s);
+hipError_t launch_compress_paged(const CompressPagedArgs* jobs, int n, hipStream_t s) {
+  // jobs with nothing to write are dropped
+  CompressPagedArgs live[kMaxPagedJobs];
+  int m = 0;
+  for (int q = 0; q < n && q < kMaxPagedJobs; ++q)
+    if (jobs[q].B > 0 && jobs[q].n_pool > 0 && jobs[q].n_tok / jobs[q].ratio > 0) live[m++] = jobs[q];
+  if (m == 0) return hipSuccess;
+  return live[0].in_dtype == CSA_F32 ? launch_paged_i<float>(live, m, s) : launch_paged_i<uint16_t>(live, m, s);
 }
 
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s) {

@@ -134,7 +134,7 @@ struct RopeArgs {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 // up to 4 jobs of one ratio and dtype pair, one launch
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s);
-hipError_t launch_compress_paged(const CompressPagedArgs& a, hipStream_t s);
+hipError_t launch_compress_paged(const CompressPagedArgs* jobs, int n, hipStream_t s);   // 1..4 jobs
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);

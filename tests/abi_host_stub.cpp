@@ -8,7 +8,7 @@
 namespace csa {
 hipError_t launch_compress(const CompressArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_compress_batch(const CompressArgs*, int, hipStream_t) { return hipSuccess; }
-hipError_t launch_compress_paged(const CompressPagedArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_compress_paged(const CompressPagedArgs*, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_index(const IndexArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_pool(const IndexPoolArgs&, hipStream_t) { return hipSuccess; }

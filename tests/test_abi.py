@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
                           "hca_attn", "sparse_mqa_attn_ex", "hca_attn_ex", "csa_compress_ex", "csa_rope",
                           "lightning_index_pool", "topk_select_pool", "sparse_mqa_attn_paged", "hca_attn_paged",
                           "lightning_index_paged", "topk_select_paged", "csa_compress_paged",
-                          "csa_compress_paged_chunk", "csa_workspace_bytes",
+                          "csa_compress_paged_chunk", "csa_compress_paged_batch", "csa_workspace_bytes",
                           "csa_last_error", "csa_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -402,6 +402,49 @@ def test_compress_paged_chunk_validation(lib):
     assert c_(B=0, p0=None, tbl=None, cb=None, pc=None) == 0
     # one entry reads prev_Cb only: without Cb the call gets as far as the scale_pool check
     assert c_(n=4, cb=None, od=2) == -1 and "scale_pool is NULL" in _err(lib)
+
+
+def test_compress_paged_batch_layout_and_validation(lib, tmp_path):
+    """csa_compress_paged_job as the binding lays it out matches the C
+    compiler's layout, and the batch entry point validates every job."""
+    import long_context_sparse_compress_amd as csa
+    J = csa._CompressPagedJob
+    if shutil.which("g++"):
+        src = tmp_path / "pj.cpp"
+        src.write_text('#include <cstddef>\n#include <cstdio>\n#include "csa.h"\n'
+                       'int main(){printf("%zu %zu %zu %zu %zu\\n", sizeof(csa_compress_paged_job), '
+                       'offsetof(csa_compress_paged_job, eps), offsetof(csa_compress_paged_job, pool), '
+                       'offsetof(csa_compress_paged_job, max_blocks), offsetof(csa_compress_paged_job, rope_anchor));}\n')
+        exe = tmp_path / "pj"
+        r = subprocess.run(["g++", "-std=c++17", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
+        assert [int(x) for x in got] == [ctypes.sizeof(J), J.eps.offset, J.pool.offset, J.max_blocks.offset,
+                                         J.rope_anchor.offset]
+    lib.csa_compress_paged_batch.argtypes = [ctypes.POINTER(J), ctypes.c_int, ctypes.c_void_p]
+
+    def job(ratio=4, od=1, n=4, cb=None, pc=A, sc=None, c=512):
+        j = J()
+        j.ratio, j.B, j.n_tok, j.c, j.pos0 = ratio, 4, n, c, A
+        j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb = A, A, cb, cb, pc, pc
+        j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype = A, None, 1e-6, 1, od
+        j.pool, j.scale_pool, j.n_pool, j.block_table, j.max_blocks = A, sc, 10, A, 8
+        j.rope_dims, j.rope_base, j.rope_anchor = 0, 10000.0, 0
+        return j
+
+    def call(*jobs, n=None):
+        arr = (J * max(1, len(jobs)))(*jobs)
+        return lib.csa_compress_paged_batch(arr, len(jobs) if n is None else n, None)
+
+    # the pointers are fake: every call below must fail validation
+    assert lib.csa_compress_paged_batch(None, 1, None) == -1 and "NULL" in _err(lib)
+    assert call(job(), n=0) == -1 and "n_jobs" in _err(lib)
+    assert call(job(), n=5) == -1 and "n_jobs" in _err(lib)
+    assert call(job(), job(od=2)) == -1 and "job 1" in _err(lib) and "scale_pool" in _err(lib)
+    assert call(job(), job(ratio=128, pc=None)) == -1 and "share ratio" in _err(lib)
+    assert call(job(od=1), job(od=0, c=128)) == -1 and "share ratio" in _err(lib)   # two float output types
+    assert call(job(n=-1)) == -1 and "job 0" in _err(lib)
 
 
 @pytest.mark.skipif(shutil.which("g++") is None or os.environ.get("CSA_ABI_HOSTCHECK_LIB") is not None,

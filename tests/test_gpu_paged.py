@@ -480,3 +480,58 @@ def test_compress_paged_chunk_write(ratio, c, out, n_tok, rope):
     assert skipped >= 1
     assert written.sum() == 3 * n_ent - skipped
     assert np.array_equal(hp[~written], hb[~written])
+
+
+@pytest.mark.parametrize("kind", ["latent_fp4_key", "latent_fp8_key", "c128a_pair"])
+def test_compress_paged_batch_equals_separate_calls(kind):
+    """csa_compress_paged_batch writes exactly what the separate calls write:
+    the paged decode step's bf16 latent with its MXFP4 (or fp8) indexer key in
+    one launch, each with RoPE, and two C128A streams; sequences at ragged
+    positions, one not at a block start and one with an absent block."""
+    ratio = 128 if kind == "c128a_pair" else 4
+    per = 32 if ratio == 4 else 1
+    pos = [4 * 1000, 128 * 7, 0, 65532, 77, 4 * 4095] if ratio == 4 else [128 * 7, 0, 128 * 8191, 130, 128 * 300]
+    B = len(pos)
+    nblk = [p // 128 + 1 for p in pos]
+    max_blocks = max(nblk) + 1
+    n_pool = sum(nblk) + 2
+    g = np.random.default_rng(zlib.crc32(f"cpb{kind}".encode()))
+    perm = g.permutation(n_pool)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+    table[1, (pos[1] // ratio) // per] = -1
+    streams = ([(512, "bf16", 64), (128, "fp4" if kind == "latent_fp4_key" else "fp8", 64)] if ratio == 4
+               else [(512, "bf16", 64), (256, "bf16", 0)])
+    tbl = dev(table, torch.int32)
+    sp = torch.tensor(pos, dtype=torch.int64, device="cuda")
+    jobs, sep = [], []
+    for si, (c, out, R) in enumerate(streams):
+        inp = synth.compressor_inputs(f"cpb.{kind}.{si}", B, ratio, c, ratio, ratio)   # pos0 > 0: with halo
+        args = dict(Ca=dev(inp["Ca"], BF), Za=dev(inp["Za"], BF), bias=dev(inp["bias"]))
+        if ratio == 4:
+            args.update(prev_Cb=dev(inp["prev_Cb"], BF), prev_Zb=dev(inp["prev_Zb"], BF))
+        if out == "fp8":
+            mk = lambda: (torch.full((n_pool, per, c), 0x33, dtype=torch.uint8, device="cuda"),
+                          torch.full((n_pool, per), 5.0, dtype=torch.float32, device="cuda"))
+        elif out == "fp4":
+            mk = lambda: (torch.full((n_pool, per, c // 2), 0x33, dtype=torch.uint8, device="cuda"),
+                          torch.full((n_pool, per, c // 32), 9, dtype=torch.uint8, device="cuda"))
+        else:
+            shape = (n_pool, per, c) if per > 1 else (n_pool, c)
+            mk = lambda: (torch.full(shape, 3.0, dtype=BF, device="cuda"), None)
+        pa, sa = mk()
+        pb, sb = mk()
+        csa.csa_compress_paged(ratio, args["Ca"], args["Za"], args["bias"], pa, tbl, sp, prev_Cb=args.get("prev_Cb"),
+                               prev_Zb=args.get("prev_Zb"), scale_pool=sa, rope_dims=R, rope_anchor=ratio - 1)
+        sep.append((pa, sa))
+        jobs.append(dict(ratio=ratio, pool=pb, scale_pool=sb, block_table=tbl, pos0=sp, rope_dims=R,
+                         rope_anchor=ratio - 1, **args))
+    csa.csa_compress_paged_batch(jobs)
+    torch.cuda.synchronize()
+    for (pa, sa), j in zip(sep, jobs):
+        assert torch.equal(pa, j["pool"])
+        if sa is not None:
+            assert torch.equal(sa, j["scale_pool"])
