@@ -115,9 +115,11 @@ def time_step(torch, wk, steps, warmup, eager):
 
 
 def time_stages(torch, wk, steps):
-    """Eager pass: events around every stage on the stream its kernels run on (ms)."""
+    """Eager pass: events around every stage on the stream its kernels run on;
+    the median over the steps (ms), so that a one-off host-side stall does not
+    stand for the stage."""
     st = torch.cuda.Stream()
-    acc = {s[0]: 0.0 for s in wk.stages}
+    acc = {s[0]: [] for s in wk.stages}
     with torch.cuda.stream(st):
         for r in range(wk.copies):
             for s in wk.stages:
@@ -133,8 +135,8 @@ def time_stages(torch, wk, steps):
                 evs.append((s[0], a, b))
         torch.cuda.synchronize()
     for n, a, b in evs:
-        acc[n] += a.elapsed_time(b)
-    return {n: v / steps for n, v in acc.items()}
+        acc[n].append(a.elapsed_time(b))
+    return {n: sorted(v)[len(v) // 2] for n, v in acc.items()}
 
 
 def time_kernel(torch, wk, stage, reps=10):
