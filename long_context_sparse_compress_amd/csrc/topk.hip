@@ -745,13 +745,36 @@ __device__ __forceinline__ void fine_slice_keys(const uint16_t* row, int64_t lo,
 }
 #define FKEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
 
+// Per 16-bit half, the smaller of a and b (one packed VALU instruction; the
+// compiler otherwise lowers a min against 1 to two compares per half).
+__device__ __forceinline__ uint32_t min_u16x2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Word w of the histogram (bins 2w, 2w + 1) lives at fine_slot(w): the 32
 // words of coarse bin j = w / 32 are 8 quads, quad q stored at q ^ (j & 7), so
 // lanes reading quad q of consecutive coarse bins hit different banks.
-__device__ __forceinline__ uint32_t fine_slot(uint32_t w) {
-  const uint32_t j = w >> 5;
-  return (j << 5) | ((((w >> 2) & 7u) ^ (j & 7u)) << 2) | (w & 3u);
+__host__ __device__ constexpr uint32_t fine_slot(uint32_t w) {
+  return ((w >> 5) << 5) | ((((w >> 2) & 7u) ^ ((w >> 5) & 7u)) << 2) | (w & 3u);
 }
+// The same for both keys of a packed pair (key a in the low half, b in the
+// high half) at once: the slot is w with bits 2..4 XORed by bits 5..7, so one
+// shift, mask and XOR on the 32-bit pair give fine_slot(a >> 1) in the low
+// half and fine_slot(b >> 1) in the high half.
+__host__ __device__ constexpr uint32_t fine_slot_pair(uint32_t keys) {
+  const uint32_t w = (keys >> 1) & 0x7fff7fffu;
+  return w ^ ((w >> 3) & 0x001c001cu);
+}
+constexpr bool fine_slot_pair_ok() {
+  for (uint32_t a = 0; a < 65536u; a += 3u) {
+    const uint32_t b = (a * 40503u + 17u) & 0xffffu;
+    if (fine_slot_pair(a | (b << 16)) != (fine_slot(a >> 1) | (fine_slot(b >> 1) << 16))) return false;
+  }
+  return true;
+}
+static_assert(fine_slot_pair_ok(), "packed slots agree with fine_slot");
 
 __global__ void __launch_bounds__(kFineThreads)
 topk_fine_record_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k,
@@ -775,34 +798,56 @@ topk_fine_record_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const i
   }
   if (tid == 0) tmp[20] = 0xffffffffu;
   __syncthreads();
+  // A whole chunk (every slice but a row's last) takes its slots and 16-bit
+  // increments from the packed key pairs; a partial one key by key.
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < 2; ++c) {
+    if (valid[c] == 0xffu) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if ((valid[c] >> u) & 1u) {
-        const uint32_t kk = FKEY(c, u);
-        atomicAdd(&hist[fine_slot(kk >> 1)], 1u << (16 * (kk & 1u)));
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sl = fine_slot_pair(kp[c][j]);
+        const uint32_t sh = (kp[c][j] << 4) & 0x00100010u;   // 16 * (key & 1), both halves
+        atomicAdd(&hist[sl & 0xffffu], 1u << (sh & 0xffffu));
+        atomicAdd(&hist[sl >> 16], 1u << (sh >> 16));
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if ((valid[c] >> u) & 1u) {
+          const uint32_t kk = FKEY(c, u);
+          atomicAdd(&hist[fine_slot(kk >> 1)], 1u << (16 * (kk & 1u)));
+        }
+    }
+  }
   __syncthreads();
   // thread t owns coarse bin cb = 1023 - t (fine bins 64 cb .. 64 cb + 63):
   // count its distinct keys and its keys
   const uint32_t cb = static_cast<uint32_t>(kCoarse - 1 - tid);
   const uint4* hq = reinterpret_cast<const uint4*>(hist) + cb * 8;
-  uint32_t nd = 0, ns = 0;
+  // Both 16-bit halves of a word are summed at once: the key counts as plain
+  // 32-bit adds (a half's sum is at most the slice's 16,384 keys, so no carry
+  // crosses into the other half), the non-empty bins as sums of min(count, 1)
+  // per half.
+  uint32_t nd2 = 0, ns2 = 0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const uint4 v = hq[q ^ (cb & 7u)];
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      nd += ((w4[j] & 0xffffu) != 0) + ((w4[j] >> 16) != 0);
-      ns += (w4[j] & 0xffffu) + (w4[j] >> 16);
+      ns2 += w4[j];
+      nd2 += min_u16x2(w4[j], 0x00010001u);
     }
   }
+  const uint32_t nd = (nd2 & 0xffffu) + (nd2 >> 16), ns = (ns2 & 0xffffu) + (ns2 >> 16);
   uint32_t tot;
   const uint32_t ex = block_exclusive_scan(nd | (ns << 16), tmp, &tot);   // both totals <= 16384
   const uint32_t incl = ex + (nd | (ns << 16));
-  if ((incl >> 16) >= static_cast<uint32_t>(k)) atomicMin(&tmp[20], static_cast<uint32_t>(tid));
+  // The keys at or above a coarse bin grow as the bin falls (as tid grows):
+  // the one thread where they first reach k names the slice's cut (a single
+  // writer, where an atomic minimum over every thread past it would
+  // serialize on one LDS word).
+  if ((incl >> 16) >= static_cast<uint32_t>(k) && (ex >> 16) < static_cast<uint32_t>(k)) tmp[20] = static_cast<uint32_t>(tid);
   __syncthreads();
   // the list runs through the coarse bin of the slice's k-th largest key (all
   // of it when the slice has fewer than k keys).  Each wave stages the
@@ -957,18 +1002,24 @@ topk_fine_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const in
   }
   __syncthreads();
   uint32_t gt_run = st[4], eq_run = fine_before[fs];
-  // ordered compaction of the slice (fields gt0 | eq0 | gt1 | eq1 of the two chunks)
-  uint32_t cnt[2][2] = {{0, 0}, {0, 0}};
+  // ordered compaction of the slice (fields gt0 | eq0 | gt1 | eq1 of the two
+  // chunks): bit u of gtm[h] / eqm[h] marks key u of chunk h above / equal to K
+  uint32_t gtm[2], eqm[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h) {
+    gtm[h] = 0;
+    eqm[h] = 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bool vv = (valid[h] >> u) & 1u;
-      cnt[h][0] += vv && FKEY(h, u) > K;
-      cnt[h][1] += vv && FKEY(h, u) == K;
+      gtm[h] |= static_cast<uint32_t>(FKEY(h, u) > K) << u;
+      eqm[h] |= static_cast<uint32_t>(FKEY(h, u) == K) << u;
     }
-  const uint64_t packed = static_cast<uint64_t>(cnt[0][0]) | (static_cast<uint64_t>(cnt[0][1]) << 16) |
-                          (static_cast<uint64_t>(cnt[1][0]) << 32) | (static_cast<uint64_t>(cnt[1][1]) << 48);
+    gtm[h] &= valid[h];
+    eqm[h] &= valid[h];
+  }
+  const uint64_t packed = static_cast<uint64_t>(__popc(gtm[0])) | (static_cast<uint64_t>(__popc(eqm[0])) << 16) |
+                          (static_cast<uint64_t>(__popc(gtm[1])) << 32) |
+                          (static_cast<uint64_t>(__popc(eqm[1])) << 48);
   uint64_t tot;
   const uint64_t ex = block_exclusive_scan_u64(packed, tmp64, &tot);
   const uint32_t tg0 = tot & 0xffffu, te0 = (tot >> 16) & 0xffffu;
@@ -976,19 +1027,19 @@ topk_fine_write_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const in
   for (int h = 0; h < 2; ++h) {
     const uint32_t gb = gt_run + (h ? tg0 + ((ex >> 32) & 0xffffu) : (ex & 0xffffu));
     const uint32_t eb = eq_run + (h ? te0 + ((ex >> 48) & 0xffffu) : ((ex >> 16) & 0xffffu));
+    // the keys taken: every one above K, and the ties in index order while
+    // fewer than rem ties of the row come before them
+    uint32_t take = gtm[h];
+    uint32_t ties = eqm[h];
+    for (uint32_t er = eb; ties != 0 && er < rem; ++er) {
+      take |= ties & (0u - ties);
+      ties &= ties - 1u;
+    }
     uint32_t pos = gb + (eb < rem ? eb : rem);
-    uint32_t er = eb;
     const int32_t i0 = static_cast<int32_t>(lo + 8 * (h * kFineThreads + tid));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (!((valid[h] >> u) & 1u)) continue;
-      const uint32_t kk = FKEY(h, u);
-      if (kk > K) {
-        out[pos++] = i0 + u;
-      } else if (kk == K) {
-        if (er < rem) out[pos++] = i0 + u;
-        ++er;
-      }
+    while (take) {
+      out[pos++] = i0 + static_cast<int32_t>(__builtin_ctz(take));
+      take &= take - 1u;
     }
   }
 }
