@@ -32,16 +32,41 @@ template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int n = 4; };
 template <> struct Vec<uint16_t> { static constexpr int n = 8; };
 
-template <typename T>
-__device__ __forceinline__ void load_vec(const T* p, float* f);
-template <>
-__device__ __forceinline__ void load_vec<float>(const float* p, float* f) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+// VEC consecutive elements of T as raw bytes (16, 8 or 4), converted when used.
+template <int BYTES> struct RawBytes;
+template <> struct RawBytes<16> { using type = uint4; };
+template <> struct RawBytes<8> { using type = uint2; };
+template <> struct RawBytes<4> { using type = uint32_t; };
+template <typename T, int VEC> using Raw = typename RawBytes<VEC * static_cast<int>(sizeof(T))>::type;
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack_raw(const Raw<T, VEC>& r, float* f) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&r);
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) f[v] = __uint_as_float(w[v]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC / 2; ++v) {
+      f[2 * v] = __uint_as_float(w[v] << 16);
+      f[2 * v + 1] = __uint_as_float(w[v] & 0xffff0000u);
+    }
+  }
 }
-template <>
-__device__ __forceinline__ void load_vec<uint16_t>(const uint16_t* p, float* f) {
-  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), f);
+
+// VEC consecutive fp32 values (VEC = 2, 4 or 8).
+template <int VEC>
+__device__ __forceinline__ void load_f32(const float* p, float* f) {
+  if constexpr (VEC % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(p + v);
+      f[v] = q.x; f[v + 1] = q.y; f[v + 2] = q.z; f[v + 3] = q.w;
+    }
+  } else {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    f[0] = q.x; f[1] = q.y;
+  }
 }
 
 template <typename T>
@@ -59,21 +84,26 @@ __device__ __forceinline__ void store_vec<uint16_t>(uint16_t* p, const float* f)
   v.w = pack_bf16x2(f[6], f[7]);
   *reinterpret_cast<uint4*>(p) = v;
 }
-// 8 channels per thread on the bf16 path but 4 on the fp32 output path is
-// never mixed: VEC follows the input type and the output writes VEC values.
+// A thread's VEC output channels (VEC = 2, 4 or 8) in one store.
 template <typename TO, int VEC>
 __device__ __forceinline__ void store_out(TO* p, const float* f) {
   if constexpr (sizeof(TO) == 4) {
+    if constexpr (VEC % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < VEC; i += 4) store_vec<float>(reinterpret_cast<float*>(p) + i, f + i);
+      for (int i = 0; i < VEC; i += 4) store_vec<float>(reinterpret_cast<float*>(p) + i, f + i);
+    } else {
+      *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
+    }
   } else {
     if constexpr (VEC == 8) {
       store_vec<uint16_t>(reinterpret_cast<uint16_t*>(p), f);
-    } else {
+    } else if constexpr (VEC == 4) {
       uint2 v;
       v.x = pack_bf16x2(f[0], f[1]);
       v.y = pack_bf16x2(f[2], f[3]);
       *reinterpret_cast<uint2*>(p) = v;
+    } else {
+      *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(f[0], f[1]);
     }
   }
 }
@@ -115,8 +145,12 @@ __device__ __forceinline__ void online_merge(Online& st, const Online& o) {
 // harmless in-range address and is masked), so all loads of a chunk,
 // including its bias rows, are in flight together.
 // Entry i of sequence b (rows of range z of nz), by a workgroup of at least
-// CT * G threads (threads past that only join the barriers).
-template <typename TI, typename TO, int RATIO, bool SPLIT>
+// CT * G threads (threads past that only join the barriers).  VEC channels a
+// thread (16-byte row loads by default) and chunks of UC rows.  Few
+// workgroups (a decode step) take VEC = 2 and UC = 8 with one row group: each
+// thread then pools all 8 rows of its two channels with no merge, and the
+// work of an entry spreads over four times the threads.
+template <typename TI, typename TO, int RATIO, bool SPLIT, int VEC = Vec<TI>::n, int UC = kChunkRows>
 __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int nz, int64_t n_tok, int c, int64_t pos0,
                                                const TI* __restrict__ Ca, const TI* __restrict__ Za,
                                                const TI* __restrict__ Cb, const TI* __restrict__ Zb,
@@ -126,10 +160,9 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                float* __restrict__ part, int rope_R, double rope_l2b,
                                                int rope_anchor, void* __restrict__ out_scale,
                                                int64_t scale_stride, int64_t out_i = -1) {
-  constexpr int VEC = Vec<TI>::n;
   const int64_t io = out_i >= 0 ? out_i : i;   // where the entry is written (a paged row: 0 from its row)
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
-  constexpr int UC = kChunkRows;
+  static_assert(VEC % 2 == 0 && 32 % VEC == 0 && UC <= ROWS, "whole RoPE pairs, whole MXFP4 blocks");
   const int CT = c / VEC;
   const int tid = threadIdx.x;
   const int ct = tid % CT;
@@ -140,10 +173,11 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 
   float gm[VEC];   // RMSNorm gain, fetched while the rows load
   if (!SPLIT && g == 0) {
+    if (gamma) {
+      load_f32<VEC>(gamma + ch0, gm);
+    } else {
 #pragma unroll
-    for (int v = 0; v < VEC; v += 4) {
-      const float4 q = gamma ? *reinterpret_cast<const float4*>(gamma + ch0 + v) : make_float4(1.f, 1.f, 1.f, 1.f);
-      gm[v] = q.x; gm[v + 1] = q.y; gm[v + 2] = q.z; gm[v + 3] = q.w;
+      for (int v = 0; v < VEC; ++v) gm[v] = 1.f;
     }
   }
 
@@ -168,7 +202,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 
   const int64_t seq = b * n_tok * c;
   for (int r0 = rlo + g; r0 < rhi; r0 += G * UC) {
-    uint4 zl[UC], xl[UC];    // raw 16-byte row slices; converted when consumed
+    Raw<TI, VEC> zl[UC], xl[UC];    // raw row slices; converted when consumed
     float bl[UC][VEC];
     bool have[UC];
 #pragma unroll
@@ -196,14 +230,9 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
         zp = here ? zs + seq + tok * c + ch0 : (pos0 > 0 ? pZb + off : Za + seq + ch0);
         xp = here ? xs + seq + tok * c + ch0 : (pos0 > 0 ? pCb + off : Ca + seq + ch0);
       }
-      zl[u] = *reinterpret_cast<const uint4*>(zp);
-      xl[u] = *reinterpret_cast<const uint4*>(xp);
-      const float* br = bias + static_cast<int64_t>(rr) * c + ch0;
-#pragma unroll
-      for (int v = 0; v < VEC; v += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(br + v);
-        bl[u][v] = q.x; bl[u][v + 1] = q.y; bl[u][v + 2] = q.z; bl[u][v + 3] = q.w;
-      }
+      zl[u] = *reinterpret_cast<const Raw<TI, VEC>*>(zp);
+      xl[u] = *reinterpret_cast<const Raw<TI, VEC>*>(xp);
+      load_f32<VEC>(bias + static_cast<int64_t>(rr) * c + ch0, bl[u]);
       have[u] = in && ok;
     }
     // logits of the chunk in the log2 domain, and their per-channel max
@@ -214,7 +243,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
       float zf[VEC];
-      load_vec<TI>(reinterpret_cast<const TI*>(&zl[u]), zf);
+      unpack_raw<TI, VEC>(zl[u], zf);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         lg[u][v] = have[u] ? (zf[v] + bl[u][v]) * kLog2e : -INFINITY;
@@ -234,7 +263,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
       float xf[VEC];
-      load_vec<TI>(reinterpret_cast<const TI*>(&xl[u]), xf);
+      unpack_raw<TI, VEC>(xl[u], xf);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         const float p = have[u] ? exp2_le0(lg[u][v] - st[v].m) : 0.f;
@@ -332,7 +361,8 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
     for (int v = 0; v < VEC; ++v) word |= f32_to_e2m1(ldexpf(o[v], -E)) << (4 * v);
     uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (b * out_stride + io * c + ch0) / 2;
     if constexpr (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = word;
-    else *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(word);
+    else if constexpr (VEC == 4) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(word);
+    else *dst = static_cast<uint8_t>(word);
     if (ct % (32 / VEC) == 0)
       static_cast<uint8_t*>(out_scale)[(b * scale_stride + io) * (c / 32) + ch0 / 32] = static_cast<uint8_t>(E + 127);
     return;
@@ -368,14 +398,13 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
     for (int w = 0; w < nw; ++w) amax = fmaxf(amax, red_max[w]);
     if (g != 0) return;
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
-    uint32_t word[VEC / 4];
+    uint32_t word[(VEC + 3) / 4] = {};
 #pragma unroll
-    for (int v = 0; v < VEC; v += 4)
-      word[v / 4] = f32_to_e4m3(o[v] / scale) | (f32_to_e4m3(o[v + 1] / scale) << 8) |
-                    (f32_to_e4m3(o[v + 2] / scale) << 16) | (f32_to_e4m3(o[v + 3] / scale) << 24);
+    for (int v = 0; v < VEC; ++v) word[v / 4] |= f32_to_e4m3(o[v] / scale) << (8 * (v % 4));
     uint8_t* dst = reinterpret_cast<uint8_t*>(out + b * out_stride + io * c + ch0);
     if constexpr (VEC == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
-    else *reinterpret_cast<uint32_t*>(dst) = word[0];
+    else if constexpr (VEC == 4) *reinterpret_cast<uint32_t*>(dst) = word[0];
+    else *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(word[0]);
     if (ct == 0) static_cast<float*>(out_scale)[b * scale_stride + io] = scale;
     return;
   }
@@ -402,7 +431,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 // groups), C128A ones up to 1024; the bound sets the register budget.
 template <int RATIO> constexpr int kCompressThreads = RATIO == 4 ? 512 : 1024;
 
-template <typename TI, typename TO, int RATIO, bool SPLIT>
+template <typename TI, typename TO, int RATIO, bool SPLIT, int VEC = Vec<TI>::n, int UC = kChunkRows>
 __global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const TI* __restrict__ Ca, const TI* __restrict__ Za,
@@ -411,7 +440,7 @@ compress_kernel(int64_t n_tok, int c, int64_t pos0,
                 const float* __restrict__ bias, const float* __restrict__ gamma, float eps,
                 TO* __restrict__ out, int64_t out_stride, int G, float* __restrict__ part, int rope_R,
                 double rope_l2b, int rope_anchor, void* __restrict__ out_scale, int64_t scale_stride) {
-  compress_entry<TI, TO, RATIO, SPLIT>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
+  compress_entry<TI, TO, RATIO, SPLIT, VEC, UC>(blockIdx.x, blockIdx.y, static_cast<int>(blockIdx.z),
                                        static_cast<int>(gridDim.z), n_tok, c, pos0, Ca, Za, Cb, Zb, pCb, pZb, bias,
                                        gamma, eps, out, out_stride, G, part, rope_R, rope_l2b, rope_anchor,
                                        out_scale, scale_stride);
@@ -447,7 +476,7 @@ struct PagedBatch {
   PagedJobDev j[kMaxPagedJobs];
 };
 
-template <typename TI, typename TO, int RATIO>
+template <typename TI, typename TO, int RATIO, int VEC, int UC>
 __device__ __forceinline__ void paged_entry(const PagedJobDev& J) {
   constexpr int SH = RATIO == 4 ? 5 : 0;   // log2 entries per block
   const int64_t b = blockIdx.y;
@@ -466,7 +495,7 @@ __device__ __forceinline__ void paged_entry(const PagedJobDev& J) {
   void* sdst = !J.scale_pool ? nullptr
                : kFp4        ? static_cast<void*>(static_cast<uint8_t*>(J.scale_pool) + row * (c / 32))
                              : static_cast<void*>(static_cast<float*>(J.scale_pool) + row);
-  compress_entry<TI, TO, RATIO, false>(i, b, 0, 1, J.n_tok, c, p0, static_cast<const TI*>(J.Ca),
+  compress_entry<TI, TO, RATIO, false, VEC, UC>(i, b, 0, 1, J.n_tok, c, p0, static_cast<const TI*>(J.Ca),
                                        static_cast<const TI*>(J.Za), static_cast<const TI*>(J.Cb),
                                        static_cast<const TI*>(J.Zb), static_cast<const TI*>(J.pCb),
                                        static_cast<const TI*>(J.pZb), J.bias, J.gamma, J.eps, dst, 0, J.G, nullptr,
@@ -476,16 +505,16 @@ __device__ __forceinline__ void paged_entry(const PagedJobDev& J) {
 // Up to four writes into pages in one launch (blockIdx.z picks the job; the
 // paged decode step's bf16 latent and quantized indexer key together).
 // MIXED: jobs writing fp8 or MXFP4 codes sit beside jobs of the float type TO.
-template <typename TI, typename TO, int RATIO, bool MIXED = false>
+template <typename TI, typename TO, int RATIO, bool MIXED = false, int VEC = Vec<TI>::n, int UC = kChunkRows>
 __global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_paged_kernel(PagedBatch jb) {
   const PagedJobDev& J = jb.j[blockIdx.z];
   if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
   if constexpr (MIXED) {
-    if (J.qfmt == 1) return paged_entry<TI, uint8_t, RATIO>(J);
-    if (J.qfmt == 2) return paged_entry<TI, E2M1x2, RATIO>(J);
+    if (J.qfmt == 1) return paged_entry<TI, uint8_t, RATIO, VEC, UC>(J);
+    if (J.qfmt == 2) return paged_entry<TI, E2M1x2, RATIO, VEC, UC>(J);
   }
-  paged_entry<TI, TO, RATIO>(J);
+  paged_entry<TI, TO, RATIO, VEC, UC>(J);
 }
 
 // Several compressions of one ratio and dtype pair in one launch (blockIdx.z
@@ -513,13 +542,13 @@ struct CompressBatch {
 // MIXED: some jobs write fp8 codes (quantize-on-write; their out_scale is
 // set) and the others TO -- the CSA layer's bf16 latent and fp8 indexer keys
 // in one launch.  The choice is per workgroup (one job each).
-template <typename TI, typename TO, int RATIO, bool MIXED = false>
+template <typename TI, typename TO, int RATIO, bool MIXED = false, int VEC = Vec<TI>::n, int UC = kChunkRows>
 __global__ void __launch_bounds__(kCompressThreads<RATIO>)
 compress_batch_kernel(CompressBatch jb) {
   const CompressJobDev& J = jb.j[blockIdx.z];
   if (static_cast<int64_t>(blockIdx.x) >= J.n_ent || static_cast<int64_t>(blockIdx.y) >= J.B) return;
   if (MIXED && J.qfmt == 1) {
-    compress_entry<TI, uint8_t, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+    compress_entry<TI, uint8_t, RATIO, false, VEC, UC>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
                                               static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                               static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
                                               static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias,
@@ -529,7 +558,7 @@ compress_batch_kernel(CompressBatch jb) {
     return;
   }
   if (MIXED && J.qfmt == 2) {
-    compress_entry<TI, E2M1x2, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+    compress_entry<TI, E2M1x2, RATIO, false, VEC, UC>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
                                              static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                              static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
                                              static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias,
@@ -538,7 +567,7 @@ compress_batch_kernel(CompressBatch jb) {
                                              J.scale_stride);
     return;
   }
-  compress_entry<TI, TO, RATIO, false>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
+  compress_entry<TI, TO, RATIO, false, VEC, UC>(blockIdx.x, blockIdx.y, 0, 1, J.n_tok, J.c, J.pos0,
                                        static_cast<const TI*>(J.Ca), static_cast<const TI*>(J.Za),
                                        static_cast<const TI*>(J.Cb), static_cast<const TI*>(J.Zb),
                                        static_cast<const TI*>(J.pCb), static_cast<const TI*>(J.pZb), J.bias, J.gamma,
@@ -602,9 +631,18 @@ compress_merge_kernel(int64_t n_ent, int c, int P, const float* __restrict__ par
 
 double rope_log2_base(const CompressArgs& a) { return a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0; }
 
-template <typename TI, typename TO, int RATIO>
-hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
-  constexpr int VEC = Vec<TI>::n;
+// A C4A launch of fewer workgroups than this (a decode step) spreads each
+// entry over c / 2 threads, each pooling all 8 rows of two channels.
+constexpr int64_t kNarrowWgs = 256;
+constexpr int kNarrowVec = 2;
+// Each job takes the layout its own call would, so a batch computes every
+// job exactly as the separate calls do (jobs of both kinds go out as two
+// launches).
+template <typename Args>
+bool narrow_job(const Args& a) { return a.ratio == 4 && (a.n_tok / a.ratio) * a.B < kNarrowWgs; }
+
+template <typename TI, typename TO, int RATIO, int VEC = Vec<TI>::n, int UC = kChunkRows>
+hipError_t launch_vt(const CompressArgs& a, hipStream_t s) {
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   const int CT = static_cast<int>(a.c / VEC);
   const int64_t n_ent = a.n_tok / RATIO;
@@ -615,12 +653,11 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
   // Row groups: enough that a thread holds at most one chunk of UC rows when
   // the workgroups are few (latency), at most 256 threads per workgroup when
   // they are many; never more groups than rows / UC.
-  constexpr int UC = kChunkRows;
   const int rows = split ? ROWS / P : ROWS;
   const int max_threads = (split ? n_wg * P : n_wg) >= 1024 ? 256 : 1024;
   int G = 1;
   while (G * 2 * CT <= max_threads && G * 2 * UC <= rows) G *= 2;
-  const int threads = CT * G;
+  const int threads = (CT * G + 63) / 64 * 64;   // whole waves: the wave reductions use every lane
   // + 64 floats: the RMSNorm sums (red[0..15]) and the fp8 amax (red_max = red + 32)
   const size_t smem = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float) + 64 * sizeof(float);
   const auto* Ca = static_cast<const TI*>(a.Ca);
@@ -644,16 +681,23 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
     }
   }
   const dim3 grid(static_cast<uint32_t>(n_ent), static_cast<uint32_t>(a.B), 1);
-  hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, false>), grid, dim3(threads), smem, s, a.n_tok,
+  hipLaunchKernelGGL((compress_kernel<TI, TO, RATIO, false, VEC, UC>), grid, dim3(threads), smem, s, a.n_tok,
                      static_cast<int>(a.c), a.pos0, Ca, Za, Cb, Zb, pCb, pZb, a.bias, a.gamma, a.eps,
                      static_cast<TO*>(a.out), stride, G, nullptr, a.rope_dims, rope_log2_base(a), a.rope_anchor,
                      a.out_scale, stride / a.c);
   return hipGetLastError();
 }
 
-template <typename TI, typename TO, int RATIO, bool MIXED = false>
-hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
-  constexpr int VEC = Vec<TI>::n;
+template <typename TI, typename TO, int RATIO>
+hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
+  if constexpr (RATIO == 4) {
+    if (narrow_job(a)) return launch_vt<TI, TO, RATIO, kNarrowVec, 8>(a, s);
+  }
+  return launch_vt<TI, TO, RATIO>(a, s);
+}
+
+template <typename TI, typename TO, int RATIO, bool MIXED, int VEC, int UC>
+hipError_t launch_batch_vt(const CompressArgs* jobs, int n, hipStream_t s) {
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   CompressBatch jb{};
   int threads = 64;
@@ -665,7 +709,7 @@ hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
     const int64_t n_ent = a.n_tok / RATIO;
     const int max_threads = n_ent * a.B >= 1024 ? 256 : 1024;
     int G = 1;
-    while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
+    while (G * 2 * CT <= max_threads && G * 2 * UC <= ROWS) G *= 2;
     threads = CT * G > threads ? CT * G : threads;
     const size_t sm = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float);
     smem = sm > smem ? sm : smem;
@@ -677,10 +721,27 @@ hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
                              (a.out_batch_stride ? a.out_batch_stride : n_ent * a.c) / a.c,
                              a.out_dtype == CSA_FP8_E4M3 ? 1 : (a.out_dtype == CSA_MXFP4 ? 2 : 0)};
   }
-  hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO, MIXED>),
+  threads = (threads + 63) / 64 * 64;   // whole waves: the wave reductions use every lane
+  hipLaunchKernelGGL((compress_batch_kernel<TI, TO, RATIO, MIXED, VEC, UC>),
                      dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
                      dim3(static_cast<uint32_t>(threads)), smem + 64 * sizeof(float), s, jb);
   return hipGetLastError();
+}
+
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
+hipError_t launch_batch_t(const CompressArgs* jobs, int n, hipStream_t s) {
+  CompressArgs nar[kMaxBatchJobs], wide[kMaxBatchJobs];
+  int nn = 0, nw = 0;
+  for (int q = 0; q < n; ++q) {
+    if (narrow_job(jobs[q])) nar[nn++] = jobs[q];
+    else wide[nw++] = jobs[q];
+  }
+  hipError_t e = hipSuccess;
+  if constexpr (RATIO == 4) {
+    if (nn) e = launch_batch_vt<TI, TO, RATIO, MIXED, kNarrowVec, 8>(nar, nn, s);
+  }
+  if (e == hipSuccess && nw) e = launch_batch_vt<TI, TO, RATIO, MIXED, Vec<TI>::n, kChunkRows>(wide, nw, s);
+  return e;
 }
 
 template <typename TI, typename TO>
@@ -708,9 +769,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 
 namespace {
 
-template <typename TI, typename TO, int RATIO, bool MIXED = false>
-hipError_t launch_paged_t(const CompressPagedArgs* jobs, int n, hipStream_t s) {
-  constexpr int VEC = Vec<TI>::n;
+template <typename TI, typename TO, int RATIO, bool MIXED, int VEC, int UC>
+hipError_t launch_paged_vt(const CompressPagedArgs* jobs, int n, hipStream_t s) {
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   PagedBatch jb{};
   int threads = 64;
@@ -722,7 +782,7 @@ hipError_t launch_paged_t(const CompressPagedArgs* jobs, int n, hipStream_t s) {
     const int64_t n_ent = a.n_tok / RATIO;
     const int max_threads = a.B * n_ent >= 1024 ? 256 : (RATIO == 4 ? 512 : 1024);
     int G = 1;
-    while (G * 2 * CT <= max_threads && G * 2 * kChunkRows <= ROWS) G *= 2;
+    while (G * 2 * CT <= max_threads && G * 2 * UC <= ROWS) G *= 2;
     threads = CT * G > threads ? CT * G : threads;
     const size_t sm = (G > 1 ? static_cast<size_t>(G / 2) * 3 * a.c : 0) * sizeof(float);
     smem = sm > smem ? sm : smem;
@@ -735,10 +795,27 @@ hipError_t launch_paged_t(const CompressPagedArgs* jobs, int n, hipStream_t s) {
                           a.out_dtype == CSA_FP8_E4M3 ? 1 : (a.out_dtype == CSA_MXFP4 ? 2 : 0)};
   }
   // + 64 floats: the RMSNorm sums and the fp8 amax
-  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO, MIXED>),
+  threads = (threads + 63) / 64 * 64;   // whole waves: the wave reductions use every lane
+  hipLaunchKernelGGL((compress_paged_kernel<TI, TO, RATIO, MIXED, VEC, UC>),
                      dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(n)),
                      dim3(static_cast<uint32_t>(threads)), smem + 64 * sizeof(float), s, jb);
   return hipGetLastError();
+}
+
+template <typename TI, typename TO, int RATIO, bool MIXED = false>
+hipError_t launch_paged_t(const CompressPagedArgs* jobs, int n, hipStream_t s) {
+  CompressPagedArgs nar[kMaxPagedJobs], wide[kMaxPagedJobs];
+  int nn = 0, nw = 0;
+  for (int q = 0; q < n; ++q) {
+    if (narrow_job(jobs[q])) nar[nn++] = jobs[q];
+    else wide[nw++] = jobs[q];
+  }
+  hipError_t e = hipSuccess;
+  if constexpr (RATIO == 4) {
+    if (nn) e = launch_paged_vt<TI, TO, RATIO, MIXED, kNarrowVec, 8>(nar, nn, s);
+  }
+  if (e == hipSuccess && nw) e = launch_paged_vt<TI, TO, RATIO, MIXED, Vec<TI>::n, kChunkRows>(wide, nw, s);
+  return e;
 }
 
 // jobs share ratio and input type; quantized jobs (C4A fp8, MXFP4) may sit

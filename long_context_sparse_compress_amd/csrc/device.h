@@ -51,10 +51,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 __device__ __forceinline__ float fast_exp2(float x) { return exp2f(x); }
 
 // Sum / max over the 64 lanes of a wave.
+// On the DPP cross-lane paths (no LDS round trip): shifts inside each row of
+// 16 lanes, then the row results carried across rows by the row broadcasts
+// of lanes 15 and 31, so lane 63 ends with the whole wave's; every lane gets
+// lane 63's value.  All 64 lanes must be active.
+#define CSA_FDPP(old, x, ctrl, rmask, bound0) \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), ctrl, rmask, 0xf, bound0))
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += CSA_FDPP(0.f, v, 0x111, 0xf, true);   // row_shr:1
+  v += CSA_FDPP(0.f, v, 0x112, 0xf, true);   // row_shr:2
+  v += CSA_FDPP(0.f, v, 0x114, 0xf, true);   // row_shr:4
+  v += CSA_FDPP(0.f, v, 0x118, 0xf, true);   // row_shr:8
+  v += CSA_FDPP(0.f, v, 0x142, 0xa, false);  // row_bcast:15 into rows 1 and 3
+  v += CSA_FDPP(0.f, v, 0x143, 0xc, false);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
@@ -62,10 +72,15 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x111, 0xf, false));
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x112, 0xf, false));
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x114, 0xf, false));
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x118, 0xf, false));
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x142, 0xa, false));
+  v = fmaxf(v, CSA_FDPP(-INFINITY, v, 0x143, 0xc, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef CSA_FDPP
 
 // Cross-lane read with a precomputed byte address (lane index * 4):
 // ds_bpermute without the per-call lane arithmetic of __shfl*.
