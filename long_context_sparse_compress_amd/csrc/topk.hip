@@ -373,6 +373,40 @@ topk_lds_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
   emit_range<KT>(lo, hi, K, rem, gtb, eqb, out, [&](int64_t i) { return keys[i]; }, prow, n_ent);
 }
 
+// Packed 16-bit integer operations on both halves of a 32-bit word at once,
+// one VALU instruction each (the compiler otherwise splits such work into
+// per-half compares and selects).
+__device__ __forceinline__ uint32_t min_u16x2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t add_u16x2(uint32_t a, uint32_t b) {   // modulo 2^16 per half
+  uint32_t r;
+  asm("v_pk_add_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t shr_u16x2(uint32_t a, uint32_t sh2) {   // sh2: the shift in both halves
+  uint32_t r;
+  asm("v_pk_lshrrev_b16 %0, %1, %2" : "=v"(r) : "v"(sh2), "v"(a));
+  return r;
+}
+
+// Order-preserving keys of two stored bf16 scores at once: 0x8000 + m for a
+// non-negative half of magnitude bits m, 0x8000 - m for a negative one (so
+// -0.0 and +0.0 share 0x8000).  The same order as key_of, one above it on
+// negative scores.
+__device__ __forceinline__ uint32_t key_pair(uint32_t w) {
+  const uint32_t sg = (w >> 15) & 0x00010001u;               // sign of each half
+  const uint32_t t = (w & 0x7fff7fffu) ^ (sg * 0xffffu);     // m, or 0xffff - m
+  return add_u16x2(t, sg + 0x80008000u);                     // + 0x8000 (+ 1 for a negative half)
+}
+
 // ------------------------------------------------------------ register path
 // bf16 rows of up to 1024 * 8 * CPT keys: thread t holds keys
 // 8 CPT t .. 8 CPT t + 8 CPT - 1 (CPT 16-byte chunks) in registers for the
@@ -419,7 +453,9 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
   uint32_t kp[CPT][4];
   uint32_t valid[CPT];
 #define KEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
-  uint32_t kmin = 0xffffu, kmax = 0u;
+  // keys and their range two at a time; a key past V takes no part (its
+  // halves enter the minimum as 0xffff and the maximum as 0)
+  uint32_t mn2 = 0xffffffffu, mx2 = 0u;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int64_t i0 = i00 + 8 * c;
@@ -429,14 +465,24 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
     const int64_t nv = V - i0;
     valid[c] = nv >= 8 ? 0xffu : (nv > 0 ? (1u << nv) - 1u : 0u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = key_of(static_cast<uint16_t>(w[j] & 0xffffu));
-      const uint32_t hi = key_of(static_cast<uint16_t>(w[j] >> 16));
-      kp[c][j] = lo | (hi << 16);
-      if ((valid[c] >> (2 * j)) & 1u) { kmin = min(kmin, lo); kmax = max(kmax, lo); }
-      if ((valid[c] >> (2 * j + 1)) & 1u) { kmin = min(kmin, hi); kmax = max(kmax, hi); }
+    for (int j = 0; j < 4; ++j) kp[c][j] = key_pair(w[j]);
+    if (valid[c] == 0xffu) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mn2 = min_u16x2(mn2, kp[c][j]);
+        mx2 = max_u16x2(mx2, kp[c][j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t vm = (valid[c] >> (2 * j)) & 3u;
+        const uint32_t keep = ((vm & 1u) ? 0xffffu : 0u) | ((vm & 2u) ? 0xffff0000u : 0u);
+        mn2 = min_u16x2(mn2, kp[c][j] | ~keep);
+        mx2 = max_u16x2(mx2, kp[c][j] & keep);
+      }
     }
   }
+  uint32_t kmin = min(mn2 & 0xffffu, mn2 >> 16), kmax = max(mx2 & 0xffffu, mx2 >> 16);
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if ((tid & 63) == 0) {
@@ -459,12 +505,26 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
         kp[c][j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2i16, kp[c][j]) - m2);
   }
 
-  // pass 1: bin (key - min) >> sh
+  // pass 1: bin (key - min) >> sh, both keys of a register shifted at once
+  // in a whole chunk
+  {
+    const uint32_t sh2 = static_cast<uint32_t>(sh) * 0x10001u;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+    for (int c = 0; c < CPT; ++c) {
+      if (valid[c] == 0xffu) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if ((valid[c] >> u) & 1u) atomicAdd(&bins[KEY(c, u) >> sh], 1u);
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t b2 = shr_u16x2(kp[c][j], sh2);
+          atomicAdd(&bins[b2 & 0xffffu], 1u);
+          atomicAdd(&bins[b2 >> 16], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if ((valid[c] >> u) & 1u) atomicAdd(&bins[KEY(c, u) >> sh], 1u);
+      }
+    }
+  }
   __syncthreads();
   // thread t owns bins 8t .. 8t+7; find the bin holding the k-th largest key
   constexpr int per = kRangeBins / NT;
@@ -523,32 +583,31 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
     rem = tmp[23];
   }
 
-  // ordered compaction: this thread's keys above K, then the first rem equal to K
-  uint32_t gt = 0, eq = 0;
+  // ordered compaction: this thread's keys above K, then the first rem equal
+  // to K.  Bit 8c + u of gtm / eqm: key u of chunk c is above / equal to K.
+  uint64_t gtm = 0, eqm = 0;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+  for (int c = 0; c < CPT; ++c) {
+    uint32_t g8 = 0, e8 = 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bool vv = (valid[c] >> u) & 1u;
-      gt += vv && KEY(c, u) > K;
-      eq += vv && KEY(c, u) == K;
+      g8 |= static_cast<uint32_t>(KEY(c, u) > K) << u;
+      e8 |= static_cast<uint32_t>(KEY(c, u) == K) << u;
     }
+    gtm |= static_cast<uint64_t>(g8 & valid[c]) << (8 * c);
+    eqm |= static_cast<uint64_t>(e8 & valid[c]) << (8 * c);
+  }
+  const uint32_t gt = static_cast<uint32_t>(__popcll(gtm)), eq = static_cast<uint32_t>(__popcll(eqm));
   uint32_t tot;
   const uint32_t ex = block_exclusive_scan(gt | (eq << 16), tmp, &tot);
-  // which of this thread's keys are taken (bit 8c + u), then one store per
-  // taken key in index order
-  uint64_t take = 0;
-  uint32_t er = ex >> 16;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool vv = (valid[c] >> u) & 1u;
-      const uint32_t kk = KEY(c, u);
-      const bool tie = vv && kk == K;
-      if ((vv && kk > K) || (tie && er < rem)) take |= uint64_t(1) << (8 * c + u);
-      er += tie;
-    }
+  // which of this thread's keys are taken (bit 8c + u): every one above K and
+  // its ties in index order while fewer than rem ties come before them; then
+  // one store per taken key in index order
+  uint64_t take = gtm;
+  for (uint32_t er = ex >> 16; eqm != 0 && er < rem; ++er) {
+    take |= eqm & (0ull - eqm);
+    eqm &= eqm - 1ull;
+  }
   uint32_t pos = (ex & 0xffffu) + min(ex >> 16, rem);
   while (take) {
     out[pos++] = pool_map(prow, n_ent, i00 + __builtin_ctzll(take));
@@ -744,14 +803,6 @@ __device__ __forceinline__ void fine_slice_keys(const uint16_t* row, int64_t lo,
   }
 }
 #define FKEY(c, u) ((kp[c][(u) >> 1] >> (16 * ((u) & 1))) & 0xffffu)
-
-// Per 16-bit half, the smaller of a and b (one packed VALU instruction; the
-// compiler otherwise lowers a min against 1 to two compares per half).
-__device__ __forceinline__ uint32_t min_u16x2(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
 
 // Word w of the histogram (bins 2w, 2w + 1) lives at fine_slot(w): the 32
 // words of coarse bin j = w / 32 are 8 quads, quad q stored at q ^ (j & 7), so
