@@ -12,9 +12,10 @@ The five configurations of the method (one GPU):
 
   csa_1m_decode   8 sequences at 1,048,576 tokens of context (Pro): the C4A
                   compressor writes the new block's 512-d latent (bf16) and its
-                  128-d key quantized on write to MXFP4 (one launch); the MXFP4
-                  indexer over 262,144 keys; top-1024; sparse MQA over 1,024
-                  entries + 128 window rows
+                  128-d key quantized on write to MXFP4 inside the MXFP4
+                  indexer's launch (lightning_index_compressed), which scores
+                  all 262,144 keys; top-1024; sparse MQA over 1,024 entries +
+                  128 window rows
   csa_decode      32 sequences at 65,536 context: C4A compress (latent + bf16
                   key), the bf16 indexer over 16,384 keys, top-512, sparse MQA
   csa_prefill     a 4,096-token chunk after 131,072 tokens: C4A compress of the
@@ -120,8 +121,10 @@ def _c4_decode_bytes(B, c, key_bytes=None):
     return B * (16 * c * 2 + out) + 8 * c * 4
 
 
-def csa_1m_decode(torch, csa, synth, copies=4):
-    """Config 5: CSA decode at 1,048,576 context, batch 8, MXFP4 indexer, top-1024."""
+def csa_1m_decode(torch, csa, synth, copies=4, fuse=True):
+    """Config 5: CSA decode at 1,048,576 context, batch 8, MXFP4 indexer, top-1024.
+    fuse: the compressor writes run inside the indexer's launch
+    (lightning_index_compressed); else a compressor launch, then the indexer."""
     bf = torch.bfloat16
     dn = synth.device_normal
     B, N, k, t = 8, 262144, 1024, 1048575
@@ -146,18 +149,29 @@ def csa_1m_decode(torch, csa, synth, copies=4):
     out = torch.empty_like(q)
     ws_t = _ws(torch, csa, csa.OP_TOPK, B, 1, N, k)
     ws_a = _ws(torch, csa, csa.OP_SPARSE_ATTN, B, 1, N, k)
-    wk = Work("csa_1m_decode", "csa_1m_decode: CSA decode at 1,048,576 context (Pro): C4A compress (latent bf16 + "
-              "key quantized on write to MXFP4), MXFP4 indexer over 262,144 keys, top-1024, sparse MQA",
+    wk = Work("csa_1m_decode" if fuse else "csa_1m_decode_separate",
+              "csa_1m_decode: CSA decode at 1,048,576 context (Pro): C4A compress (latent bf16 + key quantized on "
+              "write to MXFP4) " + ("inside the MXFP4 indexer's launch" if fuse else "in its own launch, then the "
+                                   "MXFP4 indexer") + " over 262,144 keys, top-1024, sparse MQA",
               B, copies, dict(batch=B, context=t + 1, c4a_entries=N, topk=k, window=128, heads=64, head_dim=512,
                               index_heads=64, index_dim=128, index_qk="mxfp4", scores="bf16",
                               cache_copies_rotated=copies),
               "lightning_index")
-    wk.add("compress_c4a_kv_keys", lambda r: csa.csa_compress_batch([
-        _c4_job(c4, b4, pos4, kv[r], N - 1), _c4_job(c4k, b4k, pos4, kp[r], N - 1, ks[r])]),
-        _c4_decode_bytes(B, 512) + _c4_decode_bytes(B, 128, 64 + 4), 0, "hbm")
-    wk.add("lightning_index", lambda r: csa.lightning_index(qp, w, kp[r], q_pos0=t, qk_dtype=csa.MXFP4, q_scale=qs,
-                                                            k_scale=ks[r], scores=scores, N=N),
-           B * N * 68 + B * 64 * 68 + B * 64 * 4 + B * N * 2, B * N * 64 * 128 * 2, "hbm")
+    def jobs(r):
+        return [_c4_job(c4, b4, pos4, kv[r], N - 1), _c4_job(c4k, b4k, pos4, kp[r], N - 1, ks[r])]
+
+    c_bytes = _c4_decode_bytes(B, 512) + _c4_decode_bytes(B, 128, 64 + 4)
+    i_bytes, i_flops = B * N * 68 + B * 64 * 68 + B * 64 * 4 + B * N * 2, B * N * 64 * 128 * 2
+    if fuse:
+        wk.dominant = "compress_index"
+        wk.add("compress_index", lambda r: csa.lightning_index_compressed(
+            qp, w, kp[r], jobs(r), e_new=N - 1, q_pos0=t, qk_dtype=csa.MXFP4, q_scale=qs, k_scale=ks[r],
+            scores=scores, N=N), c_bytes + i_bytes, i_flops, "hbm")
+    else:
+        wk.add("compress_c4a_kv_keys", lambda r: csa.csa_compress_batch(jobs(r)), c_bytes, 0, "hbm")
+        wk.add("lightning_index", lambda r: csa.lightning_index(qp, w, kp[r], q_pos0=t, qk_dtype=csa.MXFP4,
+                                                                q_scale=qs, k_scale=ks[r], scores=scores, N=N),
+               i_bytes, i_flops, "hbm")
     wk.add("topk_select", lambda r: csa.topk_select(scores, k, q_pos0=t, idx=idx, workspace=ws_t),
            B * N * 2 + B * k * 4, 0, "hbm")
     wk.add("sparse_mqa_attn", lambda r: csa.sparse_mqa_attn(q, kv[r], idx, raw, q_pos0=t, raw_pos0=raw0, out=out,
@@ -685,6 +699,12 @@ def csa_paged_decode(torch, csa, synth, copies=1):
     return wk
 
 
+def csa_1m_decode_separate(torch, csa, synth, copies=4):
+    """The 1M-context Pro decode with the compressor in a launch of its own (A/B
+    against the headline's single launch)."""
+    return csa_1m_decode(torch, csa, synth, copies=copies, fuse=False)
+
+
 def csa_paged_1m_decode(torch, csa, synth, copies=2):
     """The 1M-context Pro decode over the heterogeneous cache: 8 sequences at ragged
     positions near 1,048,576, their C4A latents (bf16) and MXFP4 keys in shuffled
@@ -795,5 +815,6 @@ def hbm_read(torch, csa, synth, copies=4):
 
 EXTRAS = {"csa_hca_decode": csa_hca_decode, "c128a_1m": c128a_1m, "csa_reindex_decode": csa_reindex_decode,
           "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode,
-          "csa_paged_1m_decode": csa_paged_1m_decode, "hbm_copy": hbm_copy,
+          "csa_paged_1m_decode": csa_paged_1m_decode, "csa_1m_decode_separate": csa_1m_decode_separate,
+          "hbm_copy": hbm_copy,
           "hbm_read": hbm_read}

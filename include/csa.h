@@ -6,6 +6,7 @@
  *
  *   csa_compress      C4A / C128A KV compressor
  *   csa_compress_batch  several compressor calls of one ratio in one launch
+ *   lightning_index_compressed  a decode step's compressor writes and the indexer in one call
  *   lightning_index   indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
  *   topk_select       causal Top-k over the indexer scores
  *   sparse_mqa_attn   shared-KV MQA over the Top-k entries plus the window
@@ -250,6 +251,38 @@ int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio,
                     const void* q, const void* q_scale, const float* w,
                     const void* k, const void* k_scale, int qk_dtype,
                     void* scores, int score_dtype, void* stream);
+
+/*
+ * lightning_index_compressed -- a decode step's compressor writes, then the
+ * lightning indexer, as one call.
+ *
+ * The same results as csa_compress_batch(jobs, n_jobs, stream) followed by
+ * lightning_index(...) on the same stream: the step's new C4A entry
+ * ("DeepSeek V4 结构速览", C4A Compressor: at decode the current block is
+ * pooled with the previous one into the latest entry) is written into the
+ * caches -- its 512-d latent and its indexer key, quantized on write -- and
+ * the indexer ("DeepSeek V4 结构速览", Lightning Indexer) then scores every
+ * visible key, the new one included.
+ *
+ * Arguments: those of lightning_index, then the jobs (the rules of
+ * csa_compress_batch; n_jobs may be 0, then this is lightning_index), and
+ * e_new, the key entry the jobs write (ignored when n_jobs is 0).  The jobs
+ * must not write q, q_scale, w or scores; a job may write the keys only at
+ * entry e_new.  With MXFP4 keys, T = 1 and jobs that each write one entry per
+ * sequence from bf16 rows (n_tok = 4, B as the indexer's, c <= 512, outputs
+ * bf16, fp8 or MXFP4; any output inside k / k_scale being exactly entry e_new
+ * of every sequence in their layout) the jobs run inside the indexer's launch,
+ * in the workgroup that scores entry e_new of each sequence, before it reads
+ * its keys; otherwise the call makes the two launches.  Errors: as
+ * lightning_index and csa_compress_batch; e_new outside [0, N) with jobs is
+ * CSA_ERR_INVALID_ARG.
+ */
+int lightning_index_compressed(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                               int H_I, int d_I,
+                               const void* q, const void* q_scale, const float* w,
+                               const void* k, const void* k_scale, int qk_dtype,
+                               void* scores, int score_dtype,
+                               const csa_compress_job* jobs, int n_jobs, int64_t e_new, void* stream);
 
 /*
  * topk_select -- stage 3, the causal Top-k selector.

@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "topk_select", "sparse_mqa_attn", "hca_attn",
+__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "lightning_index_compressed", "topk_select", "sparse_mqa_attn", "hca_attn",
            "sparse_mqa_attn_noalloc",
            "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "csa_compress_paged_chunk",
            "csa_compress_paged_batch",
@@ -91,6 +91,10 @@ def library() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _int, _vp]
         lib.csa_compress_batch.restype = ctypes.c_int
+        lib.lightning_index_compressed.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp,
+                                                   _vp, _int, _vp, _int, ctypes.POINTER(_CompressJob), _int, _i64,
+                                                   _vp]
+        lib.lightning_index_compressed.restype = ctypes.c_int
         lib.csa_compress_paged_batch.argtypes = [ctypes.POINTER(_CompressPagedJob), _int, _vp]
         lib.csa_compress_paged_batch.restype = ctypes.c_int
         lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
@@ -214,11 +218,8 @@ def _compress_out(Ca, ratio, out, out_dtype, cache_entry0):
     return out, _ptr(out) + cache_entry0 * row * out.element_size(), out.shape[1] * c
 
 
-def csa_compress_batch(jobs, stream=None):
-    """Several stage-1 calls of one ratio and dtype pair in one launch.  Each job
-    is a dict of csa_compress's arguments (ratio, Ca, Za, bias and optionally
-    Cb, Zb, prev_Cb, prev_Zb, pos0, gamma, eps, out, out_dtype, cache_entry0,
-    rope_dims, rope_base, rope_anchor); returns the list of outputs."""
+def _compress_jobs(jobs):
+    """ctypes array of csa_compress_job for csa_compress_batch's job dicts, and the outputs."""
     arr = (_CompressJob * len(jobs))()
     outs = []
     for j, d in zip(arr, jobs):
@@ -235,6 +236,15 @@ def csa_compress_batch(jobs, stream=None):
         j.out_scale = sptr
         j.rope_dims, j.rope_base, j.rope_anchor = (d.get("rope_dims", 0), d.get("rope_base", ROPE_BASE),
                                                    d.get("rope_anchor", 0))
+    return arr, outs
+
+
+def csa_compress_batch(jobs, stream=None):
+    """Several stage-1 calls of one ratio and dtype pair in one launch.  Each job
+    is a dict of csa_compress's arguments (ratio, Ca, Za, bias and optionally
+    Cb, Zb, prev_Cb, prev_Zb, pos0, gamma, eps, out, out_dtype, cache_entry0,
+    rope_dims, rope_base, rope_anchor); returns the list of outputs."""
+    arr, outs = _compress_jobs(jobs)
     st = library().csa_compress_batch(arr, len(jobs), _stream(stream))
     _check(st, "csa_compress_batch")
     return outs
@@ -281,6 +291,25 @@ def lightning_index(q, w, k, *, q_pos0, ratio=4, qk_dtype=None, q_scale=None, k_
                                    _ptr(k), _ptr(k_scale), qk_dtype, _ptr(scores), _dt(scores),
                                    _stream(stream))
     _check(st, "lightning_index")
+    return scores
+
+
+def lightning_index_compressed(q, w, k, jobs, *, e_new, q_pos0, ratio=4, qk_dtype=None, q_scale=None,
+                               k_scale=None, score_dtype=torch.bfloat16, scores=None, N=None, stream=None):
+    """A decode step's compressor writes (csa_compress_batch's job dicts), then
+    stage 2, in one call: the results of csa_compress_batch(jobs) followed by
+    lightning_index(...).  ``e_new`` is the key entry the jobs write."""
+    B, T = q.shape[:2]
+    N = k.shape[1] if N is None else N
+    if qk_dtype is None:
+        qk_dtype = _dt(q)
+    if scores is None:
+        scores = torch.empty(B, T, N, dtype=score_dtype, device=q.device)
+    arr, _ = _compress_jobs(jobs) if jobs else (None, [])
+    st = library().lightning_index_compressed(B, T, N, q_pos0, ratio, 64, 128, _ptr(q), _ptr(q_scale), _ptr(w),
+                                              _ptr(k), _ptr(k_scale), qk_dtype, _ptr(scores), _dt(scores), arr,
+                                              len(jobs), e_new, _stream(stream))
+    _check(st, "lightning_index_compressed")
     return scores
 
 

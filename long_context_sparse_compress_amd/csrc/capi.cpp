@@ -56,12 +56,15 @@ int csa_compress(int ratio, int64_t B, int64_t n_tok, int64_t c, int64_t pos0, c
                          out_dtype, out, out_batch_stride, nullptr, 0, 0.f, 0, workspace, ws_bytes, stream);
 }
 
-int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
+namespace {
+
+// The rules of csa_compress_batch for 1..4 jobs; the jobs' launch arguments
+// go to `a`.
+csa::Check check_jobs(const csa_compress_job* jobs, int n_jobs, csa::CompressArgs* a) {
   csa::Check ck;
   if (!jobs) ck.fail(CSA_ERR_INVALID_ARG, "jobs is NULL");
   else if (n_jobs < 1 || n_jobs > 4) ck.fail(CSA_ERR_INVALID_ARG, "n_jobs must be 1..4, got " + csa::i2s(n_jobs));
-  if (!ck.ok()) return finish(ck);
-  csa::CompressArgs a[4];
+  if (!ck.ok()) return ck;
   for (int q = 0; q < n_jobs; ++q) {
     const csa_compress_job& j = jobs[q];
     csa::Check cj = csa::check_compress(j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb,
@@ -78,13 +81,43 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
                                    "jobs of one other output type)");
     if (!cj.ok()) {
       cj.msg = "job " + csa::i2s(q) + ": " + cj.msg;
-      return finish(cj);
+      return cj;
     }
     a[q] = csa::CompressArgs{j.ratio, j.B, j.n_tok, j.c, j.pos0, j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb,
                              j.bias, j.gamma, j.eps, j.in_dtype, j.out_dtype, j.out, j.out_batch_stride, nullptr, 0,
                              j.rope_dims, j.rope_base, j.rope_anchor, j.out_scale};
   }
+  return ck;
+}
+
+}  // namespace
+
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
+  csa::CompressArgs a[4];
+  const csa::Check ck = check_jobs(jobs, n_jobs, a);
+  if (!ck.ok()) return finish(ck);
   return hip_status(csa::launch_compress_batch(a, n_jobs, as_stream(stream)), "csa_compress_batch launch");
+}
+
+int lightning_index_compressed(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int H_I, int d_I,
+                               const void* q, const void* q_scale, const float* w, const void* k,
+                               const void* k_scale, int qk_dtype, void* scores, int score_dtype,
+                               const csa_compress_job* jobs, int n_jobs, int64_t e_new, void* stream) {
+  csa::Check ck = csa::check_index(B, T, N, q_pos0, ratio, H_I, d_I, q, q_scale, w, k, k_scale, qk_dtype,
+                                   scores, score_dtype);
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs a[4];
+  if (n_jobs != 0) {
+    ck = check_jobs(jobs, n_jobs, a);
+    if (!ck.ok()) return finish(ck);
+  }
+  if (n_jobs != 0 && (e_new < 0 || e_new >= N)) {
+    ck.fail(CSA_ERR_INVALID_ARG, "e_new must lie in [0, N), got " + csa::i2s(e_new));
+    return finish(ck);
+  }
+  csa::IndexArgs ia{B, T, N, q_pos0, ratio, q, q_scale, w, k, k_scale, qk_dtype, scores, score_dtype};
+  return hip_status(csa::launch_index_jobs(ia, a, n_jobs, e_new, as_stream(stream)),
+                    "lightning_index_compressed launch");
 }
 
 int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int H_I, int d_I,

@@ -22,8 +22,11 @@
 // Because K is contracted, the order of K inside a lane's fragment is free as
 // long as q and k use the same order: every lane loads the same contiguous
 // byte range of its q row and of its key row.
+#include <cmath>
 #include <type_traits>
+#include <utility>
 
+#include "compress_entry.h"
 #include "device.h"
 #include "launch.h"
 
@@ -183,12 +186,12 @@ struct KeyPages {
 // sized for (GT = 8 needs the whole register file: one wave per SIMD).
 // PG: keys in the paged pool (decode, T = 1): a tile's block comes from the
 // block table by one wave-uniform load, ids outside the pool read block 0.
-template <int QK, int QPW, int TPW, int GT, int OCC, typename TS, bool PG = false>
-__global__ void __launch_bounds__(256, OCC)
-index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
-                  const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
-                  const float* __restrict__ w, const uint8_t* __restrict__ k,
-                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg) {
+template <int QK, int QPW, int TPW, int GT, typename TS, bool PG>
+__device__ __forceinline__ void index_mfma_body(int64_t bx, int64_t by, int64_t bz, int64_t T, int64_t N,
+                                                int64_t q_pos0, int ratio, const uint8_t* __restrict__ q,
+                                                const void* __restrict__ q_scale, const float* __restrict__ w,
+                                                const uint8_t* __restrict__ k, const void* __restrict__ k_scale,
+                                                TS* __restrict__ scores, const KeyPages& pg) {
   static_assert(GT % 4 == 0 && TPW % GT == 0, "tiles are stored four at a time");
   static_assert(!PG || QPW == 1, "paged keys: decode shape");
   constexpr int KG = GT / 4;   // 4-tile score stores per group
@@ -198,9 +201,9 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar loop control
   const int col = lane & 15;   // row of a 16-row operand tile / column of the output tile
   const int g = lane >> 4;     // lane group: K sub-range, and output rows 4g..4g+3
-  const int64_t b = blockIdx.z;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * QPW;
-  const int64_t e_wave = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * (TPW * 16);
+  const int64_t b = bz;
+  const int64_t t0 = by * QPW;
+  const int64_t e_wave = (bx * 4 + wid) * (TPW * 16);
 
   // The workgroup's q rows go through LDS once (coalesced 16-byte loads)
   // instead of every wave fetching its fragments from global memory.
@@ -339,6 +342,75 @@ index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
       }
     }
   }
+}
+
+
+template <int QK, int QPW, int TPW, int GT, int OCC, typename TS, bool PG = false>
+__global__ void __launch_bounds__(256, OCC)
+index_mfma_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                  const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
+                  const float* __restrict__ w, const uint8_t* __restrict__ k,
+                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg) {
+  index_mfma_body<QK, QPW, TPW, GT, TS, PG>(blockIdx.x, blockIdx.y, blockIdx.z, T, N, q_pos0, ratio, q, q_scale, w,
+                                            k, k_scale, scores, pg);
+}
+
+// A decode step's compressor writes in the indexer's own launch (one query a
+// sequence, contiguous keys).  Grid (X, 1, B).  The first B workgroups
+// dispatched are, for each sequence b, the one whose key run holds the
+// written entry (run x_own): it runs sequence b's share of every job -- one
+// entry each, two channels a thread -- and only then reads its keys, so it
+// scores the key it has just written; no other workgroup reads that entry.
+// Dispatched first, its extra latency overlaps the other workgroups' key
+// streams instead of adding a launch to the step.  The remaining workgroups
+// take the other runs in the plain order.
+template <int QK, int TPW, int GT, int OCC, typename TS>
+__global__ void __launch_bounds__(256, OCC)
+index_mfma_jobs_kernel(int64_t N, int64_t q_pos0, int ratio, const uint8_t* __restrict__ q,
+                       const void* __restrict__ q_scale, const float* __restrict__ w,
+                       const uint8_t* __restrict__ k, const void* __restrict__ k_scale, TS* __restrict__ scores,
+                       CompressBatch jb, int n_jobs, int64_t x_own) {
+  const int64_t X = gridDim.x, B = gridDim.z;
+  const int64_t L = blockIdx.x + X * static_cast<int64_t>(blockIdx.z);
+  int64_t bx, bz;
+  if (L < B) {
+    bx = x_own;
+    bz = L;
+    for (int j = 0; j < n_jobs; ++j) {
+      const CompressJobDev& J = jb.j[j];
+      const auto* Ca = static_cast<const uint16_t*>(J.Ca);
+      const auto* Za = static_cast<const uint16_t*>(J.Za);
+      const auto* Cb = static_cast<const uint16_t*>(J.Cb);
+      const auto* Zb = static_cast<const uint16_t*>(J.Zb);
+      const auto* pCb = static_cast<const uint16_t*>(J.pCb);
+      const auto* pZb = static_cast<const uint16_t*>(J.pZb);
+      if (J.qfmt == 2)
+        compress_entry<uint16_t, E2M1x2, 4, false, 2, 8>(0, bz, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                         J.bias, J.gamma, J.eps, static_cast<E2M1x2*>(J.out),
+                                                         J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                         J.rope_anchor, J.out_scale, J.scale_stride);
+      else if (J.qfmt == 1)
+        compress_entry<uint16_t, uint8_t, 4, false, 2, 8>(0, bz, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                          J.bias, J.gamma, J.eps, static_cast<uint8_t*>(J.out),
+                                                          J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                          J.rope_anchor, J.out_scale, J.scale_stride);
+      else
+        compress_entry<uint16_t, uint16_t, 4, false, 2, 8>(0, bz, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb,
+                                                           pZb, J.bias, J.gamma, J.eps, static_cast<uint16_t*>(J.out),
+                                                           J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                           J.rope_anchor, J.out_scale, J.scale_stride);
+      // the job's writes are visible to every wave of the workgroup, and
+      // its LDS (norm sums, RoPE table) is free for the next one
+      __syncthreads();
+    }
+  } else {
+    const int64_t m = L - B;   // X > 1 here
+    bz = m / (X - 1);
+    const int64_t xi = m % (X - 1);
+    bx = xi < x_own ? xi : xi + 1;
+  }
+  index_mfma_body<QK, 1, TPW, GT, TS, false>(bx, 0, bz, 1, N, q_pos0, ratio, q, q_scale, w, k, k_scale, scores,
+                                             KeyPages{nullptr, 0, 0, nullptr});
 }
 
 // ---------------------------------------------------------------- ring path
@@ -741,6 +813,89 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
     case CSA_MXFP4: return launch_qk<CSA_MXFP4>(a, s);
     default: return hipErrorNotSupported;
   }
+}
+
+namespace {
+
+// Whether launch_index_jobs may run the jobs inside the MXFP4 decode
+// indexer's launch: every job a one-entry C4A write from bf16 rows in the
+// narrow layout (two channels a thread, at most 256 threads), and any job
+// output that lands in the keys or their scales is exactly entry e_new in
+// the layout the indexer reads; no job output touches q, w or the scores.
+bool jobs_fusable(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e_new) {
+  if (a.qk_dtype != CSA_MXFP4 || a.T != 1 || a.block_table || a.N < 1 || e_new < 0 || e_new >= a.N) return false;
+  if (a.score_dtype != CSA_BF16 && a.score_dtype != CSA_F32) return false;
+  auto range = [](const void* p, int64_t bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return std::make_pair(b, b + static_cast<uintptr_t>(bytes));
+  };
+  auto overlap = [](std::pair<uintptr_t, uintptr_t> x, std::pair<uintptr_t, uintptr_t> y) {
+    return x.first < y.second && y.first < x.second;
+  };
+  const auto kr = range(a.k, a.B * a.N * 64), sr = range(a.k_scale, a.B * a.N * 4);
+  const auto qr = range(a.q, a.B * 64 * 64), qsr = range(a.q_scale, a.B * 64 * 4), wr = range(a.w, a.B * 64 * 4);
+  const auto scr = range(a.scores, a.B * a.N * (a.score_dtype == CSA_BF16 ? 2 : 4));
+  for (int q = 0; q < n; ++q) {
+    const CompressArgs& j = jobs[q];
+    if (j.ratio != 4 || j.in_dtype != CSA_BF16 || j.n_tok != 4 || j.B != a.B || j.c > 512 || j.c % 64) return false;
+    if (j.out_dtype != CSA_BF16 && j.out_dtype != CSA_FP8_E4M3 && j.out_dtype != CSA_MXFP4) return false;
+    const int64_t stride = j.out_batch_stride ? j.out_batch_stride : j.c;   // elements a sequence
+    const int64_t span = (j.B - 1) * stride + j.c;
+    const int64_t ob = j.out_dtype == CSA_BF16 ? 2 * span : (j.out_dtype == CSA_FP8_E4M3 ? span : span / 2);
+    const auto orr = range(j.out, ob);
+    const int64_t sb = j.out_dtype == CSA_FP8_E4M3 ? ((j.B - 1) * (stride / j.c) + 1) * 4
+                       : j.out_dtype == CSA_MXFP4  ? ((j.B - 1) * (stride / j.c) + 1) * (j.c / 32)
+                                                   : 0;
+    const auto osr = range(j.out_scale, sb);
+    for (const auto& x : {qr, qsr, wr, scr})
+      if (overlap(orr, x) || (sb && overlap(osr, x))) return false;
+    const bool in_keys = overlap(orr, kr) || (sb && overlap(osr, kr));
+    const bool in_scales = overlap(orr, sr) || (sb && overlap(osr, sr));
+    if (in_keys || in_scales) {
+      const bool key_entry = j.out_dtype == CSA_MXFP4 && j.c == 128 && stride == a.N * 128 &&
+                             orr.first == kr.first + static_cast<uintptr_t>(e_new * 64) &&
+                             osr.first == sr.first + static_cast<uintptr_t>(e_new * 4);
+      if (!key_entry) return false;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e_new, hipStream_t s) {
+  if (n < 1) return launch_index(a, s);
+  if (a.B == 0 || a.N == 0 || !jobs_fusable(a, jobs, n, e_new)) {
+    const hipError_t e = launch_compress_batch(jobs, n, s);
+    return e != hipSuccess ? e : launch_index(a, s);
+  }
+  // the MXFP4 decode shape of launch_qk: one query a wave, 8 tiles a wave;
+  // registers for five waves a SIMD, the plain kernel's occupancy
+  constexpr int TPW = 8, GT = 4, OCC = 5;
+  constexpr int64_t per_wg = 4 * TPW * 16;
+  CompressBatch jb{};
+  for (int q = 0; q < n; ++q) {
+    const CompressArgs& j = jobs[q];
+    const int64_t stride = j.out_batch_stride ? j.out_batch_stride : j.c;
+    const double l2b = j.rope_dims > 0 ? std::log2(static_cast<double>(j.rope_base)) : 0.0;
+    jb.j[q] = CompressJobDev{j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb, j.bias, j.gamma, j.out, j.n_tok, j.pos0,
+                             stride, 1, j.B, j.eps, static_cast<int>(j.c), 1, j.rope_dims, l2b, j.rope_anchor,
+                             j.out_scale, stride / j.c,
+                             j.out_dtype == CSA_FP8_E4M3 ? 1 : (j.out_dtype == CSA_MXFP4 ? 2 : 0)};
+  }
+  const dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg), 1, static_cast<uint32_t>(a.B));
+  const int64_t x_own = e_new / per_wg;
+  const auto* q = static_cast<const uint8_t*>(a.q);
+  const auto* k = static_cast<const uint8_t*>(a.k);
+  const size_t smem = 64 * sizeof(float);   // the jobs' RMSNorm sums and fp8 amax
+  if (a.score_dtype == CSA_BF16)
+    hipLaunchKernelGGL((index_mfma_jobs_kernel<CSA_MXFP4, TPW, GT, OCC, uint16_t>), grid, dim3(256), smem, s, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores), jb, n,
+                       x_own);
+  else
+    hipLaunchKernelGGL((index_mfma_jobs_kernel<CSA_MXFP4, TPW, GT, OCC, float>), grid, dim3(256), smem, s, a.N,
+                       a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores), jb, n, x_own);
+  return hipGetLastError();
 }
 
 }  // namespace csa

@@ -136,6 +136,11 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s);
 hipError_t launch_compress_paged(const CompressPagedArgs* jobs, int n, hipStream_t s);   // 1..4 jobs
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
+// The compressor jobs (1..4), then the indexer: in one launch where the
+// indexer's decode kernel can run them (MXFP4 keys, one query a sequence,
+// one-entry bf16 jobs whose writes into the keys are entry e_new), else as a
+// compressor launch followed by the indexer's.  Same results either way.
+hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e_new, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

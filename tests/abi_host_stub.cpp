@@ -10,6 +10,7 @@ hipError_t launch_compress(const CompressArgs&, hipStream_t) { return hipSuccess
 hipError_t launch_compress_batch(const CompressArgs*, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_compress_paged(const CompressPagedArgs*, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_index(const IndexArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_index_jobs(const IndexArgs&, const CompressArgs*, int, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_pool(const IndexPoolArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipSuccess; }

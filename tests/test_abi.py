@@ -137,6 +137,39 @@ def test_index_validation(lib):
     assert call(qk=7) == -2
 
 
+def test_index_compressed_validation(lib):
+    """lightning_index_compressed: the indexer's checks, then the jobs' (as
+    csa_compress_batch), then e_new (only with jobs).  Error cases only: a
+    valid call would launch."""
+    import ctypes
+    import long_context_sparse_compress_amd as csa
+    f = lib.lightning_index_compressed
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_void_p,
+                                                                                       ctypes.c_int,
+                                                                                       ctypes.POINTER(csa._CompressJob),
+                                                                                       ctypes.c_int, ctypes.c_int64,
+                                                                                       ctypes.c_void_p]
+
+    def job(**kw):
+        d = dict(ratio=4, B=2, n_tok=4, c=512, pos0=4, Ca=A, Za=A, Cb=A, Zb=A, prev_Cb=A, prev_Zb=A,
+                 bias=A, gamma=None, eps=1e-6, in_dtype=1, out_dtype=1, out=A, out_batch_stride=0)
+        d.update(kw)
+        return csa._CompressJob(**d)
+
+    def call(jobs=None, n=None, e_new=63, B=2, N=64, q_pos0=255, H=64, qk=1, qs=None, ks=None):
+        arr = (csa._CompressJob * max(1, len(jobs or [])))(*(jobs or []))
+        n = len(jobs or []) if n is None else n
+        return f(B, 1, N, q_pos0, 4, H, 128, A, qs, A, A, ks, qk, A, 1, arr, n, e_new, None)
+
+    assert call(e_new=-5, H=32) == -2 and "H_I=64" in _err(lib)  # no jobs: e_new is not looked at
+    assert call([job()], H=32) == -2 and "H_I=64" in _err(lib)   # the indexer is checked first
+    assert call([job(), job(c=128, Ca=None)]) == -1 and "job 1: Ca is NULL" in _err(lib)
+    assert call([job()], n=5) == -1 and "n_jobs" in _err(lib)
+    assert call([job()], e_new=64) == -1 and "e_new" in _err(lib)
+    assert call([job()], e_new=-1) == -1 and "e_new" in _err(lib)
+    assert call([job(ratio=128, n_tok=128, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None), job()]) == -1
+
+
 def test_topk_validation(lib):
     f = lib.topk_select
     assert f(1, 1, 64, 255, 4, 0, A, 1, A, None, 0, None) == -1 and "k must be" in _err(lib)
