@@ -198,3 +198,34 @@ def test_fallback_key_written_elsewhere():
     same results."""
     c = _case("fd.else", 2, 2048, 1000, 4 * 2048 - 1, key_entry=1500)
     _check(c, fused_launch=False)
+
+
+def test_fused_in_graph_replays():
+    """The fused call captured in a HIP graph (as the bench runs it): every
+    replay, with eager work and synchronisations between replays, gives the
+    eager call's bytes."""
+    c = _case("fd.graph", 4, 4096, 4095, 4 * 4096 - 1)
+    ref_c = c["caches"]()
+    ref_s = _fused(c, ref_c, torch.bfloat16)
+    torch.cuda.synchronize()
+    cc = c["caches"]()
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        s = _fused(c, cc, torch.bfloat16)        # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            s = _fused(c, cc, torch.bfloat16)
+    torch.cuda.synchronize()
+    e = c["e_new"]
+    for rep in range(3):
+        cc["k"][:, e].zero_()                     # the replay must rewrite the new entry
+        cc["ks"][:, e].zero_()
+        cc["kv"][:, 5].zero_()
+        s.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(s.view(torch.int16), ref_s.view(torch.int16)), f"replay {rep}: scores"
+        assert torch.equal(cc["k"][:, e], ref_c["k"][:, e]) and torch.equal(cc["ks"][:, e], ref_c["ks"][:, e])
+        assert torch.equal(cc["kv"][:, 5], ref_c["kv"][:, 5])
