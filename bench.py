@@ -16,8 +16,10 @@ rotated over several seeded copies, more than the 256 MB Infinity Cache in
 total, so each step streams its keys and rows from HBM.
 
 Timing: W untimed steps, then K steps between two HIP events on the stream
-the kernels run on (one HIP graph per cache copy; --eager times eager
-launches), ms_per_step = elapsed / K and value = query tokens / s.  A second,
+the kernels run on (one HIP graph holding a step on each cache copy in turn,
+as a serving loop captures several layers in one graph, plus single-step
+graphs for a remainder; --eager times eager launches), ms_per_step =
+elapsed / K and value = query tokens / s.  A second,
 eager pass brackets every stage with events on that stream: each stage's
 average duration (which includes its launch's dispatch).  The dominant
 kernel's launch duration is timed on its own: a HIP graph of its launches
@@ -34,7 +36,8 @@ bounded sample of each configuration's step (about --cpu-seconds each).
 --workload NAME prints the same record for one workload: a configuration
 (csa_1m_decode, csa_decode, csa_prefill, hca_decode, hca_prefill) or another
 workload (csa_hca_decode, c128a_1m, csa_reindex_decode, csa_reindex_prefill,
-csa_paged_decode, csa_paged_1m_decode, hbm_copy, hbm_read).
+csa_paged_decode, csa_paged_1m_decode, csa_1m_decode_separate, hbm_copy,
+hbm_read).
 """
 from __future__ import annotations
 
@@ -74,14 +77,18 @@ def parse():
 
 
 def time_step(torch, wk, steps, warmup, eager):
-    """Average step time over `steps` steps, copy i % copies on step i."""
+    """Average step time over exactly `steps` steps, copy i % copies on step i.
+    Graph timing: one HIP graph holds one step on each cache copy in turn (a
+    serving loop likewise captures a step's layers in one graph, so the
+    graph's own launch is paid once per several layers); `steps // copies`
+    replays of it, then single-step graphs for the remainder."""
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         for r in range(wk.copies):                 # eager warm run of every copy (also loads the kernels)
             for s in wk.stages:
                 s[1](r)
     torch.cuda.synchronize()
-    graphs = []
+    graphs, multi = [], None
     if not eager:
         for r in range(wk.copies):
             g = torch.cuda.CUDAGraph()
@@ -89,28 +96,40 @@ def time_step(torch, wk, steps, warmup, eager):
                 for s in wk.stages:
                     s[1](r)
             graphs.append(g)
+        if wk.copies > 1:
+            multi = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(multi, stream=st):
+                for r in range(wk.copies):
+                    for s in wk.stages:
+                        s[1](r)
         torch.cuda.synchronize()
 
-    def run(i):
+    def run(n):
+        """n steps, starting at copy 0."""
         if eager:
-            for s in wk.stages:
-                s[1](i % wk.copies)
-        else:
-            graphs[i % wk.copies].replay()
+            for i in range(n):
+                for s in wk.stages:
+                    s[1](i % wk.copies)
+            return
+        i = 0
+        if multi is not None:
+            for _ in range(n // wk.copies):
+                multi.replay()
+            i = n - n % wk.copies
+        for j in range(i, n):
+            graphs[j % wk.copies].replay()
 
     with torch.cuda.stream(st):
-        for i in range(warmup):
-            run(i)
+        run(warmup)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(st)
-        for i in range(steps):
-            run(i)
+        run(steps)
         e1.record(st)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    del graphs
+    del graphs, multi
     return e0.elapsed_time(e1) / steps, wall
 
 
