@@ -229,3 +229,35 @@ def test_fused_in_graph_replays():
         assert torch.equal(s.view(torch.int16), ref_s.view(torch.int16)), f"replay {rep}: scores"
         assert torch.equal(cc["k"][:, e], ref_c["k"][:, e]) and torch.equal(cc["ks"][:, e], ref_c["ks"][:, e])
         assert torch.equal(cc["kv"][:, 5], ref_c["kv"][:, 5])
+
+
+def test_no_jobs_is_the_indexer():
+    """n_jobs = 0: exactly lightning_index (e_new is not looked at)."""
+    c = _case("fd.none", 2, 1000, 999, 4 * 1000 - 1)
+    cc = c["caches"]()
+    a = csa.lightning_index(c["q"], c["w"], cc["k"], q_pos0=c["q_pos0"], qk_dtype=c["qk"], q_scale=c["qs"],
+                            k_scale=cc["ks"])
+    b = csa.lightning_index_compressed(c["q"], c["w"], cc["k"], [], e_new=-1, q_pos0=c["q_pos0"],
+                                       qk_dtype=c["qk"], q_scale=c["qs"], k_scale=cc["ks"])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fallback_two_queries_a_sequence():
+    """T = 2 (two queries a sequence): two launches, the same results as the
+    separate calls."""
+    B, N, q0 = 3, 2000, 4 * 2000 - 2
+    x = synth.device_normal("fd.t2.keys", (B, N, 128))
+    k, ks = synth.device_quant_mxfp4(x)
+    q, qs = synth.device_quant_mxfp4(synth.device_normal("fd.t2.qi", (B, 2, 64, 128)))
+    w = synth.device_uniform("fd.t2.w", (B, 2, 64))
+    c4k = _c4("fd.t2.c4k", B, 128)
+    b4k = synth.device_normal("fd.t2.b4k", (8, 128), var=0.1)
+    k1, ks1, k2, ks2 = k.clone(), ks.clone(), k.clone(), ks.clone()
+    csa.csa_compress_batch([_job(c4k, b4k, q0 - 2, k1, N - 1, ks1)])
+    s1 = csa.lightning_index(q, w, k1, q_pos0=q0, qk_dtype=csa.MXFP4, q_scale=qs, k_scale=ks1)
+    s2 = csa.lightning_index_compressed(q, w, k2, [_job(c4k, b4k, q0 - 2, k2, N - 1, ks2)], e_new=N - 1, q_pos0=q0,
+                                        qk_dtype=csa.MXFP4, q_scale=qs, k_scale=ks2)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(ks1, ks2)
+    assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
