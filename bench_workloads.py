@@ -383,7 +383,7 @@ def csa_prefill(torch, csa, synth, copies=1):
 # ---------------------------------------------------------------- HCA layer
 
 
-def _hca(torch, csa, synth, decode, copies):
+def _hca(torch, csa, synth, decode, copies, fuse=True):
     bf = torch.bfloat16
     dn = synth.device_normal
     B, T = (16, 1) if decode else (1, 2048)
@@ -413,13 +413,27 @@ def _hca(torch, csa, synth, decode, copies):
                   "chunk, dense MQA with sink over 8,176..8,192 entries + window", T, copies,
                   dict(batch=1, context=1048576, chunk=T, c128a_entries=N, window=128, heads=64, head_dim=512),
                   "hca_attn")
-    wk.add("compress_c128a_kv", lambda r: csa.csa_compress(128, c["Ca"], c["Za"], b128, pos0=cpos, out=kv[r],
-                                                           cache_entry0=cpos // 128, workspace=wsc),
-           B * ntok * 512 * 4 + B * ntok // 128 * 1024 + 128 * 512 * 4, 0, "hbm")
-    wk.add("hca_attn", lambda r: csa.hca_attn(q, kv[r], raw, q_pos0=q0, raw_pos0=raw0, sink=sink, out=out,
-                                              workspace=ws),
-           (B * rows * 1024 if decode else (N + raw.shape[1]) * 1024) + B * T * 2 * 64 * 512 * 2,
-           B * rows * 64 * 512 * 4, "hbm" if decode else "bf16")
+    c_bytes = B * ntok * 512 * 4 + B * ntok // 128 * 1024 + 128 * 512 * 4
+    a_bytes = (B * rows * 1024 if decode else (N + raw.shape[1]) * 1024) + B * T * 2 * 64 * 512 * 2
+    a_flops = B * rows * 64 * 512 * 4
+    if decode and fuse:
+        # the C128A write inside the attention's launch (hca_attn_compressed)
+        wk.dominant = "compress_attn"
+        wk.label = wk.label.replace("C128A compress of the last block, dense MQA",
+                                    "C128A compress of the last block inside the dense MQA's launch")
+        job = lambda r: dict(ratio=128, Ca=c["Ca"], Za=c["Za"], bias=b128, pos0=cpos, out=kv[r],
+                             cache_entry0=cpos // 128)
+        wk.add("compress_attn", lambda r: csa.hca_attn_compressed(q, kv[r], raw, job(r), e_new=cpos // 128,
+                                                                  q_pos0=q0, raw_pos0=raw0, sink=sink, out=out,
+                                                                  workspace=ws),
+               c_bytes + a_bytes, a_flops, "hbm")
+    else:
+        wk.add("compress_c128a_kv", lambda r: csa.csa_compress(128, c["Ca"], c["Za"], b128, pos0=cpos, out=kv[r],
+                                                               cache_entry0=cpos // 128, workspace=wsc),
+               c_bytes, 0, "hbm")
+        wk.add("hca_attn", lambda r: csa.hca_attn(q, kv[r], raw, q_pos0=q0, raw_pos0=raw0, sink=sink, out=out,
+                                                  workspace=ws),
+               a_bytes, a_flops, "hbm" if decode else "bf16")
 
     def cpu(budget):
         from oracle import attention as oa, compressor as oc
@@ -471,6 +485,14 @@ def _hca(torch, csa, synth, decode, copies):
 def hca_decode(torch, csa, synth, copies=4):
     """Config 4, decode: batch 16 at 1,048,576 context."""
     return _hca(torch, csa, synth, True, copies)
+
+
+def hca_decode_separate(torch, csa, synth, copies=4):
+    """The HCA decode with the C128A write in launches of its own (A/B against the
+    configuration's single launch)."""
+    wk = _hca(torch, csa, synth, True, copies, fuse=False)
+    wk.key = "hca_decode_separate"
+    return wk
 
 
 def hca_prefill(torch, csa, synth, copies=1):
@@ -816,5 +838,6 @@ def hbm_read(torch, csa, synth, copies=4):
 EXTRAS = {"csa_hca_decode": csa_hca_decode, "c128a_1m": c128a_1m, "csa_reindex_decode": csa_reindex_decode,
           "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode,
           "csa_paged_1m_decode": csa_paged_1m_decode, "csa_1m_decode_separate": csa_1m_decode_separate,
+          "hca_decode_separate": hca_decode_separate,
           "hbm_copy": hbm_copy,
           "hbm_read": hbm_read}

@@ -7,6 +7,7 @@
  *   csa_compress      C4A / C128A KV compressor
  *   csa_compress_batch  several compressor calls of one ratio in one launch
  *   lightning_index_compressed  a decode step's compressor writes and the indexer in one call
+ *   hca_attn_compressed  a decode step's C128A write and the HCA attention in one call
  *   lightning_index   indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
  *   topk_select       causal Top-k over the indexer scores
  *   sparse_mqa_attn   shared-KV MQA over the Top-k entries plus the window
@@ -430,6 +431,36 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
                 int io_dtype, void* out, float* lse, int flags,
                 int rope_dims, float rope_base,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attn_compressed -- a decode step's C128A write, then the HCA attention,
+ * as one call.
+ *
+ * The results of csa_compress(job) followed by hca_attn_ex(...) on the same
+ * stream: the step's new C128A entry ("DeepSeek V4 结构速览", HCA（c128a 路线）:
+ * one entry pools 128 raw tokens; "DeepSeek-V4技术报告解读，全适配国产算力" 2.1,
+ * the compression formula) is pooled into kv_cmp, and the dense attention
+ * over every visible entry plus the window reads it.  Arguments: those of
+ * hca_attn_ex, then one csa_compress_job (ratio 128; the rules of
+ * csa_compress_batch) and e_new, the kv_cmp entry it writes.  With bf16 I/O,
+ * T = 1, flags 0 and a job that writes one entry per sequence (n_tok = 128,
+ * c = 512, bf16 in and out) exactly at entry e_new of kv_cmp (e_new visible to
+ * the query, kv_cmp's layout) and touches nothing else the attention reads or
+ * writes, the entry is pooled inside the attention's launch by the workgroup
+ * whose tiles hold it, before it reads them; otherwise the call makes the
+ * compressor's launch and the attention's.  The two routes may sum the
+ * entry's row groups in a different order (differences at the rounding of the
+ * entry's bf16 store).  The workspace is the attention's
+ * (csa_workspace_bytes(CSA_OP_HCA_ATTN, ...)).  Errors: as hca_attn_ex and
+ * csa_compress_batch; a job of another ratio, or e_new outside [0, N), is
+ * CSA_ERR_INVALID_ARG.
+ */
+int hca_attn_compressed(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d,
+                        const void* q, const void* kv_cmp, const void* kv_raw, int64_t raw_pos0,
+                        int64_t n_raw, int window, float scale, const float* sink,
+                        int io_dtype, void* out, float* lse, int flags,
+                        int rope_dims, float rope_base, void* workspace, size_t ws_bytes,
+                        const csa_compress_job* job, int64_t e_new, void* stream);
 
 /*
  * sparse_mqa_attn_noalloc -- sparse_mqa_attn for callers that cannot

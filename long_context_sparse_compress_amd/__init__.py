@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "lightning_index_compressed", "topk_select", "sparse_mqa_attn", "hca_attn",
+__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "lightning_index_compressed", "hca_attn_compressed", "topk_select", "sparse_mqa_attn", "hca_attn",
            "sparse_mqa_attn_noalloc",
            "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "csa_compress_paged_chunk",
            "csa_compress_paged_batch",
@@ -95,6 +95,8 @@ def library() -> ctypes.CDLL:
                                                    _vp, _int, _vp, _int, ctypes.POINTER(_CompressJob), _int, _i64,
                                                    _vp]
         lib.lightning_index_compressed.restype = ctypes.c_int
+        lib.hca_attn_compressed.argtypes = (_SIGS["hca_attn_ex"][:-1] + [ctypes.POINTER(_CompressJob), _i64, _vp])
+        lib.hca_attn_compressed.restype = ctypes.c_int
         lib.csa_compress_paged_batch.argtypes = [ctypes.POINTER(_CompressPagedJob), _int, _vp]
         lib.csa_compress_paged_batch.restype = ctypes.c_int
         lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
@@ -424,6 +426,28 @@ def hca_attn(q, kv_cmp, kv_raw, *, q_pos0, raw_pos0, ratio=128, sink=None, windo
                                ATTN_BATCH_INVARIANT if batch_invariant else 0, rope_dims, rope_base, _ptr(ws),
                                wsb, _stream(stream))
     _check(st, "hca_attn")
+    return (out, lse) if return_lse else out
+
+
+def hca_attn_compressed(q, kv_cmp, kv_raw, job, *, e_new, q_pos0, raw_pos0, ratio=128, sink=None, window=128,
+                        scale=None, out=None, lse=None, return_lse=False, workspace=None, rope_dims=0,
+                        rope_base=ROPE_BASE, stream=None):
+    """A decode step's C128A write (one csa_compress_batch job dict, ratio 128,
+    writing entry ``e_new`` of ``kv_cmp``), then stage 5, in one call."""
+    B, T, H, d = q.shape
+    N = kv_cmp.shape[1]
+    n_raw = kv_raw.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(OP_HCA_ATTN, B, T, N, 0, q.device, workspace)
+    arr, _ = _compress_jobs([job])
+    st = library().hca_attn_compressed(B, T, N, ratio, q_pos0, H, d, _ptr(q), _ptr(kv_cmp), _ptr(kv_raw),
+                                       raw_pos0, n_raw, window, scale, _ptr(sink), _dt(q), _ptr(out), _ptr(lse), 0,
+                                       rope_dims, rope_base, _ptr(ws), wsb, arr, e_new, _stream(stream))
+    _check(st, "hca_attn_compressed")
     return (out, lse) if return_lse else out
 
 

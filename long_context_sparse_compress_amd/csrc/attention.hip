@@ -43,6 +43,7 @@
 #include <cmath>
 #include <mutex>
 
+#include "compress_entry.h"
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -86,6 +87,11 @@ struct Params {
   int page_shift;
   int64_t ring;
   const int64_t* seq_pos;
+  // a decode step's C128A write run inside the launch (dense lists): the
+  // workgroup whose tiles include list tile job_tile first pools its
+  // sequence's entry into the cache (job_tile < 0: none)
+  CompressJobDev job;
+  int64_t job_tile;
 };
 
 // Inverse partial RoPE of one output value held by this lane at column col,
@@ -262,7 +268,7 @@ __device__ __forceinline__ void lds_barrier() {
 // softmax arithmetic), so the two give identical bits -- the multi-workgroup
 // kernel the pages pair with the one-workgroup kernel, with the work divided
 // by heads instead of rows so that no cross-workgroup merge is needed.
-template <int TGN, int HB, bool PG = false>
+template <int TGN, int HB, bool PG = false, bool CJ = false>
 __global__ void __launch_bounds__(256 * TGN, 3 - TGN)
 attn_bf16_kernel(Params P) {
   static_assert(TGN == 1 || TGN == 2, "one or two tile groups");
@@ -301,6 +307,21 @@ attn_bf16_kernel(Params P) {
 
   uint8_t* const T0 = tb0[tg];
   uint8_t* const T1 = tb1[tg];
+
+  if constexpr (CJ) {
+    // The decode step's new C128A entry of sequence b, pooled by the
+    // workgroup whose tiles read it, before any of its rows are requested;
+    // the tile buffers serve as the pooling's LDS.  No other workgroup reads
+    // that entry.
+    if (tile0 <= P.job_tile && P.job_tile < tile1) {
+      const CompressJobDev& J = P.job;
+      compress_entry<uint16_t, uint16_t, 128, false, 8, 4>(
+          0, b, 0, 1, J.n_tok, J.c, J.pos0, static_cast<const uint16_t*>(J.Ca), static_cast<const uint16_t*>(J.Za),
+          nullptr, nullptr, nullptr, nullptr, J.bias, J.gamma, J.eps, static_cast<uint16_t*>(J.out), J.out_stride,
+          J.G, nullptr, J.rope_R, J.rope_l2b, J.rope_anchor, nullptr, 0, -1, reinterpret_cast<float*>(&tb0[0][0]));
+      __syncthreads();   // the entry is in the cache and the tile buffers are free
+    }
+  }
 
   // The query's own raw row is always in the list: padding rows load it (and are masked).
   const uint16_t* safe_row = static_cast<const uint16_t*>(P.kv_raw) + raw_row<PG>(P, b, l.pos) * kD;
@@ -854,6 +875,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   P.page_shift = a.page_shift; P.ring = a.ring; P.seq_pos = a.seq_pos;
   P.rope_R = a.rope_dims;
   P.rope_l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
+  P.job_tile = -1;
   const int64_t nq = a.B * a.T;
   if (a.io_dtype == CSA_F32) {
     P.splits = 1;
@@ -876,5 +898,65 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   return launch_bf16<false>(P, nq, per_split, a.flags, s);
 }
 
+
+
+// The HCA decode step's C128A write and the dense attention in one launch
+// where the attention's decode plan allows (bf16, one query a sequence,
+// contiguous cache, a two-group split plan): the workgroup whose tiles
+// include the new entry pools it first; the other splits never read it.
+// Otherwise the compressor's launch, then the attention's.
+hipError_t launch_attn_jobs(const AttnArgs& a, const CompressArgs& j, int64_t e_new, hipStream_t s) {
+  if (a.B == 0 || a.T == 0) return launch_compress(j, s);
+  const int64_t last = a.q_pos0 + a.T - 1;
+  const int64_t wlen = last - (last - a.window + 1 > 0 ? last - a.window + 1 : 0) + 1;
+  int64_t ncmp = (last + 1) / a.ratio;
+  if (ncmp > a.N) ncmp = a.N;
+  const int splits = attn_splits(a.B, a.T, ncmp + wlen);
+  const int64_t ntiles = (ncmp + wlen + kAttnTile - 1) / kAttnTile;
+  const int64_t per_split = (ntiles + splits - 1) / splits;
+  const int64_t stride = j.out_batch_stride ? j.out_batch_stride : j.c;
+  const uintptr_t kv0 = reinterpret_cast<uintptr_t>(a.kv_cmp);
+  bool fuse = !a.idx && a.io_dtype == CSA_BF16 && a.T == 1 && !a.block_table && !a.seq_pos && a.flags == 0 &&
+              splits > 1 && per_split >= 8 && j.ratio == 128 && j.n_tok == 128 && j.B == a.B && j.c == kD &&
+              j.in_dtype == CSA_BF16 && j.out_dtype == CSA_BF16 && !j.out_scale && e_new >= 0 && e_new < ncmp &&
+              stride == a.N * kD && reinterpret_cast<uintptr_t>(j.out) == kv0 + static_cast<uintptr_t>(e_new * kD * 2);
+  if (fuse) {
+    // the job writes only the new entries: nothing else the attention reads or writes
+    auto ov = [](const void* p, int64_t bytes, uintptr_t b0, uintptr_t b1) {
+      const uintptr_t x = reinterpret_cast<uintptr_t>(p);
+      return p && x < b1 && b0 < x + static_cast<uintptr_t>(bytes);
+    };
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(j.out);
+    const uintptr_t o1 = o0 + static_cast<uintptr_t>(((a.B - 1) * stride + kD) * 2);
+    fuse = !ov(a.q, a.B * kH * kD * 2, o0, o1) && !ov(a.kv_raw, a.B * a.n_raw * kD * 2, o0, o1) &&
+           !ov(a.out, a.B * kH * kD * 2, o0, o1) && !ov(a.sink, kH * 4, o0, o1) &&
+           !ov(a.lse, a.B * kH * 4, o0, o1) &&
+           !ov(a.ws, static_cast<int64_t>(attn_workspace_bytes(a.B, a.T)), o0, o1);
+  }
+  if (!fuse) {
+    const hipError_t e = launch_compress(j, s);
+    return e != hipSuccess ? e : launch_attn(a, s);
+  }
+  Params P{};
+  P.B = a.B; P.T = a.T; P.N = a.N; P.k = 0; P.ratio = a.ratio; P.q_pos0 = a.q_pos0;
+  P.q = a.q; P.kv_cmp = a.kv_cmp; P.idx = nullptr; P.kv_raw = a.kv_raw;
+  P.raw_pos0 = a.raw_pos0; P.n_raw = a.n_raw; P.window = a.window;
+  P.scale_log2 = a.scale * kLog2e; P.sink = a.sink; P.out = a.out; P.lse = a.lse;
+  P.ws = static_cast<float*>(a.ws);
+  P.rope_R = a.rope_dims;
+  P.rope_l2b = a.rope_dims > 0 ? std::log2(static_cast<double>(a.rope_base)) : 0.0;
+  P.splits = splits;
+  // 512 threads: 64 channel threads (8 channels each) x 8 row groups of 16 rows
+  const double jl2b = j.rope_dims > 0 ? std::log2(static_cast<double>(j.rope_base)) : 0.0;
+  P.job = CompressJobDev{j.Ca, j.Za, nullptr, nullptr, nullptr, nullptr, j.bias, j.gamma, j.out, j.n_tok, j.pos0,
+                         stride, 1, j.B, j.eps, static_cast<int>(j.c), 8, j.rope_dims, jl2b, j.rope_anchor, nullptr,
+                         stride / j.c, 0};
+  P.job_tile = e_new / kTile;   // a dense list: entry e is list row e
+  const int64_t nq = a.B * a.T;
+  hipLaunchKernelGGL((attn_bf16_kernel<2, 4, false, true>), dim3(static_cast<uint32_t>(nq * P.splits)), dim3(512), 0,
+                     s, P);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(nq * 16)), dim3(256), 0, s, P);
+  return hipGetLastError();
+}
 
 }  // namespace csa

@@ -208,6 +208,30 @@ int hca_attn_ex(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int 
   return hip_status(csa::launch_attn(a, as_stream(stream)), "hca_attn launch");
 }
 
+int hca_attn_compressed(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
+                        const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
+                        float scale, const float* sink, int io_dtype, void* out, float* lse, int flags, int rope_dims,
+                        float rope_base, void* workspace, size_t ws_bytes, const csa_compress_job* job, int64_t e_new,
+                        void* stream) {
+  csa::Check ck = csa::check_hca(B, T, N, ratio, q_pos0, H, d, q, kv_cmp, kv_raw, raw_pos0, n_raw, window,
+                                 scale, sink, io_dtype, out, lse, workspace, ws_bytes, flags, rope_dims, rope_base);
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs j[4];
+  ck = check_jobs(job, 1, j);
+  if (!ck.ok()) return finish(ck);
+  if (job->ratio != 128) {
+    ck.fail(CSA_ERR_INVALID_ARG, "the job must be a C128A compression (ratio 128), got ratio " + csa::i2s(job->ratio));
+    return finish(ck);
+  }
+  if (e_new < 0 || e_new >= N) {
+    ck.fail(CSA_ERR_INVALID_ARG, "e_new must lie in [0, N), got " + csa::i2s(e_new));
+    return finish(ck);
+  }
+  csa::AttnArgs a{B, T, N, 0, ratio, q_pos0, q, kv_cmp, nullptr, kv_raw, raw_pos0, n_raw, window, scale,
+                  sink, io_dtype, out, lse, workspace, flags, rope_dims, rope_base};
+  return hip_status(csa::launch_attn_jobs(a, j[0], e_new, as_stream(stream)), "hca_attn_compressed launch");
+}
+
 int hca_attn(int64_t B, int64_t T, int64_t N, int ratio, int64_t q_pos0, int H, int d, const void* q,
              const void* kv_cmp, const void* kv_raw, int64_t raw_pos0, int64_t n_raw, int window,
              float scale, const float* sink, int io_dtype, void* out, float* lse, void* workspace,

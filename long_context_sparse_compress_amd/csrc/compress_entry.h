@@ -142,7 +142,7 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
                                                float eps, TO* __restrict__ out, int64_t out_stride, int G,
                                                float* __restrict__ part, int rope_R, double rope_l2b,
                                                int rope_anchor, void* __restrict__ out_scale,
-                                               int64_t scale_stride, int64_t out_i = -1) {
+                                               int64_t scale_stride, int64_t out_i = -1, float* lds = nullptr) {
   const int64_t io = out_i >= 0 ? out_i : i;   // where the entry is written (a paged row: 0 from its row)
   constexpr int ROWS = (RATIO == 4) ? 8 : RATIO;
   static_assert(VEC % 2 == 0 && 32 % VEC == 0 && UC <= ROWS, "whole RoPE pairs, whole MXFP4 blocks");
@@ -258,7 +258,10 @@ __device__ __forceinline__ void compress_entry(int64_t i, int64_t b, int z, int 
 
   // Tree merge of the G row groups through LDS: at each level the upper half
   // of the remaining groups hands its states to the lower half.
-  extern __shared__ float smem[];
+  // LDS for the group merge and the norm sums: the launch's dynamic LDS, or
+  // `lds` when the caller lends a region of its own
+  extern __shared__ float smem_dyn[];
+  float* const smem = lds ? lds : smem_dyn;
   for (int half = G >> 1; half >= 1; half >>= 1) {
     float* base = smem + static_cast<int64_t>(g - half) * 3 * c;
     if (g >= half && g < 2 * half) {

@@ -144,6 +144,11 @@ hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// A dense decode's C128A write (one entry a sequence, at entry e_new of
+// kv_cmp), then the attention: one launch where the attention's decode plan
+// allows, else the compressor's launch and the attention's.  The entry's
+// pooling may sum its row groups in another order on the two routes.
+hipError_t launch_attn_jobs(const AttnArgs& a, const CompressArgs& job, int64_t e_new, hipStream_t s);
 // Device address, on the current device, of the attention kernels' static
 // scratch (kAttnStaticScratchBytes bytes); looked up once per device.
 hipError_t attn_static_scratch(void** ptr);

@@ -14,6 +14,7 @@ hipError_t launch_index_jobs(const IndexArgs&, const CompressArgs*, int, int64_t
 hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_pool(const IndexPoolArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_attn_jobs(const AttnArgs&, const CompressArgs&, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_rope(const RopeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t attn_static_scratch(void** ptr) {
   *ptr = nullptr;

@@ -170,6 +170,38 @@ def test_index_compressed_validation(lib):
     assert call([job(ratio=128, n_tok=128, Cb=None, Zb=None, prev_Cb=None, prev_Zb=None), job()]) == -1
 
 
+def test_hca_compressed_validation(lib):
+    """hca_attn_compressed: hca_attn_ex's checks, then the job's (ratio 128),
+    then e_new.  Error cases only: a valid call would launch."""
+    import ctypes
+    import long_context_sparse_compress_amd as csa
+    f = lib.hca_attn_compressed
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.POINTER(csa._CompressJob), ctypes.c_int64, ctypes.c_void_p]
+
+    def job(**kw):
+        d = dict(ratio=128, B=2, n_tok=128, c=512, pos0=1024 * 128 - 128, Ca=A, Za=A, Cb=None, Zb=None,
+                 prev_Cb=None, prev_Zb=None, bias=A, gamma=None, eps=1e-6, in_dtype=1, out_dtype=1, out=A,
+                 out_batch_stride=0)
+        d.update(kw)
+        return csa._CompressJob(**d)
+
+    def call(j, e_new=1023, H=64, N=1024):
+        arr = (csa._CompressJob * 1)(j)
+        wsb = lib.csa_workspace_bytes(4, 2, 1, N, 0)
+        return f(2, 1, N, 128, 1024 * 128 - 1, H, 512, A, A, A, 1024 * 128 - 128, 128, 128, 0.04, None, 1, A, None,
+                 0, 0, 0.0, A, wsb, arr, e_new, None)
+
+    assert call(job(), H=32) == -2                                   # the attention is checked first
+    assert call(job(Ca=None)) == -1 and "job 0: Ca is NULL" in _err(lib)
+    assert call(job(ratio=4, n_tok=4, Cb=A, Zb=A, prev_Cb=A, prev_Zb=A)) == -1 and "ratio 128" in _err(lib)
+    assert call(job(), e_new=1024) == -1 and "e_new" in _err(lib)
+    assert call(job(), e_new=-1) == -1 and "e_new" in _err(lib)
+
+
 def test_topk_validation(lib):
     f = lib.topk_select
     assert f(1, 1, 64, 255, 4, 0, A, 1, A, None, 0, None) == -1 and "k must be" in _err(lib)
