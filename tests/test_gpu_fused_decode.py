@@ -261,3 +261,11 @@ def test_fallback_two_queries_a_sequence():
     torch.cuda.synchronize()
     assert torch.equal(k1, k2) and torch.equal(ks1, ks2)
     assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+
+
+def test_fused_new_entry_in_a_ragged_last_tile():
+    """N = 5,000 (the last key run and its last tile partial): the written
+    entry is the very last key."""
+    c = _case("fd.rag", 3, 5000, 4999, 4 * 5000 - 1)
+    cc, s = _check(c)
+    _new_key_score(c, cc, s, 2)

@@ -171,3 +171,10 @@ def test_fused_hca_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(kv, ref_kv), f"replay {rep}: cache"
         assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}: output"
+
+
+def test_fused_hca_ragged_last_tile():
+    """4,100 entries (the new entry alone in a partial tile of the short last
+    split, followed by the window)."""
+    d = _case("fh.rag", 16, 4100, 4100 * 128 - 1)
+    _check(d, oracle_seqs=(5,))
