@@ -215,8 +215,11 @@ def csa_1m_decode(torch, csa, synth, copies=4, fuse=True):
     return wk
 
 
-def csa_decode(torch, csa, synth, copies=4):
-    """Config 2: CSA decode at 65,536 context, batch 32, bf16 indexer, top-512."""
+def csa_decode(torch, csa, synth, copies=4, fuse=True):
+    """Config 2: CSA decode at 65,536 context, batch 32, bf16 indexer, top-512.
+    fuse: the key write inside the indexer's launch (lightning_index_compressed)
+    and the latent write in spare workgroups of Top-k's (topk_select_compressed);
+    else one compressor launch for both."""
     bf = torch.bfloat16
     dn = synth.device_normal
     B, N, k, t = 32, 16384, 512, 65535
@@ -241,13 +244,27 @@ def csa_decode(torch, csa, synth, copies=4):
                               index_heads=64, index_dim=128, index_qk="bf16", scores="bf16",
                               cache_copies_rotated=copies),
               "lightning_index")
-    wk.add("compress_c4a_kv_keys", lambda r: csa.csa_compress_batch([
-        _c4_job(c4, b4, pos4, kv[r], N - 1), _c4_job(c4k, b4k, pos4, keys[r], N - 1)]),
-        _c4_decode_bytes(B, 512) + _c4_decode_bytes(B, 128), 0, "hbm")
-    wk.add("lightning_index", lambda r: csa.lightning_index(qi, w, keys[r], q_pos0=t, scores=scores),
-           B * N * 256 + B * 64 * 128 * 2 + B * 64 * 4 + B * N * 2, B * N * 64 * 128 * 2, "hbm")
-    wk.add("topk_select", lambda r: csa.topk_select(scores, k, q_pos0=t, idx=idx, workspace=ws_t),
-           B * N * 2 + B * k * 4, 0, "hbm")
+    c_lat, c_key = _c4_decode_bytes(B, 512), _c4_decode_bytes(B, 128)
+    i_bytes, i_flops = B * N * 256 + B * 64 * 128 * 2 + B * 64 * 4 + B * N * 2, B * N * 64 * 128 * 2
+    t_bytes = B * N * 2 + B * k * 4
+    if fuse:
+        wk.dominant = "compress_index"
+        wk.label = wk.label.replace("C4A compress (latent + bf16 key), bf16 indexer",
+                                    "C4A compress (bf16 key inside the bf16 indexer's launch, latent inside "
+                                    "Top-k's), bf16 indexer")
+        wk.add("compress_index", lambda r: csa.lightning_index_compressed(
+            qi, w, keys[r], [_c4_job(c4k, b4k, pos4, keys[r], N - 1)], e_new=N - 1, q_pos0=t, scores=scores),
+            c_key + i_bytes, i_flops, "hbm")
+        wk.add("compress_topk", lambda r: csa.topk_select_compressed(
+            scores, k, [_c4_job(c4, b4, pos4, kv[r], N - 1)], q_pos0=t, idx=idx, workspace=ws_t),
+            c_lat + t_bytes, 0, "hbm")
+    else:
+        wk.add("compress_c4a_kv_keys", lambda r: csa.csa_compress_batch([
+            _c4_job(c4, b4, pos4, kv[r], N - 1), _c4_job(c4k, b4k, pos4, keys[r], N - 1)]), c_lat + c_key, 0, "hbm")
+        wk.add("lightning_index", lambda r: csa.lightning_index(qi, w, keys[r], q_pos0=t, scores=scores),
+               i_bytes, i_flops, "hbm")
+        wk.add("topk_select", lambda r: csa.topk_select(scores, k, q_pos0=t, idx=idx, workspace=ws_t), t_bytes, 0,
+               "hbm")
     wk.add("sparse_mqa_attn", lambda r: csa.sparse_mqa_attn(q, kv[r], idx, raw, q_pos0=t, raw_pos0=raw0, out=out,
                                                             workspace=ws_a),
            B * ((k + 128) * 1024 + k * 4 + 2 * 64 * 512 * 2), B * (k + 128) * 64 * 512 * 4, "hbm")
@@ -287,6 +304,14 @@ def csa_decode(torch, csa, synth, copies=4):
 
 
 # ---------------------------------------------------------------- prefill CSA layer
+
+
+def csa_decode_separate(torch, csa, synth, copies=4):
+    """The CSA decode at 65,536 context with both compressor writes in a launch of
+    their own (A/B against the configuration's fused launches)."""
+    wk = csa_decode(torch, csa, synth, copies=copies, fuse=False)
+    wk.key = "csa_decode_separate"
+    return wk
 
 
 def csa_prefill(torch, csa, synth, copies=1):
@@ -838,6 +863,6 @@ def hbm_read(torch, csa, synth, copies=4):
 EXTRAS = {"csa_hca_decode": csa_hca_decode, "c128a_1m": c128a_1m, "csa_reindex_decode": csa_reindex_decode,
           "csa_reindex_prefill": csa_reindex_prefill, "csa_paged_decode": csa_paged_decode,
           "csa_paged_1m_decode": csa_paged_1m_decode, "csa_1m_decode_separate": csa_1m_decode_separate,
-          "hca_decode_separate": hca_decode_separate,
+          "hca_decode_separate": hca_decode_separate, "csa_decode_separate": csa_decode_separate,
           "hbm_copy": hbm_copy,
           "hbm_read": hbm_read}

@@ -8,6 +8,7 @@
  *   csa_compress_batch  several compressor calls of one ratio in one launch
  *   lightning_index_compressed  a decode step's compressor writes and the indexer in one call
  *   hca_attn_compressed  a decode step's C128A write and the HCA attention in one call
+ *   topk_select_compressed  a decode step's compressor writes and Top-k in one call
  *   lightning_index   indexer scores  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
  *   topk_select       causal Top-k over the indexer scores
  *   sparse_mqa_attn   shared-KV MQA over the Top-k entries plus the window
@@ -269,10 +270,11 @@ int lightning_index(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio,
  * csa_compress_batch; n_jobs may be 0, then this is lightning_index), and
  * e_new, the key entry the jobs write (ignored when n_jobs is 0).  The jobs
  * must not write q, q_scale, w or scores; a job may write the keys only at
- * entry e_new.  With MXFP4 keys, T = 1 and jobs that each write one entry per
+ * entry e_new.  With MXFP4 or bf16 keys, T = 1 and jobs that each write one entry per
  * sequence from bf16 rows (n_tok = 4, B as the indexer's, c <= 512, outputs
  * bf16, fp8 or MXFP4; any output inside k / k_scale being exactly entry e_new
- * of every sequence in their layout) the jobs run inside the indexer's launch,
+ * of every sequence in their layout: MXFP4 codes and scales for MXFP4 keys,
+ * bf16 for bf16 keys) the jobs run inside the indexer's launch,
  * in the workgroup that scores entry e_new of each sequence, before it reads
  * its keys; otherwise the call makes the two launches.  Errors: as
  * lightning_index and csa_compress_batch; e_new outside [0, N) with jobs is
@@ -303,6 +305,27 @@ int lightning_index_compressed(int64_t B, int64_t T, int64_t N, int64_t q_pos0, 
 int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k,
                 const void* scores, int score_dtype, int32_t* idx,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * topk_select_compressed -- a decode step's compressor writes and Top-k as
+ * one call.
+ *
+ * The results of csa_compress_batch(jobs, n_jobs, stream) followed by
+ * topk_select(...) on the same stream.  Top-k reads only the scores, so a
+ * write that no stage before the attention reads -- the step's new 512-d
+ * latent entry ("DeepSeek V4 结构速览", C4A Compressor) -- can go here.
+ * Arguments: those of topk_select, then the jobs (the rules of
+ * csa_compress_batch; n_jobs may be 0, then this is topk_select).  The jobs
+ * must not write the scores or idx.  With bf16 scores on the one-workgroup-a-
+ * row path (rows of up to 40,960 candidates, N a multiple of 8) and C4A jobs
+ * of one entry per sequence from bf16 rows (n_tok = 4, c <= 512), the jobs
+ * run in spare workgroups of Top-k's launch; otherwise the call makes the two
+ * launches.  Errors: as topk_select and csa_compress_batch.
+ */
+int topk_select_compressed(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k,
+                           const void* scores, int score_dtype, int32_t* idx,
+                           void* workspace, size_t ws_bytes,
+                           const csa_compress_job* jobs, int n_jobs, void* stream);
 
 /*
  * lightning_index_pool / topk_select_pool -- the hierarchical sparse indexer.

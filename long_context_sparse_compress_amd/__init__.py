@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "lightning_index_compressed", "hca_attn_compressed", "topk_select", "sparse_mqa_attn", "hca_attn",
+__all__ = ["csa_compress", "csa_compress_batch", "lightning_index", "lightning_index_compressed", "hca_attn_compressed", "topk_select_compressed", "topk_select", "sparse_mqa_attn", "hca_attn",
            "sparse_mqa_attn_noalloc",
            "rope", "lightning_index_pool", "topk_select_pool", "csa_compress_paged", "csa_compress_paged_chunk",
            "csa_compress_paged_batch",
@@ -97,6 +97,9 @@ def library() -> ctypes.CDLL:
         lib.lightning_index_compressed.restype = ctypes.c_int
         lib.hca_attn_compressed.argtypes = (_SIGS["hca_attn_ex"][:-1] + [ctypes.POINTER(_CompressJob), _i64, _vp])
         lib.hca_attn_compressed.restype = ctypes.c_int
+        lib.topk_select_compressed.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _vp, _sz,
+                                               ctypes.POINTER(_CompressJob), _int, _vp]
+        lib.topk_select_compressed.restype = ctypes.c_int
         lib.csa_compress_paged_batch.argtypes = [ctypes.POINTER(_CompressPagedJob), _int, _vp]
         lib.csa_compress_paged_batch.restype = ctypes.c_int
         lib.csa_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
@@ -324,6 +327,21 @@ def topk_select(scores, k, *, q_pos0, ratio=4, idx=None, workspace=None, stream=
     st = library().topk_select(B, T, N, q_pos0, ratio, k, _ptr(scores), _dt(scores), _ptr(idx),
                                _ptr(ws), wsb, _stream(stream))
     _check(st, "topk_select")
+    return idx
+
+
+def topk_select_compressed(scores, k, jobs, *, q_pos0, ratio=4, idx=None, workspace=None, stream=None):
+    """A decode step's compressor writes (csa_compress_batch's job dicts), then
+    stage 3, in one call: the results of csa_compress_batch(jobs) followed by
+    topk_select(...)."""
+    B, T, N = scores.shape
+    if idx is None:
+        idx = torch.empty(B, T, k, dtype=torch.int32, device=scores.device)
+    ws, wsb = _workspace(OP_TOPK, B, T, N, k, scores.device, workspace)
+    arr, _ = _compress_jobs(jobs) if jobs else (None, [])
+    st = library().topk_select_compressed(B, T, N, q_pos0, ratio, k, _ptr(scores), _dt(scores), _ptr(idx), _ptr(ws),
+                                          wsb, arr, len(jobs), _stream(stream))
+    _check(st, "topk_select_compressed")
     return idx
 
 

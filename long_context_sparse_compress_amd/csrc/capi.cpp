@@ -138,6 +138,20 @@ int topk_select(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int 
   return hip_status(csa::launch_topk(a, as_stream(stream)), "topk_select launch");
 }
 
+int topk_select_compressed(int64_t B, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k, const void* scores,
+                           int score_dtype, int32_t* idx, void* workspace, size_t ws_bytes,
+                           const csa_compress_job* jobs, int n_jobs, void* stream) {
+  csa::Check ck = csa::check_topk(B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace, ws_bytes);
+  if (!ck.ok()) return finish(ck);
+  csa::CompressArgs a[4];
+  if (n_jobs != 0) {
+    ck = check_jobs(jobs, n_jobs, a);
+    if (!ck.ok()) return finish(ck);
+  }
+  csa::TopkArgs ta{B, T, N, q_pos0, ratio, k, scores, score_dtype, idx, workspace, nullptr, 0};
+  return hip_status(csa::launch_topk_jobs(ta, a, n_jobs, as_stream(stream)), "topk_select_compressed launch");
+}
+
 int lightning_index_pool(int64_t B, int64_t T, int64_t N, int64_t P, int H_I, int d_I, const void* q,
                          const void* q_scale, const float* w, const void* k, const void* k_scale, int qk_dtype,
                          const int32_t* pool, void* scores, int score_dtype, void* stream) {

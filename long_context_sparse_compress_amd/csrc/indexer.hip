@@ -451,12 +451,20 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   }
 }
 
-template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS, bool PG = false>
+// A decode step's compressor jobs run by the ring kernel's workgroup whose
+// key run x_own holds the written entry (see index_ring_kernel).
+struct RingJobs {
+  CompressBatch jb;
+  int n;
+  int64_t x_own;
+};
+
+template <int QK, int QPW, int TPW, int D, bool XS, bool PIPE, typename TS, bool PG = false, bool CJ = false>
 __global__ void __launch_bounds__(256, PIPE ? 1 : 2)
 index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
                   const uint8_t* __restrict__ q, const void* __restrict__ q_scale,
                   const float* __restrict__ w, const uint8_t* __restrict__ k,
-                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg) {
+                  const void* __restrict__ k_scale, TS* __restrict__ scores, KeyPages pg, RingJobs rj) {
   static_assert(!PG || (QPW == 1 && TPW <= 128), "paged keys: decode shape, a wave's blocks in one lane each");
   static_assert(QK == CSA_BF16 || QK == CSA_FP8_E4M3, "MXFP4 keys use index_mfma_kernel");
   static_assert(TPW % 4 == 0 && TPW >= D, "scores leave four tiles at a time");
@@ -504,6 +512,41 @@ index_ring_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio,
   __shared__ __attribute__((aligned(16))) uint8_t ring5[D > 4 ? 4 : 1][D > 4 ? TB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ring6[D > 4 ? 4 : 1][D > 4 ? TB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ring7[D > 4 ? 4 : 1][D > 4 ? TB : 16];
+
+  if constexpr (CJ) {
+    // The workgroup whose key run holds the step's new entry writes it (and
+    // the step's other one-entry jobs of sequence b) before it stages or
+    // reads anything; ring slot 0 lends the jobs' LDS.  No other workgroup
+    // reads that entry.
+    if (static_cast<int64_t>(bx) == rj.x_own) {
+      float* const lds = reinterpret_cast<float*>(&ring0[0][0]);
+      for (int jn = 0; jn < rj.n; ++jn) {
+        const CompressJobDev& J = rj.jb.j[jn];
+        const auto* Ca = static_cast<const uint16_t*>(J.Ca);
+        const auto* Za = static_cast<const uint16_t*>(J.Za);
+        const auto* Cb = static_cast<const uint16_t*>(J.Cb);
+        const auto* Zb = static_cast<const uint16_t*>(J.Zb);
+        const auto* pCb = static_cast<const uint16_t*>(J.pCb);
+        const auto* pZb = static_cast<const uint16_t*>(J.pZb);
+        if (J.qfmt == 2)
+          compress_entry<uint16_t, E2M1x2, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                           J.bias, J.gamma, J.eps, static_cast<E2M1x2*>(J.out),
+                                                           J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                           J.rope_anchor, J.out_scale, J.scale_stride, -1, lds);
+        else if (J.qfmt == 1)
+          compress_entry<uint16_t, uint8_t, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb,
+                                                            pZb, J.bias, J.gamma, J.eps, static_cast<uint8_t*>(J.out),
+                                                            J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                            J.rope_anchor, J.out_scale, J.scale_stride, -1, lds);
+        else
+          compress_entry<uint16_t, uint16_t, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb,
+                                                             pZb, J.bias, J.gamma, J.eps, static_cast<uint16_t*>(J.out),
+                                                             J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                             J.rope_anchor, J.out_scale, J.scale_stride, -1, lds);
+        __syncthreads();   // the job's writes are visible and its LDS is free
+      }
+    }
+  }
 
   // paged: lane i holds the physical block of the wave's i-th 32-entry
   // block, loaded before anything else (the counter of loads in flight is in
@@ -750,10 +793,12 @@ hipError_t launch_ring(const IndexArgs& a, hipStream_t s) {
   const KeyPages pg{a.block_table, a.max_blocks, a.n_pool, a.seq_pos};
   if (a.score_dtype == CSA_BF16)
     hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, uint16_t, PG>), grid, dim3(256), 0, s, a.T,
-                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores), pg);
+                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<uint16_t*>(a.scores), pg,
+                       RingJobs{});
   else
     hipLaunchKernelGGL((index_ring_kernel<QK, QPW, TPW, D, XS, PIPE, float, PG>), grid, dim3(256), 0, s, a.T,
-                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores), pg);
+                       a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale, static_cast<float*>(a.scores), pg,
+                       RingJobs{});
   return hipGetLastError();
 }
 
@@ -817,13 +862,15 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
 
 namespace {
 
-// Whether launch_index_jobs may run the jobs inside the MXFP4 decode
-// indexer's launch: every job a one-entry C4A write from bf16 rows in the
+// Whether launch_index_jobs may run the jobs inside the decode indexer's
+// launch (MXFP4 keys: the register kernel; bf16 keys: the ring kernel): every job a one-entry C4A write from bf16 rows in the
 // narrow layout (two channels a thread, at most 256 threads), and any job
 // output that lands in the keys or their scales is exactly entry e_new in
 // the layout the indexer reads; no job output touches q, w or the scores.
 bool jobs_fusable(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e_new) {
-  if (a.qk_dtype != CSA_MXFP4 || a.T != 1 || a.block_table || a.N < 1 || e_new < 0 || e_new >= a.N) return false;
+  if ((a.qk_dtype != CSA_MXFP4 && a.qk_dtype != CSA_BF16) || a.T != 1 || a.block_table || a.N < 1 || e_new < 0 ||
+      e_new >= a.N)
+    return false;
   if (a.score_dtype != CSA_BF16 && a.score_dtype != CSA_F32) return false;
   auto range = [](const void* p, int64_t bytes) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(p);
@@ -832,8 +879,10 @@ bool jobs_fusable(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e
   auto overlap = [](std::pair<uintptr_t, uintptr_t> x, std::pair<uintptr_t, uintptr_t> y) {
     return x.first < y.second && y.first < x.second;
   };
-  const auto kr = range(a.k, a.B * a.N * 64), sr = range(a.k_scale, a.B * a.N * 4);
-  const auto qr = range(a.q, a.B * 64 * 64), qsr = range(a.q_scale, a.B * 64 * 4), wr = range(a.w, a.B * 64 * 4);
+  const bool bfk = a.qk_dtype == CSA_BF16;   // bf16 keys: 256-byte rows, no scales
+  const auto kr = range(a.k, a.B * a.N * (bfk ? 256 : 64)), sr = range(a.k_scale, bfk ? 0 : a.B * a.N * 4);
+  const auto qr = range(a.q, a.B * 64 * (bfk ? 256 : 64)), qsr = range(a.q_scale, bfk ? 0 : a.B * 64 * 4);
+  const auto wr = range(a.w, a.B * 64 * 4);
   const auto scr = range(a.scores, a.B * a.N * (a.score_dtype == CSA_BF16 ? 2 : 4));
   for (int q = 0; q < n; ++q) {
     const CompressArgs& j = jobs[q];
@@ -852,9 +901,12 @@ bool jobs_fusable(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e
     const bool in_keys = overlap(orr, kr) || (sb && overlap(osr, kr));
     const bool in_scales = overlap(orr, sr) || (sb && overlap(osr, sr));
     if (in_keys || in_scales) {
-      const bool key_entry = j.out_dtype == CSA_MXFP4 && j.c == 128 && stride == a.N * 128 &&
-                             orr.first == kr.first + static_cast<uintptr_t>(e_new * 64) &&
-                             osr.first == sr.first + static_cast<uintptr_t>(e_new * 4);
+      const bool key_entry =
+          bfk ? (j.out_dtype == CSA_BF16 && j.c == 128 && stride == a.N * 128 &&
+                 orr.first == kr.first + static_cast<uintptr_t>(e_new * 256))
+              : (j.out_dtype == CSA_MXFP4 && j.c == 128 && stride == a.N * 128 &&
+                 orr.first == kr.first + static_cast<uintptr_t>(e_new * 64) &&
+                 osr.first == sr.first + static_cast<uintptr_t>(e_new * 4));
       if (!key_entry) return false;
     }
   }
@@ -869,10 +921,6 @@ hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n
     const hipError_t e = launch_compress_batch(jobs, n, s);
     return e != hipSuccess ? e : launch_index(a, s);
   }
-  // the MXFP4 decode shape of launch_qk: one query a wave, 8 tiles a wave;
-  // registers for five waves a SIMD, the plain kernel's occupancy
-  constexpr int TPW = 8, GT = 4, OCC = 5;
-  constexpr int64_t per_wg = 4 * TPW * 16;
   CompressBatch jb{};
   for (int q = 0; q < n; ++q) {
     const CompressArgs& j = jobs[q];
@@ -883,10 +931,31 @@ hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n
                              j.out_scale, stride / j.c,
                              j.out_dtype == CSA_FP8_E4M3 ? 1 : (j.out_dtype == CSA_MXFP4 ? 2 : 0)};
   }
-  const dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg), 1, static_cast<uint32_t>(a.B));
-  const int64_t x_own = e_new / per_wg;
   const auto* q = static_cast<const uint8_t*>(a.q);
   const auto* k = static_cast<const uint8_t*>(a.k);
+  if (a.qk_dtype == CSA_BF16) {
+    // the bf16 decode shape of launch_qk (32 tiles a wave, a 4-slot ring):
+    // the workgroup of the new entry's key run writes it first
+    constexpr int TPW = 32;
+    constexpr int64_t per_wg = 4 * TPW * 16;
+    const dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg), 1, static_cast<uint32_t>(a.B));
+    const RingJobs rj{jb, n, e_new / per_wg};
+    if (a.score_dtype == CSA_BF16)
+      hipLaunchKernelGGL((index_ring_kernel<CSA_BF16, 1, TPW, 4, true, false, uint16_t, false, true>), grid, dim3(256),
+                         0, s, a.T, a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
+                         static_cast<uint16_t*>(a.scores), KeyPages{nullptr, 0, 0, nullptr}, rj);
+    else
+      hipLaunchKernelGGL((index_ring_kernel<CSA_BF16, 1, TPW, 4, true, false, float, false, true>), grid, dim3(256),
+                         0, s, a.T, a.N, a.q_pos0, a.ratio, q, a.q_scale, a.w, k, a.k_scale,
+                         static_cast<float*>(a.scores), KeyPages{nullptr, 0, 0, nullptr}, rj);
+    return hipGetLastError();
+  }
+  // the MXFP4 decode shape of launch_qk: one query a wave, 8 tiles a wave;
+  // registers for five waves a SIMD, the plain kernel's occupancy
+  constexpr int TPW = 8, GT = 4, OCC = 5;
+  constexpr int64_t per_wg = 4 * TPW * 16;
+  const dim3 grid(static_cast<uint32_t>((a.N + per_wg - 1) / per_wg), 1, static_cast<uint32_t>(a.B));
+  const int64_t x_own = e_new / per_wg;
   const size_t smem = 64 * sizeof(float);   // the jobs' RMSNorm sums and fp8 amax
   if (a.score_dtype == CSA_BF16)
     hipLaunchKernelGGL((index_mfma_jobs_kernel<CSA_MXFP4, TPW, GT, OCC, uint16_t>), grid, dim3(256), smem, s, a.N,

@@ -137,11 +137,15 @@ hipError_t launch_compress_batch(const CompressArgs* jobs, int n, hipStream_t s)
 hipError_t launch_compress_paged(const CompressPagedArgs* jobs, int n, hipStream_t s);   // 1..4 jobs
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 // The compressor jobs (1..4), then the indexer: in one launch where the
-// indexer's decode kernel can run them (MXFP4 keys, one query a sequence,
-// one-entry bf16 jobs whose writes into the keys are entry e_new), else as a
+// indexer's decode kernel can run them (MXFP4 or bf16 keys, one query a
+// sequence, one-entry bf16 jobs whose writes into the keys are entry e_new), else as a
 // compressor launch followed by the indexer's.  Same results either way.
 hipError_t launch_index_jobs(const IndexArgs& a, const CompressArgs* jobs, int n, int64_t e_new, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// The compressor jobs (1..4, one entry a sequence), then Top-k: in one launch
+// where the register kernel applies (the jobs in spare workgroups), else as a
+// compressor launch followed by Top-k's.  Same results either way.
+hipError_t launch_topk_jobs(const TopkArgs& a, const CompressArgs* jobs, int n, hipStream_t s);
 hipError_t launch_index_pool(const IndexPoolArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 // A dense decode's C128A write (one entry a sequence, at entry e_new of

@@ -24,6 +24,9 @@
 //  * longer fp32 rows: S workgroups per row, one slice each; per-digit
 //    histograms are merged in global workspace with atomics, one kernel per
 //    pass, then a count kernel and an ordered write kernel.
+#include <cmath>
+
+#include "compress_entry.h"
 #include "device.h"
 #include "launch.h"
 #include "validate.h"
@@ -423,14 +426,14 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
 }
 
 template <int CPT>
-__global__ void __launch_bounds__(1024)
-topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k, const uint16_t* __restrict__ scores,
-                int32_t* __restrict__ idx, const int32_t* __restrict__ pool, int64_t n_ent) {
+__device__ __forceinline__ void topk_reg_body(int64_t row, int64_t T, int64_t N, int64_t q_pos0, int ratio,
+                                              const int64_t* __restrict__ seq_pos, int k,
+                                              const uint16_t* __restrict__ scores, int32_t* __restrict__ idx,
+                                              const int32_t* __restrict__ pool, int64_t n_ent,
+                                              uint32_t* __restrict__ bins) {
   constexpr int NT = 1024;
   static_assert(8 * CPT * NT < 65536, "block-wide counts are packed in 16 bits");
-  __shared__ uint32_t bins[kRangeBins];
   __shared__ uint32_t tmp[32];
-  const int64_t row = blockIdx.x;
   const int64_t t = row % T;
   const int64_t V = row_visible(row, T, q_pos0, ratio, N, seq_pos);
   int32_t* out = idx + row * k;
@@ -614,6 +617,55 @@ topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* 
     take &= take - 1;
   }
 #undef KEY
+}
+
+template <int CPT>
+__global__ void __launch_bounds__(1024)
+topk_reg_kernel(int64_t T, int64_t N, int64_t q_pos0, int ratio, const int64_t* __restrict__ seq_pos, int k,
+                const uint16_t* __restrict__ scores, int32_t* __restrict__ idx, const int32_t* __restrict__ pool,
+                int64_t n_ent) {
+  __shared__ uint32_t bins[kRangeBins];
+  topk_reg_body<CPT>(blockIdx.x, T, N, q_pos0, ratio, seq_pos, k, scores, idx, pool, n_ent, bins);
+}
+
+// Top-k with a decode step's compressor writes in the same launch: workgroups
+// 0 .. rows-1 select as topk_reg_kernel; the ones after them each run one
+// sequence's share of a job (one entry, two channels a thread), which no
+// selection reads -- spare CUs of a launch that fills one CU a row.
+template <int CPT>
+__global__ void __launch_bounds__(1024)
+topk_reg_jobs_kernel(int64_t rows, int64_t T, int64_t N, int64_t q_pos0, int ratio, int k,
+                     const uint16_t* __restrict__ scores, int32_t* __restrict__ idx, CompressBatch jb, int64_t B) {
+  __shared__ uint32_t bins[kRangeBins];
+  if (static_cast<int64_t>(blockIdx.x) < rows) {
+    topk_reg_body<CPT>(blockIdx.x, T, N, q_pos0, ratio, nullptr, k, scores, idx, nullptr, 0, bins);
+    return;
+  }
+  const int64_t w = blockIdx.x - rows;
+  const CompressJobDev& J = jb.j[w / B];
+  const int64_t b = w % B;
+  float* const lds = reinterpret_cast<float*>(bins);
+  const auto* Ca = static_cast<const uint16_t*>(J.Ca);
+  const auto* Za = static_cast<const uint16_t*>(J.Za);
+  const auto* Cb = static_cast<const uint16_t*>(J.Cb);
+  const auto* Zb = static_cast<const uint16_t*>(J.Zb);
+  const auto* pCb = static_cast<const uint16_t*>(J.pCb);
+  const auto* pZb = static_cast<const uint16_t*>(J.pZb);
+  if (J.qfmt == 2)
+    compress_entry<uint16_t, E2M1x2, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                     J.bias, J.gamma, J.eps, static_cast<E2M1x2*>(J.out), J.out_stride,
+                                                     J.G, nullptr, J.rope_R, J.rope_l2b, J.rope_anchor, J.out_scale,
+                                                     J.scale_stride, -1, lds);
+  else if (J.qfmt == 1)
+    compress_entry<uint16_t, uint8_t, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                      J.bias, J.gamma, J.eps, static_cast<uint8_t*>(J.out),
+                                                      J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                      J.rope_anchor, J.out_scale, J.scale_stride, -1, lds);
+  else
+    compress_entry<uint16_t, uint16_t, 4, false, 2, 8>(0, b, 0, 1, J.n_tok, J.c, J.pos0, Ca, Za, Cb, Zb, pCb, pZb,
+                                                       J.bias, J.gamma, J.eps, static_cast<uint16_t*>(J.out),
+                                                       J.out_stride, J.G, nullptr, J.rope_R, J.rope_l2b,
+                                                       J.rope_anchor, J.out_scale, J.scale_stride, -1, lds);
 }
 
 // ------------------------------------------------------------ global path
@@ -1163,6 +1215,61 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return hipSuccess;
   if (a.score_dtype == CSA_BF16) return launch_typed<uint16_t>(a, s);
   return launch_typed<uint32_t>(a, s);
+}
+
+
+// Top-k, with a decode step's compressor jobs in the register kernel's launch
+// where it applies (bf16 rows that fit it, one-entry jobs from bf16 rows of
+// at most 512 channels, outputs clear of the scores and ids); otherwise the
+// jobs' launch, then Top-k's.  Same results either way.
+hipError_t launch_topk_jobs(const TopkArgs& a, const CompressArgs* jobs, int n, hipStream_t s) {
+  if (n < 1) return launch_topk(a, s);
+  const int64_t rows = a.B * a.T;
+  const int cpt = static_cast<int>((a.N + 8 * 1024 - 1) / (8 * 1024));
+  bool fuse = rows > 0 && a.score_dtype == CSA_BF16 && !a.pool && !a.seq_pos && a.N % 8 == 0 &&
+              (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && cpt <= 5;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(a.scores), s1 = s0 + static_cast<uintptr_t>(rows * a.N * 2);
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(a.idx), i1 = i0 + static_cast<uintptr_t>(rows * a.k * 4);
+  for (int q = 0; q < n && fuse; ++q) {
+    const CompressArgs& j = jobs[q];
+    fuse = j.ratio == 4 && j.n_tok == 4 && j.B == jobs[0].B && j.c <= 512 && j.in_dtype == CSA_BF16 &&
+           (j.out_dtype == CSA_BF16 || j.out_dtype == CSA_FP8_E4M3 || j.out_dtype == CSA_MXFP4);
+    const int64_t stride = j.out_batch_stride ? j.out_batch_stride : j.c;
+    const int64_t span = (j.B - 1) * stride + j.c;
+    const int64_t ob = j.out_dtype == CSA_BF16 ? 2 * span : (j.out_dtype == CSA_FP8_E4M3 ? span : span / 2);
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(j.out), o1 = o0 + static_cast<uintptr_t>(ob);
+    if ((o0 < s1 && s0 < o1) || (o0 < i1 && i0 < o1)) fuse = false;
+    if (j.out_scale) {
+      const uintptr_t c0 = reinterpret_cast<uintptr_t>(j.out_scale);
+      const uintptr_t c1 = c0 + static_cast<uintptr_t>(((j.B - 1) * (stride / j.c) + 1) * 4 * (j.c / 32 + 1));
+      if ((c0 < s1 && s0 < c1) || (c0 < i1 && i0 < c1)) fuse = false;
+    }
+  }
+  if (!fuse) {
+    const hipError_t e = launch_compress_batch(jobs, n, s);
+    return e != hipSuccess ? e : launch_topk(a, s);
+  }
+  CompressBatch jb{};
+  for (int q = 0; q < n; ++q) {
+    const CompressArgs& j = jobs[q];
+    const int64_t stride = j.out_batch_stride ? j.out_batch_stride : j.c;
+    const double l2b = j.rope_dims > 0 ? std::log2(static_cast<double>(j.rope_base)) : 0.0;
+    jb.j[q] = CompressJobDev{j.Ca, j.Za, j.Cb, j.Zb, j.prev_Cb, j.prev_Zb, j.bias, j.gamma, j.out, j.n_tok, j.pos0,
+                             stride, 1, j.B, j.eps, static_cast<int>(j.c), 1, j.rope_dims, l2b, j.rope_anchor,
+                             j.out_scale, stride / j.c,
+                             j.out_dtype == CSA_FP8_E4M3 ? 1 : (j.out_dtype == CSA_MXFP4 ? 2 : 0)};
+  }
+  const int64_t B = jobs[0].B;
+  const dim3 grid(static_cast<uint32_t>(rows + n * B));
+  const auto* sc = static_cast<const uint16_t*>(a.scores);
+  switch (cpt) {
+    case 1: hipLaunchKernelGGL(topk_reg_jobs_kernel<1>, grid, dim3(1024), 0, s, rows, a.T, a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, jb, B); break;
+    case 2: hipLaunchKernelGGL(topk_reg_jobs_kernel<2>, grid, dim3(1024), 0, s, rows, a.T, a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, jb, B); break;
+    case 3: hipLaunchKernelGGL(topk_reg_jobs_kernel<3>, grid, dim3(1024), 0, s, rows, a.T, a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, jb, B); break;
+    case 4: hipLaunchKernelGGL(topk_reg_jobs_kernel<4>, grid, dim3(1024), 0, s, rows, a.T, a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, jb, B); break;
+    default: hipLaunchKernelGGL(topk_reg_jobs_kernel<5>, grid, dim3(1024), 0, s, rows, a.T, a.N, a.q_pos0, a.ratio, a.k, sc, a.idx, jb, B); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace csa

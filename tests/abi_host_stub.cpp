@@ -12,6 +12,7 @@ hipError_t launch_compress_paged(const CompressPagedArgs*, int, hipStream_t) { r
 hipError_t launch_index(const IndexArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_jobs(const IndexArgs&, const CompressArgs*, int, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_topk(const TopkArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_topk_jobs(const TopkArgs&, const CompressArgs*, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_index_pool(const IndexPoolArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_attn_jobs(const AttnArgs&, const CompressArgs&, int64_t, hipStream_t) { return hipSuccess; }

@@ -202,6 +202,31 @@ def test_hca_compressed_validation(lib):
     assert call(job(), e_new=-1) == -1 and "e_new" in _err(lib)
 
 
+def test_topk_compressed_validation(lib):
+    """topk_select_compressed: topk_select's checks, then the jobs'.  Error
+    cases only: a valid call would launch."""
+    import ctypes
+    import long_context_sparse_compress_amd as csa
+    f = lib.topk_select_compressed
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(csa._CompressJob),
+                                         ctypes.c_int, ctypes.c_void_p]
+
+    def job(**kw):
+        d = dict(ratio=4, B=2, n_tok=4, c=512, pos0=4, Ca=A, Za=A, Cb=A, Zb=A, prev_Cb=A, prev_Zb=A,
+                 bias=A, gamma=None, eps=1e-6, in_dtype=1, out_dtype=1, out=A, out_batch_stride=0)
+        d.update(kw)
+        return csa._CompressJob(**d)
+
+    def call(jobs, n=None, k=16):
+        arr = (csa._CompressJob * len(jobs))(*jobs)
+        return f(2, 1, 64, 255, 4, k, A, 1, A, None, 0, arr, len(jobs) if n is None else n, None)
+
+    assert call([job()], k=0) == -1 and "k must be" in _err(lib)    # Top-k is checked first
+    assert call([job(Za=None)]) == -1 and "job 0: Za is NULL" in _err(lib)
+    assert call([job()], n=5) == -1 and "n_jobs" in _err(lib)
+
+
 def test_topk_validation(lib):
     f = lib.topk_select
     assert f(1, 1, 64, 255, 4, 0, A, 1, A, None, 0, None) == -1 and "k must be" in _err(lib)

@@ -39,7 +39,7 @@ def _job(c4, bias, pos0, out, entry, out_scale=None, **kw):
 
 
 def _case(tag, B, N, e_new, q_pos0, keys="mxfp4", n_kv=16, kv_entry=5, rope=0, gamma=False, fp8_side=False,
-          key_entry=None):
+          key_entry=None, key_only=False):
     """Inputs and two identical sets of caches (one per path)."""
     key_entry = e_new if key_entry is None else key_entry
     x = synth.device_normal(f"{tag}.keys", (B, N, 128))
@@ -69,9 +69,11 @@ def _case(tag, B, N, e_new, q_pos0, keys="mxfp4", n_kv=16, kv_entry=5, rope=0, g
 
     def jobs(cc):
         extra = dict(rope_dims=rope) if rope else {}
-        j = [_job(c4, b4, pos4, cc["kv"], kv_entry, gamma=g512, **extra)]
+        j = [] if key_only else [_job(c4, b4, pos4, cc["kv"], kv_entry, gamma=g512, **extra)]
         if keys == "mxfp4":
             j.append(_job(c4k, b4k, pos4, cc["k"], key_entry, cc["ks"], gamma=g128, **extra))
+        else:
+            j.append(_job(c4k, b4k, pos4, cc["k"], key_entry, gamma=g128, **extra))
         if fp8_side:
             j.append(_job(c4k, b4k, pos4, cc["f8"], 3, cc["f8s"], gamma=g128, **extra))
         return j
@@ -111,7 +113,7 @@ def _same(a, b):
                        b.view(torch.uint8) if b.dtype != torch.uint8 else b)
 
 
-def _check(c, score_dtype=torch.bfloat16, fused_launch=True):
+def _check(c, score_dtype=torch.bfloat16, fused_launch=True, kernel="index_mfma_jobs_kernel"):
     c1, c2 = c["caches"](), c["caches"]()
     s1 = _separate(c, c1, score_dtype)
     s2 = _fused(c, c2, score_dtype)
@@ -123,7 +125,7 @@ def _check(c, score_dtype=torch.bfloat16, fused_launch=True):
     names = _kernels(lambda: _fused(c, c["caches"](), score_dtype))
     if names is not None:
         ours = [n for n in names if "compress" in n or "index" in n]
-        fused = [n for n in ours if "index_mfma_jobs_kernel" in n]
+        fused = [n for n in ours if kernel in n]
         if fused_launch:
             assert len(fused) == 1 and not any("compress_batch_kernel" in n for n in ours), ours
         else:
@@ -187,10 +189,18 @@ def test_fused_new_entry_partly_visible():
     _check(c)
 
 
-def test_fallback_bf16_keys():
-    """bf16 keys: the jobs and the ring indexer in two launches."""
+def test_fused_bf16_keys_ring():
+    """bf16 keys: the jobs (latent and bf16 key) run by the ring indexer's
+    workgroup of the new entry's key run, in one launch."""
     c = _case("fd.bf", 4, 3000, 2999, 4 * 3000 - 1, keys="bf16")
-    _check(c, fused_launch=False)
+    _check(c, kernel="index_ring_kernel<1, 1, 32, 4, true, false, unsigned short, false, true>")
+
+
+def test_fused_bf16_keys_ring_decode_size():
+    """The CSA decode at 65,536 context: batch 32, 16,384 bf16 keys, the key
+    job alone in the indexer's launch."""
+    c = _case("fd.bf32", 32, 16384, 16383, 4 * 16384 - 1, keys="bf16", key_only=True)
+    _check(c, kernel="index_ring_kernel<1, 1, 32, 4, true, false, unsigned short, false, true>")
 
 
 def test_fallback_key_written_elsewhere():
@@ -269,3 +279,38 @@ def test_fused_new_entry_in_a_ragged_last_tile():
     c = _case("fd.rag", 3, 5000, 4999, 4 * 5000 - 1)
     cc, s = _check(c)
     _new_key_score(c, cc, s, 2)
+
+
+
+def _topk_case(tag, B, N, k, q_pos0):
+    scores = synth.device_normal(f"{tag}.s", (B, 1, N), BF)
+    kv = synth.device_normal(f"{tag}.kv", (B, 8, 512), BF)
+    c4 = _c4(f"{tag}.c4", B, 512)
+    b4 = synth.device_normal(f"{tag}.b4", (8, 512), var=0.1)
+    g = synth.device_uniform(f"{tag}.g", (512,)) + 0.5
+    return scores, kv, (lambda out: [_job(c4, b4, q_pos0 - 3, out, 6, gamma=g, rope_dims=64)])
+
+
+@pytest.mark.parametrize("B,N,k,fused_launch", [
+    (32, 16384, 512, True),      # the CSA decode at 65,536 context: the latent in spare workgroups
+    (3, 2000, 512, True),        # rows shorter than one chunk a thread
+    (2, 262144, 1024, False),    # long rows (the two-launch sliced path): the two calls
+])
+def test_topk_compressed(B, N, k, fused_launch):
+    """topk_select_compressed = csa_compress_batch + topk_select: the same ids
+    and the same written entry, bit for bit."""
+    q0 = 4 * N - 1
+    scores, kv, jobs = _topk_case(f"fd.tk{B}.{N}", B, N, k, q0)
+    kv1, kv2 = kv.clone(), kv.clone()
+    csa.csa_compress_batch(jobs(kv1))
+    i1 = csa.topk_select(scores, k, q_pos0=q0)
+    i2 = csa.topk_select_compressed(scores, k, jobs(kv2), q_pos0=q0)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(kv1, kv2)
+    names = _kernels(lambda: csa.topk_select_compressed(scores, k, jobs(kv.clone()), q_pos0=q0))
+    if names is not None:
+        ours = [n for n in names if "topk" in n or "compress" in n]
+        if fused_launch:
+            assert any("topk_reg_jobs_kernel" in n for n in ours) and not any("compress_batch" in n for n in ours), ours
+        else:
+            assert any("compress_batch" in n for n in ours), ours
