@@ -58,8 +58,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="all")
     p.add_argument("--rotate", type=int, default=4, help="cache copies cycled over the steps (decode workloads)")
     p.add_argument("--eager", action="store_true",
